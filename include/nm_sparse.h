@@ -1,0 +1,107 @@
+/*
+ * nm_sparse.h -- C ABI of libnmsparse.so: batch-one N:M semi-structured sparse
+ * matrix-vector product y = W x on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (the pages, cited by title and section):
+ *   [NEWS-NEW] news.bitwarelabs.com, "SparseDecoding: decoding-aware pruning for
+ *              accurate and fast LLM generation", section "What's new": decoding at
+ *              batch one is memory-bandwidth bound and dominated by sparse
+ *              matrix-vector products; N:M semi-structured sparsity keeps N weights
+ *              of every M consecutive ones; the SpMV uses bitmask indexing and
+ *              fixed-step traversal.
+ *   [KERNEL]   aimodeling.com SparseDecoding article, section "The Kernel Is the
+ *              Other Half of the Answer": a 32-bit mask word per 32 input columns,
+ *              exactly 16 set bits per word at 50% sparsity, replacing per-nonzero
+ *              32-bit column indices; 2:4, 4:8, 8:16 and 16:32 all keep half the
+ *              weights and move the same metadata; speedups are quoted against the
+ *              dense product.
+ *
+ * Format (the packed layout every entry point shares):
+ *   W        fp16 [rows][cols] row-major (out x in, y = W x), cols % 32 == 0.
+ *   masks    uint32 [rows][cols/32]; bit j (LSB = 0) of word w of row r is set iff
+ *            W[r][32w + j] is kept. Every word has exactly 32*N/M = 16 set bits and
+ *            every aligned group of M columns exactly N.
+ *   values   fp16 [rows][cols*N/M]; the kept weights of row r, word by word, in
+ *            ascending column order, so word w's values start at 16*w of the row.
+ *   x        fp16 [cols];  y  fp16 [rows].
+ *   fp16 is passed as its raw bit pattern (uint16_t).
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller. The library never
+ *     allocates, frees, copies to the host or synchronises.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).
+ *     Work is enqueued on it and the call returns at once.
+ *   - Arguments are validated before any HIP call; an invalid call returns a status
+ *     code and enqueues nothing. Calls never abort, print or throw.
+ *   - A fault inside a kernel is not reported by the call; it surfaces at the
+ *     caller's next synchronisation on the stream.
+ *   - Outputs must not alias inputs (documented, not checked).
+ *   - Thread-safe and reentrant; the only state is a per-device cache of device
+ *     attributes.
+ */
+#ifndef NM_SPARSE_H
+#define NM_SPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NM_OK = 0,
+  NM_ERR_NULL = 1,     /* a required pointer is NULL                                   */
+  NM_ERR_SHAPE = 2,    /* rows < 1, cols < 32, cols % 32 != 0, or a size overflows      */
+  NM_ERR_PATTERN = 3,  /* (N, M) not one of (2,4), (4,8), (8,16), (16,32)               */
+  NM_ERR_ALIGN = 4,    /* W, values or x not 16-byte aligned; masks not 4-byte; y not 2 */
+  NM_ERR_TOO_WIDE = 5, /* 2*cols bytes of x exceed the LDS one workgroup may use        */
+  NM_ERR_HIP = 6       /* a HIP runtime call failed (see nm_last_hip_error)             */
+} nm_status;
+
+/* Number of fp16 values of the packed matrix: rows*cols*N/M; 0 if the arguments are
+ * invalid. Pure host function. */
+size_t nm_values_count(int64_t rows, int64_t cols, int N, int M);
+
+/* Number of uint32 mask words: rows*cols/32; 0 if the arguments are invalid. */
+size_t nm_masks_count(int64_t rows, int64_t cols);
+
+/* Widest x (in columns, a multiple of 32) that nm_spmv and nm_gemv_dense accept on
+ * the current HIP device, from its per-workgroup LDS size; 0 if no device. */
+int64_t nm_max_cols(void);
+
+/* Encoder ([NEWS-NEW] N-of-M selection, [KERNEL] bitmask format).
+ * In each aligned group of M columns keep the N weights of largest magnitude, where
+ * the magnitude of an fp16 weight is its bit pattern with the sign bit cleared,
+ * compared as an unsigned integer (so -0 == +0, and +-Inf ranks below every NaN);
+ * equal magnitudes go to the lower column. Writes `masks` and `values` as described
+ * above, copying the kept bits exactly. W: [rows][cols] fp16 bits; values:
+ * nm_values_count() elements; masks: nm_masks_count() words. Bit-exact and
+ * deterministic. */
+int nm_pack(const uint16_t* W, uint16_t* values, uint32_t* masks,
+            int64_t rows, int64_t cols, int N, int M, void* stream);
+
+/* Sparse product ([NEWS-NEW], [KERNEL]): y[r] = fp16( sum_c W'[r][c] * x[c] ), where W'
+ * is the matrix the packed (values, masks) describe. Products and sums are fp32; y is
+ * rounded once to fp16 (round to nearest even). The summation order is fixed, so the
+ * result is bit-identical from run to run. Masks must be as nm_pack writes them; a
+ * malformed mask gives an unspecified y but never an out-of-bounds access. */
+int nm_spmv(const uint16_t* values, const uint32_t* masks, const uint16_t* x, uint16_t* y,
+            int64_t rows, int64_t cols, int N, int M, void* stream);
+
+/* Dense baseline, the denominator of the pages' speedups ([KERNEL]):
+ * y[r] = fp16( sum_c W[r][c] * x[c] ) with fp32 products and sums, fixed order. */
+int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,
+                  int64_t rows, int64_t cols, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* nm_status_string(int status);
+
+/* The raw hipError_t behind the last NM_ERR_HIP returned on the calling thread. */
+int nm_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NM_SPARSE_H */

@@ -1,0 +1,214 @@
+"""Python binding of libnmsparse.so: batch-one N:M sparse matrix-vector product on MI355X.
+
+Argument marshalling only: every step runs in the HIP kernels of the library; torch
+provides device memory and the current stream. The names follow the C ABI in
+include/nm_sparse.h (nm_pack, nm_spmv, nm_gemv_dense, ...). There is no CPU
+fallback: if the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libnmsparse.so")
+
+PATTERNS = ((2, 4), (4, 8), (8, 16), (16, 32))
+
+NM_OK, NM_ERR_NULL, NM_ERR_SHAPE, NM_ERR_PATTERN, NM_ERR_ALIGN, NM_ERR_TOO_WIDE, NM_ERR_HIP = range(7)
+
+# Every symbol the public headers declare, with (restype, argtypes).
+_c = ctypes
+SIGNATURES = {
+    "nm_values_count": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int, _c.c_int]),
+    "nm_masks_count": (_c.c_size_t, [_c.c_int64, _c.c_int64]),
+    "nm_max_cols": (_c.c_int64, []),
+    "nm_pack": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
+                           _c.c_int, _c.c_int, _c.c_void_p]),
+    "nm_spmv": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
+                           _c.c_int64, _c.c_int, _c.c_int, _c.c_void_p]),
+    "nm_gemv_dense": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
+                                 _c.c_void_p]),
+    "nm_status_string": (_c.c_char_p, [_c.c_int]),
+    "nm_last_hip_error": (_c.c_int, []),
+    "nm_probe_read": (_c.c_int, [_c.c_void_p, _c.c_size_t, _c.c_void_p, _c.c_uint32, _c.c_void_p]),
+    "nm_probe_copy": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class NMError(RuntimeError):
+    """A libnmsparse call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int, hip_error: int | None = None):
+        msg = f"{fn}: {status_string(status)} (status {status})"
+        if hip_error is not None:
+            msg += f", hipError {hip_error}"
+        super().__init__(msg)
+        self.status = status
+        self.hip_error = hip_error
+
+
+class NMArgumentError(NMError, ValueError):
+    """Invalid arguments rejected before any HIP call."""
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library, with argtypes set. Raises if it is not built."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(
+                        f"{LIB_PATH} is not built: run `python -m semi_structured_sparse_amd.build`")
+                handle = ctypes.CDLL(LIB_PATH)
+                for name, (res, args) in SIGNATURES.items():
+                    fn = getattr(handle, name)
+                    fn.restype = res
+                    fn.argtypes = args
+                _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().nm_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status == NM_OK:
+        return
+    if status == NM_ERR_HIP:
+        raise NMError(fn, status, lib().nm_last_hip_error())
+    raise NMArgumentError(fn, status)
+
+
+def values_count(rows: int, cols: int, N: int, M: int) -> int:
+    return int(lib().nm_values_count(rows, cols, N, M))
+
+
+def masks_count(rows: int, cols: int) -> int:
+    return int(lib().nm_masks_count(rows, cols))
+
+
+def max_cols() -> int:
+    return int(lib().nm_max_cols())
+
+
+# --------------------------------------------------------------------------- torch layer
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _require(t, name, dtype, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device (no CPU path)")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def nm_pack(W, N: int, M: int):
+    """Encode fp16 W [rows, cols] -> (values fp16 [rows, cols*N/M], masks int32 [rows, cols/32]).
+
+    masks hold the uint32 mask words (viewed as int32; bit j of word w = column 32w+j).
+    """
+    torch = _torch()
+    _require(W, "W", torch.float16, 2)
+    rows, cols = W.shape
+    nv = values_count(rows, cols, N, M)
+    if nv == 0:
+        st = NM_ERR_PATTERN if (N, M) not in PATTERNS else NM_ERR_SHAPE
+        raise NMArgumentError("nm_pack", st)
+    values = torch.empty((rows, cols * N // M), dtype=torch.float16, device=W.device)
+    masks = torch.empty((rows, cols // 32), dtype=torch.int32, device=W.device)
+    with torch.cuda.device(W.device):
+        st = lib().nm_pack(W.data_ptr(), values.data_ptr(), masks.data_ptr(), rows, cols, N, M,
+                           _stream_ptr(W))
+    _check("nm_pack", st)
+    return values, masks
+
+
+def nm_spmv(values, masks, x, N: int, M: int, out=None):
+    """y = W' x for the packed (values, masks); fp16 y [rows]."""
+    torch = _torch()
+    _require(values, "values", torch.float16, 2)
+    _require(masks, "masks", torch.int32, 2)
+    _require(x, "x", torch.float16, 1)
+    rows, words = masks.shape
+    cols = words * 32
+    if x.shape[0] != cols:
+        raise ValueError(f"x has {x.shape[0]} elements, masks describe {cols} columns")
+    if (N, M) in PATTERNS and values.shape != (rows, cols * N // M):
+        raise ValueError(f"values shape {tuple(values.shape)} != {(rows, cols * N // M)}")
+    if not (values.device == masks.device == x.device):
+        raise ValueError("values, masks and x must be on one device")
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float16, device=x.device)
+    else:
+        _require(out, "out", torch.float16, 1)
+        if out.shape[0] != rows or out.device != x.device:
+            raise ValueError("out must be fp16 [rows] on the same device")
+    with torch.cuda.device(x.device):
+        st = lib().nm_spmv(values.data_ptr(), masks.data_ptr(), x.data_ptr(), out.data_ptr(),
+                           rows, cols, N, M, _stream_ptr(x))
+    _check("nm_spmv", st)
+    return out
+
+
+def nm_gemv_dense(W, x, out=None):
+    """Dense baseline y = W x; fp16 W [rows, cols], fp16 x [cols] -> fp16 y [rows]."""
+    torch = _torch()
+    _require(W, "W", torch.float16, 2)
+    _require(x, "x", torch.float16, 1)
+    rows, cols = W.shape
+    if x.shape[0] != cols:
+        raise ValueError(f"x has {x.shape[0]} elements, W has {cols} columns")
+    if W.device != x.device:
+        raise ValueError("W and x must be on one device")
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float16, device=x.device)
+    else:
+        _require(out, "out", torch.float16, 1)
+        if out.shape[0] != rows or out.device != x.device:
+            raise ValueError("out must be fp16 [rows] on the same device")
+    with torch.cuda.device(x.device):
+        st = lib().nm_gemv_dense(W.data_ptr(), x.data_ptr(), out.data_ptr(), rows, cols,
+                                 _stream_ptr(x))
+    _check("nm_gemv_dense", st)
+    return out
+
+
+def nm_probe_read(buf, sink, magic: int = 0x9E3779B9):
+    """Stream every byte of the contiguous device tensor `buf` (read-bandwidth probe)."""
+    torch = _torch()
+    nbytes = buf.numel() * buf.element_size()
+    with torch.cuda.device(buf.device):
+        st = lib().nm_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), magic, _stream_ptr(buf))
+    _check("nm_probe_read", st)
+
+
+def nm_probe_copy(dst, src):
+    """Copy the contiguous device tensor src into dst (known-traffic kernel)."""
+    torch = _torch()
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst too small")
+    with torch.cuda.device(src.device):
+        st = lib().nm_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream_ptr(src))
+    _check("nm_probe_copy", st)

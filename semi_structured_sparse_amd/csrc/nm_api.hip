@@ -1,0 +1,148 @@
+// C ABI of libnmsparse.so: argument validation (no HIP call before it passes),
+// status strings, the per-device attribute cache and the dispatch to the kernels.
+#include <mutex>
+
+#include "nm_internal.h"
+#include "nm_sparse.h"
+
+namespace nm {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mutex;
+DeviceInfo g_dev[kMaxDevices];
+thread_local int t_last_hip_error = 0;
+
+bool valid_pattern(int N, int M) {
+  return (N == 2 && M == 4) || (N == 4 && M == 8) || (N == 8 && M == 16) || (N == 16 && M == 32);
+}
+
+// rows >= 1, cols >= 32, cols % 32 == 0, and every size the kernels form fits:
+// grid = ceil(rows / 16) blocks, int row / column indices, and rows*cols*2 bytes.
+bool valid_shape(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 32 || (cols % 32) != 0) return false;
+  if (rows > (int64_t(1) << 31) - 64 || cols > (int64_t(1) << 30)) return false;
+  if (rows > (int64_t(1) << 62) / 2 / cols) return false;  // rows*cols*2 bytes must fit
+  return true;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int hip_fail(hipError_t e) {
+  set_last_hip_error(e);
+  return NM_ERR_HIP;
+}
+
+}  // namespace
+
+void set_last_hip_error(hipError_t e) { t_last_hip_error = int(e); }
+
+hipError_t current_device_info(DeviceInfo* out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  if (g_dev[dev].device != dev) {
+    DeviceInfo info;
+    info.device = dev;
+    e = hipDeviceGetAttribute(&info.cu_count, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&info.max_lds_per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return e;
+    g_dev[dev] = info;
+  }
+  *out = g_dev[dev];
+  return hipSuccess;
+}
+
+hipError_t launch(const void* kernel, dim3 grid, dim3 block, void** args, size_t lds,
+                  hipStream_t stream) {
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+  }
+  return hipLaunchKernel(kernel, grid, block, args, lds, stream);
+}
+
+}  // namespace nm
+
+extern "C" {
+
+size_t nm_values_count(int64_t rows, int64_t cols, int N, int M) {
+  if (!nm::valid_shape(rows, cols) || !nm::valid_pattern(N, M)) return 0;
+  return size_t(rows) * size_t(cols) / size_t(M) * size_t(N);
+}
+
+size_t nm_masks_count(int64_t rows, int64_t cols) {
+  if (!nm::valid_shape(rows, cols)) return 0;
+  return size_t(rows) * size_t(cols / 32);
+}
+
+int64_t nm_max_cols(void) {
+  nm::DeviceInfo dev;
+  hipError_t e = nm::current_device_info(&dev);
+  if (e != hipSuccess) {
+    nm::set_last_hip_error(e);
+    return 0;
+  }
+  return nm::max_cols_for(dev);
+}
+
+int nm_pack(const uint16_t* W, uint16_t* values, uint32_t* masks, int64_t rows, int64_t cols,
+            int N, int M, void* stream) {
+  if (!W || !values || !masks) return NM_ERR_NULL;
+  if (!nm::valid_shape(rows, cols)) return NM_ERR_SHAPE;
+  if (!nm::valid_pattern(N, M)) return NM_ERR_PATTERN;
+  if (!nm::aligned(W, 16) || !nm::aligned(values, 16) || !nm::aligned(masks, 4)) return NM_ERR_ALIGN;
+  nm::DeviceInfo dev;
+  hipError_t e = nm::current_device_info(&dev);
+  if (e != hipSuccess) return nm::hip_fail(e);
+  e = nm::launch_pack(W, values, masks, rows, cols, N, M, static_cast<hipStream_t>(stream), dev);
+  return e == hipSuccess ? NM_OK : nm::hip_fail(e);
+}
+
+int nm_spmv(const uint16_t* values, const uint32_t* masks, const uint16_t* x, uint16_t* y,
+            int64_t rows, int64_t cols, int N, int M, void* stream) {
+  if (!values || !masks || !x || !y) return NM_ERR_NULL;
+  if (!nm::valid_shape(rows, cols)) return NM_ERR_SHAPE;
+  if (!nm::valid_pattern(N, M)) return NM_ERR_PATTERN;
+  if (!nm::aligned(values, 16) || !nm::aligned(masks, 4) || !nm::aligned(x, 16) || !nm::aligned(y, 2))
+    return NM_ERR_ALIGN;
+  nm::DeviceInfo dev;
+  hipError_t e = nm::current_device_info(&dev);
+  if (e != hipSuccess) return nm::hip_fail(e);
+  if (cols > nm::max_cols_for(dev)) return NM_ERR_TOO_WIDE;
+  e = nm::launch_spmv(values, masks, x, y, rows, cols, N, M, static_cast<hipStream_t>(stream), dev);
+  return e == hipSuccess ? NM_OK : nm::hip_fail(e);
+}
+
+int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y, int64_t rows, int64_t cols,
+                  void* stream) {
+  if (!W || !x || !y) return NM_ERR_NULL;
+  if (!nm::valid_shape(rows, cols)) return NM_ERR_SHAPE;
+  if (!nm::aligned(W, 16) || !nm::aligned(x, 16) || !nm::aligned(y, 2)) return NM_ERR_ALIGN;
+  nm::DeviceInfo dev;
+  hipError_t e = nm::current_device_info(&dev);
+  if (e != hipSuccess) return nm::hip_fail(e);
+  if (cols > nm::max_cols_for(dev)) return NM_ERR_TOO_WIDE;
+  e = nm::launch_gemv(W, x, y, rows, cols, static_cast<hipStream_t>(stream), dev);
+  return e == hipSuccess ? NM_OK : nm::hip_fail(e);
+}
+
+const char* nm_status_string(int status) {
+  switch (status) {
+    case NM_OK: return "ok";
+    case NM_ERR_NULL: return "a required pointer is NULL";
+    case NM_ERR_SHAPE: return "invalid shape: need rows >= 1, cols >= 32 and cols % 32 == 0 (and sizes that fit)";
+    case NM_ERR_PATTERN: return "unsupported N:M pattern: need 2:4, 4:8, 8:16 or 16:32";
+    case NM_ERR_ALIGN: return "misaligned pointer: W, values and x need 16 bytes, masks 4, y 2";
+    case NM_ERR_TOO_WIDE: return "cols too large: x does not fit in the LDS of one workgroup";
+    case NM_ERR_HIP: return "a HIP runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+int nm_last_hip_error(void) { return nm::t_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Internal declarations shared by the translation units of libnmsparse.so.
+// Not part of the public ABI (include/nm_sparse.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nm {
+
+// Attributes of one HIP device, read once per device and cached.
+struct DeviceInfo {
+  int device = -1;
+  int cu_count = 0;
+  int max_lds_per_block = 0;  // bytes one workgroup may allocate
+};
+
+// Attributes of the current device; returns hipSuccess or the failing call's error.
+hipError_t current_device_info(DeviceInfo* out);
+
+// Records the raw HIP error for nm_last_hip_error() on this thread.
+void set_last_hip_error(hipError_t e);
+
+// Launches a kernel through hipLaunchKernel (which reports launch errors directly,
+// without touching the thread's sticky last-error state), raising the kernel's
+// dynamic-LDS limit first when it needs more than the 64 KiB default.
+hipError_t launch(const void* kernel, dim3 grid, dim3 block, void** args, size_t lds,
+                  hipStream_t stream);
+
+// Rows of y one workgroup of the SpMV / GEMV kernels produces (16 rows x 4 lanes = 64 lanes).
+constexpr int kRowsPerBlock = 16;
+
+// LDS bytes the row-reduction scratch of the SpMV / GEMV kernels needs.
+constexpr size_t reduction_lds_bytes(int waves) { return size_t(waves) * kRowsPerBlock * sizeof(float); }
+
+// Kernel launchers (arguments already validated by the API layer).
+hipError_t launch_pack(const uint16_t* W, uint16_t* values, uint32_t* masks, int64_t rows,
+                       int64_t cols, int N, int M, hipStream_t stream, const DeviceInfo& dev);
+hipError_t launch_spmv(const uint16_t* values, const uint32_t* masks, const uint16_t* x,
+                       uint16_t* y, int64_t rows, int64_t cols, int N, int M, hipStream_t stream,
+                       const DeviceInfo& dev);
+hipError_t launch_gemv(const uint16_t* W, const uint16_t* x, uint16_t* y, int64_t rows,
+                       int64_t cols, hipStream_t stream, const DeviceInfo& dev);
+
+// Widest x the SpMV / GEMV kernels can stage for the given device.
+int64_t max_cols_for(const DeviceInfo& dev);
+
+}  // namespace nm

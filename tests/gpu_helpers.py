@@ -1,0 +1,79 @@
+"""Helpers shared by the GPU tests: device transfer, sampled-row parity checks."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import semi_structured_sparse_amd as nm
+
+
+def device():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    return torch.device("cuda:0")
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def up_f16(a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.float16)).to(device())
+
+
+def up_u32(a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint32).view(np.int32)).to(device())
+
+
+def down_bits16(t) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def down_u32(t) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint32)
+
+
+def down_f16(t) -> np.ndarray:
+    return t.cpu().numpy().view(np.float16)
+
+
+def sample_rows(rows: int, k: int = 48, seed: int = 0) -> np.ndarray:
+    """First, last, a row at each 16-row tile edge, and k random rows (sorted, unique)."""
+    rng = np.random.default_rng(seed)
+    pick = {0, rows - 1, min(rows - 1, 15), min(rows - 1, 16), rows // 2}
+    pick |= set(rng.integers(0, rows, size=min(k, rows)).tolist())
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+def check_full_layer(W_host: np.ndarray, x_host: np.ndarray, N: int, M: int, tag: str,
+                     check_dense: bool = True) -> dict:
+    """Pack on the GPU, run the sparse (and dense) product, and compare sampled rows with
+    the oracle: pack bit-exact, y within tolerance. Returns the parity figures."""
+    rows, cols = W_host.shape
+    Wd = up_f16(W_host)
+    xd = up_f16(x_host)
+    values, masks = nm.nm_pack(Wd, N, M)
+    y = nm.nm_spmv(values, masks, xd, N, M)
+    yd = nm.nm_gemv_dense(Wd, xd) if check_dense else None
+    torch.cuda.synchronize()
+    idx = sample_rows(rows)
+    it = torch.from_numpy(idx).to(device())
+    gv = down_bits16(values.index_select(0, it))
+    gm = down_u32(masks.index_select(0, it))
+    rv, rm = oracle.pack_ref(W_host[idx], N, M)
+    assert np.array_equal(gm, rm), f"{tag}: masks differ from the oracle"
+    assert np.array_equal(gv, rv), f"{tag}: values differ from the oracle"
+    ref = oracle.spmv_ref(rv, rm, x_host, cols, N, M)
+    rep = oracle.y_tolerance_report(down_f16(y)[idx], ref)
+    assert rep["ok"], f"{tag}: spmv {rep}"
+    out = {"spmv": rep}
+    if check_dense:
+        dref = oracle.gemv_ref(W_host[idx], x_host)
+        drep = oracle.y_tolerance_report(down_f16(yd)[idx], dref)
+        assert drep["ok"], f"{tag}: dense {drep}"
+        out["dense"] = drep
+    del Wd, values, masks, y, yd
+    return out

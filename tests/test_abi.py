@@ -1,0 +1,134 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every symbol the public
+headers declare, and rejects bad arguments before any HIP call (so no GPU is needed)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import semi_structured_sparse_amd as nm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A16 = 0x10000  # a 16-byte-aligned fake device address: validation never dereferences it
+
+
+def declared_functions():
+    names = []
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(nm_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_builds_and_loads():
+    assert os.path.exists(nm.LIB_PATH), "build libnmsparse.so first"
+    assert nm.lib() is not None
+
+
+def test_every_declared_symbol_is_exported():
+    decl = declared_functions()
+    assert {"nm_pack", "nm_spmv", "nm_gemv_dense", "nm_values_count", "nm_masks_count",
+            "nm_max_cols", "nm_status_string", "nm_last_hip_error", "nm_probe_read",
+            "nm_probe_copy"} <= set(decl)
+    handle = ctypes.CDLL(nm.LIB_PATH)
+    for name in decl:
+        assert hasattr(handle, name), name
+    assert set(decl) == set(nm.SIGNATURES), "binding and headers disagree"
+
+
+def test_status_strings():
+    for s in range(7):
+        assert nm.status_string(s)
+    assert nm.status_string(99) == "unknown status"
+    assert nm.status_string(0) == "ok"
+
+
+@pytest.mark.parametrize("rows,cols,N,M,want", [
+    (4096, 4096, 2, 4, 4096 * 2048), (1, 32, 16, 32, 16), (3, 96, 4, 8, 144),
+    (0, 32, 2, 4, 0), (1, 0, 2, 4, 0), (1, 48, 2, 4, 0), (1, 32, 3, 4, 0), (1, 32, 1, 4, 0),
+    (-1, 32, 2, 4, 0), (1, 16, 8, 16, 0),
+])
+def test_values_count(rows, cols, N, M, want):
+    assert nm.values_count(rows, cols, N, M) == want
+
+
+def test_masks_count():
+    assert nm.masks_count(7, 96) == 21
+    assert nm.masks_count(7, 100) == 0
+    assert nm.masks_count(1 << 40, 1 << 30) == 0  # overflow
+
+
+def _spmv(**kw):
+    a = dict(values=A16, masks=A16, x=A16, y=A16, rows=16, cols=64, N=2, M=4, stream=None)
+    a.update(kw)
+    return nm.lib().nm_spmv(a["values"], a["masks"], a["x"], a["y"], a["rows"], a["cols"],
+                            a["N"], a["M"], a["stream"])
+
+
+def _pack(**kw):
+    a = dict(W=A16, values=A16, masks=A16, rows=16, cols=64, N=2, M=4, stream=None)
+    a.update(kw)
+    return nm.lib().nm_pack(a["W"], a["values"], a["masks"], a["rows"], a["cols"], a["N"],
+                            a["M"], a["stream"])
+
+
+def _gemv(**kw):
+    a = dict(W=A16, x=A16, y=A16, rows=16, cols=64, stream=None)
+    a.update(kw)
+    return nm.lib().nm_gemv_dense(a["W"], a["x"], a["y"], a["rows"], a["cols"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(values=None), nm.NM_ERR_NULL), (dict(masks=None), nm.NM_ERR_NULL),
+    (dict(x=None), nm.NM_ERR_NULL), (dict(y=None), nm.NM_ERR_NULL),
+    (dict(rows=0), nm.NM_ERR_SHAPE), (dict(rows=-5), nm.NM_ERR_SHAPE),
+    (dict(cols=0), nm.NM_ERR_SHAPE), (dict(cols=16), nm.NM_ERR_SHAPE), (dict(cols=80), nm.NM_ERR_SHAPE),
+    (dict(rows=1 << 40), nm.NM_ERR_SHAPE),
+    (dict(N=3, M=4), nm.NM_ERR_PATTERN), (dict(N=2, M=8), nm.NM_ERR_PATTERN),
+    (dict(N=1, M=4), nm.NM_ERR_PATTERN), (dict(N=32, M=64), nm.NM_ERR_PATTERN),
+    (dict(values=A16 + 8), nm.NM_ERR_ALIGN), (dict(masks=A16 + 2), nm.NM_ERR_ALIGN),
+    (dict(x=A16 + 4), nm.NM_ERR_ALIGN), (dict(y=A16 + 1), nm.NM_ERR_ALIGN),
+])
+def test_spmv_validation(kw, want):
+    assert _spmv(**kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(W=None), nm.NM_ERR_NULL), (dict(values=None), nm.NM_ERR_NULL), (dict(masks=None), nm.NM_ERR_NULL),
+    (dict(rows=0), nm.NM_ERR_SHAPE), (dict(cols=33), nm.NM_ERR_SHAPE),
+    (dict(N=4, M=4), nm.NM_ERR_PATTERN),
+    (dict(W=A16 + 2), nm.NM_ERR_ALIGN), (dict(values=A16 + 4), nm.NM_ERR_ALIGN),
+    (dict(masks=A16 + 1), nm.NM_ERR_ALIGN),
+])
+def test_pack_validation(kw, want):
+    assert _pack(**kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(W=None), nm.NM_ERR_NULL), (dict(x=None), nm.NM_ERR_NULL), (dict(y=None), nm.NM_ERR_NULL),
+    (dict(rows=0), nm.NM_ERR_SHAPE), (dict(cols=31), nm.NM_ERR_SHAPE),
+    (dict(W=A16 + 8), nm.NM_ERR_ALIGN), (dict(x=A16 + 2), nm.NM_ERR_ALIGN), (dict(y=A16 + 1), nm.NM_ERR_ALIGN),
+])
+def test_gemv_validation(kw, want):
+    assert _gemv(**kw) == want
+
+
+def test_probe_validation():
+    L = nm.lib()
+    assert L.nm_probe_read(None, 16, A16, 0, None) == nm.NM_ERR_NULL
+    assert L.nm_probe_read(A16, 0, A16, 0, None) == nm.NM_ERR_SHAPE
+    assert L.nm_probe_read(A16, 24, A16, 0, None) == nm.NM_ERR_SHAPE
+    assert L.nm_probe_read(A16 + 8, 16, A16, 0, None) == nm.NM_ERR_ALIGN
+    assert L.nm_probe_copy(A16, None, 16, None) == nm.NM_ERR_NULL
+    assert L.nm_probe_copy(A16 + 4, A16, 16, None) == nm.NM_ERR_ALIGN
+
+
+def test_python_layer_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    W = torch.zeros(16, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        nm.nm_pack(W, 2, 4)
+    with pytest.raises(ValueError):
+        nm.nm_gemv_dense(W, torch.zeros(64, dtype=torch.float16))
