@@ -31,9 +31,9 @@ if ROOT not in sys.path:
 
 METRIC = "N:M SpMV effective HBM GB/s (% of peak) + speedup vs dense GEMV, batch 1"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak, 8 TB/s
-SPMV_SRC = os.path.join(ROOT, "semi_structured_sparse_amd", "csrc", "nm_spmv.hip")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "nm_spmv_counters.txt")
 WORKLOAD_BY_NAME = {"llama8b": 2, "qwen3": 3, "llama70b": 4}
+COPY_CAL_BYTES = 256 << 20  # size of the counter-calibration copy
 
 
 def log(msg: str) -> None:
@@ -48,7 +48,7 @@ def parse_args():
     ap.add_argument("--workload", choices=sorted(WORKLOAD_BY_NAME), default="llama8b")
     ap.add_argument("--pool-gib", type=float, default=1.0,
                     help="minimum bytes read between two reads of the same copy")
-    ap.add_argument("--cpu-rows-frac", type=float, default=0.125,
+    ap.add_argument("--cpu-rows-frac", type=float, default=0.5,
                     help="fraction of each layer's rows the CPU oracle baseline processes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--patterns", default="", help="restrict to patterns, e.g. 2:4,16:32")
@@ -63,27 +63,36 @@ def alg_bytes_dense(R, C):
     return 2 * R * C + 2 * C + 2 * R
 
 
-def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+KERNEL_SOURCES = [os.path.join(ROOT, "semi_structured_sparse_amd", "csrc", f)
+                  for f in ("nm_spmv_impl.h", "nm_spmv.hip", "nm_internal.h")]
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def read_traffic(kernel_name: str):
-    """HBM bytes per launch of `kernel_name` from the committed counter summary, or None
-    when there is none or the kernel source changed since the counters were taken."""
+    """HBM bytes per launch of `kernel_name` (averaged over the shapes it serves in one
+    step) from the committed counter summary, or None when there is none or the kernel
+    sources changed since the counters were taken."""
     if not os.path.exists(COUNTERS_FILE):
         return None
-    kv = {}
+    sha, traffic = None, {}
     with open(COUNTERS_FILE) as f:
         for line in f:
-            if ":" in line and not line.lstrip().startswith("#"):
-                k, v = line.split(":", 1)
-                kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != source_sha(SPMV_SRC):
+            line = line.strip()
+            if line.startswith("kernel_source_sha256:"):
+                sha = line.split(":", 1)[1].strip()
+            elif line.startswith("traffic "):
+                name, val = line[len("traffic "):].rsplit(":", 1)
+                traffic[name.strip()] = float(val)
+    if sha != kernel_source_sha():
         return None
-    if kv.get("kernel") != kernel_name or "traffic_bytes_per_launch" not in kv:
-        return None
-    return float(kv["traffic_bytes_per_launch"])
+    return traffic.get(kernel_name)
 
 
 def cpu_info():
@@ -181,27 +190,19 @@ def main():
     dn_args = [[(D["W"][c].data_ptr(), D["x"].data_ptr(), D["y"].data_ptr(), D["R"], D["C"])
                 for c in range(P_d)] for D in dense_list]
 
-    def sparse_step(k, sp, evs=None):
+    def sparse_step(k, sp):
         c = k % P_s
         for i in range(len(layers)):
-            if evs is not None:
-                evs[i][0].record()
             st = lib.nm_spmv(*sp_args[i][c], sp)
             if st:
                 raise RuntimeError(f"nm_spmv: {nm.status_string(st)}")
-            if evs is not None:
-                evs[i][1].record()
 
-    def dense_step(k, sp, evs=None):
+    def dense_step(k, sp):
         c = k % P_d
         for i in range(len(dense_list)):
-            if evs is not None:
-                evs[i][0].record()
             st = lib.nm_gemv_dense(*dn_args[i][c], sp)
             if st:
                 raise RuntimeError(f"nm_gemv_dense: {nm.status_string(st)}")
-            if evs is not None:
-                evs[i][1].record()
 
     # ------------------------------------------------------------------ read ceiling probe
     probe_buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
@@ -220,13 +221,10 @@ def main():
     probe_ms = statistics.median(pt)
     read_ceiling = probe_buf.numel() / (probe_ms * 1e-3) / 1e9
     log(f"read ceiling {read_ceiling:.0f} GB/s")
-
-    def head_start(ms):
-        """Queue about `ms` of untimed GPU work so that the launches that follow are all
-        enqueued before the GPU reaches them: their timing is then the GPU's, never the
-        host's launch overhead."""
-        for _ in range(max(1, int(math.ceil(ms / probe_ms)))):
-            nm.nm_probe_read(probe_buf, sink)
+    # one plain copy of known size: under a counter profile its FETCH_SIZE / WRITE_SIZE
+    # calibrate the counters against real bytes
+    nm.nm_probe_copy(probe_buf[COPY_CAL_BYTES:2 * COPY_CAL_BYTES], probe_buf[:COPY_CAL_BYTES])
+    torch.cuda.synchronize()
 
     def timed_graph(step_fn, K, W_):
         """Warm-up, then K steps captured in one HIP graph and replayed between events."""
@@ -253,37 +251,62 @@ def main():
         del g
         return start.elapsed_time(end), wall
 
-    def timed_events(step_fn, K, n_launch, per_launch):
-        """K eager steps after a GPU head start; with per_launch, an event pair around
-        every launch (launch durations as the GPU sees them)."""
-        sp = main_stream.cuda_stream
-        evs = None
-        if per_launch:
-            evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-                    for _ in range(n_launch)] for _ in range(K)]
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
+    def per_launch_us(launch_copy, n_copies, launches, reps=5):
+        """Median per-launch time of one layer: `launches` launches cycling over its
+        rotating pool, captured in a graph and replayed `reps` times between events."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream().cuda_stream
+            for k in range(launches):
+                launch_copy(k % n_copies, cs)
+        g.replay()
         torch.cuda.synchronize()
-        head_start(25.0)
-        start.record()
-        for k in range(K):
-            step_fn(k, sp, evs[k] if per_launch else None)
-        end.record()
-        torch.cuda.synchronize()
-        per = None
-        if per_launch:
-            per = [[evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(K)] for i in range(n_launch)]
-        return start.elapsed_time(end), per
+        ts = []
+        for _ in range(reps):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            g.replay()
+            b_.record()
+            torch.cuda.synchronize()
+            ts.append(a_.elapsed_time(b_) * 1e3 / launches)
+        del g
+        return statistics.median(ts)
+
+    def pool_copies(nbytes):
+        return max(2, math.ceil(pool_bytes / nbytes))
+
+    def layer_pool(tensors, nbytes):
+        """Copies of a layer's tensors so that >= pool_bytes of distinct data rotate."""
+        return [tensors] + [[t.clone() for t in tensors] for _ in range(pool_copies(nbytes) - 1)]
+
+    # Every layer gets the same number of per-layer launches (enough to cycle through the
+    # largest pool), so that each shape weighs the same in a kernel's average duration as
+    # it does in a step, in these timings and in a profiler's per-kernel statistics.
+    L_PL = max(40, max(pool_copies(L["bytes"]) for L in layers),
+               max(pool_copies(D["bytes"]) for D in dense.values()))
 
     # ------------------------------------------------------------------ timed regions
     K, Wm = args.steps, args.warmup
     ms_s, wall_s = timed_graph(sparse_step, K, Wm)
     ms_d, wall_d = timed_graph(dense_step, K, Wm)
-    ms_s_eager, _ = timed_events(sparse_step, K, len(layers), False)
-    ms_s_ev, per_s = timed_events(sparse_step, K, len(layers), True)
-    ms_d_ev, per_d = timed_events(dense_step, K, len(dense_list), True)
-    torch.cuda.synchronize()
     del probe_buf
+
+    # per-layer durations (each layer alone, its own >= pool_bytes rotation)
+    per_s = []
+    for i, L in enumerate(layers):
+        pool = layer_pool([L["values"][0], L["masks"][0]], L["bytes"])
+        argsets = [(p[0].data_ptr(), p[1].data_ptr(), L["x"].data_ptr(), L["y"].data_ptr(),
+                    L["R"], L["C"], L["N"], L["M"]) for p in pool]
+        per_s.append(per_launch_us(lambda c, sp, A=argsets: lib.nm_spmv(*A[c], sp), len(pool), L_PL))
+        del pool
+    per_d = {}
+    for D in dense_list:
+        pool = layer_pool([D["W"][0]], D["bytes"])
+        argsets = [(p[0].data_ptr(), D["x"].data_ptr(), D["y"].data_ptr(), D["R"], D["C"]) for p in pool]
+        per_d[(D["R"], D["C"])] = per_launch_us(lambda c, sp, A=argsets: lib.nm_gemv_dense(*A[c], sp),
+                                                len(pool), L_PL)
+        del pool
+    torch.cuda.synchronize()
 
     value = step_sparse * K / (ms_s * 1e-3) / 1e9
     dense_gbps = step_dense * K / (ms_d * 1e-3) / 1e9
@@ -292,34 +315,30 @@ def main():
     pats_per_shape = len(layers) / len(dense_list)
     speedup = (ms_d * pats_per_shape) / ms_s
     log(f"sparse {value:.0f} GB/s ({value / HBM_PEAK_GBPS:.1%}), dense {dense_gbps:.0f} GB/s, "
-        f"speedup {speedup:.3f}x, {ms_s / K * 1e3:.1f} us/step (graph); eager {ms_s_eager / K * 1e3:.1f}, "
-        f"with launch events {ms_s_ev / K * 1e3:.1f} us/step")
+        f"speedup {speedup:.3f}x, {ms_s / K * 1e3:.1f} us/step")
 
     per_layer = []
-    dense_med = {}
-    for i, D in enumerate(dense_list):
-        dense_med[(D["R"], D["C"])] = statistics.median(per_d[i])
-    kern_bytes, kern_ms = {}, {}
+    kern_bytes, kern_us, kern_n = {}, {}, {}
     for i, L in enumerate(layers):
-        med = statistics.median(per_s[i])
-        mean = statistics.fmean(per_s[i])
-        kname = f"nm_spmv_kernel<{L['N']},{L['M']}>"
-        kern_bytes[kname] = kern_bytes.get(kname, 0) + L["bytes"] * K
-        kern_ms[kname] = kern_ms.get(kname, 0.0) + mean * K
-        dm = dense_med[(L["R"], L["C"])]
+        us = per_s[i]
+        kname = nm.spmv_variant(L["R"], L["C"], L["N"], L["M"])
+        kern_bytes[kname] = kern_bytes.get(kname, 0) + L["bytes"]
+        kern_us[kname] = kern_us.get(kname, 0.0) + us
+        kern_n[kname] = kern_n.get(kname, 0) + 1
+        dus = per_d[(L["R"], L["C"])]
+        gbps = L["bytes"] / (us * 1e-6) / 1e9
         per_layer.append({"layer": L["name"], "shape": f"{L['R']}x{L['C']}", "pattern": f"{L['N']}:{L['M']}",
-                          "us": round(med * 1e3, 2), "GBps": round(L["bytes"] / (med * 1e-3) / 1e9, 1),
-                          "pct_peak": round(L["bytes"] / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                          "dense_us": round(dm * 1e3, 2), "speedup": round(dm / med, 3)})
-    dominant = max(kern_ms, key=lambda k: kern_ms[k])
-    achieved = kern_bytes[dominant] / (kern_ms[dominant] * 1e-3) / 1e9
-    n_launch_dom = sum(1 for L in layers if f"nm_spmv_kernel<{L['N']},{L['M']}>" == dominant)
+                          "kernel": kname, "us": round(us, 2), "GBps": round(gbps, 1),
+                          "pct_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                          "dense_us": round(dus, 2), "speedup": round(dus / us, 3)})
+    dominant = max(kern_us, key=lambda k: kern_us[k])
+    achieved = kern_bytes[dominant] / (kern_us[dominant] * 1e-6) / 1e9
     traffic = read_traffic(dominant)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": dominant,
-                "bytes_per_launch": kern_bytes[dominant] / (K * n_launch_dom),
-                "avg_launch_us": round(kern_ms[dominant] / (K * n_launch_dom) * 1e3, 3)}
+                "kernel": dominant, "launches_per_step": kern_n[dominant],
+                "bytes_per_launch": kern_bytes[dominant] / kern_n[dominant],
+                "avg_launch_us": round(kern_us[dominant] / kern_n[dominant], 3)}
 
     # ------------------------------------------------------------------ CPU oracle baseline
     cpu = None
@@ -356,10 +375,9 @@ def main():
         "dense_ms_per_step": round(ms_d / K, 5),
         "read_ceiling_GBps": round(read_ceiling, 1),
         "wall_s_sparse": round(wall_s, 4),
-        "timing": "value: K steps in one HIP graph replay between events; per_layer: median of "
-                  "event pairs around each eager launch",
-        "ms_per_step_eager": round(ms_s_eager / K, 5),
-        "ms_per_step_with_launch_events": round(ms_s_ev / K, 5),
+        "timing": "value: K steps in one HIP graph replayed between events; per_layer: each layer "
+                  "alone, the same number of launches for every layer cycling over its own >= 1 GiB "
+                  "rotation, in a graph, median of 5 replays",
         "per_layer": per_layer,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -94,6 +94,12 @@ int nm_spmv(const uint16_t* values, const uint32_t* masks, const uint16_t* x, ui
 int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,
                   int64_t rows, int64_t cols, void* stream);
 
+/* Introspection: the name of the kernel configuration nm_spmv launches for this shape
+ * and pattern on the current device, as it appears in profiler traces (for example
+ * "spmv_line_kernel<2, 2, 8, 4, true, 1>"); "" if the arguments are invalid. Static
+ * string, never NULL. Used by the benchmark to attribute measured durations. */
+const char* nm_spmv_variant(int64_t rows, int64_t cols, int N, int M);
+
 /* Static description of a status code; never NULL. */
 const char* nm_status_string(int status);
 

@@ -31,6 +31,7 @@ SIGNATURES = {
     "nm_gemv_dense": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
                                  _c.c_void_p]),
     "nm_status_string": (_c.c_char_p, [_c.c_int]),
+    "nm_spmv_variant": (_c.c_char_p, [_c.c_int64, _c.c_int64, _c.c_int, _c.c_int]),
     "nm_last_hip_error": (_c.c_int, []),
     "nm_probe_read": (_c.c_int, [_c.c_void_p, _c.c_size_t, _c.c_void_p, _c.c_uint32, _c.c_void_p]),
     "nm_probe_copy": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
@@ -96,6 +97,11 @@ def masks_count(rows: int, cols: int) -> int:
 
 def max_cols() -> int:
     return int(lib().nm_max_cols())
+
+
+def spmv_variant(rows: int, cols: int, N: int, M: int) -> str:
+    """Kernel configuration nm_spmv launches for this shape on the current device."""
+    return lib().nm_spmv_variant(rows, cols, N, M).decode()
 
 
 # --------------------------------------------------------------------------- torch layer

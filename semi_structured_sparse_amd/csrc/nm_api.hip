@@ -1,6 +1,8 @@
 // C ABI of libnmsparse.so: argument validation (no HIP call before it passes),
 // status strings, the per-device attribute cache and the dispatch to the kernels.
 #include <mutex>
+#include <set>
+#include <utility>
 
 #include "nm_internal.h"
 #include "nm_sparse.h"
@@ -12,6 +14,7 @@ constexpr int kMaxDevices = 64;
 std::mutex g_dev_mutex;
 DeviceInfo g_dev[kMaxDevices];
 thread_local int t_last_hip_error = 0;
+std::set<std::pair<const void*, int>> g_lds_raised;  // guarded by g_dev_mutex
 
 bool valid_pattern(int N, int M) {
   return (N == 2 && M == 4) || (N == 4 && M == 8) || (N == 8 && M == 16) || (N == 16 && M == 32);
@@ -57,10 +60,17 @@ hipError_t current_device_info(DeviceInfo* out) {
 }
 
 hipError_t launch(const void* kernel, dim3 grid, dim3 block, void** args, size_t lds,
-                  hipStream_t stream) {
+                  hipStream_t stream, const DeviceInfo& dev) {
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return e;
+    if (lds > size_t(dev.max_lds_per_block)) return hipErrorInvalidValue;
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    const std::pair<const void*, int> key(kernel, dev.device);
+    if (g_lds_raised.find(key) == g_lds_raised.end()) {
+      hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         dev.max_lds_per_block);
+      if (e != hipSuccess) return e;
+      g_lds_raised.insert(key);
+    }
   }
   return hipLaunchKernel(kernel, grid, block, args, lds, stream);
 }
@@ -128,6 +138,13 @@ int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y, int64_t row
   if (cols > nm::max_cols_for(dev)) return NM_ERR_TOO_WIDE;
   e = nm::launch_gemv(W, x, y, rows, cols, static_cast<hipStream_t>(stream), dev);
   return e == hipSuccess ? NM_OK : nm::hip_fail(e);
+}
+
+const char* nm_spmv_variant(int64_t rows, int64_t cols, int N, int M) {
+  if (!nm::valid_shape(rows, cols) || !nm::valid_pattern(N, M)) return "";
+  nm::DeviceInfo dev;
+  if (nm::current_device_info(&dev) != hipSuccess) return "";
+  return nm::spmv_variant(rows, cols, N, dev);
 }
 
 const char* nm_status_string(int status) {

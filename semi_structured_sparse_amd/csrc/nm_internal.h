@@ -22,10 +22,11 @@ hipError_t current_device_info(DeviceInfo* out);
 void set_last_hip_error(hipError_t e);
 
 // Launches a kernel through hipLaunchKernel (which reports launch errors directly,
-// without touching the thread's sticky last-error state), raising the kernel's
-// dynamic-LDS limit first when it needs more than the 64 KiB default.
+// without touching the thread's sticky last-error state). A kernel that needs more than
+// the 64 KiB default of dynamic LDS gets its limit raised to the device maximum once
+// per (kernel, device).
 hipError_t launch(const void* kernel, dim3 grid, dim3 block, void** args, size_t lds,
-                  hipStream_t stream);
+                  hipStream_t stream, const DeviceInfo& dev);
 
 // Rows of y one workgroup of the SpMV / GEMV kernels produces (16 rows x 4 lanes = 64 lanes).
 constexpr int kRowsPerBlock = 16;
@@ -41,6 +42,9 @@ hipError_t launch_spmv(const uint16_t* values, const uint32_t* masks, const uint
                        const DeviceInfo& dev);
 hipError_t launch_gemv(const uint16_t* W, const uint16_t* x, uint16_t* y, int64_t rows,
                        int64_t cols, hipStream_t stream, const DeviceInfo& dev);
+
+// Name of the kernel configuration launch_spmv picks (static string).
+const char* spmv_variant(int64_t rows, int64_t cols, int N, const DeviceInfo& dev);
 
 // Widest x the SpMV / GEMV kernels can stage for the given device.
 int64_t max_cols_for(const DeviceInfo& dev);

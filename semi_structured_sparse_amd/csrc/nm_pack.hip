@@ -88,7 +88,7 @@ hipError_t launch_pack_t(const uint16_t* W, uint16_t* values, uint32_t* masks, i
   const int64_t cap = int64_t(dev.cu_count > 0 ? dev.cu_count : 256) * 32;
   if (blocks > cap) blocks = cap;
   return launch(reinterpret_cast<const void*>(&nm_pack_kernel<N, M>), dim3(unsigned(blocks)),
-                dim3(kPackThreads), args, 0, stream);
+                dim3(kPackThreads), args, 0, stream, dev);
 }
 
 }  // namespace

@@ -17,9 +17,12 @@ from tests.gpu_helpers import (check_full_layer, device, down_bits16, down_f16, 
 pytestmark = pytest.mark.gpu
 PATTERNS = synth.PATTERNS
 
-# small shapes the oracle finishes fast: one word, odd word counts (ragged last step),
-# row counts that are not multiples of the 16-row tile, several tiles
-SMALL = [(1, 32), (3, 64), (17, 96), (37, 544), (16, 4096), (100, 2080), (256, 512), (33, 1056)]
+# small shapes the oracle finishes fast: 1, 2 and 3 mask words (a ragged last step of
+# 128 columns), word counts of 4k+1, 4k+2 and 4k+3 after full steps, row counts that are
+# not multiples of the row tiles, several tiles, and both workgroup shapes (more and
+# fewer than 2048 rows)
+SMALL = [(1, 32), (3, 64), (17, 96), (5, 160), (9, 192), (7, 224), (37, 544), (16, 4096),
+         (100, 2080), (256, 512), (33, 1056), (2100, 96), (2064, 160)]
 
 
 def test_native_library_is_the_in_tree_build():
