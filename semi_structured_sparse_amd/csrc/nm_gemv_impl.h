@@ -3,13 +3,14 @@
 // SparseDecoding article, "The Kernel Is the Other Half of the Answer", quotes every
 // speedup against the dense product).
 //
-// It is tuned the same way as the sparse kernel so that the ratio is fair: one
-// workgroup = 16 rows x all columns with WAVES waves splitting the columns; per step
-// each row's 64 bytes (32 columns) are loaded by 4 lanes as dwordx4 (nontemporal with
-// NT), BATCH steps in flight; x is staged once in LDS and read back as 16-byte vectors
-// (4 distinct addresses per wave instruction, broadcast); fp16 pairs are multiplied
-// and summed in fp32 by v_dot2_f32_f16; rows are reduced with DPP inside the quad and
-// in LDS across waves, in a fixed order, and rounded once to fp16.
+// It is built and tuned the same way as the sparse kernel so that the ratio is fair:
+// a workgroup covers 8*RG rows with CS waves splitting the columns; in one step the 8
+// lanes of a row each load 16 bytes of the row's next 128-byte line (64 columns), so a
+// wave instruction consumes 8 whole lines and W can be streamed with nontemporal loads
+// (NT), BATCH steps in flight; x is staged once in LDS and read back as 16-byte vectors;
+// fp16 pairs are multiplied and summed in fp32 by v_dot2_f32_f16; rows are reduced with
+// DPP across the row's 8 lanes and in LDS across waves, in a fixed order, and rounded
+// once to fp16.
 #pragma once
 
 #include "nm_spmv_impl.h"
@@ -29,70 +30,12 @@ __device__ __forceinline__ float dot8(uint4 w, uint4 xv, float acc) {
   return acc;
 }
 
-template <int WAVES, int BATCH, bool NT>
-__global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint4* __restrict__ W,
-                                                          const uint4* __restrict__ x,
-                                                          uint16_t* __restrict__ y, int rows, int cols) {
-  extern __shared__ uint4 lds[];
-  float* red = reinterpret_cast<float*>(lds + (cols >> 3));
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int u = lane & 3;
-  const int row0 = blockIdx.x * kRowsPerBlock;
-  const unsigned r = unsigned(min(row0 + (lane >> 2), rows - 1));
-
-  const int steps = cols >> 5;  // 32 columns of every row per step
-  const int s_beg = int((int64_t(steps) * wave) / WAVES);
-  const int s_end = int((int64_t(steps) * (wave + 1)) / WAVES);
-  const uint4* __restrict__ wp = W + size_t(r) * unsigned(cols >> 3) + 4 * unsigned(s_beg) + unsigned(u);
-  const uint4* xp = lds + 4 * unsigned(s_beg) + unsigned(u);
-  const int n = s_end - s_beg;
-  const int nfull = n / BATCH;
-  const int rem = n - nfull * BATCH;
-
-  uint4 wv[BATCH];
-  if (nfull > 0) {
-#pragma unroll
-    for (int i = 0; i < BATCH; ++i) wv[i] = load16<NT>(wp + 4 * i);
-  }
-
-  const int n16 = cols >> 3;
-  for (int i = tid; i < n16; i += 64 * WAVES) lds[i] = x[i];
-  __syncthreads();
-
-  float part[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int b = 0; b < nfull; ++b) {
-    if (b > 0) {
-#pragma unroll
-      for (int i = 0; i < BATCH; ++i) wv[i] = load16<NT>(wp + 4 * i);
-    }
-#pragma unroll
-    for (int i = 0; i < BATCH; ++i) part[i & 3] = dot8(wv[i], xp[4 * i], part[i & 3]);
-    wp += 4 * BATCH;
-    xp += 4 * BATCH;
-  }
-  if (rem > 0) {
-#pragma unroll
-    for (int i = 0; i < BATCH; ++i)
-      if (i < rem) wv[i] = load16<NT>(wp + 4 * i);
-#pragma unroll
-    for (int i = 0; i < BATCH; ++i)
-      if (i < rem) part[i & 3] = dot8(wv[i], xp[4 * i], part[i & 3]);
-  }
-  float acc = (part[0] + part[1]) + (part[2] + part[3]);
-
-  acc = dpp_quad_sum(acc);
-  if (u == 0) red[wave * kRowsPerBlock + (lane >> 2)] = acc;
-  __syncthreads();
-  if (tid < kRowsPerBlock) {
-    float t = 0.f;
-#pragma unroll
-    for (int k = 0; k < WAVES; ++k) t += red[k * kRowsPerBlock + tid];
-    const int rr = row0 + tid;
-    if (rr < rows) y[rr] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(t));
-  }
+// Sum over 8 consecutive lanes: DPP quad sums, then row_half_mirror (lane i of each
+// 8-lane group reads lane 7 - i, i.e. the other quad).
+__device__ __forceinline__ float dpp_octet_sum(float v) {
+  v = dpp_quad_sum(v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+  return v;
 }
 
 // Full-line variant: 8 lanes per row, each step one whole 128-byte line (64 columns) of
@@ -164,7 +107,7 @@ __global__ __launch_bounds__(64 * RG * CS) void gemv_line_kernel(const uint4* __
   }
   float acc = (part[0] + part[1]) + (part[2] + part[3]);
 
-  acc = spmv_detail::dpp_octet_sum(acc);
+  acc = dpp_octet_sum(acc);
   if (u == 0) red[wave * 8 + (lane >> 3)] = acc;
   __syncthreads();
   if (tid < ROWS) {

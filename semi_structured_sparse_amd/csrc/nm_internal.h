@@ -28,12 +28,6 @@ void set_last_hip_error(hipError_t e);
 hipError_t launch(const void* kernel, dim3 grid, dim3 block, void** args, size_t lds,
                   hipStream_t stream, const DeviceInfo& dev);
 
-// Rows of y one workgroup of the SpMV / GEMV kernels produces (16 rows x 4 lanes = 64 lanes).
-constexpr int kRowsPerBlock = 16;
-
-// LDS bytes the row-reduction scratch of the SpMV / GEMV kernels needs.
-constexpr size_t reduction_lds_bytes(int waves) { return size_t(waves) * kRowsPerBlock * sizeof(float); }
-
 // Kernel launchers (arguments already validated by the API layer).
 hipError_t launch_pack(const uint16_t* W, uint16_t* values, uint32_t* masks, int64_t rows,
                        int64_t cols, int N, int M, hipStream_t stream, const DeviceInfo& dev);

@@ -40,6 +40,14 @@ bool use_pair_table(int N, int64_t cols, const DeviceInfo& dev) {
   return N == 2 && line_lds_bytes<kPairTable>(int(cols), kMaxWaves) <= size_t(dev.max_lds_per_block);
 }
 
+bool use_rev_walk(int64_t cols, const DeviceInfo& dev) {
+  return line_lds_bytes<kRevWalk>(int(cols), kMaxWaves) <= size_t(dev.max_lds_per_block);
+}
+
+bool use_byte_lut(int64_t cols, const DeviceInfo& dev) {
+  return line_lds_bytes<kByteLut>(int(cols), kMaxWaves) <= size_t(dev.max_lds_per_block);
+}
+
 }  // namespace
 
 int64_t max_cols_for(const DeviceInfo& dev) {
@@ -52,16 +60,22 @@ int64_t max_cols_for(const DeviceInfo& dev) {
 const char* spmv_variant(int64_t rows, int64_t cols, int N, const DeviceInfo& dev) {
   // one string per (pattern, decoder, workgroup shape); they spell the template arguments
   // of spmv_line_kernel<N, RG, CS, BATCH, NTV, DEC> as profilers print them
-  static const char* const names[4][2][2] = {
+  static const char* const names[4][3][2] = {
       {{"spmv_line_kernel<2, 1, 8, 4, true, 0>", "spmv_line_kernel<2, 2, 8, 4, true, 0>"},
-       {"spmv_line_kernel<2, 1, 8, 4, true, 1>", "spmv_line_kernel<2, 2, 8, 4, true, 1>"}},
-      {{"spmv_line_kernel<4, 1, 8, 4, true, 0>", "spmv_line_kernel<4, 2, 8, 4, true, 0>"}, {"", ""}},
-      {{"spmv_line_kernel<8, 1, 8, 4, true, 0>", "spmv_line_kernel<8, 2, 8, 4, true, 0>"}, {"", ""}},
-      {{"spmv_line_kernel<16, 1, 8, 4, true, 0>", "spmv_line_kernel<16, 2, 8, 4, true, 0>"}, {"", ""}},
+       {"spmv_line_kernel<2, 1, 8, 4, true, 1>", "spmv_line_kernel<2, 2, 8, 4, true, 1>"}, {"", ""}},
+      {{"spmv_line_kernel<4, 1, 8, 4, true, 0>", "spmv_line_kernel<4, 2, 8, 4, true, 0>"}, {"", ""},
+       {"spmv_line_kernel<4, 1, 8, 4, true, 2>", "spmv_line_kernel<4, 2, 8, 4, true, 2>"}},
+      {{"spmv_line_kernel<8, 1, 8, 4, true, 0>", "spmv_line_kernel<8, 2, 8, 4, true, 0>"}, {"", ""},
+       {"spmv_line_kernel<8, 1, 8, 4, true, 2>", "spmv_line_kernel<8, 2, 8, 4, true, 2>"}},
+      {{"spmv_line_kernel<16, 1, 8, 4, true, 0>", "spmv_line_kernel<16, 2, 8, 4, true, 0>"}, {"", ""},
+       {"spmv_line_kernel<16, 1, 8, 4, true, 3>", "spmv_line_kernel<16, 2, 8, 4, true, 3>"}},
   };
   static_assert(kBatch == 4 && kNTV, "variant names spell BATCH = 4 and NTV = true");
   const int pi = N == 2 ? 0 : N == 4 ? 1 : N == 8 ? 2 : 3;
-  return names[pi][use_pair_table(N, cols, dev) ? 1 : 0][rows <= kNarrowRows ? 0 : 1];
+  const int di = N == 2 ? (use_pair_table(N, cols, dev) ? 1 : 0)
+               : (N == 4 || N == 8) ? (use_byte_lut(cols, dev) ? 2 : 0)
+                                    : (use_rev_walk(cols, dev) ? 2 : 0);
+  return names[pi][di][rows <= kNarrowRows ? 0 : 1];
 }
 
 hipError_t launch_spmv(const uint16_t* values, const uint32_t* masks, const uint16_t* x,
@@ -74,9 +88,15 @@ hipError_t launch_spmv(const uint16_t* values, const uint32_t* masks, const uint
       // 2:4 uses the x pair table (6 bytes of LDS per column) whenever it fits
       if (use_pair_table(N, cols, dev)) return launch_shape<2, kPairTable>(values, masks, x, y, r, c, stream, dev);
       return launch_shape<2, kBitWalk>(values, masks, x, y, r, c, stream, dev);
-    case 4: return launch_shape<4, kBitWalk>(values, masks, x, y, r, c, stream, dev);
-    case 8: return launch_shape<8, kBitWalk>(values, masks, x, y, r, c, stream, dev);
-    case 16: return launch_shape<16, kBitWalk>(values, masks, x, y, r, c, stream, dev);
+    case 4:
+      if (use_byte_lut(cols, dev)) return launch_shape<4, kByteLut>(values, masks, x, y, r, c, stream, dev);
+      return launch_shape<4, kBitWalk>(values, masks, x, y, r, c, stream, dev);
+    case 8:
+      if (use_byte_lut(cols, dev)) return launch_shape<8, kByteLut>(values, masks, x, y, r, c, stream, dev);
+      return launch_shape<8, kBitWalk>(values, masks, x, y, r, c, stream, dev);
+    case 16:
+      if (use_rev_walk(cols, dev)) return launch_shape<16, kRevWalk>(values, masks, x, y, r, c, stream, dev);
+      return launch_shape<16, kBitWalk>(values, masks, x, y, r, c, stream, dev);
     default: return hipErrorInvalidValue;
   }
 }

@@ -8,38 +8,35 @@
 // word w start at a fixed offset 16*w and the traversal of a word is a fixed number
 // of steps with no prefix scan.
 //
-// Work mapping (one workgroup = 16 rows x all columns, WAVES waves):
-//   * A "step" covers 64 columns (2 mask words) of every row of the tile. In one step
-//     each row's 64 bytes of packed values are split over 4 lanes: lane u of the row
-//     loads one 16-byte dwordx4 holding 8 values, the half h = u & 1 of word
-//     2*step + (u >> 1). The 16 rows x 4 lanes fill the 64 lanes of a wave, and a
-//     wave's consecutive steps walk each row 64 bytes at a time (the two halves of a
-//     128-byte line are read by consecutive instructions of the same wave).
-//   * The WAVES waves split the steps of the row range evenly (contiguous ranges) and
-//     their partial sums are combined in LDS in a fixed order.
-//   * Loads of packed values and masks are issued BATCH steps at a time.
-//   * Products are fp16 x fp16 (exact in fp32) accumulated in fp32 by v_dot2_f32_f16
-//     on pairs of values, reduced across the row's 4 lanes with DPP, then across waves
-//     in LDS, and rounded once to fp16.
+// Work mapping (spmv_line_kernel below): a workgroup covers 8*RG rows x all columns;
+// its RG*CS waves take RG groups of 8 rows, and CS waves split each row group's
+// columns into contiguous ranges. In one "step" the 8 lanes of a row each load 16 bytes
+// (8 values, half a mask word) of the row's next 128-byte line of packed values (4 mask
+// words, 128 columns), so a wave instruction consumes 8 whole cache lines. Loads are
+// issued BATCH steps at a time. Products are fp16 x fp16 (exact in fp32) accumulated in
+// fp32 by v_dot2_f32_f16 on pairs of values, reduced across the row's 8 lanes, then across
+// the CS waves in LDS in a fixed order, and rounded once to fp16.
 //
-// Two ways to find the x of each kept value (the "decoder"):
-//   * Bit walk (any pattern): x is staged in LDS and every kept value gathers its x
-//     with one 16-bit LDS read at the position of the next set bit of its mask bits
-//     (find-lowest-set-bit, then clear it: a fixed 8 steps per lane). For 2:4, 4:8 and
-//     8:16 each 16-column half of a word holds exactly 8 kept columns, so the lane
-//     owning half h walks the set bits of (mask & half h); for 16:32 the lane with the
-//     low 8 values walks the lowest 8 set bits and the lane with the high 8 values
-//     first clears the lowest 8. In one wave instruction the 32 lanes of a half-wave
-//     touch at most two adjacent mask words, i.e. 32 consecutive dwords of x, so the
-//     gathers hit distinct banks or broadcast.
-//   * Pair table (2:4 only): every aligned group of 4 columns keeps exactly 2, one of
-//     6 patterns, and the two kept values of a group are one fp16 pair of the packed
-//     row. The workgroup stages, for each group, the 6 possible x pairs (24 bytes) in
-//     LDS, in the order of the pattern's nibble n (slot (n >> 1) - 1 for n = 3, 5, 6,
-//     9, 10, 12). One 32-bit LDS read then returns the x pair of a value pair, and one
-//     v_dot2 consumes it: a 3-bit field extract, an address add, one LDS read and one
-//     dot per two values.
-//   Both decoders stay inside the LDS allocation for any mask bits (a malformed mask
+// Four ways to find the x of each kept value (the "decoder"), all with a fixed number
+// of steps per mask word and no prefix scan:
+//   * Pair table (2:4): every aligned group of 4 columns keeps exactly 2, one of 6
+//     patterns, and the two kept values of a group are one fp16 pair of the packed row.
+//     The workgroup stages, for each group, the 6 possible x pairs (24 bytes) in LDS in
+//     the order of the pattern's nibble n (slot (n >> 1) - 1 for n = 3, 5, 6, 9, 10, 12).
+//     One 32-bit LDS read returns the x pair of a value pair and one v_dot2 consumes it:
+//     a 3-bit field extract, an address add, one LDS read and one dot per two values.
+//   * Byte LUT (4:8, 8:16): x is staged in LDS with two 256-entry tables giving, for a
+//     mask byte, the byte offsets of its set bits. The two bytes of a lane's half-word
+//     give its 8 offsets (for 8:16 concatenated with one 64-bit shift by 8 * popcount of
+//     the low byte); each value then costs one SDWA byte-select add and one 16-bit LDS read.
+//   * Reversed walk (16:32): x is staged with a copy in which each mask word's 32
+//     elements are reversed. The low-half lane walks the 8 lowest set bits of the word
+//     (find-lowest-set-bit, clear it); the high-half lane walks the 8 lowest set bits of
+//     the bit-reversed word, i.e. the 8 highest columns, in the reversed copy, with its
+//     values reversed by one v_perm per pair.
+//   * Bit walk (any pattern; used when the larger tables do not fit in LDS): as above on
+//     the plain copy; for 16:32 the high-half lane walks down from the window's end.
+//   Every decoder stays inside the LDS allocation for any mask bits (a malformed mask
 //   gives an unspecified y, never an out-of-bounds access): the data region has 64
 //   bytes of padding on each side, more than the furthest a bad mask can reach.
 #pragma once
@@ -52,7 +49,7 @@ namespace spmv_detail {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-enum Decoder { kBitWalk = 0, kPairTable = 1 };
+enum Decoder { kBitWalk = 0, kPairTable = 1, kByteLut = 2, kRevWalk = 3 };
 
 constexpr int kPad = 64;  // bytes of LDS padding on each side of the x data
 
@@ -83,35 +80,44 @@ __device__ __forceinline__ float dot2(uint32_t v, half2_t x, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, v), x, acc, false);
 }
 
-// LDS layout: [reduction: WAVES x 16 floats][pad][x data][pad].
-constexpr int data_offset(int waves) { return int(reduction_lds_bytes(waves)) + kPad; }
+// Byte-LUT tables: for each mask byte b, the byte offsets 2p of its set bits p (lowest
+// first, unused entries 0), once as is and once +16 (the byte's columns 8..15 of a half-word).
+constexpr size_t kLutBytes = 2 * 256 * 8;
 
+// kRevWalk (16:32) stages x and, after it, a copy with every mask word's 32 elements in
+// reverse order, which the high-half lanes walk.
 template <int DEC>
 constexpr size_t data_bytes(int cols) {
-  return DEC == kPairTable ? size_t(cols) / 4 * 24 : size_t(cols) * 2;
-}
-
-template <int DEC>
-constexpr size_t lds_bytes(int cols, int waves) {
-  return size_t(data_offset(waves)) + data_bytes<DEC>(cols) + kPad;
+  return DEC == kPairTable ? size_t(cols) / 4 * 24
+       : DEC == kByteLut   ? size_t(cols) * 2 + kLutBytes
+       : DEC == kRevWalk   ? size_t(cols) * 4
+                           : size_t(cols) * 2;
 }
 
 // ---------------------------------------------------------------- bit-walk decoder
-// Set bits of the mask word that belong to this lane's 8 values.
+// Set bits of the mask word that belong to this lane's 8 values, lowest first.
+// For 2:4, 4:8 and 8:16 every 16-column half of a word holds exactly 8 kept columns:
+// keep_high is 0xFFFFFFFF for the low-half lane (it walks only the 8 lowest set bits,
+// which are exactly the low half's) and 0xFFFF0000 for the high-half lane. For 16:32 the
+// high-half lane walks the bit-reversed word instead, so that its 8 values are the 8
+// lowest set bits of that (see reverse_half_word for its values).
 template <int N>
 __device__ __forceinline__ uint32_t lane_bits(uint32_t m, int half, uint32_t keep_high) {
   if constexpr (N < 16) {
-    // keep_high is 0xFFFFFFFF for the low-half lane (it walks only the 8 lowest set bits,
-    // which are exactly the low half's), 0xFFFF0000 for the high-half lane.
     (void)half;
     return m & keep_high;
   } else {
     (void)keep_high;
-    uint32_t hi = m;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) hi &= hi - 1;  // clear the 8 lowest set bits
-    return half ? hi : m;
+    return half ? __builtin_bitreverse32(m) : m;
   }
+}
+
+// The high-half lane of a 16:32 word meets its values from the highest column down, so
+// its 8 values are reversed: pair j becomes (v[15-2j], v[14-2j]) of the word. One v_perm
+// per pair with a lane-dependent selector (identity for the low-half lane).
+__device__ __forceinline__ uint4 reverse_half_word(uint4 v, uint32_t sel) {
+  return make_uint4(__builtin_amdgcn_perm(v.w, v.x, sel), __builtin_amdgcn_perm(v.z, v.y, sel),
+                    __builtin_amdgcn_perm(v.y, v.z, sel), __builtin_amdgcn_perm(v.x, v.w, sel));
 }
 
 // 32-bit LDS byte address of an LDS object, and 16-bit loads from such addresses (LDS
@@ -127,18 +133,80 @@ __device__ __forceinline__ _Float16 lds_half(uint32_t a) {
   return *reinterpret_cast<lds_half_t*>(uintptr_t(a));
 }
 
-// x pairs of this lane's 8 kept columns: `bits` holds the columns as set bits relative to
-// xw, the LDS byte address of the mask word's x window (v_ffbl of an exhausted word is
-// -1: one element before the window, still inside the padded LDS data region).
-__device__ __forceinline__ void gather_bits(uint32_t bits, uint32_t xw, half2_t (&xp)[4]) {
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) const u32x2_t lds_u2_t;
+__device__ __forceinline__ uint2 lds_u2(uint32_t a) {
+  const u32x2_t t = *reinterpret_cast<lds_u2_t*>(uintptr_t(a));
+  return make_uint2(t.x, t.y);
+}
+
+// x pairs of this lane's 8 kept columns: `bits` holds the columns as set bits; column p
+// sits at LDS byte address xw + step * p (step = 2, or -2 from the window's last element
+// for a bit-reversed 16:32 word). v_ffbl of an exhausted word is -1: one element outside
+// the window, still inside the padded LDS data region.
+__device__ __forceinline__ void gather_bits(uint32_t bits, uint32_t xw, int step, half2_t (&xp)[4]) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t p0 = uint32_t(__builtin_ctz(bits));
+    const int p0 = __builtin_ctz(bits);
     bits &= bits - 1;
-    const uint32_t p1 = uint32_t(__builtin_ctz(bits));
+    const int p1 = __builtin_ctz(bits);
     bits &= bits - 1;
-    xp[k].x = lds_half(xw + 2u * p0);
-    xp[k].y = lds_half(xw + 2u * p1);
+    if (step == 2) {
+      xp[k].x = lds_half(xw + 2u * uint32_t(p0));
+      xp[k].y = lds_half(xw + 2u * uint32_t(p1));
+    } else {
+      xp[k].x = lds_half(xw + uint32_t(step * p0));
+      xp[k].y = lds_half(xw + uint32_t(step * p1));
+    }
+  }
+}
+
+// Byte-LUT gather for 4:8 and 8:16: the half-word's two mask bytes give their set-bit
+// offsets from the tables (one 64-bit LDS read each); the two lists are concatenated with
+// one 64-bit shift by 8 * popcount(low byte) (for 4:8 the low byte always holds 4); byte k
+// of the result is the offset of value k from xh, the half-word's x window.
+template <int N>
+__device__ __forceinline__ void gather_lut(uint32_t m, uint32_t sh16, uint32_t lut, uint32_t xh,
+                                           half2_t (&xp)[4]) {
+  const uint32_t b0 = __builtin_amdgcn_ubfe(m, sh16, 8);
+  const uint32_t b1 = __builtin_amdgcn_ubfe(m, sh16 + 8, 8);
+  const uint2 l0 = lds_u2(lut + 8u * b0);
+  const uint2 l1 = lds_u2(lut + 2048u + 8u * b1);
+  uint32_t lo, hi;
+  if constexpr (N == 4) {
+    lo = l0.x;
+    hi = l1.x;
+  } else {
+    const uint64_t q = (uint64_t(l0.y) << 32 | l0.x) |
+                       ((uint64_t(l1.y) << 32 | l1.x) << (8u * uint32_t(__builtin_popcount(b0))));
+    lo = uint32_t(q);
+    hi = uint32_t(q >> 32);
+  }
+  xp[0].x = lds_half(xh + (lo & 0xFFu));
+  xp[0].y = lds_half(xh + ((lo >> 8) & 0xFFu));
+  xp[1].x = lds_half(xh + ((lo >> 16) & 0xFFu));
+  xp[1].y = lds_half(xh + (lo >> 24));
+  xp[2].x = lds_half(xh + (hi & 0xFFu));
+  xp[2].y = lds_half(xh + ((hi >> 8) & 0xFFu));
+  xp[3].x = lds_half(xh + ((hi >> 16) & 0xFFu));
+  xp[3].y = lds_half(xh + (hi >> 24));
+}
+
+// Builds the two byte-LUT tables (256 entries of 8 bytes each) at `lut`.
+__device__ __forceinline__ void stage_byte_lut(uint2* lut, int tid, int nthreads) {
+  for (int b = tid; b < 256; b += nthreads) {
+    uint64_t lo = 0, hi = 0;
+    int k = 0;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      if ((b >> p) & 1) {
+        lo |= uint64_t(2 * p) << (8 * k);
+        hi |= uint64_t(2 * p + 16) << (8 * k);
+        ++k;
+      }
+    }
+    lut[b] = make_uint2(uint32_t(lo), uint32_t(lo >> 32));
+    lut[256 + b] = make_uint2(uint32_t(hi), uint32_t(hi >> 32));
   }
 }
 
@@ -188,14 +256,43 @@ struct Batch {
   }
 
   // Bit walk: `xw` is the LDS byte address of the x window of this lane's word in the
-  // batch's first step.
-  template <int N>
+  // batch's first step. 16:32 high-half lanes walk the bit-reversed word: with XR their
+  // `xw` points into the reversed copy of x (step +2); without it they walk the plain
+  // window from its last element down (step -2).
+  template <int N, bool XR>
   __device__ __forceinline__ void compute_bits(uint32_t xw, int half, uint32_t keep_high, int count,
                                                float (&part)[4]) const {
+    const bool rev = N == 16 && half;
+    const int step = (rev && !XR) ? -2 : 2;
+    const uint32_t xoff = (rev && !XR) ? 62u : 0u;
+    const uint32_t sel = rev ? 0x05040706u : 0x03020100u;
     half2_t xp[BATCH][4];
 #pragma unroll
     for (int i = 0; i < BATCH; ++i)
-      if (i < count) gather_bits(lane_bits<N>(m[i], half, keep_high), xw + uint32_t(XSTEP) * i, xp[i]);
+      if (i < count) gather_bits(lane_bits<N>(m[i], half, keep_high), xw + uint32_t(XSTEP) * i + xoff, step, xp[i]);
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      if (i < count) {
+        const uint4 vv = N == 16 ? reverse_half_word(v[i], sel) : v[i];
+        float a = part[i & 3];
+        a = dot2(vv.x, xp[i][0], a);
+        a = dot2(vv.y, xp[i][1], a);
+        a = dot2(vv.z, xp[i][2], a);
+        a = dot2(vv.w, xp[i][3], a);
+        part[i & 3] = a;
+      }
+    }
+  }
+
+  // Byte LUT (4:8, 8:16): `xh` is the LDS byte address of this lane's half-word x window
+  // in the batch's first step, `lut` the tables, `sh16` = 16 * half.
+  template <int N>
+  __device__ __forceinline__ void compute_lut(uint32_t xh, uint32_t lut, uint32_t sh16, int count,
+                                              float (&part)[4]) const {
+    half2_t xp[BATCH][4];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i)
+      if (i < count) gather_lut<N>(m[i], sh16, lut, xh + uint32_t(XSTEP) * i, xp[i]);
 #pragma unroll
     for (int i = 0; i < BATCH; ++i) {
       if (i < count) {
@@ -249,98 +346,16 @@ __device__ __forceinline__ void stage_x(const uint4* __restrict__ x, char* data,
     uint4* xs4 = reinterpret_cast<uint4*>(data);
     const int n16 = cols >> 3;
     for (int i = tid; i < n16; i += nthreads) xs4[i] = x[i];
-  }
-}
-
-template <int N, int WAVES, int BATCH, bool NT, int DEC>
-__global__ __launch_bounds__(64 * WAVES) void spmv_kernel(const uint4* __restrict__ values,
-                                                          const uint32_t* __restrict__ masks,
-                                                          const uint4* __restrict__ x,
-                                                          uint16_t* __restrict__ y, int rows, int cols) {
-  static_assert(DEC == kBitWalk || N == 2, "the pair table decodes 2:4 only");
-  extern __shared__ uint4 lds[];
-  char* lds_b = reinterpret_cast<char*>(lds);
-  float* red = reinterpret_cast<float*>(lds_b);
-  char* data = lds_b + data_offset(WAVES);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps loop bounds scalar
-  const int u = lane & 3;          // lane within the row's quad
-  const int half = u & 1;          // which 8 values of the word
-  const int wsel = u >> 1;         // which of the step's 2 words
-  const int row0 = blockIdx.x * kRowsPerBlock;
-  // Lanes past the last row read the last row again; their sums are never stored.
-  const unsigned r = unsigned(min(row0 + (lane >> 2), rows - 1));
-
-  const int words = cols >> 5;
-  const int steps = (words + 1) >> 1;
-  const int full_steps = words >> 1;
-  const int s_beg = int((int64_t(steps) * wave) / WAVES);
-  const int s_end = int((int64_t(steps) * (wave + 1)) / WAVES);
-  const int s_main = min(s_end, full_steps);
-
-  const uint4* __restrict__ vrow = values + size_t(r) * unsigned(cols >> 4);
-  const uint32_t* __restrict__ mrow = masks + size_t(r) * unsigned(words);
-  const uint32_t keep_high = half ? 0xFFFF0000u : 0xFFFFFFFFu;
-
-  // Per step the lane's values advance 64 bytes (4 x uint4) and its mask 2 words.
-  const uint4* __restrict__ vp = vrow + 4 * unsigned(s_beg) + unsigned(u);
-  const uint32_t* __restrict__ mp = mrow + 2 * unsigned(s_beg) + unsigned(wsel);
-  const int n = s_main - s_beg;      // wave-uniform
-  const int nfull = n / BATCH;
-  const int rem = n - nfull * BATCH;
-
-  using B = Batch<BATCH, NT, 4, 2, 384, 128>;
-  B A;
-  if (nfull > 0) A.load(vp, mp, BATCH);  // first batch in flight while x is staged
-
-  // Stage x (or its pair table) in LDS.
-  stage_x<DEC>(x, data, cols, tid, 64 * WAVES);
-  __syncthreads();
-
-  // This lane's x data position in the first step of its range; a step is 64 columns.
-  uint32_t xw = lds_address(data) + 128u * unsigned(s_beg) + 64u * unsigned(wsel);
-  const char* tb = data - 4 + 384 * unsigned(s_beg) + 192 * unsigned(wsel) + 96 * unsigned(half);
-  const uint32_t sh = 16u * unsigned(half) + 1u;
-
-  float part[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int b = 0; b < nfull; ++b) {
-    if (b > 0) A.load(vp, mp, BATCH);
-    if constexpr (DEC == kPairTable) A.compute_pairs(tb, sh, BATCH, part);
-    else A.template compute_bits<N>(xw, half, keep_high, BATCH, part);
-    vp += 4 * BATCH;
-    mp += 2 * BATCH;
-    xw += 128u * BATCH;
-    tb += 384 * BATCH;
-  }
-  if (rem > 0) {  // fewer than BATCH full steps left
-    B R;
-    R.load(vp, mp, rem);
-    if constexpr (DEC == kPairTable) R.compute_pairs(tb, sh, rem, part);
-    else R.template compute_bits<N>(xw, half, keep_high, rem, part);
-  }
-  // Odd word count: the last step holds a single word, owned by the lanes with wsel == 0.
-  if (s_end > full_steps && wsel == 0) {
-    const unsigned s = unsigned(full_steps);
-    Batch<1, NT, 4, 2, 384, 128> T;
-    T.load(vrow + 4 * s + unsigned(u), mrow + 2 * s, 1);
-    if constexpr (DEC == kPairTable)
-      T.compute_pairs(data - 4 + 384 * s + 96 * unsigned(half), sh, 1, part);
-    else
-      T.template compute_bits<N>(lds_address(data) + 128u * s, half, keep_high, 1, part);
-  }
-  float acc = (part[0] + part[1]) + (part[2] + part[3]);
-
-  acc = dpp_quad_sum(acc);
-  if (u == 0) red[wave * kRowsPerBlock + (lane >> 2)] = acc;
-  __syncthreads();
-  if (tid < kRowsPerBlock) {
-    float t = 0.f;
-#pragma unroll
-    for (int k = 0; k < WAVES; ++k) t += red[k * kRowsPerBlock + tid];
-    const int rr = row0 + tid;
-    if (rr < rows) y[rr] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(t));
+    if constexpr (DEC == kByteLut) stage_byte_lut(reinterpret_cast<uint2*>(data + size_t(cols) * 2), tid, nthreads);
+    if constexpr (DEC == kRevWalk) {
+      // reversed copy: quarter q of word w = quarter 3 - q of x's word w, elements reversed
+      uint4* xr4 = reinterpret_cast<uint4*>(data + size_t(cols) * 2);
+      for (int i = tid; i < n16; i += nthreads) {
+        const uint4 a = x[(i & ~3) | (3 - (i & 3))];
+        xr4[i] = make_uint4(__builtin_amdgcn_alignbit(a.w, a.w, 16), __builtin_amdgcn_alignbit(a.z, a.z, 16),
+                            __builtin_amdgcn_alignbit(a.y, a.y, 16), __builtin_amdgcn_alignbit(a.x, a.x, 16));
+      }
+    }
   }
 }
 
@@ -348,14 +363,19 @@ __global__ __launch_bounds__(64 * WAVES) void spmv_kernel(const uint4* __restric
 // Same method, with 8 lanes per row: in one step the 8 lanes of a row load the row's next
 // 128 bytes of packed values (one whole cache line, 4 mask words = 128 columns), so every
 // line is consumed by a single wave instruction and the values can be streamed with
-// nontemporal loads (NTV). A wave instruction covers 8 rows; a workgroup has RG row
-// groups of 8 rows and CS waves splitting the columns of each row group (RG*CS waves).
-// Row sums: DPP inside the quad, row_half_mirror across the two quads of the row, then
+// nontemporal loads (NTV). A wave instruction covers 8 rows. Lanes are ordered so that
+// each half-wave holds the same half of every row's line: lanes 4r..4r+3 take half-words
+// 0..3 (words 0, 1) of row r and lanes 32+4r..32+4r+3 half-words 4..7 (words 2, 3), so
+// the LDS reads of a half-wave touch only 2 consecutive mask words' x data (32 dwords:
+// no bank conflicts for the bit walk; 8 table groups for the pair table).
+// A workgroup has RG row groups of 8 rows and CS waves splitting the columns of each row
+// group (RG*CS waves). Row sums: DPP inside the quad, a swap across the half-waves, then
 // LDS across the CS waves, in a fixed order.
-__device__ __forceinline__ float dpp_octet_sum(float v) {
+// Sum over the 8 lanes of a row (lanes 4r..4r+3 and 32+4r..32+4r+3): DPP inside the
+// quad, then the partner half-wave's quad (lane ^ 32) through ds_swizzle-free bpermute.
+__device__ __forceinline__ float row8_sum(float v) {
   v = dpp_quad_sum(v);
-  // row_half_mirror: lane i of each 8-lane half-row reads lane 7 - i (the other quad)
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+  v += __shfl_xor(v, 32);
   return v;
 }
 
@@ -367,12 +387,17 @@ constexpr size_t line_lds_bytes(int cols, int waves) {
   return size_t(line_data_offset(waves)) + data_bytes<DEC>(cols) + kPad;
 }
 
+// Register budget: 64 VGPRs, so that 8 waves fit on each SIMD (two 16-wave workgroups per
+// CU). At 65..72 VGPRs only 7 fit and a CU holds a single 16-wave workgroup, which leaves
+// nothing to overlap one workgroup's staging of x and its final reduction with.
 template <int N, int RG, int CS, int BATCH, bool NTV, int DEC>
-__global__ __launch_bounds__(64 * RG * CS) void spmv_line_kernel(const uint4* __restrict__ values,
+__global__ __launch_bounds__(64 * RG * CS) __attribute__((amdgpu_waves_per_eu(8))) void spmv_line_kernel(const uint4* __restrict__ values,
                                                                  const uint32_t* __restrict__ masks,
                                                                  const uint4* __restrict__ x,
                                                                  uint16_t* __restrict__ y, int rows, int cols) {
-  static_assert(DEC == kBitWalk || N == 2, "the pair table decodes 2:4 only");
+  static_assert((DEC != kPairTable || N == 2) && (DEC != kByteLut || N == 4 || N == 8) &&
+                    (DEC != kRevWalk || N == 16),
+                "pair table: 2:4 only; byte LUT: 4:8 and 8:16 only; reversed walk: 16:32 only");
   constexpr int WAVES = RG * CS;
   constexpr int ROWS = 8 * RG;
   extern __shared__ uint4 lds[];
@@ -385,11 +410,12 @@ __global__ __launch_bounds__(64 * RG * CS) void spmv_line_kernel(const uint4* __
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rg = wave / CS;
   const int cs = wave - rg * CS;
-  const int u = lane & 7;          // lane within the row's octet: half-word u of the step
+  const int rsub = (lane & 31) >> 2;               // row within the wave's 8 rows
+  const int u = ((lane >> 5) << 2) | (lane & 3);   // half-word u of the step's 8
   const int half = u & 1;
   const int wsel = u >> 1;         // which of the step's 4 words
   const int row0 = blockIdx.x * ROWS;
-  const unsigned r = unsigned(min(row0 + 8 * rg + (lane >> 3), rows - 1));
+  const unsigned r = unsigned(min(row0 + 8 * rg + rsub, rows - 1));
 
   const int words = cols >> 5;
   const int steps = (words + 3) >> 2;
@@ -418,12 +444,18 @@ __global__ __launch_bounds__(64 * RG * CS) void spmv_line_kernel(const uint4* __
   uint32_t xw = lds_address(data) + 256u * unsigned(s_beg) + 64u * unsigned(wsel);
   const char* tb = data - 4 + 768 * unsigned(s_beg) + 192 * unsigned(wsel) + 96 * unsigned(half);
   const uint32_t sh = 16u * unsigned(half) + 1u;
+  const uint32_t sh16 = 16u * unsigned(half);
+  const uint32_t xhalf = 32u * unsigned(half);                      // byte offset of the half-word's x
+  const uint32_t lut = lds_address(data) + 2u * unsigned(cols);     // byte-LUT tables after x
+  // 16:32 high-half lanes read the reversed copy of x, which follows x
+  const uint32_t xrev = (DEC == kRevWalk && half) ? 2u * unsigned(cols) : 0u;
 
   float part[4] = {0.f, 0.f, 0.f, 0.f};
   for (int b = 0; b < nfull; ++b) {
     if (b > 0) A.load(vp, mp, BATCH);
     if constexpr (DEC == kPairTable) A.compute_pairs(tb, sh, BATCH, part);
-    else A.template compute_bits<N>(xw, half, keep_high, BATCH, part);
+    else if constexpr (DEC == kByteLut) A.template compute_lut<N>(xw + xhalf, lut, sh16, BATCH, part);
+    else A.template compute_bits<N, DEC == kRevWalk>(xw + xrev, half, keep_high, BATCH, part);
     vp += 8 * BATCH;
     mp += 4 * BATCH;
     xw += 256u * BATCH;
@@ -433,7 +465,8 @@ __global__ __launch_bounds__(64 * RG * CS) void spmv_line_kernel(const uint4* __
     B R;
     R.load(vp, mp, rem);
     if constexpr (DEC == kPairTable) R.compute_pairs(tb, sh, rem, part);
-    else R.template compute_bits<N>(xw, half, keep_high, rem, part);
+    else if constexpr (DEC == kByteLut) R.template compute_lut<N>(xw + xhalf, lut, sh16, rem, part);
+    else R.template compute_bits<N, DEC == kRevWalk>(xw + xrev, half, keep_high, rem, part);
   }
   // Last step with 1..3 words (cols not a multiple of 128): lanes whose word exists.
   if (s_end > full_steps && wsel < (words & 3)) {
@@ -442,13 +475,15 @@ __global__ __launch_bounds__(64 * RG * CS) void spmv_line_kernel(const uint4* __
     T.load(vrow + 8 * s + unsigned(u), mrow + 4 * s + unsigned(wsel), 1);
     if constexpr (DEC == kPairTable)
       T.compute_pairs(data - 4 + 768 * s + 192 * unsigned(wsel) + 96 * unsigned(half), sh, 1, part);
+    else if constexpr (DEC == kByteLut)
+      T.template compute_lut<N>(lds_address(data) + 256u * s + 64u * unsigned(wsel) + xhalf, lut, sh16, 1, part);
     else
-      T.template compute_bits<N>(lds_address(data) + 256u * s + 64u * unsigned(wsel), half, keep_high, 1, part);
+      T.template compute_bits<N, DEC == kRevWalk>(lds_address(data) + 256u * s + 64u * unsigned(wsel) + xrev, half, keep_high, 1, part);
   }
   float acc = (part[0] + part[1]) + (part[2] + part[3]);
 
-  acc = dpp_octet_sum(acc);
-  if (u == 0) red[wave * 8 + (lane >> 3)] = acc;
+  acc = row8_sum(acc);
+  if (u == 0) red[wave * 8 + rsub] = acc;
   __syncthreads();
   if (tid < ROWS) {
     const int trg = tid >> 3, trow = tid & 7;

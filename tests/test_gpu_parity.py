@@ -155,11 +155,12 @@ def test_cross_path_sparse_vs_dense_of_pruned():
 
 def test_edge_shapes_and_errors():
     mc = nm.max_cols()
-    # widest x the kernel stages, a single row and a ragged row count
+    # widest x the kernel stages (every pattern falls back to the plain bit walk there),
+    # a single row and a ragged row count
     for R, C in ((1, 32), (3, mc), (17, 32)):
         W = synth.weight(R, C, seed=740)
         x = synth.activation(C, seed=741)
-        for N, M in ((2, 4), (16, 32)):
+        for N, M in PATTERNS:
             rv, rm = oracle.pack_ref(W, N, M)
             y = nm.nm_spmv(up_f16(rv), up_u32(rm), up_f16(x), N, M)
             assert oracle.y_tolerance_report(down_f16(y), oracle.spmv_ref(rv, rm, x, C, N, M))["ok"], (R, C)
