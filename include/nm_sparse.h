@@ -96,9 +96,15 @@ int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,
 
 /* Introspection: the name of the kernel configuration nm_spmv launches for this shape
  * and pattern on the current device, as it appears in profiler traces (for example
- * "spmv_line_kernel<2, 2, 8, 4, true, 1>"); "" if the arguments are invalid. Static
+ * "spmv_kernel<2, 4, true, 1>"); "" if the arguments are invalid. Static
  * string, never NULL. Used by the benchmark to attribute measured durations. */
 const char* nm_spmv_variant(int64_t rows, int64_t cols, int N, int M);
+
+/* Introspection: the workgroup shape nm_spmv uses for this shape on the current device.
+ * Writes shape[0] = rows per workgroup, shape[1] = groups of 8 rows per workgroup,
+ * shape[2] = waves per row group (each takes a contiguous range of the columns),
+ * shape[3] = number of workgroups (ceil(rows / shape[0])). Validates like nm_spmv. */
+int nm_spmv_launch_shape(int64_t rows, int64_t cols, int N, int M, int64_t* shape);
 
 /* Static description of a status code; never NULL. */
 const char* nm_status_string(int status);

@@ -33,6 +33,8 @@ SIGNATURES = {
     "nm_status_string": (_c.c_char_p, [_c.c_int]),
     "nm_spmv_variant": (_c.c_char_p, [_c.c_int64, _c.c_int64, _c.c_int, _c.c_int]),
     "nm_last_hip_error": (_c.c_int, []),
+    "nm_spmv_launch_shape": (_c.c_int, [_c.c_int64, _c.c_int64, _c.c_int, _c.c_int,
+                                        _c.POINTER(_c.c_int64)]),
     "nm_probe_read": (_c.c_int, [_c.c_void_p, _c.c_size_t, _c.c_void_p, _c.c_uint32, _c.c_void_p]),
     "nm_probe_copy": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
 }
@@ -102,6 +104,14 @@ def max_cols() -> int:
 def spmv_variant(rows: int, cols: int, N: int, M: int) -> str:
     """Kernel configuration nm_spmv launches for this shape on the current device."""
     return lib().nm_spmv_variant(rows, cols, N, M).decode()
+
+
+def spmv_launch_shape(rows: int, cols: int, N: int, M: int) -> dict:
+    """Workgroup shape nm_spmv uses for this shape on the current device."""
+    out = (ctypes.c_int64 * 4)()
+    _check("nm_spmv_launch_shape", lib().nm_spmv_launch_shape(rows, cols, N, M, out))
+    return {"rows_per_workgroup": out[0], "row_groups": out[1], "waves_per_row_group": out[2],
+            "workgroups": out[3]}
 
 
 # --------------------------------------------------------------------------- torch layer

@@ -20,8 +20,9 @@ bool valid_pattern(int N, int M) {
   return (N == 2 && M == 4) || (N == 4 && M == 8) || (N == 8 && M == 16) || (N == 16 && M == 32);
 }
 
-// rows >= 1, cols >= 32, cols % 32 == 0, and every size the kernels form fits:
-// grid = ceil(rows / 16) blocks, int row / column indices, and rows*cols*2 bytes.
+// rows >= 1, cols >= 32, cols % 32 == 0, and every size the kernels form fits: int row
+// indices up to rows + 64 (a workgroup's rows past the last one), int column indices, and
+// rows*cols*2 bytes.
 bool valid_shape(int64_t rows, int64_t cols) {
   if (rows < 1 || cols < 32 || (cols % 32) != 0) return false;
   if (rows > (int64_t(1) << 31) - 64 || cols > (int64_t(1) << 30)) return false;
@@ -145,6 +146,22 @@ const char* nm_spmv_variant(int64_t rows, int64_t cols, int N, int M) {
   nm::DeviceInfo dev;
   if (nm::current_device_info(&dev) != hipSuccess) return "";
   return nm::spmv_variant(rows, cols, N, dev);
+}
+
+int nm_spmv_launch_shape(int64_t rows, int64_t cols, int N, int M, int64_t* shape) {
+  if (!shape) return NM_ERR_NULL;
+  if (!nm::valid_shape(rows, cols)) return NM_ERR_SHAPE;
+  if (!nm::valid_pattern(N, M)) return NM_ERR_PATTERN;
+  nm::DeviceInfo dev;
+  hipError_t e = nm::current_device_info(&dev);
+  if (e != hipSuccess) return nm::hip_fail(e);
+  if (cols > nm::max_cols_for(dev)) return NM_ERR_TOO_WIDE;
+  const nm::WorkgroupShape s = nm::spmv_shape(rows, cols, dev);
+  shape[0] = s.rpb;
+  shape[1] = s.row_groups;
+  shape[2] = s.cs;
+  shape[3] = s.grid;
+  return NM_OK;
 }
 
 const char* nm_status_string(int status) {

@@ -37,8 +37,22 @@ hipError_t launch_spmv(const uint16_t* values, const uint32_t* masks, const uint
 hipError_t launch_gemv(const uint16_t* W, const uint16_t* x, uint16_t* y, int64_t rows,
                        int64_t cols, hipStream_t stream, const DeviceInfo& dev);
 
-// Name of the kernel configuration launch_spmv picks (static string).
+// Workgroup shape of one SpMV / GEMV launch: `rpb` rows per workgroup, split into
+// `row_groups` groups of 8 rows, each with `cs` waves that split the columns; `grid`
+// workgroups.
+struct WorkgroupShape {
+  int rpb = 8;
+  int row_groups = 1;
+  int cs = 8;
+  int64_t grid = 0;
+};
+
+// Shape for `rows` rows of `steps` 128-byte lines each (the streamed bytes of a row / 128).
+WorkgroupShape workgroup_shape(int64_t rows, int64_t steps, const DeviceInfo& dev);
+
+// Name of the kernel configuration launch_spmv picks (static string) and its shape.
 const char* spmv_variant(int64_t rows, int64_t cols, int N, const DeviceInfo& dev);
+WorkgroupShape spmv_shape(int64_t rows, int64_t cols, const DeviceInfo& dev);
 
 // Widest x the SpMV / GEMV kernels can stage for the given device.
 int64_t max_cols_for(const DeviceInfo& dev);

@@ -1,6 +1,8 @@
-// nm_spmv launcher: picks the kernel configuration for the shape and launches it.
-// The kernels themselves (and the description of the method and the work mapping)
-// are in nm_spmv_impl.h.
+// nm_spmv launcher: picks the decoder and the workgroup shape for the shape of W and
+// launches spmv_kernel (nm_spmv_impl.h holds the kernel and the description of the
+// method and of the work mapping).
+#include <algorithm>
+
 #include "nm_spmv_impl.h"
 
 namespace nm {
@@ -11,71 +13,95 @@ using namespace spmv_detail;
 constexpr bool kNTV = true;  // values stream once, a whole 128-byte line per instruction
 constexpr int kBatch = 4;    // steps whose loads are issued together
 
-// Workgroup shape: RG row groups of 8 rows x CS waves splitting the columns. Narrow
-// layers (few rows) use 8-row workgroups so that more CUs get work.
-template <int N, int DEC, int RG, int CS>
-hipError_t launch_cfg(const uint16_t* values, const uint32_t* masks, const uint16_t* x, uint16_t* y,
-                      int rows, int cols, hipStream_t stream, const DeviceInfo& dev) {
-  const uint4* v4 = reinterpret_cast<const uint4*>(values);
-  const uint4* x4 = reinterpret_cast<const uint4*>(x);
-  void* args[] = {&v4, &masks, &x4, &y, &rows, &cols};
-  const dim3 grid((rows + 8 * RG - 1) / (8 * RG));
-  return launch(reinterpret_cast<const void*>(&spmv_line_kernel<N, RG, CS, kBatch, kNTV, DEC>), grid,
-                dim3(64 * RG * CS), args, line_lds_bytes<DEC>(cols, RG * CS), stream, dev);
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Decoder for the pattern: the table-driven one when its LDS image fits one workgroup,
+// else the bit walk (2 bytes of LDS per column).
+int pick_decoder(int N, int64_t cols, const DeviceInfo& dev) {
+  const size_t cap = size_t(dev.max_lds_per_block);
+  const int c = int(cols);
+  switch (N) {
+    case 2: return lds_bytes<kPairTable>(c) <= cap ? kPairTable : kBitWalk;
+    case 4:
+    case 8: return lds_bytes<kByteLut>(c) <= cap ? kByteLut : kBitWalk;
+    default: return lds_bytes<kRevWalk>(c) <= cap ? kRevWalk : kBitWalk;
+  }
 }
 
-// Narrow layers (at most this many rows) use 8-row workgroups, the others 16-row ones.
-constexpr int kNarrowRows = 2048;
+}  // namespace
+
+// Workgroup shape from the row count and the row length in steps (128-byte lines of
+// streamed data), measured on MI355X over the Llama / Qwen projection shapes (1024..28672
+// rows, 4096..28672 columns, all four patterns, and the dense product); every rule below
+// keeps the grid a near-multiple of the CU count so that each CU streams the same number
+// of rows.
+//   * long rows (more than 64 steps): one workgroup of at most 40 rows per CU and round,
+//     about 12 waves (3..12 per row group). Each workgroup stages all of x, so fewer,
+//     taller workgroups spend less on staging, and the long rows give every wave many
+//     steps;
+//   * narrow layers (at most 8 rows per CU): a few rows per workgroup and about 4 steps per
+//     wave, to spread the little work over all CUs;
+//   * otherwise: about 8 rows per workgroup (balanced over the CUs) and 8 waves per row.
+WorkgroupShape workgroup_shape(int64_t rows, int64_t steps, const DeviceInfo& dev) {
+  const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
+  WorkgroupShape s;
+  if (steps > 64) {
+    const int64_t rounds = ceil_div(rows, cus * 40);
+    s.rpb = int(ceil_div(rows, cus * rounds));
+    const int rg = int(ceil_div(s.rpb, 8));
+    s.cs = rg >= 4 ? 3 : 12 / rg;
+    if (rg * s.cs > kMaxWaves) s.cs = kMaxWaves / rg;
+  } else if (rows <= 8 * cus) {
+    s.rpb = int(std::min<int64_t>(8, ceil_div(rows, cus)));
+    s.cs = int(std::min<int64_t>(16, ceil_div(steps, 4)));
+  } else {
+    s.rpb = int(ceil_div(rows, cus * ceil_div(rows, 8 * cus)));
+    s.cs = steps < 32 ? int(ceil_div(steps, 4)) : 8;
+  }
+  s.row_groups = int(ceil_div(s.rpb, 8));
+  s.grid = ceil_div(rows, s.rpb);
+  return s;
+}
+
+namespace {
 
 template <int N, int DEC>
-hipError_t launch_shape(const uint16_t* values, const uint32_t* masks, const uint16_t* x, uint16_t* y,
-                        int rows, int cols, hipStream_t stream, const DeviceInfo& dev) {
-  if (rows <= kNarrowRows) return launch_cfg<N, DEC, 1, 8>(values, masks, x, y, rows, cols, stream, dev);
-  return launch_cfg<N, DEC, 2, 8>(values, masks, x, y, rows, cols, stream, dev);
-}
-
-constexpr int kMaxWaves = 16;  // largest workgroup the launcher uses (2 x 8 waves)
-
-bool use_pair_table(int N, int64_t cols, const DeviceInfo& dev) {
-  return N == 2 && line_lds_bytes<kPairTable>(int(cols), kMaxWaves) <= size_t(dev.max_lds_per_block);
-}
-
-bool use_rev_walk(int64_t cols, const DeviceInfo& dev) {
-  return line_lds_bytes<kRevWalk>(int(cols), kMaxWaves) <= size_t(dev.max_lds_per_block);
-}
-
-bool use_byte_lut(int64_t cols, const DeviceInfo& dev) {
-  return line_lds_bytes<kByteLut>(int(cols), kMaxWaves) <= size_t(dev.max_lds_per_block);
+hipError_t launch_kernel(const uint16_t* values, const uint32_t* masks, const uint16_t* x, uint16_t* y,
+                         int rows, int cols, const WorkgroupShape& s, hipStream_t stream, const DeviceInfo& dev) {
+  const uint4* v4 = reinterpret_cast<const uint4*>(values);
+  const uint4* x4 = reinterpret_cast<const uint4*>(x);
+  int rpb = s.rpb, cs = s.cs;
+  void* args[] = {&v4, &masks, &x4, &y, &rows, &cols, &rpb, &cs};
+  return launch(reinterpret_cast<const void*>(&spmv_kernel<N, kBatch, kNTV, DEC>), dim3(unsigned(s.grid)),
+                dim3(unsigned(64 * s.row_groups * s.cs)), args, lds_bytes<DEC>(cols), stream, dev);
 }
 
 }  // namespace
 
 int64_t max_cols_for(const DeviceInfo& dev) {
   // the bit-walk kernel (2 bytes of LDS per column) bounds the accepted width
-  const int64_t avail = int64_t(dev.max_lds_per_block) - int64_t(line_lds_bytes<kBitWalk>(0, kMaxWaves));
+  const int64_t avail = int64_t(dev.max_lds_per_block) - int64_t(lds_bytes<kBitWalk>(0));
   if (avail <= 0) return 0;
   return (avail / 2) / 32 * 32;
 }
 
+WorkgroupShape spmv_shape(int64_t rows, int64_t cols, const DeviceInfo& dev) {
+  return workgroup_shape(rows, ceil_div(cols, 128), dev);  // 128 columns = 128 bytes of values
+}
+
 const char* spmv_variant(int64_t rows, int64_t cols, int N, const DeviceInfo& dev) {
-  // one string per (pattern, decoder, workgroup shape); they spell the template arguments
-  // of spmv_line_kernel<N, RG, CS, BATCH, NTV, DEC> as profilers print them
-  static const char* const names[4][3][2] = {
-      {{"spmv_line_kernel<2, 1, 8, 4, true, 0>", "spmv_line_kernel<2, 2, 8, 4, true, 0>"},
-       {"spmv_line_kernel<2, 1, 8, 4, true, 1>", "spmv_line_kernel<2, 2, 8, 4, true, 1>"}, {"", ""}},
-      {{"spmv_line_kernel<4, 1, 8, 4, true, 0>", "spmv_line_kernel<4, 2, 8, 4, true, 0>"}, {"", ""},
-       {"spmv_line_kernel<4, 1, 8, 4, true, 2>", "spmv_line_kernel<4, 2, 8, 4, true, 2>"}},
-      {{"spmv_line_kernel<8, 1, 8, 4, true, 0>", "spmv_line_kernel<8, 2, 8, 4, true, 0>"}, {"", ""},
-       {"spmv_line_kernel<8, 1, 8, 4, true, 2>", "spmv_line_kernel<8, 2, 8, 4, true, 2>"}},
-      {{"spmv_line_kernel<16, 1, 8, 4, true, 0>", "spmv_line_kernel<16, 2, 8, 4, true, 0>"}, {"", ""},
-       {"spmv_line_kernel<16, 1, 8, 4, true, 3>", "spmv_line_kernel<16, 2, 8, 4, true, 3>"}},
+  (void)rows;
+  // one string per (pattern, decoder): the template arguments of
+  // spmv_kernel<N, BATCH, NTV, DEC> as profilers print them
+  static const char* const names[4][4] = {
+      {"spmv_kernel<2, 4, true, 0>", "spmv_kernel<2, 4, true, 1>", "", ""},
+      {"spmv_kernel<4, 4, true, 0>", "", "spmv_kernel<4, 4, true, 2>", ""},
+      {"spmv_kernel<8, 4, true, 0>", "", "spmv_kernel<8, 4, true, 2>", ""},
+      {"spmv_kernel<16, 4, true, 0>", "", "", "spmv_kernel<16, 4, true, 3>"},
   };
   static_assert(kBatch == 4 && kNTV, "variant names spell BATCH = 4 and NTV = true");
   const int pi = N == 2 ? 0 : N == 4 ? 1 : N == 8 ? 2 : 3;
-  const int di = N == 2 ? (use_pair_table(N, cols, dev) ? 1 : 0)
-               : (N == 4 || N == 8) ? (use_byte_lut(cols, dev) ? 2 : 0)
-                                    : (use_rev_walk(cols, dev) ? 2 : 0);
-  return names[pi][di][rows <= kNarrowRows ? 0 : 1];
+  return names[pi][pick_decoder(N, cols, dev)];
 }
 
 hipError_t launch_spmv(const uint16_t* values, const uint32_t* masks, const uint16_t* x,
@@ -83,20 +109,21 @@ hipError_t launch_spmv(const uint16_t* values, const uint32_t* masks, const uint
                        const DeviceInfo& dev) {
   (void)M;  // validated together with N: M == 2 * N
   const int r = int(rows), c = int(cols);
+  const WorkgroupShape s = spmv_shape(rows, cols, dev);
+  const int dec = pick_decoder(N, cols, dev);
   switch (N) {
     case 2:
-      // 2:4 uses the x pair table (6 bytes of LDS per column) whenever it fits
-      if (use_pair_table(N, cols, dev)) return launch_shape<2, kPairTable>(values, masks, x, y, r, c, stream, dev);
-      return launch_shape<2, kBitWalk>(values, masks, x, y, r, c, stream, dev);
+      if (dec == kPairTable) return launch_kernel<2, kPairTable>(values, masks, x, y, r, c, s, stream, dev);
+      return launch_kernel<2, kBitWalk>(values, masks, x, y, r, c, s, stream, dev);
     case 4:
-      if (use_byte_lut(cols, dev)) return launch_shape<4, kByteLut>(values, masks, x, y, r, c, stream, dev);
-      return launch_shape<4, kBitWalk>(values, masks, x, y, r, c, stream, dev);
+      if (dec == kByteLut) return launch_kernel<4, kByteLut>(values, masks, x, y, r, c, s, stream, dev);
+      return launch_kernel<4, kBitWalk>(values, masks, x, y, r, c, s, stream, dev);
     case 8:
-      if (use_byte_lut(cols, dev)) return launch_shape<8, kByteLut>(values, masks, x, y, r, c, stream, dev);
-      return launch_shape<8, kBitWalk>(values, masks, x, y, r, c, stream, dev);
+      if (dec == kByteLut) return launch_kernel<8, kByteLut>(values, masks, x, y, r, c, s, stream, dev);
+      return launch_kernel<8, kBitWalk>(values, masks, x, y, r, c, s, stream, dev);
     case 16:
-      if (use_rev_walk(cols, dev)) return launch_shape<16, kRevWalk>(values, masks, x, y, r, c, stream, dev);
-      return launch_shape<16, kBitWalk>(values, masks, x, y, r, c, stream, dev);
+      if (dec == kRevWalk) return launch_kernel<16, kRevWalk>(values, masks, x, y, r, c, s, stream, dev);
+      return launch_kernel<16, kBitWalk>(values, masks, x, y, r, c, s, stream, dev);
     default: return hipErrorInvalidValue;
   }
 }

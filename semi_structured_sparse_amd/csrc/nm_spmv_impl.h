@@ -8,7 +8,7 @@
 // word w start at a fixed offset 16*w and the traversal of a word is a fixed number
 // of steps with no prefix scan.
 //
-// Work mapping (spmv_line_kernel below): a workgroup covers 8*RG rows x all columns;
+// Work mapping (spmv_kernel below): a workgroup covers 8*RG rows x all columns;
 // its RG*CS waves take RG groups of 8 rows, and CS waves split each row group's
 // columns into contiguous ranges. In one "step" the 8 lanes of a row each load 16 bytes
 // (8 values, half a mask word) of the row's next 128-byte line of packed values (4 mask
@@ -212,27 +212,8 @@ __device__ __forceinline__ void stage_byte_lut(uint2* lut, int tid, int nthreads
 
 // ---------------------------------------------------------------- pair-table decoder
 // Slot of a 2:4 nibble n in its group's 6 pairs: (n >> 1) - 1, i.e. 0..5 for
-// n = 3 (cols 0,1), 5 (0,2), 6 (1,2), 9 (0,3), 10 (1,3), 12 (2,3).
-__device__ __forceinline__ void stage_pair_table(const uint4* __restrict__ x, uint32_t* __restrict__ tbl,
-                                                 int cols, int tid, int nthreads) {
-  const int pairs_of_groups = cols >> 3;  // 8 columns = 2 groups per uint4 of x
-  for (int i = tid; i < pairs_of_groups; i += nthreads) {
-    const uint4 v = x[i];
-    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
-      const uint32_t lo = d[2 * gg], hi = d[2 * gg + 1];  // (x0, x1), (x2, x3)
-      const uint32_t x0 = lo & 0xFFFFu, x1 = lo >> 16, x2 = hi & 0xFFFFu, x3 = hi >> 16;
-      uint32_t* t = tbl + 6 * (2 * i + gg);
-      t[0] = lo;                   // n = 3:  (x0, x1)
-      t[1] = x0 | (x2 << 16);      // n = 5:  (x0, x2)
-      t[2] = x1 | (x2 << 16);      // n = 6:  (x1, x2)
-      t[3] = x0 | (x3 << 16);      // n = 9:  (x0, x3)
-      t[4] = x1 | (x3 << 16);      // n = 10: (x1, x3)
-      t[5] = hi;                   // n = 12: (x2, x3)
-    }
-  }
-}
+// n = 3 (cols 0,1), 5 (0,2), 6 (1,2), 9 (0,3), 10 (1,3), 12 (2,3). The table itself is
+// written by store_x_chunk.
 
 // ---------------------------------------------------------------- batches
 // One batch of BATCH steps for one lane. Per step the lane's values advance VSTEP uint4s,
@@ -241,6 +222,19 @@ template <int BATCH, bool NTV, int VSTEP, int MSTEP, int TSTEP, int XSTEP>
 struct Batch {
   uint4 v[BATCH];
   uint32_t m[BATCH];
+
+  // Loads a whole batch unconditionally, every offset clamped to the row's last uint4 of
+  // values (vlast) and last mask word (mlast): when the batch lies inside the row the
+  // clamps change nothing; otherwise the lane reads valid data it will not use. Being
+  // branch-free, these loads let the compiler wait for earlier loads with an exact count.
+  __device__ __forceinline__ void load_clamped(const uint4* __restrict__ vrow, unsigned vo, unsigned vlast,
+                                               const uint32_t* __restrict__ mrow, unsigned mo, unsigned mlast) {
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      v[i] = load16<NTV>(vrow + min(vo + unsigned(VSTEP * i), vlast));
+      m[i] = mrow[min(mo + unsigned(MSTEP * i), mlast)];
+    }
+  }
 
   // Loads `count` steps starting at vp / mp (count == BATCH: no guards). Values may be
   // nontemporal (NTV); masks are plain loads (a mask line is shared by several steps).
@@ -337,91 +331,114 @@ struct Batch {
   }
 };
 
-// Stages x (bit walk) or its pair table in the LDS data region.
+// Writes chunk i of x (elements 8i..8i+7, one uint4) into the LDS data region in the
+// decoder's form: the plain copy; for the pair table the 6 x pairs of each of its two
+// 4-column groups; for the reversed walk also the reversed copy, in which quarter q of
+// every mask word's 32 elements holds quarter 3 - q of x, elements reversed.
 template <int DEC>
-__device__ __forceinline__ void stage_x(const uint4* __restrict__ x, char* data, int cols, int tid, int nthreads) {
+__device__ __forceinline__ void store_x_chunk(uint4 v, int i, char* data, int cols) {
   if constexpr (DEC == kPairTable) {
-    stage_pair_table(x, reinterpret_cast<uint32_t*>(data), cols, tid, nthreads);
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg) {
+      const uint32_t lo = d[2 * gg], hi = d[2 * gg + 1];  // (x0, x1), (x2, x3)
+      const uint32_t x0 = lo & 0xFFFFu, x1 = lo >> 16, x2 = hi & 0xFFFFu, x3 = hi >> 16;
+      uint32_t* t = reinterpret_cast<uint32_t*>(data) + 6 * (2 * i + gg);
+      t[0] = lo;                   // n = 3:  (x0, x1)
+      t[1] = x0 | (x2 << 16);      // n = 5:  (x0, x2)
+      t[2] = x1 | (x2 << 16);      // n = 6:  (x1, x2)
+      t[3] = x0 | (x3 << 16);      // n = 9:  (x0, x3)
+      t[4] = x1 | (x3 << 16);      // n = 10: (x1, x3)
+      t[5] = hi;                   // n = 12: (x2, x3)
+    }
   } else {
-    uint4* xs4 = reinterpret_cast<uint4*>(data);
-    const int n16 = cols >> 3;
-    for (int i = tid; i < n16; i += nthreads) xs4[i] = x[i];
-    if constexpr (DEC == kByteLut) stage_byte_lut(reinterpret_cast<uint2*>(data + size_t(cols) * 2), tid, nthreads);
+    reinterpret_cast<uint4*>(data)[i] = v;
     if constexpr (DEC == kRevWalk) {
-      // reversed copy: quarter q of word w = quarter 3 - q of x's word w, elements reversed
-      uint4* xr4 = reinterpret_cast<uint4*>(data + size_t(cols) * 2);
-      for (int i = tid; i < n16; i += nthreads) {
-        const uint4 a = x[(i & ~3) | (3 - (i & 3))];
-        xr4[i] = make_uint4(__builtin_amdgcn_alignbit(a.w, a.w, 16), __builtin_amdgcn_alignbit(a.z, a.z, 16),
-                            __builtin_amdgcn_alignbit(a.y, a.y, 16), __builtin_amdgcn_alignbit(a.x, a.x, 16));
-      }
+      const int j = (i & ~3) | (3 - (i & 3));  // the quarter that mirrors chunk i in its word
+      reinterpret_cast<uint4*>(data + size_t(cols) * 2)[j] =
+          make_uint4(__builtin_amdgcn_alignbit(v.w, v.w, 16), __builtin_amdgcn_alignbit(v.z, v.z, 16),
+                     __builtin_amdgcn_alignbit(v.y, v.y, 16), __builtin_amdgcn_alignbit(v.x, v.x, 16));
     }
   }
+  (void)cols;
 }
 
-// ---------------------------------------------------------------- full-line variant
-// Same method, with 8 lanes per row: in one step the 8 lanes of a row load the row's next
-// 128 bytes of packed values (one whole cache line, 4 mask words = 128 columns), so every
-// line is consumed by a single wave instruction and the values can be streamed with
-// nontemporal loads (NTV). A wave instruction covers 8 rows. Lanes are ordered so that
-// each half-wave holds the same half of every row's line: lanes 4r..4r+3 take half-words
-// 0..3 (words 0, 1) of row r and lanes 32+4r..32+4r+3 half-words 4..7 (words 2, 3), so
-// the LDS reads of a half-wave touch only 2 consecutive mask words' x data (32 dwords:
-// no bank conflicts for the bit walk; 8 table groups for the pair table).
-// A workgroup has RG row groups of 8 rows and CS waves splitting the columns of each row
-// group (RG*CS waves). Row sums: DPP inside the quad, a swap across the half-waves, then
-// LDS across the CS waves, in a fixed order.
+// ---------------------------------------------------------------- kernel
+// 8 lanes per row: in one step the 8 lanes of a row load the row's next 128 bytes of
+// packed values (one whole cache line, 4 mask words = 128 columns), so every line is
+// consumed by a single wave instruction and the values can be streamed with nontemporal
+// loads (NTV). A wave instruction covers 8 rows. Lanes are ordered so that each half-wave
+// holds the same half of every row's line: lanes 4r..4r+3 take half-words 0..3 (words 0,
+// 1) of row r and lanes 32+4r..32+4r+3 half-words 4..7 (words 2, 3), so the LDS reads of
+// a half-wave touch only 2 consecutive mask words' x data (no bank conflicts for the bit
+// walk; 8 table groups for the pair table).
+//
 // Sum over the 8 lanes of a row (lanes 4r..4r+3 and 32+4r..32+4r+3): DPP inside the
-// quad, then the partner half-wave's quad (lane ^ 32) through ds_swizzle-free bpermute.
+// quad, then the partner half-wave's quad (lane ^ 32).
 __device__ __forceinline__ float row8_sum(float v) {
   v = dpp_quad_sum(v);
   v += __shfl_xor(v, 32);
   return v;
 }
 
-constexpr size_t line_reduction_bytes(int waves) { return size_t(waves) * 8 * sizeof(float); }
-constexpr int line_data_offset(int waves) { return int(line_reduction_bytes(waves)) + kPad; }
+constexpr int kMaxWaves = 16;  // 1024 threads per workgroup at most
+constexpr size_t kReductionBytes = size_t(kMaxWaves) * 8 * sizeof(float);
+constexpr int kDataOffset = int(kReductionBytes) + kPad;
 
 template <int DEC>
-constexpr size_t line_lds_bytes(int cols, int waves) {
-  return size_t(line_data_offset(waves)) + data_bytes<DEC>(cols) + kPad;
+constexpr size_t lds_bytes(int cols) {
+  return size_t(kDataOffset) + data_bytes<DEC>(cols) + kPad;
 }
 
+// Workgroup shape, chosen per launch: the workgroup owns `rpb` consecutive rows (any
+// count; the grid is ceil(rows / rpb)), split into RG = ceil(rpb / 8) groups of 8 rows;
+// each group has `cs` waves that split the columns into contiguous ranges of whole steps
+// (blockDim.x == 64 * RG * cs <= 1024). Lanes of rows past the workgroup's last row load
+// that last row again (same addresses, no extra memory traffic) and their sums are dropped.
+// Row sums: DPP inside the quad, the partner half-wave, then the cs waves in LDS in a
+// fixed order.
+//
 // Register budget: 64 VGPRs, so that 8 waves fit on each SIMD (two 16-wave workgroups per
 // CU). At 65..72 VGPRs only 7 fit and a CU holds a single 16-wave workgroup, which leaves
 // nothing to overlap one workgroup's staging of x and its final reduction with.
-template <int N, int RG, int CS, int BATCH, bool NTV, int DEC>
-__global__ __launch_bounds__(64 * RG * CS) __attribute__((amdgpu_waves_per_eu(8))) void spmv_line_kernel(const uint4* __restrict__ values,
-                                                                 const uint32_t* __restrict__ masks,
-                                                                 const uint4* __restrict__ x,
-                                                                 uint16_t* __restrict__ y, int rows, int cols) {
+//
+// Order of the prologue: each thread first loads its (up to two) chunks of x, then the
+// first batch of its values, and only then writes x to LDS, so that the wait for x does
+// not include the wait for the value batch (loads complete in order) and the staging
+// overlaps the value stream.
+template <int N, int BATCH, bool NTV, int DEC>
+__global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(8))) void spmv_kernel(
+    const uint4* __restrict__ values, const uint32_t* __restrict__ masks, const uint4* __restrict__ x,
+    uint16_t* __restrict__ y, int rows, int cols, int rpb, int cs_count) {
   static_assert((DEC != kPairTable || N == 2) && (DEC != kByteLut || N == 4 || N == 8) &&
                     (DEC != kRevWalk || N == 16),
                 "pair table: 2:4 only; byte LUT: 4:8 and 8:16 only; reversed walk: 16:32 only");
-  constexpr int WAVES = RG * CS;
-  constexpr int ROWS = 8 * RG;
   extern __shared__ uint4 lds[];
   char* lds_b = reinterpret_cast<char*>(lds);
   float* red = reinterpret_cast<float*>(lds_b);
-  char* data = lds_b + line_data_offset(WAVES);
+  char* data = lds_b + kDataOffset;
 
   const int tid = threadIdx.x;
+  const int nthreads = blockDim.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rg = wave / CS;
+  const int CS = __builtin_amdgcn_readfirstlane(cs_count);
+  const int rg = __builtin_amdgcn_readfirstlane(int(unsigned(wave) / unsigned(CS)));
   const int cs = wave - rg * CS;
   const int rsub = (lane & 31) >> 2;               // row within the wave's 8 rows
   const int u = ((lane >> 5) << 2) | (lane & 3);   // half-word u of the step's 8
   const int half = u & 1;
-  const int wsel = u >> 1;         // which of the step's 4 words
-  const int row0 = blockIdx.x * ROWS;
-  const unsigned r = unsigned(min(row0 + 8 * rg + rsub, rows - 1));
+  const int wsel = u >> 1;                         // which of the step's 4 words
+  const int row0 = blockIdx.x * rpb;
+  const int row_end = min(row0 + rpb, rows);
+  const unsigned r = unsigned(min(row0 + 8 * rg + rsub, row_end - 1));
 
   const int words = cols >> 5;
   const int steps = (words + 3) >> 2;
   const int full_steps = words >> 2;
-  const int s_beg = int((int64_t(steps) * cs) / CS);
-  const int s_end = int((int64_t(steps) * (cs + 1)) / CS);
+  // steps * (cs + 1) < 2^23 * 16: 32-bit arithmetic is exact (cols <= 2^30)
+  const int s_beg = int(unsigned(steps) * unsigned(cs) / unsigned(CS));
+  const int s_end = int(unsigned(steps) * unsigned(cs + 1) / unsigned(CS));
   const int s_main = min(s_end, full_steps);
 
   const uint4* __restrict__ vrow = values + size_t(r) * unsigned(cols >> 4);
@@ -434,11 +451,23 @@ __global__ __launch_bounds__(64 * RG * CS) __attribute__((amdgpu_waves_per_eu(8)
   const int nfull = n / BATCH;
   const int rem = n - nfull * BATCH;
 
+  // prologue: x chunks, then the first value batch, then the LDS writes (all loads
+  // unconditional, see load_clamped)
+  const int n16 = cols >> 3;
+  const int i0 = tid, i1 = tid + nthreads;
+  const bool two_chunks = n16 > nthreads;  // workgroup-uniform
+  const uint4 x0 = x[min(i0, n16 - 1)];
+  uint4 x1 = make_uint4(0u, 0u, 0u, 0u);
+  if (two_chunks) x1 = x[min(i1, n16 - 1)];
+  __builtin_amdgcn_sched_barrier(0);  // keep the x loads ahead of the value batch
   using B = Batch<BATCH, NTV, 8, 4, 768, 256>;
   B A;
-  if (nfull > 0) A.load(vp, mp, BATCH);  // first batch in flight while x is staged
-
-  stage_x<DEC>(x, data, cols, tid, 64 * WAVES);
+  A.load_clamped(vrow, 8u * unsigned(s_beg) + unsigned(u), unsigned(cols >> 4) - 1u, mrow,
+                 4u * unsigned(s_beg) + unsigned(wsel), unsigned(words) - 1u);
+  if constexpr (DEC == kByteLut) stage_byte_lut(reinterpret_cast<uint2*>(data + size_t(cols) * 2), tid, nthreads);
+  if (i0 < n16) store_x_chunk<DEC>(x0, i0, data, cols);
+  if (two_chunks && i1 < n16) store_x_chunk<DEC>(x1, i1, data, cols);
+  for (int i = i1 + nthreads; i < n16; i += nthreads) store_x_chunk<DEC>(x[i], i, data, cols);
   __syncthreads();
 
   uint32_t xw = lds_address(data) + 256u * unsigned(s_beg) + 64u * unsigned(wsel);
@@ -485,13 +514,11 @@ __global__ __launch_bounds__(64 * RG * CS) __attribute__((amdgpu_waves_per_eu(8)
   acc = row8_sum(acc);
   if (u == 0) red[wave * 8 + rsub] = acc;
   __syncthreads();
-  if (tid < ROWS) {
+  if (tid < row_end - row0) {
     const int trg = tid >> 3, trow = tid & 7;
     float t = 0.f;
-#pragma unroll
     for (int k = 0; k < CS; ++k) t += red[(trg * CS + k) * 8 + trow];
-    const int rr = row0 + tid;
-    if (rr < rows) y[rr] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(t));
+    y[row0 + tid] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(t));
   }
 }
 

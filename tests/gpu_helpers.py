@@ -40,12 +40,27 @@ def down_f16(t) -> np.ndarray:
     return t.cpu().numpy().view(np.float16)
 
 
-def sample_rows(rows: int, k: int = 48, seed: int = 0) -> np.ndarray:
-    """First, last, a row at each 16-row tile edge, and k random rows (sorted, unique)."""
+def sample_rows(rows: int, k: int = 48, seed: int = 0, rpb: int | None = None) -> np.ndarray:
+    """First, last, the rows on both sides of the first and last workgroup edges (rpb rows
+    per workgroup; 16 if not given), and k random rows (sorted, unique)."""
     rng = np.random.default_rng(seed)
-    pick = {0, rows - 1, min(rows - 1, 15), min(rows - 1, 16), rows // 2}
+    t = rpb or 16
+    last0 = (rows - 1) // t * t                   # first row of the last workgroup
+    pick = {0, rows - 1, rows // 2, t - 1, t, last0 - 1, last0, last0 + 7, last0 + 8}
     pick |= set(rng.integers(0, rows, size=min(k, rows)).tolist())
-    return np.array(sorted(pick), dtype=np.int64)
+    return np.array(sorted(p for p in pick if 0 <= p < rows), dtype=np.int64)
+
+
+def check_launch_shape(rows: int, cols: int, N: int, M: int) -> dict:
+    """The workgroup shape nm_spmv reports covers every row exactly once and fits a
+    workgroup (at most 16 waves)."""
+    s = nm.spmv_launch_shape(rows, cols, N, M)
+    rpb, rg, cs, g = s["rows_per_workgroup"], s["row_groups"], s["waves_per_row_group"], s["workgroups"]
+    assert rpb >= 1 and cs >= 1, s
+    assert rg == -(-rpb // 8), s
+    assert rg * cs <= 16, s
+    assert g == -(-rows // rpb), s
+    return s
 
 
 def check_full_layer(W_host: np.ndarray, x_host: np.ndarray, N: int, M: int, tag: str,
@@ -53,13 +68,14 @@ def check_full_layer(W_host: np.ndarray, x_host: np.ndarray, N: int, M: int, tag
     """Pack on the GPU, run the sparse (and dense) product, and compare sampled rows with
     the oracle: pack bit-exact, y within tolerance. Returns the parity figures."""
     rows, cols = W_host.shape
+    shape = check_launch_shape(rows, cols, N, M)
     Wd = up_f16(W_host)
     xd = up_f16(x_host)
     values, masks = nm.nm_pack(Wd, N, M)
     y = nm.nm_spmv(values, masks, xd, N, M)
     yd = nm.nm_gemv_dense(Wd, xd) if check_dense else None
     torch.cuda.synchronize()
-    idx = sample_rows(rows)
+    idx = sample_rows(rows, rpb=shape["rows_per_workgroup"])
     it = torch.from_numpy(idx).to(device())
     gv = down_bits16(values.index_select(0, it))
     gm = down_u32(masks.index_select(0, it))

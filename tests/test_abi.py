@@ -125,6 +125,16 @@ def test_probe_validation():
     assert L.nm_probe_copy(A16 + 4, A16, 16, None) == nm.NM_ERR_ALIGN
 
 
+def test_launch_shape_validation():
+    """nm_spmv_launch_shape validates like nm_spmv, before any HIP call."""
+    L = nm.lib()
+    buf = (ctypes.c_int64 * 4)()
+    assert L.nm_spmv_launch_shape(64, 128, 2, 4, None) == nm.NM_ERR_NULL
+    assert L.nm_spmv_launch_shape(0, 128, 2, 4, buf) == nm.NM_ERR_SHAPE
+    assert L.nm_spmv_launch_shape(64, 80, 2, 4, buf) == nm.NM_ERR_SHAPE
+    assert L.nm_spmv_launch_shape(64, 128, 3, 4, buf) == nm.NM_ERR_PATTERN
+
+
 def test_python_layer_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     W = torch.zeros(16, 64, dtype=torch.float16)

@@ -19,8 +19,8 @@ PATTERNS = synth.PATTERNS
 
 # small shapes the oracle finishes fast: 1, 2 and 3 mask words (a ragged last step of
 # 128 columns), word counts of 4k+1, 4k+2 and 4k+3 after full steps, row counts that are
-# not multiples of the row tiles, several tiles, and both workgroup shapes (more and
-# fewer than 2048 rows)
+# not multiples of the workgroup's rows, several workgroups, and layers with fewer and
+# more than 8 rows per CU
 SMALL = [(1, 32), (3, 64), (17, 96), (5, 160), (9, 192), (7, 224), (37, 544), (16, 4096),
          (100, 2080), (256, 512), (33, 1056), (2100, 96), (2064, 160)]
 
@@ -64,6 +64,23 @@ def test_gemv_small():
         y = nm.nm_gemv_dense(up_f16(W), up_f16(x))
         rep = oracle.y_tolerance_report(down_f16(y), oracle.gemv_ref(W, x))
         assert rep["ok"], ((R, C), rep)
+
+
+# one or more shapes in each regime of the workgroup-shape rule: narrow layers (at most
+# 8 rows per CU), regular rows, long rows (more than 64 steps of 128 columns) in one and
+# in two rounds; ragged row counts (the last workgroup holds fewer rows than its row
+# groups cover) and ragged column counts (a last step of 1..3 mask words)
+REGIMES = [(255, 4096), (2048, 1024), (1500, 2080), (2049, 512), (5121, 4096), (300, 8320),
+           (777, 16416), (10241, 8320)]
+
+
+@pytest.mark.parametrize("N,M", PATTERNS)
+def test_workgroup_regimes(N, M):
+    for i, (R, C) in enumerate(REGIMES):
+        say(f"regime {R}x{C} {N}:{M} {nm.spmv_launch_shape(R, C, N, M)}")
+        W = synth.weight(R, C, seed=800 + i)
+        x = synth.activation(C, seed=850 + i)
+        check_full_layer(W, x, N, M, f"regime-{R}x{C}", check_dense=(N == 2))
 
 
 def test_config1_single_24():
