@@ -32,7 +32,7 @@ if ROOT not in sys.path:
 METRIC = "N:M SpMV effective HBM GB/s (% of peak) + speedup vs dense GEMV, batch 1"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak, 8 TB/s
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "nm_spmv_counters.txt")
-WORKLOAD_BY_NAME = {"llama8b": 2, "qwen3": 3, "llama70b": 4}
+WORKLOAD_BY_NAME = {"llama8b": 2, "qwen3": 3, "llama70b": 4, "decode": 5}
 COPY_CAL_BYTES = 256 << 20  # size of the counter-calibration copy
 
 
@@ -48,8 +48,10 @@ def parse_args():
     ap.add_argument("--workload", choices=sorted(WORKLOAD_BY_NAME), default="llama8b")
     ap.add_argument("--pool-gib", type=float, default=1.0,
                     help="minimum bytes read between two reads of the same copy")
-    ap.add_argument("--cpu-rows-frac", type=float, default=0.5,
+    ap.add_argument("--cpu-rows-frac", type=float, default=1.0,
                     help="fraction of each layer's rows the CPU oracle baseline processes")
+    ap.add_argument("--tokens", type=int, default=20,
+                    help="decode workload: tokens (passes over the 32 blocks) timed per graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--patterns", default="", help="restrict to patterns, e.g. 2:4,16:32")
     return ap.parse_args()
@@ -68,10 +70,16 @@ KERNEL_SOURCES = [os.path.join(ROOT, "semi_structured_sparse_amd", "csrc", f)
 
 
 def kernel_source_sha():
+    """Hash of the SpMV kernel sources with comments and blank space removed, so that
+    only a change of code (not of its comments) voids the committed counter figures."""
+    import re
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
@@ -130,6 +138,8 @@ def main():
     nm.lib()  # fail loudly if the HIP library is missing
 
     cfg = WORKLOAD_BY_NAME[args.workload]
+    if cfg == 5:
+        return decode_main(args, torch, nm, synth, dev)
     wl = synth.WORKLOADS[cfg]
     pats = [tuple(p) for p in wl["patterns"]]
     if args.patterns:
@@ -327,8 +337,11 @@ def main():
         kern_n[kname] = kern_n.get(kname, 0) + 1
         dus = per_d[(L["R"], L["C"])]
         gbps = L["bytes"] / (us * 1e-6) / 1e9
+        ls = nm.spmv_launch_shape(L["R"], L["C"], L["N"], L["M"])
         per_layer.append({"layer": L["name"], "shape": f"{L['R']}x{L['C']}", "pattern": f"{L['N']}:{L['M']}",
-                          "kernel": kname, "us": round(us, 2), "GBps": round(gbps, 1),
+                          "kernel": kname, "workgroups": ls["workgroups"],
+                          "workgroup": f"{ls['rows_per_workgroup']} rows, {ls['row_groups']}x{ls['waves_per_row_group']} waves",
+                          "us": round(us, 2), "GBps": round(gbps, 1),
                           "pct_peak": round(gbps / HBM_PEAK_GBPS, 4),
                           "dense_us": round(dus, 2), "speedup": round(dus / us, 3)})
     dominant = max(kern_us, key=lambda k: kern_us[k])
@@ -385,45 +398,210 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def decode_main(args, torch, nm, synth, dev):
+    """The Llama-3.1-8B decode sweep: 32 transformer blocks x 7 projections (q, k, v, o,
+    gate, up, down), 2:4, every projection with its own seeded W and x; a step is one
+    token, i.e. one in-order pass over the 224 products. Also timed: the dense GEMV over
+    the same 224 weights, and the same sweep with q/k/v and gate/up each fused into one
+    product over their concatenated rows (the rows of a packed matrix concatenate as they
+    are; the fused product uses the x of q, resp. gate)."""
+    wl = synth.WORKLOADS[5]
+    NB, (N, M) = wl["n_layers"], tuple(wl["patterns"][0])
+    lib = nm.lib()
+    t_gen = time.time()
+    sp, dn, cpu_layers = [], [], []
+    for b in range(NB):
+        for p, (name, R, C) in enumerate(wl["layers"]):
+            W = synth.weight(R, C, synth.decode_seed(b, p))
+            x = synth.activation(C, synth.decode_x_seed(b, p))
+            Wd = torch.from_numpy(W).to(dev)
+            xd = torch.from_numpy(x).to(dev)
+            values, masks = nm.nm_pack(Wd, N, M)
+            y = torch.empty(R, dtype=torch.float16, device=dev)
+            sp.append(dict(name=name, block=b, R=R, C=C, values=values, masks=masks, x=xd, y=y,
+                           bytes=alg_bytes_sparse(R, C, N, M)))
+            dn.append(dict(R=R, C=C, W=Wd, x=xd, y=torch.empty(R, dtype=torch.float16, device=dev),
+                           bytes=alg_bytes_dense(R, C)))
+            if b == 0:
+                cpu_layers.append(dict(name=name, R=R, C=C, N=N, M=M, x_host=x, y=y,
+                                       W_cpu=W[:max(1, int(math.ceil(R * args.cpu_rows_frac)))].copy()))
+            del W
+    # fused q/k/v and gate/up of every block
+    fused = []
+    for b in range(NB):
+        blk = sp[7 * b:7 * b + 7]
+        for idx, xsrc in (((0, 1, 2), 0), ((3,), 3), ((4, 5), 4), ((6,), 6)):
+            parts = [blk[i] for i in idx]
+            R = sum(q["R"] for q in parts)
+            C = parts[0]["C"]
+            v = torch.cat([q["values"] for q in parts]) if len(parts) > 1 else parts[0]["values"]
+            m = torch.cat([q["masks"] for q in parts]) if len(parts) > 1 else parts[0]["masks"]
+            fused.append(dict(R=R, C=C, values=v, masks=m, x=blk[xsrc]["x"],
+                              y=torch.empty(R, dtype=torch.float16, device=dev),
+                              bytes=alg_bytes_sparse(R, C, N, M)))
+    torch.cuda.synchronize()
+    log(f"decode sweep: generated and packed {len(sp)} projections in {time.time() - t_gen:.1f}s")
+
+    def sp_launches(items):
+        return [(q["values"].data_ptr(), q["masks"].data_ptr(), q["x"].data_ptr(), q["y"].data_ptr(),
+                 q["R"], q["C"], N, M) for q in items]
+    sp_a, fu_a = sp_launches(sp), sp_launches(fused)
+    dn_a = [(q["W"].data_ptr(), q["x"].data_ptr(), q["y"].data_ptr(), q["R"], q["C"]) for q in dn]
+
+    def token_sparse(A):
+        def run(sp_):
+            for a in A:
+                st = lib.nm_spmv(*a, sp_)
+                if st:
+                    raise RuntimeError(f"nm_spmv: {nm.status_string(st)}")
+        return run
+
+    def token_dense(sp_):
+        for a in dn_a:
+            st = lib.nm_gemv_dense(*a, sp_)
+            if st:
+                raise RuntimeError(f"nm_gemv_dense: {nm.status_string(st)}")
+
+    def timed_tokens(fn, K, W_):
+        s_ = torch.cuda.current_stream(dev).cuda_stream
+        for _ in range(W_):
+            fn(s_)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream().cuda_stream
+            for _ in range(K):
+                fn(cs)
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            g.replay()
+            b_.record()
+            torch.cuda.synchronize()
+            ts.append(a_.elapsed_time(b_) / K)
+        del g
+        return statistics.median(ts)
+
+    K, Wm = args.tokens, max(1, min(args.warmup, 5))
+    ms_sp = timed_tokens(token_sparse(sp_a), K, Wm)
+    ms_dn = timed_tokens(token_dense, K, Wm)
+    ms_fu = timed_tokens(token_sparse(fu_a), K, Wm)
+    bytes_tok = sum(q["bytes"] for q in sp)
+    bytes_dn = sum(q["bytes"] for q in dn)
+    value = bytes_tok / (ms_sp * 1e-3) / 1e9
+    log(f"decode: sparse {ms_sp * 1e3:.1f} us/token ({value:.0f} GB/s), dense {ms_dn * 1e3:.1f} us/token, "
+        f"fused sparse {ms_fu * 1e3:.1f} us/token, speedup {ms_dn / ms_sp:.3f}x")
+    cpu = None if args.no_cpu_baseline else cpu_baseline(cpu_layers, args.cpu_rows_frac)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms_sp, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "accumulate": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl['name']}: {NB} blocks x 7 Llama-3.1-8B projections, 2:4, batch 1, "
+                               f"a fresh seeded W and x per projection; a step is one token (224 products in order)",
+                   "bytes_per_step": bytes_tok, "parallelism": "single GPU"},
+        "pct_of_peak": round(value / HBM_PEAK_GBPS, 4),
+        "us_per_token": round(ms_sp * 1e3, 2),
+        "dense_us_per_token": round(ms_dn * 1e3, 2),
+        "dense_GBps": round(bytes_dn / (ms_dn * 1e-3) / 1e9, 1),
+        "speedup_vs_dense": round(ms_dn / ms_sp, 3),
+        "fused_qkv_gateup": {"us_per_token": round(ms_fu * 1e3, 2), "launches_per_token": len(fused) // NB * NB,
+                             "GBps": round(sum(q["bytes"] for q in fused) / (ms_fu * 1e-3) / 1e9, 1),
+                             "speedup_vs_dense": round(ms_dn / ms_fu, 3)},
+        "byte_floor_us_per_token_at_8TBps": round(bytes_tok / 8e12 * 1e6, 1),
+        "timing": "K tokens in one HIP graph replayed between events, median of 3 replays",
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(layers, frac):
-    """Time the oracle (as it is) on the first `frac` of every layer's rows, on the host
-    cores; also compare its y with the GPU's for those rows."""
+    """Time the oracle (as it is) on the first `frac` of every layer's rows on the host
+    cores: the rows are cut into chunks that a pool of threads (one per core) hands to
+    oracle.spmv_ref (numpy releases the interpreter lock inside its array operations), with
+    BLAS held to one thread per call. Also: the same oracle on one thread, and the oracle's
+    y compared with the GPU's for those rows."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
 
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
-    t_total, b_total, worst, rel = 0.0, 0, 0.0, 0.0
-    rows_total = 0
-    t_start = time.time()
     try:
         from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=cores)
+        blas_one = threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
-        limiter = None
-    for L in layers:
-        W = L["W_cpu"]
-        nrow = W.shape[0]
-        rv, rm = oracle.pack_ref(W, L["N"], L["M"])          # untimed: oracle input from W only
-        t0 = time.perf_counter()
-        y = oracle.spmv_ref(rv, rm, L["x_host"], L["C"], L["N"], L["M"])
-        t_total += time.perf_counter() - t0
-        b_total += alg_bytes_sparse(nrow, L["C"], L["N"], L["M"])
-        rows_total += nrow
-        gpu_y = L["y"][:nrow].cpu().numpy()
-        rep = oracle.y_tolerance_report(gpu_y, y)
+        blas_one = None
+    t_start = time.time()
+    chunks = []
+    for li, L in enumerate(layers):
+        n = L["W_cpu"].shape[0]
+        step = max(1, min(256, -(-n // cores)))
+        chunks += [(li, a, min(n, a + step)) for a in range(0, n, step)]
+
+    def prep(ch):          # oracle input from W only (untimed)
+        li, a, b = ch
+        L = layers[li]
+        return oracle.pack_ref(L["W_cpu"][a:b], L["N"], L["M"])
+
+    with ThreadPoolExecutor(cores) as ex:
+        packed = list(ex.map(prep, chunks))
+
+    def run(i):
+        li = chunks[i][0]
+        L = layers[li]
+        rv, rm = packed[i]
+        return oracle.spmv_ref(rv, rm, L["x_host"], L["C"], L["N"], L["M"])
+
+    passes = []
+    with ThreadPoolExecutor(cores) as ex:
+        for _ in range(3):       # three timed passes over the sample; the median is reported
+            t0 = time.perf_counter()
+            ys = list(ex.map(run, range(len(chunks))))
+            passes.append(time.perf_counter() - t0)
+    t_total = statistics.median(passes)
+    b_total = sum(alg_bytes_sparse(b - a, layers[li]["C"], layers[li]["N"], layers[li]["M"]) for li, a, b in chunks)
+    rows_total = sum(L["W_cpu"].shape[0] for L in layers)
+    worst, rel = 0.0, 0.0
+    for li, L in enumerate(layers):
+        y = np.concatenate([ys[i] for i, ch in enumerate(chunks) if ch[0] == li])
+        rep = oracle.y_tolerance_report(L["y"][:y.shape[0]].cpu().numpy(), y)
         worst = max(worst, rep["max_err_over_bound"])
         rel = max(rel, rep["rel_l2"])
-    if limiter is not None:
-        limiter.restore_original_limits()
-    log(f"cpu baseline: {b_total / t_total / 1e9:.4f} GB/s over {rows_total} rows in {t_total:.1f}s "
-        f"(leg {time.time() - t_start:.1f}s)")
+    # the same oracle on one thread, over every 16th chunk
+    t1, b1 = 0.0, 0
+    for i in range(0, len(chunks), 16):
+        li, a, b = chunks[i]
+        t0 = time.perf_counter()
+        run(i)
+        t1 += time.perf_counter() - t0
+        b1 += alg_bytes_sparse(b - a, layers[li]["C"], layers[li]["N"], layers[li]["M"])
+    if blas_one is not None:
+        blas_one.restore_original_limits()
+    del packed
+    log(f"cpu baseline: {b_total / t_total / 1e9:.4f} GB/s over {rows_total} rows in {t_total:.1f}s on "
+        f"{cores} threads, {b1 / t1 / 1e9:.4f} GB/s on 1 thread (leg {time.time() - t_start:.1f}s)")
     return {"value": round(b_total / t_total / 1e9, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {frac:g} of the rows of each of the {len(layers)} layers ({rows_total} rows), "
-                      f"densify + fp64 matvec, numpy/BLAS on {cores} threads",
+            "sample": f"first {frac:g} of the rows of each of the {len(layers)} layers ({rows_total} rows) in "
+                      f"{len(chunks)} chunks over {cores} threads; densify + fp64 matvec (numpy); median of 3 passes",
             "seconds": round(t_total, 2), "cpu_model": cpu_info(),
+            "single_thread": {"value": round(b1 / t1 / 1e9, 5), "unit": "GB/s", "seconds": round(t1, 2),
+                              "sample": "every 16th chunk, one thread"},
             "parity_vs_gpu": {"max_err_over_bound": worst, "rel_l2": rel, "ok": worst <= 1.0 and rel <= 1e-3}}
 
 

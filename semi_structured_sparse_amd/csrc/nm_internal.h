@@ -47,9 +47,6 @@ struct WorkgroupShape {
   int64_t grid = 0;
 };
 
-// Shape for `rows` rows of `steps` 128-byte lines each (the streamed bytes of a row / 128).
-WorkgroupShape workgroup_shape(int64_t rows, int64_t steps, const DeviceInfo& dev);
-
 // Name of the kernel configuration launch_spmv picks (static string) and its shape.
 const char* spmv_variant(int64_t rows, int64_t cols, int N, const DeviceInfo& dev);
 WorkgroupShape spmv_shape(int64_t rows, int64_t cols, const DeviceInfo& dev);
