@@ -1,4 +1,5 @@
-"""CPU oracle for the batch-one N:M semi-structured sparse matrix-vector product.
+"""CPU oracle for the batch-one N:M semi-structured sparse matrix-vector product
+(and its small-batch counterpart, the product with B activation vectors).
 
 TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT. Only ``tests/``,
 ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
@@ -19,6 +20,8 @@ from .nm_oracle import (  # noqa: F401
     unpack_ref,
     spmv_ref,
     gemv_ref,
+    spmm_ref,
+    gemm_ref,
     exact_ref,
     fp16_rne,
     y_tolerance_report,

@@ -167,6 +167,31 @@ def gemv_ref(W, x) -> np.ndarray:
     return Wd @ np.asarray(x, dtype=np.float16).astype(np.float64)
 
 
+def spmm_ref(values, masks, X, cols: int, N: int, M: int) -> np.ndarray:
+    """Y (float64, unrounded) [B, rows]: row b is the pruned matrix times row b of X.
+
+    X is fp16 [B, cols], one activation vector per row (the layout of a batch of B
+    tokens). [NEWS-NEW] splits inference into batch-one decoding, dominated by
+    sparse matrix-vector products, and prefill / larger batches, which run sparse
+    matrix-matrix products; for a small batch the same packed matrix is applied to
+    each of the B vectors. Densified and accumulated in fp64, like spmv_ref.
+    """
+    D = unpack_ref(values, masks, cols, N, M).view(np.float16).astype(np.float64)
+    Xf = np.asarray(X, dtype=np.float16).astype(np.float64)
+    if Xf.ndim != 2 or Xf.shape[1] != cols:
+        raise ValueError(f"X must be [B, {cols}], got {Xf.shape}")
+    return Xf @ D.T
+
+
+def gemm_ref(W, X) -> np.ndarray:
+    """Dense Y (float64, unrounded) [B, rows] = X @ W.T: the dense baseline of spmm_ref."""
+    Wd = _as_bits(W).view(np.float16).astype(np.float64)
+    Xf = np.asarray(X, dtype=np.float16).astype(np.float64)
+    if Xf.ndim != 2 or Xf.shape[1] != Wd.shape[1]:
+        raise ValueError(f"X must be [B, {Wd.shape[1]}], got {Xf.shape}")
+    return Xf @ Wd.T
+
+
 def exact_ref(W, x) -> list:
     """Exact y = W @ x as Fractions, for tiny inputs (Python-int brute force).
 

@@ -10,6 +10,8 @@ Sources of the facts (pages cited by title and section):
   fast LLM generation", "What's new": N of every M consecutive weights kept.
   aimodeling.com SparseDecoding article, "The Kernel Is the Other Half of the
   Answer": a 32-bit mask word per 32 columns, exactly 16 set bits at 50%.
+  The small-batch product (B activation vectors against one packed matrix) is the
+  matrix-matrix side of the SpMV / SpMM split the first page draws ("What's new").
 """
 from __future__ import annotations
 
@@ -277,3 +279,86 @@ def check_unit_sum(pack_fn, spmv_fn):
         v, mk = pack_fn(W, n, m)
         y = spmv_fn(v, mk, x, C, n, m)
         assert np.all(y == 32.0), (n, m, y)
+
+
+# ----------------------------------------------------------------------------
+# small-batch product (B activation vectors, one per row of X)
+# ----------------------------------------------------------------------------
+def check_spmm_worked_example(pack_fn, spmm_fn):
+    """The golden row against a batch of hand-checkable vectors: x = c/8 gives the golden
+    exact y; x = ones gives the exact sum of the kept values; a one-hot x = e_c gives
+    w_c if column c is kept and 0 otherwise (all exact in fp64)."""
+    row, x, cases = load_worked_row()
+    W = row.reshape(1, 32)
+    onehots = (0, 9, 22, 31)
+    X = np.zeros((2 + len(onehots), 32), np.float16)
+    X[0] = x
+    X[1] = 1.0
+    for i, c in enumerate(onehots):
+        X[2 + i, c] = 1.0
+    for n, m, mask, vals, y in cases:
+        values, masks = pack_fn(W, n, m)
+        got = np.asarray(spmm_fn(values, masks, X, 32, n, m))
+        assert got.shape == (X.shape[0], 1), got.shape
+        assert float(got[0, 0]) == float(y), (n, m, "x = c/8")
+        total = sum(Fraction(float(v)) for v in vals.astype(np.float64))
+        assert float(got[1, 0]) == float(total), (n, m, "x = ones")
+        for i, c in enumerate(onehots):
+            want = float(row[c]) if (mask >> c) & 1 else 0.0
+            assert float(got[2 + i, 0]) == want, (n, m, "one-hot", c)
+
+
+def check_spmm_bruteforce(pack_fn, spmm_fn, seed=7):
+    """Every row of the batch against nested-loop exact sums over the textbook-pruned
+    matrix, on tiny non-square shapes (B differs from rows, so a transposed result or
+    operand fails)."""
+    rng = np.random.default_rng(seed)
+    for R, C, B in ((1, 32, 2), (3, 64, 3), (7, 96, 5), (2, 64, 8)):
+        for n, m in PATTERNS:
+            W = (rng.standard_normal((R, C)) * 0.5).astype(np.float16)
+            W[0, :4] = np.array([1000.0, -1000.0, 2 ** -24, 3.0], np.float16)
+            X = rng.standard_normal((B, C)).astype(np.float16)
+            X[:, 0] = np.arange(B, dtype=np.float16)          # distinct rows
+            values, masks = pack_fn(W, n, m)
+            got = np.asarray(spmm_fn(values, masks, X, C, n, m))
+            assert got.shape == (B, R), (got.shape, B, R)
+            Wp = textbook_prune_dense(W, n, m)
+            for b in range(B):
+                exact = brute_force_y(Wp, X[b])
+                scale = np.abs(Wp.astype(np.float64)) @ np.abs(X[b].astype(np.float64))
+                for r in range(R):
+                    assert abs(Fraction(float(got[b, r])) - exact[r]) <= \
+                        Fraction(1e-12) * Fraction(float(scale[r]) + 1e-300), (R, C, B, n, m, b, r)
+
+
+def check_spmm_exact_linearity(pack_fn, spmm_fn, seed=8):
+    """With small-integer weights and activations every product and sum is exact in fp64,
+    so the batch product must be exactly linear in X and must permute with the rows of X."""
+    rng = np.random.default_rng(seed)
+    R, C, B = 5, 64, 4
+    W = rng.integers(-8, 9, (R, C)).astype(np.float16)
+    X1 = rng.integers(-4, 5, (B, C)).astype(np.float16)
+    X2 = rng.integers(-4, 5, (B, C)).astype(np.float16)
+    perm = np.array([2, 0, 3, 1])
+    for n, m in PATTERNS:
+        v, mk = pack_fn(W, n, m)
+        y1 = np.asarray(spmm_fn(v, mk, X1, C, n, m))
+        y2 = np.asarray(spmm_fn(v, mk, X2, C, n, m))
+        y12 = np.asarray(spmm_fn(v, mk, (X1 + X2).astype(np.float16), C, n, m))
+        assert np.array_equal(y12, y1 + y2), (n, m)
+        assert np.array_equal(np.asarray(spmm_fn(v, mk, X1[perm], C, n, m)), y1[perm]), (n, m)
+
+
+def check_gemm_bruteforce(gemm_fn, seed=9):
+    """Dense batch product on non-square shapes against nested-loop exact sums."""
+    rng = np.random.default_rng(seed)
+    for R, C, B in ((3, 32, 2), (5, 64, 7), (2, 96, 3)):
+        W = rng.standard_normal((R, C)).astype(np.float16)
+        X = rng.standard_normal((B, C)).astype(np.float16)
+        got = np.asarray(gemm_fn(W, X))
+        assert got.shape == (B, R), got.shape
+        for b in range(B):
+            exact = brute_force_y(W, X[b])
+            scale = np.abs(W.astype(np.float64)) @ np.abs(X[b].astype(np.float64))
+            for r in range(R):
+                assert abs(Fraction(float(got[b, r])) - exact[r]) <= Fraction(1e-12) * Fraction(float(scale[r])), (R, C, B, b, r)

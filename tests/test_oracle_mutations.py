@@ -116,6 +116,46 @@ def exact_drop_scale(W, x):
     return [v * 2 ** 24 for v in res]
 
 
+def spmm_transposed(values, masks, X, cols, N, M):
+    """Returns [rows, B] instead of [B, rows]."""
+    return O.spmm_ref(values, masks, X, cols, N, M).T
+
+
+def spmm_batch_reversed(values, masks, X, cols, N, M):
+    return O.spmm_ref(values, masks, np.asarray(X)[::-1], cols, N, M)
+
+
+def spmm_first_row_only(values, masks, X, cols, N, M):
+    """Applies the first activation vector to every batch row."""
+    X = np.asarray(X)
+    return O.spmm_ref(values, masks, np.repeat(X[:1], X.shape[0], axis=0), cols, N, M)
+
+
+def spmm_fp32_sum(values, masks, X, cols, N, M):
+    D = O.unpack_ref(values, masks, cols, N, M).view(np.float16).astype(np.float32)
+    return (np.asarray(X, np.float16).astype(np.float32) @ D.T).astype(np.float64)
+
+
+def spmm_unpruned_order(values, masks, X, cols, N, M):
+    """Multiplies the packed values by the first cols/2 entries of x (ignores the masks)."""
+    V = np.asarray(values).view(np.float16).astype(np.float64)
+    Xf = np.asarray(X, np.float16).astype(np.float64)
+    return Xf[:, :V.shape[1]] @ V.T
+
+
+def gemm_transposed_operand(W, X):
+    Wd = O._as_bits(W).view(np.float16).astype(np.float64)
+    Xf = np.asarray(X, np.float16).astype(np.float64)
+    return (Wd @ Xf.T).T[:, ::-1]
+
+
+def _spmm_pin_fails(spmm):
+    checks = [lambda: pins.check_spmm_worked_example(O.pack_ref, spmm),
+              lambda: pins.check_spmm_bruteforce(O.pack_ref, spmm),
+              lambda: pins.check_spmm_exact_linearity(O.pack_ref, spmm)]
+    return any(_fails(c) for c in checks)
+
+
 def _fails(fn, *args):
     try:
         fn(*args)
@@ -168,3 +208,15 @@ def test_gemv_mutant_is_caught():
 
 def test_exact_mutant_is_caught():
     assert _fails(pins.check_exact_ref, exact_drop_scale)
+
+
+@pytest.mark.parametrize("mutant", [spmm_transposed, spmm_batch_reversed, spmm_first_row_only,
+                                    spmm_fp32_sum, spmm_unpruned_order])
+def test_spmm_mutant_is_caught(mutant):
+    assert _spmm_pin_fails(mutant), mutant.__name__
+    assert not _spmm_pin_fails(O.spmm_ref)
+
+
+def test_gemm_mutant_is_caught():
+    assert _fails(pins.check_gemm_bruteforce, gemm_transposed_operand)
+    assert not _fails(pins.check_gemm_bruteforce, oracle.gemm_ref)

@@ -105,3 +105,19 @@ def test_tolerance_flags_nonfinite_and_shape():
     assert not oracle.y_within_tolerance(np.array([1, 1, np.nan, 1]), ref)
     with pytest.raises(ValueError):
         oracle.y_tolerance_report(np.ones(3), ref)
+
+
+def test_spmm_worked_example_golden():
+    pins.check_spmm_worked_example(oracle.pack_ref, oracle.spmm_ref)
+
+
+def test_spmm_brute_force():
+    pins.check_spmm_bruteforce(oracle.pack_ref, oracle.spmm_ref)
+
+
+def test_spmm_exact_linearity_and_permutation():
+    pins.check_spmm_exact_linearity(oracle.pack_ref, oracle.spmm_ref)
+
+
+def test_gemm_brute_force():
+    pins.check_gemm_bruteforce(oracle.gemm_ref)
