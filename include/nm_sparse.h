@@ -52,7 +52,8 @@ extern "C" {
 typedef enum {
   NM_OK = 0,
   NM_ERR_NULL = 1,     /* a required pointer is NULL                                   */
-  NM_ERR_SHAPE = 2,    /* rows < 1, cols < 32, cols % 32 != 0, or a size overflows      */
+  NM_ERR_SHAPE = 2,    /* rows < 1, cols < 32, cols % 32 != 0, batch not in 1..8, or a
+                          size overflows                                              */
   NM_ERR_PATTERN = 3,  /* (N, M) not one of (2,4), (4,8), (8,16), (16,32)               */
   NM_ERR_ALIGN = 4,    /* W, values or x not 16-byte aligned; masks not 4-byte; y not 2 */
   NM_ERR_TOO_WIDE = 5, /* 2*cols bytes of x exceed the LDS one workgroup may use        */
@@ -93,6 +94,24 @@ int nm_spmv(const uint16_t* values, const uint32_t* masks, const uint16_t* x, ui
  * y[r] = fp16( sum_c W[r][c] * x[c] ) with fp32 products and sums, fixed order. */
 int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,
                   int64_t rows, int64_t cols, void* stream);
+
+/* Small-batch sparse product (the matrix-matrix side of the SpMV / SpMM split that
+ * [NEWS-NEW] draws: prefill and larger batches run matrix-matrix products), for the same
+ * packed matrix and 1 <= batch <= 8 activation vectors:
+ *   Y[b][r] = fp16( sum_c W'[r][c] * X[b][c] ),  X fp16 [batch][cols], Y fp16 [batch][rows]
+ * (row b of X is one activation vector: the layout of a batch of tokens). Products and
+ * sums fp32, one RNE rounding, fixed summation order (bit-identical run to run). Any
+ * width is accepted: x is staged in LDS in column phases when it does not fit at once.
+ * batch == 1 gives the same result as nm_spmv within the tolerance of the product (it may
+ * use another summation order). X must be 16-byte aligned, Y 2-byte aligned; an invalid
+ * batch is NM_ERR_SHAPE. */
+int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
+            int64_t rows, int64_t cols, int64_t batch, int N, int M, void* stream);
+
+/* Dense counterpart of nm_spmm, the same-GPU baseline of the small-batch product:
+ * Y[b][r] = fp16( sum_c W[r][c] * X[b][c] ) with fp32 products and sums, fixed order. */
+int nm_gemm_dense(const uint16_t* W, const uint16_t* X, uint16_t* Y,
+                  int64_t rows, int64_t cols, int64_t batch, void* stream);
 
 /* Introspection: the name of the kernel configuration nm_spmv launches for this shape
  * and pattern on the current device, as it appears in profiler traces (for example

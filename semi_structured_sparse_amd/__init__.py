@@ -30,6 +30,10 @@ SIGNATURES = {
                            _c.c_int64, _c.c_int, _c.c_int, _c.c_void_p]),
     "nm_gemv_dense": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
                                  _c.c_void_p]),
+    "nm_spmm": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
+                           _c.c_int64, _c.c_int64, _c.c_int, _c.c_int, _c.c_void_p]),
+    "nm_gemm_dense": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
+                                 _c.c_int64, _c.c_void_p]),
     "nm_status_string": (_c.c_char_p, [_c.c_int]),
     "nm_spmv_variant": (_c.c_char_p, [_c.c_int64, _c.c_int64, _c.c_int, _c.c_int]),
     "nm_last_hip_error": (_c.c_int, []),
@@ -207,6 +211,59 @@ def nm_gemv_dense(W, x, out=None):
         st = lib().nm_gemv_dense(W.data_ptr(), x.data_ptr(), out.data_ptr(), rows, cols,
                                  _stream_ptr(x))
     _check("nm_gemv_dense", st)
+    return out
+
+
+def nm_spmm(values, masks, X, N: int, M: int, out=None):
+    """Y = X W'^T for a batch of 1..8 activation vectors: X fp16 [batch, cols] -> Y fp16
+    [batch, rows] (row b of Y is the packed matrix times row b of X)."""
+    torch = _torch()
+    _require(values, "values", torch.float16, 2)
+    _require(masks, "masks", torch.int32, 2)
+    _require(X, "X", torch.float16, 2)
+    rows, words = masks.shape
+    cols = words * 32
+    batch = X.shape[0]
+    if X.shape[1] != cols:
+        raise ValueError(f"X has {X.shape[1]} columns, masks describe {cols}")
+    if (N, M) in PATTERNS and values.shape != (rows, cols * N // M):
+        raise ValueError(f"values shape {tuple(values.shape)} != {(rows, cols * N // M)}")
+    if not (values.device == masks.device == X.device):
+        raise ValueError("values, masks and X must be on one device")
+    if out is None:
+        out = torch.empty((batch, rows), dtype=torch.float16, device=X.device)
+    else:
+        _require(out, "out", torch.float16, 2)
+        if tuple(out.shape) != (batch, rows) or out.device != X.device:
+            raise ValueError("out must be fp16 [batch, rows] on the same device")
+    with torch.cuda.device(X.device):
+        st = lib().nm_spmm(values.data_ptr(), masks.data_ptr(), X.data_ptr(), out.data_ptr(),
+                           rows, cols, batch, N, M, _stream_ptr(X))
+    _check("nm_spmm", st)
+    return out
+
+
+def nm_gemm_dense(W, X, out=None):
+    """Dense baseline Y = X W^T: fp16 W [rows, cols], X [batch, cols] -> Y [batch, rows]."""
+    torch = _torch()
+    _require(W, "W", torch.float16, 2)
+    _require(X, "X", torch.float16, 2)
+    rows, cols = W.shape
+    batch = X.shape[0]
+    if X.shape[1] != cols:
+        raise ValueError(f"X has {X.shape[1]} columns, W has {cols}")
+    if W.device != X.device:
+        raise ValueError("W and X must be on one device")
+    if out is None:
+        out = torch.empty((batch, rows), dtype=torch.float16, device=X.device)
+    else:
+        _require(out, "out", torch.float16, 2)
+        if tuple(out.shape) != (batch, rows) or out.device != X.device:
+            raise ValueError("out must be fp16 [batch, rows] on the same device")
+    with torch.cuda.device(X.device):
+        st = lib().nm_gemm_dense(W.data_ptr(), X.data_ptr(), out.data_ptr(), rows, cols, batch,
+                                 _stream_ptr(X))
+    _check("nm_gemm_dense", st)
     return out
 
 

@@ -141,6 +141,32 @@ int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y, int64_t row
   return e == hipSuccess ? NM_OK : nm::hip_fail(e);
 }
 
+int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
+            int64_t rows, int64_t cols, int64_t batch, int N, int M, void* stream) {
+  if (!values || !masks || !X || !Y) return NM_ERR_NULL;
+  if (!nm::valid_shape(rows, cols) || batch < 1 || batch > 8) return NM_ERR_SHAPE;
+  if (!nm::valid_pattern(N, M)) return NM_ERR_PATTERN;
+  if (!nm::aligned(values, 16) || !nm::aligned(masks, 4) || !nm::aligned(X, 16) || !nm::aligned(Y, 2))
+    return NM_ERR_ALIGN;
+  nm::DeviceInfo dev;
+  hipError_t e = nm::current_device_info(&dev);
+  if (e != hipSuccess) return nm::hip_fail(e);
+  e = nm::launch_spmm(values, masks, X, Y, rows, cols, int(batch), N, M, static_cast<hipStream_t>(stream), dev);
+  return e == hipSuccess ? NM_OK : nm::hip_fail(e);
+}
+
+int nm_gemm_dense(const uint16_t* W, const uint16_t* X, uint16_t* Y, int64_t rows, int64_t cols,
+                  int64_t batch, void* stream) {
+  if (!W || !X || !Y) return NM_ERR_NULL;
+  if (!nm::valid_shape(rows, cols) || batch < 1 || batch > 8) return NM_ERR_SHAPE;
+  if (!nm::aligned(W, 16) || !nm::aligned(X, 16) || !nm::aligned(Y, 2)) return NM_ERR_ALIGN;
+  nm::DeviceInfo dev;
+  hipError_t e = nm::current_device_info(&dev);
+  if (e != hipSuccess) return nm::hip_fail(e);
+  e = nm::launch_gemm(W, X, Y, rows, cols, int(batch), static_cast<hipStream_t>(stream), dev);
+  return e == hipSuccess ? NM_OK : nm::hip_fail(e);
+}
+
 const char* nm_spmv_variant(int64_t rows, int64_t cols, int N, int M) {
   if (!nm::valid_shape(rows, cols) || !nm::valid_pattern(N, M)) return "";
   nm::DeviceInfo dev;
@@ -168,7 +194,7 @@ const char* nm_status_string(int status) {
   switch (status) {
     case NM_OK: return "ok";
     case NM_ERR_NULL: return "a required pointer is NULL";
-    case NM_ERR_SHAPE: return "invalid shape: need rows >= 1, cols >= 32 and cols % 32 == 0 (and sizes that fit)";
+    case NM_ERR_SHAPE: return "invalid shape: need rows >= 1, cols >= 32, cols % 32 == 0, 1 <= batch <= 8 (and sizes that fit)";
     case NM_ERR_PATTERN: return "unsupported N:M pattern: need 2:4, 4:8, 8:16 or 16:32";
     case NM_ERR_ALIGN: return "misaligned pointer: W, values and x need 16 bytes, masks 4, y 2";
     case NM_ERR_TOO_WIDE: return "cols too large: x does not fit in the LDS of one workgroup";

@@ -38,6 +38,8 @@ WorkgroupShape gemv_shape(int64_t rows, int64_t cols, const DeviceInfo& dev) {
 
 }  // namespace
 
+WorkgroupShape dense_shape(int64_t rows, int64_t cols, const DeviceInfo& dev) { return gemv_shape(rows, cols, dev); }
+
 hipError_t launch_gemv(const uint16_t* W, const uint16_t* x, uint16_t* y, int64_t rows,
                        int64_t cols, hipStream_t stream, const DeviceInfo& dev) {
   const WorkgroupShape s = gemv_shape(rows, cols, dev);

@@ -47,9 +47,17 @@ struct WorkgroupShape {
   int64_t grid = 0;
 };
 
+// Small-batch products (1 <= batch <= 8): X [batch][cols], Y [batch][rows].
+hipError_t launch_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X,
+                       uint16_t* Y, int64_t rows, int64_t cols, int batch, int N, int M,
+                       hipStream_t stream, const DeviceInfo& dev);
+hipError_t launch_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y, int64_t rows,
+                       int64_t cols, int batch, hipStream_t stream, const DeviceInfo& dev);
+
 // Name of the kernel configuration launch_spmv picks (static string) and its shape.
 const char* spmv_variant(int64_t rows, int64_t cols, int N, const DeviceInfo& dev);
 WorkgroupShape spmv_shape(int64_t rows, int64_t cols, const DeviceInfo& dev);
+WorkgroupShape dense_shape(int64_t rows, int64_t cols, const DeviceInfo& dev);
 
 // Widest x the SpMV / GEMV kernels can stage for the given device.
 int64_t max_cols_for(const DeviceInfo& dev);

@@ -125,6 +125,29 @@ def test_probe_validation():
     assert L.nm_probe_copy(A16 + 4, A16, 16, None) == nm.NM_ERR_ALIGN
 
 
+@pytest.mark.parametrize("kw,want", [
+    (dict(values=None), nm.NM_ERR_NULL), (dict(X=None), nm.NM_ERR_NULL), (dict(Y=None), nm.NM_ERR_NULL),
+    (dict(batch=0), nm.NM_ERR_SHAPE), (dict(batch=9), nm.NM_ERR_SHAPE), (dict(cols=48), nm.NM_ERR_SHAPE),
+    (dict(N=2, M=8), nm.NM_ERR_PATTERN),
+    (dict(X=A16 + 8), nm.NM_ERR_ALIGN), (dict(Y=A16 + 1), nm.NM_ERR_ALIGN), (dict(masks=A16 + 2), nm.NM_ERR_ALIGN),
+])
+def test_spmm_validation(kw, want):
+    a = dict(values=A16, masks=A16, X=A16, Y=A16, rows=64, cols=128, batch=4, N=2, M=4)
+    a.update(kw)
+    assert nm.lib().nm_spmm(a["values"], a["masks"], a["X"], a["Y"], a["rows"], a["cols"], a["batch"],
+                            a["N"], a["M"], None) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(W=None), nm.NM_ERR_NULL), (dict(batch=0), nm.NM_ERR_SHAPE), (dict(batch=9), nm.NM_ERR_SHAPE),
+    (dict(X=A16 + 2), nm.NM_ERR_ALIGN),
+])
+def test_gemm_validation(kw, want):
+    a = dict(W=A16, X=A16, Y=A16, rows=64, cols=128, batch=2)
+    a.update(kw)
+    assert nm.lib().nm_gemm_dense(a["W"], a["X"], a["Y"], a["rows"], a["cols"], a["batch"], None) == want
+
+
 def test_launch_shape_validation():
     """nm_spmv_launch_shape validates like nm_spmv, before any HIP call."""
     L = nm.lib()
