@@ -54,15 +54,19 @@ def parse_args():
                     help="decode workload: tokens (passes over the 32 blocks) timed per graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--patterns", default="", help="restrict to patterns, e.g. 2:4,16:32")
+    ap.add_argument("--batch", type=int, default=1,
+                    help="activation vectors per product (1: nm_spmv / nm_gemv_dense; 2..8: "
+                         "nm_spmm / nm_gemm_dense)")
     return ap.parse_args()
 
 
-def alg_bytes_sparse(R, C, N, M):
-    return 2 * R * C * N // M + 4 * R * C // 32 + 2 * C + 2 * R
+def alg_bytes_sparse(R, C, N, M, B=1):
+    """values + masks + B activation vectors (x) + B outputs (y)."""
+    return 2 * R * C * N // M + 4 * R * C // 32 + B * (2 * C + 2 * R)
 
 
-def alg_bytes_dense(R, C):
-    return 2 * R * C + 2 * C + 2 * R
+def alg_bytes_dense(R, C, B=1):
+    return 2 * R * C + B * (2 * C + 2 * R)
 
 
 KERNEL_SOURCES = [os.path.join(ROOT, "semi_structured_sparse_amd", "csrc", f)
@@ -142,6 +146,10 @@ def main():
         return decode_main(args, torch, nm, synth, dev)
     wl = synth.WORKLOADS[cfg]
     pats = [tuple(p) for p in wl["patterns"]]
+    B = args.batch
+    if not 1 <= B <= 8:
+        print("--batch must be in 1..8", file=sys.stderr)
+        sys.exit(2)
     if args.patterns:
         want = {tuple(int(v) for v in p.split(":")) for p in args.patterns.split(",")}
         pats = [p for p in pats if p in want]
@@ -156,18 +164,21 @@ def main():
             ws, xs = synth.weight_seed(cfg, li, pat), synth.x_seed(cfg, li, pat)
             W = synth.weight(R, C, ws)
             x = synth.activation(C, xs)
+            if B > 1:  # B activation vectors, one per row; the first is the layer's x
+                x = np.stack([x] + [synth.activation(C, xs + 7919 * b) for b in range(1, B)])
             Wd = torch.from_numpy(W).to(dev)
             xd = torch.from_numpy(x).to(dev)
             values, masks = nm.nm_pack(Wd, N, M)
             ncpu = max(1, int(math.ceil(R * args.cpu_rows_frac)))
+            yshape = (R,) if B == 1 else (B, R)
             layers.append(dict(name=name, R=R, C=C, N=N, M=M, seed_w=ws, seed_x=xs,
                                values=[values], masks=[masks], x=xd, x_host=x,
-                               W_cpu=W[:ncpu].copy(), y=torch.empty(R, dtype=torch.float16, device=dev),
-                               bytes=alg_bytes_sparse(R, C, N, M)))
+                               W_cpu=W[:ncpu].copy(), y=torch.empty(yshape, dtype=torch.float16, device=dev),
+                               bytes=alg_bytes_sparse(R, C, N, M, B)))
             if (R, C) not in dense:
                 dense[(R, C)] = dict(name=name, R=R, C=C, W=[Wd], x=xd,
-                                     y=torch.empty(R, dtype=torch.float16, device=dev),
-                                     bytes=alg_bytes_dense(R, C))
+                                     y=torch.empty(yshape, dtype=torch.float16, device=dev),
+                                     bytes=alg_bytes_dense(R, C, B))
             else:
                 del Wd
             del W
@@ -194,25 +205,28 @@ def main():
 
     # Raw C-ABI calls with pre-built arguments: the Python binding's checks already ran
     # during packing and warm-up; in the timed regions only the library call remains.
+    bx = () if B == 1 else (B,)   # the batch argument of nm_spmm / nm_gemm_dense
+    sp_fn = lib.nm_spmv if B == 1 else lib.nm_spmm
+    dn_fn = lib.nm_gemv_dense if B == 1 else lib.nm_gemm_dense
     sp_args = [[(L["values"][c].data_ptr(), L["masks"][c].data_ptr(), L["x"].data_ptr(), L["y"].data_ptr(),
-                 L["R"], L["C"], L["N"], L["M"]) for c in range(P_s)] for L in layers]
+                 L["R"], L["C"]) + bx + (L["N"], L["M"]) for c in range(P_s)] for L in layers]
     dense_list = list(dense.values())
-    dn_args = [[(D["W"][c].data_ptr(), D["x"].data_ptr(), D["y"].data_ptr(), D["R"], D["C"])
+    dn_args = [[(D["W"][c].data_ptr(), D["x"].data_ptr(), D["y"].data_ptr(), D["R"], D["C"]) + bx
                 for c in range(P_d)] for D in dense_list]
 
     def sparse_step(k, sp):
         c = k % P_s
         for i in range(len(layers)):
-            st = lib.nm_spmv(*sp_args[i][c], sp)
+            st = sp_fn(*sp_args[i][c], sp)
             if st:
-                raise RuntimeError(f"nm_spmv: {nm.status_string(st)}")
+                raise RuntimeError(f"sparse product: {nm.status_string(st)}")
 
     def dense_step(k, sp):
         c = k % P_d
         for i in range(len(dense_list)):
-            st = lib.nm_gemv_dense(*dn_args[i][c], sp)
+            st = dn_fn(*dn_args[i][c], sp)
             if st:
-                raise RuntimeError(f"nm_gemv_dense: {nm.status_string(st)}")
+                raise RuntimeError(f"dense product: {nm.status_string(st)}")
 
     # ------------------------------------------------------------------ read ceiling probe
     probe_buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
@@ -306,14 +320,14 @@ def main():
     for i, L in enumerate(layers):
         pool = layer_pool([L["values"][0], L["masks"][0]], L["bytes"])
         argsets = [(p[0].data_ptr(), p[1].data_ptr(), L["x"].data_ptr(), L["y"].data_ptr(),
-                    L["R"], L["C"], L["N"], L["M"]) for p in pool]
-        per_s.append(per_launch_us(lambda c, sp, A=argsets: lib.nm_spmv(*A[c], sp), len(pool), L_PL))
+                    L["R"], L["C"]) + bx + (L["N"], L["M"]) for p in pool]
+        per_s.append(per_launch_us(lambda c, sp, A=argsets: sp_fn(*A[c], sp), len(pool), L_PL))
         del pool
     per_d = {}
     for D in dense_list:
         pool = layer_pool([D["W"][0]], D["bytes"])
-        argsets = [(p[0].data_ptr(), D["x"].data_ptr(), D["y"].data_ptr(), D["R"], D["C"]) for p in pool]
-        per_d[(D["R"], D["C"])] = per_launch_us(lambda c, sp, A=argsets: lib.nm_gemv_dense(*A[c], sp),
+        argsets = [(p[0].data_ptr(), D["x"].data_ptr(), D["y"].data_ptr(), D["R"], D["C"]) + bx for p in pool]
+        per_d[(D["R"], D["C"])] = per_launch_us(lambda c, sp, A=argsets: dn_fn(*A[c], sp),
                                                 len(pool), L_PL)
         del pool
     torch.cuda.synchronize()
@@ -331,13 +345,14 @@ def main():
     kern_bytes, kern_us, kern_n = {}, {}, {}
     for i, L in enumerate(layers):
         us = per_s[i]
-        kname = nm.spmv_variant(L["R"], L["C"], L["N"], L["M"])
+        kname = nm.spmv_variant(L["R"], L["C"], L["N"], L["M"]) if B == 1 else \
+            f"spmm_kernel<{L['N']}, {B}, {0 if L['N'] == 16 else 2}>"
         kern_bytes[kname] = kern_bytes.get(kname, 0) + L["bytes"]
         kern_us[kname] = kern_us.get(kname, 0.0) + us
         kern_n[kname] = kern_n.get(kname, 0) + 1
         dus = per_d[(L["R"], L["C"])]
         gbps = L["bytes"] / (us * 1e-6) / 1e9
-        ls = nm.spmv_launch_shape(L["R"], L["C"], L["N"], L["M"])
+        ls = nm.spmv_launch_shape(L["R"], L["C"], L["N"], L["M"])   # (batch > 1: before the 768-thread cap)
         per_layer.append({"layer": L["name"], "shape": f"{L['R']}x{L['C']}", "pattern": f"{L['N']}:{L['M']}",
                           "kernel": kname, "workgroups": ls["workgroups"],
                           "workgroup": f"{ls['rows_per_workgroup']} rows, {ls['row_groups']}x{ls['waves_per_row_group']} waves",
@@ -355,7 +370,7 @@ def main():
 
     # ------------------------------------------------------------------ CPU oracle baseline
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and B == 1:
         cpu = cpu_baseline(layers, args.cpu_rows_frac)
 
     out = {
@@ -374,8 +389,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{wl['name']}: {len(wl['layers'])} projection shapes x patterns "
-                        f"{','.join(f'{n}:{m}' for n, m in pats)}, batch 1, fp16 W ~N(0,0.02^2) "
+                        f"{','.join(f'{n}:{m}' for n, m in pats)}, batch {B}, fp16 W ~N(0,0.02^2) "
                         f"magnitude-pruned, x ~N(0,1)",
+            "batch": B,
             "layers": [f"{L['R']}x{L['C']} {L['N']}:{L['M']}" for L in layers],
             "bytes_per_step": step_sparse,
             "pool_copies_sparse": P_s,
