@@ -13,6 +13,8 @@ each one follows.
 """
 from .nm_oracle import (  # noqa: F401
     PATTERNS,
+    PATTERNS_QUARTER,
+    SUPPORTED_PATTERNS,
     magnitude_key,
     keep_ref,
     prune_ref,

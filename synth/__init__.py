@@ -30,7 +30,8 @@ BASE_SEED = 20261008
 WEIGHT_STD = 0.02
 
 PATTERNS = ((2, 4), (4, 8), (8, 16), (16, 32))
-PATTERN_ID = {p: i for i, p in enumerate(PATTERNS)}
+PATTERNS_QUARTER = ((1, 4), (2, 8), (4, 16), (8, 32))   # 25% density, 8 values per mask word
+PATTERN_ID = {p: i for i, p in enumerate(PATTERNS + PATTERNS_QUARTER)}
 
 # Workloads: name -> list of (layer name, rows, cols); rows = output features,
 # cols = input features (W is [out, in] row-major, y = W @ x).

@@ -22,6 +22,7 @@ from fractions import Fraction
 import numpy as np
 
 PATTERNS = ((2, 4), (4, 8), (8, 16), (16, 32))
+PATTERNS_QUARTER = ((1, 4), (2, 8), (4, 16), (8, 32))   # 8 kept values per mask word
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
@@ -71,11 +72,11 @@ def parse_token(tok):
     return np.float16(float(tok))
 
 
-def load_worked_row():
-    """Parse tests/golden/worked_row32.txt."""
+def load_worked_row(name="worked_row32.txt", ncases=4):
+    """Parse a golden worked-row file under tests/golden/."""
     row = x = None
     cases = []
-    with open(os.path.join(GOLDEN, "worked_row32.txt")) as f:
+    with open(os.path.join(GOLDEN, name)) as f:
         for line in f:
             line = line.strip()
             if not line or line.startswith("#"):
@@ -95,16 +96,16 @@ def load_worked_row():
                 vals = np.array([parse_token(v) for v in t[vi + 1:yi]], dtype=np.float16)
                 y = Fraction(t[yi + 1]) + int(t[yi + 2]) * Fraction(2) ** int(t[yi + 3])
                 cases.append((n, m, mask, vals, y))
-    assert row is not None and x is not None and len(row) == 32 and len(cases) == 4
+    assert row is not None and x is not None and len(row) == 32 and len(cases) == ncases
     return row, x, cases
 
 
 # ----------------------------------------------------------------------------
 # checks
 # ----------------------------------------------------------------------------
-def check_worked_example(pack_fn, spmv_fn):
+def check_worked_example(pack_fn, spmv_fn, name="worked_row32.txt"):
     """Hand-worked golden row: masks, value bits and exact y (rounded to fp64)."""
-    row, x, cases = load_worked_row()
+    row, x, cases = load_worked_row(name)
     W = row.reshape(1, 32)
     for n, m, mask, vals, y in cases:
         values, masks = pack_fn(W, n, m)
@@ -115,7 +116,7 @@ def check_worked_example(pack_fn, spmv_fn):
         assert float(got[0]) == float(y), f"{n}:{m} y {got[0]!r} != {float(y)!r}"
 
 
-def check_selection_textbook(keep_fn, seed=1):
+def check_selection_textbook(keep_fn, seed=1, patterns=PATTERNS):
     """keep_fn agrees with the sort-based rule on random groups and on every tie pattern
     of M=4 over a 3-value alphabet (with random signs, including -0)."""
     rng = np.random.default_rng(seed)
@@ -129,7 +130,7 @@ def check_selection_textbook(keep_fn, seed=1):
     pad = (-len(flat)) % 32
     flat = np.concatenate([flat, np.zeros(pad, np.float16)])
     W = flat.reshape(-1, 32)
-    for n, m in PATTERNS:
+    for n, m in patterns:
         kept = keep_fn(W, n, m)
         bits = W.view(np.uint16)
         for r in range(W.shape[0]):
@@ -145,7 +146,7 @@ def check_selection_textbook(keep_fn, seed=1):
         else:
             W = (rng.standard_normal((6, 64)) * 0.02).astype(np.float16)
         W = W.astype(np.float16)
-        for n, m in PATTERNS:
+        for n, m in patterns:
             kept = keep_fn(W, n, m)
             bits = W.view(np.uint16)
             for r in range(W.shape[0]):
@@ -156,15 +157,17 @@ def check_selection_textbook(keep_fn, seed=1):
                     assert got == want, (n, m, keys, got, want)
 
 
-CANON_LOW = {(2, 4): 0x33333333, (4, 8): 0x0F0F0F0F, (8, 16): 0x00FF00FF, (16, 32): 0x0000FFFF}
-CANON_HIGH = {(2, 4): 0xCCCCCCCC, (4, 8): 0xF0F0F0F0, (8, 16): 0xFF00FF00, (16, 32): 0xFFFF0000}
+CANON_LOW = {(2, 4): 0x33333333, (4, 8): 0x0F0F0F0F, (8, 16): 0x00FF00FF, (16, 32): 0x0000FFFF,
+             (1, 4): 0x11111111, (2, 8): 0x03030303, (4, 16): 0x000F000F, (8, 32): 0x000000FF}
+CANON_HIGH = {(2, 4): 0xCCCCCCCC, (4, 8): 0xF0F0F0F0, (8, 16): 0xFF00FF00, (16, 32): 0xFFFF0000,
+              (1, 4): 0x88888888, (2, 8): 0xC0C0C0C0, (4, 16): 0xF000F000, (8, 32): 0xFF000000}
 
 
-def check_canonical_masks(pack_fn):
+def check_canonical_masks(pack_fn, patterns=PATTERNS):
     """Closed forms: equal magnitudes (any signs) or strictly decreasing magnitudes keep
     the N lowest columns of each group; strictly increasing ones keep the N highest."""
     rng = np.random.default_rng(3)
-    for (n, m) in PATTERNS:
+    for (n, m) in patterns:
         eq = np.full((3, 64), 0.75, np.float16)
         eq = np.where(rng.integers(0, 2, eq.shape).astype(bool), -eq, eq).astype(np.float16)
         _, masks = pack_fn(eq, n, m)
@@ -179,15 +182,15 @@ def check_canonical_masks(pack_fn):
         assert np.all(masks == CANON_HIGH[(n, m)]), (n, m, "increasing")
 
 
-def check_invariants(pack_fn, unpack_fn, prune_fn, W):
+def check_invariants(pack_fn, unpack_fn, prune_fn, W, patterns=PATTERNS):
     """Structural invariants of one packed matrix, for every pattern."""
     bits = W.view(np.uint16)
     R, C = W.shape
-    for n, m in PATTERNS:
+    for n, m in patterns:
         values, masks = pack_fn(W, n, m)
         values = np.asarray(values).view(np.uint16)
         assert values.shape == (R, C * n // m) and masks.shape == (R, C // 32)
-        # 16 set bits per word, N per M-bit field
+        # 32*N/M set bits per word, N per M-bit field
         pc = np.array([[bin(int(w)).count("1") for w in row] for row in masks])
         assert np.all(pc == 32 * n // m)
         for f in range(32 // m):
@@ -225,12 +228,12 @@ def check_cross_pattern(pack_fn):
         assert np.array_equal(mk, ref_m)
 
 
-def check_spmv_bruteforce(pack_fn, spmv_fn, seed=5):
+def check_spmv_bruteforce(pack_fn, spmv_fn, seed=5, patterns=PATTERNS):
     """spmv of the packed matrix equals the exact product of the textbook-pruned dense matrix
     (within fp64 summation error) on tiny shapes, for every pattern."""
     rng = np.random.default_rng(seed)
     for R, C in ((1, 32), (2, 64), (3, 96), (7, 64)):
-        for n, m in PATTERNS:
+        for n, m in patterns:
             W = (rng.standard_normal((R, C)) * 0.5).astype(np.float16)
             # adversarial magnitudes: large values, subnormals and cancellation
             W[0, :4] = np.array([1000.0, -1000.0, 2 ** -24, 3.0], np.float16)

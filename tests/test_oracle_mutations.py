@@ -220,3 +220,26 @@ def test_spmm_mutant_is_caught(mutant):
 def test_gemm_mutant_is_caught():
     assert _fails(pins.check_gemm_bruteforce, gemm_transposed_operand)
     assert not _fails(pins.check_gemm_bruteforce, oracle.gemm_ref)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("ties_to_higher_column", dict(keep=keep_ties_high, pack=make_pack(keep_ties_high))),
+    ("keeps_smallest", dict(keep=keep_smallest, pack=make_pack(keep_smallest))),
+    ("mask_bits_reversed", dict(pack=make_pack(reverse_bits=True))),
+    ("values_descending_in_word", dict(pack=make_pack(reverse_values=True))),
+    ("x_reversed", dict(spmv=spmv_x_reversed)),
+])
+def test_quarter_mutant_is_caught(name, kw):
+    """The same slips are caught by the pins of the 25% patterns (8 values per word)."""
+    keep, pack, spmv = kw.get("keep", O.keep_ref), kw.get("pack", O.pack_ref), kw.get("spmv", O.spmv_ref)
+    Q = pins.PATTERNS_QUARTER
+    checks = [lambda: pins.check_worked_example(pack, spmv, name="worked_row32_quarter.txt"),
+              lambda: pins.check_selection_textbook(keep, patterns=Q),
+              lambda: pins.check_canonical_masks(pack, patterns=Q),
+              lambda: pins.check_spmv_bruteforce(pack, spmv, patterns=Q)]
+    assert any(_fails(c) for c in checks), name
+    real = [lambda: pins.check_worked_example(O.pack_ref, O.spmv_ref, name="worked_row32_quarter.txt"),
+            lambda: pins.check_selection_textbook(O.keep_ref, patterns=Q),
+            lambda: pins.check_canonical_masks(O.pack_ref, patterns=Q),
+            lambda: pins.check_spmv_bruteforce(O.pack_ref, O.spmv_ref, patterns=Q)]
+    assert not any(_fails(c) for c in real)

@@ -121,3 +121,26 @@ def test_spmm_exact_linearity_and_permutation():
 
 def test_gemm_brute_force():
     pins.check_gemm_bruteforce(oracle.gemm_ref)
+
+
+# ---------------------------------------------------------------- 25% density (8 values per word)
+def test_quarter_worked_example_golden():
+    pins.check_worked_example(oracle.pack_ref, oracle.spmv_ref, name="worked_row32_quarter.txt")
+
+
+def test_quarter_selection_matches_textbook_sort():
+    pins.check_selection_textbook(oracle.keep_ref, patterns=pins.PATTERNS_QUARTER)
+
+
+def test_quarter_canonical_masks_closed_form():
+    pins.check_canonical_masks(oracle.pack_ref, patterns=pins.PATTERNS_QUARTER)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties"])
+def test_quarter_invariants(kind):
+    W = synth.weight(6, 128, seed=31) if kind == "normal" else synth.tie_heavy_weight(6, 128, seed=32)
+    pins.check_invariants(oracle.pack_ref, oracle.unpack_ref, oracle.prune_ref, W, patterns=pins.PATTERNS_QUARTER)
+
+
+def test_quarter_spmv_brute_force():
+    pins.check_spmv_bruteforce(oracle.pack_ref, oracle.spmv_ref, patterns=pins.PATTERNS_QUARTER)
