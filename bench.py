@@ -53,7 +53,8 @@ def parse_args():
     ap.add_argument("--tokens", type=int, default=20,
                     help="decode workload: tokens (passes over the 32 blocks) timed per graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--patterns", default="", help="restrict to patterns, e.g. 2:4,16:32")
+    ap.add_argument("--patterns", default="", help="patterns to run instead of the workload's, e.g. 2:4,16:32 "
+                                                  "or the 25%% ones 1:4,2:8,4:16,8:32")
     ap.add_argument("--batch", type=int, default=1,
                     help="activation vectors per product (1: nm_spmv / nm_gemv_dense; 2..8: "
                          "nm_spmm / nm_gemm_dense)")
@@ -150,9 +151,12 @@ def main():
     if not 1 <= B <= 8:
         print("--batch must be in 1..8", file=sys.stderr)
         sys.exit(2)
-    if args.patterns:
-        want = {tuple(int(v) for v in p.split(":")) for p in args.patterns.split(",")}
-        pats = [p for p in pats if p in want]
+    if args.patterns:  # any supported patterns, in the order given
+        pats = [tuple(int(v) for v in p.split(":")) for p in args.patterns.split(",")]
+        bad = [p for p in pats if p not in nm.ALL_PATTERNS]
+        if bad:
+            print(f"unsupported patterns {bad}", file=sys.stderr)
+            sys.exit(2)
 
     # ------------------------------------------------------------------ inputs (untimed)
     layers = []   # sparse layers: dict(name, R, C, N, M, values[], masks[], x, y, bytes, cpu rows)

@@ -19,10 +19,13 @@
  * Format (the packed layout every entry point shares):
  *   W        fp16 [rows][cols] row-major (out x in, y = W x), cols % 32 == 0.
  *   masks    uint32 [rows][cols/32]; bit j (LSB = 0) of word w of row r is set iff
- *            W[r][32w + j] is kept. Every word has exactly 32*N/M = 16 set bits and
- *            every aligned group of M columns exactly N.
+ *            W[r][32w + j] is kept. Every word has exactly V = 32*N/M set bits (16 for
+ *            the 50% patterns, 8 for the 25% ones) and every aligned group of M columns
+ *            exactly N.
  *   values   fp16 [rows][cols*N/M]; the kept weights of row r, word by word, in
- *            ascending column order, so word w's values start at 16*w of the row.
+ *            ascending column order, so word w's values start at V*w of the row.
+ *   Patterns: 2:4, 4:8, 8:16, 16:32 (50%, the ones the pages measure) and 1:4, 2:8,
+ *            4:16, 8:32 (25%; [NEWS-NEW] states the method for N:M in general).
  *   x        fp16 [cols];  y  fp16 [rows].
  *   fp16 is passed as its raw bit pattern (uint16_t).
  *
@@ -54,7 +57,8 @@ typedef enum {
   NM_ERR_NULL = 1,     /* a required pointer is NULL                                   */
   NM_ERR_SHAPE = 2,    /* rows < 1, cols < 32, cols % 32 != 0, batch not in 1..8, or a
                           size overflows                                              */
-  NM_ERR_PATTERN = 3,  /* (N, M) not one of (2,4), (4,8), (8,16), (16,32)               */
+  NM_ERR_PATTERN = 3,  /* (N, M) not a supported pattern (nm_spmm, nm_gemm_dense: 50%
+                          patterns for batch > 1)                                    */
   NM_ERR_ALIGN = 4,    /* W, values or x not 16-byte aligned; masks not 4-byte; y not 2 */
   NM_ERR_TOO_WIDE = 5, /* 2*cols bytes of x exceed the LDS one workgroup may use        */
   NM_ERR_HIP = 6       /* a HIP runtime call failed (see nm_last_hip_error)             */
@@ -103,7 +107,8 @@ int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,
  * sums fp32, one RNE rounding, fixed summation order (bit-identical run to run). Any
  * width is accepted: x is staged in LDS in column phases when it does not fit at once.
  * batch == 1 gives the same result as nm_spmv within the tolerance of the product (it may
- * use another summation order). X must be 16-byte aligned, Y 2-byte aligned; an invalid
+ * use another summation order). The 25% patterns are accepted for batch == 1 only (and
+ * cols <= nm_max_cols()); larger batches of them return NM_ERR_PATTERN. X must be 16-byte aligned, Y 2-byte aligned; an invalid
  * batch is NM_ERR_SHAPE. */
 int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
             int64_t rows, int64_t cols, int64_t batch, int N, int M, void* stream);

@@ -15,6 +15,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libnmsparse.so")
 
 PATTERNS = ((2, 4), (4, 8), (8, 16), (16, 32))
+PATTERNS_QUARTER = ((1, 4), (2, 8), (4, 16), (8, 32))   # 25% density, single vector
+ALL_PATTERNS = PATTERNS + PATTERNS_QUARTER
 
 NM_OK, NM_ERR_NULL, NM_ERR_SHAPE, NM_ERR_PATTERN, NM_ERR_ALIGN, NM_ERR_TOO_WIDE, NM_ERR_HIP = range(7)
 
@@ -153,7 +155,7 @@ def nm_pack(W, N: int, M: int):
     rows, cols = W.shape
     nv = values_count(rows, cols, N, M)
     if nv == 0:
-        st = NM_ERR_PATTERN if (N, M) not in PATTERNS else NM_ERR_SHAPE
+        st = NM_ERR_PATTERN if (N, M) not in ALL_PATTERNS else NM_ERR_SHAPE
         raise NMArgumentError("nm_pack", st)
     values = torch.empty((rows, cols * N // M), dtype=torch.float16, device=W.device)
     masks = torch.empty((rows, cols // 32), dtype=torch.int32, device=W.device)
@@ -174,7 +176,7 @@ def nm_spmv(values, masks, x, N: int, M: int, out=None):
     cols = words * 32
     if x.shape[0] != cols:
         raise ValueError(f"x has {x.shape[0]} elements, masks describe {cols} columns")
-    if (N, M) in PATTERNS and values.shape != (rows, cols * N // M):
+    if (N, M) in ALL_PATTERNS and values.shape != (rows, cols * N // M):
         raise ValueError(f"values shape {tuple(values.shape)} != {(rows, cols * N // M)}")
     if not (values.device == masks.device == x.device):
         raise ValueError("values, masks and x must be on one device")
@@ -226,7 +228,7 @@ def nm_spmm(values, masks, X, N: int, M: int, out=None):
     batch = X.shape[0]
     if X.shape[1] != cols:
         raise ValueError(f"X has {X.shape[1]} columns, masks describe {cols}")
-    if (N, M) in PATTERNS and values.shape != (rows, cols * N // M):
+    if (N, M) in ALL_PATTERNS and values.shape != (rows, cols * N // M):
         raise ValueError(f"values shape {tuple(values.shape)} != {(rows, cols * N // M)}")
     if not (values.device == masks.device == X.device):
         raise ValueError("values, masks and X must be on one device")

@@ -16,8 +16,10 @@ DeviceInfo g_dev[kMaxDevices];
 thread_local int t_last_hip_error = 0;
 std::set<std::pair<const void*, int>> g_lds_raised;  // guarded by g_dev_mutex
 
+// 50% (16 kept values per mask word) and 25% (8 per word) patterns.
 bool valid_pattern(int N, int M) {
-  return (N == 2 && M == 4) || (N == 4 && M == 8) || (N == 8 && M == 16) || (N == 16 && M == 32);
+  return (N == 2 && M == 4) || (N == 4 && M == 8) || (N == 8 && M == 16) || (N == 16 && M == 32) ||
+         (N == 1 && M == 4) || (N == 2 && M == 8) || (N == 4 && M == 16) || (N == 8 && M == 32);
 }
 
 // rows >= 1, cols >= 32, cols % 32 == 0, and every size the kernels form fits: int row
@@ -145,12 +147,13 @@ int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, ui
             int64_t rows, int64_t cols, int64_t batch, int N, int M, void* stream) {
   if (!values || !masks || !X || !Y) return NM_ERR_NULL;
   if (!nm::valid_shape(rows, cols) || batch < 1 || batch > 8) return NM_ERR_SHAPE;
-  if (!nm::valid_pattern(N, M)) return NM_ERR_PATTERN;
+  if (!nm::valid_pattern(N, M) || (batch > 1 && M != 2 * N)) return NM_ERR_PATTERN;
   if (!nm::aligned(values, 16) || !nm::aligned(masks, 4) || !nm::aligned(X, 16) || !nm::aligned(Y, 2))
     return NM_ERR_ALIGN;
   nm::DeviceInfo dev;
   hipError_t e = nm::current_device_info(&dev);
   if (e != hipSuccess) return nm::hip_fail(e);
+  if (M != 2 * N && cols > nm::max_cols_for(dev)) return NM_ERR_TOO_WIDE;  // 25%: single-vector kernel only
   e = nm::launch_spmm(values, masks, X, Y, rows, cols, int(batch), N, M, static_cast<hipStream_t>(stream), dev);
   return e == hipSuccess ? NM_OK : nm::hip_fail(e);
 }
@@ -171,7 +174,7 @@ const char* nm_spmv_variant(int64_t rows, int64_t cols, int N, int M) {
   if (!nm::valid_shape(rows, cols) || !nm::valid_pattern(N, M)) return "";
   nm::DeviceInfo dev;
   if (nm::current_device_info(&dev) != hipSuccess) return "";
-  return nm::spmv_variant(rows, cols, N, dev);
+  return nm::spmv_variant(rows, cols, N, M, dev);
 }
 
 int nm_spmv_launch_shape(int64_t rows, int64_t cols, int N, int M, int64_t* shape) {
@@ -182,7 +185,7 @@ int nm_spmv_launch_shape(int64_t rows, int64_t cols, int N, int M, int64_t* shap
   hipError_t e = nm::current_device_info(&dev);
   if (e != hipSuccess) return nm::hip_fail(e);
   if (cols > nm::max_cols_for(dev)) return NM_ERR_TOO_WIDE;
-  const nm::WorkgroupShape s = nm::spmv_shape(rows, cols, dev);
+  const nm::WorkgroupShape s = M == 4 * N ? nm::spmv_quarter_shape(rows, cols, dev) : nm::spmv_shape(rows, cols, dev);
   shape[0] = s.rpb;
   shape[1] = s.row_groups;
   shape[2] = s.cs;
@@ -195,7 +198,7 @@ const char* nm_status_string(int status) {
     case NM_OK: return "ok";
     case NM_ERR_NULL: return "a required pointer is NULL";
     case NM_ERR_SHAPE: return "invalid shape: need rows >= 1, cols >= 32, cols % 32 == 0, 1 <= batch <= 8 (and sizes that fit)";
-    case NM_ERR_PATTERN: return "unsupported N:M pattern: need 2:4, 4:8, 8:16 or 16:32";
+    case NM_ERR_PATTERN: return "unsupported N:M pattern: need 2:4, 4:8, 8:16, 16:32 or (one vector only) 1:4, 2:8, 4:16, 8:32";
     case NM_ERR_ALIGN: return "misaligned pointer: W, values and x need 16 bytes, masks 4, y 2";
     case NM_ERR_TOO_WIDE: return "cols too large: x does not fit in the LDS of one workgroup";
     case NM_ERR_HIP: return "a HIP runtime call failed";

@@ -55,8 +55,9 @@ hipError_t launch_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y, int64_
                        int64_t cols, int batch, hipStream_t stream, const DeviceInfo& dev);
 
 // Name of the kernel configuration launch_spmv picks (static string) and its shape.
-const char* spmv_variant(int64_t rows, int64_t cols, int N, const DeviceInfo& dev);
+const char* spmv_variant(int64_t rows, int64_t cols, int N, int M, const DeviceInfo& dev);
 WorkgroupShape spmv_shape(int64_t rows, int64_t cols, const DeviceInfo& dev);
+WorkgroupShape spmv_quarter_shape(int64_t rows, int64_t cols, const DeviceInfo& dev);
 WorkgroupShape dense_shape(int64_t rows, int64_t cols, const DeviceInfo& dev);
 
 // Widest x the SpMV / GEMV kernels can stage for the given device.

@@ -10,8 +10,8 @@
 //
 // One thread encodes one mask word. Because W is row-major with 32 fp16 per word,
 // word t (row-major over rows x words) is exactly W[32t, 32t+32), its values are
-// values[16t, 16t+16) and its mask is masks[t], so the encoder is a flat map over
-// words. Each weight gets the integer key (magnitude << 5) | (31 - column in group):
+// values[V t, V t + V) with V = 32 N / M kept values per word (16 at 50% density, 8 at
+// 25%) and its mask is masks[t], so the encoder is a flat map over words. Each weight gets the integer key (magnitude << 5) | (31 - column in group):
 // keys are distinct inside a group and larger means "wins", so an element is kept
 // iff fewer than N members of its group have a larger key. The kept fp16 bits are
 // then compacted in ascending column order through a private LDS slot.
@@ -60,10 +60,11 @@ __global__ __launch_bounds__(kPackThreads) void nm_pack_kernel(const uint4* __re
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) slot[i] = d[i];
-    uint32_t out[8];
+    constexpr int V = 32 * N / M;  // kept values per word
+    uint32_t out[V / 2];
     uint32_t rest = mask;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < V / 2; ++k) {
       const uint32_t p0 = __builtin_ctz(rest | 0x80000000u);
       rest &= rest - 1;
       const uint32_t p1 = __builtin_ctz(rest | 0x80000000u);
@@ -72,8 +73,9 @@ __global__ __launch_bounds__(kPackThreads) void nm_pack_kernel(const uint4* __re
       const uint32_t hi = (slot[p1 >> 1] >> (16 * (p1 & 1))) & 0xFFFFu;
       out[k] = lo | (hi << 16);
     }
-    values[2 * t + 0] = make_uint4(out[0], out[1], out[2], out[3]);
-    values[2 * t + 1] = make_uint4(out[4], out[5], out[6], out[7]);
+#pragma unroll
+    for (int q = 0; q < V / 8; ++q)
+      values[(V / 8) * t + q] = make_uint4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
     masks[t] = mask;
   }
 }
@@ -95,13 +97,21 @@ hipError_t launch_pack_t(const uint16_t* W, uint16_t* values, uint32_t* masks, i
 
 hipError_t launch_pack(const uint16_t* W, uint16_t* values, uint32_t* masks, int64_t rows,
                        int64_t cols, int N, int M, hipStream_t stream, const DeviceInfo& dev) {
-  (void)M;  // validated together with N: M == 2 * N
   const int64_t words = rows * (cols / 32);
-  switch (N) {
-    case 2: return launch_pack_t<2, 4>(W, values, masks, words, stream, dev);
-    case 4: return launch_pack_t<4, 8>(W, values, masks, words, stream, dev);
-    case 8: return launch_pack_t<8, 16>(W, values, masks, words, stream, dev);
-    case 16: return launch_pack_t<16, 32>(W, values, masks, words, stream, dev);
+  if (M == 2 * N) {  // 50%
+    switch (N) {
+      case 2: return launch_pack_t<2, 4>(W, values, masks, words, stream, dev);
+      case 4: return launch_pack_t<4, 8>(W, values, masks, words, stream, dev);
+      case 8: return launch_pack_t<8, 16>(W, values, masks, words, stream, dev);
+      case 16: return launch_pack_t<16, 32>(W, values, masks, words, stream, dev);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (N) {  // 25%: M == 4 * N
+    case 1: return launch_pack_t<1, 4>(W, values, masks, words, stream, dev);
+    case 2: return launch_pack_t<2, 8>(W, values, masks, words, stream, dev);
+    case 4: return launch_pack_t<4, 16>(W, values, masks, words, stream, dev);
+    case 8: return launch_pack_t<8, 32>(W, values, masks, words, stream, dev);
     default: return hipErrorInvalidValue;
   }
 }

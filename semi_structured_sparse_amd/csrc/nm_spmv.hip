@@ -86,8 +86,14 @@ WorkgroupShape spmv_shape(int64_t rows, int64_t cols, const DeviceInfo& dev) {
   return workgroup_shape(rows, ceil_div(cols, 128), dev);  // 128 columns = 128 bytes of values
 }
 
-const char* spmv_variant(int64_t rows, int64_t cols, int N, const DeviceInfo& dev) {
+// 25% density: 256 columns = 128 bytes of values per step.
+WorkgroupShape spmv_quarter_shape(int64_t rows, int64_t cols, const DeviceInfo& dev) {
+  return workgroup_shape(rows, ceil_div(cols, 256), dev);
+}
+
+const char* spmv_variant(int64_t rows, int64_t cols, int N, int M, const DeviceInfo& dev) {
   (void)rows;
+  if (M == 4 * N) return "spmv_quarter_kernel<4, true>";
   // one string per (pattern, decoder): the template arguments of
   // spmv_kernel<N, BATCH, NTV, DEC> as profilers print them
   static const char* const names[4][4] = {
@@ -104,8 +110,16 @@ const char* spmv_variant(int64_t rows, int64_t cols, int N, const DeviceInfo& de
 hipError_t launch_spmv(const uint16_t* values, const uint32_t* masks, const uint16_t* x,
                        uint16_t* y, int64_t rows, int64_t cols, int N, int M, hipStream_t stream,
                        const DeviceInfo& dev) {
-  (void)M;  // validated together with N: M == 2 * N
   const int r = int(rows), c = int(cols);
+  if (M == 4 * N) {  // 25% density: one kernel for 1:4, 2:8, 4:16 and 8:32
+    const WorkgroupShape q = spmv_quarter_shape(rows, cols, dev);
+    const uint4* v4 = reinterpret_cast<const uint4*>(values);
+    const uint4* x4 = reinterpret_cast<const uint4*>(x);
+    int rr = r, cc = c, rpb = q.rpb, cs = q.cs;
+    void* args[] = {&v4, &masks, &x4, &y, &rr, &cc, &rpb, &cs};
+    return launch(reinterpret_cast<const void*>(&spmv_quarter_kernel<kBatch, kNTV>), dim3(unsigned(q.grid)),
+                  dim3(unsigned(64 * q.row_groups * q.cs)), args, lds_bytes<kBitWalk>(c), stream, dev);
+  }
   const WorkgroupShape s = spmv_shape(rows, cols, dev);
   const int dec = pick_decoder(N, cols, dev);
   switch (N) {

@@ -522,5 +522,104 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
+// ---------------------------------------------------------------- 25% density
+// The same method for N:M with N/M = 1/4 (1:4, 2:8, 4:16, 8:32): every mask word keeps 8
+// values (16 bytes), so each of a row's 8 lanes takes one whole word per step (the step
+// still covers one 128-byte line of the row's values, now 8 words = 256 columns; lanes
+// 4r..4r+3 words 0..3, lanes 32+4r..32+4r+3 words 4..7) and walks its 8 set bits with a
+// fixed number of steps (find-lowest-set-bit, clear it), gathering x from the word's
+// 32-column window of the staged copy. The pattern only fixes how the 8 bits are spread,
+// not the work, so one kernel serves all four. Workgroup shape, prologue order, register
+// budget and reduction are those of spmv_kernel.
+template <int BATCH, bool NTV>
+__global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(8))) void spmv_quarter_kernel(
+    const uint4* __restrict__ values, const uint32_t* __restrict__ masks, const uint4* __restrict__ x,
+    uint16_t* __restrict__ y, int rows, int cols, int rpb, int cs_count) {
+  extern __shared__ uint4 lds[];
+  char* lds_b = reinterpret_cast<char*>(lds);
+  float* red = reinterpret_cast<float*>(lds_b);
+  char* data = lds_b + kDataOffset;
+
+  const int tid = threadIdx.x;
+  const int nthreads = blockDim.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int CS = __builtin_amdgcn_readfirstlane(cs_count);
+  const int rg = __builtin_amdgcn_readfirstlane(int(unsigned(wave) / unsigned(CS)));
+  const int cs = wave - rg * CS;
+  const int rsub = (lane & 31) >> 2;
+  const int u = ((lane >> 5) << 2) | (lane & 3);   // the step's word u of 8
+  const int row0 = blockIdx.x * rpb;
+  const int row_end = min(row0 + rpb, rows);
+  const unsigned r = unsigned(min(row0 + 8 * rg + rsub, row_end - 1));
+
+  const int words = cols >> 5;
+  const int steps = (words + 7) >> 3;
+  const int full_steps = words >> 3;
+  const int s_beg = int(unsigned(steps) * unsigned(cs) / unsigned(CS));
+  const int s_end = int(unsigned(steps) * unsigned(cs + 1) / unsigned(CS));
+  const int s_main = min(s_end, full_steps);
+
+  const uint4* __restrict__ vrow = values + size_t(r) * unsigned(cols >> 5);   // 8 values per word
+  const uint32_t* __restrict__ mrow = masks + size_t(r) * unsigned(words);
+  const uint4* __restrict__ vp = vrow + 8 * unsigned(s_beg) + unsigned(u);
+  const uint32_t* __restrict__ mp = mrow + 8 * unsigned(s_beg) + unsigned(u);
+  const int n = s_main - s_beg;
+  const int nfull = n / BATCH;
+  const int rem = n - nfull * BATCH;
+
+  // prologue: x chunks, then the first batch (clamped into the row), then the LDS writes
+  const int n16 = cols >> 3;
+  const int i0 = tid, i1 = tid + nthreads;
+  const bool two_chunks = n16 > nthreads;
+  const uint4 x0 = x[min(i0, n16 - 1)];
+  uint4 x1 = make_uint4(0u, 0u, 0u, 0u);
+  if (two_chunks) x1 = x[min(i1, n16 - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+  using B = Batch<BATCH, NTV, 8, 8, 0, 512>;
+  B A;
+  A.load_clamped(vrow, 8u * unsigned(s_beg) + unsigned(u), unsigned(cols >> 5) - 1u, mrow,
+                 8u * unsigned(s_beg) + unsigned(u), unsigned(words) - 1u);
+  if (i0 < n16) store_x_chunk<kBitWalk>(x0, i0, data, cols);
+  if (two_chunks && i1 < n16) store_x_chunk<kBitWalk>(x1, i1, data, cols);
+  for (int i = i1 + nthreads; i < n16; i += nthreads) store_x_chunk<kBitWalk>(x[i], i, data, cols);
+  __syncthreads();
+
+  // LDS byte address of this lane's word window (32 columns) in the batch's first step
+  uint32_t xw = lds_address(data) + 512u * unsigned(s_beg) + 64u * unsigned(u);
+  constexpr uint32_t kAll = 0xFFFFFFFFu;  // the lane walks all 8 set bits of its word
+  float part[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < nfull; ++b) {
+    if (b > 0) A.load(vp, mp, BATCH);
+    A.template compute_bits<2, false>(xw, 0, kAll, BATCH, part);
+    vp += 8 * BATCH;
+    mp += 8 * BATCH;
+    xw += 512u * BATCH;
+  }
+  if (rem > 0) {
+    B R;
+    R.load(vp, mp, rem);
+    R.template compute_bits<2, false>(xw, 0, kAll, rem, part);
+  }
+  // last step with 1..7 words (cols not a multiple of 256): lanes whose word exists
+  if (s_end > full_steps && u < (words & 7)) {
+    const unsigned s = unsigned(full_steps);
+    Batch<1, NTV, 8, 8, 0, 512> T;
+    T.load(vrow + 8 * s + unsigned(u), mrow + 8 * s + unsigned(u), 1);
+    T.template compute_bits<2, false>(lds_address(data) + 512u * s + 64u * unsigned(u), 0, kAll, 1, part);
+  }
+  float acc = (part[0] + part[1]) + (part[2] + part[3]);
+
+  acc = row8_sum(acc);
+  if (u == 0) red[wave * 8 + rsub] = acc;
+  __syncthreads();
+  if (tid < row_end - row0) {
+    const int trg = tid >> 3, trow = tid & 7;
+    float t = 0.f;
+    for (int k = 0; k < CS; ++k) t += red[(trg * CS + k) * 8 + trow];
+    y[row0 + tid] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(t));
+  }
+}
+
 }  // namespace spmv_detail
 }  // namespace nm

@@ -47,8 +47,9 @@ def test_status_strings():
 
 @pytest.mark.parametrize("rows,cols,N,M,want", [
     (4096, 4096, 2, 4, 4096 * 2048), (1, 32, 16, 32, 16), (3, 96, 4, 8, 144),
-    (0, 32, 2, 4, 0), (1, 0, 2, 4, 0), (1, 48, 2, 4, 0), (1, 32, 3, 4, 0), (1, 32, 1, 4, 0),
+    (0, 32, 2, 4, 0), (1, 0, 2, 4, 0), (1, 48, 2, 4, 0), (1, 32, 3, 4, 0), (1, 32, 1, 2, 0),
     (-1, 32, 2, 4, 0), (1, 16, 8, 16, 0),
+    (1, 32, 1, 4, 8), (5, 256, 2, 8, 320), (2, 64, 4, 16, 32), (1, 32, 8, 32, 8),   # 25%
 ])
 def test_values_count(rows, cols, N, M, want):
     assert nm.values_count(rows, cols, N, M) == want
@@ -86,8 +87,8 @@ def _gemv(**kw):
     (dict(rows=0), nm.NM_ERR_SHAPE), (dict(rows=-5), nm.NM_ERR_SHAPE),
     (dict(cols=0), nm.NM_ERR_SHAPE), (dict(cols=16), nm.NM_ERR_SHAPE), (dict(cols=80), nm.NM_ERR_SHAPE),
     (dict(rows=1 << 40), nm.NM_ERR_SHAPE),
-    (dict(N=3, M=4), nm.NM_ERR_PATTERN), (dict(N=2, M=8), nm.NM_ERR_PATTERN),
-    (dict(N=1, M=4), nm.NM_ERR_PATTERN), (dict(N=32, M=64), nm.NM_ERR_PATTERN),
+    (dict(N=3, M=4), nm.NM_ERR_PATTERN), (dict(N=1, M=2), nm.NM_ERR_PATTERN),
+    (dict(N=4, M=32), nm.NM_ERR_PATTERN), (dict(N=32, M=64), nm.NM_ERR_PATTERN),
     (dict(values=A16 + 8), nm.NM_ERR_ALIGN), (dict(masks=A16 + 2), nm.NM_ERR_ALIGN),
     (dict(x=A16 + 4), nm.NM_ERR_ALIGN), (dict(y=A16 + 1), nm.NM_ERR_ALIGN),
 ])
