@@ -55,10 +55,10 @@ extern "C" {
 typedef enum {
   NM_OK = 0,
   NM_ERR_NULL = 1,     /* a required pointer is NULL                                   */
-  NM_ERR_SHAPE = 2,    /* rows < 1, cols < 32, cols % 32 != 0, batch not in 1..8, or a
-                          size overflows                                              */
-  NM_ERR_PATTERN = 3,  /* (N, M) not a supported pattern (nm_spmm, nm_gemm_dense: 50%
-                          patterns for batch > 1)                                    */
+  NM_ERR_SHAPE = 2,    /* rows < 1, cols < 32, cols % 32 != 0, batch / tokens < 1, or a
+                          size beyond an entry point's limits                         */
+  NM_ERR_PATTERN = 3,  /* (N, M) not a supported pattern (nm_spmm: 50% patterns for
+                          batch > 1; nm_spmm_prefill: 2:4 only)                       */
   NM_ERR_ALIGN = 4,    /* W, values or x not 16-byte aligned; masks not 4-byte; y not 2 */
   NM_ERR_TOO_WIDE = 5, /* 2*cols bytes of x exceed the LDS one workgroup may use        */
   NM_ERR_HIP = 6       /* a HIP runtime call failed (see nm_last_hip_error)             */
@@ -99,24 +99,56 @@ int nm_spmv(const uint16_t* values, const uint32_t* masks, const uint16_t* x, ui
 int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,
                   int64_t rows, int64_t cols, void* stream);
 
-/* Small-batch sparse product (the matrix-matrix side of the SpMV / SpMM split that
- * [NEWS-NEW] draws: prefill and larger batches run matrix-matrix products), for the same
- * packed matrix and 1 <= batch <= 8 activation vectors:
+/* Batch sparse product (the matrix-matrix side of the SpMV / SpMM split that [NEWS-NEW]
+ * draws: prefill and larger batches run matrix-matrix products), for the same packed
+ * matrix and batch >= 1 activation vectors:
  *   Y[b][r] = fp16( sum_c W'[r][c] * X[b][c] ),  X fp16 [batch][cols], Y fp16 [batch][rows]
  * (row b of X is one activation vector: the layout of a batch of tokens). Products and
- * sums fp32, one RNE rounding, fixed summation order (bit-identical run to run). Any
- * width is accepted: x is staged in LDS in column phases when it does not fit at once.
- * batch == 1 gives the same result as nm_spmv within the tolerance of the product (it may
- * use another summation order). The 25% patterns are accepted for batch == 1 only (and
- * cols <= nm_max_cols()); larger batches of them return NM_ERR_PATTERN. X must be 16-byte aligned, Y 2-byte aligned; an invalid
- * batch is NM_ERR_SHAPE. */
+ * sums fp32, one RNE rounding, fixed summation order (bit-identical run to run).
+ *   - batch <= 8: the small-batch kernel (vector units; x staged in LDS in column phases
+ *     when it does not fit at once, so any width is accepted). batch == 1 gives the same
+ *     result as nm_spmv within the tolerance of the product (it may use another summation
+ *     order).
+ *   - batch > 8 with 2:4: nm_spmm_prefill (matrix cores), with its limits.
+ *   - batch > 8 with 4:8, 8:16, 16:32: the small-batch kernel on consecutive groups of 8
+ *     rows of X (one launch per group; vector units only).
+ * The 25% patterns are accepted for batch == 1 only (and cols <= nm_max_cols()); larger
+ * batches of them return NM_ERR_PATTERN. X must be 16-byte aligned, Y 2-byte aligned;
+ * batch < 1 or above 2^24 is NM_ERR_SHAPE. */
 int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
             int64_t rows, int64_t cols, int64_t batch, int N, int M, void* stream);
 
-/* Dense counterpart of nm_spmm, the same-GPU baseline of the small-batch product:
- * Y[b][r] = fp16( sum_c W[r][c] * X[b][c] ) with fp32 products and sums, fixed order. */
+/* Dense counterpart of nm_spmm, the same-GPU baseline of the batch product:
+ * Y[b][r] = fp16( sum_c W[r][c] * X[b][c] ) with fp32 products and sums, fixed order.
+ * batch <= 8: the small-batch kernel; batch > 8: nm_gemm_dense_prefill. */
 int nm_gemm_dense(const uint16_t* W, const uint16_t* X, uint16_t* Y,
                   int64_t rows, int64_t cols, int64_t batch, void* stream);
+
+/* Prefill product of a 2:4 packed matrix on the sparse matrix cores ([NEWS-NEW]: prefill
+ * is compute-bound and runs sparse matrix-matrix products; [KERNEL]: that is where 2:4
+ * sparse matrix hardware speeds inference up, and the bitmask format): for tokens >= 1
+ * rows of X,
+ *   Y[t][r] = fp16( sum_c W'[r][c] * X[t][c] ),  X fp16 [tokens][cols], Y fp16 [tokens][rows],
+ * with the (values, masks) of nm_pack for N = 2, M = 4 (any other pattern is
+ * NM_ERR_PATTERN). fp16 products, fp32 sums in the matrix instruction's order (fixed, so
+ * bit-identical run to run), one RNE rounding. Limits: cols <= 2^21, tokens <= 2^24
+ * (NM_ERR_SHAPE beyond). Masks must be as nm_pack writes them (two bits per 4-column
+ * group); a malformed mask gives an unspecified Y but never an out-of-bounds access.
+ * values, X 16-byte aligned; masks 4-byte; Y 2-byte. */
+int nm_spmm_prefill(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
+                    int64_t rows, int64_t cols, int64_t tokens, int N, int M, void* stream);
+
+/* Dense counterpart of nm_spmm_prefill on the dense matrix cores, the same-GPU baseline of
+ * the prefill product: Y[t][r] = fp16( sum_c W[r][c] * X[t][c] ), fp32 sums in the
+ * instruction's fixed order. Same limits and alignment as nm_spmm_prefill (W 16-byte). */
+int nm_gemm_dense_prefill(const uint16_t* W, const uint16_t* X, uint16_t* Y,
+                          int64_t rows, int64_t cols, int64_t tokens, void* stream);
+
+/* Introspection: the name of the kernel configuration nm_spmm_prefill (sparse != 0) or
+ * nm_gemm_dense_prefill (sparse == 0) launches for this shape on the current device, as it
+ * appears in profiler traces (for example "prefill_spmm_kernel<2, 16, 64, 2>"); "" if the
+ * arguments are invalid. Static string, never NULL. */
+const char* nm_prefill_variant(int64_t rows, int64_t cols, int64_t tokens, int sparse);
 
 /* Introspection: the name of the kernel configuration nm_spmv launches for this shape
  * and pattern on the current device, as it appears in profiler traces (for example

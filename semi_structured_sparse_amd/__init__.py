@@ -36,6 +36,11 @@ SIGNATURES = {
                            _c.c_int64, _c.c_int64, _c.c_int, _c.c_int, _c.c_void_p]),
     "nm_gemm_dense": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
                                  _c.c_int64, _c.c_void_p]),
+    "nm_spmm_prefill": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
+                                   _c.c_int64, _c.c_int64, _c.c_int, _c.c_int, _c.c_void_p]),
+    "nm_gemm_dense_prefill": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
+                                         _c.c_int64, _c.c_void_p]),
+    "nm_prefill_variant": (_c.c_char_p, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
     "nm_status_string": (_c.c_char_p, [_c.c_int]),
     "nm_spmv_variant": (_c.c_char_p, [_c.c_int64, _c.c_int64, _c.c_int, _c.c_int]),
     "nm_last_hip_error": (_c.c_int, []),
@@ -216,9 +221,12 @@ def nm_gemv_dense(W, x, out=None):
     return out
 
 
-def nm_spmm(values, masks, X, N: int, M: int, out=None):
-    """Y = X W'^T for a batch of 1..8 activation vectors: X fp16 [batch, cols] -> Y fp16
-    [batch, rows] (row b of Y is the packed matrix times row b of X)."""
+def prefill_variant(rows: int, cols: int, tokens: int, sparse: bool) -> str:
+    """Kernel configuration nm_spmm_prefill (sparse) / nm_gemm_dense_prefill launches."""
+    return lib().nm_prefill_variant(rows, cols, tokens, 1 if sparse else 0).decode()
+
+
+def _batch_args(values, masks, X, N, M, out):
     torch = _torch()
     _require(values, "values", torch.float16, 2)
     _require(masks, "masks", torch.int32, 2)
@@ -238,6 +246,14 @@ def nm_spmm(values, masks, X, N: int, M: int, out=None):
         _require(out, "out", torch.float16, 2)
         if tuple(out.shape) != (batch, rows) or out.device != X.device:
             raise ValueError("out must be fp16 [batch, rows] on the same device")
+    return rows, cols, batch, out
+
+
+def nm_spmm(values, masks, X, N: int, M: int, out=None):
+    """Y = X W'^T for a batch of activation vectors: X fp16 [batch, cols] -> Y fp16
+    [batch, rows] (row b of Y is the packed matrix times row b of X)."""
+    torch = _torch()
+    rows, cols, batch, out = _batch_args(values, masks, X, N, M, out)
     with torch.cuda.device(X.device):
         st = lib().nm_spmm(values.data_ptr(), masks.data_ptr(), X.data_ptr(), out.data_ptr(),
                            rows, cols, batch, N, M, _stream_ptr(X))
@@ -245,8 +261,19 @@ def nm_spmm(values, masks, X, N: int, M: int, out=None):
     return out
 
 
-def nm_gemm_dense(W, X, out=None):
-    """Dense baseline Y = X W^T: fp16 W [rows, cols], X [batch, cols] -> Y [batch, rows]."""
+def nm_spmm_prefill(values, masks, X, N: int = 2, M: int = 4, out=None):
+    """Prefill product Y = X W'^T of a 2:4 packed matrix on the sparse matrix cores:
+    X fp16 [tokens, cols] -> Y fp16 [tokens, rows]."""
+    torch = _torch()
+    rows, cols, tokens, out = _batch_args(values, masks, X, N, M, out)
+    with torch.cuda.device(X.device):
+        st = lib().nm_spmm_prefill(values.data_ptr(), masks.data_ptr(), X.data_ptr(), out.data_ptr(),
+                                   rows, cols, tokens, N, M, _stream_ptr(X))
+    _check("nm_spmm_prefill", st)
+    return out
+
+
+def _dense_args(W, X, out):
     torch = _torch()
     _require(W, "W", torch.float16, 2)
     _require(X, "X", torch.float16, 2)
@@ -262,10 +289,29 @@ def nm_gemm_dense(W, X, out=None):
         _require(out, "out", torch.float16, 2)
         if tuple(out.shape) != (batch, rows) or out.device != X.device:
             raise ValueError("out must be fp16 [batch, rows] on the same device")
+    return rows, cols, batch, out
+
+
+def nm_gemm_dense(W, X, out=None):
+    """Dense baseline Y = X W^T: fp16 W [rows, cols], X [batch, cols] -> Y [batch, rows]."""
+    torch = _torch()
+    rows, cols, batch, out = _dense_args(W, X, out)
     with torch.cuda.device(X.device):
         st = lib().nm_gemm_dense(W.data_ptr(), X.data_ptr(), out.data_ptr(), rows, cols, batch,
                                  _stream_ptr(X))
     _check("nm_gemm_dense", st)
+    return out
+
+
+def nm_gemm_dense_prefill(W, X, out=None):
+    """Dense prefill baseline Y = X W^T on the dense matrix cores: fp16 W [rows, cols],
+    X [tokens, cols] -> Y [tokens, rows]."""
+    torch = _torch()
+    rows, cols, tokens, out = _dense_args(W, X, out)
+    with torch.cuda.device(X.device):
+        st = lib().nm_gemm_dense_prefill(W.data_ptr(), X.data_ptr(), out.data_ptr(), rows, cols, tokens,
+                                         _stream_ptr(X))
+    _check("nm_gemm_dense_prefill", st)
     return out
 
 

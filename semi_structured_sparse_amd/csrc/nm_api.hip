@@ -143,31 +143,74 @@ int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y, int64_t row
   return e == hipSuccess ? NM_OK : nm::hip_fail(e);
 }
 
+int nm_spmm_prefill(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y, int64_t rows,
+                    int64_t cols, int64_t tokens, int N, int M, void* stream) {
+  if (!values || !masks || !X || !Y) return NM_ERR_NULL;
+  if (!nm::valid_shape(rows, cols) || tokens < 1 || !nm::prefill_fits(rows, cols, tokens)) return NM_ERR_SHAPE;
+  if (N != 2 || M != 4) return NM_ERR_PATTERN;
+  if (!nm::aligned(values, 16) || !nm::aligned(masks, 4) || !nm::aligned(X, 16) || !nm::aligned(Y, 2))
+    return NM_ERR_ALIGN;
+  nm::DeviceInfo dev;
+  hipError_t e = nm::current_device_info(&dev);
+  if (e != hipSuccess) return nm::hip_fail(e);
+  e = nm::launch_prefill_spmm(values, masks, X, Y, rows, cols, tokens, static_cast<hipStream_t>(stream), dev);
+  return e == hipSuccess ? NM_OK : nm::hip_fail(e);
+}
+
+int nm_gemm_dense_prefill(const uint16_t* W, const uint16_t* X, uint16_t* Y, int64_t rows, int64_t cols,
+                          int64_t tokens, void* stream) {
+  if (!W || !X || !Y) return NM_ERR_NULL;
+  if (!nm::valid_shape(rows, cols) || tokens < 1 || !nm::prefill_fits(rows, cols, tokens)) return NM_ERR_SHAPE;
+  if (!nm::aligned(W, 16) || !nm::aligned(X, 16) || !nm::aligned(Y, 2)) return NM_ERR_ALIGN;
+  nm::DeviceInfo dev;
+  hipError_t e = nm::current_device_info(&dev);
+  if (e != hipSuccess) return nm::hip_fail(e);
+  e = nm::launch_prefill_gemm(W, X, Y, rows, cols, tokens, static_cast<hipStream_t>(stream), dev);
+  return e == hipSuccess ? NM_OK : nm::hip_fail(e);
+}
+
 int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
             int64_t rows, int64_t cols, int64_t batch, int N, int M, void* stream) {
   if (!values || !masks || !X || !Y) return NM_ERR_NULL;
-  if (!nm::valid_shape(rows, cols) || batch < 1 || batch > 8) return NM_ERR_SHAPE;
+  if (!nm::valid_shape(rows, cols) || batch < 1 || batch > nm::kPrefillMaxTokens) return NM_ERR_SHAPE;
   if (!nm::valid_pattern(N, M) || (batch > 1 && M != 2 * N)) return NM_ERR_PATTERN;
+  if (batch > nm::kSmallBatch && N == 2 && M == 4)  // matrix-core product
+    return nm_spmm_prefill(values, masks, X, Y, rows, cols, batch, N, M, stream);
   if (!nm::aligned(values, 16) || !nm::aligned(masks, 4) || !nm::aligned(X, 16) || !nm::aligned(Y, 2))
     return NM_ERR_ALIGN;
   nm::DeviceInfo dev;
   hipError_t e = nm::current_device_info(&dev);
   if (e != hipSuccess) return nm::hip_fail(e);
   if (M != 2 * N && cols > nm::max_cols_for(dev)) return NM_ERR_TOO_WIDE;  // 25%: single-vector kernel only
-  e = nm::launch_spmm(values, masks, X, Y, rows, cols, int(batch), N, M, static_cast<hipStream_t>(stream), dev);
-  return e == hipSuccess ? NM_OK : nm::hip_fail(e);
+  // batches beyond nm::kSmallBatch of the other 50% patterns: the small-batch kernel on
+  // consecutive groups of nm::kSmallBatch rows of X (X and Y rows are contiguous)
+  for (int64_t b0 = 0; b0 < batch; b0 += nm::kSmallBatch) {
+    const int nb = int(batch - b0 < nm::kSmallBatch ? batch - b0 : nm::kSmallBatch);
+    e = nm::launch_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb, N, M,
+                        static_cast<hipStream_t>(stream), dev);
+    if (e != hipSuccess) return nm::hip_fail(e);
+  }
+  return NM_OK;
 }
 
 int nm_gemm_dense(const uint16_t* W, const uint16_t* X, uint16_t* Y, int64_t rows, int64_t cols,
                   int64_t batch, void* stream) {
   if (!W || !X || !Y) return NM_ERR_NULL;
-  if (!nm::valid_shape(rows, cols) || batch < 1 || batch > 8) return NM_ERR_SHAPE;
+  if (!nm::valid_shape(rows, cols) || batch < 1 || batch > nm::kPrefillMaxTokens) return NM_ERR_SHAPE;
+  if (batch > nm::kSmallBatch) return nm_gemm_dense_prefill(W, X, Y, rows, cols, batch, stream);
   if (!nm::aligned(W, 16) || !nm::aligned(X, 16) || !nm::aligned(Y, 2)) return NM_ERR_ALIGN;
   nm::DeviceInfo dev;
   hipError_t e = nm::current_device_info(&dev);
   if (e != hipSuccess) return nm::hip_fail(e);
   e = nm::launch_gemm(W, X, Y, rows, cols, int(batch), static_cast<hipStream_t>(stream), dev);
   return e == hipSuccess ? NM_OK : nm::hip_fail(e);
+}
+
+const char* nm_prefill_variant(int64_t rows, int64_t cols, int64_t tokens, int sparse) {
+  if (!nm::valid_shape(rows, cols) || tokens < 1 || !nm::prefill_fits(rows, cols, tokens)) return "";
+  nm::DeviceInfo dev;
+  if (nm::current_device_info(&dev) != hipSuccess) return "";
+  return nm::prefill_variant(rows, tokens, sparse != 0, dev);
 }
 
 const char* nm_spmv_variant(int64_t rows, int64_t cols, int N, int M) {
@@ -197,7 +240,7 @@ const char* nm_status_string(int status) {
   switch (status) {
     case NM_OK: return "ok";
     case NM_ERR_NULL: return "a required pointer is NULL";
-    case NM_ERR_SHAPE: return "invalid shape: need rows >= 1, cols >= 32, cols % 32 == 0, 1 <= batch <= 8 (and sizes that fit)";
+    case NM_ERR_SHAPE: return "invalid shape: need rows >= 1, cols >= 32, cols % 32 == 0, batch/tokens >= 1 (and sizes that fit)";
     case NM_ERR_PATTERN: return "unsupported N:M pattern: need 2:4, 4:8, 8:16, 16:32 or (one vector only) 1:4, 2:8, 4:16, 8:32";
     case NM_ERR_ALIGN: return "misaligned pointer: W, values and x need 16 bytes, masks 4, y 2";
     case NM_ERR_TOO_WIDE: return "cols too large: x does not fit in the LDS of one workgroup";

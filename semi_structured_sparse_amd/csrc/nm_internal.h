@@ -47,7 +47,8 @@ struct WorkgroupShape {
   int64_t grid = 0;
 };
 
-// Small-batch products (1 <= batch <= 8): X [batch][cols], Y [batch][rows].
+// Small-batch products (1 <= batch <= kSmallBatch): X [batch][cols], Y [batch][rows].
+constexpr int64_t kSmallBatch = 8;
 hipError_t launch_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X,
                        uint16_t* Y, int64_t rows, int64_t cols, int batch, int N, int M,
                        hipStream_t stream, const DeviceInfo& dev);
@@ -62,5 +63,18 @@ WorkgroupShape dense_shape(int64_t rows, int64_t cols, const DeviceInfo& dev);
 
 // Widest x the SpMV / GEMV kernels can stage for the given device.
 int64_t max_cols_for(const DeviceInfo& dev);
+
+// Prefill-sized products on the matrix cores: X [tokens][cols], Y [tokens][rows]. The
+// sparse one takes 2:4 packed weights only. Limits: cols <= kPrefillMaxCols (byte offsets
+// inside a workgroup's slices are 32-bit), tokens <= kPrefillMaxTokens.
+constexpr int64_t kPrefillMaxCols = int64_t(1) << 21;
+constexpr int64_t kPrefillMaxTokens = int64_t(1) << 24;
+bool prefill_fits(int64_t rows, int64_t cols, int64_t tokens);
+hipError_t launch_prefill_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
+                               int64_t rows, int64_t cols, int64_t tokens, hipStream_t stream, const DeviceInfo& dev);
+hipError_t launch_prefill_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y, int64_t rows, int64_t cols,
+                               int64_t tokens, hipStream_t stream, const DeviceInfo& dev);
+// Name of the kernel configuration the prefill launchers pick (static string).
+const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev);
 
 }  // namespace nm

@@ -1,0 +1,69 @@
+// Launchers of the prefill-sized products (many tokens per weight) on the matrix cores:
+// the 2:4 sparse product and the dense product. The kernels are in nm_prefill_impl.h.
+#include "nm_internal.h"
+#include "nm_prefill_impl.h"
+
+namespace nm {
+
+using namespace prefill_detail;
+
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tile shapes (TR x TT output tiles of 16 x 16 per wave, KS columns per step, loads D steps
+// ahead), from a sweep on MI355X over 4096..14336 rows and columns at 2048 tokens: the
+// large tile (128 rows x 256 tokens per workgroup) was fastest for both products; the small
+// one (64 x 64) serves problems whose large-tile grid would leave CUs idle.
+using Large = Tile<2, 16, 64>;
+using Small = Tile<1, 4, 64>;
+constexpr int kDepth = 2;
+
+template <typename T>
+int64_t workgroups(int64_t rows, int64_t tokens) {
+  return ceil_div(rows, T::kRows) * ceil_div(tokens, T::kTokens);
+}
+
+bool use_large(int64_t rows, int64_t tokens, const DeviceInfo& dev) {
+  const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
+  return workgroups<Large>(rows, tokens) >= cus;
+}
+
+}  // namespace
+
+bool prefill_fits(int64_t rows, int64_t cols, int64_t tokens) {
+  // byte offsets inside one workgroup's slices are 32-bit; workgroup counts fit an int
+  return cols <= kPrefillMaxCols && tokens <= kPrefillMaxTokens && workgroups<Small>(rows, tokens) <= INT32_MAX;
+}
+
+hipError_t launch_prefill_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
+                               int64_t rows, int64_t cols, int64_t tokens, hipStream_t stream, const DeviceInfo& dev) {
+  if (!prefill_fits(rows, cols, tokens)) return hipErrorInvalidValue;
+  int r = int(rows), c = int(cols), t = int(tokens);
+  void* args[] = {&values, &masks, &X, &Y, &r, &c, &t};
+  if (use_large(rows, tokens, dev))
+    return launch(reinterpret_cast<const void*>(&prefill_spmm_kernel<2, 16, 64, kDepth>),
+                  dim3(unsigned(workgroups<Large>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
+  return launch(reinterpret_cast<const void*>(&prefill_spmm_kernel<1, 4, 64, kDepth>),
+                dim3(unsigned(workgroups<Small>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
+}
+
+hipError_t launch_prefill_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y, int64_t rows, int64_t cols,
+                               int64_t tokens, hipStream_t stream, const DeviceInfo& dev) {
+  if (!prefill_fits(rows, cols, tokens)) return hipErrorInvalidValue;
+  int r = int(rows), c = int(cols), t = int(tokens);
+  void* args[] = {&W, &X, &Y, &r, &c, &t};
+  if (use_large(rows, tokens, dev))
+    return launch(reinterpret_cast<const void*>(&prefill_gemm_kernel<2, 16, 64, kDepth>),
+                  dim3(unsigned(workgroups<Large>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
+  return launch(reinterpret_cast<const void*>(&prefill_gemm_kernel<1, 4, 64, kDepth>),
+                dim3(unsigned(workgroups<Small>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
+}
+
+const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev) {
+  const bool large = use_large(rows, tokens, dev);
+  if (sparse) return large ? "prefill_spmm_kernel<2, 16, 64, 2>" : "prefill_spmm_kernel<1, 4, 64, 2>";
+  return large ? "prefill_gemm_kernel<2, 16, 64, 2>" : "prefill_gemm_kernel<1, 4, 64, 2>";
+}
+
+}  // namespace nm

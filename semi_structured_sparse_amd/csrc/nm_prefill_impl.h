@@ -1,0 +1,417 @@
+// Prefill-sized products on the gfx950 matrix cores: the 2:4 sparse product on the sparse
+// matrix instruction and its dense counterpart on the dense one, from one kernel skeleton.
+//
+// Y [tokens][rows] = X [tokens][cols] W'^T, W' the pruned weight (packed: kept values in
+// row order, one 32-bit mask word per 32 columns) or the dense weight.
+//
+// Prefill is compute-bound and runs sparse matrix-matrix products (news.bitwarelabs.com
+// "SparseDecoding: decoding-aware pruning for accurate and fast LLM generation", "What's
+// new"), the regime where 2:4 sparse matrix hardware pays off (aimodeling.com SparseDecoding
+// article, "The Kernel Is the Other Half of the Answer": 1.31 to 1.46x over dense in
+// prefill on the pages' GPU). On gfx950 that hardware is v_smfmac_f32_16x16x64_f16:
+// D[16 x 16] += A[16 x 64] B[64 x 16] with A 2:4 sparse along K, given as its 32 kept
+// values plus per lane a 16-bit index word of 2-bit positions, at twice the dense rate.
+//
+// Lane layout of the sparse instruction (measured on gfx950 by multiplying one-hot
+// compressed A operands with a labelled B):
+//   A: lane l holds row l % 16. With q = l / 16 its 8 halves are the kept pairs (ascending
+//      column) of the 4-column groups b_q + {0, 1, 4, 5} of the instruction's K, b_q =
+//      8 (q & 1) + 2 (q >> 1). Nibble i of the index word is the pair's position code
+//      p0 | p1 << 2 (p0 < p1, positions 0..3 in the group) for the i-th of those groups.
+//   B: lane l holds token l % 16 at K = 16 (l / 16) + j, j = 0..15.
+//   D: lane l holds token l % 16, rows 4 (l / 16) + e, e = 0..3.
+// The instruction's K order is free as long as A and B agree, so it is permuted to suit
+// the packed format: lane q's groups are the actual column groups 4q .. 4q+3 of the
+// 64-column step. Its 8 values are then packed values 8q .. 8q+7 of the step (one 16-byte
+// load; a 2:4 group keeps exactly two values, adjacent in the packed row) and its index
+// word comes from the 16 mask bits of those groups (half q & 1 of mask word q >> 1). The
+// B lane with q = l / 16 then holds actual columns 8q .. 8q+7 and 32+8q .. 32+8q+7.
+//
+// Dense instruction v_mfma_f32_16x16x32_f16: A lane l holds row l % 16, K 8 (l / 16) + j;
+// B lane l holds token l % 16, K 8 (l / 16) + j; D as above.
+//
+// Work mapping: a workgroup of 4 waves takes 4 * 16 * TR rows x 16 * TT tokens; each wave
+// TR x TT output tiles of 16 x 16 (its own rows, all the workgroup's tokens). Per step of
+// KS columns the workgroup stages the X tile (16 * TT tokens x 2 KS bytes) in LDS
+// (double-buffered; 16-byte chunks XOR-swizzled by token so the fragment reads are free of
+// bank conflicts) and each wave loads its own weight fragments straight into registers;
+// both kinds of load are issued D steps ahead, as range-checked buffer loads. Per 64
+// columns a wave issues TR * TT sparse instructions (2 * TR * TT dense ones) and reads TT
+// X fragments from LDS, each one token tile ahead of its products. Workgroups are mapped
+// to output tiles XCD by XCD (tile_of).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace nm {
+namespace prefill_detail {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 h16_t __attribute__((ext_vector_type(16)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kWaves = 4;     // waves per workgroup, stacked along rows
+constexpr int kThreads = 64 * kWaves;
+
+// KS = columns per main-loop step (64 or 128).
+template <int TR, int TT, int KS>
+struct Tile {
+  static constexpr int kRows = kWaves * 16 * TR;      // rows per workgroup
+  static constexpr int kTokens = 16 * TT;             // tokens per workgroup
+  static constexpr int kRowBytes = 2 * KS;            // one token's X slice per step
+  static constexpr int kXBytes = kTokens * kRowBytes; // one X buffer
+  static constexpr int kXChunks = kTokens * KS / 8;   // its 16-byte chunks
+  static constexpr int kXPerThread = kXChunks / kThreads;
+  static constexpr int kSub = KS / 64;                // 64-column sub-steps
+  static_assert(KS == 64 || KS == 128, "step of 64 or 128 columns");
+  static_assert(kXChunks % kThreads == 0, "X tile must split evenly over the workgroup");
+};
+
+// 2:4 position code (p0 | p1 << 2) of each 4-bit mask nibble with two set bits, as a
+// 16-entry table of nibbles; other nibbles (malformed masks, zero-filled tails) give 0.
+constexpr uint64_t kPairCodes = (0x4ull << (4 * 0x3)) | (0x8ull << (4 * 0x5)) | (0x9ull << (4 * 0x6)) |
+                                (0xCull << (4 * 0x9)) | (0xDull << (4 * 0xA)) | (0xEull << (4 * 0xC));
+
+__device__ __forceinline__ int index_word(uint32_t m16) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w |= uint32_t((kPairCodes >> (4 * ((m16 >> (4 * i)) & 0xFu))) & 0xFu) << (4 * i);
+  return int(w);
+}
+
+// Buffer loads: a resource spans one workgroup's slice of an operand and the hardware
+// returns zero for offsets at or past its end, so lanes with nothing to load (tokens or
+// rows past the end, columns past the row) take kOutOfRange instead of a branch.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kRsrcWord3 = 0x00020000;  // 32-bit data format, raw (untyped) access
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kRsrcWord3);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
+  const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// LDS byte offset of 16-byte chunk c of token t in an X buffer with rb bytes per token:
+// the low 3 bits of the chunk index are XORed with the token's, so the 8 tokens one
+// fragment read touches at a time land on 8 different 16-byte bank groups.
+template <int RB>
+__device__ __forceinline__ uint32_t x_offset(int t, int c) { return uint32_t(t * RB + ((c ^ (t & 7)) << 4)); }
+
+__device__ __forceinline__ uint4 lds_read16(const char* base, uint32_t off) {
+  return *reinterpret_cast<const uint4*>(base + off);
+}
+
+// The X chunks this thread stages: chunk k = tid + kThreads * j is token k / (KS / 8),
+// column chunk k % (KS / 8) of the step. Tokens past the end and columns past the row
+// read as zero.
+template <int TR, int TT, int KS>
+struct XStager {
+  using T = Tile<TR, TT, KS>;
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t off[T::kXPerThread];  // byte offset of the chunk in step 0
+  int col[T::kXPerThread];
+  uint32_t dst[T::kXPerThread];
+
+  __device__ __forceinline__ void init(const uint16_t* __restrict__ X, int tokens, int cols, int t0, int tid) {
+    rsrc = make_rsrc(X + size_t(t0) * unsigned(cols), int64_t(min(T::kTokens, tokens - t0)) * cols * 2);
+#pragma unroll
+    for (int j = 0; j < T::kXPerThread; ++j) {
+      const int k = tid + kThreads * j;
+      const int t = k / (KS / 8), c = k % (KS / 8);
+      col[j] = 8 * c;
+      off[j] = uint32_t(t) * uint32_t(cols) * 2u + uint32_t(16 * c);
+      dst[j] = x_offset<T::kRowBytes>(t, c);
+    }
+  }
+  __device__ __forceinline__ void load(uint4 (&r)[T::kXPerThread], int c0, int cols) const {
+#pragma unroll
+    for (int j = 0; j < T::kXPerThread; ++j)
+      r[j] = buf_load16(rsrc, c0 + col[j] < cols ? off[j] + 2u * uint32_t(c0) : kOutOfRange);
+  }
+  __device__ __forceinline__ void store(const uint4 (&r)[T::kXPerThread], char* buf) const {
+#pragma unroll
+    for (int j = 0; j < T::kXPerThread; ++j) *reinterpret_cast<uint4*>(buf + dst[j]) = r[j];
+  }
+};
+
+// Output tile of a workgroup. Workgroups go to the 8 XCDs in turn (workgroup b to XCD
+// b % 8), each XCD with its own L2, so workgroup b is given tile L: the tiles are cut into
+// 8 contiguous runs, one per XCD, and ordered in bands of kGroup row tiles (token tile
+// outer, row tile inner within a band) so that a run is a compact block of row tiles x
+// token tiles whose weight and X slices the XCD's L2 serves to all of them. Workgroups
+// past the last multiple of 8 keep their own index.
+constexpr int kGroup = 8;
+
+struct TileCoord {
+  int rx, ty;
+};
+
+__host__ __device__ __forceinline__ TileCoord tile_of(int b, int nrx, int nty) {
+  const int nwg = nrx * nty;
+  const int full = nwg - nwg % 8;
+  const int L = b < full ? (b % 8) * (full / 8) + b / 8 : b;
+  const int band = L / (kGroup * nty);
+  const int gh = min(kGroup, nrx - band * kGroup);
+  const int idx = L - band * kGroup * nty;
+  return {band * kGroup + idx % gh, idx / gh};
+}
+
+// Writes one 16 x 16 output tile's lane share: 4 consecutive rows of one token.
+__device__ __forceinline__ void store_tile(const f4_t& d, uint16_t* __restrict__ Y, int rows, int tokens, int row,
+                                           int tok, bool vec) {
+  if (tok >= tokens || row >= rows) return;
+  uint16_t h[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) h[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(d[e]));
+  uint16_t* out = Y + size_t(tok) * unsigned(rows) + unsigned(row);
+  if (vec && row + 4 <= rows) {
+    *reinterpret_cast<uint2*>(out) = make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (row + e < rows) out[e] = h[e];
+  }
+}
+
+template <int TR, int TT>
+__device__ __forceinline__ void zero(f4_t (&acc)[TR][TT]) {
+#pragma unroll
+  for (int a = 0; a < TR; ++a)
+#pragma unroll
+    for (int b = 0; b < TT; ++b) acc[a][b] = f4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+template <int TR, int TT>
+__device__ __forceinline__ void store_all(const f4_t (&acc)[TR][TT], uint16_t* __restrict__ Y, int rows, int tokens,
+                                          int r0, int t0, int lane) {
+  const int q = lane >> 4, li = lane & 15;
+  const bool vec = (rows & 3) == 0 && (reinterpret_cast<uintptr_t>(Y) & 7) == 0;
+#pragma unroll
+  for (int a = 0; a < TR; ++a)
+#pragma unroll
+    for (int b = 0; b < TT; ++b) store_tile(acc[a][b], Y, rows, tokens, r0 + 16 * a + 4 * q, t0 + 16 * b + li, vec);
+}
+
+// Weight fragments of one step for the sparse product: per row tile and 64-column
+// sub-step, this lane's 8 kept values and its mask word.
+template <int TR, int SUB>
+struct SparseA {
+  uint4 v[TR][SUB];
+  uint32_t m[TR][SUB];
+};
+
+// Weight fragments of one step for the dense product: per row tile and 32-column slice.
+template <int TR, int SUB>
+struct DenseA {
+  uint4 v[TR][2 * SUB];
+};
+
+// The main loop shared by both products. X goes global -> registers -> LDS (two buffers),
+// weights global -> registers, D steps ahead. Step s: barrier; write X of step s + 1 (its
+// loads were issued D - 1 steps earlier) into buffer (s + 1) & 1, last read in step s - 1,
+// which every wave has finished by the barrier; take this step's weight set; issue the
+// loads of step s + D into the freed register sets; compute on buffer s & 1. Steps are
+// unrolled D at a time so every register set has a fixed name; the steps past the last
+// one (up to D - 1) skip only the math, and their loads repeat the last step, so the
+// loads and waits stay the same in every step.
+template <int TR, int TT, int KS, int D, typename AFrag, typename LoadA, typename Compute>
+__device__ __forceinline__ void main_loop(const XStager<TR, TT, KS>& xst, char (*xs)[Tile<TR, TT, KS>::kXBytes],
+                                          int cols, LoadA load_a, Compute compute) {
+  using T = Tile<TR, TT, KS>;
+  const int steps = (cols + KS - 1) / KS;
+  const int last = (steps - 1) * KS;
+  uint4 xr[D][T::kXPerThread];
+  AFrag af[D];
+#pragma unroll
+  for (int p = 0; p < D; ++p) {
+    const int c = min(p * KS, last);
+    xst.load(xr[p], c, cols);
+    load_a(af[p], c);
+  }
+  xst.store(xr[0], xs[0]);
+  for (int s0 = 0; s0 < steps; s0 += D) {
+#pragma unroll
+    for (int p = 0; p < D; ++p) {
+      const int s = s0 + p;
+      __syncthreads();
+      xst.store(xr[(p + 1) % D], xs[(s + 1) & 1]);
+      const AFrag cur = af[p];
+      const int cn = min((s + D) * KS, last);
+      xst.load(xr[p], cn, cols);
+      load_a(af[p], cn);
+      if (s < steps) compute(cur, xs[s & 1]);
+    }
+  }
+}
+
+// 2:4 sparse product: values [rows][cols / 2] fp16, masks [rows][cols / 32].
+template <int TR, int TT, int KS, int D>
+__global__ __launch_bounds__(kThreads) void prefill_spmm_kernel(const uint16_t* __restrict__ values,
+                                                                const uint32_t* __restrict__ masks,
+                                                                const uint16_t* __restrict__ X,
+                                                                uint16_t* __restrict__ Y, int rows, int cols,
+                                                                int tokens) {
+  using T = Tile<TR, TT, KS>;
+  constexpr int SUB = T::kSub;
+  __shared__ __attribute__((aligned(16))) char xs[2][T::kXBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, li = lane & 15;
+  const TileCoord tc = tile_of(int(blockIdx.x), (rows + T::kRows - 1) / T::kRows, (tokens + T::kTokens - 1) / T::kTokens);
+  const int r0 = tc.rx * T::kRows + wave * 16 * TR;
+  const int t0 = tc.ty * T::kTokens;
+  const int words = cols >> 5;
+
+  XStager<TR, TT, KS> xst;
+  xst.init(X, tokens, cols, t0, tid);
+
+  // weight slices of the workgroup's rows; this lane's row in tile a is 16 a + li of its wave
+  const int wg_rows = min(T::kRows, rows - tc.rx * T::kRows);
+  const size_t wg_r0 = size_t(tc.rx) * T::kRows;
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(values + wg_r0 * unsigned(cols >> 1), int64_t(wg_rows) * cols);
+  const __amdgpu_buffer_rsrc_t mr = make_rsrc(masks + wg_r0 * unsigned(words), int64_t(wg_rows) * words * 4);
+  uint32_t voff[TR], moff[TR];
+#pragma unroll
+  for (int a = 0; a < TR; ++a) {
+    const uint32_t rl = uint32_t(wave * 16 * TR + 16 * a + li);
+    voff[a] = rl * uint32_t(cols) + 16u * uint32_t(q);          // values 8q.. of the step
+    moff[a] = rl * uint32_t(words) * 4u + 4u * uint32_t(q >> 1);  // mask word q >> 1 of the step
+  }
+  const int qcol = 32 * (q >> 1);  // first column of this lane's mask word in a sub-step
+  const int mshift = 16 * (q & 1);
+  using AF = SparseA<TR, SUB>;
+  auto load_a = [&](AF& f, int c0) {
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      const int c = c0 + 64 * u;
+      const bool ok = c + qcol < cols;
+#pragma unroll
+      for (int a = 0; a < TR; ++a) {
+        f.v[a][u] = buf_load16(vr, ok ? voff[a] + uint32_t(c) : kOutOfRange);
+        f.m[a][u] = buf_load4(mr, ok ? moff[a] + uint32_t(c >> 3) : kOutOfRange);
+      }
+    }
+  };
+
+  f4_t acc[TR][TT];
+  zero(acc);
+  // X fragment of token 16 b + li: column chunks q and 4 + q of each 64-column sub-step
+  uint32_t b_lo[SUB], b_hi[SUB];
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) {
+    b_lo[u] = x_offset<T::kRowBytes>(li, 8 * u + q);
+    b_hi[u] = x_offset<T::kRowBytes>(li, 8 * u + 4 + q);
+  }
+  auto compute = [&](const AF& f, const char* buf) {
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      h8_t av[TR];
+      int idx[TR];
+#pragma unroll
+      for (int a = 0; a < TR; ++a) {
+        av[a] = __builtin_bit_cast(h8_t, f.v[a][u]);
+        idx[a] = index_word((f.m[a][u] >> mshift) & 0xFFFFu);
+      }
+      // X fragments are read one token tile ahead of the math that uses them
+      uint4 lo[2], hi[2];
+      lo[0] = lds_read16(buf, b_lo[u]);
+      hi[0] = lds_read16(buf, b_hi[u]);
+#pragma unroll
+      for (int b = 0; b < TT; ++b) {
+        if (b + 1 < TT) {
+          const char* tb = buf + (b + 1) * 16 * T::kRowBytes;
+          lo[(b + 1) & 1] = lds_read16(tb, b_lo[u]);
+          hi[(b + 1) & 1] = lds_read16(tb, b_hi[u]);
+        }
+        const uint4 l = lo[b & 1], h = hi[b & 1];
+        const u8_t xv = {l.x, l.y, l.z, l.w, h.x, h.y, h.z, h.w};
+        const h16_t bf = __builtin_bit_cast(h16_t, xv);
+#pragma unroll
+        for (int a = 0; a < TR; ++a)
+          acc[a][b] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(av[a], bf, acc[a][b], idx[a], 0, 0);
+      }
+    }
+  };
+  main_loop<TR, TT, KS, D, AF>(xst, xs, cols, load_a, compute);
+  store_all(acc, Y, rows, tokens, r0, t0, lane);
+}
+
+// Dense product: W [rows][cols] fp16.
+template <int TR, int TT, int KS, int D>
+__global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(const uint16_t* __restrict__ W,
+                                                                const uint16_t* __restrict__ X,
+                                                                uint16_t* __restrict__ Y, int rows, int cols,
+                                                                int tokens) {
+  using T = Tile<TR, TT, KS>;
+  constexpr int SUB = T::kSub;
+  __shared__ __attribute__((aligned(16))) char xs[2][T::kXBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, li = lane & 15;
+  const TileCoord tc = tile_of(int(blockIdx.x), (rows + T::kRows - 1) / T::kRows, (tokens + T::kTokens - 1) / T::kTokens);
+  const int r0 = tc.rx * T::kRows + wave * 16 * TR;
+  const int t0 = tc.ty * T::kTokens;
+
+  XStager<TR, TT, KS> xst;
+  xst.init(X, tokens, cols, t0, tid);
+
+  const int wg_rows = min(T::kRows, rows - tc.rx * T::kRows);
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(W + size_t(tc.rx) * T::kRows * unsigned(cols), int64_t(wg_rows) * cols * 2);
+  uint32_t woff[TR];
+#pragma unroll
+  for (int a = 0; a < TR; ++a)
+    woff[a] = uint32_t(wave * 16 * TR + 16 * a + li) * uint32_t(cols) * 2u + 16u * uint32_t(q);
+  using AF = DenseA<TR, SUB>;
+  auto load_a = [&](AF& f, int c0) {
+#pragma unroll
+    for (int g = 0; g < 2 * SUB; ++g) {
+      const int c = c0 + 32 * g;
+#pragma unroll
+      for (int a = 0; a < TR; ++a) f.v[a][g] = buf_load16(wr, c < cols ? woff[a] + 2u * uint32_t(c) : kOutOfRange);
+    }
+  };
+
+  f4_t acc[TR][TT];
+  zero(acc);
+  uint32_t b_off[2 * SUB];
+#pragma unroll
+  for (int g = 0; g < 2 * SUB; ++g) b_off[g] = x_offset<T::kRowBytes>(li, 4 * g + q);
+  auto compute = [&](const AF& f, const char* buf) {
+#pragma unroll
+    for (int g = 0; g < 2 * SUB; ++g) {
+      // X fragments are read one token tile ahead of the math that uses them
+      uint4 xf[2];
+      xf[0] = lds_read16(buf, b_off[g]);
+#pragma unroll
+      for (int b = 0; b < TT; ++b) {
+        if (b + 1 < TT) xf[(b + 1) & 1] = lds_read16(buf + (b + 1) * 16 * T::kRowBytes, b_off[g]);
+        const h8_t bf = __builtin_bit_cast(h8_t, xf[b & 1]);
+#pragma unroll
+        for (int a = 0; a < TR; ++a)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, f.v[a][g]), bf, acc[a][b], 0, 0, 0);
+        // scheduling hint: LDS reads and matrix instructions in alternating groups (two
+        // reads, then the TR products of this token tile), measured faster for this kernel
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, TR, 0);
+      }
+    }
+  };
+  main_loop<TR, TT, KS, D, AF>(xst, xs, cols, load_a, compute);
+  store_all(acc, Y, rows, tokens, r0, t0, lane);
+}
+
+}  // namespace prefill_detail
+}  // namespace nm

@@ -116,6 +116,12 @@ def activation(cols: int, seed: int) -> np.ndarray:
     return standard_normal_f32(cols, seed).astype(np.float16)
 
 
+def activations(tokens: int, cols: int, seed: int) -> np.ndarray:
+    """fp16 [tokens, cols]: a batch of activation rows (prompt tokens), N(0, 1) drawn in
+    fp32 as one stream, rounded to fp16 (RNE)."""
+    return standard_normal_f32(tokens * cols, seed).reshape(tokens, cols).astype(np.float16)
+
+
 def weight_rows(rows_idx, rows: int, cols: int, seed: int, std: float = WEIGHT_STD) -> np.ndarray:
     """The listed rows of ``weight(rows, cols, seed)`` without drawing the whole matrix.
 

@@ -128,8 +128,9 @@ def test_probe_validation():
 
 @pytest.mark.parametrize("kw,want", [
     (dict(values=None), nm.NM_ERR_NULL), (dict(X=None), nm.NM_ERR_NULL), (dict(Y=None), nm.NM_ERR_NULL),
-    (dict(batch=0), nm.NM_ERR_SHAPE), (dict(batch=9), nm.NM_ERR_SHAPE), (dict(cols=48), nm.NM_ERR_SHAPE),
-    (dict(N=2, M=8), nm.NM_ERR_PATTERN),
+    (dict(batch=0), nm.NM_ERR_SHAPE), (dict(batch=(1 << 24) + 1), nm.NM_ERR_SHAPE), (dict(cols=48), nm.NM_ERR_SHAPE),
+    (dict(N=2, M=8), nm.NM_ERR_PATTERN), (dict(N=1, M=4, batch=9), nm.NM_ERR_PATTERN),
+    (dict(batch=9, X=A16 + 8), nm.NM_ERR_ALIGN), (dict(batch=9, cols=(1 << 21) + 32), nm.NM_ERR_SHAPE),
     (dict(X=A16 + 8), nm.NM_ERR_ALIGN), (dict(Y=A16 + 1), nm.NM_ERR_ALIGN), (dict(masks=A16 + 2), nm.NM_ERR_ALIGN),
 ])
 def test_spmm_validation(kw, want):
@@ -140,13 +141,49 @@ def test_spmm_validation(kw, want):
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(W=None), nm.NM_ERR_NULL), (dict(batch=0), nm.NM_ERR_SHAPE), (dict(batch=9), nm.NM_ERR_SHAPE),
-    (dict(X=A16 + 2), nm.NM_ERR_ALIGN),
+    (dict(W=None), nm.NM_ERR_NULL), (dict(batch=0), nm.NM_ERR_SHAPE), (dict(batch=(1 << 24) + 1), nm.NM_ERR_SHAPE),
+    (dict(X=A16 + 2), nm.NM_ERR_ALIGN), (dict(batch=9, Y=A16 + 1), nm.NM_ERR_ALIGN),
+    (dict(batch=9, cols=(1 << 21) + 32), nm.NM_ERR_SHAPE),
 ])
 def test_gemm_validation(kw, want):
     a = dict(W=A16, X=A16, Y=A16, rows=64, cols=128, batch=2)
     a.update(kw)
     assert nm.lib().nm_gemm_dense(a["W"], a["X"], a["Y"], a["rows"], a["cols"], a["batch"], None) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(values=None), nm.NM_ERR_NULL), (dict(masks=None), nm.NM_ERR_NULL), (dict(X=None), nm.NM_ERR_NULL),
+    (dict(Y=None), nm.NM_ERR_NULL),
+    (dict(tokens=0), nm.NM_ERR_SHAPE), (dict(tokens=(1 << 24) + 1), nm.NM_ERR_SHAPE), (dict(rows=0), nm.NM_ERR_SHAPE),
+    (dict(cols=80), nm.NM_ERR_SHAPE), (dict(cols=(1 << 21) + 32), nm.NM_ERR_SHAPE),
+    (dict(N=4, M=8), nm.NM_ERR_PATTERN), (dict(N=1, M=4), nm.NM_ERR_PATTERN), (dict(N=3, M=4), nm.NM_ERR_PATTERN),
+    (dict(values=A16 + 8), nm.NM_ERR_ALIGN), (dict(masks=A16 + 2), nm.NM_ERR_ALIGN),
+    (dict(X=A16 + 4), nm.NM_ERR_ALIGN), (dict(Y=A16 + 1), nm.NM_ERR_ALIGN),
+])
+def test_spmm_prefill_validation(kw, want):
+    a = dict(values=A16, masks=A16, X=A16, Y=A16, rows=64, cols=128, tokens=300, N=2, M=4)
+    a.update(kw)
+    assert nm.lib().nm_spmm_prefill(a["values"], a["masks"], a["X"], a["Y"], a["rows"], a["cols"], a["tokens"],
+                                    a["N"], a["M"], None) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(W=None), nm.NM_ERR_NULL), (dict(X=None), nm.NM_ERR_NULL), (dict(Y=None), nm.NM_ERR_NULL),
+    (dict(tokens=0), nm.NM_ERR_SHAPE), (dict(cols=33), nm.NM_ERR_SHAPE), (dict(cols=(1 << 21) + 32), nm.NM_ERR_SHAPE),
+    (dict(W=A16 + 2), nm.NM_ERR_ALIGN), (dict(X=A16 + 8), nm.NM_ERR_ALIGN), (dict(Y=A16 + 1), nm.NM_ERR_ALIGN),
+])
+def test_gemm_prefill_validation(kw, want):
+    a = dict(W=A16, X=A16, Y=A16, rows=64, cols=128, tokens=300)
+    a.update(kw)
+    assert nm.lib().nm_gemm_dense_prefill(a["W"], a["X"], a["Y"], a["rows"], a["cols"], a["tokens"], None) == want
+
+
+def test_prefill_variant_validation():
+    """Invalid shapes give the empty name before any HIP call."""
+    L = nm.lib()
+    assert L.nm_prefill_variant(0, 128, 16, 1) == b""
+    assert L.nm_prefill_variant(64, 80, 16, 1) == b""
+    assert L.nm_prefill_variant(64, 128, 0, 0) == b""
 
 
 def test_launch_shape_validation():

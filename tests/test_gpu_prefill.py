@@ -1,0 +1,165 @@
+"""GPU parity tests of the prefill products on the matrix cores (nm_spmm_prefill: 2:4 on the
+sparse matrix instruction; nm_gemm_dense_prefill: dense) through the C ABI, against the CPU
+oracle (spmm_ref, gemm_ref), and of the batch routing of nm_spmm / nm_gemm_dense.
+
+Bars: Y within |y - ref| <= 2e-3 + 1e-2*|ref| per element and relative L2 <= 1e-3 (fp32
+accumulation in the matrix instruction, fp16 output, fp64 oracle); exact special cases
+(one-hot X) and structural properties (determinism, routing to the same kernel) bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import semi_structured_sparse_amd as nm
+import synth
+from tests.gpu_helpers import device, down_bits16, down_f16, down_u32, sample_rows, say, up_f16, up_u32
+
+pytestmark = pytest.mark.gpu
+
+# (rows, cols, tokens): ragged rows (tiles of 16, 64 and 128 rows), ragged tokens (tiles of
+# 16, 64 and 256), a 32-column tail step, one step, many steps; small and large tile
+# configurations (the large one needs at least one workgroup per CU)
+SMALL = [(1, 32, 1), (17, 64, 5), (16, 96, 16), (33, 128, 17), (64, 4064, 63), (65, 4096, 64),
+         (127, 544, 65), (300, 1056, 255), (129, 2080, 257), (1000, 4064, 700), (4100, 1024, 2050),
+         (4096, 160, 2048)]
+
+
+def check_prefill(W, X, tag, rows_idx=None, dense=True):
+    """Pack on the GPU (checked bit-exact against the oracle on the compared rows), run the
+    sparse and dense prefill products and compare the rows `rows_idx` (all if None) with
+    the oracle over every token."""
+    R, C = W.shape
+    Wd = up_f16(W)
+    values, masks = nm.nm_pack(Wd, 2, 4)
+    Xd = up_f16(X)
+    Y = down_f16(nm.nm_spmm_prefill(values, masks, Xd))
+    Yd = down_f16(nm.nm_gemm_dense_prefill(Wd, Xd)) if dense else None
+    idx = np.arange(R) if rows_idx is None else rows_idx
+    it = torch.from_numpy(idx).to(device())
+    rv, rm = oracle.pack_ref(W[idx], 2, 4)
+    assert np.array_equal(down_u32(masks.index_select(0, it)), rm), tag
+    assert np.array_equal(down_bits16(values.index_select(0, it)), rv), tag
+    rep = oracle.y_tolerance_report(Y[:, idx], oracle.spmm_ref(rv, rm, X, C, 2, 4))
+    assert rep["ok"], (tag, "sparse", rep)
+    if dense:
+        drep = oracle.y_tolerance_report(Yd[:, idx], oracle.gemm_ref(W[idx], X))
+        assert drep["ok"], (tag, "dense", drep)
+    return rep
+
+
+def test_prefill_small_and_ragged():
+    for i, (R, C, T) in enumerate(SMALL):
+        say(f"prefill {R}x{C} tokens={T} {nm.prefill_variant(R, C, T, True)} / {nm.prefill_variant(R, C, T, False)}")
+        W = synth.weight(R, C, seed=2100 + i)
+        X = synth.activations(T, C, seed=2150 + i)
+        rows_idx = None if R * T <= 300 * 300 else sample_rows(R, rpb=128)
+        check_prefill(W, X, (R, C, T), rows_idx)
+
+
+def test_prefill_both_tile_configurations_are_exercised():
+    """The shapes above cover the small and the large tile configuration of both products."""
+    names = {nm.prefill_variant(R, C, T, s) for R, C, T in SMALL for s in (True, False)}
+    assert names == {"prefill_spmm_kernel<1, 4, 64, 2>", "prefill_spmm_kernel<2, 16, 64, 2>",
+                     "prefill_gemm_kernel<1, 4, 64, 2>", "prefill_gemm_kernel<2, 16, 64, 2>"}, names
+
+
+def test_prefill_one_hot_tokens_are_exact():
+    """X = rows of the identity: token t gives column t of the pruned matrix, bit-exactly
+    (one nonzero product, exact in fp32), for the sparse and the dense product."""
+    R, C = 200, 256
+    W = synth.weight(R, C, seed=2200)
+    X = np.eye(C, dtype=np.float16)
+    rv, rm = oracle.pack_ref(W, 2, 4)
+    D = oracle.unpack_ref(rv, rm, C, 2, 4)            # pruned matrix, fp16 bits
+    Y = down_bits16(nm.nm_spmm_prefill(up_f16(rv), up_u32(rm), up_f16(X)))
+    want = D.T.copy()
+    want[want == 0x8000] = 0                          # -0 weights give +0 in the fp32 sum
+    assert np.array_equal(Y, want)
+    Yd = down_bits16(nm.nm_gemm_dense_prefill(up_f16(W), up_f16(X)))
+    wd = W.view(np.uint16).T.copy()
+    wd[wd == 0x8000] = 0
+    assert np.array_equal(Yd, wd)
+
+
+def test_prefill_deterministic_and_unaligned_output():
+    """Repeated calls give the same bits; an output not 8-byte aligned (scalar stores) gives
+    the same bits as an aligned one."""
+    R, C, T = 300, 1024, 300
+    W = synth.weight(R, C, seed=2300)
+    X = up_f16(synth.activations(T, C, seed=2301))
+    rv, rm = oracle.pack_ref(W, 2, 4)
+    v, m = up_f16(rv), up_u32(rm)
+    Y0 = down_bits16(nm.nm_spmm_prefill(v, m, X))
+    for _ in range(10):
+        assert np.array_equal(down_bits16(nm.nm_spmm_prefill(v, m, X)), Y0)
+    R4 = 256                                          # rows % 4 == 0: vector stores when aligned
+    v4, m4 = up_f16(rv[:R4]), up_u32(rm[:R4])
+    Ya = down_bits16(nm.nm_spmm_prefill(v4, m4, X))
+    buf = torch.empty(T * R4 + 1, dtype=torch.float16, device=device())
+    out = buf[1:].view(T, R4)
+    nm.nm_spmm_prefill(v4, m4, X, out=out)
+    assert np.array_equal(down_bits16(out), Ya)
+    assert np.array_equal(Ya, Y0[:, :R4])
+
+
+def test_batch_entry_points_route_to_prefill():
+    """nm_spmm with 2:4 and nm_gemm_dense above 8 vectors run the matrix-core kernels (same
+    bits); nm_spmm with the other 50% patterns above 8 vectors runs the small-batch kernel
+    8 vectors at a time (within tolerance of the oracle; bit-identical per group)."""
+    R, C, T = 200, 1024, 21
+    W = synth.weight(R, C, seed=2400)
+    X = synth.activations(T, C, seed=2401)
+    Xd = up_f16(X)
+    rv, rm = oracle.pack_ref(W, 2, 4)
+    v, m = up_f16(rv), up_u32(rm)
+    assert np.array_equal(down_bits16(nm.nm_spmm(v, m, Xd, 2, 4)), down_bits16(nm.nm_spmm_prefill(v, m, Xd)))
+    assert np.array_equal(down_bits16(nm.nm_gemm_dense(up_f16(W), Xd)),
+                          down_bits16(nm.nm_gemm_dense_prefill(up_f16(W), Xd)))
+    for N, M in ((4, 8), (8, 16), (16, 32)):
+        rv, rm = oracle.pack_ref(W, N, M)
+        v, m = up_f16(rv), up_u32(rm)
+        Y = nm.nm_spmm(v, m, Xd, N, M)
+        rep = oracle.y_tolerance_report(down_f16(Y), oracle.spmm_ref(rv, rm, X, C, N, M))
+        assert rep["ok"], (N, M, rep)
+        Y8 = nm.nm_spmm(v, m, up_f16(X[8:16]), N, M)
+        assert np.array_equal(down_bits16(Y)[8:16], down_bits16(Y8))
+
+
+def test_prefill_malformed_masks_stay_in_bounds():
+    """Masks without two bits per 4-column group give an unspecified Y but the kernel runs
+    to completion (every access is range-checked)."""
+    R, C, T = 130, 1056, 70
+    v = up_f16(synth.weight(R, C // 2, seed=2500))
+    X = up_f16(synth.activations(T, C, seed=2501))
+    for word in (0, 1, 0x80000000, 0xFFFFFFFF, 0x12345678):
+        m = torch.full((R, C // 32), np.uint32(word).view(np.int32).item(), dtype=torch.int32, device=device())
+        Y = nm.nm_spmm_prefill(v, m, X)
+        torch.cuda.synchronize()
+        assert Y.shape == (T, R)
+
+
+def test_prefill_argument_errors():
+    v = torch.zeros((4, 64), dtype=torch.float16, device=device())
+    m = torch.zeros((4, 4), dtype=torch.int32, device=device())
+    X = torch.zeros((3, 128), dtype=torch.float16, device=device())
+    with pytest.raises(nm.NMArgumentError) as e:
+        nm.nm_spmm_prefill(v, m, X, 4, 8)
+    assert e.value.status == nm.NM_ERR_PATTERN
+    with pytest.raises(ValueError):
+        nm.nm_spmm_prefill(v, m, torch.zeros((3, 96), dtype=torch.float16, device=device()))
+
+
+def _full_size_cases():
+    return [pytest.param(name, R, C, id=f"{name}-{R}x{C}") for name, R, C in synth.LLAMA31_8B]
+
+
+@pytest.mark.parametrize("name,R,C", _full_size_cases())
+def test_prefill_full_size_llama8b(name, R, C):
+    """The Llama-3.1-8B projection shapes with a 2048-token prompt, in the configuration
+    the benchmark times: pack bit-exact and Y within tolerance on sampled rows (all tokens)."""
+    T = 2048
+    say(f"prefill full-size {name} {R}x{C} tokens={T} {nm.prefill_variant(R, C, T, True)}")
+    W = synth.weight(R, C, synth.weight_seed(6, [l[0] for l in synth.LLAMA31_8B].index(name), (2, 4)))
+    X = synth.activations(T, C, synth.x_seed(6, 0, (2, 4)))
+    check_prefill(W, X, name, sample_rows(R, k=24, rpb=128))
