@@ -32,7 +32,9 @@ if ROOT not in sys.path:
 METRIC = "N:M SpMV effective HBM GB/s (% of peak) + speedup vs dense GEMV, batch 1"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak, 8 TB/s
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "nm_spmv_counters.txt")
-WORKLOAD_BY_NAME = {"llama8b": 2, "qwen3": 3, "llama70b": 4, "decode": 5}
+WORKLOAD_BY_NAME = {"llama8b": 2, "qwen3": 3, "llama70b": 4, "decode": 5, "prefill": 6}
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix-core peak (no sparsity credit)
+PREFILL_COUNTERS_FILE = os.path.join(ROOT, "profiles", "nm_prefill_counters.txt")
 COPY_CAL_BYTES = 256 << 20  # size of the counter-calibration copy
 
 
@@ -52,6 +54,8 @@ def parse_args():
                     help="fraction of each layer's rows the CPU oracle baseline processes")
     ap.add_argument("--tokens", type=int, default=20,
                     help="decode workload: tokens (passes over the 32 blocks) timed per graph")
+    ap.add_argument("--prompt", type=int, default=2048,
+                    help="prefill workload: prompt tokens per product (rows of X)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--patterns", default="", help="patterns to run instead of the workload's, e.g. 2:4,16:32 "
                                                   "or the 25%% ones 1:4,2:8,4:16,8:32")
@@ -72,14 +76,16 @@ def alg_bytes_dense(R, C, B=1):
 
 KERNEL_SOURCES = [os.path.join(ROOT, "semi_structured_sparse_amd", "csrc", f)
                   for f in ("nm_spmv_impl.h", "nm_spmv.hip", "nm_internal.h")]
+PREFILL_SOURCES = [os.path.join(ROOT, "semi_structured_sparse_amd", "csrc", f)
+                   for f in ("nm_prefill_impl.h", "nm_prefill.hip", "nm_internal.h")]
 
 
-def kernel_source_sha():
-    """Hash of the SpMV kernel sources with comments and blank space removed, so that
-    only a change of code (not of its comments) voids the committed counter figures."""
+def kernel_source_sha(sources=None):
+    """Hash of the kernel sources with comments and blank space removed, so that only a
+    change of code (not of its comments) voids the committed counter figures."""
     import re
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in sources or KERNEL_SOURCES:
         with open(path) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -88,14 +94,14 @@ def kernel_source_sha():
     return h.hexdigest()
 
 
-def read_traffic(kernel_name: str):
+def read_traffic(kernel_name: str, counters_file=COUNTERS_FILE, sources=None):
     """HBM bytes per launch of `kernel_name` (averaged over the shapes it serves in one
     step) from the committed counter summary, or None when there is none or the kernel
     sources changed since the counters were taken."""
-    if not os.path.exists(COUNTERS_FILE):
+    if not os.path.exists(counters_file):
         return None
     sha, traffic = None, {}
-    with open(COUNTERS_FILE) as f:
+    with open(counters_file) as f:
         for line in f:
             line = line.strip()
             if line.startswith("kernel_source_sha256:"):
@@ -103,7 +109,7 @@ def read_traffic(kernel_name: str):
             elif line.startswith("traffic "):
                 name, val = line[len("traffic "):].rsplit(":", 1)
                 traffic[name.strip()] = float(val)
-    if sha != kernel_source_sha():
+    if sha != kernel_source_sha(sources):
         return None
     return traffic.get(kernel_name)
 
@@ -145,6 +151,8 @@ def main():
     cfg = WORKLOAD_BY_NAME[args.workload]
     if cfg == 5:
         return decode_main(args, torch, nm, synth, dev)
+    if cfg == 6:
+        return prefill_main(args, torch, nm, synth, dev)
     wl = synth.WORKLOADS[cfg]
     pats = [tuple(p) for p in wl["patterns"]]
     B = args.batch
@@ -545,6 +553,192 @@ def decode_main(args, torch, nm, synth, dev):
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def prefill_main(args, torch, nm, synth, dev):
+    """Prefill: the Llama-3.1-8B projection shapes (q, kv, gate_up, down) as 2:4 packed
+    weights times a prompt of --prompt tokens (X [tokens][cols], seeded N(0,1)), on the
+    sparse matrix cores (nm_spmm_prefill); a step is one pass over the four products. Also
+    timed: the dense matrix-core product over the same dense weights (nm_gemm_dense_prefill)
+    and, as context only, torch.mm (the vendor BLAS) on the same shapes.
+
+    Useful flops of a sparse product: 2 * rows * (cols / 2) * tokens (kept weights only);
+    the roofline prices them against the dense fp16 matrix-core peak (the sparse
+    instruction's doubled rate is not counted as peak)."""
+    import numpy as np
+    lib = nm.lib()
+    T = args.prompt
+    cfg = 6
+    shapes = synth.LLAMA31_8B
+    t_gen = time.time()
+    items = []
+    for li, (name, R, C) in enumerate(shapes):
+        W = synth.weight(R, C, synth.weight_seed(cfg, li, (2, 4)))
+        X = synth.activations(T, C, synth.x_seed(cfg, li, (2, 4)))
+        Wd = torch.from_numpy(W).to(dev)
+        Xd = torch.from_numpy(X).to(dev)
+        values, masks = nm.nm_pack(Wd, 2, 4)
+        items.append(dict(name=name, R=R, C=C, W=Wd, Wt=Wd.t().contiguous(), X=Xd, X_host=X, values=values,
+                          masks=masks, Y=torch.empty((T, R), dtype=torch.float16, device=dev),
+                          Yd=torch.empty((T, R), dtype=torch.float16, device=dev),
+                          W_cpu=W, flops_useful=R * C * T, flops_dense=2 * R * C * T))
+        del W
+    torch.cuda.synchronize()
+    log(f"prefill: generated and packed {len(items)} layers x {T} tokens in {time.time() - t_gen:.1f}s")
+    sp_a = [(q["values"].data_ptr(), q["masks"].data_ptr(), q["X"].data_ptr(), q["Y"].data_ptr(), q["R"], q["C"],
+             T, 2, 4) for q in items]
+    dn_a = [(q["W"].data_ptr(), q["X"].data_ptr(), q["Yd"].data_ptr(), q["R"], q["C"], T) for q in items]
+
+    def sp_step(s_):
+        for a in sp_a:
+            st = lib.nm_spmm_prefill(*a, s_)
+            if st:
+                raise RuntimeError(f"nm_spmm_prefill: {nm.status_string(st)}")
+
+    def dn_step(s_):
+        for a in dn_a:
+            st = lib.nm_gemm_dense_prefill(*a, s_)
+            if st:
+                raise RuntimeError(f"nm_gemm_dense_prefill: {nm.status_string(st)}")
+
+    def graph_ms(fn, K, W_, reps=3):
+        s_ = torch.cuda.current_stream(dev).cuda_stream
+        for _ in range(W_):
+            fn(s_)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream().cuda_stream
+            for _ in range(K):
+                fn(cs)
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            g.replay()
+            b_.record()
+            torch.cuda.synchronize()
+            ts.append(a_.elapsed_time(b_) / K)
+        del g
+        return statistics.median(ts)
+
+    # one plain copy of known size: under a counter profile its FETCH_SIZE / WRITE_SIZE
+    # calibrate the counters against real bytes
+    cal = torch.empty(2 * COPY_CAL_BYTES, dtype=torch.uint8, device=dev)
+    nm.nm_probe_copy(cal[COPY_CAL_BYTES:], cal[:COPY_CAL_BYTES])
+    torch.cuda.synchronize()
+    del cal
+
+    K, Wm = args.steps, args.warmup
+    ms_sp = graph_ms(sp_step, K, Wm)
+    ms_dn = graph_ms(dn_step, K, Wm)
+    # per layer: each product alone, 20 launches in a graph, median of 3 replays
+    per_layer = []
+    for i, q in enumerate(items):
+        us_s = graph_ms(lambda s_, a=sp_a[i]: lib.nm_spmm_prefill(*a, s_), 20, 3) * 1e3
+        us_d = graph_ms(lambda s_, a=dn_a[i]: lib.nm_gemm_dense_prefill(*a, s_), 20, 3) * 1e3
+        Wt, Xd = q["Wt"], q["X"]
+        try:   # context only: the vendor BLAS on the same dense product
+            us_t = graph_ms(lambda s_, Wt=Wt, Xd=Xd: torch.mm(Xd, Wt), 20, 3) * 1e3
+        except Exception as e:  # pragma: no cover
+            log(f"torch.mm timing unavailable: {e}")
+            us_t = float("nan")
+        per_layer.append({"layer": q["name"], "shape": f"{q['R']}x{q['C']}", "tokens": T,
+                          "kernel": nm.prefill_variant(q["R"], q["C"], T, True),
+                          "us": round(us_s, 2), "useful_TFLOPs": round(q["flops_useful"] / us_s / 1e6, 1),
+                          "dense_equiv_TFLOPs": round(q["flops_dense"] / us_s / 1e6, 1),
+                          "dense_kernel": nm.prefill_variant(q["R"], q["C"], T, False),
+                          "dense_us": round(us_d, 2), "dense_TFLOPs": round(q["flops_dense"] / us_d / 1e6, 1),
+                          "speedup": round(us_d / us_s, 3),
+                          "torch_mm_us": None if us_t != us_t else round(us_t, 2),
+                          "torch_mm_TFLOPs": None if us_t != us_t else round(q["flops_dense"] / us_t / 1e6, 1)})
+    torch.cuda.synchronize()
+    useful = sum(q["flops_useful"] for q in items)
+    dense_f = sum(q["flops_dense"] for q in items)
+    value = useful / (ms_sp * 1e-3) / 1e12
+    log(f"prefill: sparse {ms_sp * 1e3:.1f} us/step ({value:.0f} useful TFLOP/s, "
+        f"{dense_f / (ms_sp * 1e-3) / 1e12:.0f} dense-equivalent), dense {ms_dn * 1e3:.1f} us/step, "
+        f"speedup {ms_dn / ms_sp:.3f}x")
+    # dominant kernel: the one with the most time per step
+    kern_us, kern_f, kern_n = {}, {}, {}
+    for pl, q in zip(per_layer, items):
+        k = pl["kernel"]
+        kern_us[k] = kern_us.get(k, 0.0) + pl["us"]
+        kern_f[k] = kern_f.get(k, 0) + q["flops_useful"]
+        kern_n[k] = kern_n.get(k, 0) + 1
+    dom = max(kern_us, key=lambda k: kern_us[k])
+    achieved = kern_f[dom] / (kern_us[dom] * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                "traffic": read_traffic(dom, PREFILL_COUNTERS_FILE, PREFILL_SOURCES),
+                "kernel": dom, "launches_per_step": kern_n[dom], "flops_per_launch": kern_f[dom] / kern_n[dom],
+                "avg_launch_us": round(kern_us[dom] / kern_n[dom], 3),
+                "flops_counted": "useful: 2 x rows x cols/2 x tokens (kept weights)"}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = prefill_cpu_baseline(items, T, args.cpu_rows_frac)
+    out = {
+        "metric": "2:4 prefill SpMM useful TFLOP/s on the sparse matrix cores + speedup vs dense matrix-core GEMM",
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms_sp, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "accumulate": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"llama3.1-8b prefill: {len(items)} projection shapes (q, kv, gate_up, down) x "
+                               f"{T}-token prompt, 2:4, fp16 W ~N(0,0.02^2) magnitude-pruned, X ~N(0,1)",
+                   "tokens": T, "flops_useful_per_step": useful, "parallelism": "single GPU"},
+        "dense_equiv_TFLOPs": round(dense_f / (ms_sp * 1e-3) / 1e12, 1),
+        "dense_ms_per_step": round(ms_dn, 5),
+        "dense_TFLOPs": round(dense_f / (ms_dn * 1e-3) / 1e12, 1),
+        "speedup_vs_dense": round(ms_dn / ms_sp, 3),
+        "timing": "K steps in one HIP graph replayed between events, median of 3 replays; per_layer: 20 launches "
+                  "of one product in a graph, median of 3 replays",
+        "per_layer": per_layer,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def prefill_cpu_baseline(items, T, frac):
+    """Time the oracle (as it is: densify, fp64 matrix product through numpy's BLAS) on the
+    first rows of every prefill layer with all tokens, and compare its Y with the GPU's."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        cores = 1
+    t_start = time.time()
+    flops, secs, worst, rel, rows_total = 0, 0.0, 0.0, 0.0, 0
+    for q in items:
+        n = max(16, int(q["R"] * frac) // 16 * 16)
+        n = min(n, q["R"])
+        rv, rm = oracle.pack_ref(q["W_cpu"][:n], 2, 4)
+        t0 = time.perf_counter()
+        ref = oracle.spmm_ref(rv, rm, q["X_host"], q["C"], 2, 4)
+        secs += time.perf_counter() - t0
+        flops += n * q["C"] * T
+        rows_total += n
+        rep = oracle.y_tolerance_report(q["Y"][:, :n].cpu().numpy(), ref)
+        worst = max(worst, rep["max_err_over_bound"])
+        rel = max(rel, rep["rel_l2"])
+    log(f"prefill cpu baseline: {flops / secs / 1e12:.5f} useful TFLOP/s over {rows_total} rows x {T} tokens "
+        f"in {secs:.1f}s (leg {time.time() - t_start:.1f}s)")
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {frac:g} of the rows of each of the {len(items)} layers ({rows_total} rows) x {T} "
+                      f"tokens; densify + fp64 matrix product (numpy BLAS, {cores} threads)",
+            "seconds": round(secs, 2), "cpu_model": cpu_info(),
+            "parity_vs_gpu": {"max_err_over_bound": worst, "rel_l2": rel, "ok": worst <= 1.0 and rel <= 1e-3}}
 
 
 def cpu_baseline(layers, frac):
