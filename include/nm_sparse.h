@@ -109,9 +109,9 @@ int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,
  *     when it does not fit at once, so any width is accepted). batch == 1 gives the same
  *     result as nm_spmv within the tolerance of the product (it may use another summation
  *     order).
- *   - batch > 8 with 2:4: nm_spmm_prefill (matrix cores), with its limits.
- *   - batch > 8 with 4:8, 8:16, 16:32: the small-batch kernel on consecutive groups of 8
- *     rows of X (one launch per group; vector units only).
+ *   - batch >= 32 with 2:4: nm_spmm_prefill (matrix cores), with its limits.
+ *   - other batches > 8 (2:4 below 32, and 4:8, 8:16, 16:32): the small-batch kernel on
+ *     consecutive groups of 8 rows of X (one launch per group; vector units only).
  * The 25% patterns are accepted for batch == 1 only (and cols <= nm_max_cols()); larger
  * batches of them return NM_ERR_PATTERN. X must be 16-byte aligned, Y 2-byte aligned;
  * batch < 1 or above 2^24 is NM_ERR_SHAPE. */
@@ -120,7 +120,7 @@ int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, ui
 
 /* Dense counterpart of nm_spmm, the same-GPU baseline of the batch product:
  * Y[b][r] = fp16( sum_c W[r][c] * X[b][c] ) with fp32 products and sums, fixed order.
- * batch <= 8: the small-batch kernel; batch > 8: nm_gemm_dense_prefill. */
+ * batch >= 32: nm_gemm_dense_prefill; below: the small-batch kernel, 8 vectors per launch. */
 int nm_gemm_dense(const uint16_t* W, const uint16_t* X, uint16_t* Y,
                   int64_t rows, int64_t cols, int64_t batch, void* stream);
 

@@ -174,7 +174,7 @@ int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, ui
   if (!values || !masks || !X || !Y) return NM_ERR_NULL;
   if (!nm::valid_shape(rows, cols) || batch < 1 || batch > nm::kPrefillMaxTokens) return NM_ERR_SHAPE;
   if (!nm::valid_pattern(N, M) || (batch > 1 && M != 2 * N)) return NM_ERR_PATTERN;
-  if (batch > nm::kSmallBatch && N == 2 && M == 4)  // matrix-core product
+  if (batch >= nm::kMatrixCoreMinBatch && N == 2 && M == 4)  // matrix-core product
     return nm_spmm_prefill(values, masks, X, Y, rows, cols, batch, N, M, stream);
   if (!nm::aligned(values, 16) || !nm::aligned(masks, 4) || !nm::aligned(X, 16) || !nm::aligned(Y, 2))
     return NM_ERR_ALIGN;
@@ -182,8 +182,8 @@ int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, ui
   hipError_t e = nm::current_device_info(&dev);
   if (e != hipSuccess) return nm::hip_fail(e);
   if (M != 2 * N && cols > nm::max_cols_for(dev)) return NM_ERR_TOO_WIDE;  // 25%: single-vector kernel only
-  // batches beyond nm::kSmallBatch of the other 50% patterns: the small-batch kernel on
-  // consecutive groups of nm::kSmallBatch rows of X (X and Y rows are contiguous)
+  // larger batches (other 50% patterns, or 2:4 below kMatrixCoreMinBatch): the small-batch
+  // kernel on consecutive groups of kSmallBatch rows of X (X and Y rows are contiguous)
   for (int64_t b0 = 0; b0 < batch; b0 += nm::kSmallBatch) {
     const int nb = int(batch - b0 < nm::kSmallBatch ? batch - b0 : nm::kSmallBatch);
     e = nm::launch_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb, N, M,
@@ -197,13 +197,17 @@ int nm_gemm_dense(const uint16_t* W, const uint16_t* X, uint16_t* Y, int64_t row
                   int64_t batch, void* stream) {
   if (!W || !X || !Y) return NM_ERR_NULL;
   if (!nm::valid_shape(rows, cols) || batch < 1 || batch > nm::kPrefillMaxTokens) return NM_ERR_SHAPE;
-  if (batch > nm::kSmallBatch) return nm_gemm_dense_prefill(W, X, Y, rows, cols, batch, stream);
+  if (batch >= nm::kMatrixCoreMinBatch) return nm_gemm_dense_prefill(W, X, Y, rows, cols, batch, stream);
   if (!nm::aligned(W, 16) || !nm::aligned(X, 16) || !nm::aligned(Y, 2)) return NM_ERR_ALIGN;
   nm::DeviceInfo dev;
   hipError_t e = nm::current_device_info(&dev);
   if (e != hipSuccess) return nm::hip_fail(e);
-  e = nm::launch_gemm(W, X, Y, rows, cols, int(batch), static_cast<hipStream_t>(stream), dev);
-  return e == hipSuccess ? NM_OK : nm::hip_fail(e);
+  for (int64_t b0 = 0; b0 < batch; b0 += nm::kSmallBatch) {
+    const int nb = int(batch - b0 < nm::kSmallBatch ? batch - b0 : nm::kSmallBatch);
+    e = nm::launch_gemm(W, X + b0 * cols, Y + b0 * rows, rows, cols, nb, static_cast<hipStream_t>(stream), dev);
+    if (e != hipSuccess) return nm::hip_fail(e);
+  }
+  return NM_OK;
 }
 
 const char* nm_prefill_variant(int64_t rows, int64_t cols, int64_t tokens, int sparse) {

@@ -49,6 +49,11 @@ struct WorkgroupShape {
 
 // Small-batch products (1 <= batch <= kSmallBatch): X [batch][cols], Y [batch][rows].
 constexpr int64_t kSmallBatch = 8;
+// From this many vectors on, nm_spmm (2:4) and nm_gemm_dense use the matrix-core kernels;
+// below it, the small-batch kernel 8 vectors at a time (measured faster there on MI355X:
+// the matrix-core kernels pay a fixed latency per 64-column step and have few workgroups
+// when the token count is small).
+constexpr int64_t kMatrixCoreMinBatch = 32;
 hipError_t launch_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X,
                        uint16_t* Y, int64_t rows, int64_t cols, int batch, int N, int M,
                        hipStream_t stream, const DeviceInfo& dev);

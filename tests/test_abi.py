@@ -130,7 +130,8 @@ def test_probe_validation():
     (dict(values=None), nm.NM_ERR_NULL), (dict(X=None), nm.NM_ERR_NULL), (dict(Y=None), nm.NM_ERR_NULL),
     (dict(batch=0), nm.NM_ERR_SHAPE), (dict(batch=(1 << 24) + 1), nm.NM_ERR_SHAPE), (dict(cols=48), nm.NM_ERR_SHAPE),
     (dict(N=2, M=8), nm.NM_ERR_PATTERN), (dict(N=1, M=4, batch=9), nm.NM_ERR_PATTERN),
-    (dict(batch=9, X=A16 + 8), nm.NM_ERR_ALIGN), (dict(batch=9, cols=(1 << 21) + 32), nm.NM_ERR_SHAPE),
+    (dict(batch=9, X=A16 + 8), nm.NM_ERR_ALIGN), (dict(batch=40, X=A16 + 8), nm.NM_ERR_ALIGN),
+    (dict(batch=40, cols=(1 << 21) + 32), nm.NM_ERR_SHAPE),
     (dict(X=A16 + 8), nm.NM_ERR_ALIGN), (dict(Y=A16 + 1), nm.NM_ERR_ALIGN), (dict(masks=A16 + 2), nm.NM_ERR_ALIGN),
 ])
 def test_spmm_validation(kw, want):
@@ -143,7 +144,7 @@ def test_spmm_validation(kw, want):
 @pytest.mark.parametrize("kw,want", [
     (dict(W=None), nm.NM_ERR_NULL), (dict(batch=0), nm.NM_ERR_SHAPE), (dict(batch=(1 << 24) + 1), nm.NM_ERR_SHAPE),
     (dict(X=A16 + 2), nm.NM_ERR_ALIGN), (dict(batch=9, Y=A16 + 1), nm.NM_ERR_ALIGN),
-    (dict(batch=9, cols=(1 << 21) + 32), nm.NM_ERR_SHAPE),
+    (dict(batch=40, Y=A16 + 1), nm.NM_ERR_ALIGN), (dict(batch=40, cols=(1 << 21) + 32), nm.NM_ERR_SHAPE),
 ])
 def test_gemm_validation(kw, want):
     a = dict(W=A16, X=A16, Y=A16, rows=64, cols=128, batch=2)

@@ -104,19 +104,27 @@ def test_prefill_deterministic_and_unaligned_output():
 
 
 def test_batch_entry_points_route_to_prefill():
-    """nm_spmm with 2:4 and nm_gemm_dense above 8 vectors run the matrix-core kernels (same
-    bits); nm_spmm with the other 50% patterns above 8 vectors runs the small-batch kernel
-    8 vectors at a time (within tolerance of the oracle; bit-identical per group)."""
-    R, C, T = 200, 1024, 21
+    """nm_spmm with 2:4 and nm_gemm_dense from 32 vectors on run the matrix-core kernels
+    (same bits); below 32 vectors, and for the other 50% patterns at any size, the
+    small-batch kernel runs 8 vectors at a time (within tolerance of the oracle;
+    bit-identical per group)."""
+    R, C = 200, 1024
     W = synth.weight(R, C, seed=2400)
-    X = synth.activations(T, C, seed=2401)
-    Xd = up_f16(X)
+    X40 = synth.activations(40, C, seed=2402)
     rv, rm = oracle.pack_ref(W, 2, 4)
     v, m = up_f16(rv), up_u32(rm)
+    Xd = up_f16(X40)
     assert np.array_equal(down_bits16(nm.nm_spmm(v, m, Xd, 2, 4)), down_bits16(nm.nm_spmm_prefill(v, m, Xd)))
     assert np.array_equal(down_bits16(nm.nm_gemm_dense(up_f16(W), Xd)),
                           down_bits16(nm.nm_gemm_dense_prefill(up_f16(W), Xd)))
-    for N, M in ((4, 8), (8, 16), (16, 32)):
+    T = 21
+    X = synth.activations(T, C, seed=2401)
+    Xd = up_f16(X)
+    Yd = nm.nm_gemm_dense(up_f16(W), Xd)
+    drep = oracle.y_tolerance_report(down_f16(Yd), oracle.gemm_ref(W, X))
+    assert drep["ok"], drep
+    assert np.array_equal(down_bits16(Yd)[8:16], down_bits16(nm.nm_gemm_dense(up_f16(W), up_f16(X[8:16]))))
+    for N, M in ((2, 4), (4, 8), (8, 16), (16, 32)):
         rv, rm = oracle.pack_ref(W, N, M)
         v, m = up_f16(rv), up_u32(rm)
         Y = nm.nm_spmm(v, m, Xd, N, M)
