@@ -12,10 +12,13 @@ namespace {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Tile shapes (TR x TT output tiles of 16 x 16 per wave, KS columns per step, loads D steps
-// ahead), from a sweep on MI355X over 4096..14336 rows and columns at 2048 tokens: the
-// large tile (128 rows x 256 tokens per workgroup) was fastest for both products; the small
-// one (64 x 64) serves problems whose large-tile grid would leave CUs idle.
-using Large = Tile<2, 16, 64>;
+// ahead), from sweeps on MI355X over 4096..14336 rows and columns at 2048 tokens. Large
+// tiles: the sparse product 256 rows x 128 tokens per workgroup (each X fragment serves 4
+// row tiles), the dense one 128 x 256 (each weight fragment serves 16 token tiles); each was
+// the fastest for its kernel. The small tile (64 x 64) serves problems whose large-tile grid
+// would leave CUs idle.
+using SparseLarge = Tile<4, 8, 64>;
+using DenseLarge = Tile<2, 16, 64>;
 using Small = Tile<1, 4, 64>;
 constexpr int kDepth = 2;
 
@@ -24,9 +27,10 @@ int64_t workgroups(int64_t rows, int64_t tokens) {
   return ceil_div(rows, T::kRows) * ceil_div(tokens, T::kTokens);
 }
 
+template <typename T>
 bool use_large(int64_t rows, int64_t tokens, const DeviceInfo& dev) {
   const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
-  return workgroups<Large>(rows, tokens) >= cus;
+  return workgroups<T>(rows, tokens) >= cus;
 }
 
 }  // namespace
@@ -41,9 +45,9 @@ hipError_t launch_prefill_spmm(const uint16_t* values, const uint32_t* masks, co
   if (!prefill_fits(rows, cols, tokens)) return hipErrorInvalidValue;
   int r = int(rows), c = int(cols), t = int(tokens);
   void* args[] = {&values, &masks, &X, &Y, &r, &c, &t};
-  if (use_large(rows, tokens, dev))
-    return launch(reinterpret_cast<const void*>(&prefill_spmm_kernel<2, 16, 64, kDepth>),
-                  dim3(unsigned(workgroups<Large>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
+  if (use_large<SparseLarge>(rows, tokens, dev))
+    return launch(reinterpret_cast<const void*>(&prefill_spmm_kernel<4, 8, 64, kDepth>),
+                  dim3(unsigned(workgroups<SparseLarge>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
   return launch(reinterpret_cast<const void*>(&prefill_spmm_kernel<1, 4, 64, kDepth>),
                 dim3(unsigned(workgroups<Small>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
 }
@@ -53,17 +57,19 @@ hipError_t launch_prefill_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y
   if (!prefill_fits(rows, cols, tokens)) return hipErrorInvalidValue;
   int r = int(rows), c = int(cols), t = int(tokens);
   void* args[] = {&W, &X, &Y, &r, &c, &t};
-  if (use_large(rows, tokens, dev))
+  if (use_large<DenseLarge>(rows, tokens, dev))
     return launch(reinterpret_cast<const void*>(&prefill_gemm_kernel<2, 16, 64, kDepth>),
-                  dim3(unsigned(workgroups<Large>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
+                  dim3(unsigned(workgroups<DenseLarge>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
   return launch(reinterpret_cast<const void*>(&prefill_gemm_kernel<1, 4, 64, kDepth>),
                 dim3(unsigned(workgroups<Small>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
 }
 
 const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev) {
-  const bool large = use_large(rows, tokens, dev);
-  if (sparse) return large ? "prefill_spmm_kernel<2, 16, 64, 2>" : "prefill_spmm_kernel<1, 4, 64, 2>";
-  return large ? "prefill_gemm_kernel<2, 16, 64, 2>" : "prefill_gemm_kernel<1, 4, 64, 2>";
+  if (sparse)
+    return use_large<SparseLarge>(rows, tokens, dev) ? "prefill_spmm_kernel<4, 8, 64, 2>"
+                                                     : "prefill_spmm_kernel<1, 4, 64, 2>";
+  return use_large<DenseLarge>(rows, tokens, dev) ? "prefill_gemm_kernel<2, 16, 64, 2>"
+                                                  : "prefill_gemm_kernel<1, 4, 64, 2>";
 }
 
 }  // namespace nm

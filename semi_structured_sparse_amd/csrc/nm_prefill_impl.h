@@ -99,6 +99,12 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned int u2_t __attribute__((ext_vector_type(2)));
+  const u2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(v.x, v.y);
+}
+
 __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
@@ -204,12 +210,11 @@ __device__ __forceinline__ void store_all(const f4_t (&acc)[TR][TT], uint16_t* _
     for (int b = 0; b < TT; ++b) store_tile(acc[a][b], Y, rows, tokens, r0 + 16 * a + 4 * q, t0 + 16 * b + li, vec);
 }
 
-// Weight fragments of one step for the sparse product: per row tile and 64-column
-// sub-step, this lane's 8 kept values and its mask word.
+// Weight values of one step for the sparse product: per row tile and 64-column sub-step,
+// this lane's 8 kept values. (The mask words travel separately, a block of steps at a time.)
 template <int TR, int SUB>
 struct SparseA {
   uint4 v[TR][SUB];
-  uint32_t m[TR][SUB];
 };
 
 // Weight fragments of one step for the dense product: per row tile and 32-column slice.
@@ -218,17 +223,18 @@ struct DenseA {
   uint4 v[TR][2 * SUB];
 };
 
-// The main loop shared by both products. X goes global -> registers -> LDS (two buffers),
-// weights global -> registers, D steps ahead. Step s: barrier; write X of step s + 1 (its
-// loads were issued D - 1 steps earlier) into buffer (s + 1) & 1, last read in step s - 1,
-// which every wave has finished by the barrier; take this step's weight set; issue the
-// loads of step s + D into the freed register sets; compute on buffer s & 1. Steps are
-// unrolled D at a time so every register set has a fixed name; the steps past the last
-// one (up to D - 1) skip only the math, and their loads repeat the last step, so the
-// loads and waits stay the same in every step.
+// The dense product's main loop. X goes global -> registers -> LDS (two buffers), weights
+// global -> registers, D steps ahead. Step s: barrier; write X of step s + 1 (its loads were
+// issued D - 1 steps earlier) into buffer (s + 1) & 1, last read in step s - 1, which every
+// wave has finished by the barrier; take this step's weight set; issue the loads of step
+// s + D into the freed register sets; compute on buffer s & 1. Steps are unrolled D at a
+// time so every register set has a fixed name; the steps past the last one (up to D - 1)
+// skip only the math, and their loads repeat the last step, so the loads and waits stay
+// the same in every step.
 template <int TR, int TT, int KS, int D, typename AFrag, typename LoadA, typename Compute>
-__device__ __forceinline__ void main_loop(const XStager<TR, TT, KS>& xst, char (*xs)[Tile<TR, TT, KS>::kXBytes],
-                                          int cols, LoadA load_a, Compute compute) {
+__device__ __forceinline__ void dense_main_loop(const XStager<TR, TT, KS>& xst,
+                                                char (*xs)[Tile<TR, TT, KS>::kXBytes], int cols, LoadA load_a,
+                                                Compute compute) {
   using T = Tile<TR, TT, KS>;
   const int steps = (cols + KS - 1) / KS;
   const int last = (steps - 1) * KS;
@@ -253,6 +259,53 @@ __device__ __forceinline__ void main_loop(const XStager<TR, TT, KS>& xst, char (
       load_a(af[p], cn);
       if (s < steps) compute(cur, xs[s & 1]);
     }
+  }
+}
+
+// Calls f(integral_constant<int, P>) for P = P0 .. U - 1, in order.
+template <int P0, int U, typename F>
+__device__ __forceinline__ void unroll_slots(F& f) {
+  if constexpr (P0 < U) {
+    f(std::integral_constant<int, P0>());
+    unroll_slots<P0 + 1, U>(f);
+  }
+}
+
+// The sparse product's main loop: the dense one's schedule, unrolled U steps at a time (U a
+// multiple of D) so that every slot of a mask block has a fixed name, with a hook per slot
+// (run after the slot's loads are issued) for the mask-block loads. Steps past the last one
+// (up to U - 1) skip only the math.
+template <int TR, int TT, int KS, int D, int U, typename AFrag, typename LoadA, typename Hook, typename Compute>
+__device__ __forceinline__ void sparse_main_loop(const XStager<TR, TT, KS>& xst,
+                                                 char (*xs)[Tile<TR, TT, KS>::kXBytes], int cols, LoadA load_a,
+                                                 Hook hook, Compute compute) {
+  static_assert(U % D == 0, "unroll must be a multiple of the load depth");
+  using T = Tile<TR, TT, KS>;
+  const int steps = (cols + KS - 1) / KS;
+  const int last = (steps - 1) * KS;
+  uint4 xr[D][T::kXPerThread];
+  AFrag af[D];
+#pragma unroll
+  for (int p = 0; p < D; ++p) {
+    const int c = min(p * KS, last);
+    xst.load(xr[p], c, cols);
+    load_a(af[p], c);
+  }
+  xst.store(xr[0], xs[0]);
+  for (int s0 = 0; s0 < steps; s0 += U) {
+    auto slot = [&](auto pc) {
+      constexpr int P = decltype(pc)::value;
+      const int s = s0 + P;
+      __syncthreads();
+      xst.store(xr[(P + 1) % D], xs[(s + 1) & 1]);
+      const AFrag cur = af[P % D];
+      const int cn = min((s + D) * KS, last);
+      xst.load(xr[P % D], cn, cols);
+      load_a(af[P % D], cn);
+      hook(pc, s0);
+      if (s < steps) compute(cur, xs[s & 1], pc);
+    };
+    unroll_slots<0, U>(slot);
   }
 }
 
@@ -287,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void prefill_spmm_kernel(const uint16_t* 
   for (int a = 0; a < TR; ++a) {
     const uint32_t rl = uint32_t(wave * 16 * TR + 16 * a + li);
     voff[a] = rl * uint32_t(cols) + 16u * uint32_t(q);          // values 8q.. of the step
-    moff[a] = rl * uint32_t(words) * 4u + 4u * uint32_t(q >> 1);  // mask word q >> 1 of the step
+    moff[a] = rl * uint32_t(words) * 4u + 8u * uint32_t(q);      // mask words 2q, 2q + 1 of a block
   }
   const int qcol = 32 * (q >> 1);  // first column of this lane's mask word in a sub-step
   const int mshift = 16 * (q & 1);
@@ -298,53 +351,71 @@ __global__ __launch_bounds__(kThreads) void prefill_spmm_kernel(const uint16_t* 
       const int c = c0 + 64 * u;
       const bool ok = c + qcol < cols;
 #pragma unroll
-      for (int a = 0; a < TR; ++a) {
-        f.v[a][u] = buf_load16(vr, ok ? voff[a] + uint32_t(c) : kOutOfRange);
-        f.m[a][u] = buf_load4(mr, ok ? moff[a] + uint32_t(c >> 3) : kOutOfRange);
-      }
+      for (int a = 0; a < TR; ++a) f.v[a][u] = buf_load16(vr, ok ? voff[a] + uint32_t(c) : kOutOfRange);
     }
+  };
+
+  // Mask words, a block of kMaskSteps 64-column steps (2 kMaskSteps words of each row) at
+  // a time: lane q of row li holds words 2q, 2q + 1 of the block (one 8-byte load per row
+  // tile per block instead of one 4-byte load per step; a load touches the same 16 rows
+  // either way). At step j of the block the lane needs word 2j + (q >> 1), which lane
+  // li + 16 j holds in half q >> 1; a cross-lane permute fetches it. The block for the next
+  // steps is loaded kMaskSteps - D steps into the current one, D steps ahead like the values.
+  constexpr int kMaskSteps = 4;
+  static_assert(KS == 64, "mask blocks are laid out for 64-column steps");
+  const int steps = (cols + KS - 1) / KS;
+  const int last_block = (steps - 1) / kMaskSteps;
+  uint2 mcur[TR], mnext[TR];
+  auto load_masks = [&](int blk) {
+#pragma unroll
+    for (int a = 0; a < TR; ++a) mnext[a] = buf_load8(mr, moff[a] + uint32_t(32 * min(blk, last_block)));
+  };
+  load_masks(0);
+  auto hook = [&](auto pc, int s0) {
+    constexpr int P = decltype(pc)::value;
+    if constexpr (P == 0) {
+#pragma unroll
+      for (int a = 0; a < TR; ++a) mcur[a] = mnext[a];
+    }
+    if constexpr (P == kMaskSteps - D) load_masks(s0 / kMaskSteps + 1);
   };
 
   f4_t acc[TR][TT];
   zero(acc);
-  // X fragment of token 16 b + li: column chunks q and 4 + q of each 64-column sub-step
-  uint32_t b_lo[SUB], b_hi[SUB];
+  // X fragment of token 16 b + li: column chunks q and 4 + q of the step
+  const uint32_t b_lo = x_offset<T::kRowBytes>(li, q), b_hi = x_offset<T::kRowBytes>(li, 4 + q);
+  auto compute = [&](const AF& f, const char* buf, auto pc) {
+    constexpr int J = decltype(pc)::value;           // step within the mask block
+    const int src = 4 * (li + 16 * J);               // byte address of lane li + 16 J
+    h8_t av[TR];
+    int idx[TR];
 #pragma unroll
-  for (int u = 0; u < SUB; ++u) {
-    b_lo[u] = x_offset<T::kRowBytes>(li, 8 * u + q);
-    b_hi[u] = x_offset<T::kRowBytes>(li, 8 * u + 4 + q);
-  }
-  auto compute = [&](const AF& f, const char* buf) {
+    for (int a = 0; a < TR; ++a) {
+      av[a] = __builtin_bit_cast(h8_t, f.v[a][0]);
+      const uint32_t w0 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur[a].x)));
+      const uint32_t w1 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur[a].y)));
+      idx[a] = index_word((((q >> 1) ? w1 : w0) >> mshift) & 0xFFFFu);
+    }
+    // X fragments are read one token tile ahead of the math that uses them
+    uint4 lo[2], hi[2];
+    lo[0] = lds_read16(buf, b_lo);
+    hi[0] = lds_read16(buf, b_hi);
 #pragma unroll
-    for (int u = 0; u < SUB; ++u) {
-      h8_t av[TR];
-      int idx[TR];
-#pragma unroll
-      for (int a = 0; a < TR; ++a) {
-        av[a] = __builtin_bit_cast(h8_t, f.v[a][u]);
-        idx[a] = index_word((f.m[a][u] >> mshift) & 0xFFFFu);
+    for (int b = 0; b < TT; ++b) {
+      if (b + 1 < TT) {
+        const char* tb = buf + (b + 1) * 16 * T::kRowBytes;
+        lo[(b + 1) & 1] = lds_read16(tb, b_lo);
+        hi[(b + 1) & 1] = lds_read16(tb, b_hi);
       }
-      // X fragments are read one token tile ahead of the math that uses them
-      uint4 lo[2], hi[2];
-      lo[0] = lds_read16(buf, b_lo[u]);
-      hi[0] = lds_read16(buf, b_hi[u]);
+      const uint4 l = lo[b & 1], h = hi[b & 1];
+      const u8_t xv = {l.x, l.y, l.z, l.w, h.x, h.y, h.z, h.w};
+      const h16_t bf = __builtin_bit_cast(h16_t, xv);
 #pragma unroll
-      for (int b = 0; b < TT; ++b) {
-        if (b + 1 < TT) {
-          const char* tb = buf + (b + 1) * 16 * T::kRowBytes;
-          lo[(b + 1) & 1] = lds_read16(tb, b_lo[u]);
-          hi[(b + 1) & 1] = lds_read16(tb, b_hi[u]);
-        }
-        const uint4 l = lo[b & 1], h = hi[b & 1];
-        const u8_t xv = {l.x, l.y, l.z, l.w, h.x, h.y, h.z, h.w};
-        const h16_t bf = __builtin_bit_cast(h16_t, xv);
-#pragma unroll
-        for (int a = 0; a < TR; ++a)
-          acc[a][b] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(av[a], bf, acc[a][b], idx[a], 0, 0);
-      }
+      for (int a = 0; a < TR; ++a)
+        acc[a][b] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(av[a], bf, acc[a][b], idx[a], 0, 0);
     }
   };
-  main_loop<TR, TT, KS, D, AF>(xst, xs, cols, load_a, compute);
+  sparse_main_loop<TR, TT, KS, D, kMaskSteps, AF>(xst, xs, cols, load_a, hook, compute);
   store_all(acc, Y, rows, tokens, r0, t0, lane);
 }
 
@@ -409,7 +480,7 @@ __global__ __launch_bounds__(kThreads) void prefill_gemm_kernel(const uint16_t* 
       }
     }
   };
-  main_loop<TR, TT, KS, D, AF>(xst, xs, cols, load_a, compute);
+  dense_main_loop<TR, TT, KS, D, AF>(xst, xs, cols, load_a, compute);
   store_all(acc, Y, rows, tokens, r0, t0, lane);
 }
 

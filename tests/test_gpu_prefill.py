@@ -17,12 +17,13 @@ from tests.gpu_helpers import device, down_bits16, down_f16, down_u32, sample_ro
 
 pytestmark = pytest.mark.gpu
 
-# (rows, cols, tokens): ragged rows (tiles of 16, 64 and 128 rows), ragged tokens (tiles of
-# 16, 64 and 256), a 32-column tail step, one step, many steps; small and large tile
-# configurations (the large one needs at least one workgroup per CU)
+# (rows, cols, tokens): ragged rows (tiles of 16, 64, 128 and 256 rows), ragged tokens
+# (tiles of 16, 64, 128 and 256), a 32-column tail step, one step, many steps, a last block
+# of mask steps cut short; small and large tile configurations (the large ones need at
+# least one workgroup per CU)
 SMALL = [(1, 32, 1), (17, 64, 5), (16, 96, 16), (33, 128, 17), (64, 4064, 63), (65, 4096, 64),
          (127, 544, 65), (300, 1056, 255), (129, 2080, 257), (1000, 4064, 700), (4100, 1024, 2050),
-         (4096, 160, 2048)]
+         (4096, 160, 2048), (2600, 2208, 3000)]
 
 
 def check_prefill(W, X, tag, rows_idx=None, dense=True):
@@ -60,7 +61,7 @@ def test_prefill_small_and_ragged():
 def test_prefill_both_tile_configurations_are_exercised():
     """The shapes above cover the small and the large tile configuration of both products."""
     names = {nm.prefill_variant(R, C, T, s) for R, C, T in SMALL for s in (True, False)}
-    assert names == {"prefill_spmm_kernel<1, 4, 64, 2>", "prefill_spmm_kernel<2, 16, 64, 2>",
+    assert names == {"prefill_spmm_kernel<1, 4, 64, 2>", "prefill_spmm_kernel<4, 8, 64, 2>",
                      "prefill_gemm_kernel<1, 4, 64, 2>", "prefill_gemm_kernel<2, 16, 64, 2>"}, names
 
 
