@@ -358,16 +358,18 @@ def main():
     for i, L in enumerate(layers):
         us = per_s[i]
         kname = nm.spmv_variant(L["R"], L["C"], L["N"], L["M"]) if B == 1 else \
-            f"spmm_kernel<{L['N']}, {B}, {0 if L['N'] == 16 else 2}>"
+            nm.spmm_variant(L["R"], L["C"], B, L["N"], L["M"])
         kern_bytes[kname] = kern_bytes.get(kname, 0) + L["bytes"]
         kern_us[kname] = kern_us.get(kname, 0.0) + us
         kern_n[kname] = kern_n.get(kname, 0) + 1
         dus = per_d[(L["R"], L["C"])]
         gbps = L["bytes"] / (us * 1e-6) / 1e9
-        ls = nm.spmv_launch_shape(L["R"], L["C"], L["N"], L["M"])   # (batch > 1: before the 768-thread cap)
+        ls = nm.spmv_launch_shape(L["R"], L["C"], L["N"], L["M"])
+        wg = {"workgroups": ls["workgroups"],
+              "workgroup": f"{ls['rows_per_workgroup']} rows, {ls['row_groups']}x{ls['waves_per_row_group']} waves"} \
+            if B == 1 else {}
         per_layer.append({"layer": L["name"], "shape": f"{L['R']}x{L['C']}", "pattern": f"{L['N']}:{L['M']}",
-                          "kernel": kname, "workgroups": ls["workgroups"],
-                          "workgroup": f"{ls['rows_per_workgroup']} rows, {ls['row_groups']}x{ls['waves_per_row_group']} waves",
+                          "kernel": kname, **wg,
                           "us": round(us, 2), "GBps": round(gbps, 1),
                           "pct_peak": round(gbps / HBM_PEAK_GBPS, 4),
                           "dense_us": round(dus, 2), "speedup": round(dus / us, 3)})

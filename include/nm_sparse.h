@@ -110,7 +110,9 @@ int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,
  *     result as nm_spmv within the tolerance of the product (it may use another summation
  *     order).
  *   - batch >= 32 with 2:4: nm_spmm_prefill (matrix cores), with its limits.
- *   - other batches > 8 (2:4 below 32, and 4:8, 8:16, 16:32): the small-batch kernel on
+ *   - 5 <= batch < 32 with 2:4 on layers of at least 2048 rows: the sparse matrix
+ *     instruction with X staged whole in LDS, 16 vectors per launch (cols <= 2^21).
+ *   - other batches > 8 (2:4 otherwise, and 4:8, 8:16, 16:32): the small-batch kernel on
  *     consecutive groups of 8 rows of X (one launch per group; vector units only).
  * The 25% patterns are accepted for batch == 1 only (and cols <= nm_max_cols()); larger
  * batches of them return NM_ERR_PATTERN. X must be 16-byte aligned, Y 2-byte aligned;
@@ -143,6 +145,11 @@ int nm_spmm_prefill(const uint16_t* values, const uint32_t* masks, const uint16_
  * instruction's fixed order. Same limits and alignment as nm_spmm_prefill (W 16-byte). */
 int nm_gemm_dense_prefill(const uint16_t* W, const uint16_t* X, uint16_t* Y,
                           int64_t rows, int64_t cols, int64_t tokens, void* stream);
+
+/* Introspection: the name of the kernel nm_spmm launches for this shape, batch and pattern
+ * on the current device (for more than one launch, the kernel of the first); "" if the
+ * arguments are invalid. Static string, never NULL. */
+const char* nm_spmm_variant(int64_t rows, int64_t cols, int64_t batch, int N, int M);
 
 /* Introspection: the name of the kernel configuration nm_spmm_prefill (sparse != 0) or
  * nm_gemm_dense_prefill (sparse == 0) launches for this shape on the current device, as it

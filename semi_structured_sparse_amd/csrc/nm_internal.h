@@ -60,6 +60,10 @@ hipError_t launch_spmm(const uint16_t* values, const uint32_t* masks, const uint
 hipError_t launch_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y, int64_t rows,
                        int64_t cols, int batch, hipStream_t stream, const DeviceInfo& dev);
 
+// Name of the small-batch kernel instantiation launch_spmm runs for pattern N:2N and a
+// batch of 1..8 vectors (static string; "" otherwise).
+const char* spmm_variant(int N, int64_t batch);
+
 // Name of the kernel configuration launch_spmv picks (static string) and its shape.
 const char* spmv_variant(int64_t rows, int64_t cols, int N, int M, const DeviceInfo& dev);
 WorkgroupShape spmv_shape(int64_t rows, int64_t cols, const DeviceInfo& dev);
@@ -79,6 +83,19 @@ hipError_t launch_prefill_spmm(const uint16_t* values, const uint32_t* masks, co
                                int64_t rows, int64_t cols, int64_t tokens, hipStream_t stream, const DeviceInfo& dev);
 hipError_t launch_prefill_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y, int64_t rows, int64_t cols,
                                int64_t tokens, hipStream_t stream, const DeviceInfo& dev);
+// Small-batch 2:4 product on the sparse matrix instruction, 1..16 tokens (X [tokens][cols],
+// Y [tokens][rows]); skinny_fits tells whether a shape is within its limits.
+bool skinny_fits(int64_t rows, int64_t cols, int64_t tokens, const DeviceInfo& dev);
+hipError_t launch_skinny_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
+                              int64_t rows, int64_t cols, int tokens, hipStream_t stream, const DeviceInfo& dev);
+// nm_spmm with 2:4 runs the skinny kernel for kSkinnyMinBatch <= batch < kMatrixCoreMinBatch
+// on layers of at least kSkinnyMinRows rows, kSkinnyBatch vectors per launch (measured on
+// MI355X: from 5 vectors on it beats the small-batch kernel on such layers; on smaller ones
+// its fixed cost of a few microseconds does not pay).
+constexpr int64_t kSkinnyMinBatch = 5;
+constexpr int64_t kSkinnyMinRows = 2048;
+constexpr int64_t kSkinnyBatch = 16;
+
 // Name of the kernel configuration the prefill launchers pick (static string).
 const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev);
 

@@ -1,0 +1,196 @@
+// Small-batch 2:4 product on the gfx950 sparse matrix instruction: Y [tokens][rows] =
+// X [tokens][cols] W'^T for 1 <= tokens <= 16, W' given as the packed 2:4 values and
+// bitmask (the batch side of the SpMV / SpMM split the news.bitwarelabs.com page draws in
+// "What's new"; bitmask format of the aimodeling.com page, "The Kernel Is the Other Half of
+// the Answer").
+//
+// With at most 16 tokens the product is bound by reading the packed weights once, like the
+// batch-one SpMV, so the kernel is laid out like the SpMV: a workgroup holds RG row groups
+// of 16 * TR rows, each split over CS waves along the columns; X of all tokens sits in LDS
+// (in column phases when it does not fit); each wave streams its rows' values and masks
+// with no barrier in its loop and multiplies them on the sparse matrix instruction (one
+// 16 x 16 x 64 instruction per 16 rows and 64 columns covers every token), and the CS
+// partial tiles of a row group are summed through LDS at the end.
+//
+// Operand layouts, the K permutation that makes a lane's 8 values contiguous in the packed
+// row, the index-word table and the mask-block permute are those of the prefill kernel
+// (nm_prefill_impl.h): lane (q = l / 16, li = l % 16) holds values 8q .. 8q+7 of a 64-column
+// step for row li, and the X fragment of token li at column chunks q and 4 + q of the step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nm_prefill_impl.h"
+
+namespace nm {
+namespace skinny_detail {
+
+using namespace prefill_detail;
+
+constexpr int kMaxWaves = 16;
+constexpr int kMaxTokens = 16;
+constexpr int kMaskSteps = 4;   // 64-column steps per mask block
+constexpr int kDepth = 4;       // value loads in flight per row tile
+constexpr int kThreadsFixed = 64 * kMaxWaves;           // every launch uses 16 waves
+constexpr int kXChunksPerThread = 8;                    // X staged per phase: <= 8 x 16 B per thread
+constexpr size_t kMaxXBytes = size_t(kThreadsFixed) * kXChunksPerThread * 16;   // 128 KiB
+
+// LDS bytes of the X buffer for `tokens` rows of `phase_cols` columns, and of the reduction
+// area for `waves` waves of TR tiles (one float4 per lane per tile).
+__host__ __device__ inline size_t x_bytes(int tokens, int phase_cols) { return size_t(tokens) * phase_cols * 2; }
+__host__ __device__ inline size_t red_bytes(int waves, int tr) { return size_t(waves) * tr * 64 * 16; }
+
+// LDS byte offset of 16-byte chunk c of token t, rows of rb bytes: the low 3 bits of the
+// chunk index are XORed with the token's (8 tokens read at a time land on 8 bank groups).
+__device__ __forceinline__ uint32_t xoff(int t, int c, uint32_t rb) {
+  return uint32_t(t) * rb + (uint32_t(c ^ (t & 7)) << 4);
+}
+
+template <int TR>
+__global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16_t* __restrict__ values,
+                                                                     const uint32_t* __restrict__ masks,
+                                                                     const uint16_t* __restrict__ X,
+                                                                     uint16_t* __restrict__ Y, int rows, int cols,
+                                                                     int tokens, int rg_count, int cs_count,
+                                                                     int phase_cols) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, li = lane & 15;
+  const int rg = wave / cs_count, cs = wave - rg * cs_count;
+  const int wg_rows_max = rg_count * 16 * TR;
+  const int wg_r0 = int(blockIdx.x) * wg_rows_max;
+  const int wg_rows = min(wg_rows_max, rows - wg_r0);
+  const int words = cols >> 5;
+
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(values + size_t(wg_r0) * unsigned(cols >> 1), int64_t(wg_rows) * cols);
+  const __amdgpu_buffer_rsrc_t mr = make_rsrc(masks + size_t(wg_r0) * unsigned(words), int64_t(wg_rows) * words * 4);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, int64_t(tokens) * cols * 2);
+  uint32_t voff[TR], moff[TR];
+#pragma unroll
+  for (int a = 0; a < TR; ++a) {
+    const uint32_t rl = uint32_t(rg * 16 * TR + 16 * a + li);   // row within the workgroup
+    voff[a] = rl * uint32_t(cols) + 16u * uint32_t(q);
+    moff[a] = rl * uint32_t(words) * 4u + 8u * uint32_t(q);
+  }
+  const int qcol = 32 * (q >> 1);
+  const int mshift = 16 * (q & 1);
+  const bool tok_live = li < tokens;
+
+  f4_t acc[TR];
+#pragma unroll
+  for (int a = 0; a < TR; ++a) acc[a] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 vb[kDepth][TR];
+  uint2 mcur[TR], mnext[TR];
+  for (int p0 = 0; p0 < cols; p0 += phase_cols) {
+    const int pc = min(phase_cols, cols - p0);       // columns in this phase (multiple of 32)
+    const uint32_t rb = uint32_t(2 * phase_cols);    // LDS bytes per token row
+    // this wave's steps of the phase
+    const int psteps = (pc + 63) / 64;
+    const int s_lo = int((int64_t(psteps) * cs) / cs_count), s_hi = int((int64_t(psteps) * (cs + 1)) / cs_count);
+    const int n = s_hi - s_lo;
+    const int last = max(n - 1, 0);
+    auto col_of = [&](int s) { return p0 + 64 * (s_lo + min(s, last)); };
+    // steps past the range (the last block's padding) load zeros and read no X, so they
+    // add exactly zero and every slot of a block runs the same code
+    auto load_v = [&](uint4 (&f)[TR], int s) {
+      const int c = col_of(s);
+      const bool ok = s < n && c + qcol < cols;
+#pragma unroll
+      for (int a = 0; a < TR; ++a) f[a] = buf_load16(vr, ok ? voff[a] + uint32_t(c) : kOutOfRange);
+    };
+    auto load_m = [&](int s) {   // mask block starting at step s of the range
+      const int c = col_of(s);
+#pragma unroll
+      for (int a = 0; a < TR; ++a) mnext[a] = buf_load8(mr, n > 0 ? moff[a] + uint32_t(c >> 3) : kOutOfRange);
+    };
+    // ---- X[0 .. tokens)[p0 .. p0 + pc) into registers (columns past the row read as zero):
+    // flat chunk k = tid + kThreadsFixed * j, token k / chunks; chunks past the end load out
+    // of range (zero) and are not written
+    const int chunks = psteps * 8;                   // 16-byte chunks per token row, whole steps
+    const int nchunks = tokens * chunks;
+    uint4 xs[kXChunksPerThread];
+    uint32_t xdst[kXChunksPerThread];
+#pragma unroll
+    for (int j = 0; j < kXChunksPerThread; ++j) {
+      const int k = tid + kThreadsFixed * j;
+      const int t = k / chunks, c = k - t * chunks;
+      const int col = p0 + 8 * c;
+      const bool ok = k < nchunks && col < cols;
+      xs[j] = buf_load16(xr, ok ? (uint32_t(t) * uint32_t(cols) + uint32_t(col)) * 2u : kOutOfRange);
+      xdst[j] = k < nchunks ? xoff(t, c, rb) : 0xFFFFFFFFu;
+    }
+    // then the first weight loads: they are in flight while X is written to LDS (the X
+    // loads were issued first, so waiting for them does not wait for these). The mask
+    // block goes first, as in the loop (mask block, then the block's value loads), so the
+    // waits the loop needs are the same on its first pass as on later ones.
+    load_m(0);
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) load_v(vb[d], d);
+    __syncthreads();                                 // the previous phase's LDS reads are done
+#pragma unroll
+    for (int j = 0; j < kXChunksPerThread; ++j)
+      if (xdst[j] != 0xFFFFFFFFu) *reinterpret_cast<uint4*>(lds + xdst[j]) = xs[j];
+    __syncthreads();
+    if (n > 0) {
+      const uint32_t b_lo = xoff(li, q, rb), b_hi = xoff(li, 4 + q, rb);
+      for (int s0 = 0; s0 < n; s0 += kMaskSteps) {
+#pragma unroll
+        for (int a = 0; a < TR; ++a) mcur[a] = mnext[a];
+        load_m(s0 + kMaskSteps);
+#pragma unroll
+        for (int j = 0; j < kMaskSteps; ++j) {
+          const int s = s0 + j;
+          // the products read vb[j] in place; its next load is issued after them, so the
+          // registers are never copied (a copy would wait for every load in flight)
+          const uint4 (&cur)[TR] = vb[j % kDepth];
+          const uint32_t cb = uint32_t(s_lo + min(s, last)) * 128u;   // the step's chunks start at chunk 8 (s_lo + s)
+          const int src = 4 * (li + 16 * j);
+          uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+          if (tok_live && s < n) {
+            lo = *reinterpret_cast<const uint4*>(lds + b_lo + cb);
+            hi = *reinterpret_cast<const uint4*>(lds + b_hi + cb);
+          }
+          const u8_t xv = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          const h16_t bf = __builtin_bit_cast(h16_t, xv);
+#pragma unroll
+          for (int a = 0; a < TR; ++a) {
+            const uint32_t w0 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur[a].x)));
+            const uint32_t w1 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur[a].y)));
+            const int idx = index_word((((q >> 1) ? w1 : w0) >> mshift) & 0xFFFFu);
+            acc[a] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(h8_t, cur[a]), bf, acc[a], idx, 0, 0);
+          }
+          load_v(vb[j % kDepth], s + kDepth);
+        }
+      }
+    }
+  }
+  // ---- sum the CS partial tiles of each row group; the first wave of the group stores
+  __syncthreads();
+  float4* red = reinterpret_cast<float4*>(lds);
+#pragma unroll
+  for (int a = 0; a < TR; ++a)
+    red[(wave * TR + a) * 64 + lane] = make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
+  __syncthreads();
+  if (cs != 0) return;
+#pragma unroll
+  for (int a = 0; a < TR; ++a) {
+    float4 s = red[(wave * TR + a) * 64 + lane];
+    for (int w = 1; w < cs_count; ++w) {
+      const float4 v = red[((wave + w) * TR + a) * 64 + lane];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    const int row = wg_r0 + rg * 16 * TR + 16 * a + 4 * q;
+    if (!tok_live || row >= rows) continue;
+    uint16_t* out = Y + size_t(li) * unsigned(rows);
+    const float e[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (row + k < rows) out[row + k] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(e[k]));
+  }
+}
+
+}  // namespace skinny_detail
+}  // namespace nm

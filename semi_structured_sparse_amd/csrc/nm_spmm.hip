@@ -118,6 +118,18 @@ hipError_t launch_spmm(const uint16_t* values, const uint32_t* masks, const uint
   }
 }
 
+const char* spmm_variant(int N, int64_t batch) {
+  // the instantiations launch_sparse_b picks: byte table for N = 2, 4, 8, bit walk for 16
+  static const char* const kNames[4][8] = {
+      {"spmm_kernel<2, 1, 2>", "spmm_kernel<2, 2, 2>", "spmm_kernel<2, 3, 2>", "spmm_kernel<2, 4, 2>", "spmm_kernel<2, 5, 2>", "spmm_kernel<2, 6, 2>", "spmm_kernel<2, 7, 2>", "spmm_kernel<2, 8, 2>"},
+      {"spmm_kernel<4, 1, 2>", "spmm_kernel<4, 2, 2>", "spmm_kernel<4, 3, 2>", "spmm_kernel<4, 4, 2>", "spmm_kernel<4, 5, 2>", "spmm_kernel<4, 6, 2>", "spmm_kernel<4, 7, 2>", "spmm_kernel<4, 8, 2>"},
+      {"spmm_kernel<8, 1, 2>", "spmm_kernel<8, 2, 2>", "spmm_kernel<8, 3, 2>", "spmm_kernel<8, 4, 2>", "spmm_kernel<8, 5, 2>", "spmm_kernel<8, 6, 2>", "spmm_kernel<8, 7, 2>", "spmm_kernel<8, 8, 2>"},
+      {"spmm_kernel<16, 1, 0>", "spmm_kernel<16, 2, 0>", "spmm_kernel<16, 3, 0>", "spmm_kernel<16, 4, 0>", "spmm_kernel<16, 5, 0>", "spmm_kernel<16, 6, 0>", "spmm_kernel<16, 7, 0>", "spmm_kernel<16, 8, 0>"}};
+  const int n = N == 2 ? 0 : N == 4 ? 1 : N == 8 ? 2 : N == 16 ? 3 : -1;
+  if (n < 0 || batch < 1 || batch > 8) return "";
+  return kNames[n][batch - 1];
+}
+
 hipError_t launch_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y, int64_t rows, int64_t cols,
                        int batch, hipStream_t stream, const DeviceInfo& dev) {
   if (batch == 1 && cols <= max_cols_for(dev)) return launch_gemv(W, X, Y, rows, cols, stream, dev);

@@ -179,6 +179,16 @@ def test_gemm_prefill_validation(kw, want):
     assert nm.lib().nm_gemm_dense_prefill(a["W"], a["X"], a["Y"], a["rows"], a["cols"], a["tokens"], None) == want
 
 
+def test_spmm_variant_validation():
+    """Invalid arguments give the empty name before any HIP call."""
+    L = nm.lib()
+    assert L.nm_spmm_variant(0, 128, 4, 2, 4) == b""
+    assert L.nm_spmm_variant(64, 80, 4, 2, 4) == b""
+    assert L.nm_spmm_variant(64, 128, 0, 2, 4) == b""
+    assert L.nm_spmm_variant(64, 128, 4, 3, 4) == b""
+    assert L.nm_spmm_variant(64, 128, 4, 1, 4) == b""   # 25% patterns: one vector only
+
+
 def test_prefill_variant_validation():
     """Invalid shapes give the empty name before any HIP call."""
     L = nm.lib()

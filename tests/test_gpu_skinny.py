@@ -1,0 +1,94 @@
+"""GPU parity tests of the small-batch 2:4 product on the sparse matrix instruction (nm_spmm
+with 5..31 vectors on layers of at least 2048 rows), through the C ABI, against the CPU
+oracle (spmm_ref).
+
+Bars: Y within |y - ref| <= 2e-3 + 1e-2*|ref| per element and relative L2 <= 1e-3 (fp32
+accumulation in the matrix instruction, fp16 output, fp64 oracle); exact special cases
+(one-hot X) and determinism bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import semi_structured_sparse_amd as nm
+import synth
+from tests.gpu_helpers import device, down_bits16, down_f16, down_u32, sample_rows, say, up_f16, up_u32
+
+pytestmark = pytest.mark.gpu
+SKINNY = "skinny_spmm_kernel<1>"
+
+# (rows, cols, vectors): ragged rows (16-row tiles, row groups of 1..4 tiles), a 32-column
+# tail step, steps split over 16 / 8 / 4 waves, X in several column phases (16 vectors x
+# 14336 columns > 128 KiB), more than 16 vectors (two launches), 5..31 vectors
+CASES = [(2048, 96, 5), (2049, 1056, 8), (2100, 4064, 16), (4100, 1024, 11), (4096, 14336, 16),
+         (4100, 14368, 13), (9000, 2080, 17), (14336, 4096, 8), (2600, 544, 31), (16400, 288, 6)]
+
+
+def check(R, C, T, seed, rows_idx=None):
+    W = synth.weight(R, C, seed)
+    X = synth.activations(T, C, seed + 1)
+    values, masks = nm.nm_pack(up_f16(W), 2, 4)
+    Y = down_f16(nm.nm_spmm(values, masks, up_f16(X), 2, 4))
+    idx = np.arange(R) if rows_idx is None else rows_idx
+    it = torch.from_numpy(idx).to(device())
+    rv, rm = oracle.pack_ref(W[idx], 2, 4)
+    assert np.array_equal(down_u32(masks.index_select(0, it)), rm)
+    assert np.array_equal(down_bits16(values.index_select(0, it)), rv)
+    rep = oracle.y_tolerance_report(Y[:, idx], oracle.spmm_ref(rv, rm, X, C, 2, 4))
+    assert rep["ok"], ((R, C, T), rep)
+    return rep
+
+
+@pytest.mark.parametrize("R,C,T", CASES)
+def test_skinny_parity(R, C, T):
+    assert nm.spmm_variant(R, C, T, 2, 4) == SKINNY
+    say(f"skinny {R}x{C} vectors={T}")
+    check(R, C, T, 3000 + R % 97 + C % 89 + T, sample_rows(R, k=32, rpb=16))
+
+
+def test_skinny_routing():
+    """Which kernel nm_spmm picks: the sparse matrix instruction for 2:4 at 5..31 vectors on
+    layers of >= 2048 rows; the small-batch kernel below 5 vectors, on smaller layers and
+    for the other patterns; the prefill kernel from 32 vectors on."""
+    assert nm.spmm_variant(4096, 4096, 4, 2, 4) == "spmm_kernel<2, 4, 2>"
+    assert nm.spmm_variant(2047, 4096, 8, 2, 4) == "spmm_kernel<2, 8, 2>"
+    assert nm.spmm_variant(4096, 4096, 8, 4, 8) == "spmm_kernel<4, 8, 2>"
+    assert nm.spmm_variant(4096, 4096, 20, 16, 32) == "spmm_kernel<16, 8, 0>"
+    assert nm.spmm_variant(4096, 4096, 5, 2, 4) == SKINNY
+    assert nm.spmm_variant(4096, 4096, 31, 2, 4) == SKINNY
+    assert nm.spmm_variant(4096, 4096, 32, 2, 4).startswith("prefill_spmm_kernel")
+    assert nm.spmm_variant(4096, 4096, 1, 2, 4).startswith("spmv_kernel")
+
+
+def test_skinny_one_hot_and_determinism():
+    """X = 16 rows of the identity (columns 0, 37, ..., spread over the row): token t gives
+    column c_t of the pruned matrix bit-exactly; repeated calls give the same bits."""
+    R, C = 2080, 4096
+    W = synth.weight(R, C, 3100)
+    rv, rm = oracle.pack_ref(W, 2, 4)
+    D = oracle.unpack_ref(rv, rm, C, 2, 4)
+    cols = [0, 37, 255, 256, 1000, 2047, 2048, 3001, 4000, 4095, 63, 64, 1, 2, 3, 4094]
+    X = np.zeros((16, C), np.float16)
+    for t, c in enumerate(cols):
+        X[t, c] = 1.0
+    v, m = up_f16(rv), up_u32(rm)
+    Y = down_bits16(nm.nm_spmm(v, m, up_f16(X), 2, 4))
+    want = D[:, cols].T.copy()
+    want[want == 0x8000] = 0
+    assert np.array_equal(Y, want)
+    Xr = up_f16(synth.activations(16, C, 3101))
+    Y0 = down_bits16(nm.nm_spmm(v, m, Xr, 2, 4))
+    for _ in range(10):
+        assert np.array_equal(down_bits16(nm.nm_spmm(v, m, Xr, 2, 4)), Y0)
+
+
+def test_skinny_malformed_masks_stay_in_bounds():
+    R, C, T = 2100, 1056, 9
+    v = up_f16(synth.weight(R, C // 2, 3200))
+    X = up_f16(synth.activations(T, C, 3201))
+    for word in (0, 1, 0x80000000, 0xFFFFFFFF, 0x12345678):
+        m = torch.full((R, C // 32), np.uint32(word).view(np.int32).item(), dtype=torch.int32, device=device())
+        Y = nm.nm_spmm(v, m, X, 2, 4)
+        torch.cuda.synchronize()
+        assert Y.shape == (T, R)
