@@ -15,8 +15,11 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ahead), from sweeps on MI355X over 4096..14336 rows and columns at 2048 tokens. Large
 // tiles: the sparse product 256 rows x 128 tokens per workgroup (each X fragment serves 4
 // row tiles), the dense one 128 x 256 (each weight fragment serves 16 token tiles); each was
-// the fastest for its kernel. The small tile (64 x 64) serves problems whose large-tile grid
-// would leave CUs idle.
+// the fastest for its kernel. The sparse product takes 256 x 256 when that grid still has
+// a workgroup per CU (14336 x 4096 x 2048: 247 against 294 us; with fewer workgroups it
+// loses: 4096 x 4096 x 2048: 102 against 71 us). The small tile (64 x 64) serves problems
+// whose large-tile grid would leave CUs idle.
+using SparseHuge = Tile<4, 16, 64>;   // 256 rows x 256 tokens: when even this grid fills the CUs
 using SparseLarge = Tile<4, 8, 64>;
 using DenseLarge = Tile<2, 16, 64>;
 using Small = Tile<1, 4, 64>;
@@ -45,6 +48,9 @@ hipError_t launch_prefill_spmm(const uint16_t* values, const uint32_t* masks, co
   if (!prefill_fits(rows, cols, tokens)) return hipErrorInvalidValue;
   int r = int(rows), c = int(cols), t = int(tokens);
   void* args[] = {&values, &masks, &X, &Y, &r, &c, &t};
+  if (use_large<SparseHuge>(rows, tokens, dev))
+    return launch(reinterpret_cast<const void*>(&prefill_spmm_kernel<4, 16, 64, kDepth>),
+                  dim3(unsigned(workgroups<SparseHuge>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
   if (use_large<SparseLarge>(rows, tokens, dev))
     return launch(reinterpret_cast<const void*>(&prefill_spmm_kernel<4, 8, 64, kDepth>),
                   dim3(unsigned(workgroups<SparseLarge>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
@@ -66,8 +72,9 @@ hipError_t launch_prefill_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y
 
 const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev) {
   if (sparse)
-    return use_large<SparseLarge>(rows, tokens, dev) ? "prefill_spmm_kernel<4, 8, 64, 2>"
-                                                     : "prefill_spmm_kernel<1, 4, 64, 2>";
+    return use_large<SparseHuge>(rows, tokens, dev)    ? "prefill_spmm_kernel<4, 16, 64, 2>"
+           : use_large<SparseLarge>(rows, tokens, dev) ? "prefill_spmm_kernel<4, 8, 64, 2>"
+                                                       : "prefill_spmm_kernel<1, 4, 64, 2>";
   return use_large<DenseLarge>(rows, tokens, dev) ? "prefill_gemm_kernel<2, 16, 64, 2>"
                                                   : "prefill_gemm_kernel<1, 4, 64, 2>";
 }

@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 # least one workgroup per CU)
 SMALL = [(1, 32, 1), (17, 64, 5), (16, 96, 16), (33, 128, 17), (64, 4064, 63), (65, 4096, 64),
          (127, 544, 65), (300, 1056, 255), (129, 2080, 257), (1000, 4064, 700), (4100, 1024, 2050),
-         (4096, 160, 2048), (2600, 2208, 3000)]
+         (4096, 160, 2048), (2600, 2208, 3000), (16400, 160, 1100)]
 
 
 def check_prefill(W, X, tag, rows_idx=None, dense=True):
@@ -62,6 +62,7 @@ def test_prefill_both_tile_configurations_are_exercised():
     """The shapes above cover the small and the large tile configuration of both products."""
     names = {nm.prefill_variant(R, C, T, s) for R, C, T in SMALL for s in (True, False)}
     assert names == {"prefill_spmm_kernel<1, 4, 64, 2>", "prefill_spmm_kernel<4, 8, 64, 2>",
+                     "prefill_spmm_kernel<4, 16, 64, 2>",
                      "prefill_gemm_kernel<1, 4, 64, 2>", "prefill_gemm_kernel<2, 16, 64, 2>"}, names
 
 
