@@ -86,6 +86,16 @@ int64_t nm_max_cols(void);
 int nm_pack(const uint16_t* W, uint16_t* values, uint32_t* masks,
             int64_t rows, int64_t cols, int N, int M, void* stream);
 
+/* Decoder, the inverse of nm_pack ([KERNEL] bitmask format): writes the dense matrix W'
+ * [rows][cols] fp16 that (values, masks) describe: the kept values at their columns (the
+ * value of set bit j of word w is the one after the set bits below j), +0 elsewhere.
+ * Bit-exact and deterministic. A mask word with the wrong number of set bits gives an
+ * unspecified W' but no access outside the inputs. For products that have no sparse path
+ * (for example a prefill-sized batch of a 4:8 ... 16:32 matrix), decoding once and using
+ * nm_gemm_dense_prefill is the fast route. values, W 16-byte aligned; masks 4-byte. */
+int nm_unpack(const uint16_t* values, const uint32_t* masks, uint16_t* W,
+              int64_t rows, int64_t cols, int N, int M, void* stream);
+
 /* Sparse product ([NEWS-NEW], [KERNEL]): y[r] = fp16( sum_c W'[r][c] * x[c] ), where W'
  * is the matrix the packed (values, masks) describe. Products and sums are fp32; y is
  * rounded once to fp16 (round to nearest even). The summation order is fixed, so the

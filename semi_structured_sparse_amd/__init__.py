@@ -28,6 +28,8 @@ SIGNATURES = {
     "nm_max_cols": (_c.c_int64, []),
     "nm_pack": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
                            _c.c_int, _c.c_int, _c.c_void_p]),
+    "nm_unpack": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
+                             _c.c_int, _c.c_int, _c.c_void_p]),
     "nm_spmv": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
                            _c.c_int64, _c.c_int, _c.c_int, _c.c_void_p]),
     "nm_gemv_dense": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
@@ -170,6 +172,30 @@ def nm_pack(W, N: int, M: int):
                            _stream_ptr(W))
     _check("nm_pack", st)
     return values, masks
+
+
+def nm_unpack(values, masks, N: int, M: int, out=None):
+    """Dense fp16 W' [rows, cols] from the packed (values, masks): the inverse of nm_pack."""
+    torch = _torch()
+    _require(values, "values", torch.float16, 2)
+    _require(masks, "masks", torch.int32, 2)
+    rows, words = masks.shape
+    cols = words * 32
+    if (N, M) in ALL_PATTERNS and values.shape != (rows, cols * N // M):
+        raise ValueError(f"values shape {tuple(values.shape)} != {(rows, cols * N // M)}")
+    if values.device != masks.device:
+        raise ValueError("values and masks must be on one device")
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float16, device=values.device)
+    else:
+        _require(out, "out", torch.float16, 2)
+        if tuple(out.shape) != (rows, cols) or out.device != values.device:
+            raise ValueError("out must be fp16 [rows, cols] on the same device")
+    with torch.cuda.device(values.device):
+        st = lib().nm_unpack(values.data_ptr(), masks.data_ptr(), out.data_ptr(), rows, cols, N, M,
+                             _stream_ptr(values))
+    _check("nm_unpack", st)
+    return out
 
 
 def nm_spmv(values, masks, x, N: int, M: int, out=None):

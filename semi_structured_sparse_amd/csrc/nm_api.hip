@@ -115,6 +115,19 @@ int nm_pack(const uint16_t* W, uint16_t* values, uint32_t* masks, int64_t rows, 
   return e == hipSuccess ? NM_OK : nm::hip_fail(e);
 }
 
+int nm_unpack(const uint16_t* values, const uint32_t* masks, uint16_t* W, int64_t rows, int64_t cols, int N, int M,
+              void* stream) {
+  if (!values || !masks || !W) return NM_ERR_NULL;
+  if (!nm::valid_shape(rows, cols)) return NM_ERR_SHAPE;
+  if (!nm::valid_pattern(N, M)) return NM_ERR_PATTERN;
+  if (!nm::aligned(W, 16) || !nm::aligned(values, 16) || !nm::aligned(masks, 4)) return NM_ERR_ALIGN;
+  nm::DeviceInfo dev;
+  hipError_t e = nm::current_device_info(&dev);
+  if (e != hipSuccess) return nm::hip_fail(e);
+  e = nm::launch_unpack(values, masks, W, rows, cols, N, M, static_cast<hipStream_t>(stream), dev);
+  return e == hipSuccess ? NM_OK : nm::hip_fail(e);
+}
+
 int nm_spmv(const uint16_t* values, const uint32_t* masks, const uint16_t* x, uint16_t* y,
             int64_t rows, int64_t cols, int N, int M, void* stream) {
   if (!values || !masks || !x || !y) return NM_ERR_NULL;

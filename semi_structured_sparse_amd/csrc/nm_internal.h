@@ -31,6 +31,8 @@ hipError_t launch(const void* kernel, dim3 grid, dim3 block, void** args, size_t
 // Kernel launchers (arguments already validated by the API layer).
 hipError_t launch_pack(const uint16_t* W, uint16_t* values, uint32_t* masks, int64_t rows,
                        int64_t cols, int N, int M, hipStream_t stream, const DeviceInfo& dev);
+hipError_t launch_unpack(const uint16_t* values, const uint32_t* masks, uint16_t* W, int64_t rows, int64_t cols,
+                         int N, int M, hipStream_t stream, const DeviceInfo& dev);
 hipError_t launch_spmv(const uint16_t* values, const uint32_t* masks, const uint16_t* x,
                        uint16_t* y, int64_t rows, int64_t cols, int N, int M, hipStream_t stream,
                        const DeviceInfo& dev);

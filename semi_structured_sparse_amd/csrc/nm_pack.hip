@@ -80,6 +80,61 @@ __global__ __launch_bounds__(kPackThreads) void nm_pack_kernel(const uint4* __re
   }
 }
 
+// Decoder, the inverse of the encoder: one thread writes the 32 dense fp16 of one mask
+// word, taking the kept values in ascending column order (the value of set bit j is the
+// one after all set bits below j) and +0 for dropped columns. The word's V values go
+// through a private LDS slot so that the running index can address them; a mask with
+// more than V set bits reuses the last value (unspecified result, no access outside the
+// slot).
+template <int V>
+__global__ __launch_bounds__(kPackThreads) void nm_unpack_kernel(const uint4* __restrict__ values,
+                                                                 const uint32_t* __restrict__ masks,
+                                                                 uint4* __restrict__ W, int64_t total_words) {
+  constexpr int kSlotU = V / 2 + 1;
+  __shared__ uint32_t slot_all[kPackThreads * kSlotU];
+  uint32_t* slot = slot_all + threadIdx.x * kSlotU;
+  const int64_t stride = int64_t(gridDim.x) * kPackThreads;
+  for (int64_t t = int64_t(blockIdx.x) * kPackThreads + threadIdx.x; t < total_words; t += stride) {
+#pragma unroll
+    for (int q = 0; q < V / 8; ++q) {
+      const uint4 a = values[(V / 8) * t + q];
+      slot[4 * q + 0] = a.x;
+      slot[4 * q + 1] = a.y;
+      slot[4 * q + 2] = a.z;
+      slot[4 * q + 3] = a.w;
+    }
+    const uint32_t m = masks[t];
+    uint32_t out[16];
+    uint32_t k = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t b = (m >> j) & 1u;
+      const uint32_t kk = k < uint32_t(V - 1) ? k : uint32_t(V - 1);
+      const uint32_t h = b ? (slot[kk >> 1] >> (16 * (kk & 1))) & 0xFFFFu : 0u;
+      k += b;
+      if (j & 1)
+        out[j >> 1] |= h << 16;
+      else
+        out[j >> 1] = h;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) W[4 * t + q] = make_uint4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
+  }
+}
+
+template <int V>
+hipError_t launch_unpack_t(const uint16_t* values, const uint32_t* masks, uint16_t* W, int64_t words,
+                           hipStream_t stream, const DeviceInfo& dev) {
+  const uint4* v4 = reinterpret_cast<const uint4*>(values);
+  uint4* w4 = reinterpret_cast<uint4*>(W);
+  void* args[] = {&v4, &masks, &w4, &words};
+  int64_t blocks = (words + kPackThreads - 1) / kPackThreads;
+  const int64_t cap = int64_t(dev.cu_count > 0 ? dev.cu_count : 256) * 32;
+  if (blocks > cap) blocks = cap;
+  return launch(reinterpret_cast<const void*>(&nm_unpack_kernel<V>), dim3(unsigned(blocks)), dim3(kPackThreads),
+                args, 0, stream, dev);
+}
+
 template <int N, int M>
 hipError_t launch_pack_t(const uint16_t* W, uint16_t* values, uint32_t* masks, int64_t words,
                          hipStream_t stream, const DeviceInfo& dev) {
@@ -94,6 +149,13 @@ hipError_t launch_pack_t(const uint16_t* W, uint16_t* values, uint32_t* masks, i
 }
 
 }  // namespace
+
+hipError_t launch_unpack(const uint16_t* values, const uint32_t* masks, uint16_t* W, int64_t rows, int64_t cols,
+                         int N, int M, hipStream_t stream, const DeviceInfo& dev) {
+  const int64_t words = rows * (cols / 32);
+  return M == 2 * N ? launch_unpack_t<16>(values, masks, W, words, stream, dev)
+                    : launch_unpack_t<8>(values, masks, W, words, stream, dev);
+}
 
 hipError_t launch_pack(const uint16_t* W, uint16_t* values, uint32_t* masks, int64_t rows,
                        int64_t cols, int N, int M, hipStream_t stream, const DeviceInfo& dev) {

@@ -97,6 +97,18 @@ def test_spmv_validation(kw, want):
 
 
 @pytest.mark.parametrize("kw,want", [
+    (dict(values=None), nm.NM_ERR_NULL), (dict(masks=None), nm.NM_ERR_NULL), (dict(W=None), nm.NM_ERR_NULL),
+    (dict(rows=0), nm.NM_ERR_SHAPE), (dict(cols=48), nm.NM_ERR_SHAPE),
+    (dict(N=3, M=4), nm.NM_ERR_PATTERN),
+    (dict(values=A16 + 8), nm.NM_ERR_ALIGN), (dict(masks=A16 + 2), nm.NM_ERR_ALIGN), (dict(W=A16 + 4), nm.NM_ERR_ALIGN),
+])
+def test_unpack_validation(kw, want):
+    a = dict(values=A16, masks=A16, W=A16, rows=16, cols=64, N=2, M=4)
+    a.update(kw)
+    assert nm.lib().nm_unpack(a["values"], a["masks"], a["W"], a["rows"], a["cols"], a["N"], a["M"], None) == want
+
+
+@pytest.mark.parametrize("kw,want", [
     (dict(W=None), nm.NM_ERR_NULL), (dict(values=None), nm.NM_ERR_NULL), (dict(masks=None), nm.NM_ERR_NULL),
     (dict(rows=0), nm.NM_ERR_SHAPE), (dict(cols=33), nm.NM_ERR_SHAPE),
     (dict(N=4, M=4), nm.NM_ERR_PATTERN),
