@@ -115,15 +115,16 @@ int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,
  *   Y[b][r] = fp16( sum_c W'[r][c] * X[b][c] ),  X fp16 [batch][cols], Y fp16 [batch][rows]
  * (row b of X is one activation vector: the layout of a batch of tokens). Products and
  * sums fp32, one RNE rounding, fixed summation order (bit-identical run to run).
- *   - batch <= 8: the small-batch kernel (vector units; x staged in LDS in column phases
- *     when it does not fit at once, so any width is accepted). batch == 1 gives the same
- *     result as nm_spmv within the tolerance of the product (it may use another summation
- *     order).
  *   - batch >= 32 with 2:4: nm_spmm_prefill (matrix cores), with its limits.
- *   - 5 <= batch < 32 with 2:4 on layers of at least 2048 rows: the sparse matrix
- *     instruction with X staged whole in LDS, 16 vectors per launch (cols <= 2^21).
- *   - other batches > 8 (2:4 otherwise, and 4:8, 8:16, 16:32): the small-batch kernel on
- *     consecutive groups of 8 rows of X (one launch per group; vector units only).
+ *   - on layers of at least 2048 rows, 5 <= batch < 32 with 2:4 and batch >= 5 with 4:8
+ *     or 8:16: the sparse matrix instruction with X staged in LDS, 16 vectors per launch
+ *     (cols <= 2^21). 4:8 and 8:16 keep 8 values in every 16 columns like 2:4, so each
+ *     4-column group is split into two 2:4 operands (its first two kept values and the
+ *     rest) that go through the instruction with the same X.
+ *   - otherwise the small-batch kernel (vector units; x staged in LDS in column phases
+ *     when it does not fit at once, so any width is accepted), on consecutive groups of
+ *     8 rows of X (one launch per group). batch == 1 gives the same result as nm_spmv
+ *     within the tolerance of the product (it may use another summation order).
  * The 25% patterns are accepted for batch == 1 only (and cols <= nm_max_cols()); larger
  * batches of them return NM_ERR_PATTERN. X must be 16-byte aligned, Y 2-byte aligned;
  * batch < 1 or above 2^24 is NM_ERR_SHAPE. */

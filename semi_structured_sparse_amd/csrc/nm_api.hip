@@ -195,19 +195,19 @@ int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, ui
   hipError_t e = nm::current_device_info(&dev);
   if (e != hipSuccess) return nm::hip_fail(e);
   if (M != 2 * N && cols > nm::max_cols_for(dev)) return NM_ERR_TOO_WIDE;  // 25%: single-vector kernel only
-  if (N == 2 && M == 4 && batch >= nm::kSkinnyMinBatch && rows >= nm::kSkinnyMinRows &&
-      nm::skinny_fits(rows, cols, nm::kSkinnyBatch, dev)) {
-    // 2:4 at 5..31 vectors on a large layer: the sparse matrix instruction, 16 vectors per launch
+  if (nm::use_skinny(rows, cols, batch, N, M, dev)) {
+    // 2:4 at 5..31 vectors, 4:8 and 8:16 from 5 vectors on, on a large layer: the sparse
+    // matrix instruction, 16 vectors per launch
     for (int64_t b0 = 0; b0 < batch; b0 += nm::kSkinnyBatch) {
       const int nb = int(batch - b0 < nm::kSkinnyBatch ? batch - b0 : nm::kSkinnyBatch);
-      e = nm::launch_skinny_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb,
+      e = nm::launch_skinny_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb, N, M,
                                  static_cast<hipStream_t>(stream), dev);
       if (e != hipSuccess) return nm::hip_fail(e);
     }
     return NM_OK;
   }
-  // larger batches (other 50% patterns, or 2:4 below kMatrixCoreMinBatch): the small-batch
-  // kernel on consecutive groups of kSmallBatch rows of X (X and Y rows are contiguous)
+  // otherwise (fewer vectors, smaller layers, 16:32): the small-batch kernel on consecutive
+  // groups of kSmallBatch rows of X (X and Y rows are contiguous)
   for (int64_t b0 = 0; b0 < batch; b0 += nm::kSmallBatch) {
     const int nb = int(batch - b0 < nm::kSmallBatch ? batch - b0 : nm::kSmallBatch);
     e = nm::launch_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb, N, M,
@@ -242,9 +242,7 @@ const char* nm_spmm_variant(int64_t rows, int64_t cols, int64_t batch, int N, in
   if (batch == 1 && cols <= nm::max_cols_for(dev)) return nm::spmv_variant(rows, cols, N, M, dev);
   if (N == 2 && M == 4 && batch >= nm::kMatrixCoreMinBatch)
     return nm::prefill_fits(rows, cols, batch) ? nm::prefill_variant(rows, batch, true, dev) : "";
-  if (N == 2 && M == 4 && batch >= nm::kSkinnyMinBatch && rows >= nm::kSkinnyMinRows &&
-      nm::skinny_fits(rows, cols, nm::kSkinnyBatch, dev))
-    return "skinny_spmm_kernel<1>";
+  if (nm::use_skinny(rows, cols, batch, N, M, dev)) return nm::skinny_variant(N);
   return nm::spmm_variant(N, batch < nm::kSmallBatch ? batch : nm::kSmallBatch);
 }
 

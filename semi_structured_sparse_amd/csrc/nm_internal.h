@@ -85,18 +85,23 @@ hipError_t launch_prefill_spmm(const uint16_t* values, const uint32_t* masks, co
                                int64_t rows, int64_t cols, int64_t tokens, hipStream_t stream, const DeviceInfo& dev);
 hipError_t launch_prefill_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y, int64_t rows, int64_t cols,
                                int64_t tokens, hipStream_t stream, const DeviceInfo& dev);
-// Small-batch 2:4 product on the sparse matrix instruction, 1..16 tokens (X [tokens][cols],
-// Y [tokens][rows]); skinny_fits tells whether a shape is within its limits.
-bool skinny_fits(int64_t rows, int64_t cols, int64_t tokens, const DeviceInfo& dev);
+// Small-batch 50% product on the sparse matrix instruction, 1..16 tokens (X [tokens][cols],
+// Y [tokens][rows]): 2:4 directly, 4:8 and 8:16 split into two 2:4 operands. skinny_fits
+// tells whether a pattern and shape are within its limits.
+bool skinny_fits(int64_t rows, int64_t cols, int64_t tokens, int n, int m, const DeviceInfo& dev);
 hipError_t launch_skinny_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
-                              int64_t rows, int64_t cols, int tokens, hipStream_t stream, const DeviceInfo& dev);
-// nm_spmm with 2:4 runs the skinny kernel for kSkinnyMinBatch <= batch < kMatrixCoreMinBatch
-// on layers of at least kSkinnyMinRows rows, kSkinnyBatch vectors per launch (measured on
-// MI355X: from 5 vectors on it beats the small-batch kernel on such layers; on smaller ones
-// its fixed cost of a few microseconds does not pay).
+                              int64_t rows, int64_t cols, int tokens, int n, int m, hipStream_t stream,
+                              const DeviceInfo& dev);
+// nm_spmm runs the skinny kernel, kSkinnyBatch vectors per launch, on layers of at least
+// kSkinnyMinRows rows from kSkinnyMinBatch vectors on: for 2:4 up to kMatrixCoreMinBatch
+// (the prefill kernel takes over), for 4:8 and 8:16 at any batch (measured on MI355X: from 5
+// vectors on it beats the small-batch kernel on such layers; on smaller ones its fixed cost
+// of a few microseconds does not pay).
 constexpr int64_t kSkinnyMinBatch = 5;
 constexpr int64_t kSkinnyMinRows = 2048;
 constexpr int64_t kSkinnyBatch = 16;
+bool use_skinny(int64_t rows, int64_t cols, int64_t batch, int n, int m, const DeviceInfo& dev);
+const char* skinny_variant(int n);
 
 // Name of the kernel configuration the prefill launchers pick (static string).
 const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev);

@@ -16,6 +16,19 @@
 // row, the index-word table and the mask-block permute are those of the prefill kernel
 // (nm_prefill_impl.h): lane (q = l / 16, li = l % 16) holds values 8q .. 8q+7 of a 64-column
 // step for row li, and the X fragment of token li at column chunks q and 4 + q of the step.
+//
+// 4:8 and 8:16 (SPLIT): these patterns also keep exactly 8 values per 16 aligned columns,
+// so the same 16-byte load gives a lane the kept values of its 16 columns, but a 4-column
+// group may keep 0 .. 4 of them. Each group is split in two: its first two kept values
+// (ascending column) form a pair of a 2:4 operand A, the third and fourth a pair of a 2:4
+// operand B, with zeros where a group keeps fewer; A and B go through the sparse
+// instruction with the same X fragment and add into the same accumulator. Moving the
+// values into place is a per-lane shuffle that depends only on the lane's 16 mask bits: a
+// table in LDS, indexed by (side, mask byte), gives for each output dword two byte
+// selectors (one over values 0..3, one over values 4..7, v_perm_b32) and the pairs' 2-bit
+// position codes. The low mask byte's values are ranks 0 .. c-1 of the lane's 8 and the
+// high byte's the last ones, 8 - c' .. 7 (c, c' their bit counts), so each byte's entry
+// depends on that byte alone.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -47,14 +60,91 @@ __device__ __forceinline__ uint32_t xoff(int t, int c, uint32_t rb) {
   return uint32_t(t) * rb + (uint32_t(c ^ (t & 7)) << 4);
 }
 
-template <int TR>
+// ---- split tables (4:8, 8:16) ----
+// Entry (side, byte), side 0 for the low mask byte of a lane's 16 bits, 1 for the high one:
+// sel[4 g + {0, 1}] = selectors of operand A's pair for the byte's group g (over values 0..3,
+// over values 4..7), sel[4 g + {2, 3}] the same for operand B; idx bits 4 g .. 4 g + 3 = A's
+// position code for group g, bits 8 + 4 g .. = B's. Selector byte 0x0C gives a zero byte.
+constexpr int kSplitEntries = 512;
+constexpr uint32_t kSplitSelBytes = kSplitEntries * 32;
+constexpr uint32_t kSplitLutBytes = kSplitSelBytes + kSplitEntries * 2;   // + 16-bit codes
+
+struct SplitEntry {
+  uint32_t sel[8];
+  uint32_t idx;
+};
+
+// selector bytes placing value `rank` of the lane's 8 (-1: zero) as one fp16 half, for the
+// operand pair (values 0..3) when !high, (values 4..7) when high
+__host__ __device__ constexpr uint32_t split_half_sel(int rank, bool high) {
+  if (rank < 0 || (rank >= 4) != high) return 0x0C0Cu;
+  const uint32_t b = 2u * uint32_t(rank & 3);
+  return b | (b + 1u) << 8;
+}
+
+__host__ __device__ constexpr SplitEntry split_entry(int side, int byte) {
+  SplitEntry e{};
+  const int c = __builtin_popcount(unsigned(byte));
+  int rank = side ? 8 - c : 0;                       // rank of the byte's first kept value
+  uint32_t idx = 0;
+  for (int g = 0; g < 2; ++g) {
+    const int nib = (byte >> (4 * g)) & 15;
+    int p[4] = {0, 0, 0, 0}, k = 0;
+    for (int b = 0; b < 4; ++b)
+      if ((nib >> b) & 1) p[k++] = b;
+    // pairs as (rank of the value at the lower position, at the higher), -1 = zero; the
+    // positions stay distinct and ascending
+    int a0 = -1, a1 = -1, b0 = -1, b1 = -1, ca = 0x4, cb = 0x4;
+    if (k >= 2) { a0 = rank; a1 = rank + 1; ca = p[0] | p[1] << 2; }
+    else if (k == 1) {
+      if (p[0] < 3) { a0 = rank; ca = p[0] | 3 << 2; } else { a1 = rank; ca = 2 | 3 << 2; }
+    }
+    if (k == 4) { b0 = rank + 2; b1 = rank + 3; cb = 2 | 3 << 2; }
+    else if (k == 3) {
+      if (p[2] < 3) { b0 = rank + 2; cb = p[2] | 3 << 2; } else { b1 = rank + 2; cb = 2 | 3 << 2; }
+    }
+    e.sel[4 * g + 0] = split_half_sel(a0, false) | split_half_sel(a1, false) << 16;
+    e.sel[4 * g + 1] = split_half_sel(a0, true) | split_half_sel(a1, true) << 16;
+    e.sel[4 * g + 2] = split_half_sel(b0, false) | split_half_sel(b1, false) << 16;
+    e.sel[4 * g + 3] = split_half_sel(b0, true) | split_half_sel(b1, true) << 16;
+    idx |= uint32_t(ca) << (4 * g) | uint32_t(cb) << (8 + 4 * g);
+    rank += k;
+  }
+  e.idx = idx;
+  return e;
+}
+
+// The tables as laid out in LDS (17 KiB): entry e's selectors at 32 e, its codes at
+// kSplitSelBytes + 2 e. Built at compile time; each workgroup copies them to LDS once.
+struct SplitTable {
+  uint4 sel[2 * kSplitEntries];
+  uint16_t idx[kSplitEntries];
+};
+static_assert(sizeof(SplitTable) == kSplitLutBytes, "split table layout");
+
+__host__ __device__ constexpr SplitTable make_split_table() {
+  SplitTable t{};
+  for (int e = 0; e < kSplitEntries; ++e) {
+    const SplitEntry x = split_entry(e >> 8, e & 255);
+    t.sel[2 * e] = uint4{x.sel[0], x.sel[1], x.sel[2], x.sel[3]};
+    t.sel[2 * e + 1] = uint4{x.sel[4], x.sel[5], x.sel[6], x.sel[7]};
+    t.idx[e] = uint16_t(x.idx);
+  }
+  return t;
+}
+
+__device__ const SplitTable kSplitTable = make_split_table();
+
+template <int TR, bool SPLIT>
 __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16_t* __restrict__ values,
                                                                      const uint32_t* __restrict__ masks,
                                                                      const uint16_t* __restrict__ X,
                                                                      uint16_t* __restrict__ Y, int rows, int cols,
                                                                      int tokens, int rg_count, int cs_count,
                                                                      int phase_cols) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
+  extern __shared__ __attribute__((aligned(16))) char lds_base[];
+  // SPLIT: the split tables first, X after them
+  char* const lds = lds_base + (SPLIT ? kSplitLutBytes : 0);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, li = lane & 15;
@@ -84,6 +174,14 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
 
   uint4 vb[kDepth][TR];
   uint2 mcur[TR], mnext[TR];
+  // SPLIT: this thread's 16-byte chunks of the split tables (1024 + 64 chunks), loaded
+  // before anything else so that the waits for X below cover them
+  uint4 lut_a{}, lut_b{};
+  if constexpr (SPLIT) {
+    const uint4* tab = reinterpret_cast<const uint4*>(&kSplitTable);
+    lut_a = tab[tid];
+    lut_b = tab[2 * kSplitEntries + (tid & 63)];
+  }
   for (int p0 = 0; p0 < cols; p0 += phase_cols) {
     const int pc = min(phase_cols, cols - p0);       // columns in this phase (multiple of 32)
     const uint32_t rb = uint32_t(2 * phase_cols);    // LDS bytes per token row
@@ -130,6 +228,12 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) load_v(vb[d], d);
     __syncthreads();                                 // the previous phase's LDS reads are done
+    if constexpr (SPLIT) {
+      if (p0 == 0) {
+        reinterpret_cast<uint4*>(lds_base)[tid] = lut_a;
+        if (tid < 64) reinterpret_cast<uint4*>(lds_base)[2 * kSplitEntries + tid] = lut_b;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < kXChunksPerThread; ++j)
       if (xdst[j] != 0xFFFFFFFFu) *reinterpret_cast<uint4*>(lds + xdst[j]) = xs[j];
@@ -159,8 +263,29 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
           for (int a = 0; a < TR; ++a) {
             const uint32_t w0 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur[a].x)));
             const uint32_t w1 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur[a].y)));
-            const int idx = index_word((((q >> 1) ? w1 : w0) >> mshift) & 0xFFFFu);
-            acc[a] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(h8_t, cur[a]), bf, acc[a], idx, 0, 0);
+            const uint32_t m16 = (((q >> 1) ? w1 : w0) >> mshift) & 0xFFFFu;
+            if constexpr (SPLIT) {
+              const uint32_t e0 = 32u * (m16 & 0xFFu), e1 = 32u * (256u + (m16 >> 8));
+              const uint4 s0 = *reinterpret_cast<const uint4*>(lds_base + e0);
+              const uint4 s1 = *reinterpret_cast<const uint4*>(lds_base + e0 + 16);
+              const uint4 s2 = *reinterpret_cast<const uint4*>(lds_base + e1);
+              const uint4 s3 = *reinterpret_cast<const uint4*>(lds_base + e1 + 16);
+              const uint16_t* codes = reinterpret_cast<const uint16_t*>(lds_base + kSplitSelBytes);
+              const uint32_t i0 = codes[m16 & 0xFFu], i1 = codes[256u + (m16 >> 8)];
+              const uint4 v = cur[a];
+              auto pick = [&](uint32_t lo_sel, uint32_t hi_sel) {
+                return __builtin_amdgcn_perm(v.y, v.x, lo_sel) | __builtin_amdgcn_perm(v.w, v.z, hi_sel);
+              };
+              const uint4 va = make_uint4(pick(s0.x, s0.y), pick(s1.x, s1.y), pick(s2.x, s2.y), pick(s3.x, s3.y));
+              const uint4 vb2 = make_uint4(pick(s0.z, s0.w), pick(s1.z, s1.w), pick(s2.z, s2.w), pick(s3.z, s3.w));
+              const int ia = int(__builtin_amdgcn_perm(i1, i0, 0x0C0C0400u));   // A codes of groups 0..3
+              const int ib = int(__builtin_amdgcn_perm(i1, i0, 0x0C0C0501u));   // B codes
+              acc[a] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(h8_t, va), bf, acc[a], ia, 0, 0);
+              acc[a] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(h8_t, vb2), bf, acc[a], ib, 0, 0);
+            } else {
+              acc[a] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(h8_t, cur[a]), bf, acc[a],
+                                                                index_word(m16), 0, 0);
+            }
           }
           load_v(vb[j % kDepth], s + kDepth);
         }
@@ -169,7 +294,7 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
   }
   // ---- sum the CS partial tiles of each row group; the first wave of the group stores
   __syncthreads();
-  float4* red = reinterpret_cast<float4*>(lds);
+  float4* red = reinterpret_cast<float4*>(lds_base);
 #pragma unroll
   for (int a = 0; a < TR; ++a)
     red[(wave * TR + a) * 64 + lane] = make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);

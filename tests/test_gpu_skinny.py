@@ -1,6 +1,6 @@
-"""GPU parity tests of the small-batch 2:4 product on the sparse matrix instruction (nm_spmm
-with 5..31 vectors on layers of at least 2048 rows), through the C ABI, against the CPU
-oracle (spmm_ref).
+"""GPU parity tests of the small-batch 50% products on the sparse matrix instruction (nm_spmm
+on layers of at least 2048 rows: 2:4 with 5..31 vectors; 4:8 and 8:16, split into two 2:4
+operands, from 5 vectors on), through the C ABI, against the CPU oracle (spmm_ref).
 
 Bars: Y within |y - ref| <= 2e-3 + 1e-2*|ref| per element and relative L2 <= 1e-3 (fp32
 accumulation in the matrix instruction, fp16 output, fp64 oracle); exact special cases
@@ -16,7 +16,8 @@ import synth
 from tests.gpu_helpers import device, down_bits16, down_f16, down_u32, sample_rows, say, up_f16, up_u32
 
 pytestmark = pytest.mark.gpu
-SKINNY = "skinny_spmm_kernel<1>"
+SKINNY = {2: "skinny_spmm_kernel<1, false>", 4: "skinny_spmm_kernel<1, true>", 8: "skinny_spmm_kernel<1, true>"}
+PATTERNS = [(2, 4), (4, 8), (8, 16)]
 
 # (rows, cols, vectors): ragged rows (16-row tiles, row groups of 1..4 tiles), a 32-column
 # tail step, steps split over 16 / 8 / 4 waves, X in several column phases (16 vectors x
@@ -25,70 +26,88 @@ CASES = [(2048, 96, 5), (2049, 1056, 8), (2100, 4064, 16), (4100, 1024, 11), (40
          (4100, 14368, 13), (9000, 2080, 17), (14336, 4096, 8), (2600, 544, 31), (16400, 288, 6)]
 
 
-def check(R, C, T, seed, rows_idx=None):
+def check(R, C, T, seed, N=2, M=4, rows_idx=None):
     W = synth.weight(R, C, seed)
     X = synth.activations(T, C, seed + 1)
-    values, masks = nm.nm_pack(up_f16(W), 2, 4)
-    Y = down_f16(nm.nm_spmm(values, masks, up_f16(X), 2, 4))
+    values, masks = nm.nm_pack(up_f16(W), N, M)
+    Y = down_f16(nm.nm_spmm(values, masks, up_f16(X), N, M))
     idx = np.arange(R) if rows_idx is None else rows_idx
     it = torch.from_numpy(idx).to(device())
-    rv, rm = oracle.pack_ref(W[idx], 2, 4)
+    rv, rm = oracle.pack_ref(W[idx], N, M)
     assert np.array_equal(down_u32(masks.index_select(0, it)), rm)
     assert np.array_equal(down_bits16(values.index_select(0, it)), rv)
-    rep = oracle.y_tolerance_report(Y[:, idx], oracle.spmm_ref(rv, rm, X, C, 2, 4))
-    assert rep["ok"], ((R, C, T), rep)
+    rep = oracle.y_tolerance_report(Y[:, idx], oracle.spmm_ref(rv, rm, X, C, N, M))
+    assert rep["ok"], ((R, C, T, N, M), rep)
     return rep
 
 
+@pytest.mark.parametrize("N,M", PATTERNS)
 @pytest.mark.parametrize("R,C,T", CASES)
-def test_skinny_parity(R, C, T):
-    assert nm.spmm_variant(R, C, T, 2, 4) == SKINNY
-    say(f"skinny {R}x{C} vectors={T}")
-    check(R, C, T, 3000 + R % 97 + C % 89 + T, sample_rows(R, k=32, rpb=16))
+def test_skinny_parity(R, C, T, N, M):
+    assert nm.spmm_variant(R, C, T, N, M) == SKINNY[N]
+    say(f"skinny {N}:{M} {R}x{C} vectors={T}")
+    check(R, C, T, 3000 + R % 97 + C % 89 + T + N, N, M, sample_rows(R, k=32, rpb=16))
+
+
+@pytest.mark.parametrize("N,M", [(4, 8), (8, 16)])
+def test_skinny_split_large_batches(N, M):
+    """4:8 and 8:16 stay on the split kernel beyond 31 vectors (16 per launch; a ragged last
+    launch of 4)."""
+    R, C, T = 2064, 1024, 36
+    assert nm.spmm_variant(R, C, T, N, M) == SKINNY[N]
+    say(f"skinny {N}:{M} {R}x{C} vectors={T}")
+    check(R, C, T, 3050 + N, N, M, sample_rows(R, k=32, rpb=16))
 
 
 def test_skinny_routing():
-    """Which kernel nm_spmm picks: the sparse matrix instruction for 2:4 at 5..31 vectors on
-    layers of >= 2048 rows; the small-batch kernel below 5 vectors, on smaller layers and
-    for the other patterns; the prefill kernel from 32 vectors on."""
+    """Which kernel nm_spmm picks: the sparse matrix instruction on layers of >= 2048 rows for
+    2:4 at 5..31 vectors and for 4:8 and 8:16 from 5 vectors on; the small-batch kernel
+    below 5 vectors, on smaller layers and for 16:32; the prefill kernel for 2:4 from 32
+    vectors on."""
     assert nm.spmm_variant(4096, 4096, 4, 2, 4) == "spmm_kernel<2, 4, 2>"
     assert nm.spmm_variant(2047, 4096, 8, 2, 4) == "spmm_kernel<2, 8, 2>"
-    assert nm.spmm_variant(4096, 4096, 8, 4, 8) == "spmm_kernel<4, 8, 2>"
+    assert nm.spmm_variant(2047, 4096, 8, 4, 8) == "spmm_kernel<4, 8, 2>"
+    assert nm.spmm_variant(4096, 4096, 4, 8, 16) == "spmm_kernel<8, 4, 2>"
     assert nm.spmm_variant(4096, 4096, 20, 16, 32) == "spmm_kernel<16, 8, 0>"
-    assert nm.spmm_variant(4096, 4096, 5, 2, 4) == SKINNY
-    assert nm.spmm_variant(4096, 4096, 31, 2, 4) == SKINNY
+    for N, M in PATTERNS:
+        assert nm.spmm_variant(4096, 4096, 5, N, M) == SKINNY[N]
+        assert nm.spmm_variant(4096, 4096, 31, N, M) == SKINNY[N]
+    assert nm.spmm_variant(4096, 4096, 32, 4, 8) == SKINNY[4]
+    assert nm.spmm_variant(4096, 4096, 2048, 8, 16) == SKINNY[8]
     assert nm.spmm_variant(4096, 4096, 32, 2, 4).startswith("prefill_spmm_kernel")
     assert nm.spmm_variant(4096, 4096, 1, 2, 4).startswith("spmv_kernel")
 
 
-def test_skinny_one_hot_and_determinism():
+@pytest.mark.parametrize("N,M", PATTERNS)
+def test_skinny_one_hot_and_determinism(N, M):
     """X = 16 rows of the identity (columns 0, 37, ..., spread over the row): token t gives
     column c_t of the pruned matrix bit-exactly; repeated calls give the same bits."""
     R, C = 2080, 4096
-    W = synth.weight(R, C, 3100)
-    rv, rm = oracle.pack_ref(W, 2, 4)
-    D = oracle.unpack_ref(rv, rm, C, 2, 4)
+    W = synth.weight(R, C, 3100 + N)
+    rv, rm = oracle.pack_ref(W, N, M)
+    D = oracle.unpack_ref(rv, rm, C, N, M)
     cols = [0, 37, 255, 256, 1000, 2047, 2048, 3001, 4000, 4095, 63, 64, 1, 2, 3, 4094]
     X = np.zeros((16, C), np.float16)
     for t, c in enumerate(cols):
         X[t, c] = 1.0
     v, m = up_f16(rv), up_u32(rm)
-    Y = down_bits16(nm.nm_spmm(v, m, up_f16(X), 2, 4))
+    Y = down_bits16(nm.nm_spmm(v, m, up_f16(X), N, M))
     want = D[:, cols].T.copy()
     want[want == 0x8000] = 0
     assert np.array_equal(Y, want)
     Xr = up_f16(synth.activations(16, C, 3101))
-    Y0 = down_bits16(nm.nm_spmm(v, m, Xr, 2, 4))
+    Y0 = down_bits16(nm.nm_spmm(v, m, Xr, N, M))
     for _ in range(10):
-        assert np.array_equal(down_bits16(nm.nm_spmm(v, m, Xr, 2, 4)), Y0)
+        assert np.array_equal(down_bits16(nm.nm_spmm(v, m, Xr, N, M)), Y0)
 
 
-def test_skinny_malformed_masks_stay_in_bounds():
+@pytest.mark.parametrize("N,M", PATTERNS)
+def test_skinny_malformed_masks_stay_in_bounds(N, M):
     R, C, T = 2100, 1056, 9
     v = up_f16(synth.weight(R, C // 2, 3200))
     X = up_f16(synth.activations(T, C, 3201))
     for word in (0, 1, 0x80000000, 0xFFFFFFFF, 0x12345678):
         m = torch.full((R, C // 32), np.uint32(word).view(np.int32).item(), dtype=torch.int32, device=device())
-        Y = nm.nm_spmm(v, m, X, 2, 4)
+        Y = nm.nm_spmm(v, m, X, N, M)
         torch.cuda.synchronize()
         assert Y.shape == (T, R)
