@@ -72,16 +72,32 @@ struct Tile {
 };
 
 // 2:4 position code (p0 | p1 << 2) of each 4-bit mask nibble with two set bits, as a
-// 16-entry table of nibbles; other nibbles (malformed masks, zero-filled tails) give 0.
+// 16-entry table of nibbles (the definition pair_codes32 is checked against).
 constexpr uint64_t kPairCodes = (0x4ull << (4 * 0x3)) | (0x8ull << (4 * 0x5)) | (0x9ull << (4 * 0x6)) |
                                 (0xCull << (4 * 0x9)) | (0xDull << (4 * 0xA)) | (0xEull << (4 * 0xC));
 
-__device__ __forceinline__ int index_word(uint32_t m16) {
-  uint32_t w = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w |= uint32_t((kPairCodes >> (4 * ((m16 >> (4 * i)) & 0xFu))) & 0xFu) << (4 * i);
-  return int(w);
+// The position codes of all 8 nibbles of a mask word at once (nibble i of the result is the
+// code of nibble i), by bit operations: for a nibble with exactly two set bits b_p0, b_p1
+// (p0 < p1), p0 = 0 iff b0, 1 iff !b0 & b1, else 2; p1 = 3 iff b3, 2 iff !b3 & b2, else 1. So
+// code bit 0 = !b0 & b1, bit 1 = !b0 & !b1, bit 2 = b3 | !b2, bit 3 = b3 | b2. The table above
+// on every nibble with two set bits (checked below at compile time); other nibbles
+// (zero-filled tails, malformed masks) get some code, and their values are zero or the
+// result is unspecified anyway.
+__host__ __device__ constexpr uint32_t pair_codes32(uint32_t m) {
+  const uint32_t t = m >> 1;
+  return (~m & t & 0x11111111u) | ((~(m | t) & 0x11111111u) << 1) | ((t | ~m) & 0x44444444u) |
+         ((m | (m << 1)) & 0x88888888u);
 }
+
+constexpr bool pair_codes_match_table() {
+  for (uint32_t n = 0; n < 16; ++n) {
+    if (__builtin_popcount(n) != 2) continue;
+    for (int i = 0; i < 8; ++i)
+      if (((pair_codes32(n << (4 * i)) >> (4 * i)) & 0xFu) != ((kPairCodes >> (4 * n)) & 0xFu)) return false;
+  }
+  return true;
+}
+static_assert(pair_codes_match_table(), "bitwise position codes disagree with the table");
 
 // Buffer loads: a resource spans one workgroup's slice of an operand and the hardware
 // returns zero for offsets at or past its end, so lanes with nothing to load (tokens or
@@ -373,9 +389,9 @@ __global__ __launch_bounds__(kThreads) void prefill_spmm_kernel(const uint16_t* 
   load_masks(0);
   auto hook = [&](auto pc, int s0) {
     constexpr int P = decltype(pc)::value;
-    if constexpr (P == 0) {
+    if constexpr (P == 0) {   // the position codes of the block's words, once per block
 #pragma unroll
-      for (int a = 0; a < TR; ++a) mcur[a] = mnext[a];
+      for (int a = 0; a < TR; ++a) mcur[a] = make_uint2(pair_codes32(mnext[a].x), pair_codes32(mnext[a].y));
     }
     if constexpr (P == kMaskSteps - D) load_masks(s0 / kMaskSteps + 1);
   };
@@ -394,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void prefill_spmm_kernel(const uint16_t* 
       av[a] = __builtin_bit_cast(h8_t, f.v[a][0]);
       const uint32_t w0 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur[a].x)));
       const uint32_t w1 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur[a].y)));
-      idx[a] = index_word((((q >> 1) ? w1 : w0) >> mshift) & 0xFFFFu);
+      idx[a] = int(__builtin_amdgcn_ubfe((q >> 1) ? w1 : w0, uint32_t(mshift), 16));
     }
     // X fragments are read one token tile ahead of the math that uses them
     uint4 lo[2], hi[2];

@@ -146,7 +146,10 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
   // SPLIT: the split tables first, X after them
   char* const lds = lds_base + (SPLIT ? kSplitLutBytes : 0);
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // the wave index and everything derived from it are wave-uniform (scalar registers): the
+  // loop bounds, the step offsets and the checks on them cost no vector instructions
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, li = lane & 15;
   const int rg = wave / cs_count, cs = wave - rg * cs_count;
   const int wg_rows_max = rg_count * 16 * TR;
@@ -165,8 +168,10 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
     moff[a] = rl * uint32_t(words) * 4u + 8u * uint32_t(q);
   }
   const int qcol = 32 * (q >> 1);
-  const int mshift = 16 * (q & 1);
+  const uint32_t mshift = 16u * uint32_t(q & 1);
   const bool tok_live = li < tokens;
+  // token rows past the batch read the last token's X: their products are never stored
+  const int xt = min(li, tokens - 1);
 
   f4_t acc[TR];
 #pragma unroll
@@ -190,35 +195,46 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
     const int s_lo = int((int64_t(psteps) * cs) / cs_count), s_hi = int((int64_t(psteps) * (cs + 1)) / cs_count);
     const int n = s_hi - s_lo;
     const int last = max(n - 1, 0);
-    auto col_of = [&](int s) { return p0 + 64 * (s_lo + min(s, last)); };
-    // steps past the range (the last block's padding) load zeros and read no X, so they
-    // add exactly zero and every slot of a block runs the same code
+    const int c_lo = p0 + 64 * s_lo;                 // first column of the wave's range
+    // value loads: step s of the range is inside the row for this lane iff s < s_lim; steps
+    // past it (the last block's padding, a 32-column tail) load zeros, so they add exactly
+    // zero and every slot of a block runs the same code
+    const int s_lim = min(n, (cols - c_lo - qcol + 63) / 64);
+    uint32_t vbase[TR];
+#pragma unroll
+    for (int a = 0; a < TR; ++a) vbase[a] = voff[a] + uint32_t(c_lo);
     auto load_v = [&](uint4 (&f)[TR], int s) {
-      const int c = col_of(s);
-      const bool ok = s < n && c + qcol < cols;
+      const bool ok = s < s_lim;
 #pragma unroll
-      for (int a = 0; a < TR; ++a) f[a] = buf_load16(vr, ok ? voff[a] + uint32_t(c) : kOutOfRange);
+      for (int a = 0; a < TR; ++a) f[a] = buf_load16(vr, ok ? vbase[a] + 64u * uint32_t(s) : kOutOfRange);
     };
-    auto load_m = [&](int s) {   // mask block starting at step s of the range
-      const int c = col_of(s);
+    auto load_m = [&](int s) {   // mask block starting at step s of the range (clamped into it)
+      const uint32_t cm = uint32_t(c_lo + 64 * min(s, last)) >> 3;
 #pragma unroll
-      for (int a = 0; a < TR; ++a) mnext[a] = buf_load8(mr, n > 0 ? moff[a] + uint32_t(c >> 3) : kOutOfRange);
+      for (int a = 0; a < TR; ++a) mnext[a] = buf_load8(mr, n > 0 ? moff[a] + cm : kOutOfRange);
     };
     // ---- X[0 .. tokens)[p0 .. p0 + pc) into registers (columns past the row read as zero):
-    // flat chunk k = tid + kThreadsFixed * j, token k / chunks; chunks past the end load out
-    // of range (zero) and are not written
+    // flat chunk k = tid + kThreadsFixed * j of token t = k / chunks, chunk c = k % chunks
+    // (one division, then steps of kThreadsFixed); chunks past the end load out of range
+    // (zero) and are not written
     const int chunks = psteps * 8;                   // 16-byte chunks per token row, whole steps
     const int nchunks = tokens * chunks;
+    const int dt = kThreadsFixed / chunks, dc = kThreadsFixed - dt * chunks;
     uint4 xs[kXChunksPerThread];
     uint32_t xdst[kXChunksPerThread];
+    {
+      int t = tid / chunks, c = tid - t * chunks;
 #pragma unroll
-    for (int j = 0; j < kXChunksPerThread; ++j) {
-      const int k = tid + kThreadsFixed * j;
-      const int t = k / chunks, c = k - t * chunks;
-      const int col = p0 + 8 * c;
-      const bool ok = k < nchunks && col < cols;
-      xs[j] = buf_load16(xr, ok ? (uint32_t(t) * uint32_t(cols) + uint32_t(col)) * 2u : kOutOfRange);
-      xdst[j] = k < nchunks ? xoff(t, c, rb) : 0xFFFFFFFFu;
+      for (int j = 0; j < kXChunksPerThread; ++j) {
+        const int k = tid + kThreadsFixed * j;
+        const int col = p0 + 8 * c;
+        const bool ok = k < nchunks && col < cols;
+        xs[j] = buf_load16(xr, ok ? (uint32_t(t) * uint32_t(cols) + uint32_t(col)) * 2u : kOutOfRange);
+        xdst[j] = k < nchunks ? xoff(t, c, rb) : 0xFFFFFFFFu;
+        t += dt;
+        c += dc;
+        if (c >= chunks) { c -= chunks; ++t; }
+      }
     }
     // then the first weight loads: they are in flight while X is written to LDS (the X
     // loads were issued first, so waiting for them does not wait for these). The mask
@@ -239,10 +255,13 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
       if (xdst[j] != 0xFFFFFFFFu) *reinterpret_cast<uint4*>(lds + xdst[j]) = xs[j];
     __syncthreads();
     if (n > 0) {
-      const uint32_t b_lo = xoff(li, q, rb), b_hi = xoff(li, 4 + q, rb);
+      const uint32_t b_lo = xoff(xt, q, rb), b_hi = xoff(xt, 4 + q, rb);
       for (int s0 = 0; s0 < n; s0 += kMaskSteps) {
+        // 2:4: the position codes of the block's words, once per block; the steps then
+        // only fetch and shift them
 #pragma unroll
-        for (int a = 0; a < TR; ++a) mcur[a] = mnext[a];
+        for (int a = 0; a < TR; ++a)
+          mcur[a] = SPLIT ? mnext[a] : make_uint2(pair_codes32(mnext[a].x), pair_codes32(mnext[a].y));
         load_m(s0 + kMaskSteps);
 #pragma unroll
         for (int j = 0; j < kMaskSteps; ++j) {
@@ -250,10 +269,11 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
           // the products read vb[j] in place; its next load is issued after them, so the
           // registers are never copied (a copy would wait for every load in flight)
           const uint4 (&cur)[TR] = vb[j % kDepth];
-          const uint32_t cb = uint32_t(s_lo + min(s, last)) * 128u;   // the step's chunks start at chunk 8 (s_lo + s)
           const int src = 4 * (li + 16 * j);
+          // X of the step (chunks 8 (s_lo + s) ..); zero past the range (a wave-uniform test)
           uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-          if (tok_live && s < n) {
+          if (s < n) {
+            const uint32_t cb = uint32_t(s_lo + s) * 128u;
             lo = *reinterpret_cast<const uint4*>(lds + b_lo + cb);
             hi = *reinterpret_cast<const uint4*>(lds + b_hi + cb);
           }
@@ -263,7 +283,7 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
           for (int a = 0; a < TR; ++a) {
             const uint32_t w0 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur[a].x)));
             const uint32_t w1 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur[a].y)));
-            const uint32_t m16 = (((q >> 1) ? w1 : w0) >> mshift) & 0xFFFFu;
+            const uint32_t m16 = __builtin_amdgcn_ubfe((q >> 1) ? w1 : w0, mshift, 16);
             if constexpr (SPLIT) {
               const uint32_t e0 = 32u * (m16 & 0xFFu), e1 = 32u * (256u + (m16 >> 8));
               const uint4 s0 = *reinterpret_cast<const uint4*>(lds_base + e0);
@@ -283,8 +303,9 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
               acc[a] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(h8_t, va), bf, acc[a], ia, 0, 0);
               acc[a] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(h8_t, vb2), bf, acc[a], ib, 0, 0);
             } else {
+              // m16 holds the position codes of the lane's 4 groups
               acc[a] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(h8_t, cur[a]), bf, acc[a],
-                                                                index_word(m16), 0, 0);
+                                                                int(m16), 0, 0);
             }
           }
           load_v(vb[j % kDepth], s + kDepth);
