@@ -11,8 +11,8 @@ import torch
 import oracle
 import semi_structured_sparse_amd as nm
 import synth
-from tests.gpu_helpers import (check_full_layer, device, down_bits16, down_f16, down_u32, say,
-                               up_f16, up_u32)
+from tests.gpu_helpers import (check_full_layer, device, down_bits16, down_f16, down_u32, sample_rows,
+                               say, up_f16, up_u32)
 
 pytestmark = pytest.mark.gpu
 PATTERNS = synth.PATTERNS
@@ -268,3 +268,33 @@ def test_decode_sweep_blocks(block):
         W = synth.weight(R, C, synth.decode_seed(block, p))
         x = synth.activation(C, synth.decode_x_seed(block, p))
         check_full_layer(W, x, 2, 4, f"decode-{block}-{name}", check_dense=(p in (0, 4)))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("parts,name", [((0, 1, 2), "qkv"), ((4, 5), "gate_up")])
+def test_decode_fused_products(parts, name):
+    """The fused products the decode benchmark times: q/k/v (6144 x 4096) and gate/up
+    (28672 x 4096) of block 0, each part packed alone and the packed rows concatenated, all
+    parts applied to the x of the first: pack bit-exact per part and y within tolerance on
+    sampled rows of the fused product, in its own launch configuration."""
+    shapes = [synth.LLAMA31_8B_DECODE_LAYER[p] for p in parts]
+    C = shapes[0][2]
+    Ws = [synth.weight(R, C, synth.decode_seed(0, p)) for p, (_, R, _) in zip(parts, shapes)]
+    x = synth.activation(C, synth.decode_x_seed(0, parts[0]))
+    packed = [nm.nm_pack(up_f16(W), 2, 4) for W in Ws]
+    values = torch.cat([v for v, _ in packed])
+    masks = torch.cat([m for _, m in packed])
+    R = values.shape[0]
+    say(f"decode fused {name} {R}x{C} rpb={nm.spmv_launch_shape(R, C, 2, 4)['rows_per_workgroup']}")
+    y = down_f16(nm.nm_spmv(values, masks, up_f16(x), 2, 4))
+    Wcat = np.concatenate(Ws)
+    idx = sample_rows(R, k=64, rpb=nm.spmv_launch_shape(R, C, 2, 4)["rows_per_workgroup"])
+    # the part boundaries and their neighbours too
+    edges = np.cumsum([W.shape[0] for W in Ws])[:-1]
+    idx = np.unique(np.concatenate([idx, edges - 1, edges]))
+    it = torch.from_numpy(idx).to(device())
+    rv, rm = oracle.pack_ref(Wcat[idx], 2, 4)
+    assert np.array_equal(down_u32(masks.index_select(0, it)), rm)
+    assert np.array_equal(down_bits16(values.index_select(0, it)), rv)
+    rep = oracle.y_tolerance_report(y[idx], oracle.spmv_ref(rv, rm, x, C, 2, 4))
+    assert rep["ok"], (name, rep)
