@@ -1,0 +1,123 @@
+"""GPU tests of the entry points under HIP graph capture: every product is captured once
+into a torch.cuda.CUDAGraph and replayed several times, with the program's own eager work
+(other products, torch ops, a new input written in place) between the replays. Each replay
+must give the bits an eager call gives on the same inputs (the kernels are deterministic),
+and the first eager result is checked against the CPU oracle, so the captured path is tied
+to the oracle too. The library allocates nothing and records no memset, so nothing it
+captures depends on the capture-time state of its buffers."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import semi_structured_sparse_amd as nm
+import synth
+from tests.gpu_helpers import device, down_bits16, down_f16, say, up_f16
+
+pytestmark = pytest.mark.gpu
+REPLAYS = 4
+
+
+def _replay_and_check(run, inputs, out, reseed):
+    """run(): the product writing into `out`; inputs: tensors it reads; reseed(i): new
+    contents for the inputs (written in place) before replay i. Captures run(), then for
+    each replay: refresh the inputs, do unrelated eager work, replay, and compare with an
+    eager call on the same inputs."""
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()                                     # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    scratch = torch.empty(1 << 20, dtype=torch.float16, device=device())
+    for i in range(REPLAYS):
+        reseed(i)
+        scratch.normal_()                         # eager work between the replays
+        _ = (scratch * 2).sum()
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        got = down_bits16(out).copy()
+        out.fill_(float("nan"))
+        run()                                     # eager on the same inputs
+        torch.cuda.synchronize()
+        want = down_bits16(out)
+        assert np.array_equal(got, want), f"replay {i} differs from the eager call"
+    del g
+
+
+@pytest.mark.parametrize("N,M", synth.PATTERNS)
+def test_spmv_graph_replays(N, M):
+    R, C = 2100, 4096
+    say(f"graph spmv {N}:{M} {R}x{C}")
+    W = synth.weight(R, C, 5000 + N)
+    x = synth.activation(C, 5001 + N)
+    values, masks = nm.nm_pack(up_f16(W), N, M)
+    xd = up_f16(x)
+    y = torch.empty(R, dtype=torch.float16, device=device())
+    nm.nm_spmv(values, masks, xd, N, M, out=y)
+    torch.cuda.synchronize()
+    rv, rm = oracle.pack_ref(W[:64], N, M)
+    assert oracle.y_tolerance_report(down_f16(y)[:64], oracle.spmv_ref(rv, rm, x, C, N, M))["ok"]
+
+    def reseed(i):
+        xd.copy_(up_f16(synth.activation(C, 5100 + 10 * N + i)))
+
+    _replay_and_check(lambda: nm.nm_spmv(values, masks, xd, N, M, out=y), [values, masks, xd], y, reseed)
+
+
+def test_gemv_dense_graph_replays():
+    R, C = 1500, 4096
+    W = up_f16(synth.weight(R, C, 5200))
+    x = synth.activation(C, 5201)
+    xd = up_f16(x)
+    y = torch.empty(R, dtype=torch.float16, device=device())
+    _replay_and_check(lambda: nm.nm_gemv_dense(W, xd, out=y), [W, xd], y,
+                      lambda i: xd.copy_(up_f16(synth.activation(C, 5210 + i))))
+
+
+# batch products: the small-batch kernel (B = 4), the skinny kernel (2:4 at B = 8) and its
+# split variant (4:8 at B = 8, 8:16 at B = 20 in two launches), the prefill kernel (B = 40)
+BATCH_CASES = [(2, 4, 4), (2, 4, 8), (4, 8, 8), (8, 16, 20), (16, 32, 6), (2, 4, 40)]
+
+
+@pytest.mark.parametrize("N,M,B", BATCH_CASES)
+def test_spmm_graph_replays(N, M, B):
+    R, C = 2064, 1024
+    say(f"graph spmm {N}:{M} {R}x{C} B={B} {nm.spmm_variant(R, C, B, N, M)}")
+    W = synth.weight(R, C, 5300 + N + B)
+    X = synth.activations(B, C, 5301 + N + B)
+    values, masks = nm.nm_pack(up_f16(W), N, M)
+    Xd = up_f16(X)
+    Y = torch.empty((B, R), dtype=torch.float16, device=device())
+    nm.nm_spmm(values, masks, Xd, N, M, out=Y)
+    torch.cuda.synchronize()
+    rv, rm = oracle.pack_ref(W[:48], N, M)
+    rep = oracle.y_tolerance_report(down_f16(Y)[:, :48], oracle.spmm_ref(rv, rm, X, C, N, M))
+    assert rep["ok"], rep
+
+    def reseed(i):
+        Xd.copy_(up_f16(synth.activations(B, C, 5400 + 10 * B + i)))
+
+    _replay_and_check(lambda: nm.nm_spmm(values, masks, Xd, N, M, out=Y), [values, masks, Xd], Y, reseed)
+
+
+def test_prefill_graph_replays():
+    R, C, T = 1000, 2048, 300
+    W = synth.weight(R, C, 5500)
+    values, masks = nm.nm_pack(up_f16(W), 2, 4)
+    Wd = up_f16(W)
+    Xd = up_f16(synth.activations(T, C, 5501))
+    Y = torch.empty((T, R), dtype=torch.float16, device=device())
+    Yd = torch.empty((T, R), dtype=torch.float16, device=device())
+
+    def reseed(i):
+        Xd.copy_(up_f16(synth.activations(T, C, 5510 + i)))
+
+    _replay_and_check(lambda: nm.nm_spmm_prefill(values, masks, Xd, out=Y), [values, masks, Xd], Y, reseed)
+    _replay_and_check(lambda: nm.nm_gemm_dense_prefill(Wd, Xd, out=Yd), [Wd, Xd], Yd, reseed)
