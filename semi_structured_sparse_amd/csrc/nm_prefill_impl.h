@@ -356,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void prefill_spmm_kernel(const uint16_t* 
   for (int a = 0; a < TR; ++a) {
     const uint32_t rl = uint32_t(wave * 16 * TR + 16 * a + li);
     voff[a] = rl * uint32_t(cols) + 16u * uint32_t(q);          // values 8q.. of the step
-    moff[a] = rl * uint32_t(words) * 4u + 8u * uint32_t(q);      // mask words 2q, 2q + 1 of a block
+    moff[a] = rl * uint32_t(words) * 4u + 16u * uint32_t(q);     // mask words 4q .. 4q + 3 of a block
   }
   const int qcol = 32 * (q >> 1);  // first column of this lane's mask word in a sub-step
   const int mshift = 16 * (q & 1);
@@ -372,26 +372,29 @@ __global__ __launch_bounds__(kThreads) void prefill_spmm_kernel(const uint16_t* 
   };
 
   // Mask words, a block of kMaskSteps 64-column steps (2 kMaskSteps words of each row) at
-  // a time: lane q of row li holds words 2q, 2q + 1 of the block (one 8-byte load per row
-  // tile per block instead of one 4-byte load per step; a load touches the same 16 rows
-  // either way). At step j of the block the lane needs word 2j + (q >> 1), which lane
-  // li + 16 j holds in half q >> 1; a cross-lane permute fetches it. The block for the next
-  // steps is loaded kMaskSteps - D steps into the current one, D steps ahead like the values.
-  constexpr int kMaskSteps = 4;
+  // a time: lane q of row li holds words 4q .. 4q + 3 of the block (one 16-byte load per
+  // row tile per block instead of one 4-byte load per step; a load touches the same 16
+  // rows either way, so fewer, wider loads cost less). At step j of the block the lane
+  // needs word 2j + (q >> 1), which lane li + 16 (j / 2) holds as its word 2 (j % 2) +
+  // (q >> 1); a cross-lane permute fetches it. The block for the next steps is loaded
+  // kMaskSteps - D steps into the current one, D steps ahead like the values.
+  constexpr int kMaskSteps = 8;
   static_assert(KS == 64, "mask blocks are laid out for 64-column steps");
   const int steps = (cols + KS - 1) / KS;
   const int last_block = (steps - 1) / kMaskSteps;
-  uint2 mcur[TR], mnext[TR];
+  uint4 mcur[TR], mnext[TR];
   auto load_masks = [&](int blk) {
 #pragma unroll
-    for (int a = 0; a < TR; ++a) mnext[a] = buf_load8(mr, moff[a] + uint32_t(32 * min(blk, last_block)));
+    for (int a = 0; a < TR; ++a) mnext[a] = buf_load16(mr, moff[a] + uint32_t(64 * min(blk, last_block)));
   };
   load_masks(0);
   auto hook = [&](auto pc, int s0) {
     constexpr int P = decltype(pc)::value;
     if constexpr (P == 0) {   // the position codes of the block's words, once per block
 #pragma unroll
-      for (int a = 0; a < TR; ++a) mcur[a] = make_uint2(pair_codes32(mnext[a].x), pair_codes32(mnext[a].y));
+      for (int a = 0; a < TR; ++a)
+        mcur[a] = make_uint4(pair_codes32(mnext[a].x), pair_codes32(mnext[a].y), pair_codes32(mnext[a].z),
+                             pair_codes32(mnext[a].w));
     }
     if constexpr (P == kMaskSteps - D) load_masks(s0 / kMaskSteps + 1);
   };
@@ -402,14 +405,14 @@ __global__ __launch_bounds__(kThreads) void prefill_spmm_kernel(const uint16_t* 
   const uint32_t b_lo = x_offset<T::kRowBytes>(li, q), b_hi = x_offset<T::kRowBytes>(li, 4 + q);
   auto compute = [&](const AF& f, const char* buf, auto pc) {
     constexpr int J = decltype(pc)::value;           // step within the mask block
-    const int src = 4 * (li + 16 * J);               // byte address of lane li + 16 J
+    const int src = 4 * (li + 16 * (J >> 1));        // byte address of lane li + 16 (J / 2)
     h8_t av[TR];
     int idx[TR];
 #pragma unroll
     for (int a = 0; a < TR; ++a) {
       av[a] = __builtin_bit_cast(h8_t, f.v[a][0]);
-      const uint32_t w0 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur[a].x)));
-      const uint32_t w1 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur[a].y)));
+      const uint32_t w0 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int((J & 1) ? mcur[a].z : mcur[a].x)));
+      const uint32_t w1 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int((J & 1) ? mcur[a].w : mcur[a].y)));
       idx[a] = int(__builtin_amdgcn_ubfe((q >> 1) ? w1 : w0, uint32_t(mshift), 16));
     }
     // X fragments are read one token tile ahead of the math that uses them

@@ -13,9 +13,10 @@
 // partial tiles of a row group are summed through LDS at the end.
 //
 // Operand layouts, the K permutation that makes a lane's 8 values contiguous in the packed
-// row, the index-word table and the mask-block permute are those of the prefill kernel
-// (nm_prefill_impl.h): lane (q = l / 16, li = l % 16) holds values 8q .. 8q+7 of a 64-column
-// step for row li, and the X fragment of token li at column chunks q and 4 + q of the step.
+// row, the position codes and the mask-block permute are those of the prefill kernel
+// (nm_prefill_impl.h), with mask blocks of 4 steps here (a wave may own only 4 steps):
+// lane (q = l / 16, li = l % 16) holds values 8q .. 8q+7 of a 64-column step for row li,
+// and the X fragment of token li at column chunks q and 4 + q of the step.
 //
 // 4:8 and 8:16 (SPLIT): these patterns also keep exactly 8 values per 16 aligned columns,
 // so the same 16-byte load gives a lane the kept values of its 16 columns, but a 4-column
