@@ -713,6 +713,10 @@ def prefill_main(args, torch, nm, synth, dev):
     print(json.dumps(out), flush=True)
 
 
+def _rows_phrase(frac):
+    return "all rows" if frac >= 1.0 else f"the first {frac:g} of the rows"
+
+
 def prefill_cpu_baseline(items, T, frac):
     """Time the oracle (as it is: densify, fp64 matrix product through numpy's BLAS) on the
     first rows of every prefill layer with all tokens, and compare its Y with the GPU's."""
@@ -739,7 +743,7 @@ def prefill_cpu_baseline(items, T, frac):
     log(f"prefill cpu baseline: {flops / secs / 1e12:.5f} useful TFLOP/s over {rows_total} rows x {T} tokens "
         f"in {secs:.1f}s (leg {time.time() - t_start:.1f}s)")
     return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {frac:g} of the rows of each of the {len(items)} layers ({rows_total} rows) x {T} "
+            "sample": f"{_rows_phrase(frac)} of each of the {len(items)} layers ({rows_total} rows) x {T} "
                       f"tokens; densify + fp64 matrix product (numpy BLAS, {cores} threads)",
             "seconds": round(secs, 2), "cpu_model": cpu_info(),
             "parity_vs_gpu": {"max_err_over_bound": worst, "rel_l2": rel, "ok": worst <= 1.0 and rel <= 1e-3}}
@@ -815,7 +819,7 @@ def cpu_baseline(layers, frac):
     log(f"cpu baseline: {b_total / t_total / 1e9:.4f} GB/s over {rows_total} rows in {t_total:.1f}s on "
         f"{cores} threads, {b1 / t1 / 1e9:.4f} GB/s on 1 thread (leg {time.time() - t_start:.1f}s)")
     return {"value": round(b_total / t_total / 1e9, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {frac:g} of the rows of each of the {len(layers)} layers ({rows_total} rows) in "
+            "sample": f"{_rows_phrase(frac)} of each of the {len(layers)} layers ({rows_total} rows) in "
                       f"{len(chunks)} chunks over {cores} threads; densify + fp64 matvec (numpy); median of 3 passes",
             "seconds": round(t_total, 2), "cpu_model": cpu_info(),
             "single_thread": {"value": round(b1 / t1 / 1e9, 5), "unit": "GB/s", "seconds": round(t1, 2),
