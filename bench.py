@@ -561,8 +561,9 @@ def decode_main(args, torch, nm, synth, dev):
 
 def prefill_main(args, torch, nm, synth, dev):
     """Prefill: the Llama-3.1-8B projection shapes (q, kv, gate_up, down) as 2:4 packed
-    weights times a prompt of --prompt tokens (X [tokens][cols], seeded N(0,1)), on the
-    sparse matrix cores (nm_spmm_prefill); a step is one pass over the four products. Also
+    weights (or the first of --patterns: 4:8 or 8:16, as two 2:4 operands) times a prompt of
+    --prompt tokens (X [tokens][cols], seeded N(0,1)), on the sparse matrix cores
+    (nm_spmm_prefill); a step is one pass over the four products. Also
     timed: the dense matrix-core product over the same dense weights (nm_gemm_dense_prefill)
     and, as context only, torch.mm (the vendor BLAS) on the same shapes.
 
@@ -574,14 +575,22 @@ def prefill_main(args, torch, nm, synth, dev):
     T = args.prompt
     cfg = 6
     shapes = synth.LLAMA31_8B
+    pat = (2, 4)
+    if args.patterns:   # one of the patterns with a matrix-core product
+        pat = tuple(int(v) for v in args.patterns.split(",")[0].split(":"))
+        if pat not in ((2, 4), (4, 8), (8, 16)):
+            print(f"prefill: pattern {pat} has no matrix-core product (2:4, 4:8, 8:16)", file=sys.stderr)
+            sys.exit(2)
+    N, M = pat
+    split = pat != (2, 4)
     t_gen = time.time()
     items = []
     for li, (name, R, C) in enumerate(shapes):
-        W = synth.weight(R, C, synth.weight_seed(cfg, li, (2, 4)))
-        X = synth.activations(T, C, synth.x_seed(cfg, li, (2, 4)))
+        W = synth.weight(R, C, synth.weight_seed(cfg, li, pat))
+        X = synth.activations(T, C, synth.x_seed(cfg, li, pat))
         Wd = torch.from_numpy(W).to(dev)
         Xd = torch.from_numpy(X).to(dev)
-        values, masks = nm.nm_pack(Wd, 2, 4)
+        values, masks = nm.nm_pack(Wd, N, M)
         items.append(dict(name=name, R=R, C=C, W=Wd, Wt=Wd.t().contiguous(), X=Xd, X_host=X, values=values,
                           masks=masks, Y=torch.empty((T, R), dtype=torch.float16, device=dev),
                           Yd=torch.empty((T, R), dtype=torch.float16, device=dev),
@@ -590,7 +599,7 @@ def prefill_main(args, torch, nm, synth, dev):
     torch.cuda.synchronize()
     log(f"prefill: generated and packed {len(items)} layers x {T} tokens in {time.time() - t_gen:.1f}s")
     sp_a = [(q["values"].data_ptr(), q["masks"].data_ptr(), q["X"].data_ptr(), q["Y"].data_ptr(), q["R"], q["C"],
-             T, 2, 4) for q in items]
+             T, N, M) for q in items]
     dn_a = [(q["W"].data_ptr(), q["X"].data_ptr(), q["Yd"].data_ptr(), q["R"], q["C"], T) for q in items]
 
     def sp_step(s_):
@@ -650,7 +659,7 @@ def prefill_main(args, torch, nm, synth, dev):
             log(f"torch.mm timing unavailable: {e}")
             us_t = float("nan")
         per_layer.append({"layer": q["name"], "shape": f"{q['R']}x{q['C']}", "tokens": T,
-                          "kernel": nm.prefill_variant(q["R"], q["C"], T, True),
+                          "kernel": nm.prefill_variant(q["R"], q["C"], T, True, split=split),
                           "us": round(us_s, 2), "useful_TFLOPs": round(q["flops_useful"] / us_s / 1e6, 1),
                           "dense_equiv_TFLOPs": round(q["flops_dense"] / us_s / 1e6, 1),
                           "dense_kernel": nm.prefill_variant(q["R"], q["C"], T, False),
@@ -682,9 +691,9 @@ def prefill_main(args, torch, nm, synth, dev):
                 "flops_counted": "useful: 2 x rows x cols/2 x tokens (kept weights)"}
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = prefill_cpu_baseline(items, T, args.cpu_rows_frac)
+        cpu = prefill_cpu_baseline(items, T, args.cpu_rows_frac, N, M)
     out = {
-        "metric": "2:4 prefill SpMM useful TFLOP/s on the sparse matrix cores + speedup vs dense matrix-core GEMM",
+        "metric": f"{N}:{M} prefill SpMM useful TFLOP/s on the sparse matrix cores + speedup vs dense matrix-core GEMM",
         "value": round(value, 1),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -698,7 +707,7 @@ def prefill_main(args, torch, nm, synth, dev):
         "accumulate": "f32",
         "data": "synthetic",
         "config": {"workload": f"llama3.1-8b prefill: {len(items)} projection shapes (q, kv, gate_up, down) x "
-                               f"{T}-token prompt, 2:4, fp16 W ~N(0,0.02^2) magnitude-pruned, X ~N(0,1)",
+                               f"{T}-token prompt, {N}:{M}, fp16 W ~N(0,0.02^2) magnitude-pruned, X ~N(0,1)",
                    "tokens": T, "flops_useful_per_step": useful, "parallelism": "single GPU"},
         "dense_equiv_TFLOPs": round(dense_f / (ms_sp * 1e-3) / 1e12, 1),
         "dense_ms_per_step": round(ms_dn, 5),
@@ -717,7 +726,7 @@ def _rows_phrase(frac):
     return "all rows" if frac >= 1.0 else f"the first {frac:g} of the rows"
 
 
-def prefill_cpu_baseline(items, T, frac):
+def prefill_cpu_baseline(items, T, frac, N=2, M=4):
     """Time the oracle (as it is: densify, fp64 matrix product through numpy's BLAS) on the
     first rows of every prefill layer with all tokens, and compare its Y with the GPU's."""
     import oracle
@@ -731,9 +740,9 @@ def prefill_cpu_baseline(items, T, frac):
     for q in items:
         n = max(16, int(q["R"] * frac) // 16 * 16)
         n = min(n, q["R"])
-        rv, rm = oracle.pack_ref(q["W_cpu"][:n], 2, 4)
+        rv, rm = oracle.pack_ref(q["W_cpu"][:n], N, M)
         t0 = time.perf_counter()
-        ref = oracle.spmm_ref(rv, rm, q["X_host"], q["C"], 2, 4)
+        ref = oracle.spmm_ref(rv, rm, q["X_host"], q["C"], N, M)
         secs += time.perf_counter() - t0
         flops += n * q["C"] * T
         rows_total += n

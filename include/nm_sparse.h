@@ -58,7 +58,7 @@ typedef enum {
   NM_ERR_SHAPE = 2,    /* rows < 1, cols < 32, cols % 32 != 0, batch / tokens < 1, or a
                           size beyond an entry point's limits                         */
   NM_ERR_PATTERN = 3,  /* (N, M) not a supported pattern (nm_spmm: 50% patterns for
-                          batch > 1; nm_spmm_prefill: 2:4 only)                       */
+                          batch > 1; nm_spmm_prefill: 2:4, 4:8, 8:16)                 */
   NM_ERR_ALIGN = 4,    /* W, values or x not 16-byte aligned; masks not 4-byte; y not 2 */
   NM_ERR_TOO_WIDE = 5, /* 2*cols bytes of x exceed the LDS one workgroup may use        */
   NM_ERR_HIP = 6       /* a HIP runtime call failed (see nm_last_hip_error)             */
@@ -115,12 +115,12 @@ int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,
  *   Y[b][r] = fp16( sum_c W'[r][c] * X[b][c] ),  X fp16 [batch][cols], Y fp16 [batch][rows]
  * (row b of X is one activation vector: the layout of a batch of tokens). Products and
  * sums fp32, one RNE rounding, fixed summation order (bit-identical run to run).
- *   - batch >= 32 with 2:4: nm_spmm_prefill (matrix cores), with its limits.
- *   - on layers of at least 2048 rows, 5 <= batch < 32 with 2:4 and batch >= 5 with 4:8
- *     or 8:16: the sparse matrix instruction with X staged in LDS, 16 vectors per launch
- *     (cols <= 2^21). 4:8 and 8:16 keep 8 values in every 16 columns like 2:4, so each
- *     4-column group is split into two 2:4 operands (its first two kept values and the
- *     rest) that go through the instruction with the same X.
+ *   - batch >= 32 with 2:4, 4:8 or 8:16: nm_spmm_prefill (matrix cores), with its limits.
+ *   - on layers of at least 2048 rows, 5 <= batch < 32 with 2:4, 4:8 or 8:16: the sparse
+ *     matrix instruction with X staged in LDS, 16 vectors per launch (cols <= 2^21). 4:8
+ *     and 8:16 keep 8 values in every 16 columns like 2:4, so each 4-column group is split
+ *     into two 2:4 operands (its first two kept values and the rest) that go through the
+ *     instruction with the same X.
  *   - otherwise the small-batch kernel (vector units; x staged in LDS in column phases
  *     when it does not fit at once, so any width is accepted), on consecutive groups of
  *     8 rows of X (one launch per group). batch == 1 gives the same result as nm_spmv
@@ -137,17 +137,19 @@ int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, ui
 int nm_gemm_dense(const uint16_t* W, const uint16_t* X, uint16_t* Y,
                   int64_t rows, int64_t cols, int64_t batch, void* stream);
 
-/* Prefill product of a 2:4 packed matrix on the sparse matrix cores ([NEWS-NEW]: prefill
+/* Prefill product of a packed 50% matrix on the sparse matrix cores ([NEWS-NEW]: prefill
  * is compute-bound and runs sparse matrix-matrix products; [KERNEL]: that is where 2:4
  * sparse matrix hardware speeds inference up, and the bitmask format): for tokens >= 1
  * rows of X,
  *   Y[t][r] = fp16( sum_c W'[r][c] * X[t][c] ),  X fp16 [tokens][cols], Y fp16 [tokens][rows],
- * with the (values, masks) of nm_pack for N = 2, M = 4 (any other pattern is
- * NM_ERR_PATTERN). fp16 products, fp32 sums in the matrix instruction's order (fixed, so
- * bit-identical run to run), one RNE rounding. Limits: cols <= 2^21, tokens <= 2^24
- * (NM_ERR_SHAPE beyond). Masks must be as nm_pack writes them (two bits per 4-column
- * group); a malformed mask gives an unspecified Y but never an out-of-bounds access.
- * values, X 16-byte aligned; masks 4-byte; Y 2-byte. */
+ * with the (values, masks) of nm_pack for (N, M) = (2, 4), (4, 8) or (8, 16) (others are
+ * NM_ERR_PATTERN). 2:4 runs on the 2:4 sparse instruction directly; 4:8 and 8:16, which
+ * keep 8 values in every 16 columns, as two 2:4 operands per 4-column group (its first two
+ * kept values, and the rest), so at twice the instruction count. fp16 products, fp32 sums
+ * in the matrix instruction's order (fixed, so bit-identical run to run), one RNE
+ * rounding. Limits: cols <= 2^21, tokens <= 2^24 (NM_ERR_SHAPE beyond). Masks must be as
+ * nm_pack writes them; a malformed mask gives an unspecified Y but never an out-of-bounds
+ * access. values, X 16-byte aligned; masks 4-byte; Y 2-byte. */
 int nm_spmm_prefill(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
                     int64_t rows, int64_t cols, int64_t tokens, int N, int M, void* stream);
 
@@ -162,10 +164,11 @@ int nm_gemm_dense_prefill(const uint16_t* W, const uint16_t* X, uint16_t* Y,
  * arguments are invalid. Static string, never NULL. */
 const char* nm_spmm_variant(int64_t rows, int64_t cols, int64_t batch, int N, int M);
 
-/* Introspection: the name of the kernel configuration nm_spmm_prefill (sparse != 0) or
- * nm_gemm_dense_prefill (sparse == 0) launches for this shape on the current device, as it
- * appears in profiler traces (for example "prefill_spmm_kernel<2, 16, 64, 2>"); "" if the
- * arguments are invalid. Static string, never NULL. */
+/* Introspection: the name of the kernel configuration nm_spmm_prefill (sparse == 1: 2:4;
+ * sparse == 2: 4:8 or 8:16) or nm_gemm_dense_prefill (sparse == 0) launches for this shape
+ * on the current device, as it appears in profiler traces (for example
+ * "prefill_spmm_kernel<4, 8, 64, 2>"); "" if the arguments are invalid. Static string,
+ * never NULL. */
 const char* nm_prefill_variant(int64_t rows, int64_t cols, int64_t tokens, int sparse);
 
 /* Introspection: the name of the kernel configuration nm_spmv launches for this shape

@@ -160,13 +160,13 @@ int nm_spmm_prefill(const uint16_t* values, const uint32_t* masks, const uint16_
                     int64_t cols, int64_t tokens, int N, int M, void* stream) {
   if (!values || !masks || !X || !Y) return NM_ERR_NULL;
   if (!nm::valid_shape(rows, cols) || tokens < 1 || !nm::prefill_fits(rows, cols, tokens)) return NM_ERR_SHAPE;
-  if (N != 2 || M != 4) return NM_ERR_PATTERN;
+  if (!nm::prefill_pattern(N, M)) return NM_ERR_PATTERN;
   if (!nm::aligned(values, 16) || !nm::aligned(masks, 4) || !nm::aligned(X, 16) || !nm::aligned(Y, 2))
     return NM_ERR_ALIGN;
   nm::DeviceInfo dev;
   hipError_t e = nm::current_device_info(&dev);
   if (e != hipSuccess) return nm::hip_fail(e);
-  e = nm::launch_prefill_spmm(values, masks, X, Y, rows, cols, tokens, static_cast<hipStream_t>(stream), dev);
+  e = nm::launch_prefill_spmm(values, masks, X, Y, rows, cols, tokens, N, M, static_cast<hipStream_t>(stream), dev);
   return e == hipSuccess ? NM_OK : nm::hip_fail(e);
 }
 
@@ -187,7 +187,7 @@ int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, ui
   if (!values || !masks || !X || !Y) return NM_ERR_NULL;
   if (!nm::valid_shape(rows, cols) || batch < 1 || batch > nm::kPrefillMaxTokens) return NM_ERR_SHAPE;
   if (!nm::valid_pattern(N, M) || (batch > 1 && M != 2 * N)) return NM_ERR_PATTERN;
-  if (batch >= nm::kMatrixCoreMinBatch && N == 2 && M == 4)  // matrix-core product
+  if (batch >= nm::kMatrixCoreMinBatch && nm::prefill_pattern(N, M))  // matrix-core product
     return nm_spmm_prefill(values, masks, X, Y, rows, cols, batch, N, M, stream);
   if (!nm::aligned(values, 16) || !nm::aligned(masks, 4) || !nm::aligned(X, 16) || !nm::aligned(Y, 2))
     return NM_ERR_ALIGN;
@@ -196,8 +196,8 @@ int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, ui
   if (e != hipSuccess) return nm::hip_fail(e);
   if (M != 2 * N && cols > nm::max_cols_for(dev)) return NM_ERR_TOO_WIDE;  // 25%: single-vector kernel only
   if (nm::use_skinny(rows, cols, batch, N, M, dev)) {
-    // 2:4 at 5..31 vectors, 4:8 and 8:16 from 5 vectors on, on a large layer: the sparse
-    // matrix instruction, 16 vectors per launch
+    // 2:4, 4:8 and 8:16 at 5..31 vectors on a large layer: the sparse matrix instruction,
+    // 16 vectors per launch
     for (int64_t b0 = 0; b0 < batch; b0 += nm::kSkinnyBatch) {
       const int nb = int(batch - b0 < nm::kSkinnyBatch ? batch - b0 : nm::kSkinnyBatch);
       e = nm::launch_skinny_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb, N, M,
@@ -240,8 +240,8 @@ const char* nm_spmm_variant(int64_t rows, int64_t cols, int64_t batch, int N, in
   nm::DeviceInfo dev;
   if (nm::current_device_info(&dev) != hipSuccess) return "";
   if (batch == 1 && cols <= nm::max_cols_for(dev)) return nm::spmv_variant(rows, cols, N, M, dev);
-  if (N == 2 && M == 4 && batch >= nm::kMatrixCoreMinBatch)
-    return nm::prefill_fits(rows, cols, batch) ? nm::prefill_variant(rows, batch, true, dev) : "";
+  if (nm::prefill_pattern(N, M) && batch >= nm::kMatrixCoreMinBatch)
+    return nm::prefill_fits(rows, cols, batch) ? nm::prefill_variant(rows, batch, true, dev, N != 2) : "";
   if (nm::use_skinny(rows, cols, batch, N, M, dev)) return nm::skinny_variant(N);
   return nm::spmm_variant(N, batch < nm::kSmallBatch ? batch : nm::kSmallBatch);
 }
@@ -250,7 +250,7 @@ const char* nm_prefill_variant(int64_t rows, int64_t cols, int64_t tokens, int s
   if (!nm::valid_shape(rows, cols) || tokens < 1 || !nm::prefill_fits(rows, cols, tokens)) return "";
   nm::DeviceInfo dev;
   if (nm::current_device_info(&dev) != hipSuccess) return "";
-  return nm::prefill_variant(rows, tokens, sparse != 0, dev);
+  return nm::prefill_variant(rows, tokens, sparse != 0, dev, sparse == 2);
 }
 
 const char* nm_spmv_variant(int64_t rows, int64_t cols, int N, int M) {

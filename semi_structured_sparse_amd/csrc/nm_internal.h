@@ -81,8 +81,11 @@ int64_t max_cols_for(const DeviceInfo& dev);
 constexpr int64_t kPrefillMaxCols = int64_t(1) << 21;
 constexpr int64_t kPrefillMaxTokens = int64_t(1) << 24;
 bool prefill_fits(int64_t rows, int64_t cols, int64_t tokens);
+// 50% patterns with a matrix-core product: 2:4, and 4:8 / 8:16 as two 2:4 operands.
+bool prefill_pattern(int n, int m);
 hipError_t launch_prefill_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
-                               int64_t rows, int64_t cols, int64_t tokens, hipStream_t stream, const DeviceInfo& dev);
+                               int64_t rows, int64_t cols, int64_t tokens, int n, int m, hipStream_t stream,
+                               const DeviceInfo& dev);
 hipError_t launch_prefill_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y, int64_t rows, int64_t cols,
                                int64_t tokens, hipStream_t stream, const DeviceInfo& dev);
 // Small-batch 50% product on the sparse matrix instruction, 1..16 tokens (X [tokens][cols],
@@ -93,10 +96,9 @@ hipError_t launch_skinny_spmm(const uint16_t* values, const uint32_t* masks, con
                               int64_t rows, int64_t cols, int tokens, int n, int m, hipStream_t stream,
                               const DeviceInfo& dev);
 // nm_spmm runs the skinny kernel, kSkinnyBatch vectors per launch, on layers of at least
-// kSkinnyMinRows rows from kSkinnyMinBatch vectors on: for 2:4 up to kMatrixCoreMinBatch
-// (the prefill kernel takes over), for 4:8 and 8:16 at any batch (measured on MI355X: from 5
-// vectors on it beats the small-batch kernel on such layers; on smaller ones its fixed cost
-// of a few microseconds does not pay).
+// kSkinnyMinRows rows from kSkinnyMinBatch vectors up to kMatrixCoreMinBatch, where the
+// prefill kernels take over (measured on MI355X: from 5 vectors on it beats the small-batch
+// kernel on such layers; on smaller ones its fixed cost of a few microseconds does not pay).
 constexpr int64_t kSkinnyMinBatch = 5;
 constexpr int64_t kSkinnyMinRows = 2048;
 constexpr int64_t kSkinnyBatch = 16;
@@ -104,6 +106,6 @@ bool use_skinny(int64_t rows, int64_t cols, int64_t batch, int n, int m, const D
 const char* skinny_variant(int n);
 
 // Name of the kernel configuration the prefill launchers pick (static string).
-const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev);
+const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev, bool split = false);
 
 }  // namespace nm

@@ -1,5 +1,6 @@
 // Launchers of the prefill-sized products (many tokens per weight) on the matrix cores:
-// the 2:4 sparse product and the dense product. The kernels are in nm_prefill_impl.h.
+// the 50% sparse products (2:4 directly, 4:8 and 8:16 split into two 2:4 operands) and the
+// dense product. The kernels are in nm_prefill_impl.h.
 #include "nm_internal.h"
 #include "nm_prefill_impl.h"
 
@@ -43,18 +44,25 @@ bool prefill_fits(int64_t rows, int64_t cols, int64_t tokens) {
   return cols <= kPrefillMaxCols && tokens <= kPrefillMaxTokens && workgroups<Small>(rows, tokens) <= INT32_MAX;
 }
 
+bool prefill_pattern(int n, int m) { return 2 * n == m && (n == 2 || n == 4 || n == 8); }
+
 hipError_t launch_prefill_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
-                               int64_t rows, int64_t cols, int64_t tokens, hipStream_t stream, const DeviceInfo& dev) {
-  if (!prefill_fits(rows, cols, tokens)) return hipErrorInvalidValue;
+                               int64_t rows, int64_t cols, int64_t tokens, int n, int m, hipStream_t stream,
+                               const DeviceInfo& dev) {
+  if (!prefill_fits(rows, cols, tokens) || !prefill_pattern(n, m)) return hipErrorInvalidValue;
   int r = int(rows), c = int(cols), t = int(tokens);
   void* args[] = {&values, &masks, &X, &Y, &r, &c, &t};
+  const bool split = n != 2;
   if (use_large<SparseHuge>(rows, tokens, dev))
-    return launch(reinterpret_cast<const void*>(&prefill_spmm_kernel<4, 16, 64, kDepth>),
+    return launch(split ? reinterpret_cast<const void*>(&prefill_split_kernel<4, 16, 64, kDepth>)
+                        : reinterpret_cast<const void*>(&prefill_spmm_kernel<4, 16, 64, kDepth>),
                   dim3(unsigned(workgroups<SparseHuge>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
   if (use_large<SparseLarge>(rows, tokens, dev))
-    return launch(reinterpret_cast<const void*>(&prefill_spmm_kernel<4, 8, 64, kDepth>),
+    return launch(split ? reinterpret_cast<const void*>(&prefill_split_kernel<4, 8, 64, kDepth>)
+                        : reinterpret_cast<const void*>(&prefill_spmm_kernel<4, 8, 64, kDepth>),
                   dim3(unsigned(workgroups<SparseLarge>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
-  return launch(reinterpret_cast<const void*>(&prefill_spmm_kernel<1, 4, 64, kDepth>),
+  return launch(split ? reinterpret_cast<const void*>(&prefill_split_kernel<1, 4, 64, kDepth>)
+                      : reinterpret_cast<const void*>(&prefill_spmm_kernel<1, 4, 64, kDepth>),
                 dim3(unsigned(workgroups<Small>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
 }
 
@@ -70,7 +78,11 @@ hipError_t launch_prefill_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y
                 dim3(unsigned(workgroups<Small>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
 }
 
-const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev) {
+const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev, bool split) {
+  if (sparse && split)
+    return use_large<SparseHuge>(rows, tokens, dev)    ? "prefill_split_kernel<4, 16, 64, 2>"
+           : use_large<SparseLarge>(rows, tokens, dev) ? "prefill_split_kernel<4, 8, 64, 2>"
+                                                       : "prefill_split_kernel<1, 4, 64, 2>";
   if (sparse)
     return use_large<SparseHuge>(rows, tokens, dev)    ? "prefill_spmm_kernel<4, 16, 64, 2>"
            : use_large<SparseLarge>(rows, tokens, dev) ? "prefill_spmm_kernel<4, 8, 64, 2>"

@@ -99,6 +99,94 @@ constexpr bool pair_codes_match_table() {
 }
 static_assert(pair_codes_match_table(), "bitwise position codes disagree with the table");
 
+// ---- 4:8 and 8:16 on the 2:4 instruction (split operands) ----
+// These patterns keep exactly 8 values in every 16 aligned columns, so a lane's 16-byte
+// load holds the kept values of its 16 columns (4 groups), but a 4-column group may keep
+// 0 .. 4 of them. Each group is split in two: its first two kept values (ascending column)
+// form a pair of a 2:4 operand A, the third and fourth a pair of a 2:4 operand B, with
+// zeros where a group keeps fewer; A and B go through the sparse instruction with the same
+// X fragment into the same accumulator. Moving the values into place is a per-lane shuffle
+// that depends only on the lane's 16 mask bits: a table indexed by (side, mask byte) gives
+// for each output dword two byte selectors (one over values 0..3, one over values 4..7,
+// v_perm_b32, results ORed) and the pairs' 2-bit position codes. The low mask byte's values
+// are ranks 0 .. c-1 of the lane's 8 and the high byte's the last ones, 8 - c' .. 7 (c, c'
+// their bit counts), so each byte's entry depends on that byte alone.
+//
+// ---- split tables (4:8, 8:16) ----
+// Entry (side, byte), side 0 for the low mask byte of a lane's 16 bits, 1 for the high one:
+// sel[4 g + {0, 1}] = selectors of operand A's pair for the byte's group g (over values 0..3,
+// over values 4..7), sel[4 g + {2, 3}] the same for operand B; idx bits 4 g .. 4 g + 3 = A's
+// position code for group g, bits 8 + 4 g .. = B's. Selector byte 0x0C gives a zero byte.
+constexpr int kSplitEntries = 512;
+constexpr uint32_t kSplitSelBytes = kSplitEntries * 32;
+constexpr uint32_t kSplitLutBytes = kSplitSelBytes + kSplitEntries * 2;   // + 16-bit codes
+
+struct SplitEntry {
+  uint32_t sel[8];
+  uint32_t idx;
+};
+
+// selector bytes placing value `rank` of the lane's 8 (-1: zero) as one fp16 half, for the
+// operand pair (values 0..3) when !high, (values 4..7) when high
+__host__ __device__ constexpr uint32_t split_half_sel(int rank, bool high) {
+  if (rank < 0 || (rank >= 4) != high) return 0x0C0Cu;
+  const uint32_t b = 2u * uint32_t(rank & 3);
+  return b | (b + 1u) << 8;
+}
+
+__host__ __device__ constexpr SplitEntry split_entry(int side, int byte) {
+  SplitEntry e{};
+  const int c = __builtin_popcount(unsigned(byte));
+  int rank = side ? 8 - c : 0;                       // rank of the byte's first kept value
+  uint32_t idx = 0;
+  for (int g = 0; g < 2; ++g) {
+    const int nib = (byte >> (4 * g)) & 15;
+    int p[4] = {0, 0, 0, 0}, k = 0;
+    for (int b = 0; b < 4; ++b)
+      if ((nib >> b) & 1) p[k++] = b;
+    // pairs as (rank of the value at the lower position, at the higher), -1 = zero; the
+    // positions stay distinct and ascending
+    int a0 = -1, a1 = -1, b0 = -1, b1 = -1, ca = 0x4, cb = 0x4;
+    if (k >= 2) { a0 = rank; a1 = rank + 1; ca = p[0] | p[1] << 2; }
+    else if (k == 1) {
+      if (p[0] < 3) { a0 = rank; ca = p[0] | 3 << 2; } else { a1 = rank; ca = 2 | 3 << 2; }
+    }
+    if (k == 4) { b0 = rank + 2; b1 = rank + 3; cb = 2 | 3 << 2; }
+    else if (k == 3) {
+      if (p[2] < 3) { b0 = rank + 2; cb = p[2] | 3 << 2; } else { b1 = rank + 2; cb = 2 | 3 << 2; }
+    }
+    e.sel[4 * g + 0] = split_half_sel(a0, false) | split_half_sel(a1, false) << 16;
+    e.sel[4 * g + 1] = split_half_sel(a0, true) | split_half_sel(a1, true) << 16;
+    e.sel[4 * g + 2] = split_half_sel(b0, false) | split_half_sel(b1, false) << 16;
+    e.sel[4 * g + 3] = split_half_sel(b0, true) | split_half_sel(b1, true) << 16;
+    idx |= uint32_t(ca) << (4 * g) | uint32_t(cb) << (8 + 4 * g);
+    rank += k;
+  }
+  e.idx = idx;
+  return e;
+}
+
+// The tables as laid out in LDS (17 KiB): entry e's selectors at 32 e, its codes at
+// kSplitSelBytes + 2 e. Built at compile time; each workgroup copies them to LDS once.
+struct SplitTable {
+  uint4 sel[2 * kSplitEntries];
+  uint16_t idx[kSplitEntries];
+};
+static_assert(sizeof(SplitTable) == kSplitLutBytes, "split table layout");
+
+__host__ __device__ constexpr SplitTable make_split_table() {
+  SplitTable t{};
+  for (int e = 0; e < kSplitEntries; ++e) {
+    const SplitEntry x = split_entry(e >> 8, e & 255);
+    t.sel[2 * e] = uint4{x.sel[0], x.sel[1], x.sel[2], x.sel[3]};
+    t.sel[2 * e + 1] = uint4{x.sel[4], x.sel[5], x.sel[6], x.sel[7]};
+    t.idx[e] = uint16_t(x.idx);
+  }
+  return t;
+}
+
+__device__ const SplitTable kSplitTable = make_split_table();
+
 // Buffer loads: a resource spans one workgroup's slice of an operand and the hardware
 // returns zero for offsets at or past its end, so lanes with nothing to load (tokens or
 // rows past the end, columns past the row) take kOutOfRange instead of a branch.
@@ -289,12 +377,14 @@ __device__ __forceinline__ void unroll_slots(F& f) {
 
 // The sparse product's main loop: the dense one's schedule, unrolled U steps at a time (U a
 // multiple of D) so that every slot of a mask block has a fixed name, with a hook per slot
-// (run after the slot's loads are issued) for the mask-block loads. Steps past the last one
-// (up to U - 1) skip only the math.
-template <int TR, int TT, int KS, int D, int U, typename AFrag, typename LoadA, typename Hook, typename Compute>
+// (run after the slot's loads are issued) for the mask-block loads, and a stage callback
+// run once after the first loads are issued (LDS writes of data loaded before them). Steps
+// past the last one (up to U - 1) skip only the math.
+template <int TR, int TT, int KS, int D, int U, typename AFrag, typename LoadA, typename Hook, typename Compute,
+          typename Stage>
 __device__ __forceinline__ void sparse_main_loop(const XStager<TR, TT, KS>& xst,
                                                  char (*xs)[Tile<TR, TT, KS>::kXBytes], int cols, LoadA load_a,
-                                                 Hook hook, Compute compute) {
+                                                 Hook hook, Compute compute, Stage stage) {
   static_assert(U % D == 0, "unroll must be a multiple of the load depth");
   using T = Tile<TR, TT, KS>;
   const int steps = (cols + KS - 1) / KS;
@@ -307,6 +397,7 @@ __device__ __forceinline__ void sparse_main_loop(const XStager<TR, TT, KS>& xst,
     xst.load(xr[p], c, cols);
     load_a(af[p], c);
   }
+  stage();
   xst.store(xr[0], xs[0]);
   for (int s0 = 0; s0 < steps; s0 += U) {
     auto slot = [&](auto pc) {
@@ -325,16 +416,17 @@ __device__ __forceinline__ void sparse_main_loop(const XStager<TR, TT, KS>& xst,
   }
 }
 
-// 2:4 sparse product: values [rows][cols / 2] fp16, masks [rows][cols / 32].
-template <int TR, int TT, int KS, int D>
-__global__ __launch_bounds__(kThreads) void prefill_spmm_kernel(const uint16_t* __restrict__ values,
-                                                                const uint32_t* __restrict__ masks,
-                                                                const uint16_t* __restrict__ X,
-                                                                uint16_t* __restrict__ Y, int rows, int cols,
-                                                                int tokens) {
+// The sparse products: values [rows][cols / 2] fp16, masks [rows][cols / 32]; 2:4 directly
+// (SPLIT false), 4:8 and 8:16 split into two 2:4 operands (SPLIT true, lut = the split
+// tables in LDS).
+template <int TR, int TT, int KS, int D, bool SPLIT>
+__device__ __forceinline__ void prefill_sparse_body(const uint16_t* __restrict__ values,
+                                                    const uint32_t* __restrict__ masks,
+                                                    const uint16_t* __restrict__ X, uint16_t* __restrict__ Y,
+                                                    int rows, int cols, int tokens,
+                                                    char (*xs)[Tile<TR, TT, KS>::kXBytes], char* lut) {
   using T = Tile<TR, TT, KS>;
   constexpr int SUB = T::kSub;
-  __shared__ __attribute__((aligned(16))) char xs[2][T::kXBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, li = lane & 15;
@@ -342,6 +434,24 @@ __global__ __launch_bounds__(kThreads) void prefill_spmm_kernel(const uint16_t* 
   const int r0 = tc.rx * T::kRows + wave * 16 * TR;
   const int t0 = tc.ty * T::kTokens;
   const int words = cols >> 5;
+
+  // SPLIT: this thread's 16-byte chunks of the split tables, loaded before anything else
+  // and written to LDS with the first X chunks (the wait for those covers them)
+  constexpr int kLutChunks = int(kSplitLutBytes / 16);
+  constexpr int kLutPer = SPLIT ? (kLutChunks + kThreads - 1) / kThreads : 1;
+  uint4 lreg[kLutPer];
+  if constexpr (SPLIT) {
+    const uint4* tab = reinterpret_cast<const uint4*>(&kSplitTable);
+#pragma unroll
+    for (int j = 0; j < kLutPer; ++j) lreg[j] = tab[min(tid + kThreads * j, kLutChunks - 1)];
+  }
+  auto stage = [&] {
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int j = 0; j < kLutPer; ++j)
+        if (tid + kThreads * j < kLutChunks) reinterpret_cast<uint4*>(lut)[tid + kThreads * j] = lreg[j];
+    }
+  };
 
   XStager<TR, TT, KS> xst;
   xst.init(X, tokens, cols, t0, tid);
@@ -390,11 +500,12 @@ __global__ __launch_bounds__(kThreads) void prefill_spmm_kernel(const uint16_t* 
   load_masks(0);
   auto hook = [&](auto pc, int s0) {
     constexpr int P = decltype(pc)::value;
-    if constexpr (P == 0) {   // the position codes of the block's words, once per block
+    if constexpr (P == 0) {   // 2:4: the position codes of the block's words, once per block
 #pragma unroll
       for (int a = 0; a < TR; ++a)
-        mcur[a] = make_uint4(pair_codes32(mnext[a].x), pair_codes32(mnext[a].y), pair_codes32(mnext[a].z),
-                             pair_codes32(mnext[a].w));
+        mcur[a] = SPLIT ? mnext[a]
+                        : make_uint4(pair_codes32(mnext[a].x), pair_codes32(mnext[a].y), pair_codes32(mnext[a].z),
+                                     pair_codes32(mnext[a].w));
     }
     if constexpr (P == kMaskSteps - D) load_masks(s0 / kMaskSteps + 1);
   };
@@ -406,14 +517,36 @@ __global__ __launch_bounds__(kThreads) void prefill_spmm_kernel(const uint16_t* 
   auto compute = [&](const AF& f, const char* buf, auto pc) {
     constexpr int J = decltype(pc)::value;           // step within the mask block
     const int src = 4 * (li + 16 * (J >> 1));        // byte address of lane li + 16 (J / 2)
-    h8_t av[TR];
-    int idx[TR];
+    h8_t av[TR], bv[SPLIT ? TR : 1];
+    int idx[TR], idb[SPLIT ? TR : 1];
 #pragma unroll
     for (int a = 0; a < TR; ++a) {
-      av[a] = __builtin_bit_cast(h8_t, f.v[a][0]);
       const uint32_t w0 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int((J & 1) ? mcur[a].z : mcur[a].x)));
       const uint32_t w1 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int((J & 1) ? mcur[a].w : mcur[a].y)));
-      idx[a] = int(__builtin_amdgcn_ubfe((q >> 1) ? w1 : w0, uint32_t(mshift), 16));
+      const uint32_t m16 = __builtin_amdgcn_ubfe((q >> 1) ? w1 : w0, uint32_t(mshift), 16);
+      if constexpr (SPLIT) {
+        // the lane's 16 mask bits select the table entries of its two bytes
+        const uint32_t e0 = 32u * (m16 & 0xFFu), e1 = 32u * (256u + (m16 >> 8));
+        const uint4 s0 = *reinterpret_cast<const uint4*>(lut + e0);
+        const uint4 s1 = *reinterpret_cast<const uint4*>(lut + e0 + 16);
+        const uint4 s2 = *reinterpret_cast<const uint4*>(lut + e1);
+        const uint4 s3 = *reinterpret_cast<const uint4*>(lut + e1 + 16);
+        const uint16_t* codes = reinterpret_cast<const uint16_t*>(lut + kSplitSelBytes);
+        const uint32_t i0 = codes[m16 & 0xFFu], i1 = codes[256u + (m16 >> 8)];
+        const uint4 v = f.v[a][0];
+        auto pick = [&](uint32_t lo_sel, uint32_t hi_sel) {
+          return __builtin_amdgcn_perm(v.y, v.x, lo_sel) | __builtin_amdgcn_perm(v.w, v.z, hi_sel);
+        };
+        av[a] = __builtin_bit_cast(
+            h8_t, make_uint4(pick(s0.x, s0.y), pick(s1.x, s1.y), pick(s2.x, s2.y), pick(s3.x, s3.y)));
+        bv[a] = __builtin_bit_cast(
+            h8_t, make_uint4(pick(s0.z, s0.w), pick(s1.z, s1.w), pick(s2.z, s2.w), pick(s3.z, s3.w)));
+        idx[a] = int(__builtin_amdgcn_perm(i1, i0, 0x0C0C0400u));   // A codes of groups 0..3
+        idb[a] = int(__builtin_amdgcn_perm(i1, i0, 0x0C0C0501u));   // B codes
+      } else {
+        av[a] = __builtin_bit_cast(h8_t, f.v[a][0]);
+        idx[a] = int(m16);
+      }
     }
     // X fragments are read one token tile ahead of the math that uses them
     uint4 lo[2], hi[2];
@@ -430,12 +563,37 @@ __global__ __launch_bounds__(kThreads) void prefill_spmm_kernel(const uint16_t* 
       const u8_t xv = {l.x, l.y, l.z, l.w, h.x, h.y, h.z, h.w};
       const h16_t bf = __builtin_bit_cast(h16_t, xv);
 #pragma unroll
-      for (int a = 0; a < TR; ++a)
+      for (int a = 0; a < TR; ++a) {
         acc[a][b] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(av[a], bf, acc[a][b], idx[a], 0, 0);
+        if constexpr (SPLIT) acc[a][b] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(bv[a], bf, acc[a][b], idb[a], 0, 0);
+      }
     }
   };
-  sparse_main_loop<TR, TT, KS, D, kMaskSteps, AF>(xst, xs, cols, load_a, hook, compute);
+  sparse_main_loop<TR, TT, KS, D, kMaskSteps, AF>(xst, xs, cols, load_a, hook, compute, stage);
   store_all(acc, Y, rows, tokens, r0, t0, lane);
+}
+
+// 2:4 sparse product.
+template <int TR, int TT, int KS, int D>
+__global__ __launch_bounds__(kThreads) void prefill_spmm_kernel(const uint16_t* __restrict__ values,
+                                                                const uint32_t* __restrict__ masks,
+                                                                const uint16_t* __restrict__ X,
+                                                                uint16_t* __restrict__ Y, int rows, int cols,
+                                                                int tokens) {
+  __shared__ __attribute__((aligned(16))) char xs[2][Tile<TR, TT, KS>::kXBytes];
+  prefill_sparse_body<TR, TT, KS, D, false>(values, masks, X, Y, rows, cols, tokens, xs, nullptr);
+}
+
+// 4:8 and 8:16 sparse product (split operands).
+template <int TR, int TT, int KS, int D>
+__global__ __launch_bounds__(kThreads) void prefill_split_kernel(const uint16_t* __restrict__ values,
+                                                                 const uint32_t* __restrict__ masks,
+                                                                 const uint16_t* __restrict__ X,
+                                                                 uint16_t* __restrict__ Y, int rows, int cols,
+                                                                 int tokens) {
+  __shared__ __attribute__((aligned(16))) char xs[2][Tile<TR, TT, KS>::kXBytes];
+  __shared__ __attribute__((aligned(16))) char lut[kSplitLutBytes];
+  prefill_sparse_body<TR, TT, KS, D, true>(values, masks, X, Y, rows, cols, tokens, xs, lut);
 }
 
 // Dense product: W [rows][cols] fp16.

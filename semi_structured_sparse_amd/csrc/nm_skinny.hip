@@ -56,7 +56,7 @@ bool skinny_fits(int64_t rows, int64_t cols, int64_t tokens, int n, int m, const
 bool use_skinny(int64_t rows, int64_t cols, int64_t batch, int n, int m, const DeviceInfo& dev) {
   if (batch < kSkinnyMinBatch || rows < kSkinnyMinRows || !skinny_fits(rows, cols, kSkinnyBatch, n, m, dev))
     return false;
-  return n != 2 || batch < kMatrixCoreMinBatch;
+  return batch < kMatrixCoreMinBatch;   // beyond: the prefill kernels
 }
 
 const char* skinny_variant(int n) { return n == 2 ? "skinny_spmm_kernel<1, false>" : "skinny_spmm_kernel<1, true>"; }

@@ -18,18 +18,9 @@
 // lane (q = l / 16, li = l % 16) holds values 8q .. 8q+7 of a 64-column step for row li,
 // and the X fragment of token li at column chunks q and 4 + q of the step.
 //
-// 4:8 and 8:16 (SPLIT): these patterns also keep exactly 8 values per 16 aligned columns,
-// so the same 16-byte load gives a lane the kept values of its 16 columns, but a 4-column
-// group may keep 0 .. 4 of them. Each group is split in two: its first two kept values
-// (ascending column) form a pair of a 2:4 operand A, the third and fourth a pair of a 2:4
-// operand B, with zeros where a group keeps fewer; A and B go through the sparse
-// instruction with the same X fragment and add into the same accumulator. Moving the
-// values into place is a per-lane shuffle that depends only on the lane's 16 mask bits: a
-// table in LDS, indexed by (side, mask byte), gives for each output dword two byte
-// selectors (one over values 0..3, one over values 4..7, v_perm_b32) and the pairs' 2-bit
-// position codes. The low mask byte's values are ranks 0 .. c-1 of the lane's 8 and the
-// high byte's the last ones, 8 - c' .. 7 (c, c' their bit counts), so each byte's entry
-// depends on that byte alone.
+// 4:8 and 8:16 (SPLIT): each 4-column group is split into two 2:4 operands (its first two
+// kept values, and the rest) by the split tables of nm_prefill_impl.h, which this kernel
+// keeps in LDS; both operands go through the sparse instruction with the same X fragment.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -61,80 +52,6 @@ __device__ __forceinline__ uint32_t xoff(int t, int c, uint32_t rb) {
   return uint32_t(t) * rb + (uint32_t(c ^ (t & 7)) << 4);
 }
 
-// ---- split tables (4:8, 8:16) ----
-// Entry (side, byte), side 0 for the low mask byte of a lane's 16 bits, 1 for the high one:
-// sel[4 g + {0, 1}] = selectors of operand A's pair for the byte's group g (over values 0..3,
-// over values 4..7), sel[4 g + {2, 3}] the same for operand B; idx bits 4 g .. 4 g + 3 = A's
-// position code for group g, bits 8 + 4 g .. = B's. Selector byte 0x0C gives a zero byte.
-constexpr int kSplitEntries = 512;
-constexpr uint32_t kSplitSelBytes = kSplitEntries * 32;
-constexpr uint32_t kSplitLutBytes = kSplitSelBytes + kSplitEntries * 2;   // + 16-bit codes
-
-struct SplitEntry {
-  uint32_t sel[8];
-  uint32_t idx;
-};
-
-// selector bytes placing value `rank` of the lane's 8 (-1: zero) as one fp16 half, for the
-// operand pair (values 0..3) when !high, (values 4..7) when high
-__host__ __device__ constexpr uint32_t split_half_sel(int rank, bool high) {
-  if (rank < 0 || (rank >= 4) != high) return 0x0C0Cu;
-  const uint32_t b = 2u * uint32_t(rank & 3);
-  return b | (b + 1u) << 8;
-}
-
-__host__ __device__ constexpr SplitEntry split_entry(int side, int byte) {
-  SplitEntry e{};
-  const int c = __builtin_popcount(unsigned(byte));
-  int rank = side ? 8 - c : 0;                       // rank of the byte's first kept value
-  uint32_t idx = 0;
-  for (int g = 0; g < 2; ++g) {
-    const int nib = (byte >> (4 * g)) & 15;
-    int p[4] = {0, 0, 0, 0}, k = 0;
-    for (int b = 0; b < 4; ++b)
-      if ((nib >> b) & 1) p[k++] = b;
-    // pairs as (rank of the value at the lower position, at the higher), -1 = zero; the
-    // positions stay distinct and ascending
-    int a0 = -1, a1 = -1, b0 = -1, b1 = -1, ca = 0x4, cb = 0x4;
-    if (k >= 2) { a0 = rank; a1 = rank + 1; ca = p[0] | p[1] << 2; }
-    else if (k == 1) {
-      if (p[0] < 3) { a0 = rank; ca = p[0] | 3 << 2; } else { a1 = rank; ca = 2 | 3 << 2; }
-    }
-    if (k == 4) { b0 = rank + 2; b1 = rank + 3; cb = 2 | 3 << 2; }
-    else if (k == 3) {
-      if (p[2] < 3) { b0 = rank + 2; cb = p[2] | 3 << 2; } else { b1 = rank + 2; cb = 2 | 3 << 2; }
-    }
-    e.sel[4 * g + 0] = split_half_sel(a0, false) | split_half_sel(a1, false) << 16;
-    e.sel[4 * g + 1] = split_half_sel(a0, true) | split_half_sel(a1, true) << 16;
-    e.sel[4 * g + 2] = split_half_sel(b0, false) | split_half_sel(b1, false) << 16;
-    e.sel[4 * g + 3] = split_half_sel(b0, true) | split_half_sel(b1, true) << 16;
-    idx |= uint32_t(ca) << (4 * g) | uint32_t(cb) << (8 + 4 * g);
-    rank += k;
-  }
-  e.idx = idx;
-  return e;
-}
-
-// The tables as laid out in LDS (17 KiB): entry e's selectors at 32 e, its codes at
-// kSplitSelBytes + 2 e. Built at compile time; each workgroup copies them to LDS once.
-struct SplitTable {
-  uint4 sel[2 * kSplitEntries];
-  uint16_t idx[kSplitEntries];
-};
-static_assert(sizeof(SplitTable) == kSplitLutBytes, "split table layout");
-
-__host__ __device__ constexpr SplitTable make_split_table() {
-  SplitTable t{};
-  for (int e = 0; e < kSplitEntries; ++e) {
-    const SplitEntry x = split_entry(e >> 8, e & 255);
-    t.sel[2 * e] = uint4{x.sel[0], x.sel[1], x.sel[2], x.sel[3]};
-    t.sel[2 * e + 1] = uint4{x.sel[4], x.sel[5], x.sel[6], x.sel[7]};
-    t.idx[e] = uint16_t(x.idx);
-  }
-  return t;
-}
-
-__device__ const SplitTable kSplitTable = make_split_table();
 
 template <int TR, bool SPLIT>
 __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16_t* __restrict__ values,

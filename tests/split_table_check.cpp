@@ -1,4 +1,4 @@
-// Host check of the split tables of the small-batch 4:8 / 8:16 kernel (nm_skinny_impl.h).
+// Host check of the split tables of the 4:8 / 8:16 products (nm_prefill_impl.h).
 // For every 16-bit mask chunk that a 4:8 or 8:16 row can hold (every choice of 4 of each 8
 // columns, every choice of 8 of 16 columns) and 8 distinct nonzero values, the two 2:4
 // operands built from the table entries, decoded as the sparse matrix instruction reads
@@ -12,9 +12,9 @@
 #include <cstdint>
 #include <cstdio>
 
-#include "nm_skinny_impl.h"
+#include "nm_prefill_impl.h"
 
-using nm::skinny_detail::SplitTable;
+using nm::prefill_detail::SplitTable;
 
 static uint32_t perm(uint32_t a, uint32_t b, uint32_t sel, bool* ok) {
   const uint64_t d = (uint64_t(a) << 32) | b;
@@ -67,7 +67,7 @@ static int check(const SplitTable& t, uint32_t m16) {
 }
 
 int main() {
-  static const SplitTable t = nm::skinny_detail::make_split_table();
+  static const SplitTable t = nm::prefill_detail::make_split_table();
   int fails = 0, n48 = 0, n816 = 0;
   for (uint32_t m16 = 0; m16 < 65536; ++m16) {
     const bool p48 = __builtin_popcount(m16 & 0xFF) == 4 && __builtin_popcount(m16 >> 8) == 4;

@@ -154,7 +154,7 @@ def test_prefill_argument_errors():
     m = torch.zeros((4, 4), dtype=torch.int32, device=device())
     X = torch.zeros((3, 128), dtype=torch.float16, device=device())
     with pytest.raises(nm.NMArgumentError) as e:
-        nm.nm_spmm_prefill(v, m, X, 4, 8)
+        nm.nm_spmm_prefill(v, m, X, 16, 32)
     assert e.value.status == nm.NM_ERR_PATTERN
     with pytest.raises(ValueError):
         nm.nm_spmm_prefill(v, m, torch.zeros((3, 96), dtype=torch.float16, device=device()))
@@ -173,3 +173,79 @@ def test_prefill_full_size_llama8b(name, R, C):
     W = synth.weight(R, C, synth.weight_seed(6, [l[0] for l in synth.LLAMA31_8B].index(name), (2, 4)))
     X = synth.activations(T, C, synth.x_seed(6, 0, (2, 4)))
     check_prefill(W, X, name, sample_rows(R, k=24, rpb=128))
+
+
+# 4:8 and 8:16 (split into two 2:4 operands): ragged rows and tokens, a 32-column tail step,
+# tiles of all three configurations
+SPLIT_SMALL = [(17, 64, 5), (33, 128, 17), (65, 4096, 64), (300, 1056, 255), (129, 2080, 257), (4100, 1024, 2050),
+               (16400, 160, 1100), (2600, 2208, 3000)]
+SPLIT_NAMES = {"prefill_split_kernel<1, 4, 64, 2>", "prefill_split_kernel<4, 8, 64, 2>",
+               "prefill_split_kernel<4, 16, 64, 2>"}
+
+
+def check_split(W, X, N, M, tag, rows_idx=None):
+    R, C = W.shape
+    values, masks = nm.nm_pack(up_f16(W), N, M)
+    Y = down_f16(nm.nm_spmm_prefill(values, masks, up_f16(X), N, M))
+    idx = np.arange(R) if rows_idx is None else rows_idx
+    rv, rm = oracle.pack_ref(W[idx], N, M)
+    rep = oracle.y_tolerance_report(Y[:, idx], oracle.spmm_ref(rv, rm, X, C, N, M))
+    assert rep["ok"], (tag, N, M, rep)
+    return rep
+
+
+@pytest.mark.parametrize("N,M", [(4, 8), (8, 16)])
+def test_prefill_split_small_and_ragged(N, M):
+    names = set()
+    for i, (R, C, T) in enumerate(SPLIT_SMALL):
+        names.add(nm.prefill_variant(R, C, T, True, split=True))
+        say(f"prefill split {N}:{M} {R}x{C} tokens={T} {nm.prefill_variant(R, C, T, True, split=True)}")
+        W = synth.weight(R, C, seed=2600 + 10 * i + N)
+        X = synth.activations(T, C, seed=2650 + i)
+        check_split(W, X, N, M, (R, C, T), None if R * T <= 300 * 300 else sample_rows(R, rpb=128))
+    assert names == SPLIT_NAMES, names
+
+
+@pytest.mark.parametrize("N,M", [(4, 8), (8, 16)])
+def test_prefill_split_one_hot_and_routing(N, M):
+    """One-hot tokens give the pruned matrix's columns bit-exactly; nm_spmm from 32 vectors
+    on runs the same kernel (same bits), and the result is deterministic."""
+    R, C = 200, 256
+    W = synth.weight(R, C, seed=2700 + N)
+    rv, rm = oracle.pack_ref(W, N, M)
+    D = oracle.unpack_ref(rv, rm, C, N, M)
+    X = np.eye(C, dtype=np.float16)
+    v, m = up_f16(rv), up_u32(rm)
+    Y = down_bits16(nm.nm_spmm_prefill(v, m, up_f16(X), N, M))
+    want = D.T.copy()
+    want[want == 0x8000] = 0
+    assert np.array_equal(Y, want)
+    Xr = up_f16(synth.activations(40, C, seed=2701))
+    assert nm.spmm_variant(R, C, 40, N, M).startswith("prefill_split_kernel")
+    Y0 = down_bits16(nm.nm_spmm_prefill(v, m, Xr, N, M))
+    assert np.array_equal(down_bits16(nm.nm_spmm(v, m, Xr, N, M)), Y0)
+    for _ in range(5):
+        assert np.array_equal(down_bits16(nm.nm_spmm_prefill(v, m, Xr, N, M)), Y0)
+
+
+@pytest.mark.parametrize("N,M", [(4, 8), (8, 16)])
+def test_prefill_split_malformed_masks_stay_in_bounds(N, M):
+    R, C, T = 130, 1056, 70
+    v = up_f16(synth.weight(R, C // 2, seed=2800))
+    X = up_f16(synth.activations(T, C, seed=2801))
+    for word in (0, 1, 0x80000000, 0xFFFFFFFF, 0x12345678):
+        m = torch.full((R, C // 32), np.uint32(word).view(np.int32).item(), dtype=torch.int32, device=device())
+        Y = nm.nm_spmm_prefill(v, m, X, N, M)
+        torch.cuda.synchronize()
+        assert Y.shape == (T, R)
+
+
+@pytest.mark.parametrize("N,M", [(4, 8), (8, 16)])
+def test_prefill_split_full_size_down_proj(N, M):
+    """The Llama-3.1-8B down projection (4096 x 14336) with a 2048-token prompt, in the
+    configuration nm_spmm_prefill picks: Y within tolerance on sampled rows (all tokens)."""
+    R, C, T = 4096, 14336, 2048
+    say(f"prefill split full-size {N}:{M} {R}x{C} tokens={T} {nm.prefill_variant(R, C, T, True, split=True)}")
+    W = synth.weight(R, C, synth.weight_seed(6, 3, (N, M)))
+    X = synth.activations(T, C, synth.x_seed(6, 0, (N, M)))
+    check_split(W, X, N, M, "down", sample_rows(R, k=24, rpb=128))

@@ -50,10 +50,9 @@ def test_skinny_parity(R, C, T, N, M):
 
 
 @pytest.mark.parametrize("N,M", [(4, 8), (8, 16)])
-def test_skinny_split_large_batches(N, M):
-    """4:8 and 8:16 stay on the split kernel beyond 31 vectors (16 per launch; a ragged last
-    launch of 4)."""
-    R, C, T = 2064, 1024, 36
+def test_skinny_split_two_launches(N, M):
+    """4:8 and 8:16 at 20 vectors: two launches of the split kernel (16, then a ragged 4)."""
+    R, C, T = 2064, 1024, 20
     assert nm.spmm_variant(R, C, T, N, M) == SKINNY[N]
     say(f"skinny {N}:{M} {R}x{C} vectors={T}")
     check(R, C, T, 3050 + N, N, M, sample_rows(R, k=32, rpb=16))
@@ -61,9 +60,8 @@ def test_skinny_split_large_batches(N, M):
 
 def test_skinny_routing():
     """Which kernel nm_spmm picks: the sparse matrix instruction on layers of >= 2048 rows for
-    2:4 at 5..31 vectors and for 4:8 and 8:16 from 5 vectors on; the small-batch kernel
-    below 5 vectors, on smaller layers and for 16:32; the prefill kernel for 2:4 from 32
-    vectors on."""
+    2:4, 4:8 and 8:16 at 5..31 vectors; the small-batch kernel below 5 vectors, on smaller
+    layers and for 16:32; the prefill kernels from 32 vectors on."""
     assert nm.spmm_variant(4096, 4096, 4, 2, 4) == "spmm_kernel<2, 4, 2>"
     assert nm.spmm_variant(2047, 4096, 8, 2, 4) == "spmm_kernel<2, 8, 2>"
     assert nm.spmm_variant(2047, 4096, 8, 4, 8) == "spmm_kernel<4, 8, 2>"
@@ -72,8 +70,9 @@ def test_skinny_routing():
     for N, M in PATTERNS:
         assert nm.spmm_variant(4096, 4096, 5, N, M) == SKINNY[N]
         assert nm.spmm_variant(4096, 4096, 31, N, M) == SKINNY[N]
-    assert nm.spmm_variant(4096, 4096, 32, 4, 8) == SKINNY[4]
-    assert nm.spmm_variant(4096, 4096, 2048, 8, 16) == SKINNY[8]
+    assert nm.spmm_variant(4096, 4096, 32, 4, 8).startswith("prefill_split_kernel")
+    assert nm.spmm_variant(4096, 4096, 2048, 8, 16) == "prefill_split_kernel<4, 8, 64, 2>"
+    assert nm.spmm_variant(4096, 4096, 40, 16, 32) == "spmm_kernel<16, 8, 0>"
     assert nm.spmm_variant(4096, 4096, 32, 2, 4).startswith("prefill_spmm_kernel")
     assert nm.spmm_variant(4096, 4096, 1, 2, 4).startswith("spmv_kernel")
 

@@ -1,4 +1,4 @@
-"""Host check of the split tables that let the small-batch kernel run 4:8 and 8:16 on the 2:4
+"""Host check of the split tables that let the 4:8 and 8:16 products run on the 2:4
 sparse matrix instruction: builds tests/split_table_check.cpp (host code only) with hipcc
 and runs it. Every 16-bit mask chunk a 4:8 or 8:16 row can hold is checked."""
 import os
