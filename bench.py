@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 METRIC = "N:M SpMV effective HBM GB/s (% of peak) + speedup vs dense GEMV, batch 1"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak, 8 TB/s
+CPU_LEG_SECONDS = 10.0  # oracle work the CPU baseline leg repeats its sample for
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "nm_spmv_counters.txt")
 WORKLOAD_BY_NAME = {"llama8b": 2, "qwen3": 3, "llama70b": 4, "decode": 5, "prefill": 6}
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix-core peak (no sparsity credit)
@@ -436,7 +437,8 @@ def decode_main(args, torch, nm, synth, dev):
     token, i.e. one in-order pass over the 224 products. Also timed: the dense GEMV over
     the same 224 weights, and the same sweep with q/k/v and gate/up each fused into one
     product over their concatenated rows (the rows of a packed matrix concatenate as they
-    are; the fused product uses the x of q, resp. gate)."""
+    are; the fused product uses the x of q, resp. gate), timed against the dense GEMV fused
+    the same way."""
     wl = synth.WORKLOADS[5]
     NB, (N, M) = wl["n_layers"], tuple(wl["patterns"][0])
     lib = nm.lib()
@@ -458,8 +460,8 @@ def decode_main(args, torch, nm, synth, dev):
                 cpu_layers.append(dict(name=name, R=R, C=C, N=N, M=M, x_host=x, y=y,
                                        W_cpu=W[:max(1, int(math.ceil(R * args.cpu_rows_frac)))].copy()))
             del W
-    # fused q/k/v and gate/up of every block
-    fused = []
+    # fused q/k/v and gate/up of every block, sparse and dense alike
+    fused, fused_dn = [], []
     for b in range(NB):
         blk = sp[7 * b:7 * b + 7]
         for idx, xsrc in (((0, 1, 2), 0), ((3,), 3), ((4, 5), 4), ((6,), 6)):
@@ -471,6 +473,11 @@ def decode_main(args, torch, nm, synth, dev):
             fused.append(dict(R=R, C=C, values=v, masks=m, x=blk[xsrc]["x"],
                               y=torch.empty(R, dtype=torch.float16, device=dev),
                               bytes=alg_bytes_sparse(R, C, N, M)))
+            dparts = [dn[7 * b + i] for i in idx]
+            Wf = torch.cat([q["W"] for q in dparts]) if len(dparts) > 1 else dparts[0]["W"]
+            fused_dn.append(dict(R=R, C=C, W=Wf, x=blk[xsrc]["x"],
+                                 y=torch.empty(R, dtype=torch.float16, device=dev),
+                                 bytes=alg_bytes_dense(R, C)))
     torch.cuda.synchronize()
     log(f"decode sweep: generated and packed {len(sp)} projections in {time.time() - t_gen:.1f}s")
 
@@ -478,7 +485,9 @@ def decode_main(args, torch, nm, synth, dev):
         return [(q["values"].data_ptr(), q["masks"].data_ptr(), q["x"].data_ptr(), q["y"].data_ptr(),
                  q["R"], q["C"], N, M) for q in items]
     sp_a, fu_a = sp_launches(sp), sp_launches(fused)
-    dn_a = [(q["W"].data_ptr(), q["x"].data_ptr(), q["y"].data_ptr(), q["R"], q["C"]) for q in dn]
+    def dn_launches(items):
+        return [(q["W"].data_ptr(), q["x"].data_ptr(), q["y"].data_ptr(), q["R"], q["C"]) for q in items]
+    dn_a, fdn_a = dn_launches(dn), dn_launches(fused_dn)
 
     def token_sparse(A):
         def run(sp_):
@@ -488,11 +497,13 @@ def decode_main(args, torch, nm, synth, dev):
                     raise RuntimeError(f"nm_spmv: {nm.status_string(st)}")
         return run
 
-    def token_dense(sp_):
-        for a in dn_a:
-            st = lib.nm_gemv_dense(*a, sp_)
-            if st:
-                raise RuntimeError(f"nm_gemv_dense: {nm.status_string(st)}")
+    def token_dense(A):
+        def run(sp_):
+            for a in A:
+                st = lib.nm_gemv_dense(*a, sp_)
+                if st:
+                    raise RuntimeError(f"nm_gemv_dense: {nm.status_string(st)}")
+        return run
 
     def timed_tokens(fn, K, W_):
         s_ = torch.cuda.current_stream(dev).cuda_stream
@@ -519,13 +530,15 @@ def decode_main(args, torch, nm, synth, dev):
 
     K, Wm = args.tokens, max(1, min(args.warmup, 5))
     ms_sp = timed_tokens(token_sparse(sp_a), K, Wm)
-    ms_dn = timed_tokens(token_dense, K, Wm)
+    ms_dn = timed_tokens(token_dense(dn_a), K, Wm)
     ms_fu = timed_tokens(token_sparse(fu_a), K, Wm)
+    ms_fu_dn = timed_tokens(token_dense(fdn_a), K, Wm)
     bytes_tok = sum(q["bytes"] for q in sp)
     bytes_dn = sum(q["bytes"] for q in dn)
     value = bytes_tok / (ms_sp * 1e-3) / 1e9
     log(f"decode: sparse {ms_sp * 1e3:.1f} us/token ({value:.0f} GB/s), dense {ms_dn * 1e3:.1f} us/token, "
-        f"fused sparse {ms_fu * 1e3:.1f} us/token, speedup {ms_dn / ms_sp:.3f}x")
+        f"speedup {ms_dn / ms_sp:.3f}x; fused q/k/v and gate/up: sparse {ms_fu * 1e3:.1f} us/token, "
+        f"dense {ms_fu_dn * 1e3:.1f} us/token, speedup {ms_fu_dn / ms_fu:.3f}x")
     cpu = None if args.no_cpu_baseline else cpu_baseline(cpu_layers, args.cpu_rows_frac)
     out = {
         "metric": METRIC,
@@ -551,7 +564,9 @@ def decode_main(args, torch, nm, synth, dev):
         "speedup_vs_dense": round(ms_dn / ms_sp, 3),
         "fused_qkv_gateup": {"us_per_token": round(ms_fu * 1e3, 2), "launches_per_token": len(fused) // NB * NB,
                              "GBps": round(sum(q["bytes"] for q in fused) / (ms_fu * 1e-3) / 1e9, 1),
-                             "speedup_vs_dense": round(ms_dn / ms_fu, 3)},
+                             "dense_us_per_token": round(ms_fu_dn * 1e3, 2),
+                             "dense_GBps": round(sum(q["bytes"] for q in fused_dn) / (ms_fu_dn * 1e-3) / 1e9, 1),
+                             "speedup_vs_fused_dense": round(ms_fu_dn / ms_fu, 3)},
         "byte_floor_us_per_token_at_8TBps": round(bytes_tok / 8e12 * 1e6, 1),
         "timing": "K tokens in one HIP graph replayed between events, median of 3 replays",
         "cpu_baseline": cpu,
@@ -801,7 +816,9 @@ def cpu_baseline(layers, frac):
 
     passes = []
     with ThreadPoolExecutor(cores) as ex:
-        for _ in range(3):       # three timed passes over the sample; the median is reported
+        # timed passes over the sample until about CPU_LEG_SECONDS of oracle work (at least 3,
+        # at most 50); the median pass is reported
+        while len(passes) < 3 or (sum(passes) < CPU_LEG_SECONDS and len(passes) < 50):
             t0 = time.perf_counter()
             ys = list(ex.map(run, range(len(chunks))))
             passes.append(time.perf_counter() - t0)
@@ -829,7 +846,8 @@ def cpu_baseline(layers, frac):
         f"{cores} threads, {b1 / t1 / 1e9:.4f} GB/s on 1 thread (leg {time.time() - t_start:.1f}s)")
     return {"value": round(b_total / t_total / 1e9, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{_rows_phrase(frac)} of each of the {len(layers)} layers ({rows_total} rows) in "
-                      f"{len(chunks)} chunks over {cores} threads; densify + fp64 matvec (numpy); median of 3 passes",
+                      f"{len(chunks)} chunks over {cores} threads; densify + fp64 matvec (numpy); median of "
+                      f"{len(passes)} passes ({sum(passes):.1f} s of oracle work)",
             "seconds": round(t_total, 2), "cpu_model": cpu_info(),
             "single_thread": {"value": round(b1 / t1 / 1e9, 5), "unit": "GB/s", "seconds": round(t1, 2),
                               "sample": "every 16th chunk, one thread"},
