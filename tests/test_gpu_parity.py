@@ -69,9 +69,11 @@ def test_gemv_small():
 # one or more shapes in each regime of the workgroup-shape rule: narrow layers (at most
 # 8 rows per CU), regular rows, long rows (more than 64 steps of 128 columns) in one and
 # in two rounds; ragged row counts (the last workgroup holds fewer rows than its row
-# groups cover) and ragged column counts (a last step of 1..3 mask words)
+# groups cover) and ragged column counts (a last step of 1..3 mask words). The long-row
+# kernel keeps two batches of 4 steps in flight; its waves see 1, 2, 3 and 4+ full batches
+# and 0..3 remaining steps across these shapes (199 x 20000: 12 waves of 13 steps).
 REGIMES = [(255, 4096), (2048, 1024), (1500, 2080), (2049, 512), (5121, 4096), (300, 8320),
-           (777, 16416), (10241, 8320)]
+           (777, 16416), (10241, 8320), (199, 20000)]
 
 
 @pytest.mark.parametrize("N,M", PATTERNS)
