@@ -73,7 +73,7 @@ def test_gemv_small():
 # kernel keeps two batches of 4 steps in flight; its waves see 1, 2, 3 and 4+ full batches
 # and 0..3 remaining steps across these shapes (199 x 20000: 12 waves of 13 steps).
 REGIMES = [(255, 4096), (2048, 1024), (1500, 2080), (2049, 512), (5121, 4096), (300, 8320),
-           (777, 16416), (10241, 8320), (199, 20000)]
+           (777, 16416), (10241, 8320), (199, 20000), (1023, 4096), (510, 2048), (1024, 2080)]
 
 
 @pytest.mark.parametrize("N,M", PATTERNS)
