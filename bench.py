@@ -569,9 +569,27 @@ def decode_main(args, torch, nm, synth, dev):
                              "speedup_vs_fused_dense": round(ms_fu_dn / ms_fu, 3)},
         "byte_floor_us_per_token_at_8TBps": round(bytes_tok / 8e12 * 1e6, 1),
         "timing": "K tokens in one HIP graph replayed between events, median of 3 replays",
+        "roofline": decode_roofline(nm, sp, ms_sp, N, M),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def decode_roofline(nm, items, ms_token, N, M):
+    """Roofline of the decode sweep: every product of the token runs one kernel variant (2:4:
+    the pair table), so its average launch is the token time over the launches, and its achieved
+    rate is the token's algorithmic bytes over the token time (gaps between launches
+    included, as in the per-layer figures of the projection workloads)."""
+    names = {nm.spmv_variant(q["R"], q["C"], N, M) for q in items}
+    if len(names) != 1:
+        return None
+    n = len(items)
+    b = sum(q["bytes"] for q in items) / n
+    us = ms_token * 1e3 / n
+    achieved = b / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": names.pop(),
+            "launches_per_step": n, "bytes_per_launch": round(b), "avg_launch_us": round(us, 3)}
 
 
 def prefill_main(args, torch, nm, synth, dev):
