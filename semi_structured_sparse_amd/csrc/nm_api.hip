@@ -268,7 +268,7 @@ int nm_spmv_launch_shape(int64_t rows, int64_t cols, int N, int M, int64_t* shap
   hipError_t e = nm::current_device_info(&dev);
   if (e != hipSuccess) return nm::hip_fail(e);
   if (cols > nm::max_cols_for(dev)) return NM_ERR_TOO_WIDE;
-  const nm::WorkgroupShape s = M == 4 * N ? nm::spmv_quarter_shape(rows, cols, dev) : nm::spmv_shape(rows, cols, dev);
+  const nm::WorkgroupShape s = M == 4 * N ? nm::spmv_quarter_shape(rows, cols, dev) : nm::spmv_shape(rows, cols, N, dev);
   shape[0] = s.rpb;
   shape[1] = s.row_groups;
   shape[2] = s.cs;

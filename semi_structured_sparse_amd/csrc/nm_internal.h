@@ -47,6 +47,7 @@ struct WorkgroupShape {
   int row_groups = 1;
   int cs = 8;
   int64_t grid = 0;
+  int ci = 1;  // column ranges per wave (the narrow-layer kernel when > 1)
 };
 
 // Small-batch products (1 <= batch <= kSmallBatch): X [batch][cols], Y [batch][rows].
@@ -68,7 +69,7 @@ const char* spmm_variant(int N, int64_t batch);
 
 // Name of the kernel configuration launch_spmv picks (static string) and its shape.
 const char* spmv_variant(int64_t rows, int64_t cols, int N, int M, const DeviceInfo& dev);
-WorkgroupShape spmv_shape(int64_t rows, int64_t cols, const DeviceInfo& dev);
+WorkgroupShape spmv_shape(int64_t rows, int64_t cols, int N, const DeviceInfo& dev);
 WorkgroupShape spmv_quarter_shape(int64_t rows, int64_t cols, const DeviceInfo& dev);
 WorkgroupShape dense_shape(int64_t rows, int64_t cols, const DeviceInfo& dev);
 

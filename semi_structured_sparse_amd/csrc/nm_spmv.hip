@@ -62,6 +62,24 @@ WorkgroupShape workgroup_shape(int64_t rows, int64_t steps, const DeviceInfo& de
   return s;
 }
 
+// The kernel for a shape's column ranges per wave: the narrow kernel serves the 16:32
+// reversed walk only (the bit walk, which narrow layers never need on this GPU, and the
+// other patterns take spmv_kernel, which suits any wave count).
+template <int N, int DEC>
+const void* kernel_for(int ci) {
+  if constexpr (DEC != kRevWalk) {
+    (void)ci;
+    return reinterpret_cast<const void*>(&spmv_kernel<N, kBatch, kNTV, DEC>);
+  } else {
+    switch (ci) {
+      case 2: return reinterpret_cast<const void*>(&spmv_narrow_kernel<N, kBatch, kNTV, DEC, 2>);
+      case 4: return reinterpret_cast<const void*>(&spmv_narrow_kernel<N, kBatch, kNTV, DEC, 4>);
+      case 8: return reinterpret_cast<const void*>(&spmv_narrow_kernel<N, kBatch, kNTV, DEC, 8>);
+      default: return reinterpret_cast<const void*>(&spmv_kernel<N, kBatch, kNTV, DEC>);
+    }
+  }
+}
+
 template <int N, int DEC>
 hipError_t launch_kernel(const uint16_t* values, const uint32_t* masks, const uint16_t* x, uint16_t* y,
                          int rows, int cols, const WorkgroupShape& s, hipStream_t stream, const DeviceInfo& dev) {
@@ -69,8 +87,8 @@ hipError_t launch_kernel(const uint16_t* values, const uint32_t* masks, const ui
   const uint4* x4 = reinterpret_cast<const uint4*>(x);
   int rpb = s.rpb, cs = s.cs;
   void* args[] = {&v4, &masks, &x4, &y, &rows, &cols, &rpb, &cs};
-  return launch(reinterpret_cast<const void*>(&spmv_kernel<N, kBatch, kNTV, DEC>), dim3(unsigned(s.grid)),
-                dim3(unsigned(64 * s.row_groups * s.cs)), args, lds_bytes<DEC>(cols), stream, dev);
+  return launch(kernel_for<N, DEC>(s.ci), dim3(unsigned(s.grid)), dim3(unsigned(64 * s.row_groups * s.cs)), args,
+                lds_bytes<DEC>(cols), stream, dev);
 }
 
 }  // namespace
@@ -82,8 +100,26 @@ int64_t max_cols_for(const DeviceInfo& dev) {
   return (avail / 2) / 32 * 32;
 }
 
-WorkgroupShape spmv_shape(int64_t rows, int64_t cols, const DeviceInfo& dev) {
-  return workgroup_shape(rows, ceil_div(cols, 128), dev);  // 128 columns = 128 bytes of values
+// 50% patterns: 128 columns = 128 bytes of values per step. Narrow 16:32 layers (at most 8
+// rows per CU, at most 64 steps per row) whose workgroups hold 1, 2 or 4 rows take the narrow
+// kernel when every lane can get exactly one batch: CI = 8 / rows column ranges per wave of
+// 4 whole steps each, steps / (4 CI) waves. Measured on MI355X on the 1024-row Llama and Qwen
+// layers: 4-8% faster for 16:32, whose decoder does the most vector work per value; within
+// +-3% (run-to-run spread) for the table decoders of 2:4, 4:8 and 8:16, which keep the
+// kernel whose spare lanes repeat the last row.
+WorkgroupShape spmv_shape(int64_t rows, int64_t cols, int N, const DeviceInfo& dev) {
+  const int64_t steps = ceil_div(cols, 128);
+  WorkgroupShape s = workgroup_shape(rows, steps, dev);
+  const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
+  const bool narrow = steps <= 64 && rows <= 8 * cus;  // the rule's narrow-layer class
+  if (N == 16 && narrow && s.rpb < 8 && 8 % s.rpb == 0 && cols % 128 == 0) {
+    const int ci = 8 / s.rpb;
+    if (steps % (int64_t(kBatch) * ci) == 0) {
+      s.ci = ci;
+      s.cs = int(steps / (int64_t(kBatch) * ci));
+    }
+  }
+  return s;
 }
 
 // 25% density: 256 columns = 128 bytes of values per step.
@@ -92,8 +128,17 @@ WorkgroupShape spmv_quarter_shape(int64_t rows, int64_t cols, const DeviceInfo& 
 }
 
 const char* spmv_variant(int64_t rows, int64_t cols, int N, int M, const DeviceInfo& dev) {
-  (void)rows;
   if (M == 4 * N) return "spmv_quarter_kernel<4, true>";
+  const int pi = N == 2 ? 0 : N == 4 ? 1 : N == 8 ? 2 : 3;
+  const int dec = pick_decoder(N, cols, dev);
+  const int ci = spmv_shape(rows, cols, N, dev).ci;
+  if (ci > 1 && dec == kRevWalk) {
+    // spmv_narrow_kernel<16, BATCH, NTV, kRevWalk, CI>
+    static const char* const narrow[3] = {"spmv_narrow_kernel<16, 4, true, 3, 2>",
+                                          "spmv_narrow_kernel<16, 4, true, 3, 4>",
+                                          "spmv_narrow_kernel<16, 4, true, 3, 8>"};
+    return narrow[ci == 2 ? 0 : ci == 4 ? 1 : 2];
+  }
   // one string per (pattern, decoder): the template arguments of
   // spmv_kernel<N, BATCH, NTV, DEC> as profilers print them
   static const char* const names[4][4] = {
@@ -103,8 +148,7 @@ const char* spmv_variant(int64_t rows, int64_t cols, int N, int M, const DeviceI
       {"spmv_kernel<16, 4, true, 0>", "", "", "spmv_kernel<16, 4, true, 3>"},
   };
   static_assert(kBatch == 4 && kNTV, "variant names spell BATCH = 4 and NTV = true");
-  const int pi = N == 2 ? 0 : N == 4 ? 1 : N == 8 ? 2 : 3;
-  return names[pi][pick_decoder(N, cols, dev)];
+  return names[pi][dec];
 }
 
 hipError_t launch_spmv(const uint16_t* values, const uint32_t* masks, const uint16_t* x,
@@ -120,7 +164,7 @@ hipError_t launch_spmv(const uint16_t* values, const uint32_t* masks, const uint
     return launch(reinterpret_cast<const void*>(&spmv_quarter_kernel<kBatch, kNTV>), dim3(unsigned(q.grid)),
                   dim3(unsigned(64 * q.row_groups * q.cs)), args, lds_bytes<kBitWalk>(c), stream, dev);
   }
-  const WorkgroupShape s = spmv_shape(rows, cols, dev);
+  const WorkgroupShape s = spmv_shape(rows, cols, N, dev);
   const int dec = pick_decoder(N, cols, dev);
   switch (N) {
     case 2:

@@ -402,7 +402,14 @@ constexpr size_t lds_bytes(int cols) {
 // first batch of its values, and only then writes x to LDS, so that the wait for x does
 // not include the wait for the value batch (loads complete in order) and the staging
 // overlaps the value stream.
-template <int N, int BATCH, bool NTV, int DEC>
+//
+// CI > 1 (narrow layers of RPW = 8 / CI rows per workgroup, cols a multiple of 128): a wave
+// covers RPW rows and the lanes of row slot s take row s % RPW and the (s / RPW)-th of CI
+// equal, contiguous column ranges inside the wave's range, so that no lane repeats another
+// lane's row; the launcher picks CS = steps / (BATCH * CI), so that every lane has exactly
+// one batch of whole steps, which the prologue loads. The CI partial sums of a row are added
+// across lanes before the LDS reduction.
+template <int N, int BATCH, bool NTV, int DEC, int CI>
 __device__ __forceinline__ void spmv_body(
     const uint4* __restrict__ values, const uint32_t* __restrict__ masks, const uint4* __restrict__ x,
     uint16_t* __restrict__ y, int rows, int cols, int rpb, int cs_count) {
@@ -421,20 +428,26 @@ __device__ __forceinline__ void spmv_body(
   const int CS = __builtin_amdgcn_readfirstlane(cs_count);
   const int rg = __builtin_amdgcn_readfirstlane(int(unsigned(wave) / unsigned(CS)));
   const int cs = wave - rg * CS;
-  const int rsub = (lane & 31) >> 2;               // row within the wave's 8 rows
+  static_assert(CI == 1 || CI == 2 || CI == 4 || CI == 8, "column parts per wave: 1, 2, 4 or 8");
+  constexpr int RPW = 8 / CI;                      // rows per wave
+  const int rsub = (lane & 31) >> 2;               // row slot within the wave's 8
+  const int rrow = rsub % RPW;                     // its row within the wave's RPW rows
+  const int cpart = rsub / RPW;                    // its column range of the wave's CI
   const int u = ((lane >> 5) << 2) | (lane & 3);   // half-word u of the step's 8
   const int half = u & 1;
   const int wsel = u >> 1;                         // which of the step's 4 words
   const int row0 = blockIdx.x * rpb;
   const int row_end = min(row0 + rpb, rows);
-  const unsigned r = unsigned(min(row0 + 8 * rg + rsub, row_end - 1));
+  const unsigned r = unsigned(min(row0 + 8 * rg + rrow, row_end - 1));
 
   const int words = cols >> 5;
   const int steps = (words + 3) >> 2;
   const int full_steps = words >> 2;
   // steps * (cs + 1) < 2^23 * 16: 32-bit arithmetic is exact (cols <= 2^30)
-  const int s_beg = int(unsigned(steps) * unsigned(cs) / unsigned(CS));
-  const int s_end = int(unsigned(steps) * unsigned(cs + 1) / unsigned(CS));
+  // CI > 1: every lane has `len` == BATCH whole steps (steps == full_steps)
+  const int len = steps / (CS * CI);
+  const int s_beg = CI == 1 ? int(unsigned(steps) * unsigned(cs) / unsigned(CS)) : len * (cs * CI + cpart);
+  const int s_end = CI == 1 ? int(unsigned(steps) * unsigned(cs + 1) / unsigned(CS)) : s_beg + len;
   const int s_main = min(s_end, full_steps);
 
   const uint4* __restrict__ vrow = values + size_t(r) * unsigned(cols >> 4);
@@ -443,7 +456,7 @@ __device__ __forceinline__ void spmv_body(
 
   const uint4* __restrict__ vp = vrow + 8 * unsigned(s_beg) + unsigned(u);
   const uint32_t* __restrict__ mp = mrow + 4 * unsigned(s_beg) + unsigned(wsel);
-  const int n = s_main - s_beg;
+  const int n = CI == 1 ? s_main - s_beg : len;    // wave-uniform
   const int nfull = n / BATCH;
   const int rem = n - nfull * BATCH;
 
@@ -482,18 +495,23 @@ __device__ __forceinline__ void spmv_body(
     else if constexpr (DEC == kByteLut) S.template compute_lut<N>(xw_ + xhalf, lut, sh16, count, part);
     else S.template compute_bits<N, DEC == kRevWalk>(xw_ + xrev, half, keep_high, count, part);
   };
-  for (int b = 0; b < nfull; ++b) {
-    if (b > 0) A.load(vp, mp, BATCH);
+  if constexpr (CI > 1) {
+    // every lane has exactly one batch (the launcher sets len == BATCH): the prologue's
     compute(A, xw, tb, BATCH);
-    vp += 8 * BATCH;
-    mp += 4 * BATCH;
-    xw += 256u * BATCH;
-    tb += 768 * BATCH;
-  }
-  if (rem > 0) {
-    B R;
-    R.load(vp, mp, rem);
-    compute(R, xw, tb, rem);
+  } else {
+    for (int b = 0; b < nfull; ++b) {
+      if (b > 0) A.load(vp, mp, BATCH);
+      compute(A, xw, tb, BATCH);
+      vp += 8 * BATCH;
+      mp += 4 * BATCH;
+      xw += 256u * BATCH;
+      tb += 768 * BATCH;
+    }
+    if (rem > 0) {
+      B R;
+      R.load(vp, mp, rem);
+      compute(R, xw, tb, rem);
+    }
   }
   // Last step with 1..3 words (cols not a multiple of 128): lanes whose word exists.
   if (s_end > full_steps && wsel < (words & 3)) {
@@ -510,7 +528,10 @@ __device__ __forceinline__ void spmv_body(
   float acc = (part[0] + part[1]) + (part[2] + part[3]);
 
   acc = row8_sum(acc);
-  if (u == 0) red[wave * 8 + rsub] = acc;
+  // CI > 1: add the row's CI column ranges (row slots rrow + k * RPW, lanes 4 * RPW apart)
+#pragma unroll
+  for (int d = 4 * RPW; d < 32; d <<= 1) acc += __shfl_xor(acc, d);
+  if (u == 0 && cpart == 0) red[wave * 8 + rsub] = acc;
   __syncthreads();
   if (tid < row_end - row0) {
     const int trg = tid >> 3, trow = tid & 7;
@@ -529,7 +550,16 @@ template <int N, int BATCH, bool NTV, int DEC>
 __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(8))) void spmv_kernel(
     const uint4* __restrict__ values, const uint32_t* __restrict__ masks, const uint4* __restrict__ x,
     uint16_t* __restrict__ y, int rows, int cols, int rpb, int cs_count) {
-  spmv_body<N, BATCH, NTV, DEC>(values, masks, x, y, rows, cols, rpb, cs_count);
+  spmv_body<N, BATCH, NTV, DEC, 1>(values, masks, x, y, rows, cols, rpb, cs_count);
+}
+
+// Narrow layers (at most 8 rows per CU, at most 64 steps per row): rows per workgroup
+// 8 / CI with CI column ranges per wave, the same register budget.
+template <int N, int BATCH, bool NTV, int DEC, int CI>
+__global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(8))) void spmv_narrow_kernel(
+    const uint4* __restrict__ values, const uint32_t* __restrict__ masks, const uint4* __restrict__ x,
+    uint16_t* __restrict__ y, int rows, int cols, int rpb, int cs_count) {
+  spmv_body<N, BATCH, NTV, DEC, CI>(values, masks, x, y, rows, cols, rpb, cs_count);
 }
 
 // ---------------------------------------------------------------- 25% density

@@ -73,7 +73,8 @@ def test_gemv_small():
 # kernel keeps two batches of 4 steps in flight; its waves see 1, 2, 3 and 4+ full batches
 # and 0..3 remaining steps across these shapes (199 x 20000: 12 waves of 13 steps).
 REGIMES = [(255, 4096), (2048, 1024), (1500, 2080), (2049, 512), (5121, 4096), (300, 8320),
-           (777, 16416), (10241, 8320), (199, 20000), (1023, 4096), (510, 2048), (1024, 2080)]
+           (777, 16416), (10241, 8320), (199, 20000), (1023, 4096), (510, 2048), (1024, 2080),
+           (1024, 4608)]
 
 
 @pytest.mark.parametrize("N,M", PATTERNS)
@@ -83,6 +84,26 @@ def test_workgroup_regimes(N, M):
         W = synth.weight(R, C, seed=800 + i)
         x = synth.activation(C, seed=850 + i)
         check_full_layer(W, x, N, M, f"regime-{R}x{C}", check_dense=(N == 2))
+
+
+def test_narrow_kernel_routing():
+    """16:32 layers of at most 8 rows per CU whose workgroups hold 1, 2 or 4 rows take the
+    narrow kernel when the row's steps of 128 columns split into 8 / rows column ranges of
+    exactly 4 steps per wave (steps / (4 * 8 / rows) waves); other shapes and patterns keep
+    spmv_kernel. The shapes of test_workgroup_regimes and the closed-form tests cover both."""
+    assert nm.spmv_variant(1024, 4096, 16, 32) == "spmv_narrow_kernel<16, 4, true, 3, 2>"
+    assert nm.spmv_launch_shape(1024, 4096, 16, 32)["waves_per_row_group"] == 4
+    assert nm.spmv_variant(1023, 4096, 16, 32) == "spmv_narrow_kernel<16, 4, true, 3, 2>"
+    assert nm.spmv_variant(510, 2048, 16, 32) == "spmv_narrow_kernel<16, 4, true, 3, 4>"
+    assert nm.spmv_variant(255, 4096, 16, 32) == "spmv_narrow_kernel<16, 4, true, 3, 8>"
+    assert nm.spmv_launch_shape(255, 4096, 16, 32)["waves_per_row_group"] == 1
+    assert nm.spmv_variant(1024, 4096, 2, 4) == "spmv_kernel<2, 4, true, 1>"   # table decoders
+    assert nm.spmv_variant(1024, 4096, 8, 16) == "spmv_kernel<8, 4, true, 2>"
+    assert nm.spmv_launch_shape(1024, 4096, 8, 16)["waves_per_row_group"] == 8
+    assert nm.spmv_variant(1024, 2080, 16, 32) == "spmv_kernel<16, 4, true, 3>"   # a partial last step
+    assert nm.spmv_variant(1024, 4608, 16, 32) == "spmv_kernel<16, 4, true, 3>"   # 36 steps: no 4-step split
+    assert nm.spmv_variant(1500, 4096, 16, 32) == "spmv_kernel<16, 4, true, 3>"   # 6 rows per workgroup
+    assert nm.spmv_variant(4096, 4096, 16, 32) == "spmv_kernel<16, 4, true, 3>"
 
 
 def test_config1_single_24():
@@ -208,15 +229,16 @@ def test_edge_shapes_and_errors():
 def test_malformed_masks_stay_in_bounds():
     """Masks with too few set bits give an unspecified y but run to completion: every LDS
     read stays inside the word's x window by construction (bit 31 sentinel)."""
-    R, C = 64, 1024
-    v = up_f16(synth.weight(R, C // 2, seed=750))
-    x = up_f16(synth.activation(C, seed=751))
-    for N, M in PATTERNS:
-        for word in (0, 1, 0x80000000, 0xFFFFFFFF):
-            m = torch.full((R, C // 32), np.uint32(word).view(np.int32).item(), dtype=torch.int32, device=device())
-            y = nm.nm_spmv(v, m, x, N, M)
-            torch.cuda.synchronize()
-            assert y.shape == (R,)
+    for R, C in ((64, 1024), (64, 4096)):   # 64 x 4096: the narrow kernel for 16:32
+        v = up_f16(synth.weight(R, C // 2, seed=750))
+        x = up_f16(synth.activation(C, seed=751))
+        for N, M in PATTERNS:
+            for word in (0, 1, 0x80000000, 0xFFFFFFFF):
+                m = torch.full((R, C // 32), np.uint32(word).view(np.int32).item(), dtype=torch.int32,
+                               device=device())
+                y = nm.nm_spmv(v, m, x, N, M)
+                torch.cuda.synchronize()
+                assert y.shape == (R,)
 
 
 def test_non_default_stream():
