@@ -1,0 +1,69 @@
+"""Host logic of bench.py, on the CPU: the one-GPU guard, the algorithmic byte counts the
+roofline divides by, the source hash that voids committed counter figures once a kernel
+changes, and the roofline object of the decode sweep."""
+import os
+import subprocess
+import sys
+
+import bench
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""   # no JSON line
+
+
+def test_algorithmic_bytes_closed_forms():
+    """values + masks + x + y: 1.125 R C + 2 (R + C) bytes at 50% (R C / 2 fp16 values and
+    one 4-byte word per 32 columns), 0.625 R C + 2 (R + C) at 25%, 2 R C + 2 (R + C) dense;
+    a batch of B vectors moves B copies of x and y."""
+    for R, C in ((4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336), (256, 512), (28672, 8192)):
+        for N, M in ((2, 4), (4, 8), (8, 16), (16, 32)):
+            assert bench.alg_bytes_sparse(R, C, N, M) == 9 * R * C // 8 + 2 * (R + C)
+        for N, M in ((1, 4), (2, 8), (4, 16), (8, 32)):
+            assert bench.alg_bytes_sparse(R, C, N, M) == 5 * R * C // 8 + 2 * (R + C)
+        assert bench.alg_bytes_dense(R, C) == 2 * R * C + 2 * (R + C)
+        assert bench.alg_bytes_sparse(R, C, 2, 4, B=8) == 9 * R * C // 8 + 8 * 2 * (R + C)
+        assert bench.alg_bytes_dense(R, C, B=4) == 2 * R * C + 4 * 2 * (R + C)
+    # the per-launch figure of the 4096 x 4096 layers in the committed counter summaries
+    assert bench.alg_bytes_sparse(4096, 4096, 2, 4) == 18_890_752
+
+
+def test_traffic_figures_are_void_once_the_kernel_code_changes(tmp_path):
+    src = tmp_path / "kernel.h"
+    src.write_text("int a = 1;  // a comment\n/* block */\n")
+    counters = tmp_path / "counters.txt"
+    counters.write_text(f"# header\nkernel_source_sha256: {bench.kernel_source_sha([str(src)])}\n"
+                        "fetch_factor: 2.0\ntraffic k<1, 2>: 123456\n")
+    assert bench.read_traffic("k<1, 2>", str(counters), [str(src)]) == 123456.0
+    assert bench.read_traffic("k<3, 4>", str(counters), [str(src)]) is None
+    src.write_text("int a = 1;   // another comment\n\n")   # comments and spacing only: still valid
+    assert bench.read_traffic("k<1, 2>", str(counters), [str(src)]) == 123456.0
+    src.write_text("int a = 2;\n")                            # a change of code voids them
+    assert bench.read_traffic("k<1, 2>", str(counters), [str(src)]) is None
+    assert bench.read_traffic("k<1, 2>", str(tmp_path / "missing.txt"), [str(src)]) is None
+
+
+class _Variants:
+    """Stands in for the binding's kernel-name query."""
+
+    def __init__(self, names):
+        self.names = names
+
+    def spmv_variant(self, R, C, N, M):
+        return self.names[(R, C)]
+
+
+def test_decode_roofline():
+    items = [dict(R=4096, C=4096, bytes=30_000_000), dict(R=1024, C=4096, bytes=40_000_000)]
+    one = _Variants({(4096, 4096): "k", (1024, 4096): "k"})
+    r = bench.decode_roofline(one, items, ms_token=0.01, N=2, M=4)   # 10 us per token, 2 launches
+    assert r["kernel"] == "k" and r["launches_per_step"] == 2
+    assert r["bytes_per_launch"] == 35_000_000 and abs(r["avg_launch_us"] - 5.0) < 1e-9
+    assert abs(r["achieved"] - 7000.0) < 0.05 and abs(r["frac"] - 0.875) < 1e-4
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["traffic"] is None
+    two = _Variants({(4096, 4096): "k", (1024, 4096): "other"})
+    assert bench.decode_roofline(two, items, ms_token=0.01, N=2, M=4) is None
