@@ -105,6 +105,18 @@ def test_spmm_regimes(B):
 
 
 @pytest.mark.parametrize("N,M", PATTERNS)
+def test_spmm_narrow_layers_all_rows(N, M):
+    """Every row of 1023- and 1000-row layers (4 rows per workgroup, whose spare lanes repeat
+    the last row; the last workgroup of the first holds 3), at several batches, against the
+    oracle."""
+    for i, (R, C) in enumerate(((1023, 2048), (1000, 1024))):
+        W = synth.weight(R, C, seed=1600 + i)
+        for B in (2, 3, 5, 8):
+            say(f"narrow spmm B={B} {R}x{C} {N}:{M} {nm.spmm_variant(R, C, B, N, M)}")
+            check_spmm(W, batch_x(B, C, 1650 + 10 * i + B), N, M, (B, R, C, N))
+
+
+@pytest.mark.parametrize("N,M", PATTERNS)
 def test_spmm_rows_of_x_are_independent(N, M):
     """Permuting the rows of X permutes the rows of Y bit-exactly (each output row is
     computed alone, in a fixed order), and repeated calls give the same bits."""
@@ -137,15 +149,16 @@ def test_spmm_batch1_is_the_spmv_kernel(N, M):
 def test_spmm_malformed_masks_stay_in_bounds():
     """Masks with the wrong number of set bits give an unspecified Y but the kernel runs to
     completion (every x read stays inside the padded LDS buffer)."""
-    R, C, B = 64, 1024, 8
-    v = up_f16(synth.weight(R, C // 2, seed=1500))
-    X = up_f16(batch_x(B, C, 1501))
-    for N, M in PATTERNS:
-        for word in (0, 1, 0x80000000, 0xFFFFFFFF):
-            m = torch.full((R, C // 32), np.uint32(word).view(np.int32).item(), dtype=torch.int32, device=device())
-            Y = nm.nm_spmm(v, m, X, N, M)
-            torch.cuda.synchronize()
-            assert Y.shape == (B, R)
+    for R, C, B in ((64, 1024, 8), (1024, 1024, 8)):
+        v = up_f16(synth.weight(R, C // 2, seed=1500))
+        X = up_f16(batch_x(B, C, 1501))
+        for N, M in PATTERNS:
+            for word in (0, 1, 0x80000000, 0xFFFFFFFF):
+                m = torch.full((R, C // 32), np.uint32(word).view(np.int32).item(), dtype=torch.int32,
+                               device=device())
+                Y = nm.nm_spmm(v, m, X, N, M)
+                torch.cuda.synchronize()
+                assert Y.shape == (B, R)
 
 
 def test_spmm_argument_errors():
