@@ -51,10 +51,11 @@ def _replay_and_check(run, inputs, out, reseed):
     del g
 
 
+# 2100 x 4096: spmv_kernel; 1024 x 4096: at 16:32 the narrow kernel
+@pytest.mark.parametrize("R,C", [(2100, 4096), (1024, 4096)])
 @pytest.mark.parametrize("N,M", synth.PATTERNS)
-def test_spmv_graph_replays(N, M):
-    R, C = 2100, 4096
-    say(f"graph spmv {N}:{M} {R}x{C}")
+def test_spmv_graph_replays(N, M, R, C):
+    say(f"graph spmv {N}:{M} {R}x{C} {nm.spmv_variant(R, C, N, M)}")
     W = synth.weight(R, C, 5000 + N)
     x = synth.activation(C, 5001 + N)
     values, masks = nm.nm_pack(up_f16(W), N, M)
