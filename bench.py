@@ -17,6 +17,7 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -528,17 +529,40 @@ def decode_main(args, torch, nm, synth, dev):
         del g
         return statistics.median(ts)
 
+    # q/k/v and gate/up as groups of their separate matrices (nm_spmv_group, one launch each)
+    def group_launches():
+        out = []
+        for b in range(NB):
+            blk = sp[7 * b:7 * b + 7]
+            for idx in ((0, 1, 2), (3,), (4, 5), (6,)):
+                parts = [blk[i] for i in idx]
+                n = len(parts)
+                out.append((n, (ctypes.c_void_p * n)(*[q["values"].data_ptr() for q in parts]),
+                            (ctypes.c_void_p * n)(*[q["masks"].data_ptr() for q in parts]),
+                            parts[0]["x"].data_ptr(), (ctypes.c_void_p * n)(*[q["y"].data_ptr() for q in parts]),
+                            (ctypes.c_int64 * n)(*[q["R"] for q in parts]), parts[0]["C"]))
+        return out
+    gr_a = group_launches()
+
+    def token_group(sp_):
+        for n, v, m, x, y, r, c in gr_a:
+            st = lib.nm_spmv_group(n, v, m, x, y, r, c, N, M, sp_)
+            if st:
+                raise RuntimeError(f"nm_spmv_group: {nm.status_string(st)}")
+
     K, Wm = args.tokens, max(1, min(args.warmup, 5))
     ms_sp = timed_tokens(token_sparse(sp_a), K, Wm)
     ms_dn = timed_tokens(token_dense(dn_a), K, Wm)
     ms_fu = timed_tokens(token_sparse(fu_a), K, Wm)
     ms_fu_dn = timed_tokens(token_dense(fdn_a), K, Wm)
+    ms_gr = timed_tokens(token_group, K, Wm)
     bytes_tok = sum(q["bytes"] for q in sp)
     bytes_dn = sum(q["bytes"] for q in dn)
     value = bytes_tok / (ms_sp * 1e-3) / 1e9
     log(f"decode: sparse {ms_sp * 1e3:.1f} us/token ({value:.0f} GB/s), dense {ms_dn * 1e3:.1f} us/token, "
         f"speedup {ms_dn / ms_sp:.3f}x; fused q/k/v and gate/up: sparse {ms_fu * 1e3:.1f} us/token, "
-        f"dense {ms_fu_dn * 1e3:.1f} us/token, speedup {ms_fu_dn / ms_fu:.3f}x")
+        f"dense {ms_fu_dn * 1e3:.1f} us/token, speedup {ms_fu_dn / ms_fu:.3f}x; grouped (separate matrices): "
+        f"sparse {ms_gr * 1e3:.1f} us/token")
     cpu = None if args.no_cpu_baseline else cpu_baseline(cpu_layers, args.cpu_rows_frac)
     out = {
         "metric": METRIC,
@@ -567,6 +591,10 @@ def decode_main(args, torch, nm, synth, dev):
                              "dense_us_per_token": round(ms_fu_dn * 1e3, 2),
                              "dense_GBps": round(sum(q["bytes"] for q in fused_dn) / (ms_fu_dn * 1e-3) / 1e9, 1),
                              "speedup_vs_fused_dense": round(ms_fu_dn / ms_fu, 3)},
+        "grouped_qkv_gateup": {"us_per_token": round(ms_gr * 1e3, 2), "launches_per_token": len(gr_a) // NB * NB,
+                               "GBps": round(bytes_tok / (ms_gr * 1e-3) / 1e9, 1),
+                               "speedup_vs_fused_dense": round(ms_fu_dn / ms_gr, 3),
+                               "note": "q/k/v and gate/up through nm_spmv_group from their separate matrices"},
         "byte_floor_us_per_token_at_8TBps": round(bytes_tok / 8e12 * 1e6, 1),
         "timing": "K tokens in one HIP graph replayed between events, median of 3 replays",
         "roofline": decode_roofline(nm, sp, ms_sp, N, M),

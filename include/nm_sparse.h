@@ -104,6 +104,27 @@ int nm_unpack(const uint16_t* values, const uint32_t* masks, uint16_t* W,
 int nm_spmv(const uint16_t* values, const uint32_t* masks, const uint16_t* x, uint16_t* y,
             int64_t rows, int64_t cols, int N, int M, void* stream);
 
+/* Several sparse products that share one input x, in one launch ([NEWS-NEW]: every
+ * linear layer of a decoding step is a batch-one sparse product; q, k and v, or gate and
+ * up, read the same activation): y[k][r] = fp16( sum_c W'_k[r][c] * x[c] ) for
+ * k < count, 1 <= count <= NM_MAX_SPMV_GROUP, each as nm_spmv computes it. values, masks, y
+ * and rows are HOST arrays of `count` entries: product k's packed matrix (device pointers),
+ * its output (device pointer, rows[k] elements) and its row count; all share cols, N:M and
+ * x (device, cols elements). The arrays are read during the call only. One launch covers
+ * every product when cols <= 8192 and the pattern is 2:4, 4:8, 8:16 or 16:32, with the
+ * workgroup shape nm_spmv would give their rows together; then each y is bit-identical to
+ * nm_spmv's when nm_spmv alone runs the same number of waves per row and not its
+ * narrow-layer path (every product of 4096 columns, for instance), and within the same
+ * tolerance of the exact product otherwise. Other shapes and patterns take one nm_spmv
+ * launch per product.
+ * Alignment as nm_spmv; the outputs must not alias each other or the inputs. Status codes
+ * as nm_spmv, with NM_ERR_SHAPE also for count outside 1..NM_MAX_SPMV_GROUP. Allocates
+ * nothing. */
+#define NM_MAX_SPMV_GROUP 8
+int nm_spmv_group(int count, const uint16_t* const* values, const uint32_t* const* masks,
+                  const uint16_t* x, uint16_t* const* y, const int64_t* rows, int64_t cols,
+                  int N, int M, void* stream);
+
 /* Dense baseline, the denominator of the pages' speedups ([KERNEL]):
  * y[r] = fp16( sum_c W[r][c] * x[c] ) with fp32 products and sums, fixed order. */
 int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,

@@ -34,6 +34,9 @@ SIGNATURES = {
                            _c.c_int64, _c.c_int, _c.c_int, _c.c_void_p]),
     "nm_gemv_dense": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
                                  _c.c_void_p]),
+    "nm_spmv_group": (_c.c_int, [_c.c_int, _c.POINTER(_c.c_void_p), _c.POINTER(_c.c_void_p), _c.c_void_p,
+                                 _c.POINTER(_c.c_void_p), _c.POINTER(_c.c_int64), _c.c_int64, _c.c_int, _c.c_int,
+                                 _c.c_void_p]),
     "nm_spmm": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
                            _c.c_int64, _c.c_int64, _c.c_int, _c.c_int, _c.c_void_p]),
     "nm_gemm_dense": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
@@ -223,6 +226,49 @@ def nm_spmv(values, masks, x, N: int, M: int, out=None):
                            rows, cols, N, M, _stream_ptr(x))
     _check("nm_spmv", st)
     return out
+
+
+MAX_SPMV_GROUP = 8
+
+
+def nm_spmv_group(values_list, masks_list, x, N: int, M: int, outs=None):
+    """y_k = W'_k x for several packed matrices that share x and cols, in one launch;
+    returns the list of fp16 y_k [rows_k]."""
+    torch = _torch()
+    count = len(values_list)
+    if count != len(masks_list) or not 1 <= count <= MAX_SPMV_GROUP:
+        raise ValueError(f"need 1..{MAX_SPMV_GROUP} (values, masks) pairs, got {count} and {len(masks_list)}")
+    _require(x, "x", torch.float16, 1)
+    cols = x.shape[0]
+    rows = []
+    for k, (values, masks) in enumerate(zip(values_list, masks_list)):
+        _require(values, f"values[{k}]", torch.float16, 2)
+        _require(masks, f"masks[{k}]", torch.int32, 2)
+        r, words = masks.shape
+        if words * 32 != cols:
+            raise ValueError(f"masks[{k}] describe {words * 32} columns, x has {cols}")
+        if (N, M) in ALL_PATTERNS and values.shape != (r, cols * N // M):
+            raise ValueError(f"values[{k}] shape {tuple(values.shape)} != {(r, cols * N // M)}")
+        if values.device != x.device or masks.device != x.device:
+            raise ValueError("every matrix and x must be on one device")
+        rows.append(r)
+    if outs is None:
+        outs = [torch.empty(r, dtype=torch.float16, device=x.device) for r in rows]
+    else:
+        if len(outs) != count:
+            raise ValueError("one output per product")
+        for k, (o, r) in enumerate(zip(outs, rows)):
+            _require(o, f"outs[{k}]", torch.float16, 1)
+            if o.shape[0] != r or o.device != x.device:
+                raise ValueError(f"outs[{k}] must be fp16 [{r}] on the same device")
+    vp = (ctypes.c_void_p * count)(*[v.data_ptr() for v in values_list])
+    mp = (ctypes.c_void_p * count)(*[m.data_ptr() for m in masks_list])
+    yp = (ctypes.c_void_p * count)(*[o.data_ptr() for o in outs])
+    rp = (ctypes.c_int64 * count)(*rows)
+    with torch.cuda.device(x.device):
+        st = lib().nm_spmv_group(count, vp, mp, x.data_ptr(), yp, rp, cols, N, M, _stream_ptr(x))
+    _check("nm_spmv_group", st)
+    return outs
 
 
 def nm_gemv_dense(W, x, out=None):

@@ -143,6 +143,26 @@ int nm_spmv(const uint16_t* values, const uint32_t* masks, const uint16_t* x, ui
   return e == hipSuccess ? NM_OK : nm::hip_fail(e);
 }
 
+int nm_spmv_group(int count, const uint16_t* const* values, const uint32_t* const* masks, const uint16_t* x,
+                  uint16_t* const* y, const int64_t* rows, int64_t cols, int N, int M, void* stream) {
+  if (!values || !masks || !x || !y || !rows) return NM_ERR_NULL;
+  if (count < 1 || count > nm::kMaxSpmvGroup) return NM_ERR_SHAPE;
+  for (int k = 0; k < count; ++k)
+    if (!values[k] || !masks[k] || !y[k]) return NM_ERR_NULL;
+  for (int k = 0; k < count; ++k)
+    if (!nm::valid_shape(rows[k], cols)) return NM_ERR_SHAPE;
+  if (!nm::valid_pattern(N, M)) return NM_ERR_PATTERN;
+  if (!nm::aligned(x, 16)) return NM_ERR_ALIGN;
+  for (int k = 0; k < count; ++k)
+    if (!nm::aligned(values[k], 16) || !nm::aligned(masks[k], 4) || !nm::aligned(y[k], 2)) return NM_ERR_ALIGN;
+  nm::DeviceInfo dev;
+  hipError_t e = nm::current_device_info(&dev);
+  if (e != hipSuccess) return nm::hip_fail(e);
+  if (cols > nm::max_cols_for(dev)) return NM_ERR_TOO_WIDE;
+  e = nm::launch_spmv_group(count, values, masks, x, y, rows, cols, N, M, static_cast<hipStream_t>(stream), dev);
+  return e == hipSuccess ? NM_OK : nm::hip_fail(e);
+}
+
 int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y, int64_t rows, int64_t cols,
                   void* stream) {
   if (!W || !x || !y) return NM_ERR_NULL;

@@ -70,6 +70,10 @@ const char* spmm_variant(int N, int64_t batch);
 // Name of the kernel configuration launch_spmv picks (static string) and its shape.
 const char* spmv_variant(int64_t rows, int64_t cols, int N, int M, const DeviceInfo& dev);
 WorkgroupShape spmv_shape(int64_t rows, int64_t cols, int N, const DeviceInfo& dev);
+constexpr int kMaxSpmvGroup = 8;  // products per nm_spmv_group call
+hipError_t launch_spmv_group(int count, const uint16_t* const* values, const uint32_t* const* masks,
+                             const uint16_t* x, uint16_t* const* y, const int64_t* rows, int64_t cols, int N,
+                             int M, hipStream_t stream, const DeviceInfo& dev);
 WorkgroupShape spmv_quarter_shape(int64_t rows, int64_t cols, const DeviceInfo& dev);
 WorkgroupShape dense_shape(int64_t rows, int64_t cols, const DeviceInfo& dev);
 

@@ -183,4 +183,68 @@ hipError_t launch_spmv(const uint16_t* values, const uint32_t* masks, const uint
   }
 }
 
+// Products sharing x in one launch of spmv_group_kernel when the columns are at most 64
+// steps (every workgroup one row group), the pattern is a 50% one with its table decoder,
+// and there are at most kMaxGroup products: all take the workgroup shape the rule gives
+// their rows together (as if their rows were concatenated), so that small products do not
+// run workgroups whose lanes repeat rows. A row's summation order depends on the wave count
+// only, not on the rows per workgroup, so a product's y is bit-identical to a separate
+// launch of spmv_kernel whenever the rule gives that product alone the same wave count (for
+// example every product of 4096 columns: 8 waves). Otherwise one nm_spmv launch per product.
+static_assert(kMaxGroup == kMaxSpmvGroup, "one group size for the kernel and the ABI");
+
+hipError_t launch_spmv_group(int count, const uint16_t* const* values, const uint32_t* const* masks,
+                             const uint16_t* x, uint16_t* const* y, const int64_t* rows, int64_t cols, int N,
+                             int M, hipStream_t stream, const DeviceInfo& dev) {
+  if (count == 1) return launch_spmv(values[0], masks[0], x, y[0], rows[0], cols, N, M, stream, dev);
+  const int64_t steps = ceil_div(cols, 128);
+  const int dec = pick_decoder(N, cols, dev);
+  bool one = M == 2 * N && steps <= 64 && count <= kMaxGroup && dec != kBitWalk;
+  GroupArgs a{};
+  int64_t grid = 0;
+  if (one) {
+    int64_t total = 0;
+    for (int k = 0; k < count; ++k) total += rows[k];
+    const WorkgroupShape s = workgroup_shape(total, steps, dev);
+    if (s.row_groups != 1) one = false;
+    a.cs = s.cs;
+    a.rpb = s.rpb;
+    for (int k = 0; k < count && one; ++k) {
+      a.block0[k] = int(grid);
+      grid += ceil_div(rows[k], s.rpb);
+      a.values[k] = reinterpret_cast<const uint4*>(values[k]);
+      a.masks[k] = masks[k];
+      a.y[k] = y[k];
+      a.rows[k] = int(rows[k]);
+    }
+    if (grid > (int64_t(1) << 31) - 1) one = false;
+  }
+  if (!one) {
+    for (int k = 0; k < count; ++k) {
+      const hipError_t e = launch_spmv(values[k], masks[k], x, y[k], rows[k], cols, N, M, stream, dev);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  a.block0[count] = int(grid);
+  a.x = reinterpret_cast<const uint4*>(x);
+  a.cols = int(cols);
+  a.count = count;
+  void* args[] = {&a};
+  const void* fn = nullptr;
+  size_t lds = 0;
+  switch (N) {
+    case 2: fn = reinterpret_cast<const void*>(&spmv_group_kernel<2, kBatch, kNTV, kPairTable>);
+            lds = lds_bytes<kPairTable>(int(cols)); break;
+    case 4: fn = reinterpret_cast<const void*>(&spmv_group_kernel<4, kBatch, kNTV, kByteLut>);
+            lds = lds_bytes<kByteLut>(int(cols)); break;
+    case 8: fn = reinterpret_cast<const void*>(&spmv_group_kernel<8, kBatch, kNTV, kByteLut>);
+            lds = lds_bytes<kByteLut>(int(cols)); break;
+    case 16: fn = reinterpret_cast<const void*>(&spmv_group_kernel<16, kBatch, kNTV, kRevWalk>);
+             lds = lds_bytes<kRevWalk>(int(cols)); break;
+    default: return hipErrorInvalidValue;
+  }
+  return launch(fn, dim3(unsigned(grid)), dim3(unsigned(64 * a.cs)), args, lds, stream, dev);
+}
+
 }  // namespace nm

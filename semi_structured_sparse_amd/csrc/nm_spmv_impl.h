@@ -409,10 +409,12 @@ constexpr size_t lds_bytes(int cols) {
 // lane's row; the launcher picks CS = steps / (BATCH * CI), so that every lane has exactly
 // one batch of whole steps, which the prologue loads. The CI partial sums of a row are added
 // across lanes before the LDS reduction.
+//
+// `block` is the workgroup's index within the product (blockIdx.x for a single product).
 template <int N, int BATCH, bool NTV, int DEC, int CI>
 __device__ __forceinline__ void spmv_body(
     const uint4* __restrict__ values, const uint32_t* __restrict__ masks, const uint4* __restrict__ x,
-    uint16_t* __restrict__ y, int rows, int cols, int rpb, int cs_count) {
+    uint16_t* __restrict__ y, int rows, int cols, int rpb, int cs_count, int block) {
   static_assert((DEC != kPairTable || N == 2) && (DEC != kByteLut || N == 4 || N == 8) &&
                     (DEC != kRevWalk || N == 16),
                 "pair table: 2:4 only; byte LUT: 4:8 and 8:16 only; reversed walk: 16:32 only");
@@ -436,7 +438,7 @@ __device__ __forceinline__ void spmv_body(
   const int u = ((lane >> 5) << 2) | (lane & 3);   // half-word u of the step's 8
   const int half = u & 1;
   const int wsel = u >> 1;                         // which of the step's 4 words
-  const int row0 = blockIdx.x * rpb;
+  const int row0 = block * rpb;
   const int row_end = min(row0 + rpb, rows);
   const unsigned r = unsigned(min(row0 + 8 * rg + rrow, row_end - 1));
 
@@ -550,7 +552,7 @@ template <int N, int BATCH, bool NTV, int DEC>
 __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(8))) void spmv_kernel(
     const uint4* __restrict__ values, const uint32_t* __restrict__ masks, const uint4* __restrict__ x,
     uint16_t* __restrict__ y, int rows, int cols, int rpb, int cs_count) {
-  spmv_body<N, BATCH, NTV, DEC, 1>(values, masks, x, y, rows, cols, rpb, cs_count);
+  spmv_body<N, BATCH, NTV, DEC, 1>(values, masks, x, y, rows, cols, rpb, cs_count, int(blockIdx.x));
 }
 
 // Narrow layers (at most 8 rows per CU, at most 64 steps per row): rows per workgroup
@@ -559,7 +561,39 @@ template <int N, int BATCH, bool NTV, int DEC, int CI>
 __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(8))) void spmv_narrow_kernel(
     const uint4* __restrict__ values, const uint32_t* __restrict__ masks, const uint4* __restrict__ x,
     uint16_t* __restrict__ y, int rows, int cols, int rpb, int cs_count) {
-  spmv_body<N, BATCH, NTV, DEC, CI>(values, masks, x, y, rows, cols, rpb, cs_count);
+  spmv_body<N, BATCH, NTV, DEC, CI>(values, masks, x, y, rows, cols, rpb, cs_count, int(blockIdx.x));
+}
+
+// Several products that share x and one workgroup shape, in one launch (for example q, k
+// and v, or gate and up, stored as separate matrices): product k owns workgroups
+// [block0[k], block0[k + 1]) of the grid and runs the single-product body on them, so its y
+// is the one a launch of spmv_kernel with the same rows per workgroup and waves gives. One
+// launch fills and drains the memory pipeline once for all of them.
+constexpr int kMaxGroup = 8;
+struct GroupArgs {
+  const uint4* x;
+  int cols;
+  int cs;   // waves per workgroup (one row group)
+  int rpb;  // rows per workgroup
+  int count;
+  int block0[kMaxGroup + 1];
+  const uint4* values[kMaxGroup];
+  const uint32_t* masks[kMaxGroup];
+  uint16_t* y[kMaxGroup];
+  int rows[kMaxGroup];
+};
+
+template <int N, int BATCH, bool NTV, int DEC>
+__global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(8))) void spmv_group_kernel(
+    const GroupArgs a) {
+  const int b = int(blockIdx.x);
+  // the product this workgroup serves: the number of product starts at or below b (static
+  // indices, so the starts come in one scalar load rather than a chain of dependent ones)
+  int k = 0;
+#pragma unroll
+  for (int j = 1; j < kMaxGroup; ++j) k += (j < a.count && b >= a.block0[j]) ? 1 : 0;
+  spmv_body<N, BATCH, NTV, DEC, 1>(a.values[k], a.masks[k], a.x, a.y[k], a.rows[k], a.cols, a.rpb, a.cs,
+                                   b - a.block0[k]);
 }
 
 // ---------------------------------------------------------------- 25% density

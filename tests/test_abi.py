@@ -128,6 +128,35 @@ def test_gemv_validation(kw, want):
     assert _gemv(**kw) == want
 
 
+def _group(count=3, values=None, masks=None, x=A16, y=None, rows=None, cols=64, N=2, M=4, nulls=False):
+    n = max(count, 1)
+    P = ctypes.c_void_p * n
+    vals = P(*([A16] * n)) if values is None else P(*values)
+    msks = P(*([A16] * n)) if masks is None else P(*masks)
+    outs = P(*([A16] * n)) if y is None else P(*y)
+    rws = (ctypes.c_int64 * n)(*([16] * n if rows is None else rows))
+    if nulls:
+        return nm.lib().nm_spmv_group(count, None, msks, x, outs, rws, cols, N, M, None)
+    return nm.lib().nm_spmv_group(count, vals, msks, x, outs, rws, cols, N, M, None)
+
+
+def test_spmv_group_validation():
+    """nm_spmv_group validates every product before any HIP call."""
+    assert _group(nulls=True) == nm.NM_ERR_NULL
+    assert _group(x=None) == nm.NM_ERR_NULL
+    assert _group(values=[A16, 0, A16]) == nm.NM_ERR_NULL
+    assert _group(y=[A16, A16, 0]) == nm.NM_ERR_NULL
+    assert _group(count=0) == nm.NM_ERR_SHAPE
+    assert _group(count=9) == nm.NM_ERR_SHAPE
+    assert _group(rows=[16, 0, 16]) == nm.NM_ERR_SHAPE
+    assert _group(cols=48) == nm.NM_ERR_SHAPE
+    assert _group(N=3) == nm.NM_ERR_PATTERN
+    assert _group(x=A16 + 2) == nm.NM_ERR_ALIGN
+    assert _group(values=[A16, A16 + 8, A16]) == nm.NM_ERR_ALIGN
+    assert _group(masks=[A16, A16, A16 + 2]) == nm.NM_ERR_ALIGN
+    assert _group(y=[A16 + 1, A16, A16]) == nm.NM_ERR_ALIGN
+
+
 def test_probe_validation():
     L = nm.lib()
     assert L.nm_probe_read(None, 16, A16, 0, None) == nm.NM_ERR_NULL
