@@ -258,3 +258,9 @@ def test_python_layer_rejects_cpu_tensors():
         nm.nm_pack(W, 2, 4)
     with pytest.raises(ValueError):
         nm.nm_gemv_dense(W, torch.zeros(64, dtype=torch.float16))
+    v = torch.zeros(16, 32, dtype=torch.float16)
+    m = torch.zeros(16, 2, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        nm.nm_spmv_group([v], [m], torch.zeros(64, dtype=torch.float16), 2, 4)
+    with pytest.raises(ValueError):   # no products, or more than the group holds
+        nm.nm_spmv_group([], [], torch.zeros(64, dtype=torch.float16), 2, 4)
