@@ -59,6 +59,14 @@ def test_group_ragged(N, M):
     _check((1, 7, 300, 2049), 2080, N, M, seed=6100 + N, bitwise=False)
 
 
+@pytest.mark.parametrize("N,M", synth.PATTERNS)
+def test_group_tiny(N, M):
+    """Rows of 1..3 at 32 and 96 columns (one and three mask words: only a partial step)."""
+    for C in (32, 96):
+        say(f"group tiny {N}:{M} x{C}")
+        _check((1, 2, 3), C, N, M, seed=6700 + C + N, bitwise=False)
+
+
 def test_group_gate_up_and_eight_products():
     """gate and up (14336 rows each, 4096 columns) on sampled rows; eight products of
     mixed rows (the largest group) on every row."""
