@@ -59,6 +59,8 @@ def parse_args():
     ap.add_argument("--prompt", type=int, default=2048,
                     help="prefill workload: prompt tokens per product (rows of X)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="default workload: skip the Llama-3.3-70B 2:4 layers and the decode sweep")
     ap.add_argument("--patterns", default="", help="patterns to run instead of the workload's, e.g. 2:4,16:32 "
                                                   "or the 25%% ones 1:4,2:8,4:16,8:32")
     ap.add_argument("--batch", type=int, default=1,
@@ -131,6 +133,235 @@ def cpu_info():
     return model
 
 
+def graph_us_per_launch(torch, launch, launches, reps=5):
+    """Median time per launch of `launch(k, stream)` for k = 0..launches-1, captured in one
+    HIP graph and replayed `reps` times between events."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream().cuda_stream
+        for k in range(launches):
+            launch(k, cs)
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        g.replay()
+        b_.record()
+        torch.cuda.synchronize()
+        ts.append(a_.elapsed_time(b_) * 1e3 / launches)
+    del g
+    return statistics.median(ts)
+
+
+def pool_copies(nbytes, pool_bytes):
+    """Copies of an operand of `nbytes` such that >= pool_bytes of distinct data rotate."""
+    return max(2, math.ceil(pool_bytes / nbytes))
+
+
+# Launch shapes of the shaped read probe (workgroups per CU, lanes per workgroup, loads in
+# flight per lane, blocked slices) tried at each layer's byte count; the fastest is the
+# attainable time of a single launch that only reads those bytes. They are the fastest
+# shapes of a sweep on MI355X over 1..16 workgroups per CU, 256..1024 lanes, 1..8 loads in
+# flight and both layouts at 4.7..264 MB: many resident waves with one or two 16-byte loads
+# in flight each, sweeping the buffer grid-stride, read fastest at every size.
+PROBE_SHAPES = ((4, 512, 1, 0), (8, 256, 1, 0), (3, 512, 2, 0), (2, 1024, 1, 0), (16, 256, 2, 0),
+                (8, 512, 1, 0), (16, 512, 4, 0), (16, 1024, 2, 0), (1, 512, 4, 0))
+
+
+class ReadCeiling:
+    """Attainable single-launch read times (the shaped read probe, fastest of PROBE_SHAPES,
+    each launch on the next region of a >= 2 GiB buffer) and the whole-chip read rate."""
+
+    def __init__(self, torch, nm, dev, buf_bytes=4 << 30):
+        self.torch, self.nm, self.dev = torch, nm, dev
+        self.lib = nm.lib()
+        self.buf = torch.empty(buf_bytes, dtype=torch.uint8, device=dev)
+        self.sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        props = torch.cuda.get_device_properties(dev)
+        self.cus = int(getattr(props, "multi_processor_count", 256) or 256)
+        self.cache = {}
+
+    def chip_rate_gbps(self):
+        """Whole-chip read rate of nm_probe_read over 2 GiB (median of 10)."""
+        torch, nm = self.torch, self.nm
+        part = self.buf[:2 << 30]
+        for _ in range(3):
+            nm.nm_probe_read(part, self.sink)
+        torch.cuda.synchronize()
+        pt = []
+        for _ in range(10):
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            nm.nm_probe_read(part, self.sink)
+            b_.record()
+            torch.cuda.synchronize()
+            pt.append(a_.elapsed_time(b_))
+        return part.numel() / (statistics.median(pt) * 1e-3) / 1e9
+
+    def attainable_us(self, nbytes, launches=40):
+        """(time, shape) of the fastest probe shape reading `nbytes` in one launch."""
+        nbytes = nbytes - nbytes % 16
+        if nbytes in self.cache:
+            return self.cache[nbytes]
+        step = (nbytes + 4095) // 4096 * 4096
+        nreg = self.buf.numel() // step
+        base = self.buf.data_ptr()
+        sink = self.sink.data_ptr()
+        best = None
+        for wpc, threads, unroll, blocked in PROBE_SHAPES:
+            blocks = wpc * self.cus
+
+            def launch(k, s_, b=blocks, t=threads, u=unroll, bl=blocked):
+                st = self.lib.nm_probe_read_shaped(base + (k % nreg) * step, nbytes, sink, 0x9E3779B9, b, t, u, bl, s_)
+                if st:
+                    raise RuntimeError(f"nm_probe_read_shaped: {self.nm.status_string(st)}")
+            us = graph_us_per_launch(self.torch, launch, launches, reps=3)
+            if best is None or us < best[0]:
+                best = (us, {"workgroups": blocks, "threads": threads, "loads_in_flight": unroll,
+                             "layout": "blocked" if blocked else "grid-stride"})
+        self.cache[nbytes] = best
+        return best
+
+    def release(self):
+        del self.buf
+        self.torch.cuda.empty_cache()
+
+
+def parity_failures(obj, path="", under=False) -> list:
+    """Paths of every parity record whose "ok" is false, anywhere in the bench's output: a
+    dict with an "ok" key that sits under a key starting with "parity" (directly or deeper)."""
+    bad = []
+    if isinstance(obj, dict):
+        if under and obj.get("ok") is False:
+            bad.append(path)
+        for k, v in obj.items():
+            p = f"{path}.{k}" if path else str(k)
+            bad += parity_failures(v, p, under or str(k).startswith("parity"))
+    elif isinstance(obj, list):
+        for i, v in enumerate(obj):
+            bad += parity_failures(v, f"{path}[{i}]", under)
+    return bad
+
+
+def emit(out) -> int:
+    """Print the JSON line; the exit status is 3 when any parity record failed."""
+    bad = parity_failures(out)
+    out["parity_ok"] = not bad
+    print(json.dumps(out), flush=True)
+    if bad:
+        log(f"PARITY FAILED: {', '.join(bad)}")
+        return 3
+    return 0
+
+
+def make_layers(torch, nm, synth, dev, cfg, specs, pats, B, cpu_rows_frac, keep_cpu=True):
+    """Seeded W and x of every (layer, pattern), packed on the GPU; the dense W once per shape."""
+    import numpy as np
+    layers, dense = [], {}
+    for li, (name, R, C) in specs:
+        for pat in pats:
+            N, M = pat
+            ws, xs = synth.weight_seed(cfg, li, pat), synth.x_seed(cfg, li, pat)
+            W = synth.weight(R, C, ws)
+            x = synth.activation(C, xs)
+            if B > 1:  # B activation vectors, one per row; the first is the layer's x
+                x = np.stack([x] + [synth.activation(C, xs + 7919 * b) for b in range(1, B)])
+            Wd = torch.from_numpy(W).to(dev)
+            xd = torch.from_numpy(x).to(dev)
+            values, masks = nm.nm_pack(Wd, N, M)
+            ncpu = max(1, int(math.ceil(R * cpu_rows_frac)))
+            yshape = (R,) if B == 1 else (B, R)
+            layers.append(dict(name=name, R=R, C=C, N=N, M=M, seed_w=ws, seed_x=xs,
+                               values=[values], masks=[masks], x=xd, x_host=x,
+                               W_cpu=W[:ncpu].copy() if keep_cpu else None,
+                               y=torch.empty(yshape, dtype=torch.float16, device=dev),
+                               bytes=alg_bytes_sparse(R, C, N, M, B)))
+            if (R, C) not in dense:
+                dense[(R, C)] = dict(name=name, R=R, C=C, W=[Wd], x=xd,
+                                     y=torch.empty(yshape, dtype=torch.float16, device=dev),
+                                     bytes=alg_bytes_dense(R, C, B))
+            else:
+                del Wd
+            del W
+    torch.cuda.synchronize()
+    return layers, dense
+
+
+def per_layer_times(torch, nm, layers, dense, B, pool_bytes, launches, ceiling=None, tag=None):
+    """Each layer alone: `launches` launches cycling over its own >= pool_bytes rotation, in a
+    graph (median of 5 replays), for the sparse product and for the dense one of its shape."""
+    lib = nm.lib()
+    sp_fn = lib.nm_spmv if B == 1 else lib.nm_spmm
+    dn_fn = lib.nm_gemv_dense if B == 1 else lib.nm_gemm_dense
+    bx = () if B == 1 else (B,)
+
+    def rotation(tensors, nbytes):
+        return [tensors] + [[t.clone() for t in tensors] for _ in range(pool_copies(nbytes, pool_bytes) - 1)]
+
+    def checked(fn, name):
+        def call(*a):
+            st = fn(*a)
+            if st:
+                raise RuntimeError(f"{name}: {nm.status_string(st)}")
+        return call
+    sp_call, dn_call = checked(sp_fn, "sparse product"), checked(dn_fn, "dense product")
+    per_s = []
+    for L in layers:
+        pool = rotation([L["values"][0], L["masks"][0]], L["bytes"])
+        argsets = [(p[0].data_ptr(), p[1].data_ptr(), L["x"].data_ptr(), L["y"].data_ptr(),
+                    L["R"], L["C"]) + bx + (L["N"], L["M"]) for p in pool]
+        per_s.append(graph_us_per_launch(torch, lambda c, sp, A=argsets: sp_call(*A[c % len(A)], sp), launches))
+        del pool
+    per_d = {}
+    for D in dense.values():
+        pool = rotation([D["W"][0]], D["bytes"])
+        argsets = [(p[0].data_ptr(), D["x"].data_ptr(), D["y"].data_ptr(), D["R"], D["C"]) + bx for p in pool]
+        per_d[(D["R"], D["C"])] = graph_us_per_launch(
+            torch, lambda c, sp, A=argsets: dn_call(*A[c % len(A)], sp), launches)
+        del pool
+    torch.cuda.synchronize()
+    rows = []
+    for L, us in zip(layers, per_s):
+        kname = nm.spmv_variant(L["R"], L["C"], L["N"], L["M"]) if B == 1 else \
+            nm.spmm_variant(L["R"], L["C"], B, L["N"], L["M"])
+        dus = per_d[(L["R"], L["C"])]
+        gbps = L["bytes"] / (us * 1e-6) / 1e9
+        rec = {"layer": L["name"], "shape": f"{L['R']}x{L['C']}", "pattern": f"{L['N']}:{L['M']}", "kernel": kname}
+        if tag:
+            rec["workload"] = tag
+            rec["in_step"] = False
+        if B == 1:
+            ls = nm.spmv_launch_shape(L["R"], L["C"], L["N"], L["M"])
+            rec["workgroups"] = ls["workgroups"]
+            rec["workgroup"] = f"{ls['rows_per_workgroup']} rows, {ls['row_groups']}x{ls['waves_per_row_group']} waves"
+        rec.update({"us": round(us, 2), "GBps": round(gbps, 1), "pct_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                    "dense_us": round(dus, 2), "speedup": round(dus / us, 3)})
+        if ceiling is not None:
+            att, shape = ceiling.attainable_us(L["bytes"])
+            rec["attainable_us"] = round(att, 2)
+            rec["frac_of_attainable"] = round(att / us, 4)
+            rec["attainable_probe"] = shape
+        rows.append(rec)
+    return rows, per_s
+
+
+def pattern_spread(per_layer) -> dict:
+    """Per shape: (slowest - fastest) / fastest time over the patterns measured at it."""
+    by = {}
+    for r in per_layer:
+        if r.get("in_step", True):
+            by.setdefault(r["shape"], {})[r["pattern"]] = r["us"]
+    out = {}
+    for shape, t in by.items():
+        if len(t) > 1:
+            lo, hi = min(t.values()), max(t.values())
+            out[shape] = {"spread": round((hi - lo) / lo, 4), "fastest": min(t, key=t.get),
+                          "slowest": max(t, key=t.get)}
+    return out
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -139,7 +370,6 @@ def main():
               file=sys.stderr, flush=True)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import semi_structured_sparse_amd as nm
@@ -154,9 +384,9 @@ def main():
 
     cfg = WORKLOAD_BY_NAME[args.workload]
     if cfg == 5:
-        return decode_main(args, torch, nm, synth, dev)
+        sys.exit(decode_main(args, torch, nm, synth, dev))
     if cfg == 6:
-        return prefill_main(args, torch, nm, synth, dev)
+        sys.exit(prefill_main(args, torch, nm, synth, dev))
     wl = synth.WORKLOADS[cfg]
     pats = [tuple(p) for p in wl["patterns"]]
     B = args.batch
@@ -169,43 +399,20 @@ def main():
         if bad:
             print(f"unsupported patterns {bad}", file=sys.stderr)
             sys.exit(2)
+    # the default run also covers the Llama-3.3-70B 2:4 layers and the decode sweep
+    extra = cfg == 2 and B == 1 and not args.patterns and not args.no_extra
 
     # ------------------------------------------------------------------ inputs (untimed)
-    layers = []   # sparse layers: dict(name, R, C, N, M, values[], masks[], x, y, bytes, cpu rows)
-    dense = {}    # shape -> dict(W[], x, y, bytes)
     t_gen = time.time()
-    for li, (name, R, C) in enumerate(wl["layers"]):
-        for pat in pats:
-            N, M = pat
-            ws, xs = synth.weight_seed(cfg, li, pat), synth.x_seed(cfg, li, pat)
-            W = synth.weight(R, C, ws)
-            x = synth.activation(C, xs)
-            if B > 1:  # B activation vectors, one per row; the first is the layer's x
-                x = np.stack([x] + [synth.activation(C, xs + 7919 * b) for b in range(1, B)])
-            Wd = torch.from_numpy(W).to(dev)
-            xd = torch.from_numpy(x).to(dev)
-            values, masks = nm.nm_pack(Wd, N, M)
-            ncpu = max(1, int(math.ceil(R * args.cpu_rows_frac)))
-            yshape = (R,) if B == 1 else (B, R)
-            layers.append(dict(name=name, R=R, C=C, N=N, M=M, seed_w=ws, seed_x=xs,
-                               values=[values], masks=[masks], x=xd, x_host=x,
-                               W_cpu=W[:ncpu].copy(), y=torch.empty(yshape, dtype=torch.float16, device=dev),
-                               bytes=alg_bytes_sparse(R, C, N, M, B)))
-            if (R, C) not in dense:
-                dense[(R, C)] = dict(name=name, R=R, C=C, W=[Wd], x=xd,
-                                     y=torch.empty(yshape, dtype=torch.float16, device=dev),
-                                     bytes=alg_bytes_dense(R, C, B))
-            else:
-                del Wd
-            del W
-    torch.cuda.synchronize()
+    layers, dense = make_layers(torch, nm, synth, dev, cfg, list(enumerate(wl["layers"])), pats, B,
+                                args.cpu_rows_frac)
     log(f"generated and packed {len(layers)} layers in {time.time() - t_gen:.1f}s")
 
     pool_bytes = args.pool_gib * (1 << 30)
     step_sparse = sum(L["bytes"] for L in layers)
     step_dense = sum(D["bytes"] for D in dense.values())
-    P_s = max(2, math.ceil(pool_bytes / step_sparse))
-    P_d = max(2, math.ceil(pool_bytes / step_dense))
+    P_s = pool_copies(step_sparse, pool_bytes)
+    P_d = pool_copies(step_dense, pool_bytes)
     for L in layers:
         for _ in range(P_s - 1):
             L["values"].append(L["values"][0].clone())
@@ -245,25 +452,12 @@ def main():
                 raise RuntimeError(f"dense product: {nm.status_string(st)}")
 
     # ------------------------------------------------------------------ read ceiling probe
-    probe_buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
-    sink = torch.zeros(4, dtype=torch.int32, device=dev)
-    for _ in range(3):
-        nm.nm_probe_read(probe_buf, sink)
-    torch.cuda.synchronize()
-    pt = []
-    for _ in range(10):
-        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a_.record()
-        nm.nm_probe_read(probe_buf, sink)
-        b_.record()
-        torch.cuda.synchronize()
-        pt.append(a_.elapsed_time(b_))
-    probe_ms = statistics.median(pt)
-    read_ceiling = probe_buf.numel() / (probe_ms * 1e-3) / 1e9
+    ceiling = ReadCeiling(torch, nm, dev)
+    read_ceiling = ceiling.chip_rate_gbps()
     log(f"read ceiling {read_ceiling:.0f} GB/s")
     # one plain copy of known size: under a counter profile its FETCH_SIZE / WRITE_SIZE
     # calibrate the counters against real bytes
-    nm.nm_probe_copy(probe_buf[COPY_CAL_BYTES:2 * COPY_CAL_BYTES], probe_buf[:COPY_CAL_BYTES])
+    nm.nm_probe_copy(ceiling.buf[COPY_CAL_BYTES:2 * COPY_CAL_BYTES], ceiling.buf[:COPY_CAL_BYTES])
     torch.cuda.synchronize()
 
     def timed_graph(step_fn, K, W_):
@@ -291,62 +485,20 @@ def main():
         del g
         return start.elapsed_time(end), wall
 
-    def per_launch_us(launch_copy, n_copies, launches, reps=5):
-        """Median per-launch time of one layer: `launches` launches cycling over its
-        rotating pool, captured in a graph and replayed `reps` times between events."""
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            cs = torch.cuda.current_stream().cuda_stream
-            for k in range(launches):
-                launch_copy(k % n_copies, cs)
-        g.replay()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(reps):
-            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a_.record()
-            g.replay()
-            b_.record()
-            torch.cuda.synchronize()
-            ts.append(a_.elapsed_time(b_) * 1e3 / launches)
-        del g
-        return statistics.median(ts)
-
-    def pool_copies(nbytes):
-        return max(2, math.ceil(pool_bytes / nbytes))
-
-    def layer_pool(tensors, nbytes):
-        """Copies of a layer's tensors so that >= pool_bytes of distinct data rotate."""
-        return [tensors] + [[t.clone() for t in tensors] for _ in range(pool_copies(nbytes) - 1)]
-
     # Every layer gets the same number of per-layer launches (enough to cycle through the
     # largest pool), so that each shape weighs the same in a kernel's average duration as
     # it does in a step, in these timings and in a profiler's per-kernel statistics.
-    L_PL = max(40, max(pool_copies(L["bytes"]) for L in layers),
-               max(pool_copies(D["bytes"]) for D in dense.values()))
+    L_PL = max(40, max(pool_copies(L["bytes"], pool_bytes) for L in layers),
+               max(pool_copies(D["bytes"], pool_bytes) for D in dense.values()))
 
     # ------------------------------------------------------------------ timed regions
     K, Wm = args.steps, args.warmup
     ms_s, wall_s = timed_graph(sparse_step, K, Wm)
     ms_d, wall_d = timed_graph(dense_step, K, Wm)
-    del probe_buf
 
     # per-layer durations (each layer alone, its own >= pool_bytes rotation)
-    per_s = []
-    for i, L in enumerate(layers):
-        pool = layer_pool([L["values"][0], L["masks"][0]], L["bytes"])
-        argsets = [(p[0].data_ptr(), p[1].data_ptr(), L["x"].data_ptr(), L["y"].data_ptr(),
-                    L["R"], L["C"]) + bx + (L["N"], L["M"]) for p in pool]
-        per_s.append(per_launch_us(lambda c, sp, A=argsets: sp_fn(*A[c], sp), len(pool), L_PL))
-        del pool
-    per_d = {}
-    for D in dense_list:
-        pool = layer_pool([D["W"][0]], D["bytes"])
-        argsets = [(p[0].data_ptr(), D["x"].data_ptr(), D["y"].data_ptr(), D["R"], D["C"]) + bx for p in pool]
-        per_d[(D["R"], D["C"])] = per_launch_us(lambda c, sp, A=argsets: dn_fn(*A[c], sp),
-                                                len(pool), L_PL)
-        del pool
-    torch.cuda.synchronize()
+    per_layer, per_s = per_layer_times(torch, nm, layers, dense, B, pool_bytes, L_PL,
+                                       ceiling=ceiling if B == 1 else None)
 
     value = step_sparse * K / (ms_s * 1e-3) / 1e9
     dense_gbps = step_dense * K / (ms_d * 1e-3) / 1e9
@@ -357,26 +509,12 @@ def main():
     log(f"sparse {value:.0f} GB/s ({value / HBM_PEAK_GBPS:.1%}), dense {dense_gbps:.0f} GB/s, "
         f"speedup {speedup:.3f}x, {ms_s / K * 1e3:.1f} us/step")
 
-    per_layer = []
     kern_bytes, kern_us, kern_n = {}, {}, {}
-    for i, L in enumerate(layers):
-        us = per_s[i]
-        kname = nm.spmv_variant(L["R"], L["C"], L["N"], L["M"]) if B == 1 else \
-            nm.spmm_variant(L["R"], L["C"], B, L["N"], L["M"])
+    for L, us, rec in zip(layers, per_s, per_layer):
+        kname = rec["kernel"]
         kern_bytes[kname] = kern_bytes.get(kname, 0) + L["bytes"]
         kern_us[kname] = kern_us.get(kname, 0.0) + us
         kern_n[kname] = kern_n.get(kname, 0) + 1
-        dus = per_d[(L["R"], L["C"])]
-        gbps = L["bytes"] / (us * 1e-6) / 1e9
-        ls = nm.spmv_launch_shape(L["R"], L["C"], L["N"], L["M"])
-        wg = {"workgroups": ls["workgroups"],
-              "workgroup": f"{ls['rows_per_workgroup']} rows, {ls['row_groups']}x{ls['waves_per_row_group']} waves"} \
-            if B == 1 else {}
-        per_layer.append({"layer": L["name"], "shape": f"{L['R']}x{L['C']}", "pattern": f"{L['N']}:{L['M']}",
-                          "kernel": kname, **wg,
-                          "us": round(us, 2), "GBps": round(gbps, 1),
-                          "pct_peak": round(gbps / HBM_PEAK_GBPS, 4),
-                          "dense_us": round(dus, 2), "speedup": round(dus / us, 3)})
     dominant = max(kern_us, key=lambda k: kern_us[k])
     achieved = kern_bytes[dominant] / (kern_us[dominant] * 1e-6) / 1e9
     traffic = read_traffic(dominant)
@@ -385,11 +523,48 @@ def main():
                 "kernel": dominant, "launches_per_step": kern_n[dominant],
                 "bytes_per_launch": kern_bytes[dominant] / kern_n[dominant],
                 "avg_launch_us": round(kern_us[dominant] / kern_n[dominant], 3)}
+    if B == 1:
+        att = sum(r["attainable_us"] for r in per_layer if r["kernel"] == dominant)
+        roofline["frac_of_attainable"] = round(att / kern_us[dominant], 4)
+
+    # ------------------------------------------------------------------ the other 2:4 layers
+    more = []
+    if extra:
+        for L in layers:   # the step's pools are no longer needed
+            del L["values"][1:], L["masks"][1:]
+        for D in dense.values():
+            del D["W"][1:]
+        torch.cuda.empty_cache()
+        t_gen = time.time()
+        wl70 = synth.WORKLOADS[4]
+        l70, d70 = make_layers(torch, nm, synth, dev, 4, list(enumerate(wl70["layers"])), [(2, 4)], 1,
+                               args.cpu_rows_frac, keep_cpu=False)
+        log(f"llama3.3-70b 2:4 layers generated and packed in {time.time() - t_gen:.1f}s")
+        L70 = max(40, max(pool_copies(L["bytes"], pool_bytes) for L in l70))
+        more, _ = per_layer_times(torch, nm, l70, d70, 1, pool_bytes, L70, ceiling=ceiling, tag=wl70["name"])
+        del l70, d70
+        # one GPU's share of the 70B MLP split over 8 GPUs (rows of gate/up, columns of down)
+        shards = list(enumerate(synth.LLAMA33_70B_TP8_SHARDS, start=len(wl70["layers"])))
+        lsh, dsh = make_layers(torch, nm, synth, dev, 4, shards, [(2, 4)], 1, args.cpu_rows_frac, keep_cpu=False)
+        Lsh = max(40, max(pool_copies(L["bytes"], pool_bytes) for L in lsh))
+        more += per_layer_times(torch, nm, lsh, dsh, 1, pool_bytes, Lsh, ceiling=ceiling,
+                                tag="llama3.3-70b-mlp-8-way-shard")[0]
+        del lsh, dsh
+        torch.cuda.empty_cache()
+    ceiling.release()
 
     # ------------------------------------------------------------------ CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline and B == 1:
         cpu = cpu_baseline(layers, args.cpu_rows_frac)
+    decode = None
+    if extra:
+        for L in layers:
+            L["values"], L["masks"], L["W_cpu"] = None, None, None
+        dense.clear()
+        torch.cuda.empty_cache()
+        decode = decode_sweep(args, torch, nm, synth, dev, args.tokens, max(1, min(args.warmup, 5)),
+                              with_cpu=not args.no_cpu_baseline)
 
     out = {
         "metric": METRIC,
@@ -424,27 +599,33 @@ def main():
         "wall_s_sparse": round(wall_s, 4),
         "timing": "value: K steps in one HIP graph replayed between events; per_layer: each layer "
                   "alone, the same number of launches for every layer cycling over its own >= 1 GiB "
-                  "rotation, in a graph, median of 5 replays",
-        "per_layer": per_layer,
+                  "rotation, in a graph, median of 5 replays; attainable_us: the fastest shape of the "
+                  "read probe reading the layer's bytes in one launch, timed the same way",
+        "per_layer": per_layer + more,
+        "pattern_spread": pattern_spread(per_layer),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(out), flush=True)
+    if decode is not None:
+        out["decode"] = decode
+    sys.exit(emit(out))
 
 
-def decode_main(args, torch, nm, synth, dev):
+def decode_sweep(args, torch, nm, synth, dev, K, Wm, with_cpu=True):
     """The Llama-3.1-8B decode sweep: 32 transformer blocks x 7 projections (q, k, v, o,
     gate, up, down), 2:4, every projection with its own seeded W and x; a step is one
     token, i.e. one in-order pass over the 224 products. Also timed: the dense GEMV over
-    the same 224 weights, and the same sweep with q/k/v and gate/up each fused into one
-    product over their concatenated rows (the rows of a packed matrix concatenate as they
-    are; the fused product uses the x of q, resp. gate), timed against the dense GEMV fused
-    the same way."""
+    the same 224 weights, and two sweeps in which q/k/v and gate/up read one x, as they do
+    in the model (the x of q, resp. gate): fused into one product over their concatenated
+    rows (against the dense GEMV fused the same way), and grouped from their separate
+    matrices (nm_spmv_group). Each sweep writes its own outputs, and each is checked against
+    the oracle on the x it used, in the first and the last block."""
     wl = synth.WORKLOADS[5]
     NB, (N, M) = wl["n_layers"], tuple(wl["patterns"][0])
     lib = nm.lib()
     t_gen = time.time()
-    sp, dn, cpu_layers = [], [], []
+    check_blocks = (0, NB - 1)
+    sp, dn, host = [], [], {}
     for b in range(NB):
         for p, (name, R, C) in enumerate(wl["layers"]):
             W = synth.weight(R, C, synth.decode_seed(b, p))
@@ -452,31 +633,33 @@ def decode_main(args, torch, nm, synth, dev):
             Wd = torch.from_numpy(W).to(dev)
             xd = torch.from_numpy(x).to(dev)
             values, masks = nm.nm_pack(Wd, N, M)
-            y = torch.empty(R, dtype=torch.float16, device=dev)
-            sp.append(dict(name=name, block=b, R=R, C=C, values=values, masks=masks, x=xd, y=y,
+            sp.append(dict(name=name, block=b, R=R, C=C, values=values, masks=masks, x=xd,
+                           y=torch.empty(R, dtype=torch.float16, device=dev),    # plain sweep
+                           yg=torch.empty(R, dtype=torch.float16, device=dev),   # grouped sweep
                            bytes=alg_bytes_sparse(R, C, N, M)))
             dn.append(dict(R=R, C=C, W=Wd, x=xd, y=torch.empty(R, dtype=torch.float16, device=dev),
                            bytes=alg_bytes_dense(R, C)))
-            if b == 0:
-                cpu_layers.append(dict(name=name, R=R, C=C, N=N, M=M, x_host=x, y=y,
-                                       W_cpu=W[:max(1, int(math.ceil(R * args.cpu_rows_frac)))].copy()))
+            if b in check_blocks:
+                host[(b, p)] = (W, x)
             del W
-    # fused q/k/v and gate/up of every block, sparse and dense alike
+    # which projection's x each projection reads when q/k/v and gate/up share theirs
+    shared_x = {0: 0, 1: 0, 2: 0, 3: 3, 4: 4, 5: 4, 6: 6}
+    groups = ((0, 1, 2), (3,), (4, 5), (6,))
     fused, fused_dn = [], []
     for b in range(NB):
         blk = sp[7 * b:7 * b + 7]
-        for idx, xsrc in (((0, 1, 2), 0), ((3,), 3), ((4, 5), 4), ((6,), 6)):
+        for idx in groups:
             parts = [blk[i] for i in idx]
             R = sum(q["R"] for q in parts)
             C = parts[0]["C"]
             v = torch.cat([q["values"] for q in parts]) if len(parts) > 1 else parts[0]["values"]
             m = torch.cat([q["masks"] for q in parts]) if len(parts) > 1 else parts[0]["masks"]
-            fused.append(dict(R=R, C=C, values=v, masks=m, x=blk[xsrc]["x"],
+            fused.append(dict(block=b, idx=idx, R=R, C=C, values=v, masks=m, x=blk[idx[0]]["x"],
                               y=torch.empty(R, dtype=torch.float16, device=dev),
                               bytes=alg_bytes_sparse(R, C, N, M)))
             dparts = [dn[7 * b + i] for i in idx]
             Wf = torch.cat([q["W"] for q in dparts]) if len(dparts) > 1 else dparts[0]["W"]
-            fused_dn.append(dict(R=R, C=C, W=Wf, x=blk[xsrc]["x"],
+            fused_dn.append(dict(R=R, C=C, W=Wf, x=blk[idx[0]]["x"],
                                  y=torch.empty(R, dtype=torch.float16, device=dev),
                                  bytes=alg_bytes_dense(R, C)))
     torch.cuda.synchronize()
@@ -486,6 +669,7 @@ def decode_main(args, torch, nm, synth, dev):
         return [(q["values"].data_ptr(), q["masks"].data_ptr(), q["x"].data_ptr(), q["y"].data_ptr(),
                  q["R"], q["C"], N, M) for q in items]
     sp_a, fu_a = sp_launches(sp), sp_launches(fused)
+
     def dn_launches(items):
         return [(q["W"].data_ptr(), q["x"].data_ptr(), q["y"].data_ptr(), q["R"], q["C"]) for q in items]
     dn_a, fdn_a = dn_launches(dn), dn_launches(fused_dn)
@@ -506,7 +690,7 @@ def decode_main(args, torch, nm, synth, dev):
                     raise RuntimeError(f"nm_gemv_dense: {nm.status_string(st)}")
         return run
 
-    def timed_tokens(fn, K, W_):
+    def timed_tokens(fn, K_, W_):
         s_ = torch.cuda.current_stream(dev).cuda_stream
         for _ in range(W_):
             fn(s_)
@@ -514,7 +698,7 @@ def decode_main(args, torch, nm, synth, dev):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             cs = torch.cuda.current_stream().cuda_stream
-            for _ in range(K):
+            for _ in range(K_):
                 fn(cs)
         g.replay()
         torch.cuda.synchronize()
@@ -525,24 +709,22 @@ def decode_main(args, torch, nm, synth, dev):
             g.replay()
             b_.record()
             torch.cuda.synchronize()
-            ts.append(a_.elapsed_time(b_) / K)
+            ts.append(a_.elapsed_time(b_) / K_)
         del g
         return statistics.median(ts)
 
-    # q/k/v and gate/up as groups of their separate matrices (nm_spmv_group, one launch each)
-    def group_launches():
-        out = []
-        for b in range(NB):
-            blk = sp[7 * b:7 * b + 7]
-            for idx in ((0, 1, 2), (3,), (4, 5), (6,)):
-                parts = [blk[i] for i in idx]
-                n = len(parts)
-                out.append((n, (ctypes.c_void_p * n)(*[q["values"].data_ptr() for q in parts]),
-                            (ctypes.c_void_p * n)(*[q["masks"].data_ptr() for q in parts]),
-                            parts[0]["x"].data_ptr(), (ctypes.c_void_p * n)(*[q["y"].data_ptr() for q in parts]),
-                            (ctypes.c_int64 * n)(*[q["R"] for q in parts]), parts[0]["C"]))
-        return out
-    gr_a = group_launches()
+    # q/k/v and gate/up as groups of their separate matrices (nm_spmv_group, one launch each),
+    # writing the grouped outputs
+    gr_a = []
+    for b in range(NB):
+        blk = sp[7 * b:7 * b + 7]
+        for idx in groups:
+            parts = [blk[i] for i in idx]
+            n = len(parts)
+            gr_a.append((n, (ctypes.c_void_p * n)(*[q["values"].data_ptr() for q in parts]),
+                         (ctypes.c_void_p * n)(*[q["masks"].data_ptr() for q in parts]),
+                         parts[0]["x"].data_ptr(), (ctypes.c_void_p * n)(*[q["yg"].data_ptr() for q in parts]),
+                         (ctypes.c_int64 * n)(*[q["R"] for q in parts]), parts[0]["C"]))
 
     def token_group(sp_):
         for n, v, m, x, y, r, c in gr_a:
@@ -550,57 +732,137 @@ def decode_main(args, torch, nm, synth, dev):
             if st:
                 raise RuntimeError(f"nm_spmv_group: {nm.status_string(st)}")
 
-    K, Wm = args.tokens, max(1, min(args.warmup, 5))
     ms_sp = timed_tokens(token_sparse(sp_a), K, Wm)
     ms_dn = timed_tokens(token_dense(dn_a), K, Wm)
     ms_fu = timed_tokens(token_sparse(fu_a), K, Wm)
     ms_fu_dn = timed_tokens(token_dense(fdn_a), K, Wm)
     ms_gr = timed_tokens(token_group, K, Wm)
+    torch.cuda.synchronize()
     bytes_tok = sum(q["bytes"] for q in sp)
     bytes_dn = sum(q["bytes"] for q in dn)
-    value = bytes_tok / (ms_sp * 1e-3) / 1e9
-    log(f"decode: sparse {ms_sp * 1e3:.1f} us/token ({value:.0f} GB/s), dense {ms_dn * 1e3:.1f} us/token, "
+    gbps = bytes_tok / (ms_sp * 1e-3) / 1e9
+    log(f"decode: sparse {ms_sp * 1e3:.1f} us/token ({gbps:.0f} GB/s), dense {ms_dn * 1e3:.1f} us/token, "
         f"speedup {ms_dn / ms_sp:.3f}x; fused q/k/v and gate/up: sparse {ms_fu * 1e3:.1f} us/token, "
         f"dense {ms_fu_dn * 1e3:.1f} us/token, speedup {ms_fu_dn / ms_fu:.3f}x; grouped (separate matrices): "
         f"sparse {ms_gr * 1e3:.1f} us/token")
-    cpu = None if args.no_cpu_baseline else cpu_baseline(cpu_layers, args.cpu_rows_frac)
+
+    # ---------------------------------------------------------------- parity (untimed)
+    # outputs of the checked blocks as the three sweeps left them
+    outs = {"plain": {}, "grouped": {}, "fused": {}}
+    for b in check_blocks:
+        for p in range(7):
+            q = sp[7 * b + p]
+            outs["plain"][(b, p)] = q["y"].cpu().numpy()
+            outs["grouped"][(b, p)] = q["yg"].cpu().numpy()
+        for f in fused[4 * b:4 * b + 4]:
+            yf = f["y"].cpu().numpy()
+            r0 = 0
+            for p in f["idx"]:
+                R = sp[7 * b + p]["R"]
+                outs["fused"][(b, p)] = yf[r0:r0 + R]
+                r0 += R
+    own = {k: host[k][1] for k in host}
+    shared = {(b, p): host[(b, shared_x[p])][1] for (b, p) in host}
+    parity = {"plain": oracle_parity(host, own, outs["plain"], N, M),
+              "grouped": oracle_parity(host, shared, outs["grouped"], N, M),
+              "fused": oracle_parity(host, shared, outs["fused"], N, M)}
+    for k, v in parity.items():
+        v["blocks"] = list(check_blocks)
+    log("decode parity: " + ", ".join(f"{k} max_err/bound {v['max_err_over_bound']:.3f} ok={v['ok']}"
+                                      for k, v in parity.items()))
+    cpu = None
+    if with_cpu:
+        cpu_layers = [dict(name=wl["layers"][p][0], R=wl["layers"][p][1], C=wl["layers"][p][2], N=N, M=M,
+                           x_host=host[(0, p)][1], y=sp[p]["y"], W_cpu=host[(0, p)][0]) for p in range(7)]
+        cpu = cpu_baseline(cpu_layers, 1.0)
+    return {
+        "workload": f"{wl['name']}: {NB} blocks x 7 Llama-3.1-8B projections, 2:4, batch 1, a fresh seeded W "
+                    f"and x per projection; a step is one token (224 products in order)",
+        "us_per_token": round(ms_sp * 1e3, 2),
+        "GBps": round(gbps, 1),
+        "pct_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "bytes_per_token": bytes_tok,
+        "dense_us_per_token": round(ms_dn * 1e3, 2),
+        "dense_GBps": round(bytes_dn / (ms_dn * 1e-3) / 1e9, 1),
+        "speedup_vs_dense": round(ms_dn / ms_sp, 3),
+        "fused_qkv_gateup": {"us_per_token": round(ms_fu * 1e3, 2), "launches_per_token": len(fused) // NB,
+                             "GBps": round(sum(q["bytes"] for q in fused) / (ms_fu * 1e-3) / 1e9, 1),
+                             "dense_us_per_token": round(ms_fu_dn * 1e3, 2),
+                             "dense_GBps": round(sum(q["bytes"] for q in fused_dn) / (ms_fu_dn * 1e-3) / 1e9, 1),
+                             "speedup_vs_fused_dense": round(ms_fu_dn / ms_fu, 3),
+                             "x": "q, k, v read the x of q; gate, up the x of gate (concatenated rows)"},
+        "grouped_qkv_gateup": {"us_per_token": round(ms_gr * 1e3, 2), "launches_per_token": len(gr_a) // NB,
+                               "GBps": round(bytes_tok / (ms_gr * 1e-3) / 1e9, 1),
+                               "speedup_vs_fused_dense": round(ms_fu_dn / ms_gr, 3),
+                               "x": "q, k, v read the x of q; gate, up the x of gate (nm_spmv_group over the "
+                                    "separate matrices)"},
+        "byte_floor_us_per_token_at_8TBps": round(bytes_tok / 8e12 * 1e6, 1),
+        "timing": "K tokens in one HIP graph replayed between events, median of 3 replays",
+        "parity": parity,
+        "roofline": decode_roofline(nm, sp, ms_sp, N, M),
+        "cpu_baseline": cpu,
+    }
+
+
+def oracle_parity(host, xs, ys, N, M) -> dict:
+    """Each GPU output ys[k] against the oracle (pack, then densify + fp64 matvec) of the
+    weights host[k][0] on the x it used, xs[k]; rows in chunks over the host cores."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(16, cores))
+
+    def one(k):
+        W = host[k][0]
+        x = xs[k]
+        refs = []
+        for a in range(0, W.shape[0], 512):
+            rv, rm = oracle.pack_ref(W[a:a + 512], N, M)
+            refs.append(oracle.spmv_ref(rv, rm, x, W.shape[1], N, M))
+        return k, np.concatenate(refs)
+
+    worst, rel, rows = 0.0, 0.0, 0
+    finite = True
+    with ThreadPoolExecutor(cores) as ex:
+        for k, ref in ex.map(one, sorted(ys)):
+            rep = oracle.y_tolerance_report(ys[k], ref)
+            worst = max(worst, rep["max_err_over_bound"])
+            rel = max(rel, rep["rel_l2"])
+            finite = finite and rep["finite"]
+            rows += ref.shape[0]
+    return {"max_err_over_bound": worst, "rel_l2": rel, "rows": rows,
+            "ok": bool(finite and worst <= 1.0 and rel <= 1e-3)}
+
+
+def decode_main(args, torch, nm, synth, dev) -> int:
+    """--workload decode: the decode sweep as the line's own workload."""
+    K, Wm = args.tokens, max(1, min(args.warmup, 5))
+    d = decode_sweep(args, torch, nm, synth, dev, K, Wm, with_cpu=not args.no_cpu_baseline)
     out = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": d["GBps"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": Wm,
-        "ms_per_step": round(ms_sp, 5),
+        "ms_per_step": round(d["us_per_token"] * 1e-3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "accumulate": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{wl['name']}: {NB} blocks x 7 Llama-3.1-8B projections, 2:4, batch 1, "
-                               f"a fresh seeded W and x per projection; a step is one token (224 products in order)",
-                   "bytes_per_step": bytes_tok, "parallelism": "single GPU"},
-        "pct_of_peak": round(value / HBM_PEAK_GBPS, 4),
-        "us_per_token": round(ms_sp * 1e3, 2),
-        "dense_us_per_token": round(ms_dn * 1e3, 2),
-        "dense_GBps": round(bytes_dn / (ms_dn * 1e-3) / 1e9, 1),
-        "speedup_vs_dense": round(ms_dn / ms_sp, 3),
-        "fused_qkv_gateup": {"us_per_token": round(ms_fu * 1e3, 2), "launches_per_token": len(fused) // NB * NB,
-                             "GBps": round(sum(q["bytes"] for q in fused) / (ms_fu * 1e-3) / 1e9, 1),
-                             "dense_us_per_token": round(ms_fu_dn * 1e3, 2),
-                             "dense_GBps": round(sum(q["bytes"] for q in fused_dn) / (ms_fu_dn * 1e-3) / 1e9, 1),
-                             "speedup_vs_fused_dense": round(ms_fu_dn / ms_fu, 3)},
-        "grouped_qkv_gateup": {"us_per_token": round(ms_gr * 1e3, 2), "launches_per_token": len(gr_a) // NB * NB,
-                               "GBps": round(bytes_tok / (ms_gr * 1e-3) / 1e9, 1),
-                               "speedup_vs_fused_dense": round(ms_fu_dn / ms_gr, 3),
-                               "note": "q/k/v and gate/up through nm_spmv_group from their separate matrices"},
-        "byte_floor_us_per_token_at_8TBps": round(bytes_tok / 8e12 * 1e6, 1),
-        "timing": "K tokens in one HIP graph replayed between events, median of 3 replays",
-        "roofline": decode_roofline(nm, sp, ms_sp, N, M),
-        "cpu_baseline": cpu,
+        "config": {"workload": d["workload"], "bytes_per_step": d["bytes_per_token"], "parallelism": "single GPU"},
+        "roofline": d["roofline"],
+        "cpu_baseline": d["cpu_baseline"],
+        "decode": {k: v for k, v in d.items() if k not in ("roofline", "cpu_baseline", "workload")},
     }
-    print(json.dumps(out), flush=True)
+    return emit(out)
 
 
 def decode_roofline(nm, items, ms_token, N, M):
@@ -780,7 +1042,7 @@ def prefill_main(args, torch, nm, synth, dev):
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(out), flush=True)
+    return emit(out)
 
 
 def _rows_phrase(frac):

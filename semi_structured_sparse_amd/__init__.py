@@ -53,6 +53,8 @@ SIGNATURES = {
     "nm_spmv_launch_shape": (_c.c_int, [_c.c_int64, _c.c_int64, _c.c_int, _c.c_int,
                                         _c.POINTER(_c.c_int64)]),
     "nm_probe_read": (_c.c_int, [_c.c_void_p, _c.c_size_t, _c.c_void_p, _c.c_uint32, _c.c_void_p]),
+    "nm_probe_read_shaped": (_c.c_int, [_c.c_void_p, _c.c_size_t, _c.c_void_p, _c.c_uint32, _c.c_int, _c.c_int,
+                                        _c.c_int, _c.c_int, _c.c_void_p]),
     "nm_probe_copy": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
 }
 

@@ -163,7 +163,7 @@ __device__ __forceinline__ void gather_bits(uint32_t bits, uint32_t xw, int step
 
 // Byte-LUT gather for 4:8 and 8:16: the half-word's two mask bytes give their set-bit
 // offsets from the tables (one 64-bit LDS read each); the two lists are concatenated with
-// one 64-bit shift by 8 * popcount(low byte) (for 4:8 the low byte always holds 4); byte k
+// one 64-bit shift by 8 * popcount(low byte), modulo 64 (for 4:8 the low byte always holds 4); byte k
 // of the result is the offset of value k from xh, the half-word's x window.
 template <int N>
 __device__ __forceinline__ void gather_lut(uint32_t m, uint32_t sh16, uint32_t lut, uint32_t xh,
@@ -177,8 +177,11 @@ __device__ __forceinline__ void gather_lut(uint32_t m, uint32_t sh16, uint32_t l
     lo = l0.x;
     hi = l1.x;
   } else {
-    const uint64_t q = (uint64_t(l0.y) << 32 | l0.x) |
-                       ((uint64_t(l1.y) << 32 | l1.x) << (8u * uint32_t(__builtin_popcount(b0))));
+    // A valid half-word keeps 8 values, so when the low byte keeps all 8 (a shift of 64) the
+    // high byte keeps none and its list is 0: the shift amount is taken modulo 64, which keeps
+    // the shift defined and leaves the result unchanged.
+    const uint32_t shift = (8u * uint32_t(__builtin_popcount(b0))) & 63u;
+    const uint64_t q = (uint64_t(l0.y) << 32 | l0.x) | ((uint64_t(l1.y) << 32 | l1.x) << shift);
     lo = uint32_t(q);
     hi = uint32_t(q >> 32);
   }

@@ -43,6 +43,9 @@ QWEN3 = [("q14b_proj", 5120, 5120), ("kv_proj", 1024, 5120),
          ("down32b_proj", 5120, 25600)]
 LLAMA33_70B = [("qo_proj", 8192, 8192), ("kv_proj", 1024, 8192),
                ("gate_up_proj", 28672, 8192), ("down_proj", 8192, 28672)]
+# One GPU's share of the Llama-3.3-70B MLP split 8 ways: the gate/up rows (28672 / 8) and
+# the down projection's columns (28672 / 8, whole 32-column mask words).
+LLAMA33_70B_TP8_SHARDS = [("gate_up_rows_1of8", 3584, 8192), ("down_cols_1of8", 8192, 3584)]
 LLAMA31_8B_DECODE_LAYER = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096),
                            ("o", 4096, 4096), ("gate", 14336, 4096), ("up", 14336, 4096),
                            ("down", 4096, 14336)]

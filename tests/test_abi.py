@@ -165,6 +165,15 @@ def test_probe_validation():
     assert L.nm_probe_read(A16 + 8, 16, A16, 0, None) == nm.NM_ERR_ALIGN
     assert L.nm_probe_copy(A16, None, 16, None) == nm.NM_ERR_NULL
     assert L.nm_probe_copy(A16 + 4, A16, 16, None) == nm.NM_ERR_ALIGN
+    # the shaped read: every launch-shape argument outside its range is rejected
+    rs = L.nm_probe_read_shaped
+    assert rs(None, 16, A16, 0, 256, 512, 4, 0, None) == nm.NM_ERR_NULL
+    assert rs(A16, 0, A16, 0, 256, 512, 4, 0, None) == nm.NM_ERR_SHAPE
+    assert rs(A16 + 8, 16, A16, 0, 256, 512, 4, 0, None) == nm.NM_ERR_ALIGN
+    for blocks, threads, unroll, blocked in ((0, 512, 4, 0), ((1 << 20) + 1, 512, 4, 0), (256, 32, 4, 0),
+                                             (256, 1088, 4, 0), (256, 500, 4, 0), (256, 512, 3, 0),
+                                             (256, 512, 16, 0), (256, 512, 4, 2), (256, 512, 4, -1)):
+        assert rs(A16, 16, A16, 0, blocks, threads, unroll, blocked, None) == nm.NM_ERR_SHAPE
 
 
 @pytest.mark.parametrize("kw,want", [

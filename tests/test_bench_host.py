@@ -67,3 +67,46 @@ def test_decode_roofline():
     assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["traffic"] is None
     two = _Variants({(4096, 4096): "k", (1024, 4096): "other"})
     assert bench.decode_roofline(two, items, ms_token=0.01, N=2, M=4) is None
+
+
+def test_parity_gate_finds_every_failed_record(capsys):
+    """Any parity record (a dict under a key starting with "parity") whose ok is false, at any
+    depth, fails the run: the JSON line is still printed, and the exit status is 3."""
+    good = {"max_err_over_bound": 0.05, "rel_l2": 2e-4, "ok": True}
+    bad = {"max_err_over_bound": 1703.5, "rel_l2": 1.45, "ok": False}
+    out = {"value": 1.0, "cpu_baseline": {"parity_vs_gpu": dict(good)},
+           "decode": {"parity": {"plain": dict(good), "grouped": dict(bad), "fused": dict(good)},
+                      "cpu_baseline": {"parity_vs_gpu": dict(good)}},
+           "per_layer": [{"parity_rows": dict(bad)}]}
+    assert bench.parity_failures(out) == ["decode.parity.grouped", "per_layer[0].parity_rows"]
+    assert bench.emit(out) == 3
+    line = capsys.readouterr().out.strip()
+    assert '"parity_ok": false' in line and line.startswith("{")
+    out["decode"]["parity"]["grouped"] = dict(good)
+    out["per_layer"] = []
+    assert bench.parity_failures(out) == []
+    assert bench.emit(out) == 0
+    assert '"parity_ok": true' in capsys.readouterr().out
+    # a record with no verdict, or a non-parity "ok", is not a failure
+    assert bench.parity_failures({"parity": {"rows": 3}, "status": {"ok": False}}) == []
+
+
+def test_pattern_spread():
+    per_layer = [
+        {"shape": "4096x4096", "pattern": "2:4", "us": 5.0},
+        {"shape": "4096x4096", "pattern": "16:32", "us": 5.5},
+        {"shape": "4096x4096", "pattern": "4:8", "us": 5.2},
+        {"shape": "1024x4096", "pattern": "2:4", "us": 3.0},
+        {"shape": "28672x8192", "pattern": "2:4", "us": 39.0, "in_step": False},
+        {"shape": "28672x8192", "pattern": "16:32", "us": 45.0, "in_step": False},
+    ]
+    s = bench.pattern_spread(per_layer)
+    assert set(s) == {"4096x4096"}   # one pattern only, or outside the step: no spread
+    assert abs(s["4096x4096"]["spread"] - 0.1) < 1e-9
+    assert s["4096x4096"]["fastest"] == "2:4" and s["4096x4096"]["slowest"] == "16:32"
+
+
+def test_pool_copies():
+    assert bench.pool_copies(600e6, 1 << 30) == 2
+    assert bench.pool_copies(4.7e6, 1 << 30) == 229
+    assert bench.pool_copies(3e9, 1 << 30) == 2

@@ -179,6 +179,32 @@ def test_unit_sum_closed_form(N, M):
     assert np.all(down_u32(masks) == {2: 0x33333333, 4: 0x0F0F0F0F, 8: 0x00FF00FF, 16: 0x0000FFFF}[N])
 
 
+@pytest.mark.parametrize("N,M", PATTERNS)
+def test_whole_byte_halves(N, M):
+    """Groups whose kept values all sit in one byte of a mask half-word: magnitudes rising or
+    falling across each group of M, chosen at random per group, so that 8:16 half-words read
+    0xFF/0x00 and 0x00/0xFF (the byte-table decoder's shift of 64 and of 0) in every mix."""
+    R, C = 64, 4096
+    rng = np.random.default_rng(4242)
+    ramp = (np.arange(1, M + 1, dtype=np.float32) / M) * 0.05
+    W = np.empty((R, C), np.float32)
+    for g in range(C // M):
+        rise = rng.integers(0, 2, size=R).astype(bool)
+        mags = np.where(rise[:, None], ramp[None, :], ramp[None, ::-1])
+        W[:, g * M:(g + 1) * M] = mags * rng.choice([-1.0, 1.0], size=(R, M))
+    W = W.astype(np.float16)
+    x = synth.activation(C, seed=4243)
+    values, masks = nm.nm_pack(up_f16(W), N, M)
+    rv, rm = oracle.pack_ref(W, N, M)
+    assert np.array_equal(down_bits16(values), rv) and np.array_equal(down_u32(masks), rm)
+    if N == 8:
+        halves = np.concatenate([rm & 0xFFFF, rm >> 16]).ravel()
+        assert {0x00FF, 0xFF00} <= set(halves.tolist())
+    y = down_f16(nm.nm_spmv(values, masks, up_f16(x), N, M))
+    rep = oracle.y_tolerance_report(y, oracle.spmv_ref(rv, rm, x, C, N, M))
+    assert rep["ok"], rep
+
+
 def test_cross_path_sparse_vs_dense_of_pruned():
     R, C = 300, 4096
     W = synth.weight(R, C, seed=730)
