@@ -93,3 +93,41 @@ def check_full_layer(W_host: np.ndarray, x_host: np.ndarray, N: int, M: int, tag
         out["dense"] = drep
     del Wd, values, masks, y, yd
     return out
+
+
+def check_all_rows(W_host: np.ndarray, x_host: np.ndarray, N: int, M: int, tag: str, chunk: int = 512) -> dict:
+    """Pack on the GPU and run the sparse product, then compare EVERY row with the oracle:
+    values and masks bit-exact, y within tolerance. The oracle runs on chunks of rows over a
+    pool of host threads (numpy releases the interpreter lock in its array operations)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    rows, cols = W_host.shape
+    Wd = up_f16(W_host)
+    values, masks = nm.nm_pack(Wd, N, M)
+    y = nm.nm_spmv(values, masks, up_f16(x_host), N, M)
+    torch.cuda.synchronize()
+    del Wd
+    gv, gm, gy = down_bits16(values), down_u32(masks), down_f16(y)
+    del values, masks, y
+
+    def one(a):
+        b = min(rows, a + chunk)
+        rv, rm = oracle.pack_ref(W_host[a:b], N, M)
+        bad = int(np.count_nonzero(gv[a:b] != rv)) + int(np.count_nonzero(gm[a:b] != rm))
+        return a, bad, oracle.spmv_ref(rv, rm, x_host, cols, N, M)
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    ref = np.empty(rows, np.float64)
+    mismatches = 0
+    with ThreadPoolExecutor(max(1, min(16, cores))) as ex:
+        for a, bad, r in ex.map(one, range(0, rows, chunk)):
+            mismatches += bad
+            ref[a:a + r.shape[0]] = r
+    assert mismatches == 0, f"{tag}: {mismatches} packed words/values differ from the oracle"
+    rep = oracle.y_tolerance_report(gy, ref)
+    assert rep["ok"], f"{tag}: spmv {rep}"
+    return rep
