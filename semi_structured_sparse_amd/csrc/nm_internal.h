@@ -100,12 +100,17 @@ bool skinny_fits(int64_t rows, int64_t cols, int64_t tokens, int n, int m, const
 hipError_t launch_skinny_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
                               int64_t rows, int64_t cols, int tokens, int n, int m, hipStream_t stream,
                               const DeviceInfo& dev);
-// nm_spmm runs the skinny kernel, kSkinnyBatch vectors per launch, on layers of at least
-// kSkinnyMinRows rows from kSkinnyMinBatch vectors up to kMatrixCoreMinBatch, where the
-// prefill kernels take over (measured on MI355X: from 5 vectors on it beats the small-batch
-// kernel on such layers; on smaller ones its fixed cost of a few microseconds does not pay).
+// nm_spmm runs the skinny kernel, kSkinnyBatch vectors per launch, from kSkinnyMinBatch
+// vectors up to kMatrixCoreMinBatch, where the prefill kernels take over: on layers of at
+// least kSkinnyMinRows rows for 2:4, 4:8 and 8:16; on smaller layers (down to
+// kSkinnySmallMinRows rows) for 2:4, and for the split 4:8 / 8:16 from 9 vectors (at most
+// 5120 columns) or 12. Measured on MI355X over 256..1536 rows x 4096..8192 columns at 5..16
+// vectors: there the skinny kernel's fixed cost (about 6 us) is below the small-batch
+// kernel's time for 2:4 at every batch (1024 x 4096 at 8 vectors: 6.7 against 8.0 us), and
+// for the split patterns once the small-batch kernel needs a second pass of 8 vectors.
 constexpr int64_t kSkinnyMinBatch = 5;
 constexpr int64_t kSkinnyMinRows = 2048;
+constexpr int64_t kSkinnySmallMinRows = 256;
 constexpr int64_t kSkinnyBatch = 16;
 bool use_skinny(int64_t rows, int64_t cols, int64_t batch, int n, int m, const DeviceInfo& dev);
 const char* skinny_variant(int n);

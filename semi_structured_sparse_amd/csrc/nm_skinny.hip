@@ -54,9 +54,11 @@ bool skinny_fits(int64_t rows, int64_t cols, int64_t tokens, int n, int m, const
 }
 
 bool use_skinny(int64_t rows, int64_t cols, int64_t batch, int n, int m, const DeviceInfo& dev) {
-  if (batch < kSkinnyMinBatch || rows < kSkinnyMinRows || !skinny_fits(rows, cols, kSkinnyBatch, n, m, dev))
+  if (batch < kSkinnyMinBatch || batch >= kMatrixCoreMinBatch)   // beyond: the prefill kernels
     return false;
-  return batch < kMatrixCoreMinBatch;   // beyond: the prefill kernels
+  if (rows < kSkinnySmallMinRows || !skinny_fits(rows, cols, kSkinnyBatch, n, m, dev)) return false;
+  if (rows >= kSkinnyMinRows || n == 2) return true;
+  return batch >= 12 || (batch >= 9 && cols <= 5120);   // the split patterns on smaller layers
 }
 
 const char* skinny_variant(int n) { return n == 2 ? "skinny_spmm_kernel<1, false>" : "skinny_spmm_kernel<1, true>"; }

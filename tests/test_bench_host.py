@@ -110,3 +110,9 @@ def test_pool_copies():
     assert bench.pool_copies(600e6, 1 << 30) == 2
     assert bench.pool_copies(4.7e6, 1 << 30) == 229
     assert bench.pool_copies(3e9, 1 << 30) == 2
+
+
+def test_best_dense_is_the_faster_of_ours_and_the_vendor_blas():
+    assert bench.best_dense_us(299.5, 206.3) == 206.3
+    assert bench.best_dense_us(80.2, 84.1) == 80.2
+    assert bench.best_dense_us(80.2, float("nan")) == 80.2

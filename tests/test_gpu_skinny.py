@@ -1,6 +1,7 @@
 """GPU parity tests of the small-batch 50% products on the sparse matrix instruction (nm_spmm
-on layers of at least 2048 rows: 2:4 with 5..31 vectors; 4:8 and 8:16, split into two 2:4
-operands, from 5 vectors on), through the C ABI, against the CPU oracle (spmm_ref).
+with 5..31 vectors: 2:4 on layers of at least 256 rows; 4:8 and 8:16, split into two 2:4
+operands, on layers of at least 2048 rows, and on smaller ones from 9 or 12 vectors), through
+the C ABI, against the CPU oracle (spmm_ref).
 
 Bars: Y within |y - ref| <= 2e-3 + 1e-2*|ref| per element and relative L2 <= 1e-3 (fp32
 accumulation in the matrix instruction, fp16 output, fp64 oracle); exact special cases
@@ -49,6 +50,19 @@ def test_skinny_parity(R, C, T, N, M):
     check(R, C, T, 3000 + R % 97 + C % 89 + T + N, N, M, sample_rows(R, k=32, rpb=16))
 
 
+# smaller layers (fewer than 2048 rows): ragged rows, a 32-column tail, one and two launches
+SMALL_CASES = [((2, 4), 256, 4096, 5), ((2, 4), 1024, 4096, 8), ((2, 4), 300, 1056, 6), ((2, 4), 1000, 8192, 17),
+               ((4, 8), 1024, 4096, 9), ((8, 16), 1030, 5120, 16), ((8, 16), 512, 8192, 12), ((4, 8), 777, 2080, 20)]
+
+
+@pytest.mark.parametrize("pat,R,C,T", SMALL_CASES)
+def test_skinny_small_layers(pat, R, C, T):
+    N, M = pat
+    assert nm.spmm_variant(R, C, T, N, M) == SKINNY[N]
+    say(f"skinny small {N}:{M} {R}x{C} vectors={T}")
+    check(R, C, T, 3100 + R % 97 + C % 89 + T + N, N, M)
+
+
 @pytest.mark.parametrize("N,M", [(4, 8), (8, 16)])
 def test_skinny_split_two_launches(N, M):
     """4:8 and 8:16 at 20 vectors: two launches of the split kernel (16, then a ragged 4)."""
@@ -59,12 +73,21 @@ def test_skinny_split_two_launches(N, M):
 
 
 def test_skinny_routing():
-    """Which kernel nm_spmm picks: the sparse matrix instruction on layers of >= 2048 rows for
-    2:4, 4:8 and 8:16 at 5..31 vectors; the small-batch kernel below 5 vectors, on smaller
-    layers and for 16:32; the prefill kernels from 32 vectors on."""
+    """Which kernel nm_spmm picks: the sparse matrix instruction at 5..31 vectors for 2:4 on
+    layers of >= 256 rows and for 4:8 and 8:16 on layers of >= 2048 rows (on smaller ones from
+    9 vectors up to 5120 columns, else from 12); the small-batch kernel below 5 vectors, on
+    smaller layers and for 16:32; the prefill kernels from 32 vectors on."""
     assert nm.spmm_variant(4096, 4096, 4, 2, 4) == "spmm_kernel<2, 4, 2>"
-    assert nm.spmm_variant(2047, 4096, 8, 2, 4) == "spmm_kernel<2, 8, 2>"
+    assert nm.spmm_variant(2047, 4096, 8, 2, 4) == SKINNY[2]
+    assert nm.spmm_variant(1024, 4096, 5, 2, 4) == SKINNY[2]
+    assert nm.spmm_variant(256, 8192, 8, 2, 4) == SKINNY[2]
+    assert nm.spmm_variant(255, 4096, 8, 2, 4) == "spmm_kernel<2, 8, 2>"
     assert nm.spmm_variant(2047, 4096, 8, 4, 8) == "spmm_kernel<4, 8, 2>"
+    assert nm.spmm_variant(1024, 4096, 9, 4, 8) == SKINNY[4]
+    assert nm.spmm_variant(1024, 5120, 9, 8, 16) == SKINNY[8]
+    assert nm.spmm_variant(1024, 8192, 9, 8, 16) == "spmm_kernel<8, 8, 2>"
+    assert nm.spmm_variant(1024, 8192, 12, 8, 16) == SKINNY[8]
+    assert nm.spmm_variant(1024, 4096, 16, 16, 32) == "spmm_kernel<16, 8, 0>"
     assert nm.spmm_variant(4096, 4096, 4, 8, 16) == "spmm_kernel<8, 4, 2>"
     assert nm.spmm_variant(4096, 4096, 20, 16, 32) == "spmm_kernel<16, 8, 0>"
     for N, M in PATTERNS:
