@@ -137,11 +137,10 @@ int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,
  * (row b of X is one activation vector: the layout of a batch of tokens). Products and
  * sums fp32, one RNE rounding, fixed summation order (bit-identical run to run).
  *   - batch >= 32 with 2:4, 4:8 or 8:16: nm_spmm_prefill (matrix cores), with its limits.
- *   - on layers of at least 2048 rows, 5 <= batch < 32 with 2:4, 4:8 or 8:16: the sparse
- *     matrix instruction with X staged in LDS, 16 vectors per launch (cols <= 2^21). 4:8
- *     and 8:16 keep 8 values in every 16 columns like 2:4, so each 4-column group is split
- *     into two 2:4 operands (its first two kept values and the rest) that go through the
- *     instruction with the same X.
+ *   - 5 <= batch < 32 where it was measured faster than the small-batch kernel (2:4 on
+ *     layers of at least 256 rows; 4:8 and 8:16 on layers of at least 2048 rows, and on
+ *     smaller ones from 9 or 12 vectors; 16:32 from 12 vectors on layers of at least 4096
+ *     rows and at most 4096 columns): nm_spmm_skinny.
  *   - otherwise the small-batch kernel (vector units; x staged in LDS in column phases
  *     when it does not fit at once, so any width is accepted), on consecutive groups of
  *     8 rows of X (one launch per group). batch == 1 gives the same result as nm_spmv
@@ -151,6 +150,19 @@ int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,
  * batch < 1 or above 2^24 is NM_ERR_SHAPE. */
 int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
             int64_t rows, int64_t cols, int64_t batch, int N, int M, void* stream);
+
+/* The batch product of nm_spmm on the matrix instructions for any batch >= 1, whatever
+ * nm_spmm's routing would pick (the same Y definition, summation in the instructions' fixed
+ * order, bit-identical run to run), for the 50% patterns: 2:4 on the 2:4 sparse instruction
+ * directly; 4:8 and 8:16 as two 2:4 operands per 4-column group (its first two kept values,
+ * and the rest); 16:32, whose 16 kept values may sit anywhere in a 32-column word, with each
+ * word's values expanded to dense 32-column fragments for the dense instruction. X is
+ * staged in LDS in column phases, 16 vectors per launch. Limits: cols <= 2^21, batch <= 2^24
+ * (NM_ERR_SHAPE beyond); other patterns are NM_ERR_PATTERN. Masks must be as nm_pack writes
+ * them; a malformed mask gives an unspecified Y but never an out-of-bounds access. values
+ * and X 16-byte aligned, masks 4-byte, Y 2-byte. Allocates nothing. */
+int nm_spmm_skinny(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
+                   int64_t rows, int64_t cols, int64_t batch, int N, int M, void* stream);
 
 /* Dense counterpart of nm_spmm, the same-GPU baseline of the batch product:
  * Y[b][r] = fp16( sum_c W[r][c] * X[b][c] ) with fp32 products and sums, fixed order.

@@ -39,6 +39,8 @@ SIGNATURES = {
                                  _c.c_void_p]),
     "nm_spmm": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
                            _c.c_int64, _c.c_int64, _c.c_int, _c.c_int, _c.c_void_p]),
+    "nm_spmm_skinny": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
+                                  _c.c_int64, _c.c_int64, _c.c_int, _c.c_int, _c.c_void_p]),
     "nm_gemm_dense": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
                                  _c.c_int64, _c.c_void_p]),
     "nm_spmm_prefill": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
@@ -339,6 +341,18 @@ def nm_spmm(values, masks, X, N: int, M: int, out=None):
         st = lib().nm_spmm(values.data_ptr(), masks.data_ptr(), X.data_ptr(), out.data_ptr(),
                            rows, cols, batch, N, M, _stream_ptr(X))
     _check("nm_spmm", st)
+    return out
+
+
+def nm_spmm_skinny(values, masks, X, N: int, M: int, out=None):
+    """nm_spmm's batch product on the matrix instructions for any batch and 50% pattern,
+    whatever nm_spmm would pick: X fp16 [batch, cols] -> Y fp16 [batch, rows]."""
+    torch = _torch()
+    rows, cols, batch, out = _batch_args(values, masks, X, N, M, out)
+    with torch.cuda.device(X.device):
+        st = lib().nm_spmm_skinny(values.data_ptr(), masks.data_ptr(), X.data_ptr(), out.data_ptr(),
+                                  rows, cols, batch, N, M, _stream_ptr(X))
+    _check("nm_spmm_skinny", st)
     return out
 
 

@@ -216,8 +216,8 @@ int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, ui
   if (e != hipSuccess) return nm::hip_fail(e);
   if (M != 2 * N && cols > nm::max_cols_for(dev)) return NM_ERR_TOO_WIDE;  // 25%: single-vector kernel only
   if (nm::use_skinny(rows, cols, batch, N, M, dev)) {
-    // 2:4, 4:8 and 8:16 at 5..31 vectors on a large layer: the sparse matrix instruction,
-    // 16 vectors per launch
+    // 50% patterns at 5..31 vectors where measured faster: the matrix instructions, 16
+    // vectors per launch
     for (int64_t b0 = 0; b0 < batch; b0 += nm::kSkinnyBatch) {
       const int nb = int(batch - b0 < nm::kSkinnyBatch ? batch - b0 : nm::kSkinnyBatch);
       e = nm::launch_skinny_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb, N, M,
@@ -226,12 +226,34 @@ int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, ui
     }
     return NM_OK;
   }
-  // otherwise (fewer vectors, smaller layers, 16:32): the small-batch kernel on consecutive
+  // otherwise (fewer vectors, smaller layers, most 16:32 shapes): the small-batch kernel on consecutive
   // groups of kSmallBatch rows of X (X and Y rows are contiguous)
   for (int64_t b0 = 0; b0 < batch; b0 += nm::kSmallBatch) {
     const int nb = int(batch - b0 < nm::kSmallBatch ? batch - b0 : nm::kSmallBatch);
     e = nm::launch_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb, N, M,
                         static_cast<hipStream_t>(stream), dev);
+    if (e != hipSuccess) return nm::hip_fail(e);
+  }
+  return NM_OK;
+}
+
+int nm_spmm_skinny(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
+                   int64_t rows, int64_t cols, int64_t batch, int N, int M, void* stream) {
+  if (!values || !masks || !X || !Y) return NM_ERR_NULL;
+  if (!nm::valid_shape(rows, cols) || batch < 1 || batch > nm::kPrefillMaxTokens || cols > nm::kPrefillMaxCols)
+    return NM_ERR_SHAPE;
+  if (!nm::skinny_pattern(N, M)) return NM_ERR_PATTERN;
+  if (!nm::aligned(values, 16) || !nm::aligned(masks, 4) || !nm::aligned(X, 16) || !nm::aligned(Y, 2))
+    return NM_ERR_ALIGN;
+  nm::DeviceInfo dev;
+  hipError_t e = nm::current_device_info(&dev);
+  if (e != hipSuccess) return nm::hip_fail(e);
+  const int64_t first = batch < nm::kSkinnyBatch ? batch : nm::kSkinnyBatch;
+  if (!nm::skinny_fits(rows, cols, first, N, M, dev)) return NM_ERR_SHAPE;
+  for (int64_t b0 = 0; b0 < batch; b0 += nm::kSkinnyBatch) {
+    const int nb = int(batch - b0 < nm::kSkinnyBatch ? batch - b0 : nm::kSkinnyBatch);
+    e = nm::launch_skinny_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb, N, M,
+                               static_cast<hipStream_t>(stream), dev);
     if (e != hipSuccess) return nm::hip_fail(e);
   }
   return NM_OK;

@@ -93,9 +93,12 @@ hipError_t launch_prefill_spmm(const uint16_t* values, const uint32_t* masks, co
                                const DeviceInfo& dev);
 hipError_t launch_prefill_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y, int64_t rows, int64_t cols,
                                int64_t tokens, hipStream_t stream, const DeviceInfo& dev);
-// Small-batch 50% product on the sparse matrix instruction, 1..16 tokens (X [tokens][cols],
-// Y [tokens][rows]): 2:4 directly, 4:8 and 8:16 split into two 2:4 operands. skinny_fits
-// tells whether a pattern and shape are within its limits.
+// Small-batch 50% product on the matrix instructions, 1..16 tokens (X [tokens][cols],
+// Y [tokens][rows]): 2:4 directly, 4:8 and 8:16 split into two 2:4 operands on the sparse
+// instruction, 16:32 expanded to dense fragments on the dense one. skinny_pattern tells
+// whether a pattern has this product; skinny_fits whether a pattern and shape are within its
+// limits.
+bool skinny_pattern(int n, int m);
 bool skinny_fits(int64_t rows, int64_t cols, int64_t tokens, int n, int m, const DeviceInfo& dev);
 hipError_t launch_skinny_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
                               int64_t rows, int64_t cols, int tokens, int n, int m, hipStream_t stream,
@@ -108,10 +111,18 @@ hipError_t launch_skinny_spmm(const uint16_t* values, const uint32_t* masks, con
 // vectors: there the skinny kernel's fixed cost (about 6 us) is below the small-batch
 // kernel's time for 2:4 at every batch (1024 x 4096 at 8 vectors: 6.7 against 8.0 us), and
 // for the split patterns once the small-batch kernel needs a second pass of 8 vectors.
+// 16:32, whose expansion costs LDS traffic every step, only from kSkinnyExpandMinBatch
+// vectors on layers of at least kSkinnyExpandMinRows rows and at most kSkinnyExpandMaxCols
+// columns (X of 16 vectors in one LDS phase): measured there at 1.2-1.5x the small-batch
+// kernel (4096 x 4096 at 16 vectors: 15.6 against 21.5 us), and behind it elsewhere (at 5..8
+// vectors, on 1024-row layers, on 5120 columns and more).
 constexpr int64_t kSkinnyMinBatch = 5;
 constexpr int64_t kSkinnyMinRows = 2048;
 constexpr int64_t kSkinnySmallMinRows = 256;
 constexpr int64_t kSkinnyBatch = 16;
+constexpr int64_t kSkinnyExpandMinBatch = 12;
+constexpr int64_t kSkinnyExpandMinRows = 4096;
+constexpr int64_t kSkinnyExpandMaxCols = 4096;
 bool use_skinny(int64_t rows, int64_t cols, int64_t batch, int n, int m, const DeviceInfo& dev);
 const char* skinny_variant(int n);
 

@@ -1,5 +1,6 @@
-// Launcher of the small-batch 50% products on the sparse matrix instruction (1..16 tokens):
-// 2:4 directly, 4:8 and 8:16 split into two 2:4 operands. The kernel is in nm_skinny_impl.h.
+// Launcher of the small-batch 50% products on the matrix instructions (1..16 tokens): 2:4
+// directly, 4:8 and 8:16 split into two 2:4 operands, 16:32 expanded to dense fragments. The
+// kernels are in nm_skinny_impl.h.
 #include <algorithm>
 
 #include "nm_internal.h"
@@ -23,13 +24,20 @@ struct SkinnyShape {
 // 16) with CS = 16 / RG waves splitting the columns; about one workgroup per CU. X is
 // staged in column phases of at most 128 KiB (and the device's per-workgroup LDS, less the
 // split tables when the pattern needs them).
-size_t x_budget(bool split, const DeviceInfo& dev) {
+int mode_of(int n) { return n == 2 ? kModeDirect : n == 16 ? kModeExpand : kModeSplit; }
+
+size_t lead_of(int mode) {
+  return mode == kModeSplit ? lead_bytes<1, kModeSplit>() : mode == kModeExpand ? lead_bytes<1, kModeExpand>() : 0;
+}
+
+size_t x_budget(int mode, const DeviceInfo& dev) {
   const size_t lds = size_t(dev.max_lds_per_block > 0 ? dev.max_lds_per_block : 65536);
-  const size_t avail = split ? (lds > kSplitLutBytes ? lds - kSplitLutBytes : 0) : lds;
+  const size_t lead = lead_of(mode);
+  const size_t avail = lds > lead ? lds - lead : 0;
   return std::min<size_t>(kMaxXBytes, avail);
 }
 
-SkinnyShape skinny_shape(int64_t rows, int64_t cols, int tokens, bool split, const DeviceInfo& dev) {
+SkinnyShape skinny_shape(int64_t rows, int64_t cols, int tokens, int mode, const DeviceInfo& dev) {
   const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
   const int64_t tiles = ceil_div(rows, 16);
   const int64_t want = std::min<int64_t>(kMaxWaves, std::max<int64_t>(1, ceil_div(tiles, cus)));
@@ -37,42 +45,46 @@ SkinnyShape skinny_shape(int64_t rows, int64_t cols, int tokens, bool split, con
   while (s.rg < want) s.rg *= 2;
   s.cs = kMaxWaves / s.rg;
   s.grid = ceil_div(tiles, s.rg);
-  const int64_t pc_max = int64_t(x_budget(split, dev) / (2 * size_t(tokens))) / 64 * 64;
+  const int64_t pc_max = int64_t(x_budget(mode, dev) / (2 * size_t(tokens))) / 64 * 64;
   s.phase_cols = int(std::min<int64_t>(pc_max, ceil_div(cols, 64) * 64));
-  s.lds = std::max((split ? kSplitLutBytes : 0) + x_bytes(tokens, s.phase_cols), red_bytes(kMaxWaves, 1));
+  s.lds = std::max(lead_of(mode) + x_bytes(tokens, s.phase_cols), red_bytes(kMaxWaves, 1));
   return s;
 }
 
 }  // namespace
 
-bool skinny_pattern(int n, int m) { return 2 * n == m && (n == 2 || n == 4 || n == 8); }
+bool skinny_pattern(int n, int m) { return 2 * n == m && (n == 2 || n == 4 || n == 8 || n == 16); }
 
 bool skinny_fits(int64_t rows, int64_t cols, int64_t tokens, int n, int m, const DeviceInfo& dev) {
   // byte offsets inside a workgroup's slices are 32-bit; X of one phase must fit LDS
   if (!skinny_pattern(n, m) || tokens < 1 || tokens > kMaxTokens || cols > kPrefillMaxCols) return false;
-  return x_budget(n != 2, dev) >= 2 * size_t(tokens) * 64 && ceil_div(rows, 16) <= INT32_MAX;
+  return x_budget(mode_of(n), dev) >= 2 * size_t(tokens) * 64 && ceil_div(rows, 16) <= INT32_MAX;
 }
 
 bool use_skinny(int64_t rows, int64_t cols, int64_t batch, int n, int m, const DeviceInfo& dev) {
   if (batch < kSkinnyMinBatch || batch >= kMatrixCoreMinBatch)   // beyond: the prefill kernels
     return false;
   if (rows < kSkinnySmallMinRows || !skinny_fits(rows, cols, kSkinnyBatch, n, m, dev)) return false;
+  if (n == 16) return batch >= kSkinnyExpandMinBatch && rows >= kSkinnyExpandMinRows && cols <= kSkinnyExpandMaxCols;
   if (rows >= kSkinnyMinRows || n == 2) return true;
   return batch >= 12 || (batch >= 9 && cols <= 5120);   // the split patterns on smaller layers
 }
 
-const char* skinny_variant(int n) { return n == 2 ? "skinny_spmm_kernel<1, false>" : "skinny_spmm_kernel<1, true>"; }
+const char* skinny_variant(int n) {
+  return n == 2 ? "skinny_spmm_kernel<1, false>" : n == 16 ? "skinny_expand_kernel<1>" : "skinny_spmm_kernel<1, true>";
+}
 
 hipError_t launch_skinny_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
                               int64_t rows, int64_t cols, int tokens, int n, int m, hipStream_t stream,
                               const DeviceInfo& dev) {
   if (!skinny_fits(rows, cols, tokens, n, m, dev)) return hipErrorInvalidValue;
-  const bool split = n != 2;
-  const SkinnyShape s = skinny_shape(rows, cols, tokens, split, dev);
+  const int mode = mode_of(n);
+  const SkinnyShape s = skinny_shape(rows, cols, tokens, mode, dev);
   int r = int(rows), c = int(cols), t = tokens, rg = s.rg, cs = s.cs, pc = s.phase_cols;
   void* args[] = {&values, &masks, &X, &Y, &r, &c, &t, &rg, &cs, &pc};
-  const void* k = split ? reinterpret_cast<const void*>(&skinny_spmm_kernel<1, true>)
-                        : reinterpret_cast<const void*>(&skinny_spmm_kernel<1, false>);
+  const void* k = mode == kModeSplit    ? reinterpret_cast<const void*>(&skinny_spmm_kernel<1, true>)
+                : mode == kModeExpand   ? reinterpret_cast<const void*>(&skinny_expand_kernel<1>)
+                                        : reinterpret_cast<const void*>(&skinny_spmm_kernel<1, false>);
   return launch(k, dim3(unsigned(s.grid)), dim3(kThreadsFixed), args, s.lds, stream, dev);
 }
 

@@ -21,6 +21,13 @@
 // 4:8 and 8:16 (SPLIT): each 4-column group is split into two 2:4 operands (its first two
 // kept values, and the rest) by the split tables of nm_prefill_impl.h, which this kernel
 // keeps in LDS; both operands go through the sparse instruction with the same X fragment.
+//
+// 16:32 (EXPAND, skinny_expand_kernel): a word's 16 kept values may sit anywhere in its 32
+// columns, so the dense 16 x 16 x 32 instruction takes each word, with the lanes' fragments
+// expanded to dense columns: each wave writes the step's loaded values (16 rows x 64 bytes)
+// to its own LDS area, and lane (row, q) reads the 8 halves from its mask byte's first kept
+// value on and places them with the expansion table (nm_prefill_impl.h). The X fragments,
+// loads, mask blocks and reduction are those of the 2:4 kernel.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -53,16 +60,31 @@ __device__ __forceinline__ uint32_t xoff(int t, int c, uint32_t rb) {
 }
 
 
-template <int TR, bool SPLIT>
-__global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16_t* __restrict__ values,
-                                                                     const uint32_t* __restrict__ masks,
-                                                                     const uint16_t* __restrict__ X,
-                                                                     uint16_t* __restrict__ Y, int rows, int cols,
-                                                                     int tokens, int rg_count, int cs_count,
-                                                                     int phase_cols) {
+// What the kernel does with the packed operand: 2:4 directly, 4:8 / 8:16 split, 16:32
+// expanded.
+constexpr int kModeDirect = 0, kModeSplit = 1, kModeExpand = 2;
+// EXPAND: LDS bytes of one wave's area per row tile: the step's values of 16 rows (64 bytes
+// each) and room for a window read past the last row's second word
+constexpr uint32_t kExpandWaveBytes = 16 * 64 + 64;
+
+// LDS bytes ahead of X: the split tables, or the expansion table and the waves' value areas.
+template <int TR, int MODE>
+__host__ __device__ constexpr uint32_t lead_bytes() {
+  return MODE == kModeSplit ? kSplitLutBytes
+       : MODE == kModeExpand ? kExpandBytes + uint32_t(kMaxWaves) * TR * kExpandWaveBytes
+                             : 0u;
+}
+
+template <int TR, int MODE>
+__device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ values, const uint32_t* __restrict__ masks,
+                                            const uint16_t* __restrict__ X, uint16_t* __restrict__ Y, int rows,
+                                            int cols, int tokens, int rg_count, int cs_count, int phase_cols) {
+  constexpr bool SPLIT = MODE == kModeSplit;
+  constexpr bool EXPAND = MODE == kModeExpand;
   extern __shared__ __attribute__((aligned(16))) char lds_base[];
-  // SPLIT: the split tables first, X after them
-  char* const lds = lds_base + (SPLIT ? kSplitLutBytes : 0);
+  // SPLIT: the split tables first, X after them; EXPAND: the expansion table and the waves'
+  // value areas, then X
+  char* const lds = lds_base + lead_bytes<TR, MODE>();
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // the wave index and everything derived from it are wave-uniform (scalar registers): the
@@ -104,6 +126,10 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
     const uint4* tab = reinterpret_cast<const uint4*>(&kSplitTable);
     lut_a = tab[tid];
     lut_b = tab[2 * kSplitEntries + (tid & 63)];
+  }
+  if constexpr (EXPAND) {   // the expansion table: 2 * kExpandEntries chunks of 16 bytes
+    const uint4* tab = reinterpret_cast<const uint4*>(&kExpandTable);
+    lut_a = tab[tid & (2 * kExpandEntries - 1)];
   }
   for (int p0 = 0; p0 < cols; p0 += phase_cols) {
     const int pc = min(phase_cols, cols - p0);       // columns in this phase (multiple of 32)
@@ -168,6 +194,9 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
         if (tid < 64) reinterpret_cast<uint4*>(lds_base)[2 * kSplitEntries + tid] = lut_b;
       }
     }
+    if constexpr (EXPAND) {
+      if (p0 == 0 && tid < 2 * kExpandEntries) reinterpret_cast<uint4*>(lds_base)[tid] = lut_a;
+    }
 #pragma unroll
     for (int j = 0; j < kXChunksPerThread; ++j)
       if (xdst[j] != 0xFFFFFFFFu) *reinterpret_cast<uint4*>(lds + xdst[j]) = xs[j];
@@ -179,7 +208,7 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
         // only fetch and shift them
 #pragma unroll
         for (int a = 0; a < TR; ++a)
-          mcur[a] = SPLIT ? mnext[a] : make_uint2(pair_codes32(mnext[a].x), pair_codes32(mnext[a].y));
+          mcur[a] = (SPLIT || EXPAND) ? mnext[a] : make_uint2(pair_codes32(mnext[a].x), pair_codes32(mnext[a].y));
         load_m(s0 + kMaskSteps);
 #pragma unroll
         for (int j = 0; j < kMaskSteps; ++j) {
@@ -201,6 +230,43 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
           for (int a = 0; a < TR; ++a) {
             const uint32_t w0 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur[a].x)));
             const uint32_t w1 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur[a].y)));
+            if constexpr (EXPAND) {
+              // the step's values to this wave's area (row li at 64 li, lane q's 16 bytes at
+              // 16 q), visible to the other lanes of the wave before they are read back
+              char* const va = lds_base + kExpandBytes + uint32_t(wave * TR + a) * kExpandWaveBytes;
+              *reinterpret_cast<uint4*>(va + 64 * li + 16 * q) = cur[a];
+              __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+              __builtin_amdgcn_wave_barrier();
+              __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+              for (int i = 0; i < 2; ++i) {   // word i of the step: one dense 16 x 16 x 32 product
+                const uint32_t w = i ? w1 : w0;
+                const uint32_t byte = __builtin_amdgcn_ubfe(w, 8u * uint32_t(q), 8);
+                // first kept value of the lane's byte among the word's 16 (at most 16 for a
+                // valid mask; clamped so that any mask keeps the window inside the area)
+                const uint32_t pc = min(uint32_t(__builtin_popcount(w & ((1u << (8 * q)) - 1u))), 16u);
+                const uint32_t off = 64u * uint32_t(li) + 32u * uint32_t(i) + 2u * pc;   // window, bytes
+                const uint32_t* wd = reinterpret_cast<const uint32_t*>(va + (off & ~3u));
+                const uint32_t sh = (off & 2u) * 8u;   // 16 when the window starts mid-dword
+                const uint32_t r0 = wd[0], r1 = wd[1], r2 = wd[2], r3 = wd[3], r4 = wd[4];
+                const uint32_t v0 = __builtin_amdgcn_alignbit(r1, r0, sh), v1 = __builtin_amdgcn_alignbit(r2, r1, sh);
+                const uint32_t v2 = __builtin_amdgcn_alignbit(r3, r2, sh), v3 = __builtin_amdgcn_alignbit(r4, r3, sh);
+                const uint4 s0 = *reinterpret_cast<const uint4*>(lds_base + 32u * byte);
+                const uint4 s1 = *reinterpret_cast<const uint4*>(lds_base + 32u * byte + 16u);
+                auto pick = [&](uint32_t lo_sel, uint32_t hi_sel) {
+                  return __builtin_amdgcn_perm(v1, v0, lo_sel) | __builtin_amdgcn_perm(v3, v2, hi_sel);
+                };
+                const uint4 dense = make_uint4(pick(s0.x, s0.y), pick(s0.z, s0.w), pick(s1.x, s1.y), pick(s1.z, s1.w));
+                const uint4 xf = i ? hi : lo;   // X of the word's columns 8q .. 8q+7, every token
+                acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, dense),
+                                                                __builtin_bit_cast(h8_t, xf), acc[a], 0, 0, 0);
+              }
+              // every lane has read the area before the next step writes it
+              __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+              __builtin_amdgcn_wave_barrier();
+              __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+              continue;
+            }
             const uint32_t m16 = __builtin_amdgcn_ubfe((q >> 1) ? w1 : w0, mshift, 16);
             if constexpr (SPLIT) {
               const uint32_t e0 = 32u * (m16 & 0xFFu), e1 = 32u * (256u + (m16 >> 8));
@@ -254,6 +320,27 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
     for (int k = 0; k < 4; ++k)
       if (row + k < rows) out[row + k] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(e[k]));
   }
+}
+
+template <int TR, bool SPLIT>
+__global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16_t* __restrict__ values,
+                                                                     const uint32_t* __restrict__ masks,
+                                                                     const uint16_t* __restrict__ X,
+                                                                     uint16_t* __restrict__ Y, int rows, int cols,
+                                                                     int tokens, int rg_count, int cs_count,
+                                                                     int phase_cols) {
+  skinny_body<TR, SPLIT ? kModeSplit : kModeDirect>(values, masks, X, Y, rows, cols, tokens, rg_count, cs_count,
+                                                     phase_cols);
+}
+
+template <int TR>
+__global__ __launch_bounds__(kThreadsFixed) void skinny_expand_kernel(const uint16_t* __restrict__ values,
+                                                                       const uint32_t* __restrict__ masks,
+                                                                       const uint16_t* __restrict__ X,
+                                                                       uint16_t* __restrict__ Y, int rows, int cols,
+                                                                       int tokens, int rg_count, int cs_count,
+                                                                       int phase_cols) {
+  skinny_body<TR, kModeExpand>(values, masks, X, Y, rows, cols, tokens, rg_count, cs_count, phase_cols);
 }
 
 }  // namespace skinny_detail

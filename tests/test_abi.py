@@ -192,6 +192,25 @@ def test_spmm_validation(kw, want):
 
 
 @pytest.mark.parametrize("kw,want", [
+    (dict(values=None), nm.NM_ERR_NULL), (dict(masks=None), nm.NM_ERR_NULL), (dict(X=None), nm.NM_ERR_NULL),
+    (dict(Y=None), nm.NM_ERR_NULL),
+    (dict(batch=0), nm.NM_ERR_SHAPE), (dict(batch=(1 << 24) + 1), nm.NM_ERR_SHAPE), (dict(rows=0), nm.NM_ERR_SHAPE),
+    (dict(cols=80), nm.NM_ERR_SHAPE), (dict(cols=(1 << 21) + 32), nm.NM_ERR_SHAPE),
+    (dict(N=1, M=4), nm.NM_ERR_PATTERN), (dict(N=3, M=6), nm.NM_ERR_PATTERN), (dict(N=2, M=8), nm.NM_ERR_PATTERN),
+    (dict(values=A16 + 8), nm.NM_ERR_ALIGN), (dict(masks=A16 + 2), nm.NM_ERR_ALIGN),
+    (dict(X=A16 + 4), nm.NM_ERR_ALIGN), (dict(Y=A16 + 1), nm.NM_ERR_ALIGN),
+    # every 50% pattern passes the pattern check and reaches the alignment check
+    (dict(N=4, M=8, values=A16 + 8), nm.NM_ERR_ALIGN), (dict(N=8, M=16, X=A16 + 4), nm.NM_ERR_ALIGN),
+    (dict(N=16, M=32, Y=A16 + 1), nm.NM_ERR_ALIGN),
+])
+def test_spmm_skinny_validation(kw, want):
+    a = dict(values=A16, masks=A16, X=A16, Y=A16, rows=64, cols=128, batch=7, N=2, M=4)
+    a.update(kw)
+    assert nm.lib().nm_spmm_skinny(a["values"], a["masks"], a["X"], a["Y"], a["rows"], a["cols"], a["batch"],
+                                   a["N"], a["M"], None) == want
+
+
+@pytest.mark.parametrize("kw,want", [
     (dict(W=None), nm.NM_ERR_NULL), (dict(batch=0), nm.NM_ERR_SHAPE), (dict(batch=(1 << 24) + 1), nm.NM_ERR_SHAPE),
     (dict(X=A16 + 2), nm.NM_ERR_ALIGN), (dict(batch=9, Y=A16 + 1), nm.NM_ERR_ALIGN),
     (dict(batch=40, Y=A16 + 1), nm.NM_ERR_ALIGN), (dict(batch=40, cols=(1 << 21) + 32), nm.NM_ERR_SHAPE),

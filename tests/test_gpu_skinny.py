@@ -1,7 +1,9 @@
-"""GPU parity tests of the small-batch 50% products on the sparse matrix instruction (nm_spmm
-with 5..31 vectors: 2:4 on layers of at least 256 rows; 4:8 and 8:16, split into two 2:4
-operands, on layers of at least 2048 rows, and on smaller ones from 9 or 12 vectors), through
-the C ABI, against the CPU oracle (spmm_ref).
+"""GPU parity tests of the small-batch 50% products on the matrix instructions, through the
+C ABI, against the CPU oracle (spmm_ref): nm_spmm_skinny for every 50% pattern (2:4 direct;
+4:8 and 8:16 split into two 2:4 operands; 16:32 expanded to dense fragments) on ragged
+shapes, and nm_spmm where its routing picks them (5..31 vectors: 2:4 on layers of at least
+256 rows; 4:8 and 8:16 on layers of at least 2048 rows, and on smaller ones from 9 or 12
+vectors; 16:32 from 12 vectors on layers of >= 4096 rows and <= 4096 columns).
 
 Bars: Y within |y - ref| <= 2e-3 + 1e-2*|ref| per element and relative L2 <= 1e-3 (fp32
 accumulation in the matrix instruction, fp16 output, fp64 oracle); exact special cases
@@ -17,8 +19,9 @@ import synth
 from tests.gpu_helpers import device, down_bits16, down_f16, down_u32, sample_rows, say, up_f16, up_u32
 
 pytestmark = pytest.mark.gpu
-SKINNY = {2: "skinny_spmm_kernel<1, false>", 4: "skinny_spmm_kernel<1, true>", 8: "skinny_spmm_kernel<1, true>"}
-PATTERNS = [(2, 4), (4, 8), (8, 16)]
+SKINNY = {2: "skinny_spmm_kernel<1, false>", 4: "skinny_spmm_kernel<1, true>", 8: "skinny_spmm_kernel<1, true>",
+          16: "skinny_expand_kernel<1>"}
+PATTERNS = [(2, 4), (4, 8), (8, 16), (16, 32)]
 
 # (rows, cols, vectors): ragged rows (16-row tiles, row groups of 1..4 tiles), a 32-column
 # tail step, steps split over 16 / 8 / 4 waves, X in several column phases (16 vectors x
@@ -27,11 +30,11 @@ CASES = [(2048, 96, 5), (2049, 1056, 8), (2100, 4064, 16), (4100, 1024, 11), (40
          (4100, 14368, 13), (9000, 2080, 17), (14336, 4096, 8), (2600, 544, 31), (16400, 288, 6)]
 
 
-def check(R, C, T, seed, N=2, M=4, rows_idx=None):
+def check(R, C, T, seed, N=2, M=4, rows_idx=None, fn=nm.nm_spmm):
     W = synth.weight(R, C, seed)
     X = synth.activations(T, C, seed + 1)
     values, masks = nm.nm_pack(up_f16(W), N, M)
-    Y = down_f16(nm.nm_spmm(values, masks, up_f16(X), N, M))
+    Y = down_f16(fn(values, masks, up_f16(X), N, M))
     idx = np.arange(R) if rows_idx is None else rows_idx
     it = torch.from_numpy(idx).to(device())
     rv, rm = oracle.pack_ref(W[idx], N, M)
@@ -45,9 +48,21 @@ def check(R, C, T, seed, N=2, M=4, rows_idx=None):
 @pytest.mark.parametrize("N,M", PATTERNS)
 @pytest.mark.parametrize("R,C,T", CASES)
 def test_skinny_parity(R, C, T, N, M):
-    assert nm.spmm_variant(R, C, T, N, M) == SKINNY[N]
     say(f"skinny {N}:{M} {R}x{C} vectors={T}")
-    check(R, C, T, 3000 + R % 97 + C % 89 + T + N, N, M, sample_rows(R, k=32, rpb=16))
+    check(R, C, T, 3000 + R % 97 + C % 89 + T + N, N, M, sample_rows(R, k=32, rpb=16), fn=nm.nm_spmm_skinny)
+
+
+# nm_spmm's routing to the skinny kernels, 16:32 included (ragged rows, two launches)
+ROUTED_CASES = [((2, 4), 4100, 1024, 11), ((8, 16), 2100, 4064, 16), ((16, 32), 4096, 4096, 12),
+                ((16, 32), 4100, 4064, 16), ((16, 32), 14336, 4096, 20)]
+
+
+@pytest.mark.parametrize("pat,R,C,T", ROUTED_CASES)
+def test_skinny_routed(pat, R, C, T):
+    N, M = pat
+    assert nm.spmm_variant(R, C, T, N, M) == SKINNY[N]
+    say(f"skinny routed {N}:{M} {R}x{C} vectors={T}")
+    check(R, C, T, 3300 + R % 97 + C % 89 + T + N, N, M, sample_rows(R, k=32, rpb=16))
 
 
 # smaller layers (fewer than 2048 rows): ragged rows, a 32-column tail, one and two launches
@@ -75,8 +90,9 @@ def test_skinny_split_two_launches(N, M):
 def test_skinny_routing():
     """Which kernel nm_spmm picks: the sparse matrix instruction at 5..31 vectors for 2:4 on
     layers of >= 256 rows and for 4:8 and 8:16 on layers of >= 2048 rows (on smaller ones from
-    9 vectors up to 5120 columns, else from 12); the small-batch kernel below 5 vectors, on
-    smaller layers and for 16:32; the prefill kernels from 32 vectors on."""
+    9 vectors up to 5120 columns, else from 12), and for 16:32 from 12 vectors on layers of
+    >= 4096 rows and <= 4096 columns; the small-batch kernel below 5 vectors, on smaller
+    layers and for other 16:32 shapes; the prefill kernels from 32 vectors on."""
     assert nm.spmm_variant(4096, 4096, 4, 2, 4) == "spmm_kernel<2, 4, 2>"
     assert nm.spmm_variant(2047, 4096, 8, 2, 4) == SKINNY[2]
     assert nm.spmm_variant(1024, 4096, 5, 2, 4) == SKINNY[2]
@@ -87,10 +103,15 @@ def test_skinny_routing():
     assert nm.spmm_variant(1024, 5120, 9, 8, 16) == SKINNY[8]
     assert nm.spmm_variant(1024, 8192, 9, 8, 16) == "spmm_kernel<8, 8, 2>"
     assert nm.spmm_variant(1024, 8192, 12, 8, 16) == SKINNY[8]
+    assert nm.spmm_variant(4096, 4096, 12, 16, 32) == SKINNY[16]
+    assert nm.spmm_variant(14336, 4096, 31, 16, 32) == SKINNY[16]
+    assert nm.spmm_variant(4096, 4096, 11, 16, 32) == "spmm_kernel<16, 8, 0>"
+    assert nm.spmm_variant(4095, 4096, 16, 16, 32) == "spmm_kernel<16, 8, 0>"
+    assert nm.spmm_variant(4096, 4128, 16, 16, 32) == "spmm_kernel<16, 8, 0>"
     assert nm.spmm_variant(1024, 4096, 16, 16, 32) == "spmm_kernel<16, 8, 0>"
+    assert nm.spmm_variant(4096, 4096, 5, 16, 32) == "spmm_kernel<16, 5, 0>"
     assert nm.spmm_variant(4096, 4096, 4, 8, 16) == "spmm_kernel<8, 4, 2>"
-    assert nm.spmm_variant(4096, 4096, 20, 16, 32) == "spmm_kernel<16, 8, 0>"
-    for N, M in PATTERNS:
+    for N, M in PATTERNS[:3]:
         assert nm.spmm_variant(4096, 4096, 5, N, M) == SKINNY[N]
         assert nm.spmm_variant(4096, 4096, 31, N, M) == SKINNY[N]
     assert nm.spmm_variant(4096, 4096, 32, 4, 8).startswith("prefill_split_kernel")
@@ -113,14 +134,14 @@ def test_skinny_one_hot_and_determinism(N, M):
     for t, c in enumerate(cols):
         X[t, c] = 1.0
     v, m = up_f16(rv), up_u32(rm)
-    Y = down_bits16(nm.nm_spmm(v, m, up_f16(X), N, M))
+    Y = down_bits16(nm.nm_spmm_skinny(v, m, up_f16(X), N, M))
     want = D[:, cols].T.copy()
     want[want == 0x8000] = 0
     assert np.array_equal(Y, want)
     Xr = up_f16(synth.activations(16, C, 3101))
-    Y0 = down_bits16(nm.nm_spmm(v, m, Xr, N, M))
+    Y0 = down_bits16(nm.nm_spmm_skinny(v, m, Xr, N, M))
     for _ in range(10):
-        assert np.array_equal(down_bits16(nm.nm_spmm(v, m, Xr, N, M)), Y0)
+        assert np.array_equal(down_bits16(nm.nm_spmm_skinny(v, m, Xr, N, M)), Y0)
 
 
 @pytest.mark.parametrize("N,M", PATTERNS)
@@ -130,6 +151,6 @@ def test_skinny_malformed_masks_stay_in_bounds(N, M):
     X = up_f16(synth.activations(T, C, 3201))
     for word in (0, 1, 0x80000000, 0xFFFFFFFF, 0x12345678):
         m = torch.full((R, C // 32), np.uint32(word).view(np.int32).item(), dtype=torch.int32, device=device())
-        Y = nm.nm_spmm(v, m, X, N, M)
+        Y = nm.nm_spmm_skinny(v, m, X, N, M)
         torch.cuda.synchronize()
         assert Y.shape == (T, R)
