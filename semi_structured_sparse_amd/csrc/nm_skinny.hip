@@ -20,10 +20,12 @@ struct SkinnyShape {
   size_t lds = 0;
 };
 
-// Workgroup shape: 16 waves, RG row groups of 16 rows (a power of two, so that RG * CS =
-// 16) with CS = 16 / RG waves splitting the columns; about one workgroup per CU. X is
+// Workgroup shape: 16 waves, RG = ceil(tiles / CUs) row groups of 16 rows with CS =
+// floor(16 / RG) waves splitting the columns (RG * CS <= 16 waves own rows), so that the
+// grid is as close to one workgroup per CU as whole row groups allow: 17408 rows take 218
+// workgroups of 5 x 3 waves, where a power-of-two RG (8 x 2) would leave 120 CUs idle. X is
 // staged in column phases of at most 128 KiB (and the device's per-workgroup LDS, less the
-// split tables when the pattern needs them).
+// tables the pattern needs).
 int mode_of(int n) { return n == 2 ? kModeDirect : n == 16 ? kModeExpand : kModeSplit; }
 
 size_t lead_of(int mode) {
@@ -42,7 +44,7 @@ SkinnyShape skinny_shape(int64_t rows, int64_t cols, int tokens, int mode, const
   const int64_t tiles = ceil_div(rows, 16);
   const int64_t want = std::min<int64_t>(kMaxWaves, std::max<int64_t>(1, ceil_div(tiles, cus)));
   SkinnyShape s;
-  while (s.rg < want) s.rg *= 2;
+  s.rg = int(want);
   s.cs = kMaxWaves / s.rg;
   s.grid = ceil_div(tiles, s.rg);
   const int64_t pc_max = int64_t(x_budget(mode, dev) / (2 * size_t(tokens))) / 64 * 64;

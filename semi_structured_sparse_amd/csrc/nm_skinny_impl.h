@@ -6,7 +6,8 @@
 //
 // With at most 16 tokens the product is bound by reading the packed weights once, like the
 // batch-one SpMV, so the kernel is laid out like the SpMV: a workgroup holds RG row groups
-// of 16 * TR rows, each split over CS waves along the columns; X of all tokens sits in LDS
+// of 16 * TR rows, each split over CS waves along the columns (RG * CS <= 16; the other
+// waves only help stage X); X of all tokens sits in LDS
 // (in column phases when it does not fit); each wave streams its rows' values and masks
 // with no barrier in its loop and multiplies them on the sparse matrix instruction (one
 // 16 x 16 x 64 instruction per 16 rows and 64 columns covers every token), and the CS
@@ -92,6 +93,9 @@ __device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ values,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, li = lane & 15;
   const int rg = wave / cs_count, cs = wave - rg * cs_count;
+  // waves past rg_count * cs_count (when 16 is not a multiple of cs_count) stage X and meet
+  // the barriers but own no rows
+  const bool active = rg < rg_count;
   const int wg_rows_max = rg_count * 16 * TR;
   const int wg_r0 = int(blockIdx.x) * wg_rows_max;
   const int wg_rows = min(wg_rows_max, rows - wg_r0);
@@ -137,7 +141,7 @@ __device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ values,
     // this wave's steps of the phase
     const int psteps = (pc + 63) / 64;
     const int s_lo = int((int64_t(psteps) * cs) / cs_count), s_hi = int((int64_t(psteps) * (cs + 1)) / cs_count);
-    const int n = s_hi - s_lo;
+    const int n = active ? s_hi - s_lo : 0;
     const int last = max(n - 1, 0);
     const int c_lo = p0 + 64 * s_lo;                 // first column of the wave's range
     // value loads: step s of the range is inside the row for this lane iff s < s_lim; steps
@@ -304,7 +308,7 @@ __device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ values,
   for (int a = 0; a < TR; ++a)
     red[(wave * TR + a) * 64 + lane] = make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
   __syncthreads();
-  if (cs != 0) return;
+  if (cs != 0 || !active) return;
 #pragma unroll
   for (int a = 0; a < TR; ++a) {
     float4 s = red[(wave * TR + a) * 64 + lane];

@@ -143,28 +143,29 @@ __device__ __forceinline__ uint2 lds_u2(uint32_t a) {
 // x pairs of this lane's 8 kept columns: `bits` holds the columns as set bits; column p
 // sits at LDS byte address xw + step * p (step = 2, or -2 from the window's last element
 // for a bit-reversed 16:32 word). v_ffbl of an exhausted word is -1: one element outside
-// the window, still inside the padded LDS data region.
+// the window, still inside the padded LDS data region. The 8 addresses come first, then the
+// 8 reads, then the pairs, so that the step's reads are in flight together (one LDS round
+// trip per step rather than one per pair).
 __device__ __forceinline__ void gather_bits(uint32_t bits, uint32_t xw, int step, half2_t (&xp)[4]) {
+  uint32_t a[8];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < 8; ++k) {
     const int p0 = __builtin_ctz(bits);
     bits &= bits - 1;
-    const int p1 = __builtin_ctz(bits);
-    bits &= bits - 1;
-    if (step == 2) {
-      xp[k].x = lds_half(xw + 2u * uint32_t(p0));
-      xp[k].y = lds_half(xw + 2u * uint32_t(p1));
-    } else {
-      xp[k].x = lds_half(xw + uint32_t(step * p0));
-      xp[k].y = lds_half(xw + uint32_t(step * p1));
-    }
+    a[k] = xw + uint32_t(step * p0);
   }
+  _Float16 h[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) h[k] = lds_half(a[k]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) xp[k] = half2_t{h[2 * k], h[2 * k + 1]};
 }
 
 // Byte-LUT gather for 4:8 and 8:16: the half-word's two mask bytes give their set-bit
 // offsets from the tables (one 64-bit LDS read each); the two lists are concatenated with
 // one 64-bit shift by 8 * popcount(low byte), modulo 64 (for 4:8 the low byte always holds 4); byte k
-// of the result is the offset of value k from xh, the half-word's x window.
+// of the result is the offset of value k from xh, the half-word's x window. The 8 reads are
+// issued before the pairs are formed, as in gather_bits.
 template <int N>
 __device__ __forceinline__ void gather_lut(uint32_t m, uint32_t sh16, uint32_t lut, uint32_t xh,
                                            half2_t (&xp)[4]) {
@@ -185,14 +186,17 @@ __device__ __forceinline__ void gather_lut(uint32_t m, uint32_t sh16, uint32_t l
     lo = uint32_t(q);
     hi = uint32_t(q >> 32);
   }
-  xp[0].x = lds_half(xh + (lo & 0xFFu));
-  xp[0].y = lds_half(xh + ((lo >> 8) & 0xFFu));
-  xp[1].x = lds_half(xh + ((lo >> 16) & 0xFFu));
-  xp[1].y = lds_half(xh + (lo >> 24));
-  xp[2].x = lds_half(xh + (hi & 0xFFu));
-  xp[2].y = lds_half(xh + ((hi >> 8) & 0xFFu));
-  xp[3].x = lds_half(xh + ((hi >> 16) & 0xFFu));
-  xp[3].y = lds_half(xh + (hi >> 24));
+  _Float16 h[8];
+  h[0] = lds_half(xh + (lo & 0xFFu));
+  h[1] = lds_half(xh + ((lo >> 8) & 0xFFu));
+  h[2] = lds_half(xh + ((lo >> 16) & 0xFFu));
+  h[3] = lds_half(xh + (lo >> 24));
+  h[4] = lds_half(xh + (hi & 0xFFu));
+  h[5] = lds_half(xh + ((hi >> 8) & 0xFFu));
+  h[6] = lds_half(xh + ((hi >> 16) & 0xFFu));
+  h[7] = lds_half(xh + (hi >> 24));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) xp[k] = half2_t{h[2 * k], h[2 * k + 1]};
 }
 
 // Builds the two byte-LUT tables (256 entries of 8 bytes each) at `lut`.
