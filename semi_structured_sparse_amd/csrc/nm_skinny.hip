@@ -15,7 +15,7 @@ namespace {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct SkinnyShape {
-  int rg = 1, cs = 16, phase_cols = 64;
+  int rg = 1, cs = 16, phase_cols = 128;
   int64_t grid = 0;
   size_t lds = 0;
 };
@@ -29,7 +29,7 @@ struct SkinnyShape {
 int mode_of(int n) { return n == 2 ? kModeDirect : n == 16 ? kModeExpand : kModeSplit; }
 
 size_t lead_of(int mode) {
-  return mode == kModeSplit ? lead_bytes<1, kModeSplit>() : mode == kModeExpand ? lead_bytes<1, kModeExpand>() : 0;
+  return mode == kModeSplit ? lead_bytes<kModeSplit>() : mode == kModeExpand ? lead_bytes<kModeExpand>() : 0;
 }
 
 size_t x_budget(int mode, const DeviceInfo& dev) {
@@ -47,9 +47,10 @@ SkinnyShape skinny_shape(int64_t rows, int64_t cols, int tokens, int mode, const
   s.rg = int(want);
   s.cs = kMaxWaves / s.rg;
   s.grid = ceil_div(tiles, s.rg);
-  const int64_t pc_max = int64_t(x_budget(mode, dev) / (2 * size_t(tokens))) / 64 * 64;
-  s.phase_cols = int(std::min<int64_t>(pc_max, ceil_div(cols, 64) * 64));
-  s.lds = std::max(lead_of(mode) + x_bytes(tokens, s.phase_cols), red_bytes(kMaxWaves, 1));
+  // phases of whole 128-column lines (the loads of the 2:4 and split kernels cover lines)
+  const int64_t pc_max = int64_t(x_budget(mode, dev) / (2 * size_t(tokens))) / 128 * 128;
+  s.phase_cols = int(std::min<int64_t>(pc_max, ceil_div(cols, 128) * 128));
+  s.lds = std::max(lead_of(mode) + x_bytes(tokens, s.phase_cols), red_bytes(kMaxWaves));
   return s;
 }
 
@@ -60,7 +61,7 @@ bool skinny_pattern(int n, int m) { return 2 * n == m && (n == 2 || n == 4 || n 
 bool skinny_fits(int64_t rows, int64_t cols, int64_t tokens, int n, int m, const DeviceInfo& dev) {
   // byte offsets inside a workgroup's slices are 32-bit; X of one phase must fit LDS
   if (!skinny_pattern(n, m) || tokens < 1 || tokens > kMaxTokens || cols > kPrefillMaxCols) return false;
-  return x_budget(mode_of(n), dev) >= 2 * size_t(tokens) * 64 && ceil_div(rows, 16) <= INT32_MAX;
+  return x_budget(mode_of(n), dev) >= 2 * size_t(tokens) * 128 && ceil_div(rows, 16) <= INT32_MAX;
 }
 
 bool use_skinny(int64_t rows, int64_t cols, int64_t batch, int n, int m, const DeviceInfo& dev) {

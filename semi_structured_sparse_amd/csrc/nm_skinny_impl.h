@@ -1,34 +1,30 @@
-// Small-batch 2:4 product on the gfx950 sparse matrix instruction: Y [tokens][rows] =
-// X [tokens][cols] W'^T for 1 <= tokens <= 16, W' given as the packed 2:4 values and
-// bitmask (the batch side of the SpMV / SpMM split the news.bitwarelabs.com page draws in
-// "What's new"; bitmask format of the aimodeling.com page, "The Kernel Is the Other Half of
-// the Answer").
+// Small-batch 50% products on the gfx950 matrix instructions: Y [tokens][rows] =
+// X [tokens][cols] W'^T for 1 <= tokens <= 16, W' given as the packed values and bitmask
+// (the batch side of the SpMV / SpMM split the news.bitwarelabs.com page draws in "What's
+// new"; bitmask format of the aimodeling.com page, "The Kernel Is the Other Half of the
+// Answer").
 //
 // With at most 16 tokens the product is bound by reading the packed weights once, like the
-// batch-one SpMV, so the kernel is laid out like the SpMV: a workgroup holds RG row groups
-// of 16 * TR rows, each split over CS waves along the columns (RG * CS <= 16; the other
-// waves only help stage X); X of all tokens sits in LDS
-// (in column phases when it does not fit); each wave streams its rows' values and masks
-// with no barrier in its loop and multiplies them on the sparse matrix instruction (one
-// 16 x 16 x 64 instruction per 16 rows and 64 columns covers every token), and the CS
-// partial tiles of a row group are summed through LDS at the end.
+// batch-one SpMV, so the kernels are laid out like the SpMV: a workgroup holds RG row groups
+// of 16 rows, each split over CS waves along the columns (RG * CS <= 16; the other waves
+// only help stage X); X of all tokens sits in LDS (in column phases when it does not fit);
+// each wave streams its rows' values and masks with no barrier in its loop and multiplies
+// them on a matrix instruction that covers every token at once, and the CS partial tiles of
+// a row group are summed through LDS at the end.
 //
-// Operand layouts, the K permutation that makes a lane's 8 values contiguous in the packed
-// row, the position codes and the mask-block permute are those of the prefill kernel
-// (nm_prefill_impl.h), with mask blocks of 4 steps here (a wave may own only 4 steps):
-// lane (q = l / 16, li = l % 16) holds values 8q .. 8q+7 of a 64-column step for row li,
-// and the X fragment of token li at column chunks q and 4 + q of the step.
+// 2:4 (skinny_spmm_kernel<1, false>): the 2:4 sparse instruction (16 x 16 x 64) directly,
+// with the position codes of the prefill kernel (nm_prefill_impl.h). 4:8 and 8:16
+// (skinny_spmm_kernel<1, true>): these patterns keep exactly 8 values in every 16 aligned
+// columns, so each 4-column group is split into two 2:4 operands (its first two kept values,
+// and the rest) by the split tables of nm_prefill_impl.h, kept in LDS; both operands go
+// through the sparse instruction with the same X fragment. Both read whole 128-byte lines
+// per load (skinny_line_body).
 //
-// 4:8 and 8:16 (SPLIT): each 4-column group is split into two 2:4 operands (its first two
-// kept values, and the rest) by the split tables of nm_prefill_impl.h, which this kernel
-// keeps in LDS; both operands go through the sparse instruction with the same X fragment.
-//
-// 16:32 (EXPAND, skinny_expand_kernel): a word's 16 kept values may sit anywhere in its 32
-// columns, so the dense 16 x 16 x 32 instruction takes each word, with the lanes' fragments
-// expanded to dense columns: each wave writes the step's loaded values (16 rows x 64 bytes)
-// to its own LDS area, and lane (row, q) reads the 8 halves from its mask byte's first kept
-// value on and places them with the expansion table (nm_prefill_impl.h). The X fragments,
-// loads, mask blocks and reduction are those of the 2:4 kernel.
+// 16:32 (skinny_expand_kernel): a word's 16 kept values may sit anywhere in its 32 columns,
+// so the dense 16 x 16 x 32 instruction takes each word, with the lanes' fragments expanded
+// to dense columns: each wave writes the step's loaded values (16 rows x 64 bytes) to its
+// own LDS area, and lane (row, q) reads the 8 halves from its mask byte's first kept value
+// on and places them with the expansion table (nm_prefill_impl.h) (skinny_expand_body).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -43,16 +39,14 @@ using namespace prefill_detail;
 
 constexpr int kMaxWaves = 16;
 constexpr int kMaxTokens = 16;
-constexpr int kMaskSteps = 4;   // 64-column steps per mask block
-constexpr int kDepth = 4;       // value loads in flight per row tile
 constexpr int kThreadsFixed = 64 * kMaxWaves;           // every launch uses 16 waves
 constexpr int kXChunksPerThread = 8;                    // X staged per phase: <= 8 x 16 B per thread
 constexpr size_t kMaxXBytes = size_t(kThreadsFixed) * kXChunksPerThread * 16;   // 128 KiB
 
 // LDS bytes of the X buffer for `tokens` rows of `phase_cols` columns, and of the reduction
-// area for `waves` waves of TR tiles (one float4 per lane per tile).
+// area for `waves` waves (one float4 per lane).
 __host__ __device__ inline size_t x_bytes(int tokens, int phase_cols) { return size_t(tokens) * phase_cols * 2; }
-__host__ __device__ inline size_t red_bytes(int waves, int tr) { return size_t(waves) * tr * 64 * 16; }
+__host__ __device__ inline size_t red_bytes(int waves) { return size_t(waves) * 64 * 16; }
 
 // LDS byte offset of 16-byte chunk c of token t, rows of rb bytes: the low 3 bits of the
 // chunk index are XORed with the token's (8 tokens read at a time land on 8 bank groups).
@@ -60,69 +54,166 @@ __device__ __forceinline__ uint32_t xoff(int t, int c, uint32_t rb) {
   return uint32_t(t) * rb + (uint32_t(c ^ (t & 7)) << 4);
 }
 
-
 // What the kernel does with the packed operand: 2:4 directly, 4:8 / 8:16 split, 16:32
 // expanded.
 constexpr int kModeDirect = 0, kModeSplit = 1, kModeExpand = 2;
-// EXPAND: LDS bytes of one wave's area per row tile: the step's values of 16 rows (64 bytes
-// each) and room for a window read past the last row's second word
+// EXPAND: LDS bytes of one wave's area: the step's values of 16 rows (64 bytes each) and
+// room for a window read past the last row's second word
 constexpr uint32_t kExpandWaveBytes = 16 * 64 + 64;
 
 // LDS bytes ahead of X: the split tables, or the expansion table and the waves' value areas.
-template <int TR, int MODE>
+template <int MODE>
 __host__ __device__ constexpr uint32_t lead_bytes() {
   return MODE == kModeSplit ? kSplitLutBytes
-       : MODE == kModeExpand ? kExpandBytes + uint32_t(kMaxWaves) * TR * kExpandWaveBytes
+       : MODE == kModeExpand ? kExpandBytes + uint32_t(kMaxWaves) * kExpandWaveBytes
                              : 0u;
 }
 
-template <int TR, int MODE>
-__device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ values, const uint32_t* __restrict__ masks,
-                                            const uint16_t* __restrict__ X, uint16_t* __restrict__ Y, int rows,
-                                            int cols, int tokens, int rg_count, int cs_count, int phase_cols) {
-  constexpr bool SPLIT = MODE == kModeSplit;
-  constexpr bool EXPAND = MODE == kModeExpand;
-  extern __shared__ __attribute__((aligned(16))) char lds_base[];
-  // SPLIT: the split tables first, X after them; EXPAND: the expansion table and the waves'
-  // value areas, then X
-  char* const lds = lds_base + lead_bytes<TR, MODE>();
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  // the wave index and everything derived from it are wave-uniform (scalar registers): the
-  // loop bounds, the step offsets and the checks on them cost no vector instructions
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int q = lane >> 4, li = lane & 15;
-  const int rg = wave / cs_count, cs = wave - rg * cs_count;
-  // waves past rg_count * cs_count (when 16 is not a multiple of cs_count) stage X and meet
-  // the barriers but own no rows
-  const bool active = rg < rg_count;
-  const int wg_rows_max = rg_count * 16 * TR;
-  const int wg_r0 = int(blockIdx.x) * wg_rows_max;
-  const int wg_rows = min(wg_rows_max, rows - wg_r0);
-  const int words = cols >> 5;
+// The workgroup's view of the launch: its rows, the wave's place in them, and the buffer
+// resources of its slices of the packed matrix and of X.
+struct Tile {
+  int lane, wave, q, li, rg, cs;
+  bool active;   // the wave owns rows (rg < rg_count)
+  int wg_r0, words;
+  __amdgpu_buffer_rsrc_t vr, mr, xr;
 
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(values + size_t(wg_r0) * unsigned(cols >> 1), int64_t(wg_rows) * cols);
-  const __amdgpu_buffer_rsrc_t mr = make_rsrc(masks + size_t(wg_r0) * unsigned(words), int64_t(wg_rows) * words * 4);
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, int64_t(tokens) * cols * 2);
-  uint32_t voff[TR], moff[TR];
-#pragma unroll
-  for (int a = 0; a < TR; ++a) {
-    const uint32_t rl = uint32_t(rg * 16 * TR + 16 * a + li);   // row within the workgroup
-    voff[a] = rl * uint32_t(cols) + 16u * uint32_t(q);
-    moff[a] = rl * uint32_t(words) * 4u + 8u * uint32_t(q);
+  __device__ __forceinline__ Tile(const uint16_t* values, const uint32_t* masks, const uint16_t* X, int rows,
+                                  int cols, int tokens, int rg_count, int cs_count) {
+    const int tid = threadIdx.x;
+    lane = tid & 63;
+    // the wave index and everything derived from it are wave-uniform (scalar registers):
+    // the loop bounds, the step offsets and the checks on them cost no vector instructions
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    q = lane >> 4;
+    li = lane & 15;
+    rg = wave / cs_count;
+    cs = wave - rg * cs_count;
+    // waves past rg_count * cs_count (when 16 is not a multiple of cs_count) stage X and
+    // meet the barriers but own no rows
+    active = rg < rg_count;
+    const int wg_rows_max = rg_count * 16;
+    wg_r0 = int(blockIdx.x) * wg_rows_max;
+    const int wg_rows = min(wg_rows_max, rows - wg_r0);
+    words = cols >> 5;
+    vr = make_rsrc(values + size_t(wg_r0) * unsigned(cols >> 1), int64_t(wg_rows) * cols);
+    mr = make_rsrc(masks + size_t(wg_r0) * unsigned(words), int64_t(wg_rows) * words * 4);
+    xr = make_rsrc(X, int64_t(tokens) * cols * 2);
   }
-  const int qcol = 32 * (q >> 1);
-  const uint32_t mshift = 16u * uint32_t(q & 1);
-  const bool tok_live = li < tokens;
+};
+
+// X[0 .. tokens)[p0 .. p0 + chunks * 8) of one phase: flat chunk k = tid + kThreadsFixed * j
+// of token t = k / chunks, chunk c = k % chunks (one division, then steps of kThreadsFixed).
+// Chunks past the row load out of range (zero); chunks past the end are not written.
+struct XStage {
+  uint4 xs[kXChunksPerThread];
+  uint32_t xdst[kXChunksPerThread];
+
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t xr, int tokens, int cols, int p0, int chunks,
+                                       uint32_t rb) {
+    const int tid = threadIdx.x;
+    const int nchunks = tokens * chunks;
+    const int dt = kThreadsFixed / chunks, dc = kThreadsFixed - dt * chunks;
+    int t = tid / chunks, c = tid - t * chunks;
+#pragma unroll
+    for (int j = 0; j < kXChunksPerThread; ++j) {
+      const int k = tid + kThreadsFixed * j;
+      const int col = p0 + 8 * c;
+      const bool ok = k < nchunks && col < cols;
+      xs[j] = buf_load16(xr, ok ? (uint32_t(t) * uint32_t(cols) + uint32_t(col)) * 2u : kOutOfRange);
+      xdst[j] = k < nchunks ? xoff(t, c, rb) : 0xFFFFFFFFu;
+      t += dt;
+      c += dc;
+      if (c >= chunks) { c -= chunks; ++t; }
+    }
+  }
+
+  __device__ __forceinline__ void store(char* lds) const {
+#pragma unroll
+    for (int j = 0; j < kXChunksPerThread; ++j)
+      if (xdst[j] != 0xFFFFFFFFu) *reinterpret_cast<uint4*>(lds + xdst[j]) = xs[j];
+  }
+};
+
+// The CS partial tiles of each row group summed through LDS in a fixed order; the group's
+// first wave rounds once and stores. D layout of the instructions: lane (q, li) holds token
+// li, rows 4q .. 4q+3 of the tile.
+__device__ __forceinline__ void reduce_store(const Tile& w, f4_t acc, int cs_count, int rows, int tokens,
+                                             uint16_t* __restrict__ Y, char* lds_base) {
+  __syncthreads();
+  float4* red = reinterpret_cast<float4*>(lds_base);
+  red[w.wave * 64 + w.lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  __syncthreads();
+  if (w.cs != 0 || !w.active) return;
+  float4 s = red[w.wave * 64 + w.lane];
+  for (int k = 1; k < cs_count; ++k) {
+    const float4 v = red[(w.wave + k) * 64 + w.lane];
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  const int row = w.wg_r0 + w.rg * 16 + 4 * w.q;
+  if (w.li >= tokens || row >= rows) return;
+  uint16_t* out = Y + size_t(w.li) * unsigned(rows);
+  const float e[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (row + k < rows) out[row + k] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(e[k]));
+}
+
+// ---- 2:4 (DIRECT) and 4:8 / 8:16 (SPLIT): whole 128-byte lines per load.
+// The instruction's A layout puts 16 rows on the lanes of every 16-lane row (lane l: row
+// l % 16), so a load shaped like the operand covers 16 rows x 64 bytes: half of each row's
+// 128-byte line, whose other half the next step's load requests later. Measured on MI355X
+// this holds the weight stream well below the SpMV's (14336 x 4096 at 8 vectors: 20.3 us
+// with such loads against 16.7 us when every load covers whole lines). So each load here
+// covers 8 rows x one whole line (128 columns, two 64-column products): load h (0, 1) gives
+// lane l row 8h + l % 8 and 16-byte chunk 2 (l / 16) + (l / 8) % 2 of the line. One row_ror:8
+// DPP move and a select per dword then give, for j = 0, 1, the operand T_j in which lane l
+// holds row l % 16, chunk 2 (l / 16) + j:
+//   T_0 = (l % 16 < 8) ? load0 : ror8(load1),   T_1 = (l % 16 < 8) ? ror8(load0) : load1.
+// Product j takes T_j, so its logical K index k (A lane q holds k = 16q .. 16q+15) sits at
+// line column 32 (k / 16) + 16 j + k % 16: the X fragment of lane q (K = 8q .. 8q+7 and
+// 32+8q .. 32+8q+7) is the line's 8-column chunks 4 (q / 2) + q % 2 + 2 j and that plus 8,
+// and the mask bits of lane q are half j of the line's word q.
+__device__ __forceinline__ uint4 ror8_rows(uint4 v) {   // row_ror:8 inside every 16-lane row
+  return make_uint4(uint32_t(__builtin_amdgcn_mov_dpp(int(v.x), 0x128, 0xF, 0xF, false)),
+                    uint32_t(__builtin_amdgcn_mov_dpp(int(v.y), 0x128, 0xF, 0xF, false)),
+                    uint32_t(__builtin_amdgcn_mov_dpp(int(v.z), 0x128, 0xF, 0xF, false)),
+                    uint32_t(__builtin_amdgcn_mov_dpp(int(v.w), 0x128, 0xF, 0xF, false)));
+}
+
+__device__ __forceinline__ uint4 sel4(bool c, uint4 a, uint4 b) {
+  return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
+constexpr int kLineDepth = 2;   // lines (two loads each) in flight per wave
+constexpr int kMaskLines = 2;   // lines per mask block (8 words of each row)
+
+template <int MODE>
+__device__ __forceinline__ void skinny_line_body(const uint16_t* __restrict__ values,
+                                                 const uint32_t* __restrict__ masks,
+                                                 const uint16_t* __restrict__ X, uint16_t* __restrict__ Y,
+                                                 int rows, int cols, int tokens, int rg_count, int cs_count,
+                                                 int phase_cols) {
+  constexpr bool SPLIT = MODE == kModeSplit;
+  static_assert(MODE == kModeDirect || MODE == kModeSplit, "whole-line loads: 2:4 and the split patterns");
+  extern __shared__ __attribute__((aligned(16))) char lds_base[];
+  char* const lds = lds_base + lead_bytes<MODE>();   // SPLIT: the split tables first, X after them
+  const int tid = threadIdx.x;
+  const Tile w(values, masks, X, rows, cols, tokens, rg_count, cs_count);
+  const int q = w.q, li = w.li;
+  // value loads: lane l of load h reads row 8h + l % 8 of the row group, chunk kc of the line
+  const int kc = 2 * q + ((w.lane >> 3) & 1);
+  const uint32_t voff0 = uint32_t(w.rg * 16 + (w.lane & 7)) * uint32_t(cols) + 16u * uint32_t(kc);
+  const uint32_t voff1 = voff0 + 8u * uint32_t(cols);
+  // mask blocks: lane (q, li) holds words 2q, 2q+1 of the block for row li
+  const uint32_t moff = uint32_t(w.rg * 16 + li) * uint32_t(w.words) * 4u + 8u * uint32_t(q);
+  const bool lo8 = (w.lane & 8) == 0;
+  const int xq = 4 * (q >> 1) + (q & 1);   // X chunk of lane q in product 0 of a line
   // token rows past the batch read the last token's X: their products are never stored
   const int xt = min(li, tokens - 1);
 
-  f4_t acc[TR];
-#pragma unroll
-  for (int a = 0; a < TR; ++a) acc[a] = f4_t{0.f, 0.f, 0.f, 0.f};
-
-  uint4 vb[kDepth][TR];
-  uint2 mcur[TR], mnext[TR];
+  f4_t acc = f4_t{0.f, 0.f, 0.f, 0.f};
+  uint4 va[kLineDepth], vb[kLineDepth];
+  uint2 mcur, mnext;
   // SPLIT: this thread's 16-byte chunks of the split tables (1024 + 64 chunks), loaded
   // before anything else so that the waits for X below cover them
   uint4 lut_a{}, lut_b{};
@@ -131,66 +222,37 @@ __device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ values,
     lut_a = tab[tid];
     lut_b = tab[2 * kSplitEntries + (tid & 63)];
   }
-  if constexpr (EXPAND) {   // the expansion table: 2 * kExpandEntries chunks of 16 bytes
-    const uint4* tab = reinterpret_cast<const uint4*>(&kExpandTable);
-    lut_a = tab[tid & (2 * kExpandEntries - 1)];
-  }
   for (int p0 = 0; p0 < cols; p0 += phase_cols) {
     const int pc = min(phase_cols, cols - p0);       // columns in this phase (multiple of 32)
     const uint32_t rb = uint32_t(2 * phase_cols);    // LDS bytes per token row
-    // this wave's steps of the phase
-    const int psteps = (pc + 63) / 64;
-    const int s_lo = int((int64_t(psteps) * cs) / cs_count), s_hi = int((int64_t(psteps) * (cs + 1)) / cs_count);
-    const int n = active ? s_hi - s_lo : 0;
+    // this wave's lines of the phase (phase_cols is a multiple of 128)
+    const int plines = (pc + 127) / 128;
+    const int l_lo = int((int64_t(plines) * w.cs) / cs_count);
+    const int l_hi = int((int64_t(plines) * (w.cs + 1)) / cs_count);
+    const int n = w.active ? l_hi - l_lo : 0;
     const int last = max(n - 1, 0);
-    const int c_lo = p0 + 64 * s_lo;                 // first column of the wave's range
-    // value loads: step s of the range is inside the row for this lane iff s < s_lim; steps
-    // past it (the last block's padding, a 32-column tail) load zeros, so they add exactly
-    // zero and every slot of a block runs the same code
-    const int s_lim = min(n, (cols - c_lo - qcol + 63) / 64);
-    uint32_t vbase[TR];
-#pragma unroll
-    for (int a = 0; a < TR; ++a) vbase[a] = voff[a] + uint32_t(c_lo);
-    auto load_v = [&](uint4 (&f)[TR], int s) {
-      const bool ok = s < s_lim;
-#pragma unroll
-      for (int a = 0; a < TR; ++a) f[a] = buf_load16(vr, ok ? vbase[a] + 64u * uint32_t(s) : kOutOfRange);
+    const int c_lo = p0 + 128 * l_lo;                // first column of the wave's range
+    // line p of the range holds this lane's chunk iff p < p_lim; lines past it (the last
+    // block's padding, a tail of 32 to 96 columns) load zeros, which add exactly zero
+    const int p_lim = min(n, (cols - c_lo - 16 * kc + 127) / 128);
+    const uint32_t vb0 = voff0 + uint32_t(c_lo), vb1 = voff1 + uint32_t(c_lo);
+    auto load_line = [&](uint4& f0, uint4& f1, int p) {
+      const bool ok = p < p_lim;
+      f0 = buf_load16(w.vr, ok ? vb0 + 128u * uint32_t(p) : kOutOfRange);
+      f1 = buf_load16(w.vr, ok ? vb1 + 128u * uint32_t(p) : kOutOfRange);
     };
-    auto load_m = [&](int s) {   // mask block starting at step s of the range (clamped into it)
-      const uint32_t cm = uint32_t(c_lo + 64 * min(s, last)) >> 3;
-#pragma unroll
-      for (int a = 0; a < TR; ++a) mnext[a] = buf_load8(mr, n > 0 ? moff[a] + cm : kOutOfRange);
+    auto load_m = [&](int p) {   // mask block starting at line p of the range (clamped into it)
+      const uint32_t cm = uint32_t(c_lo + 128 * min(p, last)) >> 3;
+      mnext = buf_load8(w.mr, n > 0 ? moff + cm : kOutOfRange);
     };
-    // ---- X[0 .. tokens)[p0 .. p0 + pc) into registers (columns past the row read as zero):
-    // flat chunk k = tid + kThreadsFixed * j of token t = k / chunks, chunk c = k % chunks
-    // (one division, then steps of kThreadsFixed); chunks past the end load out of range
-    // (zero) and are not written
-    const int chunks = psteps * 8;                   // 16-byte chunks per token row, whole steps
-    const int nchunks = tokens * chunks;
-    const int dt = kThreadsFixed / chunks, dc = kThreadsFixed - dt * chunks;
-    uint4 xs[kXChunksPerThread];
-    uint32_t xdst[kXChunksPerThread];
-    {
-      int t = tid / chunks, c = tid - t * chunks;
-#pragma unroll
-      for (int j = 0; j < kXChunksPerThread; ++j) {
-        const int k = tid + kThreadsFixed * j;
-        const int col = p0 + 8 * c;
-        const bool ok = k < nchunks && col < cols;
-        xs[j] = buf_load16(xr, ok ? (uint32_t(t) * uint32_t(cols) + uint32_t(col)) * 2u : kOutOfRange);
-        xdst[j] = k < nchunks ? xoff(t, c, rb) : 0xFFFFFFFFu;
-        t += dt;
-        c += dc;
-        if (c >= chunks) { c -= chunks; ++t; }
-      }
-    }
-    // then the first weight loads: they are in flight while X is written to LDS (the X
-    // loads were issued first, so waiting for them does not wait for these). The mask
-    // block goes first, as in the loop (mask block, then the block's value loads), so the
-    // waits the loop needs are the same on its first pass as on later ones.
+    XStage xst;
+    xst.load(w.xr, tokens, cols, p0, plines * 16, rb);
+    // then the first weight loads, in flight while X is written to LDS (the X loads were
+    // issued first, so waiting for them does not wait for these; mask block first, as in
+    // the loop, so that the loop's waits are the same on every pass)
     load_m(0);
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) load_v(vb[d], d);
+    for (int d = 0; d < kLineDepth; ++d) load_line(va[d], vb[d], d);
     __syncthreads();                                 // the previous phase's LDS reads are done
     if constexpr (SPLIT) {
       if (p0 == 0) {
@@ -198,80 +260,48 @@ __device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ values,
         if (tid < 64) reinterpret_cast<uint4*>(lds_base)[2 * kSplitEntries + tid] = lut_b;
       }
     }
-    if constexpr (EXPAND) {
-      if (p0 == 0 && tid < 2 * kExpandEntries) reinterpret_cast<uint4*>(lds_base)[tid] = lut_a;
-    }
-#pragma unroll
-    for (int j = 0; j < kXChunksPerThread; ++j)
-      if (xdst[j] != 0xFFFFFFFFu) *reinterpret_cast<uint4*>(lds + xdst[j]) = xs[j];
+    xst.store(lds);
     __syncthreads();
     if (n > 0) {
-      const uint32_t b_lo = xoff(xt, q, rb), b_hi = xoff(xt, 4 + q, rb);
-      for (int s0 = 0; s0 < n; s0 += kMaskSteps) {
-        // 2:4: the position codes of the block's words, once per block; the steps then
-        // only fetch and shift them
+      // X fragment addresses of products 0 and 1 of the phase's first line
+      const uint32_t b_lo0 = xoff(xt, xq, rb), b_hi0 = xoff(xt, xq + 8, rb);
+      const uint32_t b_lo1 = xoff(xt, xq + 2, rb), b_hi1 = xoff(xt, xq + 10, rb);
+      for (int pb = 0; pb < n; pb += kMaskLines) {
+        // 2:4: the position codes of the block's words, once per block
+        mcur = SPLIT ? mnext : make_uint2(pair_codes32(mnext.x), pair_codes32(mnext.y));
+        load_m(pb + kMaskLines);
 #pragma unroll
-        for (int a = 0; a < TR; ++a)
-          mcur[a] = (SPLIT || EXPAND) ? mnext[a] : make_uint2(pair_codes32(mnext[a].x), pair_codes32(mnext[a].y));
-        load_m(s0 + kMaskSteps);
-#pragma unroll
-        for (int j = 0; j < kMaskSteps; ++j) {
-          const int s = s0 + j;
-          // the products read vb[j] in place; its next load is issued after them, so the
-          // registers are never copied (a copy would wait for every load in flight)
-          const uint4 (&cur)[TR] = vb[j % kDepth];
-          const int src = 4 * (li + 16 * j);
-          // X of the step (chunks 8 (s_lo + s) ..); zero past the range (a wave-uniform test)
-          uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-          if (s < n) {
-            const uint32_t cb = uint32_t(s_lo + s) * 128u;
-            lo = *reinterpret_cast<const uint4*>(lds + b_lo + cb);
-            hi = *reinterpret_cast<const uint4*>(lds + b_hi + cb);
+        for (int j = 0; j < kMaskLines; ++j) {
+          const int p = pb + j;
+          const int d = j % kLineDepth;
+          // word q of line j of the block is word 4j + q, held by lane (li, 2j + q / 2) as
+          // component q % 2
+          const int src = 4 * (li + 16 * (2 * j + (q >> 1)));
+          const uint32_t wx = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur.x)));
+          const uint32_t wy = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur.y)));
+          const uint32_t word = (q & 1) ? wy : wx;
+          // the line's two operands in the instruction's layout
+          const uint4 t0 = sel4(lo8, va[d], ror8_rows(vb[d]));
+          const uint4 t1 = sel4(lo8, ror8_rows(va[d]), vb[d]);
+          // X of the line's two products; zero past the range (a wave-uniform test)
+          uint4 x0l = make_uint4(0, 0, 0, 0), x0h = x0l, x1l = x0l, x1h = x0l;
+          if (p < n) {
+            const uint32_t cb = uint32_t(l_lo + p) * 256u;
+            x0l = *reinterpret_cast<const uint4*>(lds + b_lo0 + cb);
+            x0h = *reinterpret_cast<const uint4*>(lds + b_hi0 + cb);
+            x1l = *reinterpret_cast<const uint4*>(lds + b_lo1 + cb);
+            x1h = *reinterpret_cast<const uint4*>(lds + b_hi1 + cb);
           }
-          const u8_t xv = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          const h16_t bf = __builtin_bit_cast(h16_t, xv);
+          // the loaded registers are free once the operands are formed: the line after the
+          // next one is requested now, while the products run
+          load_line(va[d], vb[d], p + kLineDepth);
 #pragma unroll
-          for (int a = 0; a < TR; ++a) {
-            const uint32_t w0 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur[a].x)));
-            const uint32_t w1 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur[a].y)));
-            if constexpr (EXPAND) {
-              // the step's values to this wave's area (row li at 64 li, lane q's 16 bytes at
-              // 16 q), visible to the other lanes of the wave before they are read back
-              char* const va = lds_base + kExpandBytes + uint32_t(wave * TR + a) * kExpandWaveBytes;
-              *reinterpret_cast<uint4*>(va + 64 * li + 16 * q) = cur[a];
-              __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-              __builtin_amdgcn_wave_barrier();
-              __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-              for (int i = 0; i < 2; ++i) {   // word i of the step: one dense 16 x 16 x 32 product
-                const uint32_t w = i ? w1 : w0;
-                const uint32_t byte = __builtin_amdgcn_ubfe(w, 8u * uint32_t(q), 8);
-                // first kept value of the lane's byte among the word's 16 (at most 16 for a
-                // valid mask; clamped so that any mask keeps the window inside the area)
-                const uint32_t pc = min(uint32_t(__builtin_popcount(w & ((1u << (8 * q)) - 1u))), 16u);
-                const uint32_t off = 64u * uint32_t(li) + 32u * uint32_t(i) + 2u * pc;   // window, bytes
-                const uint32_t* wd = reinterpret_cast<const uint32_t*>(va + (off & ~3u));
-                const uint32_t sh = (off & 2u) * 8u;   // 16 when the window starts mid-dword
-                const uint32_t r0 = wd[0], r1 = wd[1], r2 = wd[2], r3 = wd[3], r4 = wd[4];
-                const uint32_t v0 = __builtin_amdgcn_alignbit(r1, r0, sh), v1 = __builtin_amdgcn_alignbit(r2, r1, sh);
-                const uint32_t v2 = __builtin_amdgcn_alignbit(r3, r2, sh), v3 = __builtin_amdgcn_alignbit(r4, r3, sh);
-                const uint4 s0 = *reinterpret_cast<const uint4*>(lds_base + 32u * byte);
-                const uint4 s1 = *reinterpret_cast<const uint4*>(lds_base + 32u * byte + 16u);
-                auto pick = [&](uint32_t lo_sel, uint32_t hi_sel) {
-                  return __builtin_amdgcn_perm(v1, v0, lo_sel) | __builtin_amdgcn_perm(v3, v2, hi_sel);
-                };
-                const uint4 dense = make_uint4(pick(s0.x, s0.y), pick(s0.z, s0.w), pick(s1.x, s1.y), pick(s1.z, s1.w));
-                const uint4 xf = i ? hi : lo;   // X of the word's columns 8q .. 8q+7, every token
-                acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, dense),
-                                                                __builtin_bit_cast(h8_t, xf), acc[a], 0, 0, 0);
-              }
-              // every lane has read the area before the next step writes it
-              __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-              __builtin_amdgcn_wave_barrier();
-              __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-              continue;
-            }
-            const uint32_t m16 = __builtin_amdgcn_ubfe((q >> 1) ? w1 : w0, mshift, 16);
+          for (int h = 0; h < 2; ++h) {
+            const uint4 cur = h ? t1 : t0;
+            const uint4 lo = h ? x1l : x0l, hi = h ? x1h : x0h;
+            const u8_t xv = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            const h16_t bf = __builtin_bit_cast(h16_t, xv);
+            const uint32_t m16 = __builtin_amdgcn_ubfe(word, 16u * uint32_t(h), 16);
             if constexpr (SPLIT) {
               const uint32_t e0 = 32u * (m16 & 0xFFu), e1 = 32u * (256u + (m16 >> 8));
               const uint4 s0 = *reinterpret_cast<const uint4*>(lds_base + e0);
@@ -280,52 +310,150 @@ __device__ __forceinline__ void skinny_body(const uint16_t* __restrict__ values,
               const uint4 s3 = *reinterpret_cast<const uint4*>(lds_base + e1 + 16);
               const uint16_t* codes = reinterpret_cast<const uint16_t*>(lds_base + kSplitSelBytes);
               const uint32_t i0 = codes[m16 & 0xFFu], i1 = codes[256u + (m16 >> 8)];
-              const uint4 v = cur[a];
               auto pick = [&](uint32_t lo_sel, uint32_t hi_sel) {
-                return __builtin_amdgcn_perm(v.y, v.x, lo_sel) | __builtin_amdgcn_perm(v.w, v.z, hi_sel);
+                return __builtin_amdgcn_perm(cur.y, cur.x, lo_sel) | __builtin_amdgcn_perm(cur.w, cur.z, hi_sel);
               };
-              const uint4 va = make_uint4(pick(s0.x, s0.y), pick(s1.x, s1.y), pick(s2.x, s2.y), pick(s3.x, s3.y));
-              const uint4 vb2 = make_uint4(pick(s0.z, s0.w), pick(s1.z, s1.w), pick(s2.z, s2.w), pick(s3.z, s3.w));
+              const uint4 opa = make_uint4(pick(s0.x, s0.y), pick(s1.x, s1.y), pick(s2.x, s2.y), pick(s3.x, s3.y));
+              const uint4 opb = make_uint4(pick(s0.z, s0.w), pick(s1.z, s1.w), pick(s2.z, s2.w), pick(s3.z, s3.w));
               const int ia = int(__builtin_amdgcn_perm(i1, i0, 0x0C0C0400u));   // A codes of groups 0..3
               const int ib = int(__builtin_amdgcn_perm(i1, i0, 0x0C0C0501u));   // B codes
-              acc[a] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(h8_t, va), bf, acc[a], ia, 0, 0);
-              acc[a] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(h8_t, vb2), bf, acc[a], ib, 0, 0);
+              acc = __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(h8_t, opa), bf, acc, ia, 0, 0);
+              acc = __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(h8_t, opb), bf, acc, ib, 0, 0);
             } else {
               // m16 holds the position codes of the lane's 4 groups
-              acc[a] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(h8_t, cur[a]), bf, acc[a],
-                                                                int(m16), 0, 0);
+              acc = __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(h8_t, cur), bf, acc, int(m16), 0, 0);
             }
           }
-          load_v(vb[j % kDepth], s + kDepth);
         }
       }
     }
   }
-  // ---- sum the CS partial tiles of each row group; the first wave of the group stores
-  __syncthreads();
-  float4* red = reinterpret_cast<float4*>(lds_base);
-#pragma unroll
-  for (int a = 0; a < TR; ++a)
-    red[(wave * TR + a) * 64 + lane] = make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
-  __syncthreads();
-  if (cs != 0 || !active) return;
-#pragma unroll
-  for (int a = 0; a < TR; ++a) {
-    float4 s = red[(wave * TR + a) * 64 + lane];
-    for (int w = 1; w < cs_count; ++w) {
-      const float4 v = red[((wave + w) * TR + a) * 64 + lane];
-      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-    }
-    const int row = wg_r0 + rg * 16 * TR + 16 * a + 4 * q;
-    if (!tok_live || row >= rows) continue;
-    uint16_t* out = Y + size_t(li) * unsigned(rows);
-    const float e[4] = {s.x, s.y, s.z, s.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (row + k < rows) out[row + k] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(e[k]));
-  }
+  reduce_store(w, acc, cs_count, rows, tokens, Y, lds_base);
 }
 
+// ---- 16:32 (EXPAND): 64-column steps, each wave's values of a step through its own LDS area.
+constexpr int kMaskSteps = 4;   // 64-column steps per mask block
+constexpr int kDepth = 4;       // value loads in flight per wave
+
+__device__ __forceinline__ void skinny_expand_body(const uint16_t* __restrict__ values,
+                                                   const uint32_t* __restrict__ masks,
+                                                   const uint16_t* __restrict__ X, uint16_t* __restrict__ Y,
+                                                   int rows, int cols, int tokens, int rg_count, int cs_count,
+                                                   int phase_cols) {
+  extern __shared__ __attribute__((aligned(16))) char lds_base[];
+  // the expansion table and the waves' value areas, then X
+  char* const lds = lds_base + lead_bytes<kModeExpand>();
+  const int tid = threadIdx.x;
+  const Tile w(values, masks, X, rows, cols, tokens, rg_count, cs_count);
+  const int q = w.q, li = w.li;
+  // lane (q, li) loads values 8q .. 8q+7 of a 64-column step for row li, and words 2q, 2q+1
+  // of a mask block
+  const uint32_t rl = uint32_t(w.rg * 16 + li);   // row within the workgroup
+  const uint32_t voff = rl * uint32_t(cols) + 16u * uint32_t(q);
+  const uint32_t moff = rl * uint32_t(w.words) * 4u + 8u * uint32_t(q);
+  const int qcol = 32 * (q >> 1);
+  // token rows past the batch read the last token's X: their products are never stored
+  const int xt = min(li, tokens - 1);
+  char* const area = lds_base + kExpandBytes + uint32_t(w.wave) * kExpandWaveBytes;
+
+  f4_t acc = f4_t{0.f, 0.f, 0.f, 0.f};
+  uint4 vbuf[kDepth];
+  uint2 mcur, mnext;
+  // the expansion table: 2 * kExpandEntries chunks of 16 bytes, loaded first so that the
+  // waits for X cover it
+  const uint4 lut = reinterpret_cast<const uint4*>(&kExpandTable)[tid & (2 * kExpandEntries - 1)];
+  for (int p0 = 0; p0 < cols; p0 += phase_cols) {
+    const int pc = min(phase_cols, cols - p0);       // columns in this phase (multiple of 32)
+    const uint32_t rb = uint32_t(2 * phase_cols);    // LDS bytes per token row
+    // this wave's steps of the phase
+    const int psteps = (pc + 63) / 64;
+    const int s_lo = int((int64_t(psteps) * w.cs) / cs_count), s_hi = int((int64_t(psteps) * (w.cs + 1)) / cs_count);
+    const int n = w.active ? s_hi - s_lo : 0;
+    const int last = max(n - 1, 0);
+    const int c_lo = p0 + 64 * s_lo;                 // first column of the wave's range
+    // value loads: step s of the range is inside the row for this lane iff s < s_lim; steps
+    // past it (the last block's padding, a 32-column tail) load zeros, so they add exactly
+    // zero and every slot of a block runs the same code
+    const int s_lim = min(n, (cols - c_lo - qcol + 63) / 64);
+    const uint32_t vbase = voff + uint32_t(c_lo);
+    auto load_v = [&](uint4& f, int s) { f = buf_load16(w.vr, s < s_lim ? vbase + 64u * uint32_t(s) : kOutOfRange); };
+    auto load_m = [&](int s) {   // mask block starting at step s of the range (clamped into it)
+      const uint32_t cm = uint32_t(c_lo + 64 * min(s, last)) >> 3;
+      mnext = buf_load8(w.mr, n > 0 ? moff + cm : kOutOfRange);
+    };
+    XStage xst;
+    xst.load(w.xr, tokens, cols, p0, psteps * 8, rb);
+    load_m(0);
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) load_v(vbuf[d], d);
+    __syncthreads();                                 // the previous phase's LDS reads are done
+    if (p0 == 0 && tid < 2 * kExpandEntries) reinterpret_cast<uint4*>(lds_base)[tid] = lut;
+    xst.store(lds);
+    __syncthreads();
+    if (n > 0) {
+      const uint32_t b_lo = xoff(xt, q, rb), b_hi = xoff(xt, 4 + q, rb);
+      for (int s0 = 0; s0 < n; s0 += kMaskSteps) {
+        mcur = mnext;
+        load_m(s0 + kMaskSteps);
+#pragma unroll
+        for (int j = 0; j < kMaskSteps; ++j) {
+          const int s = s0 + j;
+          // the products read vbuf[j] in place; its next load is issued after them, so the
+          // registers are never copied (a copy would wait for every load in flight)
+          const uint4 cur = vbuf[j % kDepth];
+          const int src = 4 * (li + 16 * j);
+          // X of the step (chunks 8 (s_lo + s) ..); zero past the range (a wave-uniform test)
+          uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+          if (s < n) {
+            const uint32_t cb = uint32_t(s_lo + s) * 128u;
+            lo = *reinterpret_cast<const uint4*>(lds + b_lo + cb);
+            hi = *reinterpret_cast<const uint4*>(lds + b_hi + cb);
+          }
+          const uint32_t w0 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur.x)));
+          const uint32_t w1 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mcur.y)));
+          // the step's values to this wave's area (row li at 64 li, lane q's 16 bytes at
+          // 16 q), visible to the other lanes of the wave before they are read back
+          *reinterpret_cast<uint4*>(area + 64 * li + 16 * q) = cur;
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {   // word i of the step: one dense 16 x 16 x 32 product
+            const uint32_t wi = i ? w1 : w0;
+            const uint32_t byte = __builtin_amdgcn_ubfe(wi, 8u * uint32_t(q), 8);
+            // first kept value of the lane's byte among the word's 16 (at most 16 for a
+            // valid mask; clamped so that any mask keeps the window inside the area)
+            const uint32_t first = min(uint32_t(__builtin_popcount(wi & ((1u << (8 * q)) - 1u))), 16u);
+            const uint32_t off = 64u * uint32_t(li) + 32u * uint32_t(i) + 2u * first;   // window, bytes
+            const uint32_t* wd = reinterpret_cast<const uint32_t*>(area + (off & ~3u));
+            const uint32_t sh = (off & 2u) * 8u;   // 16 when the window starts mid-dword
+            const uint32_t r0 = wd[0], r1 = wd[1], r2 = wd[2], r3 = wd[3], r4 = wd[4];
+            const uint32_t v0 = __builtin_amdgcn_alignbit(r1, r0, sh), v1 = __builtin_amdgcn_alignbit(r2, r1, sh);
+            const uint32_t v2 = __builtin_amdgcn_alignbit(r3, r2, sh), v3 = __builtin_amdgcn_alignbit(r4, r3, sh);
+            const uint4 s0 = *reinterpret_cast<const uint4*>(lds_base + 32u * byte);
+            const uint4 s1 = *reinterpret_cast<const uint4*>(lds_base + 32u * byte + 16u);
+            auto pick = [&](uint32_t lo_sel, uint32_t hi_sel) {
+              return __builtin_amdgcn_perm(v1, v0, lo_sel) | __builtin_amdgcn_perm(v3, v2, hi_sel);
+            };
+            const uint4 dense = make_uint4(pick(s0.x, s0.y), pick(s0.z, s0.w), pick(s1.x, s1.y), pick(s1.z, s1.w));
+            const uint4 xf = i ? hi : lo;   // X of the word's columns 8q .. 8q+7, every token
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, dense),
+                                                         __builtin_bit_cast(h8_t, xf), acc, 0, 0, 0);
+          }
+          // every lane has read the area before the next step writes it
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          load_v(vbuf[j % kDepth], s + kDepth);
+        }
+      }
+    }
+  }
+  reduce_store(w, acc, cs_count, rows, tokens, Y, lds_base);
+}
+
+// TR (row tiles per wave) is 1: one 16-row tile per wave; the parameter stays in the kernel
+// names that profiles and tests refer to.
 template <int TR, bool SPLIT>
 __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16_t* __restrict__ values,
                                                                      const uint32_t* __restrict__ masks,
@@ -333,7 +461,8 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
                                                                      uint16_t* __restrict__ Y, int rows, int cols,
                                                                      int tokens, int rg_count, int cs_count,
                                                                      int phase_cols) {
-  skinny_body<TR, SPLIT ? kModeSplit : kModeDirect>(values, masks, X, Y, rows, cols, tokens, rg_count, cs_count,
+  static_assert(TR == 1, "one row tile per wave");
+  skinny_line_body<SPLIT ? kModeSplit : kModeDirect>(values, masks, X, Y, rows, cols, tokens, rg_count, cs_count,
                                                      phase_cols);
 }
 
@@ -344,7 +473,8 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_expand_kernel(const uint
                                                                        uint16_t* __restrict__ Y, int rows, int cols,
                                                                        int tokens, int rg_count, int cs_count,
                                                                        int phase_cols) {
-  skinny_body<TR, kModeExpand>(values, masks, X, Y, rows, cols, tokens, rg_count, cs_count, phase_cols);
+  static_assert(TR == 1, "one row tile per wave");
+  skinny_expand_body(values, masks, X, Y, rows, cols, tokens, rg_count, cs_count, phase_cols);
 }
 
 }  // namespace skinny_detail
