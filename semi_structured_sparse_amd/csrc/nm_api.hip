@@ -285,7 +285,7 @@ const char* nm_spmm_variant(int64_t rows, int64_t cols, int64_t batch, int N, in
   if (nm::prefill_pattern(N, M) && batch >= nm::kMatrixCoreMinBatch)
     return nm::prefill_fits(rows, cols, batch) ? nm::prefill_variant(rows, batch, true, dev, N != 2) : "";
   if (nm::use_skinny(rows, cols, batch, N, M, dev)) return nm::skinny_variant(N);
-  return nm::spmm_variant(N, batch < nm::kSmallBatch ? batch : nm::kSmallBatch);
+  return nm::spmm_variant(rows, cols, N, batch < nm::kSmallBatch ? batch : nm::kSmallBatch, dev);
 }
 
 const char* nm_prefill_variant(int64_t rows, int64_t cols, int64_t tokens, int sparse) {

@@ -63,9 +63,9 @@ hipError_t launch_spmm(const uint16_t* values, const uint32_t* masks, const uint
 hipError_t launch_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y, int64_t rows,
                        int64_t cols, int batch, hipStream_t stream, const DeviceInfo& dev);
 
-// Name of the small-batch kernel instantiation launch_spmm runs for pattern N:2N and a
-// batch of 1..8 vectors (static string; "" otherwise).
-const char* spmm_variant(int N, int64_t batch);
+// Name of the small-batch kernel instantiation launch_spmm runs for a rows x cols layer,
+// pattern N:2N and a batch of 1..8 vectors (static string; "" otherwise).
+const char* spmm_variant(int64_t rows, int64_t cols, int N, int64_t batch, const DeviceInfo& dev);
 
 // Name of the kernel configuration launch_spmv picks (static string) and its shape.
 const char* spmv_variant(int64_t rows, int64_t cols, int N, int M, const DeviceInfo& dev);

@@ -1,6 +1,8 @@
 // nm_spmm / nm_gemm_dense launchers: decoder, interleave, phase width and workgroup
 // shape for a batch of 1..8 activation vectors. The kernels are in nm_spmm_impl.h.
 #include <algorithm>
+#include <string>
+#include <vector>
 
 #include "nm_spmm_impl.h"
 
@@ -17,10 +19,14 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // per CU: up to 56 rows (7 groups of 8) and 16 / groups waves per group, 2..8 (48 rows
 // when a workgroup may hold at most 12 waves). For 14336x4096 at B = 8 that is 22.5 us
 // against 38.5 us with the single-vector rule's 8-row workgroups.
-template <int N, int B>
-WorkgroupShape spmm_shape(int64_t rows, const DeviceInfo& dev) {
+//
+// Narrow layers (at most 4 rows per workgroup): the lanes of the 8 row slots of a wave would
+// repeat rows, so the narrow kernel gives each row's slots CI = 2 (3..4 rows) or 4 (1..2
+// rows) parts of the wave's columns instead (ci), when every part still holds a whole batch
+// of 4 steps (1024 x 8192 and 1024 x 14336: 5-12% faster at 2..8 vectors; with fewer steps
+// per part, 1024 x 4096, it was 2-9% slower, so those keep CI = 1).
+WorkgroupShape spmm_shape_for(int64_t rows, int64_t cols, int maxw, const DeviceInfo& dev) {
   const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
-  const int maxw = max_waves<N, B>();
   const int64_t max_rpb = 8 * (maxw / 2);  // row groups of at least 2 waves
   WorkgroupShape s;
   const int64_t passes = ceil_div(rows, cus * max_rpb);
@@ -29,7 +35,28 @@ WorkgroupShape spmm_shape(int64_t rows, const DeviceInfo& dev) {
   s.cs = std::max(2, std::min(8, maxw / s.row_groups));
   if (s.row_groups * s.cs > maxw) s.cs = maxw / s.row_groups;
   s.grid = ceil_div(rows, s.rpb);
+  const int64_t wave_steps = ceil_div(cols, 128) / s.cs;   // steps per wave (at least)
+  for (int ci : {4, 2}) {
+    if (s.rpb <= 8 / ci && wave_steps >= int64_t(4) * ci) {
+      s.ci = ci;
+      break;
+    }
+  }
   return s;
+}
+
+template <int N, int B>
+WorkgroupShape spmm_shape(int64_t rows, int64_t cols, const DeviceInfo& dev) {
+  return spmm_shape_for(rows, cols, max_waves<N, B>(), dev);
+}
+
+template <int N, int B, int DEC>
+const void* spmm_kernel_for(int ci) {
+  switch (ci) {
+    case 2: return reinterpret_cast<const void*>(&spmm_narrow_kernel<N, B, DEC, 2>);
+    case 4: return reinterpret_cast<const void*>(&spmm_narrow_kernel<N, B, DEC, 4>);
+    default: return reinterpret_cast<const void*>(&spmm_kernel<N, B, DEC>);
+  }
 }
 
 template <int N, int B, int DEC>
@@ -39,12 +66,12 @@ hipError_t launch_sparse(const uint16_t* values, const uint32_t* masks, const ui
   const int cap = max_phase_cols<B, DEC>(size_t(dev.max_lds_per_block));
   if (cap < 128) return hipErrorInvalidValue;
   const int phase = int(std::min<int64_t>(cap, ceil_div(cols, 128) * 128));
-  const WorkgroupShape s = spmm_shape<N, B>(rows, dev);
+  const WorkgroupShape s = spmm_shape<N, B>(rows, cols, dev);
   const uint4* v4 = reinterpret_cast<const uint4*>(values);
   int rpb = s.rpb, cs = s.cs;
   void* args[] = {&v4, &masks, &X, &Y, &rows, &cols, &rpb, &cs, const_cast<int*>(&phase)};
-  return launch(reinterpret_cast<const void*>(&spmm_kernel<N, B, DEC>), dim3(unsigned(s.grid)),
-                dim3(unsigned(64 * s.row_groups * s.cs)), args, lds_bytes<B, DEC>(phase), stream, dev);
+  return launch(spmm_kernel_for<N, B, DEC>(s.ci), dim3(unsigned(s.grid)), dim3(unsigned(64 * s.row_groups * s.cs)),
+                args, lds_bytes<B, DEC>(phase), stream, dev);
 }
 
 template <int B>
@@ -118,15 +145,30 @@ hipError_t launch_spmm(const uint16_t* values, const uint32_t* masks, const uint
   }
 }
 
-const char* spmm_variant(int N, int64_t batch) {
+const char* spmm_variant(int64_t rows, int64_t cols, int N, int64_t batch, const DeviceInfo& dev) {
+  const int n = N == 2 ? 0 : N == 4 ? 1 : N == 8 ? 2 : N == 16 ? 3 : -1;
+  if (n < 0 || batch < 1 || batch > 8) return "";
   // the instantiations launch_sparse_b picks: byte table for N = 2, 4, 8, bit walk for 16
+  const int b = int(batch);
+  const int ci = spmm_shape_for(rows, cols, max_waves_of(N, b), dev).ci;
+  if (ci > 1) {
+    // spmm_narrow_kernel<N, B, DEC, CI> as profilers print it
+    static const std::vector<std::string> narrow = [] {
+      std::vector<std::string> v;
+      for (int nn : {2, 4, 8, 16})
+        for (int bb = 1; bb <= 8; ++bb)
+          for (int cc : {2, 4})
+            v.push_back("spmm_narrow_kernel<" + std::to_string(nn) + ", " + std::to_string(bb) + ", " +
+                        std::to_string(nn == 16 ? int(kBitWalk) : int(kByteLut)) + ", " + std::to_string(cc) + ">");
+      return v;
+    }();
+    return narrow[size_t((n * 8 + (b - 1)) * 2 + (ci == 4 ? 1 : 0))].c_str();
+  }
   static const char* const kNames[4][8] = {
       {"spmm_kernel<2, 1, 2>", "spmm_kernel<2, 2, 2>", "spmm_kernel<2, 3, 2>", "spmm_kernel<2, 4, 2>", "spmm_kernel<2, 5, 2>", "spmm_kernel<2, 6, 2>", "spmm_kernel<2, 7, 2>", "spmm_kernel<2, 8, 2>"},
       {"spmm_kernel<4, 1, 2>", "spmm_kernel<4, 2, 2>", "spmm_kernel<4, 3, 2>", "spmm_kernel<4, 4, 2>", "spmm_kernel<4, 5, 2>", "spmm_kernel<4, 6, 2>", "spmm_kernel<4, 7, 2>", "spmm_kernel<4, 8, 2>"},
       {"spmm_kernel<8, 1, 2>", "spmm_kernel<8, 2, 2>", "spmm_kernel<8, 3, 2>", "spmm_kernel<8, 4, 2>", "spmm_kernel<8, 5, 2>", "spmm_kernel<8, 6, 2>", "spmm_kernel<8, 7, 2>", "spmm_kernel<8, 8, 2>"},
       {"spmm_kernel<16, 1, 0>", "spmm_kernel<16, 2, 0>", "spmm_kernel<16, 3, 0>", "spmm_kernel<16, 4, 0>", "spmm_kernel<16, 5, 0>", "spmm_kernel<16, 6, 0>", "spmm_kernel<16, 7, 0>", "spmm_kernel<16, 8, 0>"}};
-  const int n = N == 2 ? 0 : N == 4 ? 1 : N == 8 ? 2 : N == 16 ? 3 : -1;
-  if (n < 0 || batch < 1 || batch > 8) return "";
   return kNames[n][batch - 1];
 }
 

@@ -246,16 +246,18 @@ __device__ __forceinline__ void load_group(const uint16_t* __restrict__ X, int c
 // (80 VGPRs) for B = 1, 5 (96) for B = 2..5, 4 (128) for B = 6..8, 3 (168) for 16:32 at
 // B = 6..8 (its high-half lanes also hold their values reversed): the B accumulators and
 // the x reads of a step (SB/2 dwords per kept value) grow with B.
+constexpr int waves_per_eu_of(int N, int B) { return B <= 1 ? 6 : B <= 5 ? 5 : (N == 16 ? 3 : 4); }
 template <int N, int B>
 constexpr int waves_per_eu() {
-  return B <= 1 ? 6 : B <= 5 ? 5 : (N == 16 ? 3 : 4);
+  return waves_per_eu_of(N, B);
 }
 
 // Largest workgroup: 16 waves, but 12 where 3 waves per SIMD are needed (a 16-wave
 // workgroup needs 4 per SIMD, i.e. at most 128 VGPRs).
+constexpr int max_waves_of(int N, int B) { return waves_per_eu_of(N, B) < 4 ? 12 : kMaxWaves; }
 template <int N, int B>
 constexpr int max_waves() {
-  return waves_per_eu<N, B>() < 4 ? 12 : kMaxWaves;
+  return max_waves_of(N, B);
 }
 
 // The dense kernel holds no decode state: 8 waves per SIMD up to B = 4, 6 up to 6, 4 above.
@@ -264,12 +266,19 @@ constexpr int dense_waves_per_eu() {
   return B <= 4 ? 8 : B <= 6 ? 6 : 4;
 }
 
-template <int N, int B, int DEC>
-__global__ __launch_bounds__((64 * max_waves<N, B>())) __attribute__((amdgpu_waves_per_eu((waves_per_eu<N, B>())))) void spmm_kernel(
-    const uint4* __restrict__ values, const uint32_t* __restrict__ masks, const uint16_t* __restrict__ X,
-    uint16_t* __restrict__ Y, int rows, int cols, int rpb, int cs_count, int phase_cols) {
+// CI > 1 (narrow layers, rpb <= RPW = 8 / CI rows per workgroup, one row group): the lanes
+// of row slot s take row s % RPW and the (s / RPW)-th of CI near-equal, contiguous parts of
+// the wave's steps, so that no lane repeats another lane's row (with 8-row slots and 4-row
+// workgroups half of every wave would); the CI partial sums of a row are added across lanes
+// before the LDS reduction.
+template <int N, int B, int DEC, int CI>
+__device__ __forceinline__ void spmm_body(const uint4* __restrict__ values, const uint32_t* __restrict__ masks,
+                                          const uint16_t* __restrict__ X, uint16_t* __restrict__ Y, int rows,
+                                          int cols, int rpb, int cs_count, int phase_cols) {
   static_assert(DEC == kByteLut || (DEC == kBitWalk), "byte LUT or bit walk");
   static_assert(DEC != kByteLut || N <= 8, "the byte LUT needs at most 8 kept columns per mask half-word");
+  static_assert(CI == 1 || CI == 2 || CI == 4, "column parts per wave: 1, 2 or 4");
+  constexpr int RPW = 8 / CI;                      // rows per wave
   constexpr int SB = stride_of<B>();
   constexpr int BATCH = 4;
   extern __shared__ uint4 lds[];
@@ -285,13 +294,15 @@ __global__ __launch_bounds__((64 * max_waves<N, B>())) __attribute__((amdgpu_wav
   const int CS = __builtin_amdgcn_readfirstlane(cs_count);
   const int rg = __builtin_amdgcn_readfirstlane(int(unsigned(wave) / unsigned(CS)));
   const int cs = wave - rg * CS;
-  const int rsub = (lane & 31) >> 2;
+  const int rsub = (lane & 31) >> 2;               // row slot within the wave's 8
+  const int rrow = rsub % RPW;                     // its row within the wave's RPW rows
+  const int cpart = rsub / RPW;                    // its part of the wave's steps
   const int u = ((lane >> 5) << 2) | (lane & 3);
   const int half = u & 1;
   const int wsel = u >> 1;
   const int row0 = blockIdx.x * rpb;
   const int row_end = min(row0 + rpb, rows);
-  const unsigned r = unsigned(min(row0 + 8 * rg + rsub, row_end - 1));
+  const unsigned r = unsigned(min(row0 + 8 * rg + rrow, row_end - 1));
 
   const int words = cols >> 5;
   const int steps = (words + 3) >> 2;
@@ -311,8 +322,11 @@ __global__ __launch_bounds__((64 * max_waves<N, B>())) __attribute__((amdgpu_wav
   for (int p0 = 0; p0 < steps; p0 += psteps) {
     const int p1 = min(steps, p0 + psteps);
     const int pn = p1 - p0;
-    const int s_beg = p0 + int(unsigned(pn) * unsigned(cs) / unsigned(CS));
-    const int s_end = p0 + int(unsigned(pn) * unsigned(cs + 1) / unsigned(CS));
+    const int w_beg = p0 + int(unsigned(pn) * unsigned(cs) / unsigned(CS));
+    const int w_end = p0 + int(unsigned(pn) * unsigned(cs + 1) / unsigned(CS));
+    // this lane's part of the wave's steps (the whole range when CI == 1)
+    const int s_beg = w_beg + int(unsigned(w_end - w_beg) * unsigned(cpart) / unsigned(CI));
+    const int s_end = w_beg + int(unsigned(w_end - w_beg) * unsigned(cpart + 1) / unsigned(CI));
     const int s_main = min(s_end, full_steps);
     const int n = max(0, s_main - s_beg);
     const int nfull = n / BATCH;
@@ -374,11 +388,14 @@ __global__ __launch_bounds__((64 * max_waves<N, B>())) __attribute__((amdgpu_wav
     }
   }
 
-  // row sums: DPP inside the quad and the partner half-wave, then LDS across the CS waves
+  // row sums: DPP inside the quad and the partner half-wave, the CI parts (row slots
+  // rrow + k * RPW, lanes 4 * RPW apart), then LDS across the CS waves
 #pragma unroll
   for (int b = 0; b < B; ++b) {
-    const float s = row8_sum(acc[b]);
-    if (u == 0) red[(wave * 8 + rsub) * kMaxBatch + b] = s;
+    float s = row8_sum(acc[b]);
+#pragma unroll
+    for (int d = 4 * RPW; d < 32; d <<= 1) s += __shfl_xor(s, d);
+    if (u == 0 && cpart == 0) red[(wave * 8 + rrow) * kMaxBatch + b] = s;
   }
   __syncthreads();
   const int nr = row_end - row0;
@@ -391,6 +408,20 @@ __global__ __launch_bounds__((64 * max_waves<N, B>())) __attribute__((amdgpu_wav
       Y[size_t(b) * unsigned(rows) + unsigned(row0 + rr)] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(t));
     }
   }
+}
+
+template <int N, int B, int DEC>
+__global__ __launch_bounds__((64 * max_waves<N, B>())) __attribute__((amdgpu_waves_per_eu((waves_per_eu<N, B>())))) void spmm_kernel(
+    const uint4* __restrict__ values, const uint32_t* __restrict__ masks, const uint16_t* __restrict__ X,
+    uint16_t* __restrict__ Y, int rows, int cols, int rpb, int cs_count, int phase_cols) {
+  spmm_body<N, B, DEC, 1>(values, masks, X, Y, rows, cols, rpb, cs_count, phase_cols);
+}
+
+template <int N, int B, int DEC, int CI>
+__global__ __launch_bounds__((64 * max_waves<N, B>())) __attribute__((amdgpu_waves_per_eu((waves_per_eu<N, B>())))) void spmm_narrow_kernel(
+    const uint4* __restrict__ values, const uint32_t* __restrict__ masks, const uint16_t* __restrict__ X,
+    uint16_t* __restrict__ Y, int rows, int cols, int rpb, int cs_count, int phase_cols) {
+  spmm_body<N, B, DEC, CI>(values, masks, X, Y, rows, cols, rpb, cs_count, phase_cols);
 }
 
 // ---------------------------------------------------------------- dense counterpart

@@ -101,7 +101,7 @@ def test_skinny_routing():
     assert nm.spmm_variant(2047, 4096, 8, 4, 8) == "spmm_kernel<4, 8, 2>"
     assert nm.spmm_variant(1024, 4096, 9, 4, 8) == SKINNY[4]
     assert nm.spmm_variant(1024, 5120, 9, 8, 16) == SKINNY[8]
-    assert nm.spmm_variant(1024, 8192, 9, 8, 16) == "spmm_kernel<8, 8, 2>"
+    assert nm.spmm_variant(1024, 8192, 9, 8, 16) == "spmm_narrow_kernel<8, 8, 2, 2>"
     assert nm.spmm_variant(1024, 8192, 12, 8, 16) == SKINNY[8]
     assert nm.spmm_variant(4096, 4096, 12, 16, 32) == SKINNY[16]
     assert nm.spmm_variant(14336, 4096, 31, 16, 32) == SKINNY[16]

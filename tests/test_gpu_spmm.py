@@ -106,13 +106,18 @@ def test_spmm_regimes(B):
 
 @pytest.mark.parametrize("N,M", PATTERNS)
 def test_spmm_narrow_layers_all_rows(N, M):
-    """Every row of 1023- and 1000-row layers (4 rows per workgroup, whose spare lanes repeat
-    the last row; the last workgroup of the first holds 3), at several batches, against the
-    oracle."""
-    for i, (R, C) in enumerate(((1023, 2048), (1000, 1024))):
+    """Every row of narrow layers (at most 4 rows per workgroup) at several batches, against
+    the oracle: 1023 x 2048 (4 rows per workgroup, the last one 3; too few steps per wave for
+    column parts, so spare lanes repeat the last row), 1000 x 8192 (each row on 2 parts of a
+    wave's lanes) and 300 x 16416 (2 rows per workgroup on 4 parts, a one-word tail step)."""
+    for i, (R, C, ci) in enumerate(((1023, 2048, 1), (1000, 8192, 2), (300, 16416, 4))):
         W = synth.weight(R, C, seed=1600 + i)
         for B in (2, 3, 5, 8):
-            say(f"narrow spmm B={B} {R}x{C} {N}:{M} {nm.spmm_variant(R, C, B, N, M)}")
+            name = nm.spmm_variant(R, C, B, N, M)
+            say(f"narrow spmm B={B} {R}x{C} {N}:{M} {name}")
+            if not name.startswith("skinny"):
+                want = f"spmm_narrow_kernel<{N}, {B}, " if ci > 1 else f"spmm_kernel<{N}, {B}, "
+                assert name.startswith(want) and (ci == 1 or name.endswith(f", {ci}>")), name
             check_spmm(W, batch_x(B, C, 1650 + 10 * i + B), N, M, (B, R, C, N))
 
 
