@@ -1,5 +1,5 @@
 // Host check of the expansion table of the 16:32 product on the dense matrix instruction
-// (nm_prefill_impl.h). For every mask byte (which columns of 8 a lane's fragment keeps) and
+// (nm_skinny_impl.h). For every mask byte (which columns of 8 a lane's fragment keeps) and
 // every start offset of the lane's 8-half window, the 4 output dwords built from the table
 // entry must hold the byte's kept values in ascending column order at their columns and
 // zeros at the other columns. The byte selection of v_perm_b32 is emulated from its
@@ -10,9 +10,9 @@
 #include <cstdint>
 #include <cstdio>
 
-#include "nm_prefill_impl.h"
+#include "nm_skinny_impl.h"
 
-using nm::prefill_detail::ExpandTable;
+using nm::skinny_detail::ExpandTable;
 
 static uint32_t perm(uint32_t a, uint32_t b, uint32_t sel, bool* ok) {
   const uint64_t d = (uint64_t(a) << 32) | b;
@@ -28,7 +28,7 @@ static uint32_t perm(uint32_t a, uint32_t b, uint32_t sel, bool* ok) {
 }
 
 int main() {
-  static const ExpandTable t = nm::prefill_detail::make_expand_table();
+  static const ExpandTable t = nm::skinny_detail::make_expand_table();
   int failures = 0, cases = 0;
   // a packed word of 16 distinct nonzero halves, and the window of 8 starting at `pc`
   uint16_t word[24];
