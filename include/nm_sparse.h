@@ -151,6 +151,28 @@ int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,
 int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
             int64_t rows, int64_t cols, int64_t batch, int N, int M, void* stream);
 
+/* nm_spmm with a caller-owned workspace. The same Y definition and routing as nm_spmm; where
+ * nm_spmm_workspace_bytes(...) for the same arguments is > 0 (50% patterns on the matrix
+ * instructions, layers too short to fill the GPU: e.g. 1024 rows at 5..31 vectors) and
+ * workspace_bytes is at least that, the columns of each 16-row tile go to 2, 4 or 8
+ * workgroups whose fp32 partial tiles the last-arriving one sums in split order (fixed, so
+ * bit-identical run to run, but not bit-identical to nm_spmm's unsplit order: the same
+ * tolerance against the exact product). workspace: device memory, 16-byte aligned, owned by
+ * the caller; its first 256-byte-rounded tile-count * 4 bytes are counters that must be zero
+ * before the first call on it (e.g. one hipMemset when allocated); every call leaves them
+ * zero again. NULL or a smaller workspace runs the unsplit kernels (no error). Calls that use
+ * one workspace must be ordered (one stream): overlapping calls on it race. Other arguments
+ * and errors as nm_spmm; a misaligned workspace is NM_ERR_ALIGN. */
+int nm_spmm_ws(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
+               int64_t rows, int64_t cols, int64_t batch, int N, int M, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace nm_spmm_ws can use for these arguments on the current device; 0 when
+ * the shape takes no column split (or the arguments are invalid, or no device). At most
+ * tiles * 4 rounded up to 256, plus tiles * 8 KiB (tiles = ceil(rows / 16); only layers of at
+ * most as many tiles as the GPU has CUs take a split). */
+size_t nm_spmm_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, int N, int M);
+
 /* The batch product of nm_spmm on the matrix instructions for any batch >= 1, whatever
  * nm_spmm's routing would pick (the same Y definition, summation in the instructions' fixed
  * order, bit-identical run to run), for the 50% patterns: 2:4 on the 2:4 sparse instruction

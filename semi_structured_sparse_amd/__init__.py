@@ -39,6 +39,9 @@ SIGNATURES = {
                                  _c.c_void_p]),
     "nm_spmm": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
                            _c.c_int64, _c.c_int64, _c.c_int, _c.c_int, _c.c_void_p]),
+    "nm_spmm_ws": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
+                              _c.c_int64, _c.c_int, _c.c_int, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "nm_spmm_workspace_bytes": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int, _c.c_int]),
     "nm_spmm_skinny": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
                                   _c.c_int64, _c.c_int64, _c.c_int, _c.c_int, _c.c_void_p]),
     "nm_gemm_dense": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
@@ -341,6 +344,39 @@ def nm_spmm(values, masks, X, N: int, M: int, out=None):
         st = lib().nm_spmm(values.data_ptr(), masks.data_ptr(), X.data_ptr(), out.data_ptr(),
                            rows, cols, batch, N, M, _stream_ptr(X))
     _check("nm_spmm", st)
+    return out
+
+
+def spmm_workspace_bytes(rows: int, cols: int, batch: int, N: int, M: int) -> int:
+    """Workspace bytes nm_spmm_ws can use for this shape (0: no column split)."""
+    return int(lib().nm_spmm_workspace_bytes(rows, cols, batch, N, M))
+
+
+def spmm_workspace(rows: int, cols: int, batch: int, N: int, M: int, device=None):
+    """A zeroed uint8 workspace for nm_spmm_ws of this shape (None when it takes none)."""
+    torch = _torch()
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    with torch.cuda.device(dev):
+        n = spmm_workspace_bytes(rows, cols, batch, N, M)
+    return torch.zeros(n, dtype=torch.uint8, device=dev) if n > 0 else None
+
+
+def nm_spmm_ws(values, masks, X, N: int, M: int, workspace=None, out=None):
+    """nm_spmm with a caller-owned workspace (a uint8 device tensor whose counters start at
+    zero, e.g. from spmm_workspace; None runs nm_spmm's kernels): short layers split their
+    columns over several workgroups. Calls sharing a workspace must be stream-ordered."""
+    torch = _torch()
+    rows, cols, batch, out = _batch_args(values, masks, X, N, M, out)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _require(workspace, "workspace", torch.uint8, 1)
+        if workspace.device != X.device:
+            raise ValueError("workspace must be on X's device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    with torch.cuda.device(X.device):
+        st = lib().nm_spmm_ws(values.data_ptr(), masks.data_ptr(), X.data_ptr(), out.data_ptr(),
+                              rows, cols, batch, N, M, ws_ptr, ws_bytes, _stream_ptr(X))
+    _check("nm_spmm_ws", st)
     return out
 
 

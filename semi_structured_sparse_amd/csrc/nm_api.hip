@@ -202,39 +202,66 @@ int nm_gemm_dense_prefill(const uint16_t* W, const uint16_t* X, uint16_t* Y, int
   return e == hipSuccess ? NM_OK : nm::hip_fail(e);
 }
 
-int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
-            int64_t rows, int64_t cols, int64_t batch, int N, int M, void* stream) {
+namespace nm {
+// nm_spmm's dispatch, with an optional workspace for the skinny kernels' column splits.
+int spmm_dispatch(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y, int64_t rows,
+                  int64_t cols, int64_t batch, int N, int M, void* stream, void* workspace, size_t workspace_bytes) {
   if (!values || !masks || !X || !Y) return NM_ERR_NULL;
-  if (!nm::valid_shape(rows, cols) || batch < 1 || batch > nm::kPrefillMaxTokens) return NM_ERR_SHAPE;
-  if (!nm::valid_pattern(N, M) || (batch > 1 && M != 2 * N)) return NM_ERR_PATTERN;
-  if (batch >= nm::kMatrixCoreMinBatch && nm::prefill_pattern(N, M))  // matrix-core product
+  if (!valid_shape(rows, cols) || batch < 1 || batch > kPrefillMaxTokens) return NM_ERR_SHAPE;
+  if (!valid_pattern(N, M) || (batch > 1 && M != 2 * N)) return NM_ERR_PATTERN;
+  if (!aligned(workspace, 16)) return NM_ERR_ALIGN;
+  if (batch >= kMatrixCoreMinBatch && prefill_pattern(N, M))  // matrix-core product
     return nm_spmm_prefill(values, masks, X, Y, rows, cols, batch, N, M, stream);
-  if (!nm::aligned(values, 16) || !nm::aligned(masks, 4) || !nm::aligned(X, 16) || !nm::aligned(Y, 2))
-    return NM_ERR_ALIGN;
-  nm::DeviceInfo dev;
-  hipError_t e = nm::current_device_info(&dev);
-  if (e != hipSuccess) return nm::hip_fail(e);
-  if (M != 2 * N && cols > nm::max_cols_for(dev)) return NM_ERR_TOO_WIDE;  // 25%: single-vector kernel only
-  if (nm::use_skinny(rows, cols, batch, N, M, dev)) {
+  if (!aligned(values, 16) || !aligned(masks, 4) || !aligned(X, 16) || !aligned(Y, 2)) return NM_ERR_ALIGN;
+  DeviceInfo dev;
+  hipError_t e = current_device_info(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (M != 2 * N && cols > max_cols_for(dev)) return NM_ERR_TOO_WIDE;  // 25%: single-vector kernel only
+  if (use_skinny(rows, cols, batch, N, M, dev)) {
     // 50% patterns at 5..31 vectors where measured faster: the matrix instructions, 16
-    // vectors per launch
-    for (int64_t b0 = 0; b0 < batch; b0 += nm::kSkinnyBatch) {
-      const int nb = int(batch - b0 < nm::kSkinnyBatch ? batch - b0 : nm::kSkinnyBatch);
-      e = nm::launch_skinny_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb, N, M,
-                                 static_cast<hipStream_t>(stream), dev);
-      if (e != hipSuccess) return nm::hip_fail(e);
+    // vectors per launch (launches in stream order, so one workspace serves them all)
+    for (int64_t b0 = 0; b0 < batch; b0 += kSkinnyBatch) {
+      const int nb = int(batch - b0 < kSkinnyBatch ? batch - b0 : kSkinnyBatch);
+      e = launch_skinny_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb, N, M,
+                             static_cast<hipStream_t>(stream), dev, workspace, workspace_bytes);
+      if (e != hipSuccess) return hip_fail(e);
     }
     return NM_OK;
   }
   // otherwise (fewer vectors, smaller layers, most 16:32 shapes): the small-batch kernel on consecutive
   // groups of kSmallBatch rows of X (X and Y rows are contiguous)
-  for (int64_t b0 = 0; b0 < batch; b0 += nm::kSmallBatch) {
-    const int nb = int(batch - b0 < nm::kSmallBatch ? batch - b0 : nm::kSmallBatch);
-    e = nm::launch_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb, N, M,
-                        static_cast<hipStream_t>(stream), dev);
-    if (e != hipSuccess) return nm::hip_fail(e);
+  for (int64_t b0 = 0; b0 < batch; b0 += kSmallBatch) {
+    const int nb = int(batch - b0 < kSmallBatch ? batch - b0 : kSmallBatch);
+    e = launch_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb, N, M,
+                    static_cast<hipStream_t>(stream), dev);
+    if (e != hipSuccess) return hip_fail(e);
   }
   return NM_OK;
+}
+
+// Workspace bytes spmm_dispatch can use for the product (0 when it would not use one).
+size_t spmm_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev) {
+  if (!valid_shape(rows, cols) || !valid_pattern(N, M) || batch < 1 || batch > kPrefillMaxTokens) return 0;
+  if (batch >= kMatrixCoreMinBatch || !use_skinny(rows, cols, batch, N, M, dev)) return 0;
+  return skinny_workspace_bytes(rows, cols, int(batch < kSkinnyBatch ? batch : kSkinnyBatch), N, dev);
+}
+}  // namespace nm
+
+int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
+            int64_t rows, int64_t cols, int64_t batch, int N, int M, void* stream) {
+  return nm::spmm_dispatch(values, masks, X, Y, rows, cols, batch, N, M, stream, nullptr, 0);
+}
+
+int nm_spmm_ws(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y, int64_t rows,
+               int64_t cols, int64_t batch, int N, int M, void* workspace, size_t workspace_bytes, void* stream) {
+  return nm::spmm_dispatch(values, masks, X, Y, rows, cols, batch, N, M, stream, workspace, workspace_bytes);
+}
+
+size_t nm_spmm_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, int N, int M) {
+  if (!nm::valid_shape(rows, cols) || !nm::valid_pattern(N, M) || batch < 1) return 0;
+  nm::DeviceInfo dev;
+  if (nm::current_device_info(&dev) != hipSuccess) return 0;
+  return nm::spmm_workspace_bytes(rows, cols, batch, N, M, dev);
 }
 
 int nm_spmm_skinny(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,

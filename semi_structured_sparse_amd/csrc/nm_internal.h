@@ -100,9 +100,16 @@ hipError_t launch_prefill_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y
 // limits.
 bool skinny_pattern(int n, int m);
 bool skinny_fits(int64_t rows, int64_t cols, int64_t tokens, int n, int m, const DeviceInfo& dev);
+// With a workspace of at least skinny_workspace_bytes for a launch of `tokens` vectors (0:
+// that launch takes no column split), layers of at most half as many 16-row tiles as CUs
+// split their columns over several workgroups per tile where that measured faster; without
+// one (or a smaller one) they run unsplit. The bytes do not grow with tokens: the size for
+// the largest launch serves the smaller ones. The workspace's counters must be zero before
+// the first launch; every launch leaves them zero.
+size_t skinny_workspace_bytes(int64_t rows, int64_t cols, int tokens, int n, const DeviceInfo& dev);
 hipError_t launch_skinny_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
                               int64_t rows, int64_t cols, int tokens, int n, int m, hipStream_t stream,
-                              const DeviceInfo& dev);
+                              const DeviceInfo& dev, void* workspace = nullptr, size_t workspace_bytes = 0);
 // nm_spmm runs the skinny kernel, kSkinnyBatch vectors per launch, from kSkinnyMinBatch
 // vectors up to kMatrixCoreMinBatch, where the prefill kernels take over: on layers of at
 // least kSkinnyMinRows rows for 2:4, 4:8 and 8:16; on smaller layers (down to

@@ -16,6 +16,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct SkinnyShape {
   int rg = 1, cs = 16, phase_cols = 128;
+  int splits = 1;   // workgroups per row group's columns (with a workspace)
   int64_t grid = 0;
   size_t lds = 0;
 };
@@ -39,14 +40,36 @@ size_t x_budget(int mode, const DeviceInfo& dev) {
   return std::min<size_t>(kMaxXBytes, avail);
 }
 
-SkinnyShape skinny_shape(int64_t rows, int64_t cols, int tokens, int mode, const DeviceInfo& dev) {
+// Column splits: a layer of at most half as many 16-row tiles as CUs (1024 rows: 64 tiles)
+// leaves most CUs idle, so with a workspace its columns can go to S = 2, 4 or 8 workgroups per
+// tile (S * tiles <= CUs, at least 2 lines per split), whose partial tiles the last of them
+// sums (SplitWs). The hand-off (partial store, count, the last workgroup's loads) costs about
+// 1.3 us, so a split is taken where it measured faster on MI355X (1024 x 4096 at 16 vectors
+// 2:4: 8.4 us unsplit, 8.7 split; 1024 x 8192: 13.3 against 9.3; 1024 x 14336: 22.3 against
+// 10.8): rows of at least 64 lines; at least 40 lines from 8 vectors with S >= 4; the split
+// patterns' slower lines from 9 vectors with S >= 4. Not for 16:32 (its expansion kernel
+// has no split).
+int splits_for(int64_t tiles, int64_t cols, int tokens, int mode, const DeviceInfo& dev) {
+  if (mode == kModeExpand) return 1;
+  const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
+  const int64_t lines = ceil_div(cols, 128);
+  int s = 1;
+  while (s < kMaxSplits && tiles * (2 * s) <= cus && lines >= int64_t(2) * (2 * s)) s *= 2;
+  const bool pays = lines >= 64 || (s >= 4 && lines >= 40 && tokens >= 8) ||
+                    (s >= 4 && mode == kModeSplit && tokens >= 9);
+  return pays ? s : 1;
+}
+
+SkinnyShape skinny_shape(int64_t rows, int64_t cols, int tokens, int mode, const DeviceInfo& dev,
+                         bool with_ws = false) {
   const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
   const int64_t tiles = ceil_div(rows, 16);
   const int64_t want = std::min<int64_t>(kMaxWaves, std::max<int64_t>(1, ceil_div(tiles, cus)));
   SkinnyShape s;
   s.rg = int(want);
   s.cs = kMaxWaves / s.rg;
-  s.grid = ceil_div(tiles, s.rg);
+  s.splits = with_ws && s.rg == 1 ? splits_for(tiles, cols, tokens, mode, dev) : 1;
+  s.grid = ceil_div(tiles, s.rg) * s.splits;
   // phases of whole 128-column lines (the loads of the 2:4 and split kernels cover lines)
   const int64_t pc_max = int64_t(x_budget(mode, dev) / (2 * size_t(tokens))) / 128 * 128;
   s.phase_cols = int(std::min<int64_t>(pc_max, ceil_div(cols, 128) * 128));
@@ -77,17 +100,36 @@ const char* skinny_variant(int n) {
   return n == 2 ? "skinny_spmm_kernel<1, false>" : n == 16 ? "skinny_expand_kernel<1>" : "skinny_spmm_kernel<1, true>";
 }
 
+size_t skinny_workspace_bytes(int64_t rows, int64_t cols, int tokens, int n, const DeviceInfo& dev) {
+  const int64_t tiles = ceil_div(rows, 16);
+  if (ceil_div(tiles, dev.cu_count > 0 ? dev.cu_count : 256) > 1) return 0;
+  const int splits = splits_for(tiles, cols, tokens, mode_of(n), dev);
+  if (splits == 1) return 0;
+  // counters (padded to 256 bytes), then one 1 KiB fp32 partial per tile and split
+  return size_t(ceil_div(tiles * 4, 256) * 256) + size_t(tiles) * size_t(splits) * 1024u;
+}
+
 hipError_t launch_skinny_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
                               int64_t rows, int64_t cols, int tokens, int n, int m, hipStream_t stream,
-                              const DeviceInfo& dev) {
+                              const DeviceInfo& dev, void* workspace, size_t workspace_bytes) {
   if (!skinny_fits(rows, cols, tokens, n, m, dev)) return hipErrorInvalidValue;
   const int mode = mode_of(n);
-  const SkinnyShape s = skinny_shape(rows, cols, tokens, mode, dev);
-  int r = int(rows), c = int(cols), t = tokens, rg = s.rg, cs = s.cs, pc = s.phase_cols;
-  void* args[] = {&values, &masks, &X, &Y, &r, &c, &t, &rg, &cs, &pc};
-  const void* k = mode == kModeSplit    ? reinterpret_cast<const void*>(&skinny_spmm_kernel<1, true>)
-                : mode == kModeExpand   ? reinterpret_cast<const void*>(&skinny_expand_kernel<1>)
-                                        : reinterpret_cast<const void*>(&skinny_spmm_kernel<1, false>);
+  const size_t need = skinny_workspace_bytes(rows, cols, tokens, n, dev);
+  const bool split = need > 0 && workspace != nullptr && workspace_bytes >= need;
+  const SkinnyShape s = skinny_shape(rows, cols, tokens, mode, dev, split);
+  int r = int(rows), c = int(cols), t = tokens, rg = s.rg, cs = s.cs, pc = s.phase_cols, sp = s.splits;
+  const int64_t tiles = ceil_div(rows, 16);
+  unsigned* cnt = split ? static_cast<unsigned*>(workspace) : nullptr;
+  float4* part = split ? reinterpret_cast<float4*>(static_cast<char*>(workspace) + ceil_div(tiles * 4, 256) * 256)
+                       : nullptr;
+  if (mode == kModeExpand) {
+    void* args[] = {&values, &masks, &X, &Y, &r, &c, &t, &rg, &cs, &pc};
+    return launch(reinterpret_cast<const void*>(&skinny_expand_kernel<1>), dim3(unsigned(s.grid)),
+                  dim3(kThreadsFixed), args, s.lds, stream, dev);
+  }
+  void* args[] = {&values, &masks, &X, &Y, &r, &c, &t, &rg, &cs, &pc, &sp, &part, &cnt};
+  const void* k = mode == kModeSplit ? reinterpret_cast<const void*>(&skinny_spmm_kernel<1, true>)
+                                     : reinterpret_cast<const void*>(&skinny_spmm_kernel<1, false>);
   return launch(k, dim3(unsigned(s.grid)), dim3(kThreadsFixed), args, s.lds, stream, dev);
 }
 

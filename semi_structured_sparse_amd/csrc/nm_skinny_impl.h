@@ -115,16 +115,36 @@ __host__ __device__ constexpr uint32_t lead_bytes() {
                              : 0u;
 }
 
+// Partial tiles of column splits cross workgroups on different XCDs, whose L2 caches are
+// not coherent with each other: buffer accesses with the SC1 cache-policy bit are (the form
+// the compiler gives device-scope atomic loads and stores), so no fence has to write back or
+// invalidate a whole L2.
+constexpr int kCoherentAux = 16;   // SC1
+
+__device__ __forceinline__ void coherent_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v) {
+  typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
+  const u4_t u = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(u, r, off, 0, kCoherentAux);
+}
+
+__device__ __forceinline__ float4 coherent_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
+  const u4_t u = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherentAux);
+  return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+
 // The workgroup's view of the launch: its rows, the wave's place in them, and the buffer
-// resources of its slices of the packed matrix and of X.
+// resources of its slices of the packed matrix and of X. With `splits` > 1 the columns of
+// each group of row tiles are split over that many consecutive workgroups (split = which).
 struct Tile {
   int lane, wave, q, li, rg, cs;
   bool active;   // the wave owns rows (rg < rg_count)
   int wg_r0, words;
+  int tile0, split;   // first 16-row tile of the workgroup; its part of the columns
   __amdgpu_buffer_rsrc_t vr, mr, xr;
 
   __device__ __forceinline__ Tile(const uint16_t* values, const uint32_t* masks, const uint16_t* X, int rows,
-                                  int cols, int tokens, int rg_count, int cs_count) {
+                                  int cols, int tokens, int rg_count, int cs_count, int splits = 1) {
     const int tid = threadIdx.x;
     lane = tid & 63;
     // the wave index and everything derived from it are wave-uniform (scalar registers):
@@ -138,7 +158,10 @@ struct Tile {
     // meet the barriers but own no rows
     active = rg < rg_count;
     const int wg_rows_max = rg_count * 16;
-    wg_r0 = int(blockIdx.x) * wg_rows_max;
+    const int wg = int(blockIdx.x) / splits;
+    split = int(blockIdx.x) - wg * splits;
+    tile0 = wg * rg_count;
+    wg_r0 = wg * wg_rows_max;
     const int wg_rows = min(wg_rows_max, rows - wg_r0);
     words = cols >> 5;
     vr = make_rsrc(values + size_t(wg_r0) * unsigned(cols >> 1), int64_t(wg_rows) * cols);
@@ -180,11 +203,25 @@ struct XStage {
   }
 };
 
+// Column splits (splits > 1): each workgroup of a tile's group leaves its fp32 partial tile
+// (one float4 per lane, 1 KiB per 16-row tile) in part[(tile * splits + split) * 64 + lane]
+// and counts itself in cnt[tile]; the last one to arrive sums the splits' partials in split
+// order (the same order whichever arrives last), rounds once, stores, and sets the count back
+// to zero, so the counters are zero again after every launch.
+constexpr int kMaxSplits = 8;
+
+struct SplitWs {
+  float4* part;
+  unsigned* cnt;
+  int splits;
+};
+
 // The CS partial tiles of each row group summed through LDS in a fixed order; the group's
-// first wave rounds once and stores. D layout of the instructions: lane (q, li) holds token
-// li, rows 4q .. 4q+3 of the tile.
+// first wave rounds once and stores (with column splits, the last split's first wave). D
+// layout of the instructions: lane (q, li) holds token li, rows 4q .. 4q+3 of the tile.
 __device__ __forceinline__ void reduce_store(const Tile& w, f4_t acc, int cs_count, int rows, int tokens,
-                                             uint16_t* __restrict__ Y, char* lds_base) {
+                                             uint16_t* __restrict__ Y, char* lds_base,
+                                             const SplitWs& sw = SplitWs{nullptr, nullptr, 1}) {
   __syncthreads();
   float4* red = reinterpret_cast<float4*>(lds_base);
   red[w.wave * 64 + w.lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -194,6 +231,30 @@ __device__ __forceinline__ void reduce_store(const Tile& w, f4_t acc, int cs_cou
   for (int k = 1; k < cs_count; ++k) {
     const float4 v = red[(w.wave + k) * 64 + w.lane];
     s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  if (sw.splits > 1) {
+    const int tile = w.tile0 + w.rg;
+    const __amdgpu_buffer_rsrc_t pr =
+        make_rsrc(sw.part + size_t(tile) * unsigned(sw.splits) * 64u, int64_t(sw.splits) * 1024);
+    coherent_store16(pr, uint32_t(w.split * 64 + w.lane) * 16u, s);
+    // the partial has reached the device's coherence point before the count moves
+    __builtin_amdgcn_s_waitcnt(0);
+    unsigned old = 0;
+    if (w.lane == 0) old = atomicAdd(sw.cnt + tile, 1u);
+    old = unsigned(__shfl(int(old), 0));
+    if (old != unsigned(sw.splits - 1)) return;
+    // the last of the tile's workgroups: every other split's partial is complete
+    // (all kMaxSplits loads issued at once; those past the resource's splits * 1 KiB read
+    // zero, and adding zero after the last split leaves the sum as it is)
+    float4 v[kMaxSplits];
+#pragma unroll
+    for (int k = 0; k < kMaxSplits; ++k) v[k] = coherent_load16(pr, uint32_t(k * 64 + w.lane) * 16u);
+    s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < kMaxSplits; ++k) {
+      s.x += v[k].x; s.y += v[k].y; s.z += v[k].z; s.w += v[k].w;
+    }
+    if (w.lane == 0) atomicExch(sw.cnt + tile, 0u);
   }
   const int row = w.wg_r0 + w.rg * 16 + 4 * w.q;
   if (w.li >= tokens || row >= rows) return;
@@ -238,14 +299,18 @@ __device__ __forceinline__ void skinny_line_body(const uint16_t* __restrict__ va
                                                  const uint32_t* __restrict__ masks,
                                                  const uint16_t* __restrict__ X, uint16_t* __restrict__ Y,
                                                  int rows, int cols, int tokens, int rg_count, int cs_count,
-                                                 int phase_cols) {
+                                                 int phase_cols, const SplitWs& sw) {
   constexpr bool SPLIT = MODE == kModeSplit;
   static_assert(MODE == kModeDirect || MODE == kModeSplit, "whole-line loads: 2:4 and the split patterns");
   extern __shared__ __attribute__((aligned(16))) char lds_base[];
   char* const lds = lds_base + lead_bytes<MODE>();   // SPLIT: the split tables first, X after them
   const int tid = threadIdx.x;
-  const Tile w(values, masks, X, rows, cols, tokens, rg_count, cs_count);
+  const Tile w(values, masks, X, rows, cols, tokens, rg_count, cs_count, sw.splits);
   const int q = w.q, li = w.li;
+  // this workgroup's columns: lines [L s / S, L (s + 1) / S) of the row's L for split s of S
+  const int lines = (cols + 127) >> 7;
+  const int c_beg = 128 * int((int64_t(lines) * w.split) / sw.splits);
+  const int c_end = min(cols, 128 * int((int64_t(lines) * (w.split + 1)) / sw.splits));
   // value loads: lane l of load h reads row 8h + l % 8 of the row group, chunk kc of the line
   const int kc = 2 * q + ((w.lane >> 3) & 1);
   const uint32_t voff0 = uint32_t(w.rg * 16 + (w.lane & 7)) * uint32_t(cols) + 16u * uint32_t(kc);
@@ -268,8 +333,8 @@ __device__ __forceinline__ void skinny_line_body(const uint16_t* __restrict__ va
     lut_a = tab[tid];
     lut_b = tab[2 * kSplitEntries + (tid & 63)];
   }
-  for (int p0 = 0; p0 < cols; p0 += phase_cols) {
-    const int pc = min(phase_cols, cols - p0);       // columns in this phase (multiple of 32)
+  for (int p0 = c_beg; p0 < c_end; p0 += phase_cols) {
+    const int pc = min(phase_cols, c_end - p0);      // columns in this phase (multiple of 32)
     const uint32_t rb = uint32_t(2 * phase_cols);    // LDS bytes per token row
     // this wave's lines of the phase (phase_cols is a multiple of 128)
     const int plines = (pc + 127) / 128;
@@ -301,7 +366,7 @@ __device__ __forceinline__ void skinny_line_body(const uint16_t* __restrict__ va
     for (int d = 0; d < kLineDepth; ++d) load_line(va[d], vb[d], d);
     __syncthreads();                                 // the previous phase's LDS reads are done
     if constexpr (SPLIT) {
-      if (p0 == 0) {
+      if (p0 == c_beg) {
         reinterpret_cast<uint4*>(lds_base)[tid] = lut_a;
         if (tid < 64) reinterpret_cast<uint4*>(lds_base)[2 * kSplitEntries + tid] = lut_b;
       }
@@ -374,7 +439,7 @@ __device__ __forceinline__ void skinny_line_body(const uint16_t* __restrict__ va
       }
     }
   }
-  reduce_store(w, acc, cs_count, rows, tokens, Y, lds_base);
+  reduce_store(w, acc, cs_count, rows, tokens, Y, lds_base, sw);
 }
 
 // ---- 16:32 (EXPAND): 64-column steps, each wave's values of a step through its own LDS area.
@@ -506,10 +571,11 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
                                                                      const uint16_t* __restrict__ X,
                                                                      uint16_t* __restrict__ Y, int rows, int cols,
                                                                      int tokens, int rg_count, int cs_count,
-                                                                     int phase_cols) {
+                                                                     int phase_cols, int splits, float4* part,
+                                                                     unsigned* cnt) {
   static_assert(TR == 1, "one row tile per wave");
   skinny_line_body<SPLIT ? kModeSplit : kModeDirect>(values, masks, X, Y, rows, cols, tokens, rg_count, cs_count,
-                                                     phase_cols);
+                                                     phase_cols, SplitWs{part, cnt, splits});
 }
 
 template <int TR>

@@ -222,6 +222,31 @@ def test_gemm_validation(kw, want):
 
 
 @pytest.mark.parametrize("kw,want", [
+    (dict(values=None), nm.NM_ERR_NULL), (dict(Y=None), nm.NM_ERR_NULL), (dict(batch=0), nm.NM_ERR_SHAPE),
+    (dict(cols=48), nm.NM_ERR_SHAPE), (dict(N=2, M=8, batch=9), nm.NM_ERR_PATTERN),
+    (dict(X=A16 + 8), nm.NM_ERR_ALIGN), (dict(Y=A16 + 1), nm.NM_ERR_ALIGN),
+    # the workspace must be 16-byte aligned whatever kernel the shape takes
+    (dict(ws=A16 + 8), nm.NM_ERR_ALIGN), (dict(ws=A16 + 4, batch=40), nm.NM_ERR_ALIGN),
+    (dict(ws=A16 + 8, batch=1), nm.NM_ERR_ALIGN),
+])
+def test_spmm_ws_validation(kw, want):
+    """nm_spmm_ws: nm_spmm's checks, plus the workspace's alignment, before any HIP call."""
+    a = dict(values=A16, masks=A16, X=A16, Y=A16, rows=1024, cols=4096, batch=8, N=2, M=4, ws=A16)
+    a.update(kw)
+    assert nm.lib().nm_spmm_ws(a["values"], a["masks"], a["X"], a["Y"], a["rows"], a["cols"], a["batch"],
+                               a["N"], a["M"], a["ws"], 1 << 20, None) == want
+
+
+def test_spmm_workspace_bytes_invalid_arguments():
+    """Invalid shapes and patterns need no workspace (0, no HIP call)."""
+    ws = nm.lib().nm_spmm_workspace_bytes
+    assert ws(0, 4096, 8, 2, 4) == 0
+    assert ws(1024, 48, 8, 2, 4) == 0
+    assert ws(1024, 4096, 0, 2, 4) == 0
+    assert ws(1024, 4096, 8, 3, 4) == 0
+
+
+@pytest.mark.parametrize("kw,want", [
     (dict(values=None), nm.NM_ERR_NULL), (dict(masks=None), nm.NM_ERR_NULL), (dict(X=None), nm.NM_ERR_NULL),
     (dict(Y=None), nm.NM_ERR_NULL),
     (dict(tokens=0), nm.NM_ERR_SHAPE), (dict(tokens=(1 << 24) + 1), nm.NM_ERR_SHAPE), (dict(rows=0), nm.NM_ERR_SHAPE),

@@ -154,3 +154,83 @@ def test_skinny_malformed_masks_stay_in_bounds(N, M):
         Y = nm.nm_spmm_skinny(v, m, X, N, M)
         torch.cuda.synchronize()
         assert Y.shape == (T, R)
+
+
+# Column splits (nm_spmm_ws): layers of at most half as many 16-row tiles as CUs take 2, 4 or 8
+# workgroups per tile where that pays (rows of >= 64 lines of 128 columns; >= 40 lines from 8
+# vectors; the split patterns from 9 vectors), each on a range of whole lines, the last to
+# arrive summing the partial tiles. Ragged rows; a ragged last split (8224 columns = 64.25
+# lines over 8 splits, 2080 = 16.25 over 4); several X phases inside one split (16 vectors x
+# 14336 columns); two launches on one workspace, both split (17, 31 vectors) or the second not
+# (1024 x 5120 at 20 vectors: 16 split, then 4 unsplit).
+SPLIT_CASES = [((2, 4), 1024, 8192, 8), ((2, 4), 512, 8192, 5), ((2, 4), 1000, 8192, 17), ((2, 4), 300, 8224, 6),
+               ((2, 4), 2048, 14336, 16), ((4, 8), 1024, 4096, 9), ((8, 16), 1030, 8192, 16),
+               ((8, 16), 512, 8192, 12), ((4, 8), 777, 2080, 31), ((2, 4), 256, 5120, 31), ((2, 4), 1024, 5120, 20)]
+
+
+def _counter_bytes(rows):
+    return -(-(-(-rows // 16) * 4) // 256) * 256
+
+
+@pytest.mark.parametrize("pat,R,C,T", SPLIT_CASES)
+def test_skinny_column_split(pat, R, C, T):
+    N, M = pat
+    need = nm.spmm_workspace_bytes(R, C, T, N, M)
+    assert need > _counter_bytes(R), (R, C, T, need)
+    ws = nm.spmm_workspace(R, C, T, N, M)
+    say(f"skinny split {N}:{M} {R}x{C} vectors={T} workspace={need}")
+    check(R, C, T, 3400 + R % 97 + C % 89 + T + N, N, M,
+                fn=lambda v, m, x, n, mm: nm.nm_spmm_ws(v, m, x, n, mm, ws))
+    # every call leaves the counters at zero, and repeated calls give the same bits
+    assert int(ws[:_counter_bytes(R)].count_nonzero()) == 0
+    W = synth.weight(R, C, 3400 + R % 97 + C % 89 + T + N)
+    v, m = nm.nm_pack(up_f16(W), N, M)
+    X = up_f16(synth.activations(T, C, 3401 + R % 97 + C % 89 + T + N))
+    Y0 = down_bits16(nm.nm_spmm_ws(v, m, X, N, M, ws))
+    for _ in range(5):
+        assert np.array_equal(down_bits16(nm.nm_spmm_ws(v, m, X, N, M, ws)), Y0)
+    assert int(ws[:_counter_bytes(R)].count_nonzero()) == 0
+
+
+def test_skinny_column_split_small_workspace_runs_unsplit():
+    """A workspace smaller than nm_spmm_workspace_bytes (or none) runs nm_spmm's kernels:
+    bit-identical to nm_spmm; shapes without a split need no workspace."""
+    N, M, R, C, T = 2, 4, 1024, 8192, 8
+    W = synth.weight(R, C, 3500)
+    v, m = nm.nm_pack(up_f16(W), N, M)
+    X = up_f16(synth.activations(T, C, 3501))
+    want = down_bits16(nm.nm_spmm(v, m, X, N, M))
+    need = nm.spmm_workspace_bytes(R, C, T, N, M)
+    assert need > 0
+    small = torch.zeros(need - 16, dtype=torch.uint8, device=device())
+    assert np.array_equal(down_bits16(nm.nm_spmm_ws(v, m, X, N, M, small)), want)
+    assert np.array_equal(down_bits16(nm.nm_spmm_ws(v, m, X, N, M, None)), want)
+    assert int(small.count_nonzero()) == 0
+    # no split: 16:32 (expanded fragments), fewer than 5 vectors, layers that fill the GPU,
+    # the prefill sizes, and where the hand-off costs more than it saves (2:4 rows of 32 lines)
+    assert nm.spmm_workspace_bytes(4096, 4096, 16, 16, 32) == 0
+    assert nm.spmm_workspace_bytes(1024, 8192, 4, 2, 4) == 0
+    assert nm.spmm_workspace_bytes(4096, 8192, 8, 2, 4) == 0
+    assert nm.spmm_workspace_bytes(1024, 8192, 40, 2, 4) == 0
+    assert nm.spmm_workspace_bytes(1024, 4096, 16, 2, 4) == 0
+    assert nm.spmm_workspace_bytes(2048, 4096, 16, 4, 8) == 0
+    assert nm.spmm_workspace_bytes(1024, 5120, 5, 2, 4) == 0
+    # sizes: counters padded to 256 bytes, then 1 KiB per tile and split
+    assert nm.spmm_workspace_bytes(1024, 8192, 8, 2, 4) == 256 + 64 * 4 * 1024
+    assert nm.spmm_workspace_bytes(512, 4096, 12, 8, 16) == 256 + 32 * 8 * 1024
+    assert nm.spmm_workspace_bytes(2048, 8192, 5, 2, 4) == 512 + 128 * 2 * 1024
+
+
+def test_skinny_column_split_shared_workspace():
+    """One workspace, sized for the larger shape, serves a larger then a smaller product and
+    a pattern change, in stream order; each matches its own fresh-workspace result."""
+    cases = [((2, 4), 1024, 8192, 16), ((8, 16), 512, 4096, 9), ((2, 4), 1024, 8192, 5)]
+    need = max(nm.spmm_workspace_bytes(R, C, T, N, M) for (N, M), R, C, T in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device=device())
+    for k, ((N, M), R, C, T) in enumerate(cases):
+        W = synth.weight(R, C, 3600 + k)
+        v, m = nm.nm_pack(up_f16(W), N, M)
+        X = up_f16(synth.activations(T, C, 3610 + k))
+        got = down_bits16(nm.nm_spmm_ws(v, m, X, N, M, ws))
+        want = down_bits16(nm.nm_spmm_ws(v, m, X, N, M, nm.spmm_workspace(R, C, T, N, M)))
+        assert np.array_equal(got, want), ((N, M), R, C, T)
