@@ -158,9 +158,10 @@ int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, ui
  * workgroups whose fp32 partial tiles the last-arriving one sums in split order (fixed, so
  * bit-identical run to run, but not bit-identical to nm_spmm's unsplit order: the same
  * tolerance against the exact product). workspace: device memory, 16-byte aligned, owned by
- * the caller; its first 256-byte-rounded tile-count * 4 bytes are counters that must be zero
- * before the first call on it (e.g. one hipMemset when allocated); every call leaves them
- * zero again. NULL or a smaller workspace runs the unsplit kernels (no error). Calls that use
+ * the caller; its first 4 * CU-count bytes, rounded up to 256 (1 KiB on MI355X), are
+ * counters that must be zero before the first call on it (e.g. one hipMemset when
+ * allocated); every call leaves them zero again, so one workspace serves any sequence of
+ * shapes on the device. NULL or a smaller workspace runs the unsplit kernels (no error). Calls that use
  * one workspace must be ordered (one stream): overlapping calls on it race. Other arguments
  * and errors as nm_spmm; a misaligned workspace is NM_ERR_ALIGN. */
 int nm_spmm_ws(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
@@ -168,9 +169,9 @@ int nm_spmm_ws(const uint16_t* values, const uint32_t* masks, const uint16_t* X,
                size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace nm_spmm_ws can use for these arguments on the current device; 0 when
- * the shape takes no column split (or the arguments are invalid, or no device). At most
- * tiles * 4 rounded up to 256, plus tiles * 8 KiB (tiles = ceil(rows / 16); only layers of at
- * most as many tiles as the GPU has CUs take a split). */
+ * the shape takes no column split (or the arguments are invalid, or no device): the
+ * counters, then tiles * splits KiB (tiles = ceil(rows / 16), splits <= 8, tiles * splits <=
+ * CU count; at most 257 KiB on MI355X). */
 size_t nm_spmm_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, int N, int M);
 
 /* The batch product of nm_spmm on the matrix instructions for any batch >= 1, whatever

@@ -100,13 +100,20 @@ const char* skinny_variant(int n) {
   return n == 2 ? "skinny_spmm_kernel<1, false>" : n == 16 ? "skinny_expand_kernel<1>" : "skinny_spmm_kernel<1, true>";
 }
 
+// The workspace: one counter per tile in a region of fixed size on a device (4 bytes per
+// CU, rounded up to 256: a split layer has fewer tiles than CUs), so that every shape finds
+// its counters where the previous calls left zeros; then one 1 KiB fp32 partial per tile
+// and split.
+size_t counter_bytes(const DeviceInfo& dev) {
+  return size_t(ceil_div(4 * int64_t(dev.cu_count > 0 ? dev.cu_count : 256), 256) * 256);
+}
+
 size_t skinny_workspace_bytes(int64_t rows, int64_t cols, int tokens, int n, const DeviceInfo& dev) {
   const int64_t tiles = ceil_div(rows, 16);
   if (ceil_div(tiles, dev.cu_count > 0 ? dev.cu_count : 256) > 1) return 0;
   const int splits = splits_for(tiles, cols, tokens, mode_of(n), dev);
   if (splits == 1) return 0;
-  // counters (padded to 256 bytes), then one 1 KiB fp32 partial per tile and split
-  return size_t(ceil_div(tiles * 4, 256) * 256) + size_t(tiles) * size_t(splits) * 1024u;
+  return counter_bytes(dev) + size_t(tiles) * size_t(splits) * 1024u;
 }
 
 hipError_t launch_skinny_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
@@ -118,10 +125,8 @@ hipError_t launch_skinny_spmm(const uint16_t* values, const uint32_t* masks, con
   const bool split = need > 0 && workspace != nullptr && workspace_bytes >= need;
   const SkinnyShape s = skinny_shape(rows, cols, tokens, mode, dev, split);
   int r = int(rows), c = int(cols), t = tokens, rg = s.rg, cs = s.cs, pc = s.phase_cols, sp = s.splits;
-  const int64_t tiles = ceil_div(rows, 16);
   unsigned* cnt = split ? static_cast<unsigned*>(workspace) : nullptr;
-  float4* part = split ? reinterpret_cast<float4*>(static_cast<char*>(workspace) + ceil_div(tiles * 4, 256) * 256)
-                       : nullptr;
+  float4* part = split ? reinterpret_cast<float4*>(static_cast<char*>(workspace) + counter_bytes(dev)) : nullptr;
   if (mode == kModeExpand) {
     void* args[] = {&values, &masks, &X, &Y, &r, &c, &t, &rg, &cs, &pc};
     return launch(reinterpret_cast<const void*>(&skinny_expand_kernel<1>), dim3(unsigned(s.grid)),

@@ -168,28 +168,30 @@ SPLIT_CASES = [((2, 4), 1024, 8192, 8), ((2, 4), 512, 8192, 5), ((2, 4), 1000, 8
                ((8, 16), 512, 8192, 12), ((4, 8), 777, 2080, 31), ((2, 4), 256, 5120, 31), ((2, 4), 1024, 5120, 20)]
 
 
-def _counter_bytes(rows):
-    return -(-(-(-rows // 16) * 4) // 256) * 256
+def _counter_bytes():
+    """The counters' region: 4 bytes per CU, rounded up to 256."""
+    cus = torch.cuda.get_device_properties(device()).multi_processor_count
+    return -(-(4 * cus) // 256) * 256
 
 
 @pytest.mark.parametrize("pat,R,C,T", SPLIT_CASES)
 def test_skinny_column_split(pat, R, C, T):
     N, M = pat
     need = nm.spmm_workspace_bytes(R, C, T, N, M)
-    assert need > _counter_bytes(R), (R, C, T, need)
+    assert need > _counter_bytes(), (R, C, T, need)
     ws = nm.spmm_workspace(R, C, T, N, M)
     say(f"skinny split {N}:{M} {R}x{C} vectors={T} workspace={need}")
     check(R, C, T, 3400 + R % 97 + C % 89 + T + N, N, M,
                 fn=lambda v, m, x, n, mm: nm.nm_spmm_ws(v, m, x, n, mm, ws))
     # every call leaves the counters at zero, and repeated calls give the same bits
-    assert int(ws[:_counter_bytes(R)].count_nonzero()) == 0
+    assert int(ws[:_counter_bytes()].count_nonzero()) == 0
     W = synth.weight(R, C, 3400 + R % 97 + C % 89 + T + N)
     v, m = nm.nm_pack(up_f16(W), N, M)
     X = up_f16(synth.activations(T, C, 3401 + R % 97 + C % 89 + T + N))
     Y0 = down_bits16(nm.nm_spmm_ws(v, m, X, N, M, ws))
     for _ in range(5):
         assert np.array_equal(down_bits16(nm.nm_spmm_ws(v, m, X, N, M, ws)), Y0)
-    assert int(ws[:_counter_bytes(R)].count_nonzero()) == 0
+    assert int(ws[:_counter_bytes()].count_nonzero()) == 0
 
 
 def test_skinny_column_split_small_workspace_runs_unsplit():
@@ -215,16 +217,20 @@ def test_skinny_column_split_small_workspace_runs_unsplit():
     assert nm.spmm_workspace_bytes(1024, 4096, 16, 2, 4) == 0
     assert nm.spmm_workspace_bytes(2048, 4096, 16, 4, 8) == 0
     assert nm.spmm_workspace_bytes(1024, 5120, 5, 2, 4) == 0
-    # sizes: counters padded to 256 bytes, then 1 KiB per tile and split
-    assert nm.spmm_workspace_bytes(1024, 8192, 8, 2, 4) == 256 + 64 * 4 * 1024
-    assert nm.spmm_workspace_bytes(512, 4096, 12, 8, 16) == 256 + 32 * 8 * 1024
-    assert nm.spmm_workspace_bytes(2048, 8192, 5, 2, 4) == 512 + 128 * 2 * 1024
+    # sizes: the counters (4 bytes per CU, rounded up to 256), then 1 KiB per tile and split
+    c = _counter_bytes()
+    if torch.cuda.get_device_properties(device()).multi_processor_count == 256:
+        assert nm.spmm_workspace_bytes(1024, 8192, 8, 2, 4) == c + 64 * 4 * 1024
+        assert nm.spmm_workspace_bytes(512, 4096, 12, 8, 16) == c + 32 * 8 * 1024
+        assert nm.spmm_workspace_bytes(2048, 8192, 5, 2, 4) == c + 128 * 2 * 1024
 
 
 def test_skinny_column_split_shared_workspace():
-    """One workspace, sized for the larger shape, serves a larger then a smaller product and
-    a pattern change, in stream order; each matches its own fresh-workspace result."""
-    cases = [((2, 4), 1024, 8192, 16), ((8, 16), 512, 4096, 9), ((2, 4), 1024, 8192, 5)]
+    """One workspace, sized for the largest shape, serves products of more and fewer tiles
+    and a pattern change, in stream order (a shape of 128 tiles after ones of 32 and 64
+    finds its counters at zero); each matches its own fresh-workspace result."""
+    cases = [((2, 4), 1024, 8192, 16), ((8, 16), 512, 4096, 9), ((2, 4), 2048, 8192, 8), ((2, 4), 512, 8192, 5),
+             ((2, 4), 2048, 14336, 12), ((2, 4), 1024, 8192, 5)]
     need = max(nm.spmm_workspace_bytes(R, C, T, N, M) for (N, M), R, C, T in cases)
     ws = torch.zeros(need, dtype=torch.uint8, device=device())
     for k, ((N, M), R, C, T) in enumerate(cases):
