@@ -61,7 +61,9 @@ typedef enum {
                           batch > 1; nm_spmm_prefill: 2:4, 4:8, 8:16)                 */
   NM_ERR_ALIGN = 4,    /* W, values or x not 16-byte aligned; masks not 4-byte; y not 2 */
   NM_ERR_TOO_WIDE = 5, /* 2*cols bytes of x exceed the LDS one workgroup may use        */
-  NM_ERR_HIP = 6       /* a HIP runtime call failed (see nm_last_hip_error)             */
+  NM_ERR_HIP = 6,      /* a HIP runtime call failed (see nm_last_hip_error)             */
+  NM_ERR_SCRATCH = 7   /* nm_spmm_noalloc: the shape's column split needs more than the
+                          library's static scratch (NM_NOALLOC_SCRATCH_BYTES)              */
 } nm_status;
 
 /* Number of fp16 values of the packed matrix: rows*cols*N/M; 0 if the arguments are
@@ -173,6 +175,21 @@ int nm_spmm_ws(const uint16_t* values, const uint32_t* masks, const uint16_t* X,
  * counters, then tiles * splits KiB (tiles = ceil(rows / 16), splits <= 8, tiles * splits <=
  * CU count; at most 257 KiB on MI355X). */
 size_t nm_spmm_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, int N, int M);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): nm_spmm_ws with its workspace in a
+ * static device array of the library, NM_NOALLOC_SCRATCH_BYTES per GPU, held from the first
+ * call on that GPU until the process ends. The same arguments, routing, Y and errors as
+ * nm_spmm_ws with a workspace of that size; a shape whose column split needs more
+ * (nm_spmm_workspace_bytes > NM_NOALLOC_SCRATCH_BYTES; none on MI355X, whose largest is
+ * 257 KiB) is NM_ERR_SCRATCH before any launch. Calls no hipMalloc/hipFree. The first call
+ * on a GPU looks the array up (hipGetSymbolAddress) and queues a fill kernel that clears it
+ * on `stream`, ahead of its own kernels; the kernels leave the counters at zero after every
+ * call. All calls on one GPU share the array: calls that overlap on one GPU (other streams,
+ * other threads, without ordering between them) race and give unspecified Y. */
+#define NM_NOALLOC_SCRATCH_BYTES (512u * 1024u)
+int nm_spmm_noalloc(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
+                    int64_t rows, int64_t cols, int64_t batch, int N, int M, void* stream);
 
 /* The batch product of nm_spmm on the matrix instructions for any batch >= 1, whatever
  * nm_spmm's routing would pick (the same Y definition, summation in the instructions' fixed

@@ -18,7 +18,7 @@ PATTERNS = ((2, 4), (4, 8), (8, 16), (16, 32))
 PATTERNS_QUARTER = ((1, 4), (2, 8), (4, 16), (8, 32))   # 25% density, single vector
 ALL_PATTERNS = PATTERNS + PATTERNS_QUARTER
 
-NM_OK, NM_ERR_NULL, NM_ERR_SHAPE, NM_ERR_PATTERN, NM_ERR_ALIGN, NM_ERR_TOO_WIDE, NM_ERR_HIP = range(7)
+NM_OK, NM_ERR_NULL, NM_ERR_SHAPE, NM_ERR_PATTERN, NM_ERR_ALIGN, NM_ERR_TOO_WIDE, NM_ERR_HIP, NM_ERR_SCRATCH = range(8)
 
 # Every symbol the public headers declare, with (restype, argtypes).
 _c = ctypes
@@ -42,6 +42,8 @@ SIGNATURES = {
     "nm_spmm_ws": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
                               _c.c_int64, _c.c_int, _c.c_int, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "nm_spmm_workspace_bytes": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int, _c.c_int]),
+    "nm_spmm_noalloc": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
+                                   _c.c_int64, _c.c_int64, _c.c_int, _c.c_int, _c.c_void_p]),
     "nm_spmm_skinny": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64,
                                   _c.c_int64, _c.c_int64, _c.c_int, _c.c_int, _c.c_void_p]),
     "nm_gemm_dense": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
@@ -377,6 +379,19 @@ def nm_spmm_ws(values, masks, X, N: int, M: int, workspace=None, out=None):
         st = lib().nm_spmm_ws(values.data_ptr(), masks.data_ptr(), X.data_ptr(), out.data_ptr(),
                               rows, cols, batch, N, M, ws_ptr, ws_bytes, _stream_ptr(X))
     _check("nm_spmm_ws", st)
+    return out
+
+
+def nm_spmm_noalloc(values, masks, X, N: int, M: int, out=None):
+    """nm_spmm_ws with the library's static per-GPU scratch as the workspace (for callers
+    that cannot allocate; calls overlapping on one GPU race). out=None allocates Y here in
+    the binding, not in the library: pass `out` to allocate nothing."""
+    torch = _torch()
+    rows, cols, batch, out = _batch_args(values, masks, X, N, M, out)
+    with torch.cuda.device(X.device):
+        st = lib().nm_spmm_noalloc(values.data_ptr(), masks.data_ptr(), X.data_ptr(), out.data_ptr(),
+                                   rows, cols, batch, N, M, _stream_ptr(X))
+    _check("nm_spmm_noalloc", st)
     return out
 
 

@@ -78,6 +78,56 @@ hipError_t launch(const void* kernel, dim3 grid, dim3 block, void** args, size_t
   return hipLaunchKernel(kernel, grid, block, args, lds, stream);
 }
 
+// nm_spmm's argument checks, before any HIP call.
+int spmm_check(const uint16_t* values, const uint32_t* masks, const uint16_t* X, const uint16_t* Y, int64_t rows,
+               int64_t cols, int64_t batch, int N, int M) {
+  if (!values || !masks || !X || !Y) return NM_ERR_NULL;
+  if (!valid_shape(rows, cols) || batch < 1 || batch > kPrefillMaxTokens) return NM_ERR_SHAPE;
+  if (!valid_pattern(N, M) || (batch > 1 && M != 2 * N)) return NM_ERR_PATTERN;
+  if (!aligned(values, 16) || !aligned(masks, 4) || !aligned(X, 16) || !aligned(Y, 2)) return NM_ERR_ALIGN;
+  return NM_OK;
+}
+
+// nm_spmm's dispatch, with an optional workspace for the skinny kernels' column splits.
+int spmm_dispatch(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y, int64_t rows,
+                  int64_t cols, int64_t batch, int N, int M, void* stream, void* workspace, size_t workspace_bytes) {
+  const int st = spmm_check(values, masks, X, Y, rows, cols, batch, N, M);
+  if (st != NM_OK) return st;
+  if (!aligned(workspace, 16)) return NM_ERR_ALIGN;
+  if (batch >= kMatrixCoreMinBatch && prefill_pattern(N, M))  // matrix-core product
+    return nm_spmm_prefill(values, masks, X, Y, rows, cols, batch, N, M, stream);
+  DeviceInfo dev;
+  hipError_t e = current_device_info(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (M != 2 * N && cols > max_cols_for(dev)) return NM_ERR_TOO_WIDE;  // 25%: single-vector kernel only
+  if (use_skinny(rows, cols, batch, N, M, dev)) {
+    // 50% patterns at 5..31 vectors where measured faster: the matrix instructions, 16
+    // vectors per launch (launches in stream order, so one workspace serves them all)
+    for (int64_t b0 = 0; b0 < batch; b0 += kSkinnyBatch) {
+      const int nb = int(batch - b0 < kSkinnyBatch ? batch - b0 : kSkinnyBatch);
+      e = launch_skinny_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb, N, M,
+                             static_cast<hipStream_t>(stream), dev, workspace, workspace_bytes);
+      if (e != hipSuccess) return hip_fail(e);
+    }
+    return NM_OK;
+  }
+  // otherwise (fewer vectors, smaller layers, most 16:32 shapes): the small-batch kernel on consecutive
+  // groups of kSmallBatch rows of X (X and Y rows are contiguous)
+  for (int64_t b0 = 0; b0 < batch; b0 += kSmallBatch) {
+    const int nb = int(batch - b0 < kSmallBatch ? batch - b0 : kSmallBatch);
+    e = launch_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb, N, M,
+                    static_cast<hipStream_t>(stream), dev);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return NM_OK;
+}
+
+// Workspace bytes spmm_dispatch can use for the product (0 when it would not use one).
+size_t spmm_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev) {
+  if (!valid_shape(rows, cols) || !valid_pattern(N, M) || batch < 1 || batch > kPrefillMaxTokens) return 0;
+  if (batch >= kMatrixCoreMinBatch || !use_skinny(rows, cols, batch, N, M, dev)) return 0;
+  return skinny_workspace_bytes(rows, cols, int(batch < kSkinnyBatch ? batch : kSkinnyBatch), N, dev);
+}
 }  // namespace nm
 
 extern "C" {
@@ -202,50 +252,6 @@ int nm_gemm_dense_prefill(const uint16_t* W, const uint16_t* X, uint16_t* Y, int
   return e == hipSuccess ? NM_OK : nm::hip_fail(e);
 }
 
-namespace nm {
-// nm_spmm's dispatch, with an optional workspace for the skinny kernels' column splits.
-int spmm_dispatch(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y, int64_t rows,
-                  int64_t cols, int64_t batch, int N, int M, void* stream, void* workspace, size_t workspace_bytes) {
-  if (!values || !masks || !X || !Y) return NM_ERR_NULL;
-  if (!valid_shape(rows, cols) || batch < 1 || batch > kPrefillMaxTokens) return NM_ERR_SHAPE;
-  if (!valid_pattern(N, M) || (batch > 1 && M != 2 * N)) return NM_ERR_PATTERN;
-  if (!aligned(workspace, 16)) return NM_ERR_ALIGN;
-  if (batch >= kMatrixCoreMinBatch && prefill_pattern(N, M))  // matrix-core product
-    return nm_spmm_prefill(values, masks, X, Y, rows, cols, batch, N, M, stream);
-  if (!aligned(values, 16) || !aligned(masks, 4) || !aligned(X, 16) || !aligned(Y, 2)) return NM_ERR_ALIGN;
-  DeviceInfo dev;
-  hipError_t e = current_device_info(&dev);
-  if (e != hipSuccess) return hip_fail(e);
-  if (M != 2 * N && cols > max_cols_for(dev)) return NM_ERR_TOO_WIDE;  // 25%: single-vector kernel only
-  if (use_skinny(rows, cols, batch, N, M, dev)) {
-    // 50% patterns at 5..31 vectors where measured faster: the matrix instructions, 16
-    // vectors per launch (launches in stream order, so one workspace serves them all)
-    for (int64_t b0 = 0; b0 < batch; b0 += kSkinnyBatch) {
-      const int nb = int(batch - b0 < kSkinnyBatch ? batch - b0 : kSkinnyBatch);
-      e = launch_skinny_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb, N, M,
-                             static_cast<hipStream_t>(stream), dev, workspace, workspace_bytes);
-      if (e != hipSuccess) return hip_fail(e);
-    }
-    return NM_OK;
-  }
-  // otherwise (fewer vectors, smaller layers, most 16:32 shapes): the small-batch kernel on consecutive
-  // groups of kSmallBatch rows of X (X and Y rows are contiguous)
-  for (int64_t b0 = 0; b0 < batch; b0 += kSmallBatch) {
-    const int nb = int(batch - b0 < kSmallBatch ? batch - b0 : kSmallBatch);
-    e = launch_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb, N, M,
-                    static_cast<hipStream_t>(stream), dev);
-    if (e != hipSuccess) return hip_fail(e);
-  }
-  return NM_OK;
-}
-
-// Workspace bytes spmm_dispatch can use for the product (0 when it would not use one).
-size_t spmm_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev) {
-  if (!valid_shape(rows, cols) || !valid_pattern(N, M) || batch < 1 || batch > kPrefillMaxTokens) return 0;
-  if (batch >= kMatrixCoreMinBatch || !use_skinny(rows, cols, batch, N, M, dev)) return 0;
-  return skinny_workspace_bytes(rows, cols, int(batch < kSkinnyBatch ? batch : kSkinnyBatch), N, dev);
-}
-}  // namespace nm
 
 int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
             int64_t rows, int64_t cols, int64_t batch, int N, int M, void* stream) {
@@ -354,6 +360,7 @@ const char* nm_status_string(int status) {
     case NM_ERR_ALIGN: return "misaligned pointer: W, values and x need 16 bytes, masks 4, y 2";
     case NM_ERR_TOO_WIDE: return "cols too large: x does not fit in the LDS of one workgroup";
     case NM_ERR_HIP: return "a HIP runtime call failed";
+    case NM_ERR_SCRATCH: return "the column split of this shape needs more than the library's static scratch";
     default: return "unknown status";
   }
 }

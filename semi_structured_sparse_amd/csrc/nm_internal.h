@@ -133,6 +133,15 @@ constexpr int64_t kSkinnyExpandMaxCols = 4096;
 bool use_skinny(int64_t rows, int64_t cols, int64_t batch, int n, int m, const DeviceInfo& dev);
 const char* skinny_variant(int n);
 
+// nm_spmm's argument checks (host only, no HIP call): NM_OK or the status to return.
+int spmm_check(const uint16_t* values, const uint32_t* masks, const uint16_t* X, const uint16_t* Y, int64_t rows,
+               int64_t cols, int64_t batch, int N, int M);
+// nm_spmm's dispatch; with a workspace of at least spmm_workspace_bytes (counters zero) the
+// skinny kernels split the columns of short layers.
+int spmm_dispatch(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y, int64_t rows,
+                  int64_t cols, int64_t batch, int N, int M, void* stream, void* workspace, size_t workspace_bytes);
+size_t spmm_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev);
+
 // Name of the kernel configuration the prefill launchers pick (static string).
 const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev, bool split = false);
 

@@ -39,8 +39,9 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert nm.status_string(s)
+    assert "scratch" in nm.status_string(nm.NM_ERR_SCRATCH)
     assert nm.status_string(99) == "unknown status"
     assert nm.status_string(0) == "ok"
 
@@ -235,6 +236,34 @@ def test_spmm_ws_validation(kw, want):
     a.update(kw)
     assert nm.lib().nm_spmm_ws(a["values"], a["masks"], a["X"], a["Y"], a["rows"], a["cols"], a["batch"],
                                a["N"], a["M"], a["ws"], 1 << 20, None) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(values=None), nm.NM_ERR_NULL), (dict(X=None), nm.NM_ERR_NULL), (dict(batch=0), nm.NM_ERR_SHAPE),
+    (dict(rows=0), nm.NM_ERR_SHAPE), (dict(cols=48), nm.NM_ERR_SHAPE), (dict(N=2, M=8, batch=9), nm.NM_ERR_PATTERN),
+    (dict(N=3, M=4), nm.NM_ERR_PATTERN), (dict(X=A16 + 8), nm.NM_ERR_ALIGN), (dict(Y=A16 + 1), nm.NM_ERR_ALIGN),
+    (dict(masks=A16 + 2, batch=40), nm.NM_ERR_ALIGN),
+])
+def test_spmm_noalloc_validation(kw, want):
+    """nm_spmm_noalloc: nm_spmm's checks before any HIP call (so before the scratch lookup)."""
+    a = dict(values=A16, masks=A16, X=A16, Y=A16, rows=1024, cols=8192, batch=8, N=2, M=4)
+    a.update(kw)
+    assert nm.lib().nm_spmm_noalloc(a["values"], a["masks"], a["X"], a["Y"], a["rows"], a["cols"], a["batch"],
+                                    a["N"], a["M"], None) == want
+
+
+def test_noalloc_scratch_is_static_and_bounded():
+    """The scratch array is a file-scope static device array of the declared size, reached
+    through hipGetSymbolAddress; the entry point's source calls no allocator."""
+    src = open(os.path.join(ROOT, "semi_structured_sparse_amd", "csrc", "nm_noalloc.hip")).read()
+    code = re.sub(r"//[^\n]*", "", src)
+    assert re.search(r"static __device__ __align__\(256\) unsigned char scratch\[kScratchBytes\]", code)
+    assert "hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))" in code
+    for alloc in ("hipMalloc", "hipFree", "hipMemset", "hipExtMalloc", "hipHostMalloc", "malloc(", "new "):
+        assert alloc not in code, alloc
+    hdr = open(os.path.join(ROOT, "include", "nm_sparse.h")).read()
+    m = re.search(r"#define NM_NOALLOC_SCRATCH_BYTES \((\d+)u \* (\d+)u\)", hdr)
+    assert m and int(m.group(1)) * int(m.group(2)) == 512 * 1024
 
 
 def test_spmm_workspace_bytes_invalid_arguments():
