@@ -132,7 +132,13 @@ hipError_t launch_skinny_spmm(const uint16_t* values, const uint32_t* masks, con
     return launch(reinterpret_cast<const void*>(&skinny_expand_kernel<1>), dim3(unsigned(s.grid)),
                   dim3(kThreadsFixed), args, s.lds, stream, dev);
   }
-  void* args[] = {&values, &masks, &X, &Y, &r, &c, &t, &rg, &cs, &pc, &sp, &part, &cnt};
+  if (s.splits > 1) {
+    void* args[] = {&values, &masks, &X, &Y, &r, &c, &t, &cs, &pc, &sp, &part, &cnt};
+    const void* k = mode == kModeSplit ? reinterpret_cast<const void*>(&skinny_colsplit_kernel<true>)
+                                       : reinterpret_cast<const void*>(&skinny_colsplit_kernel<false>);
+    return launch(k, dim3(unsigned(s.grid)), dim3(kThreadsFixed), args, s.lds, stream, dev);
+  }
+  void* args[] = {&values, &masks, &X, &Y, &r, &c, &t, &rg, &cs, &pc};
   const void* k = mode == kModeSplit ? reinterpret_cast<const void*>(&skinny_spmm_kernel<1, true>)
                                      : reinterpret_cast<const void*>(&skinny_spmm_kernel<1, false>);
   return launch(k, dim3(unsigned(s.grid)), dim3(kThreadsFixed), args, s.lds, stream, dev);

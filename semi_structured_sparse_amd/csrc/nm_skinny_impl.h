@@ -158,8 +158,10 @@ struct Tile {
     // meet the barriers but own no rows
     active = rg < rg_count;
     const int wg_rows_max = rg_count * 16;
-    const int wg = int(blockIdx.x) / splits;
-    split = int(blockIdx.x) - wg * splits;
+    // splits is 1, 2, 4 or 8: a shift, and none of it without a split
+    const int sh = splits == 1 ? 0 : splits == 2 ? 1 : splits == 4 ? 2 : 3;
+    const int wg = int(blockIdx.x) >> sh;
+    split = int(blockIdx.x) & (splits - 1);
     tile0 = wg * rg_count;
     wg_r0 = wg * wg_rows_max;
     const int wg_rows = min(wg_rows_max, rows - wg_r0);
@@ -294,7 +296,9 @@ __device__ __forceinline__ uint4 sel4(bool c, uint4 a, uint4 b) {
 constexpr int kLineDepth = 2;   // lines (two loads each) in flight per wave
 constexpr int kMaskLines = 2;   // lines per mask block (8 words of each row)
 
-template <int MODE>
+// COLS: the column-split form (skinny_colsplit_kernel); without it the split bookkeeping is
+// compiled out, so that the unsplit kernel is the same code as before the split existed.
+template <int MODE, bool COLS>
 __device__ __forceinline__ void skinny_line_body(const uint16_t* __restrict__ values,
                                                  const uint32_t* __restrict__ masks,
                                                  const uint16_t* __restrict__ X, uint16_t* __restrict__ Y,
@@ -305,12 +309,16 @@ __device__ __forceinline__ void skinny_line_body(const uint16_t* __restrict__ va
   extern __shared__ __attribute__((aligned(16))) char lds_base[];
   char* const lds = lds_base + lead_bytes<MODE>();   // SPLIT: the split tables first, X after them
   const int tid = threadIdx.x;
-  const Tile w(values, masks, X, rows, cols, tokens, rg_count, cs_count, sw.splits);
+  const Tile w(values, masks, X, rows, cols, tokens, rg_count, cs_count, COLS ? sw.splits : 1);
   const int q = w.q, li = w.li;
   // this workgroup's columns: lines [L s / S, L (s + 1) / S) of the row's L for split s of S
-  const int lines = (cols + 127) >> 7;
-  const int c_beg = 128 * int((int64_t(lines) * w.split) / sw.splits);
-  const int c_end = min(cols, 128 * int((int64_t(lines) * (w.split + 1)) / sw.splits));
+  // (lines <= 2^14 and splits <= 8: 32-bit products); without a split the whole row
+  int c_beg = 0, c_end = cols;
+  if constexpr (COLS) {
+    const unsigned lines = unsigned(cols + 127) >> 7;
+    c_beg = 128 * int(lines * unsigned(w.split) / unsigned(sw.splits));
+    c_end = min(cols, 128 * int(lines * unsigned(w.split + 1) / unsigned(sw.splits)));
+  }
   // value loads: lane l of load h reads row 8h + l % 8 of the row group, chunk kc of the line
   const int kc = 2 * q + ((w.lane >> 3) & 1);
   const uint32_t voff0 = uint32_t(w.rg * 16 + (w.lane & 7)) * uint32_t(cols) + 16u * uint32_t(kc);
@@ -439,7 +447,10 @@ __device__ __forceinline__ void skinny_line_body(const uint16_t* __restrict__ va
       }
     }
   }
-  reduce_store(w, acc, cs_count, rows, tokens, Y, lds_base, sw);
+  if constexpr (COLS)
+    reduce_store(w, acc, cs_count, rows, tokens, Y, lds_base, sw);
+  else
+    reduce_store(w, acc, cs_count, rows, tokens, Y, lds_base);
 }
 
 // ---- 16:32 (EXPAND): 64-column steps, each wave's values of a step through its own LDS area.
@@ -571,11 +582,23 @@ __global__ __launch_bounds__(kThreadsFixed) void skinny_spmm_kernel(const uint16
                                                                      const uint16_t* __restrict__ X,
                                                                      uint16_t* __restrict__ Y, int rows, int cols,
                                                                      int tokens, int rg_count, int cs_count,
-                                                                     int phase_cols, int splits, float4* part,
-                                                                     unsigned* cnt) {
+                                                                     int phase_cols) {
   static_assert(TR == 1, "one row tile per wave");
-  skinny_line_body<SPLIT ? kModeSplit : kModeDirect>(values, masks, X, Y, rows, cols, tokens, rg_count, cs_count,
-                                                     phase_cols, SplitWs{part, cnt, splits});
+  skinny_line_body<SPLIT ? kModeSplit : kModeDirect, false>(values, masks, X, Y, rows, cols, tokens, rg_count,
+                                                            cs_count, phase_cols, SplitWs{nullptr, nullptr, 1});
+}
+
+// The same products with the columns of each 16-row tile split over `splits` (2, 4 or 8)
+// consecutive workgroups, one tile per workgroup (SplitWs: partials and counters).
+template <bool SPLIT>
+__global__ __launch_bounds__(kThreadsFixed) void skinny_colsplit_kernel(const uint16_t* __restrict__ values,
+                                                                         const uint32_t* __restrict__ masks,
+                                                                         const uint16_t* __restrict__ X,
+                                                                         uint16_t* __restrict__ Y, int rows, int cols,
+                                                                         int tokens, int cs_count, int phase_cols,
+                                                                         int splits, float4* part, unsigned* cnt) {
+  skinny_line_body<SPLIT ? kModeSplit : kModeDirect, true>(values, masks, X, Y, rows, cols, tokens, 1, cs_count,
+                                                           phase_cols, SplitWs{part, cnt, splits});
 }
 
 template <int TR>
