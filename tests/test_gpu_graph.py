@@ -3,8 +3,9 @@ into a torch.cuda.CUDAGraph and replayed several times, with the program's own e
 (other products, torch ops, a new input written in place) between the replays. Each replay
 must give the bits an eager call gives on the same inputs (the kernels are deterministic),
 and the first eager result is checked against the CPU oracle, so the captured path is tied
-to the oracle too. The library allocates nothing and records no memset, so nothing it
-captures depends on the capture-time state of its buffers."""
+to the oracle too. The library allocates nothing and records no memset (the column split
+resets its counters in its kernels), so nothing it captures depends on the capture-time
+state of its buffers."""
 import numpy as np
 import pytest
 import torch
@@ -122,3 +123,36 @@ def test_prefill_graph_replays():
 
     _replay_and_check(lambda: nm.nm_spmm_prefill(values, masks, Xd, out=Y), [values, masks, Xd], Y, reseed)
     _replay_and_check(lambda: nm.nm_gemm_dense_prefill(Wd, Xd, out=Yd), [Wd, Xd], Yd, reseed)
+
+
+# column splits (nm_spmm_ws, and nm_spmm_noalloc on the library's static scratch): the
+# counters are reset by the kernels themselves, so replays find them at zero
+SPLIT_GRAPH_CASES = [(2, 4, 1024, 8192, 8), (4, 8, 1024, 4096, 12), (2, 4, 1000, 8192, 17)]
+
+
+@pytest.mark.parametrize("N,M,R,C,B", SPLIT_GRAPH_CASES)
+def test_spmm_column_split_graph_replays(N, M, R, C, B):
+    need = nm.spmm_workspace_bytes(R, C, B, N, M)
+    assert need > 0
+    say(f"graph spmm column split {N}:{M} {R}x{C} B={B} workspace={need}")
+    W = synth.weight(R, C, 5600 + N + B)
+    X = synth.activations(B, C, 5601 + N + B)
+    values, masks = nm.nm_pack(up_f16(W), N, M)
+    Xd = up_f16(X)
+    ws = nm.spmm_workspace(R, C, B, N, M)
+    Y = torch.empty((B, R), dtype=torch.float16, device=device())
+    nm.nm_spmm_ws(values, masks, Xd, N, M, ws, out=Y)
+    torch.cuda.synchronize()
+    rv, rm = oracle.pack_ref(W[:48], N, M)
+    rep = oracle.y_tolerance_report(down_f16(Y)[:, :48], oracle.spmm_ref(rv, rm, X, C, N, M))
+    assert rep["ok"], rep
+
+    def reseed(i):
+        Xd.copy_(up_f16(synth.activations(B, C, 5700 + 10 * B + i)))
+
+    _replay_and_check(lambda: nm.nm_spmm_ws(values, masks, Xd, N, M, ws, out=Y), [values, masks, Xd], Y, reseed)
+    cus = torch.cuda.get_device_properties(device()).multi_processor_count
+    assert int(ws[:-(-(4 * cus) // 256) * 256].count_nonzero()) == 0
+    Yn = torch.empty((B, R), dtype=torch.float16, device=device())
+    _replay_and_check(lambda: nm.nm_spmm_noalloc(values, masks, Xd, N, M, out=Yn), [values, masks, Xd], Yn, reseed)
+    assert np.array_equal(down_bits16(Yn), down_bits16(nm.nm_spmm_ws(values, masks, Xd, N, M, ws)))
