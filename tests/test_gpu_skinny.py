@@ -240,3 +240,29 @@ def test_skinny_column_split_shared_workspace():
         got = down_bits16(nm.nm_spmm_ws(v, m, X, N, M, ws))
         want = down_bits16(nm.nm_spmm_ws(v, m, X, N, M, nm.spmm_workspace(R, C, T, N, M)))
         assert np.array_equal(got, want), ((N, M), R, C, T)
+
+
+# boundaries of the column split: 128 tiles (half the CUs of a 256-CU part: 2 splits) against
+# 129 (none); batch 5 (first skinny size), 31 (last, two launches) and 32 (prefill route, no
+# workspace); a workspace of exactly nm_spmm_workspace_bytes
+@pytest.mark.parametrize("R,C,T,N,M", [(2048, 8192, 5, 2, 4), (2064, 8192, 8, 2, 4), (2048, 8192, 31, 8, 16),
+                                       (1024, 8192, 32, 2, 4), (1040, 14336, 16, 2, 4)])
+def test_skinny_column_split_boundaries(R, C, T, N, M):
+    need = nm.spmm_workspace_bytes(R, C, T, N, M)
+    cus = torch.cuda.get_device_properties(device()).multi_processor_count
+    tiles = -(-R // 16)
+    if T >= 32 or 2 * tiles > cus:
+        assert need == 0, (R, C, T, need)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=device())[:need] if need else None
+    say(f"skinny split boundary {N}:{M} {R}x{C} vectors={T} workspace={need}")
+    W = synth.weight(R, C, 3800 + R % 97 + T)
+    X = synth.activations(T, C, 3801 + R % 97 + T)
+    v, m = nm.nm_pack(up_f16(W), N, M)
+    Xd = up_f16(X)
+    got = down_f16(nm.nm_spmm_ws(v, m, Xd, N, M, ws))
+    idx = sample_rows(R, k=24, rpb=16)
+    rv, rm = oracle.pack_ref(W[idx], N, M)
+    rep = oracle.y_tolerance_report(got[:, idx], oracle.spmm_ref(rv, rm, X, C, N, M))
+    assert rep["ok"], rep
+    if need == 0:   # no split: nm_spmm's kernels, bit for bit
+        assert np.array_equal(down_bits16(nm.nm_spmm_ws(v, m, Xd, N, M, ws)), down_bits16(nm.nm_spmm(v, m, Xd, N, M)))
