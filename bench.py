@@ -64,8 +64,8 @@ def parse_args():
     ap.add_argument("--patterns", default="", help="patterns to run instead of the workload's, e.g. 2:4,16:32 "
                                                   "or the 25%% ones 1:4,2:8,4:16,8:32")
     ap.add_argument("--batch", type=int, default=1,
-                    help="activation vectors per product (1: nm_spmv / nm_gemv_dense; 2..8: "
-                         "nm_spmm / nm_gemm_dense)")
+                    help="activation vectors per product (1: nm_spmv / nm_gemv_dense; 2..31: "
+                         "nm_spmm_ws with a workspace per layer / nm_gemm_dense)")
     return ap.parse_args()
 
 
@@ -289,11 +289,28 @@ def make_layers(torch, nm, synth, dev, cfg, specs, pats, B, cpu_rows_frac, keep_
     return layers, dense
 
 
+def ws_args(L, B):
+    """The workspace arguments of nm_spmm_ws for layer L (none at batch one; NULL where the
+    shape takes no column split)."""
+    if B == 1:
+        return ()
+    ws = L.get("ws")
+    return (None, 0) if ws is None else (ws.data_ptr(), ws.numel())
+
+
+def batch_kernel_name(nm, L, B):
+    """Kernel of nm_spmm_ws for layer L: the column-split kernel where it has a workspace,
+    nm_spmm's kernel otherwise (for several launches, the first one's)."""
+    if L.get("ws") is not None:
+        return f"skinny_colsplit_kernel<{'false' if L['N'] == 2 else 'true'}>"
+    return nm.spmm_variant(L["R"], L["C"], B, L["N"], L["M"])
+
+
 def per_layer_times(torch, nm, layers, dense, B, pool_bytes, launches, ceiling=None, tag=None):
     """Each layer alone: `launches` launches cycling over its own >= pool_bytes rotation, in a
     graph (median of 5 replays), for the sparse product and for the dense one of its shape."""
     lib = nm.lib()
-    sp_fn = lib.nm_spmv if B == 1 else lib.nm_spmm
+    sp_fn = lib.nm_spmv if B == 1 else lib.nm_spmm_ws
     dn_fn = lib.nm_gemv_dense if B == 1 else lib.nm_gemm_dense
     bx = () if B == 1 else (B,)
 
@@ -311,7 +328,7 @@ def per_layer_times(torch, nm, layers, dense, B, pool_bytes, launches, ceiling=N
     for L in layers:
         pool = rotation([L["values"][0], L["masks"][0]], L["bytes"])
         argsets = [(p[0].data_ptr(), p[1].data_ptr(), L["x"].data_ptr(), L["y"].data_ptr(),
-                    L["R"], L["C"]) + bx + (L["N"], L["M"]) for p in pool]
+                    L["R"], L["C"]) + bx + (L["N"], L["M"]) + ws_args(L, B) for p in pool]
         per_s.append(graph_us_per_launch(torch, lambda c, sp, A=argsets: sp_call(*A[c % len(A)], sp), launches))
         del pool
     per_d = {}
@@ -324,8 +341,7 @@ def per_layer_times(torch, nm, layers, dense, B, pool_bytes, launches, ceiling=N
     torch.cuda.synchronize()
     rows = []
     for L, us in zip(layers, per_s):
-        kname = nm.spmv_variant(L["R"], L["C"], L["N"], L["M"]) if B == 1 else \
-            nm.spmm_variant(L["R"], L["C"], B, L["N"], L["M"])
+        kname = nm.spmv_variant(L["R"], L["C"], L["N"], L["M"]) if B == 1 else batch_kernel_name(nm, L, B)
         dus = per_d[(L["R"], L["C"])]
         gbps = L["bytes"] / (us * 1e-6) / 1e9
         rec = {"layer": L["name"], "shape": f"{L['R']}x{L['C']}", "pattern": f"{L['N']}:{L['M']}", "kernel": kname}
@@ -390,8 +406,8 @@ def main():
     wl = synth.WORKLOADS[cfg]
     pats = [tuple(p) for p in wl["patterns"]]
     B = args.batch
-    if not 1 <= B <= 8:
-        print("--batch must be in 1..8", file=sys.stderr)
+    if not 1 <= B <= 31:
+        print("--batch must be in 1..31", file=sys.stderr)
         sys.exit(2)
     if args.patterns:  # any supported patterns, in the order given
         pats = [tuple(int(v) for v in p.split(":")) for p in args.patterns.split(",")]
@@ -428,11 +444,14 @@ def main():
 
     # Raw C-ABI calls with pre-built arguments: the Python binding's checks already ran
     # during packing and warm-up; in the timed regions only the library call remains.
-    bx = () if B == 1 else (B,)   # the batch argument of nm_spmm / nm_gemm_dense
-    sp_fn = lib.nm_spmv if B == 1 else lib.nm_spmm
+    bx = () if B == 1 else (B,)   # the batch argument of nm_spmm_ws / nm_gemm_dense
+    sp_fn = lib.nm_spmv if B == 1 else lib.nm_spmm_ws
     dn_fn = lib.nm_gemv_dense if B == 1 else lib.nm_gemm_dense
+    if B > 1:   # one zeroed workspace per layer (launches are stream-ordered), where it splits
+        for L in layers:
+            L["ws"] = nm.spmm_workspace(L["R"], L["C"], B, L["N"], L["M"], device=dev)
     sp_args = [[(L["values"][c].data_ptr(), L["masks"][c].data_ptr(), L["x"].data_ptr(), L["y"].data_ptr(),
-                 L["R"], L["C"]) + bx + (L["N"], L["M"]) for c in range(P_s)] for L in layers]
+                 L["R"], L["C"]) + bx + (L["N"], L["M"]) + ws_args(L, B) for c in range(P_s)] for L in layers]
     dense_list = list(dense.values())
     dn_args = [[(D["W"][c].data_ptr(), D["x"].data_ptr(), D["y"].data_ptr(), D["R"], D["C"]) + bx
                 for c in range(P_d)] for D in dense_list]
@@ -555,8 +574,8 @@ def main():
 
     # ------------------------------------------------------------------ CPU oracle baseline
     cpu = None
-    if not args.no_cpu_baseline and B == 1:
-        cpu = cpu_baseline(layers, args.cpu_rows_frac)
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(layers, args.cpu_rows_frac, B)
     decode = None
     if extra:
         for L in layers:
@@ -1094,12 +1113,12 @@ def prefill_cpu_baseline(items, T, frac, N=2, M=4):
             "parity_vs_gpu": {"max_err_over_bound": worst, "rel_l2": rel, "ok": worst <= 1.0 and rel <= 1e-3}}
 
 
-def cpu_baseline(layers, frac):
+def cpu_baseline(layers, frac, B=1):
     """Time the oracle (as it is) on the first `frac` of every layer's rows on the host
     cores: the rows are cut into chunks that a pool of threads (one per core) hands to
-    oracle.spmv_ref (numpy releases the interpreter lock inside its array operations), with
-    BLAS held to one thread per call. Also: the same oracle on one thread, and the oracle's
-    y compared with the GPU's for those rows."""
+    oracle.spmv_ref (oracle.spmm_ref for B > 1 vectors; numpy releases the interpreter lock
+    inside its array operations), with BLAS held to one thread per call. Also: the same
+    oracle on one thread, and the oracle's y compared with the GPU's for those rows."""
     import numpy as np
     from concurrent.futures import ThreadPoolExecutor
 
@@ -1133,6 +1152,8 @@ def cpu_baseline(layers, frac):
         li = chunks[i][0]
         L = layers[li]
         rv, rm = packed[i]
+        if B > 1:
+            return oracle.spmm_ref(rv, rm, L["x_host"], L["C"], L["N"], L["M"])
         return oracle.spmv_ref(rv, rm, L["x_host"], L["C"], L["N"], L["M"])
 
     passes = []
@@ -1144,12 +1165,13 @@ def cpu_baseline(layers, frac):
             ys = list(ex.map(run, range(len(chunks))))
             passes.append(time.perf_counter() - t0)
     t_total = statistics.median(passes)
-    b_total = sum(alg_bytes_sparse(b - a, layers[li]["C"], layers[li]["N"], layers[li]["M"]) for li, a, b in chunks)
+    b_total = sum(alg_bytes_sparse(b - a, layers[li]["C"], layers[li]["N"], layers[li]["M"], B)
+                  for li, a, b in chunks)
     rows_total = sum(L["W_cpu"].shape[0] for L in layers)
     worst, rel = 0.0, 0.0
     for li, L in enumerate(layers):
-        y = np.concatenate([ys[i] for i, ch in enumerate(chunks) if ch[0] == li])
-        rep = oracle.y_tolerance_report(L["y"][:y.shape[0]].cpu().numpy(), y)
+        y = np.concatenate([ys[i] for i, ch in enumerate(chunks) if ch[0] == li], axis=-1)
+        rep = oracle.y_tolerance_report(L["y"][..., :y.shape[-1]].cpu().numpy(), y)
         worst = max(worst, rep["max_err_over_bound"])
         rel = max(rel, rep["rel_l2"])
     # the same oracle on one thread, over every 16th chunk
@@ -1159,7 +1181,7 @@ def cpu_baseline(layers, frac):
         t0 = time.perf_counter()
         run(i)
         t1 += time.perf_counter() - t0
-        b1 += alg_bytes_sparse(b - a, layers[li]["C"], layers[li]["N"], layers[li]["M"])
+        b1 += alg_bytes_sparse(b - a, layers[li]["C"], layers[li]["N"], layers[li]["M"], B)
     if blas_one is not None:
         blas_one.restore_original_limits()
     del packed
@@ -1167,7 +1189,8 @@ def cpu_baseline(layers, frac):
         f"{cores} threads, {b1 / t1 / 1e9:.4f} GB/s on 1 thread (leg {time.time() - t_start:.1f}s)")
     return {"value": round(b_total / t_total / 1e9, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{_rows_phrase(frac)} of each of the {len(layers)} layers ({rows_total} rows) in "
-                      f"{len(chunks)} chunks over {cores} threads; densify + fp64 matvec (numpy); median of "
+                      f"{len(chunks)} chunks over {cores} threads; densify + fp64 "
+                      f"{'matvec' if B == 1 else f'product with the {B} vectors'} (numpy); median of "
                       f"{len(passes)} passes ({sum(passes):.1f} s of oracle work)",
             "seconds": round(t_total, 2), "cpu_model": cpu_info(),
             "single_thread": {"value": round(b1 / t1 / 1e9, 5), "unit": "GB/s", "seconds": round(t1, 2),
