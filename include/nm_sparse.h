@@ -141,8 +141,12 @@ int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,
  *   - batch >= 32 with 2:4, 4:8 or 8:16: nm_spmm_prefill (matrix cores), with its limits.
  *   - 5 <= batch < 32 where it was measured faster than the small-batch kernel (2:4 on
  *     layers of at least 256 rows; 4:8 and 8:16 on layers of at least 2048 rows, and on
- *     smaller ones from 9 or 12 vectors; 16:32 from 12 vectors on layers of at least 4096
- *     rows and at most 4096 columns): nm_spmm_skinny.
+ *     smaller ones from 9 or 12 vectors): nm_spmm_skinny.
+ *   - 16:32 from 5 vectors (any batch: it has no prefill kernel), per launch of up to 16
+ *     vectors: nm_spmm_skinny's expansion kernel for a launch of at least 14 vectors on
+ *     layers of at least 2048 rows (4096 if wider than 4096 columns), or of at least 12 on
+ *     layers of at least 4096 rows and at most 4096 columns; the small-batch kernel for the
+ *     other launches (e.g. 24 vectors: one launch of 16 expanded, 8 on the small-batch one).
  *   - otherwise the small-batch kernel (vector units; x staged in LDS in column phases
  *     when it does not fit at once, so any width is accepted), on consecutive groups of
  *     8 rows of X (one launch per group). batch == 1 gives the same result as nm_spmv

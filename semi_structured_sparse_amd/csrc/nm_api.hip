@@ -100,6 +100,27 @@ int spmm_dispatch(const uint16_t* values, const uint32_t* masks, const uint16_t*
   hipError_t e = current_device_info(&dev);
   if (e != hipSuccess) return hip_fail(e);
   if (M != 2 * N && cols > max_cols_for(dev)) return NM_ERR_TOO_WIDE;  // 25%: single-vector kernel only
+  if (N == 16 && M == 32 && batch >= kSkinnyMinBatch) {
+    // 16:32 from 5 vectors, any batch (it has no prefill kernel): each launch of up to 16
+    // vectors on the expansion kernel where that measured faster, else on the small-batch
+    // kernel 8 vectors at a time
+    for (int64_t b0 = 0; b0 < batch; b0 += kSkinnyBatch) {
+      const int64_t nb = batch - b0 < kSkinnyBatch ? batch - b0 : kSkinnyBatch;
+      if (skinny_expand_chunk(rows, cols, nb, dev)) {
+        e = launch_skinny_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, int(nb), N, M,
+                               static_cast<hipStream_t>(stream), dev);
+        if (e != hipSuccess) return hip_fail(e);
+        continue;
+      }
+      for (int64_t c0 = b0; c0 < b0 + nb; c0 += kSmallBatch) {
+        const int nc = int(b0 + nb - c0 < kSmallBatch ? b0 + nb - c0 : kSmallBatch);
+        e = launch_spmm(values, masks, X + c0 * cols, Y + c0 * rows, rows, cols, nc, N, M,
+                        static_cast<hipStream_t>(stream), dev);
+        if (e != hipSuccess) return hip_fail(e);
+      }
+    }
+    return NM_OK;
+  }
   if (use_skinny(rows, cols, batch, N, M, dev)) {
     // 50% patterns at 5..31 vectors where measured faster: the matrix instructions, 16
     // vectors per launch (launches in stream order, so one workspace serves them all)
@@ -317,6 +338,9 @@ const char* nm_spmm_variant(int64_t rows, int64_t cols, int64_t batch, int N, in
   if (batch == 1 && cols <= nm::max_cols_for(dev)) return nm::spmv_variant(rows, cols, N, M, dev);
   if (nm::prefill_pattern(N, M) && batch >= nm::kMatrixCoreMinBatch)
     return nm::prefill_fits(rows, cols, batch) ? nm::prefill_variant(rows, batch, true, dev, N != 2) : "";
+  if (N == 16 && batch >= nm::kSkinnyMinBatch &&
+      nm::skinny_expand_chunk(rows, cols, batch < nm::kSkinnyBatch ? batch : nm::kSkinnyBatch, dev))
+    return nm::skinny_variant(N);
   if (nm::use_skinny(rows, cols, batch, N, M, dev)) return nm::skinny_variant(N);
   return nm::spmm_variant(rows, cols, N, batch < nm::kSmallBatch ? batch : nm::kSmallBatch, dev);
 }

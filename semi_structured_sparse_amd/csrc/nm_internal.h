@@ -130,7 +130,13 @@ constexpr int64_t kSkinnyBatch = 16;
 constexpr int64_t kSkinnyExpandMinBatch = 12;
 constexpr int64_t kSkinnyExpandMinRows = 4096;
 constexpr int64_t kSkinnyExpandMaxCols = 4096;
+constexpr int64_t kSkinnyExpandFullChunk = 14;     // vectors of a nearly full 16-vector launch
+constexpr int64_t kSkinnyExpandFullMinRows = 2048;
 bool use_skinny(int64_t rows, int64_t cols, int64_t batch, int n, int m, const DeviceInfo& dev);
+// 16:32 is routed per launch of up to kSkinnyBatch vectors: a launch of `tokens` vectors
+// takes the expansion kernel where that measured faster than the small-batch kernel (whose
+// time grows with every 8 vectors while the expansion kernel's hardly does).
+bool skinny_expand_chunk(int64_t rows, int64_t cols, int64_t tokens, const DeviceInfo& dev);
 const char* skinny_variant(int n);
 
 // nm_spmm's argument checks (host only, no HIP call): NM_OK or the status to return.

@@ -91,9 +91,24 @@ bool use_skinny(int64_t rows, int64_t cols, int64_t batch, int n, int m, const D
   if (batch < kSkinnyMinBatch || batch >= kMatrixCoreMinBatch)   // beyond: the prefill kernels
     return false;
   if (rows < kSkinnySmallMinRows || !skinny_fits(rows, cols, kSkinnyBatch, n, m, dev)) return false;
-  if (n == 16) return batch >= kSkinnyExpandMinBatch && rows >= kSkinnyExpandMinRows && cols <= kSkinnyExpandMaxCols;
+  if (n == 16) return false;   // routed per launch (skinny_expand_chunk)
   if (rows >= kSkinnyMinRows || n == 2) return true;
   return batch >= 12 || (batch >= 9 && cols <= 5120);   // the split patterns on smaller layers
+}
+
+// From a sweep at 12..31 vectors on MI355X (16:32, µs per product): a launch of 14..16
+// vectors takes about as long as one of 12, and as one of 5, while the small-batch kernel pays
+// per 8 vectors: at 16 vectors 4096 x 14336 runs in 42.4 against 53.3 µs, 4096 x 8192 24.9
+// against 32.8, 8192 x 8192 38.2 against 48.7, 2048 x 4096 14.7 against 15.9; at 12 vectors
+// the expansion wins only with X in one phase (<= 4096 columns) on >= 4096 rows (4096 x 4096:
+// 15.4 against 18.9), and on 1024-row layers, or 2048 rows of more than 4096 columns, it
+// loses or ties at every count.
+bool skinny_expand_chunk(int64_t rows, int64_t cols, int64_t tokens, const DeviceInfo& dev) {
+  if (rows < kSkinnySmallMinRows || !skinny_fits(rows, cols, kSkinnyBatch, 16, 32, dev)) return false;
+  if (tokens >= kSkinnyExpandFullChunk && rows >= kSkinnyExpandFullMinRows &&
+      (rows >= kSkinnyExpandMinRows || cols <= kSkinnyExpandMaxCols))
+    return true;
+  return tokens >= kSkinnyExpandMinBatch && rows >= kSkinnyExpandMinRows && cols <= kSkinnyExpandMaxCols;
 }
 
 const char* skinny_variant(int n) {

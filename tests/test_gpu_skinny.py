@@ -3,7 +3,9 @@ C ABI, against the CPU oracle (spmm_ref): nm_spmm_skinny for every 50% pattern (
 4:8 and 8:16 split into two 2:4 operands; 16:32 expanded to dense fragments) on ragged
 shapes, and nm_spmm where its routing picks them (5..31 vectors: 2:4 on layers of at least
 256 rows; 4:8 and 8:16 on layers of at least 2048 rows, and on smaller ones from 9 or 12
-vectors; 16:32 from 12 vectors on layers of >= 4096 rows and <= 4096 columns).
+vectors; 16:32 per launch of up to 16 vectors, from 14 vectors on layers of >= 2048 rows
+(>= 4096 rows if wider than 4096 columns) and from 12 on >= 4096 rows of <= 4096 columns,
+the small-batch kernel for the other launches).
 
 Bars: Y within |y - ref| <= 2e-3 + 1e-2*|ref| per element and relative L2 <= 1e-3 (fp32
 accumulation in the matrix instruction, fp16 output, fp64 oracle); exact special cases
@@ -53,8 +55,11 @@ def test_skinny_parity(R, C, T, N, M):
 
 
 # nm_spmm's routing to the skinny kernels, 16:32 included (ragged rows, two launches)
+# (16:32 at 20 and 24 vectors: an expansion launch of 16, then the small-batch kernel for the
+# rest; 31 on 2050 rows: two expansion launches, 16 and 15)
 ROUTED_CASES = [((2, 4), 4100, 1024, 11), ((8, 16), 2100, 4064, 16), ((16, 32), 4096, 4096, 12),
-                ((16, 32), 4100, 4064, 16), ((16, 32), 14336, 4096, 20)]
+                ((16, 32), 4100, 4064, 16), ((16, 32), 14336, 4096, 20), ((16, 32), 4096, 14336, 24),
+                ((16, 32), 2050, 4096, 31), ((16, 32), 4100, 8192, 40)]
 
 
 @pytest.mark.parametrize("pat,R,C,T", ROUTED_CASES)
@@ -90,9 +95,11 @@ def test_skinny_split_two_launches(N, M):
 def test_skinny_routing():
     """Which kernel nm_spmm picks: the sparse matrix instruction at 5..31 vectors for 2:4 on
     layers of >= 256 rows and for 4:8 and 8:16 on layers of >= 2048 rows (on smaller ones from
-    9 vectors up to 5120 columns, else from 12), and for 16:32 from 12 vectors on layers of
-    >= 4096 rows and <= 4096 columns; the small-batch kernel below 5 vectors, on smaller
-    layers and for other 16:32 shapes; the prefill kernels from 32 vectors on."""
+    9 vectors up to 5120 columns, else from 12); for 16:32, per launch of up to 16 vectors,
+    the expansion kernel from 14 vectors on >= 2048 rows (>= 4096 if wider than 4096
+    columns) and from 12 on >= 4096 rows of <= 4096 columns; the small-batch kernel below 5
+    vectors, on smaller layers and for the other 16:32 launches; the prefill kernels from 32
+    vectors on (16:32, which has none, keeps its per-launch routing at any batch)."""
     assert nm.spmm_variant(4096, 4096, 4, 2, 4) == "spmm_kernel<2, 4, 2>"
     assert nm.spmm_variant(2047, 4096, 8, 2, 4) == SKINNY[2]
     assert nm.spmm_variant(1024, 4096, 5, 2, 4) == SKINNY[2]
@@ -106,8 +113,14 @@ def test_skinny_routing():
     assert nm.spmm_variant(4096, 4096, 12, 16, 32) == SKINNY[16]
     assert nm.spmm_variant(14336, 4096, 31, 16, 32) == SKINNY[16]
     assert nm.spmm_variant(4096, 4096, 11, 16, 32) == "spmm_kernel<16, 8, 0>"
-    assert nm.spmm_variant(4095, 4096, 16, 16, 32) == "spmm_kernel<16, 8, 0>"
-    assert nm.spmm_variant(4096, 4128, 16, 16, 32) == "spmm_kernel<16, 8, 0>"
+    assert nm.spmm_variant(4095, 4096, 16, 16, 32) == SKINNY[16]
+    assert nm.spmm_variant(4095, 4096, 13, 16, 32) == "spmm_kernel<16, 8, 0>"
+    assert nm.spmm_variant(4096, 4128, 16, 16, 32) == SKINNY[16]
+    assert nm.spmm_variant(4096, 14336, 12, 16, 32) == "spmm_kernel<16, 8, 0>"
+    assert nm.spmm_variant(4096, 14336, 14, 16, 32) == SKINNY[16]
+    assert nm.spmm_variant(2048, 4096, 15, 16, 32) == SKINNY[16]
+    assert nm.spmm_variant(2048, 8192, 16, 16, 32) == "spmm_kernel<16, 8, 0>"
+    assert nm.spmm_variant(2047, 4096, 16, 16, 32) == "spmm_kernel<16, 8, 0>"
     assert nm.spmm_variant(1024, 4096, 16, 16, 32) == "spmm_kernel<16, 8, 0>"
     assert nm.spmm_variant(4096, 4096, 5, 16, 32) == "spmm_kernel<16, 5, 0>"
     assert nm.spmm_variant(4096, 4096, 4, 8, 16) == "spmm_kernel<8, 4, 2>"
@@ -116,7 +129,7 @@ def test_skinny_routing():
         assert nm.spmm_variant(4096, 4096, 31, N, M) == SKINNY[N]
     assert nm.spmm_variant(4096, 4096, 32, 4, 8).startswith("prefill_split_kernel")
     assert nm.spmm_variant(4096, 4096, 2048, 8, 16) == "prefill_split_kernel<4, 8, 64, 2>"
-    assert nm.spmm_variant(4096, 4096, 40, 16, 32) == "spmm_kernel<16, 8, 0>"
+    assert nm.spmm_variant(4096, 4096, 40, 16, 32) == SKINNY[16]
     assert nm.spmm_variant(4096, 4096, 32, 2, 4).startswith("prefill_spmm_kernel")
     assert nm.spmm_variant(4096, 4096, 1, 2, 4).startswith("spmv_kernel")
 
