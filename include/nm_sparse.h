@@ -141,7 +141,9 @@ int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,
  *   - batch >= 32 with 2:4, 4:8 or 8:16: nm_spmm_prefill (matrix cores), with its limits.
  *   - 5 <= batch < 32 where it was measured faster than the small-batch kernel (2:4 on
  *     layers of at least 256 rows; 4:8 and 8:16 on layers of at least 2048 rows, and on
- *     smaller ones from 9 or 12 vectors): nm_spmm_skinny.
+ *     smaller ones from 9 or 12 vectors): nm_spmm_skinny, 16 vectors per launch, each
+ *     launch routed by the same rule at its own count (17..20 vectors: the last 1..4 on
+ *     the small-batch kernel).
  *   - 16:32 from 5 vectors (any batch: it has no prefill kernel), per launch of up to 16
  *     vectors: nm_spmm_skinny's expansion kernel for a launch of at least 14 vectors on
  *     layers of at least 2048 rows (4096 if wider than 4096 columns), or of at least 12 on

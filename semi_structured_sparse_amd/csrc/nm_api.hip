@@ -121,13 +121,22 @@ int spmm_dispatch(const uint16_t* values, const uint32_t* masks, const uint16_t*
     }
     return NM_OK;
   }
-  if (use_skinny(rows, cols, batch, N, M, dev)) {
+  if (use_skinny(rows, cols, batch < kSkinnyBatch ? batch : kSkinnyBatch, N, M, dev)) {
     // 50% patterns at 5..31 vectors where measured faster: the matrix instructions, 16
-    // vectors per launch (launches in stream order, so one workspace serves them all)
+    // vectors per launch (launches in stream order, so one workspace serves them all); a
+    // last launch too small for them (17..20 vectors leave 1..4) runs on the small-batch kernel
     for (int64_t b0 = 0; b0 < batch; b0 += kSkinnyBatch) {
       const int nb = int(batch - b0 < kSkinnyBatch ? batch - b0 : kSkinnyBatch);
-      e = launch_skinny_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb, N, M,
-                             static_cast<hipStream_t>(stream), dev, workspace, workspace_bytes);
+      if (use_skinny(rows, cols, nb, N, M, dev)) {
+        e = launch_skinny_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb, N, M,
+                               static_cast<hipStream_t>(stream), dev, workspace, workspace_bytes);
+      } else {
+        e = launch_spmm(values, masks, X + b0 * cols, Y + b0 * rows, rows, cols, nb < kSmallBatch ? nb : int(kSmallBatch),
+                        N, M, static_cast<hipStream_t>(stream), dev);
+        if (e == hipSuccess && nb > kSmallBatch)
+          e = launch_spmm(values, masks, X + (b0 + kSmallBatch) * cols, Y + (b0 + kSmallBatch) * rows, rows, cols,
+                          int(nb - kSmallBatch), N, M, static_cast<hipStream_t>(stream), dev);
+      }
       if (e != hipSuccess) return hip_fail(e);
     }
     return NM_OK;
@@ -146,7 +155,8 @@ int spmm_dispatch(const uint16_t* values, const uint32_t* masks, const uint16_t*
 // Workspace bytes spmm_dispatch can use for the product (0 when it would not use one).
 size_t spmm_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev) {
   if (!valid_shape(rows, cols) || !valid_pattern(N, M) || batch < 1 || batch > kPrefillMaxTokens) return 0;
-  if (batch >= kMatrixCoreMinBatch || !use_skinny(rows, cols, batch, N, M, dev)) return 0;
+  if (batch >= kMatrixCoreMinBatch || !use_skinny(rows, cols, batch < kSkinnyBatch ? batch : kSkinnyBatch, N, M, dev))
+    return 0;
   return skinny_workspace_bytes(rows, cols, int(batch < kSkinnyBatch ? batch : kSkinnyBatch), N, dev);
 }
 }  // namespace nm
@@ -341,7 +351,8 @@ const char* nm_spmm_variant(int64_t rows, int64_t cols, int64_t batch, int N, in
   if (N == 16 && batch >= nm::kSkinnyMinBatch &&
       nm::skinny_expand_chunk(rows, cols, batch < nm::kSkinnyBatch ? batch : nm::kSkinnyBatch, dev))
     return nm::skinny_variant(N);
-  if (nm::use_skinny(rows, cols, batch, N, M, dev)) return nm::skinny_variant(N);
+  if (nm::use_skinny(rows, cols, batch < nm::kSkinnyBatch ? batch : nm::kSkinnyBatch, N, M, dev))
+    return nm::skinny_variant(N);
   return nm::spmm_variant(rows, cols, N, batch < nm::kSmallBatch ? batch : nm::kSmallBatch, dev);
 }
 

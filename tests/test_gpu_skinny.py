@@ -85,7 +85,8 @@ def test_skinny_small_layers(pat, R, C, T):
 
 @pytest.mark.parametrize("N,M", [(4, 8), (8, 16)])
 def test_skinny_split_two_launches(N, M):
-    """4:8 and 8:16 at 20 vectors: two launches of the split kernel (16, then a ragged 4)."""
+    """4:8 and 8:16 at 20 vectors: a launch of 16 on the split kernel, then the last 4 on the
+    small-batch kernel (a launch too small for the matrix instructions)."""
     R, C, T = 2064, 1024, 20
     assert nm.spmm_variant(R, C, T, N, M) == SKINNY[N]
     say(f"skinny {N}:{M} {R}x{C} vectors={T}")
@@ -174,8 +175,8 @@ def test_skinny_malformed_masks_stay_in_bounds(N, M):
 # vectors; the split patterns from 9 vectors), each on a range of whole lines, the last to
 # arrive summing the partial tiles. Ragged rows; a ragged last split (8224 columns = 64.25
 # lines over 8 splits, 2080 = 16.25 over 4); several X phases inside one split (16 vectors x
-# 14336 columns); two launches on one workspace, both split (17, 31 vectors) or the second not
-# (1024 x 5120 at 20 vectors: 16 split, then 4 unsplit).
+# 14336 columns); two launches on one workspace, both split (31 vectors), or the second on
+# the small-batch kernel (17 and 20 vectors: the last 1 or 4).
 SPLIT_CASES = [((2, 4), 1024, 8192, 8), ((2, 4), 512, 8192, 5), ((2, 4), 1000, 8192, 17), ((2, 4), 300, 8224, 6),
                ((2, 4), 2048, 14336, 16), ((4, 8), 1024, 4096, 9), ((8, 16), 1030, 8192, 16),
                ((8, 16), 512, 8192, 12), ((4, 8), 777, 2080, 31), ((2, 4), 256, 5120, 31), ((2, 4), 1024, 5120, 20)]
