@@ -138,7 +138,10 @@ int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,
  *   Y[b][r] = fp16( sum_c W'[r][c] * X[b][c] ),  X fp16 [batch][cols], Y fp16 [batch][rows]
  * (row b of X is one activation vector: the layout of a batch of tokens). Products and
  * sums fp32, one RNE rounding, fixed summation order (bit-identical run to run).
- *   - batch >= 32 with 2:4, 4:8 or 8:16: nm_spmm_prefill (matrix cores), with its limits.
+ *   - batch >= 32 with 2:4, 4:8 or 8:16: nm_spmm_prefill (matrix cores), with its limits,
+ *     except 32..48 vectors on layers of at most 4096 rows and 32 on layers of at most
+ *     8192 rows where nm_spmm_skinny takes the layer (next item): there 16-vector
+ *     launches measured faster than the prefill kernel.
  *   - 5 <= batch < 32 where it was measured faster than the small-batch kernel (2:4 on
  *     layers of at least 256 rows; 4:8 and 8:16 on layers of at least 2048 rows, and on
  *     smaller ones from 9 or 12 vectors): nm_spmm_skinny, 16 vectors per launch, each

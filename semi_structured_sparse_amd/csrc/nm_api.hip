@@ -78,6 +78,21 @@ hipError_t launch(const void* kernel, dim3 grid, dim3 block, void** args, size_t
   return hipLaunchKernel(kernel, grid, block, args, lds, stream);
 }
 
+// The prefill kernels take the 50% patterns they cover from kMatrixCoreMinBatch vectors,
+// except where 16-vector launches of the skinny kernels measured faster: the prefill kernels
+// cost a fixed time per 64-column step on a grid of few workgroups, nearly the same from
+// 32 to 128 vectors, while the skinny launches add up per 16. Measured on MI355X (2:4, µs at
+// 32 / 48 / 64 vectors, skinny against prefill): 4096 x 4096 16.7 / 23.9 / 30.9 against
+// 26.3; 4096 x 14336 44.6 / 65.0 / 84.8 against 82; 8192 x 8192 40.4 / 59.7 against 51;
+// 14336 x 4096 32.7 against 27.9 already at 32. So: up to 48 vectors on layers of at most
+// 4096 rows, up to 32 on layers of at most 8192, where the skinny kernels take the layer.
+bool prefill_route(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev) {
+  if (batch < kMatrixCoreMinBatch || !prefill_pattern(N, M)) return false;
+  const bool short_batch = (batch <= kSkinnyBeforePrefillMaxBatch && rows <= kSkinnyBeforePrefillMaxRows) ||
+                           (batch <= kMatrixCoreMinBatch && rows <= 2 * kSkinnyBeforePrefillMaxRows);
+  return !(short_batch && use_skinny(rows, cols, kSkinnyBatch, N, M, dev));
+}
+
 // nm_spmm's argument checks, before any HIP call.
 int spmm_check(const uint16_t* values, const uint32_t* masks, const uint16_t* X, const uint16_t* Y, int64_t rows,
                int64_t cols, int64_t batch, int N, int M) {
@@ -85,6 +100,9 @@ int spmm_check(const uint16_t* values, const uint32_t* masks, const uint16_t* X,
   if (!valid_shape(rows, cols) || batch < 1 || batch > kPrefillMaxTokens) return NM_ERR_SHAPE;
   if (!valid_pattern(N, M) || (batch > 1 && M != 2 * N)) return NM_ERR_PATTERN;
   if (!aligned(values, 16) || !aligned(masks, 4) || !aligned(X, 16) || !aligned(Y, 2)) return NM_ERR_ALIGN;
+  // beyond 2^21 columns no skinny launch fits, so such batches go to the prefill kernels,
+  // whose limit this is
+  if (batch >= kMatrixCoreMinBatch && prefill_pattern(N, M) && cols > kPrefillMaxCols) return NM_ERR_SHAPE;
   return NM_OK;
 }
 
@@ -94,11 +112,11 @@ int spmm_dispatch(const uint16_t* values, const uint32_t* masks, const uint16_t*
   const int st = spmm_check(values, masks, X, Y, rows, cols, batch, N, M);
   if (st != NM_OK) return st;
   if (!aligned(workspace, 16)) return NM_ERR_ALIGN;
-  if (batch >= kMatrixCoreMinBatch && prefill_pattern(N, M))  // matrix-core product
-    return nm_spmm_prefill(values, masks, X, Y, rows, cols, batch, N, M, stream);
   DeviceInfo dev;
   hipError_t e = current_device_info(&dev);
   if (e != hipSuccess) return hip_fail(e);
+  if (prefill_route(rows, cols, batch, N, M, dev))  // matrix-core prefill product
+    return nm_spmm_prefill(values, masks, X, Y, rows, cols, batch, N, M, stream);
   if (M != 2 * N && cols > max_cols_for(dev)) return NM_ERR_TOO_WIDE;  // 25%: single-vector kernel only
   if (N == 16 && M == 32 && batch >= kSkinnyMinBatch) {
     // 16:32 from 5 vectors, any batch (it has no prefill kernel): each launch of up to 16
@@ -155,7 +173,8 @@ int spmm_dispatch(const uint16_t* values, const uint32_t* masks, const uint16_t*
 // Workspace bytes spmm_dispatch can use for the product (0 when it would not use one).
 size_t spmm_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev) {
   if (!valid_shape(rows, cols) || !valid_pattern(N, M) || batch < 1 || batch > kPrefillMaxTokens) return 0;
-  if (batch >= kMatrixCoreMinBatch || !use_skinny(rows, cols, batch < kSkinnyBatch ? batch : kSkinnyBatch, N, M, dev))
+  if (prefill_route(rows, cols, batch, N, M, dev) ||
+      !use_skinny(rows, cols, batch < kSkinnyBatch ? batch : kSkinnyBatch, N, M, dev))
     return 0;
   return skinny_workspace_bytes(rows, cols, int(batch < kSkinnyBatch ? batch : kSkinnyBatch), N, dev);
 }
@@ -346,7 +365,7 @@ const char* nm_spmm_variant(int64_t rows, int64_t cols, int64_t batch, int N, in
   nm::DeviceInfo dev;
   if (nm::current_device_info(&dev) != hipSuccess) return "";
   if (batch == 1 && cols <= nm::max_cols_for(dev)) return nm::spmv_variant(rows, cols, N, M, dev);
-  if (nm::prefill_pattern(N, M) && batch >= nm::kMatrixCoreMinBatch)
+  if (nm::prefill_route(rows, cols, batch, N, M, dev))
     return nm::prefill_fits(rows, cols, batch) ? nm::prefill_variant(rows, batch, true, dev, N != 2) : "";
   if (N == 16 && batch >= nm::kSkinnyMinBatch &&
       nm::skinny_expand_chunk(rows, cols, batch < nm::kSkinnyBatch ? batch : nm::kSkinnyBatch, dev))

@@ -131,6 +131,10 @@ constexpr int64_t kSkinnyExpandMinBatch = 12;
 constexpr int64_t kSkinnyExpandMinRows = 4096;
 constexpr int64_t kSkinnyExpandMaxCols = 4096;
 constexpr int64_t kSkinnyExpandFullChunk = 14;     // vectors of a nearly full 16-vector launch
+// Batches of 32 .. kSkinnyBeforePrefillMaxBatch vectors stay on skinny launches on layers of
+// at most kSkinnyBeforePrefillMaxRows rows (32 vectors up to twice that), see prefill_route.
+constexpr int64_t kSkinnyBeforePrefillMaxBatch = 48;
+constexpr int64_t kSkinnyBeforePrefillMaxRows = 4096;
 constexpr int64_t kSkinnyExpandFullMinRows = 2048;
 bool use_skinny(int64_t rows, int64_t cols, int64_t batch, int n, int m, const DeviceInfo& dev);
 // 16:32 is routed per launch of up to kSkinnyBatch vectors: a launch of `tokens` vectors
@@ -147,6 +151,9 @@ int spmm_check(const uint16_t* values, const uint32_t* masks, const uint16_t* X,
 int spmm_dispatch(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y, int64_t rows,
                   int64_t cols, int64_t batch, int N, int M, void* stream, void* workspace, size_t workspace_bytes);
 size_t spmm_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev);
+
+// Whether nm_spmm runs a batch on the prefill kernels (else on skinny or small-batch launches).
+bool prefill_route(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev);
 
 // Name of the kernel configuration the prefill launchers pick (static string).
 const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev, bool split = false);

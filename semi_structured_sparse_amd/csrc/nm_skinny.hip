@@ -88,7 +88,7 @@ bool skinny_fits(int64_t rows, int64_t cols, int64_t tokens, int n, int m, const
 }
 
 bool use_skinny(int64_t rows, int64_t cols, int64_t batch, int n, int m, const DeviceInfo& dev) {
-  if (batch < kSkinnyMinBatch || batch >= kMatrixCoreMinBatch)   // beyond: the prefill kernels
+  if (batch < kSkinnyMinBatch || batch > kSkinnyBatch)   // per launch of at most 16 vectors
     return false;
   if (rows < kSkinnySmallMinRows || !skinny_fits(rows, cols, kSkinnyBatch, n, m, dev)) return false;
   if (n == 16) return false;   // routed per launch (skinny_expand_chunk)

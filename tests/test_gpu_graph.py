@@ -85,8 +85,8 @@ def test_gemv_dense_graph_replays():
 
 # batch products: the small-batch kernel (B = 4), the skinny kernel (2:4 at B = 8) and its
 # split variant (4:8 at B = 8; 8:16 at B = 20: 16 on it, the last 4 on the small-batch kernel),
-# the prefill kernel (B = 40)
-BATCH_CASES = [(2, 4, 4), (2, 4, 8), (4, 8, 8), (8, 16, 20), (16, 32, 6), (2, 4, 40)]
+# three skinny launches (2:4 at B = 40) and the prefill kernel (B = 64)
+BATCH_CASES = [(2, 4, 4), (2, 4, 8), (4, 8, 8), (8, 16, 20), (16, 32, 6), (2, 4, 40), (2, 4, 64)]
 
 
 @pytest.mark.parametrize("N,M,B", BATCH_CASES)

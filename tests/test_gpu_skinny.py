@@ -128,10 +128,19 @@ def test_skinny_routing():
     for N, M in PATTERNS[:3]:
         assert nm.spmm_variant(4096, 4096, 5, N, M) == SKINNY[N]
         assert nm.spmm_variant(4096, 4096, 31, N, M) == SKINNY[N]
-    assert nm.spmm_variant(4096, 4096, 32, 4, 8).startswith("prefill_split_kernel")
+    # 32..48 vectors stay on 16-vector launches on <= 4096 rows (32 on <= 8192 rows), where
+    # the skinny kernels take the layer; the prefill kernels beyond
+    assert nm.spmm_variant(4096, 4096, 32, 4, 8) == SKINNY[4]
+    assert nm.spmm_variant(4096, 14336, 48, 2, 4) == SKINNY[2]
+    assert nm.spmm_variant(4096, 4096, 49, 2, 4).startswith("prefill_spmm_kernel")
+    assert nm.spmm_variant(8192, 8192, 32, 2, 4) == SKINNY[2]
+    assert nm.spmm_variant(8192, 8192, 33, 2, 4).startswith("prefill_spmm_kernel")
+    assert nm.spmm_variant(14336, 4096, 32, 2, 4).startswith("prefill_spmm_kernel")
+    assert nm.spmm_variant(4096, 4096, 64, 4, 8).startswith("prefill_split_kernel")
+    assert nm.spmm_variant(200, 1024, 40, 2, 4).startswith("prefill_spmm_kernel")   # no skinny below 256 rows
     assert nm.spmm_variant(4096, 4096, 2048, 8, 16) == "prefill_split_kernel<4, 8, 64, 2>"
     assert nm.spmm_variant(4096, 4096, 40, 16, 32) == SKINNY[16]
-    assert nm.spmm_variant(4096, 4096, 32, 2, 4).startswith("prefill_spmm_kernel")
+    assert nm.spmm_variant(4096, 4096, 64, 2, 4).startswith("prefill_spmm_kernel")
     assert nm.spmm_variant(4096, 4096, 1, 2, 4).startswith("spmv_kernel")
 
 
@@ -227,7 +236,7 @@ def test_skinny_column_split_small_workspace_runs_unsplit():
     assert nm.spmm_workspace_bytes(4096, 4096, 16, 16, 32) == 0
     assert nm.spmm_workspace_bytes(1024, 8192, 4, 2, 4) == 0
     assert nm.spmm_workspace_bytes(4096, 8192, 8, 2, 4) == 0
-    assert nm.spmm_workspace_bytes(1024, 8192, 40, 2, 4) == 0
+    assert nm.spmm_workspace_bytes(1024, 8192, 64, 2, 4) == 0
     assert nm.spmm_workspace_bytes(1024, 4096, 16, 2, 4) == 0
     assert nm.spmm_workspace_bytes(2048, 4096, 16, 4, 8) == 0
     assert nm.spmm_workspace_bytes(1024, 5120, 5, 2, 4) == 0
@@ -257,16 +266,19 @@ def test_skinny_column_split_shared_workspace():
 
 
 # boundaries of the column split: 128 tiles (half the CUs of a 256-CU part: 2 splits) against
-# 129 (none); batch 5 (first skinny size), 31 (last, two launches) and 32 (prefill route, no
-# workspace); a workspace of exactly nm_spmm_workspace_bytes
+# 129 (none); batch 5 (first skinny size), 31 and 48 (two and three split launches on a
+# 1024-row layer) and 49 (prefill route, no workspace); a workspace of exactly
+# nm_spmm_workspace_bytes
 @pytest.mark.parametrize("R,C,T,N,M", [(2048, 8192, 5, 2, 4), (2064, 8192, 8, 2, 4), (2048, 8192, 31, 8, 16),
-                                       (1024, 8192, 32, 2, 4), (1040, 14336, 16, 2, 4)])
+                                       (1024, 8192, 48, 2, 4), (1024, 8192, 49, 2, 4), (1040, 14336, 16, 2, 4)])
 def test_skinny_column_split_boundaries(R, C, T, N, M):
     need = nm.spmm_workspace_bytes(R, C, T, N, M)
     cus = torch.cuda.get_device_properties(device()).multi_processor_count
     tiles = -(-R // 16)
-    if T >= 32 or 2 * tiles > cus:
+    if T > 48 or 2 * tiles > cus:
         assert need == 0, (R, C, T, need)
+    else:
+        assert need > 0, (R, C, T)
     ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=device())[:need] if need else None
     say(f"skinny split boundary {N}:{M} {R}x{C} vectors={T} workspace={need}")
     W = synth.weight(R, C, 3800 + R % 97 + T)
