@@ -299,10 +299,10 @@ def ws_args(L, B):
 
 
 def batch_kernel_name(nm, L, B):
-    """Kernel of nm_spmm_ws for layer L: the column-split kernel where it has a workspace,
+    """Kernel of nm_spmm_ws for layer L: a column-split kernel where it has a workspace,
     nm_spmm's kernel otherwise (for several launches, the first one's)."""
     if L.get("ws") is not None:
-        return f"skinny_colsplit_kernel<{'false' if L['N'] == 2 else 'true'}>"
+        return nm.spmm_ws_variant(L["R"], L["C"], B, L["N"], L["M"])
     return nm.spmm_variant(L["R"], L["C"], B, L["N"], L["M"])
 
 

@@ -162,41 +162,49 @@ int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,
 int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
             int64_t rows, int64_t cols, int64_t batch, int N, int M, void* stream);
 
-/* nm_spmm with a caller-owned workspace. The same Y definition and routing as nm_spmm; where
- * nm_spmm_workspace_bytes(...) for the same arguments is > 0 (50% patterns on the matrix
- * instructions, layers too short to fill the GPU: e.g. 1024 rows at 5..31 vectors) and
- * workspace_bytes is at least that, the columns of each 16-row tile go to 2, 4 or 8
- * workgroups whose fp32 partial tiles the last-arriving one sums in split order (fixed, so
- * bit-identical run to run, but not bit-identical to nm_spmm's unsplit order: the same
+/* nm_spmm with a caller-owned workspace. The same Y definition as nm_spmm. Where
+ * nm_spmm_workspace_bytes(...) for the same arguments is > 0 and workspace_bytes is at least
+ * that, work that would leave most CUs idle is split over more workgroups:
+ *   - skinny launches (50% patterns at 5..16 vectors per launch, nm_spmm's route) on layers
+ *     too short to fill the GPU (e.g. 1024 rows): the columns of each 16-row tile go to 2, 4
+ *     or 8 workgroups;
+ *   - 2:4, 4:8 and 8:16 batches of more than 16 vectors whose output tiles of 64 rows x 32
+ *     (up to 32 vectors) or 64 vectors are too few to fill the GPU (mid-size batches: e.g.
+ *     up to 256 tokens on 4096 x 4096): instead of nm_spmm's route, one launch of the
+ *     prefill kernel with each tile's columns split over 2 .. 8 workgroups, whole blocks of
+ *     512 columns each ([NEWS-NEW]: batched tokens run matrix-matrix products).
+ * In both the last-arriving workgroup of a tile sums the fp32 partial tiles in split order
+ * (fixed, so bit-identical run to run, but not bit-identical to nm_spmm's order: the same
  * tolerance against the exact product). workspace: device memory, 16-byte aligned, owned by
  * the caller; its first 4 * CU-count bytes, rounded up to 256 (1 KiB on MI355X), are
  * counters that must be zero before the first call on it (e.g. one hipMemset when
  * allocated); every call leaves them zero again, so one workspace serves any sequence of
- * shapes on the device. NULL or a smaller workspace runs the unsplit kernels (no error). Calls that use
- * one workspace must be ordered (one stream): overlapping calls on it race. Other arguments
- * and errors as nm_spmm; a misaligned workspace is NM_ERR_ALIGN. */
+ * shapes on the device. NULL or a smaller workspace runs nm_spmm's kernels (no error). Calls
+ * that use one workspace must be ordered (one stream): overlapping calls on it race. Other
+ * arguments and errors as nm_spmm; a misaligned workspace is NM_ERR_ALIGN. */
 int nm_spmm_ws(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
                int64_t rows, int64_t cols, int64_t batch, int N, int M, void* workspace,
                size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace nm_spmm_ws can use for these arguments on the current device; 0 when
- * the shape takes no column split (or the arguments are invalid, or no device): the
- * counters, then tiles * splits KiB (tiles = ceil(rows / 16), splits <= 8, tiles * splits <=
- * CU count; at most 257 KiB on MI355X). */
+ * the shape takes no split (or the arguments are invalid, or no device): the counters, then
+ * the partial tiles, 1 KiB per 16-row tile and split on the skinny kernels (at most 257 KiB
+ * on MI355X), 8 or 16 KiB per 64-row tile and split on the prefill kernel (the grid within
+ * two workgroups per CU: at most 8 MiB + 1 KiB on MI355X). */
 size_t nm_spmm_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, int N, int M);
 
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation): nm_spmm_ws with its workspace in a
  * static device array of the library, NM_NOALLOC_SCRATCH_BYTES per GPU, held from the first
  * call on that GPU until the process ends. The same arguments, routing, Y and errors as
- * nm_spmm_ws with a workspace of that size; a shape whose column split needs more
+ * nm_spmm_ws with a workspace of that size; a shape whose split needs more
  * (nm_spmm_workspace_bytes > NM_NOALLOC_SCRATCH_BYTES; none on MI355X, whose largest is
- * 257 KiB) is NM_ERR_SCRATCH before any launch. Calls no hipMalloc/hipFree. The first call
+ * 8 MiB + 1 KiB) is NM_ERR_SCRATCH before any launch. Calls no hipMalloc/hipFree. The first call
  * on a GPU looks the array up (hipGetSymbolAddress) and queues a fill kernel that clears it
  * on `stream`, ahead of its own kernels; the kernels leave the counters at zero after every
  * call. All calls on one GPU share the array: calls that overlap on one GPU (other streams,
  * other threads, without ordering between them) race and give unspecified Y. */
-#define NM_NOALLOC_SCRATCH_BYTES (512u * 1024u)
+#define NM_NOALLOC_SCRATCH_BYTES (8u * 1024u * 1024u + 4096u)
 int nm_spmm_noalloc(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
                     int64_t rows, int64_t cols, int64_t batch, int N, int M, void* stream);
 
@@ -245,6 +253,11 @@ int nm_gemm_dense_prefill(const uint16_t* W, const uint16_t* X, uint16_t* Y,
  * on the current device (for more than one launch, the kernel of the first); "" if the
  * arguments are invalid. Static string, never NULL. */
 const char* nm_spmm_variant(int64_t rows, int64_t cols, int64_t batch, int N, int M);
+
+/* Introspection: the name of the kernel nm_spmm_ws launches for these arguments with a
+ * workspace of nm_spmm_workspace_bytes (the column-split kernels where it takes them, else as
+ * nm_spmm_variant); "" if the arguments are invalid. Static string, never NULL. */
+const char* nm_spmm_ws_variant(int64_t rows, int64_t cols, int64_t batch, int N, int M);
 
 /* Introspection: the name of the kernel configuration nm_spmm_prefill (sparse == 1: 2:4;
  * sparse == 2: 4:8 or 8:16) or nm_gemm_dense_prefill (sparse == 0) launches for this shape

@@ -54,6 +54,7 @@ SIGNATURES = {
                                          _c.c_int64, _c.c_void_p]),
     "nm_prefill_variant": (_c.c_char_p, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
     "nm_spmm_variant": (_c.c_char_p, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int, _c.c_int]),
+    "nm_spmm_ws_variant": (_c.c_char_p, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int, _c.c_int]),
     "nm_status_string": (_c.c_char_p, [_c.c_int]),
     "nm_spmv_variant": (_c.c_char_p, [_c.c_int64, _c.c_int64, _c.c_int, _c.c_int]),
     "nm_last_hip_error": (_c.c_int, []),
@@ -306,6 +307,12 @@ def nm_gemv_dense(W, x, out=None):
 def spmm_variant(rows: int, cols: int, batch: int, N: int, M: int) -> str:
     """Kernel nm_spmm launches for this shape, batch and pattern (the first, if several)."""
     return lib().nm_spmm_variant(rows, cols, batch, N, M).decode()
+
+
+def spmm_ws_variant(rows: int, cols: int, batch: int, N: int, M: int) -> str:
+    """Kernel nm_spmm_ws launches with a workspace of spmm_workspace_bytes (the first, if
+    several)."""
+    return lib().nm_spmm_ws_variant(rows, cols, batch, N, M).decode()
 
 
 def prefill_variant(rows: int, cols: int, tokens: int, sparse: bool, split: bool = False) -> str:

@@ -1,5 +1,6 @@
 // C ABI of libnmsparse.so: argument validation (no HIP call before it passes),
 // status strings, the per-device attribute cache and the dispatch to the kernels.
+#include <cstring>
 #include <mutex>
 #include <set>
 #include <utility>
@@ -93,6 +94,15 @@ bool prefill_route(int64_t rows, int64_t cols, int64_t batch, int N, int M, cons
   return !(short_batch && use_skinny(rows, cols, kSkinnyBatch, N, M, dev));
 }
 
+// From a sweep on MI355X at 17..256 vectors (µs, column split against the unsplit prefill
+// kernel and against 16-vector skinny launches): 4096 x 4096 2:4 at 32 vectors 10.8 against
+// 25.9 and 16.7; 1024 x 8192 at 64 12.3 against 48.7 and 46.3; 4096 x 14336 4:8 at 64 30.7
+// against 97.2 and 106; 14336 x 4096 at 64 26.8 against 27.9. At 16 vectors and below one
+// skinny launch is as fast or faster (4096 x 4096 2:4: 9.2 against 11.9).
+bool colsplit_route(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev) {
+  return batch > kSkinnyBatch && prefill_pattern(N, M) && prefill_workspace_bytes(rows, cols, batch, dev) > 0;
+}
+
 // nm_spmm's argument checks, before any HIP call.
 int spmm_check(const uint16_t* values, const uint32_t* masks, const uint16_t* X, const uint16_t* Y, int64_t rows,
                int64_t cols, int64_t batch, int N, int M) {
@@ -115,8 +125,19 @@ int spmm_dispatch(const uint16_t* values, const uint32_t* masks, const uint16_t*
   DeviceInfo dev;
   hipError_t e = current_device_info(&dev);
   if (e != hipSuccess) return hip_fail(e);
-  if (prefill_route(rows, cols, batch, N, M, dev))  // matrix-core prefill product
-    return nm_spmm_prefill(values, masks, X, Y, rows, cols, batch, N, M, stream);
+  if (workspace != nullptr && colsplit_route(rows, cols, batch, N, M, dev) &&
+      workspace_bytes >= prefill_workspace_bytes(rows, cols, batch, dev)) {
+    // column-split prefill product (launch_prefill_spmm takes the split with this workspace)
+    e = launch_prefill_spmm(values, masks, X, Y, rows, cols, batch, N, M, static_cast<hipStream_t>(stream), dev,
+                            workspace, workspace_bytes);
+    return e == hipSuccess ? NM_OK : hip_fail(e);
+  }
+  if (prefill_route(rows, cols, batch, N, M, dev)) {  // matrix-core prefill product
+    if (!prefill_fits(rows, cols, batch)) return NM_ERR_SHAPE;
+    e = launch_prefill_spmm(values, masks, X, Y, rows, cols, batch, N, M, static_cast<hipStream_t>(stream), dev,
+                            workspace, workspace_bytes);
+    return e == hipSuccess ? NM_OK : hip_fail(e);
+  }
   if (M != 2 * N && cols > max_cols_for(dev)) return NM_ERR_TOO_WIDE;  // 25%: single-vector kernel only
   if (N == 16 && M == 32 && batch >= kSkinnyMinBatch) {
     // 16:32 from 5 vectors, any batch (it has no prefill kernel): each launch of up to 16
@@ -173,9 +194,9 @@ int spmm_dispatch(const uint16_t* values, const uint32_t* masks, const uint16_t*
 // Workspace bytes spmm_dispatch can use for the product (0 when it would not use one).
 size_t spmm_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev) {
   if (!valid_shape(rows, cols) || !valid_pattern(N, M) || batch < 1 || batch > kPrefillMaxTokens) return 0;
-  if (prefill_route(rows, cols, batch, N, M, dev) ||
-      !use_skinny(rows, cols, batch < kSkinnyBatch ? batch : kSkinnyBatch, N, M, dev))
-    return 0;
+  if (colsplit_route(rows, cols, batch, N, M, dev)) return prefill_workspace_bytes(rows, cols, batch, dev);
+  if (prefill_route(rows, cols, batch, N, M, dev)) return 0;
+  if (!use_skinny(rows, cols, batch < kSkinnyBatch ? batch : kSkinnyBatch, N, M, dev)) return 0;
   return skinny_workspace_bytes(rows, cols, int(batch < kSkinnyBatch ? batch : kSkinnyBatch), N, dev);
 }
 }  // namespace nm
@@ -373,6 +394,18 @@ const char* nm_spmm_variant(int64_t rows, int64_t cols, int64_t batch, int N, in
   if (nm::use_skinny(rows, cols, batch < nm::kSkinnyBatch ? batch : nm::kSkinnyBatch, N, M, dev))
     return nm::skinny_variant(N);
   return nm::spmm_variant(rows, cols, N, batch < nm::kSmallBatch ? batch : nm::kSmallBatch, dev);
+}
+
+const char* nm_spmm_ws_variant(int64_t rows, int64_t cols, int64_t batch, int N, int M) {
+  const char* v = nm_spmm_variant(rows, cols, batch, N, M);
+  if (*v == '\0') return v;
+  nm::DeviceInfo dev;
+  if (nm::current_device_info(&dev) != hipSuccess) return "";
+  if (nm::colsplit_route(rows, cols, batch, N, M, dev)) return nm::prefill_colsplit_variant(rows, cols, batch, dev, N != 2);
+  const int nb = int(batch < nm::kSkinnyBatch ? batch : nm::kSkinnyBatch);
+  if (N != 16 && std::strcmp(v, nm::skinny_variant(N)) == 0 && nm::skinny_workspace_bytes(rows, cols, nb, N, dev) > 0)
+    return N == 2 ? "skinny_colsplit_kernel<false>" : "skinny_colsplit_kernel<true>";
+  return v;
 }
 
 const char* nm_prefill_variant(int64_t rows, int64_t cols, int64_t tokens, int sparse) {

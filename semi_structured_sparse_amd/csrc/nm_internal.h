@@ -88,9 +88,18 @@ constexpr int64_t kPrefillMaxTokens = int64_t(1) << 24;
 bool prefill_fits(int64_t rows, int64_t cols, int64_t tokens);
 // 50% patterns with a matrix-core product: 2:4, and 4:8 / 8:16 as two 2:4 operands.
 bool prefill_pattern(int n, int m);
+// With a workspace of at least prefill_workspace_bytes (0: the shape takes no column split)
+// a grid too small for the CUs (mid-size batches) splits each output tile's columns over
+// several workgroups; without one (or a smaller one) it runs unsplit. The counters must be
+// zero before the launch, which leaves them zero (the same counter region as the skinny
+// kernels' column splits, so one workspace serves both in stream order).
+size_t prefill_workspace_bytes(int64_t rows, int64_t cols, int64_t tokens, const DeviceInfo& dev);
 hipError_t launch_prefill_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
                                int64_t rows, int64_t cols, int64_t tokens, int n, int m, hipStream_t stream,
-                               const DeviceInfo& dev);
+                               const DeviceInfo& dev, void* workspace = nullptr, size_t workspace_bytes = 0);
+// Bytes at the start of a workspace that hold the column splits' per-tile counters (fixed
+// per device, so that every shape finds its counters where earlier launches left zeros).
+size_t counter_bytes(const DeviceInfo& dev);
 hipError_t launch_prefill_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y, int64_t rows, int64_t cols,
                                int64_t tokens, hipStream_t stream, const DeviceInfo& dev);
 // Small-batch 50% product on the matrix instructions, 1..16 tokens (X [tokens][cols],
@@ -147,15 +156,22 @@ const char* skinny_variant(int n);
 int spmm_check(const uint16_t* values, const uint32_t* masks, const uint16_t* X, const uint16_t* Y, int64_t rows,
                int64_t cols, int64_t batch, int N, int M);
 // nm_spmm's dispatch; with a workspace of at least spmm_workspace_bytes (counters zero) the
-// skinny kernels split the columns of short layers.
+// skinny kernels split the columns of short layers, and batches of more than kSkinnyBatch
+// vectors take the column-split prefill kernel where colsplit_route says so.
 int spmm_dispatch(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y, int64_t rows,
                   int64_t cols, int64_t batch, int N, int M, void* stream, void* workspace, size_t workspace_bytes);
 size_t spmm_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev);
 
 // Whether nm_spmm runs a batch on the prefill kernels (else on skinny or small-batch launches).
 bool prefill_route(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev);
+// Whether nm_spmm_ws, given a workspace of prefill_workspace_bytes, runs a batch on the
+// column-split prefill kernel: 2:4, 4:8 and 8:16 batches of more than kSkinnyBatch vectors
+// whose small-tile grid leaves CUs idle.
+bool colsplit_route(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev);
 
 // Name of the kernel configuration the prefill launchers pick (static string).
 const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev, bool split = false);
+// The column-split kernel launch_prefill_spmm runs with a workspace ("" if none).
+const char* prefill_colsplit_variant(int64_t rows, int64_t cols, int64_t tokens, const DeviceInfo& dev, bool split);
 
 }  // namespace nm

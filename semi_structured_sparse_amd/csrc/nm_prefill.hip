@@ -46,13 +46,73 @@ bool prefill_fits(int64_t rows, int64_t cols, int64_t tokens) {
 
 bool prefill_pattern(int n, int m) { return 2 * n == m && (n == 2 || n == 4 || n == 8); }
 
+namespace {
+
+// Column splits where the small-tile grid leaves CUs idle: tiles of 64 rows x 32 tokens (up
+// to 32 tokens) or x 64 tokens, and S = 2, 4, .. kMaxColSplits workgroups per tile while every
+// split keeps at least one block of kColBlock columns and the grid stays within one
+// workgroup per CU, or two where the CUs have at least 4 blocks each. Fitted to a sweep on
+// MI355X (17..256 tokens, 1024..14336 rows and columns): one workgroup per CU costs about
+// 7.6 us plus 0.31 us per 64-column step, two about 11.9 us plus 0.175 us per step of the CU
+// (4096 x 4096 x 64, 2:4: 12.6 us at 4 splits against 14.7 at 8; 8192 x 8192 x 32: 23.1 us at
+// 4 against 27.6 at 2). Where one workgroup per CU allows no split, 2 splits if two fit.
+struct ColPlan {
+  int splits = 1, blocks = 0, tt = 4;
+  int64_t tiles = 0;
+};
+
+ColPlan colsplit_plan(int64_t rows, int64_t cols, int64_t tokens, const DeviceInfo& dev) {
+  ColPlan p;
+  if (use_large<SparseLarge>(rows, tokens, dev)) return p;
+  const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
+  p.tt = tokens <= 32 ? 2 : 4;
+  p.tiles = ceil_div(rows, Small::kRows) * ceil_div(tokens, 16 * p.tt);
+  const int64_t nblk = ceil_div(cols, kColBlock);
+  const int64_t cap = p.tiles * nblk >= 4 * cus ? 2 * cus : cus;   // workgroups in the grid
+  int s = 1;
+  while (s < kMaxColSplits && p.tiles * (2 * s) <= cap && 2 * s <= nblk) s *= 2;
+  if (s == 1 && p.tiles * 2 <= 2 * cus && nblk >= 2) s = 2;
+  if (s == 1) return p;
+  p.blocks = int(ceil_div(nblk, s));
+  p.splits = int(ceil_div(nblk, p.blocks));   // every split non-empty
+  return p;
+}
+
+size_t colsplit_bytes(const ColPlan& p, const DeviceInfo& dev) {
+  if (p.splits == 1) return 0;
+  return counter_bytes(dev) + size_t(p.tiles) * size_t(p.splits) * size_t(kThreads) * size_t(p.tt) * 16u;
+}
+
+template <bool SPLIT>
+const void* colsplit_kernel(int tt) {
+  return tt == 2 ? reinterpret_cast<const void*>(&prefill_colsplit_kernel<1, 2, 64, kDepth, SPLIT>)
+                 : reinterpret_cast<const void*>(&prefill_colsplit_kernel<1, 4, 64, kDepth, SPLIT>);
+}
+
+}  // namespace
+
+size_t prefill_workspace_bytes(int64_t rows, int64_t cols, int64_t tokens, const DeviceInfo& dev) {
+  if (!prefill_fits(rows, cols, tokens)) return 0;
+  return colsplit_bytes(colsplit_plan(rows, cols, tokens, dev), dev);
+}
+
 hipError_t launch_prefill_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
                                int64_t rows, int64_t cols, int64_t tokens, int n, int m, hipStream_t stream,
-                               const DeviceInfo& dev) {
+                               const DeviceInfo& dev, void* workspace, size_t workspace_bytes) {
   if (!prefill_fits(rows, cols, tokens) || !prefill_pattern(n, m)) return hipErrorInvalidValue;
   int r = int(rows), c = int(cols), t = int(tokens);
-  void* args[] = {&values, &masks, &X, &Y, &r, &c, &t};
   const bool split = n != 2;
+  const ColPlan p = colsplit_plan(rows, cols, tokens, dev);
+  const size_t need = colsplit_bytes(p, dev);
+  if (need > 0 && workspace != nullptr && workspace_bytes >= need) {
+    int sp = p.splits, bl = p.blocks;
+    unsigned* cnt = static_cast<unsigned*>(workspace);
+    float4* part = reinterpret_cast<float4*>(static_cast<char*>(workspace) + counter_bytes(dev));
+    void* cargs[] = {&values, &masks, &X, &Y, &r, &c, &t, &sp, &bl, &part, &cnt};
+    return launch(split ? colsplit_kernel<true>(p.tt) : colsplit_kernel<false>(p.tt),
+                  dim3(unsigned(p.tiles * p.splits)), dim3(kThreads), cargs, 0, stream, dev);
+  }
+  void* args[] = {&values, &masks, &X, &Y, &r, &c, &t};
   if (use_large<SparseHuge>(rows, tokens, dev))
     return launch(split ? reinterpret_cast<const void*>(&prefill_split_kernel<4, 16, 64, kDepth>)
                         : reinterpret_cast<const void*>(&prefill_spmm_kernel<4, 16, 64, kDepth>),
@@ -76,6 +136,14 @@ hipError_t launch_prefill_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y
                   dim3(unsigned(workgroups<DenseLarge>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
   return launch(reinterpret_cast<const void*>(&prefill_gemm_kernel<1, 4, 64, kDepth>),
                 dim3(unsigned(workgroups<Small>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
+}
+
+const char* prefill_colsplit_variant(int64_t rows, int64_t cols, int64_t tokens, const DeviceInfo& dev, bool split) {
+  const ColPlan p = colsplit_plan(rows, cols, tokens, dev);
+  if (p.splits == 1) return "";
+  if (split)
+    return p.tt == 2 ? "prefill_colsplit_kernel<1, 2, 64, 2, true>" : "prefill_colsplit_kernel<1, 4, 64, 2, true>";
+  return p.tt == 2 ? "prefill_colsplit_kernel<1, 2, 64, 2, false>" : "prefill_colsplit_kernel<1, 4, 64, 2, false>";
 }
 
 const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev, bool split) {

@@ -213,6 +213,24 @@ __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
+// Partial tiles of column splits cross workgroups on different XCDs, whose L2 caches are
+// not coherent with each other: buffer accesses with the SC1 cache-policy bit are (the form
+// the compiler gives device-scope atomic loads and stores), so no fence has to write back or
+// invalidate a whole L2.
+constexpr int kCoherentAux = 16;   // SC1
+
+__device__ __forceinline__ void coherent_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v) {
+  typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
+  const u4_t u = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(u, r, off, 0, kCoherentAux);
+}
+
+__device__ __forceinline__ float4 coherent_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
+  const u4_t u = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherentAux);
+  return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+
 // LDS byte offset of 16-byte chunk c of token t in an X buffer with rb bytes per token:
 // the low 3 bits of the chunk index are XORed with the token's, so the 8 tokens one
 // fragment read touches at a time land on 8 different 16-byte bank groups.
@@ -436,25 +454,27 @@ __device__ __forceinline__ void unroll_slots(F& f) {
   }
 }
 
-// The sparse product's main loop: the dense one's schedule, unrolled U steps at a time (U a
-// multiple of D) so that every slot of a mask block has a fixed name, with a hook per slot
-// (run after the slot's loads are issued) for the mask-block loads, and a stage callback
-// run once after the first loads are issued (LDS writes of data loaded before them). Steps
-// past the last one (up to U - 1) skip only the math.
+// The sparse product's main loop over columns c_beg .. c_end - 1 (c_beg a multiple of U *
+// KS, so that step s of the range is step s of its mask block): the dense one's schedule,
+// unrolled U steps at a time (U a multiple of D) so that every slot of a mask block has a
+// fixed name, with a hook per slot (run after the slot's loads are issued) for the
+// mask-block loads, and a stage callback run once after the first loads are issued (LDS
+// writes of data loaded before them). Steps past the last one (up to U - 1) skip only the
+// math.
 template <int TR, int TT, int KS, int D, int U, typename AFrag, typename LoadA, typename Hook, typename Compute,
           typename Stage>
 __device__ __forceinline__ void sparse_main_loop(const XStager<TR, TT, KS>& xst,
-                                                 char (*xs)[Tile<TR, TT, KS>::kXBytes], int cols, LoadA load_a,
-                                                 Hook hook, Compute compute, Stage stage) {
+                                                 char (*xs)[Tile<TR, TT, KS>::kXBytes], int cols, int c_beg,
+                                                 int c_end, LoadA load_a, Hook hook, Compute compute, Stage stage) {
   static_assert(U % D == 0, "unroll must be a multiple of the load depth");
   using T = Tile<TR, TT, KS>;
-  const int steps = (cols + KS - 1) / KS;
-  const int last = (steps - 1) * KS;
+  const int steps = (c_end - c_beg + KS - 1) / KS;
+  const int last = c_beg + (steps - 1) * KS;
   uint4 xr[D][T::kXPerThread];
   AFrag af[D];
 #pragma unroll
   for (int p = 0; p < D; ++p) {
-    const int c = min(p * KS, last);
+    const int c = min(c_beg + p * KS, last);
     xst.load(xr[p], c, cols);
     load_a(af[p], c);
   }
@@ -467,7 +487,7 @@ __device__ __forceinline__ void sparse_main_loop(const XStager<TR, TT, KS>& xst,
       __syncthreads();
       xst.store(xr[(P + 1) % D], xs[(s + 1) & 1]);
       const AFrag cur = af[P % D];
-      const int cn = min((s + D) * KS, last);
+      const int cn = min(c_beg + (s + D) * KS, last);
       xst.load(xr[P % D], cn, cols);
       load_a(af[P % D], cn);
       hook(pc, s0);
@@ -477,21 +497,91 @@ __device__ __forceinline__ void sparse_main_loop(const XStager<TR, TT, KS>& xst,
   }
 }
 
+// ---- column splits (mid-size batches) ----
+// With a few hundred tokens or fewer the grid of output tiles leaves most CUs idle while each
+// workgroup walks every column in turn, so the columns of a tile can go to `splits`
+// consecutive workgroups, each taking whole blocks of kColBlock columns (one block of mask
+// words per row). Each leaves its fp32 partial tile in part (per tile, per split, one float4
+// per lane and 16 x 16 tile: kThreads * TR * TT float4) and counts itself in cnt[tile]; the
+// last to arrive sums the partials in split order (the same order whichever arrives last),
+// resets the count to zero and stores the tile. Consecutive workgroups land on different
+// XCDs, so with 8 splits each XCD takes one column range of every tile and its L2 serves that
+// range of X to all of them.
+constexpr int kColBlock = 512;
+constexpr int kMaxColSplits = 8;
+
+struct ColSplit {
+  float4* part;
+  unsigned* cnt;
+  int splits, tile, split;
+  unsigned* flag;   // one LDS word: the count this workgroup's arrival saw
+};
+
+// Hands the partial tile over; true in the workgroup that then holds the tile's sum in acc.
+template <int TR, int TT>
+__device__ __forceinline__ bool split_handoff(f4_t (&acc)[TR][TT], const ColSplit& cs) {
+  constexpr int kPer = kThreads * TR * TT;   // float4 per partial tile
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t pr =
+      make_rsrc(cs.part + size_t(cs.tile) * unsigned(cs.splits) * unsigned(kPer), int64_t(cs.splits) * kPer * 16);
+#pragma unroll
+  for (int a = 0; a < TR; ++a)
+#pragma unroll
+    for (int b = 0; b < TT; ++b)
+      coherent_store16(pr, uint32_t((cs.split * TR * TT + a * TT + b) * kThreads + tid) * 16u,
+                       make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]));
+  // every wave's partial has reached the device's coherence point before the count moves
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) *cs.flag = atomicAdd(cs.cnt + cs.tile, 1u);
+  __syncthreads();
+  if (*cs.flag != unsigned(cs.splits - 1)) return false;
+  // the tile's last workgroup: every split's partial is complete. All kMaxColSplits loads
+  // are issued at once (one memory round trip), then summed in split order; those past the
+  // last split are outside the resource and read zero, and adding zero after the last split
+  // leaves the sum as it is.
+  float4 v[kMaxColSplits][TR][TT];
+#pragma unroll
+  for (int k = 0; k < kMaxColSplits; ++k)
+#pragma unroll
+    for (int a = 0; a < TR; ++a)
+#pragma unroll
+      for (int b = 0; b < TT; ++b)
+        v[k][a][b] = coherent_load16(pr, uint32_t((k * TR * TT + a * TT + b) * kThreads + tid) * 16u);
+  zero(acc);
+#pragma unroll
+  for (int k = 0; k < kMaxColSplits; ++k) {
+#pragma unroll
+    for (int a = 0; a < TR; ++a)
+#pragma unroll
+      for (int b = 0; b < TT; ++b) {
+        acc[a][b][0] += v[k][a][b].x;
+        acc[a][b][1] += v[k][a][b].y;
+        acc[a][b][2] += v[k][a][b].z;
+        acc[a][b][3] += v[k][a][b].w;
+      }
+  }
+  if (tid == 0) atomicExch(cs.cnt + cs.tile, 0u);
+  return true;
+}
+
 // The sparse products: values [rows][cols / 2] fp16, masks [rows][cols / 32]; 2:4 directly
 // (SPLIT false), 4:8 and 8:16 split into two 2:4 operands (SPLIT true, lut = the split
 // tables in LDS).
-template <int TR, int TT, int KS, int D, bool SPLIT>
+// COLS: one of a tile's column splits (columns c_beg .. c_end - 1; the hand-off to the
+// tile's last workgroup in split_handoff), else the whole row (c_beg = 0, c_end = cols).
+template <int TR, int TT, int KS, int D, bool SPLIT, bool COLS>
 __device__ __forceinline__ void prefill_sparse_body(const uint16_t* __restrict__ values,
                                                     const uint32_t* __restrict__ masks,
                                                     const uint16_t* __restrict__ X, uint16_t* __restrict__ Y,
                                                     int rows, int cols, int tokens,
-                                                    char (*xs)[Tile<TR, TT, KS>::kXBytes], char* lut) {
+                                                    char (*xs)[Tile<TR, TT, KS>::kXBytes], char* lut,
+                                                    TileCoord tc, int c_beg, int c_end, const ColSplit& cs) {
   using T = Tile<TR, TT, KS>;
   constexpr int SUB = T::kSub;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, li = lane & 15;
-  const TileCoord tc = tile_of(int(blockIdx.x), (rows + T::kRows - 1) / T::kRows, (tokens + T::kTokens - 1) / T::kTokens);
   const int r0 = tc.rx * T::kRows + wave * 16 * TR;
   const int t0 = tc.ty * T::kTokens;
   const int words = cols >> 5;
@@ -551,12 +641,14 @@ __device__ __forceinline__ void prefill_sparse_body(const uint16_t* __restrict__
   // kMaskSteps - D steps into the current one, D steps ahead like the values.
   constexpr int kMaskSteps = 8;
   static_assert(KS == 64, "mask blocks are laid out for 64-column steps");
-  const int steps = (cols + KS - 1) / KS;
-  const int last_block = (steps - 1) / kMaskSteps;
+  static_assert(kMaskSteps * KS == kColBlock, "column splits cover whole mask blocks");
+  const int steps = (c_end - c_beg + KS - 1) / KS;
+  const int first_block = c_beg / kColBlock, last_block = (steps - 1) / kMaskSteps;
   uint4 mcur[TR], mnext[TR];
-  auto load_masks = [&](int blk) {
+  auto load_masks = [&](int blk) {   // blk counts from the range's first block
 #pragma unroll
-    for (int a = 0; a < TR; ++a) mnext[a] = buf_load16(mr, moff[a] + uint32_t(64 * min(blk, last_block)));
+    for (int a = 0; a < TR; ++a)
+      mnext[a] = buf_load16(mr, moff[a] + uint32_t(64 * (first_block + min(blk, last_block))));
   };
   load_masks(0);
   auto hook = [&](auto pc, int s0) {
@@ -630,7 +722,10 @@ __device__ __forceinline__ void prefill_sparse_body(const uint16_t* __restrict__
       }
     }
   };
-  sparse_main_loop<TR, TT, KS, D, kMaskSteps, AF>(xst, xs, cols, load_a, hook, compute, stage);
+  sparse_main_loop<TR, TT, KS, D, kMaskSteps, AF>(xst, xs, cols, c_beg, c_end, load_a, hook, compute, stage);
+  if constexpr (COLS) {
+    if (!split_handoff<TR, TT>(acc, cs)) return;
+  }
   // (the split kernels keep the direct stores: with the staged ones their 256 x 256 tile
   // measured 8% slower on 14336 x 4096 x 2048, the 2:4 and dense kernels 2-6% faster)
   if constexpr (SPLIT)
@@ -646,8 +741,11 @@ __global__ __launch_bounds__(kThreads) void prefill_spmm_kernel(const uint16_t* 
                                                                 const uint16_t* __restrict__ X,
                                                                 uint16_t* __restrict__ Y, int rows, int cols,
                                                                 int tokens) {
-  __shared__ __attribute__((aligned(16))) char xs[2][Tile<TR, TT, KS>::kXBytes];
-  prefill_sparse_body<TR, TT, KS, D, false>(values, masks, X, Y, rows, cols, tokens, xs, nullptr);
+  using T = Tile<TR, TT, KS>;
+  __shared__ __attribute__((aligned(16))) char xs[2][T::kXBytes];
+  const TileCoord tc = tile_of(int(blockIdx.x), (rows + T::kRows - 1) / T::kRows, (tokens + T::kTokens - 1) / T::kTokens);
+  prefill_sparse_body<TR, TT, KS, D, false, false>(values, masks, X, Y, rows, cols, tokens, xs, nullptr, tc, 0, cols,
+                                                   ColSplit{});
 }
 
 // 4:8 and 8:16 sparse product (split operands).
@@ -657,9 +755,37 @@ __global__ __launch_bounds__(kThreads) void prefill_split_kernel(const uint16_t*
                                                                  const uint16_t* __restrict__ X,
                                                                  uint16_t* __restrict__ Y, int rows, int cols,
                                                                  int tokens) {
-  __shared__ __attribute__((aligned(16))) char xs[2][Tile<TR, TT, KS>::kXBytes];
+  using T = Tile<TR, TT, KS>;
+  __shared__ __attribute__((aligned(16))) char xs[2][T::kXBytes];
   __shared__ __attribute__((aligned(16))) char lut[kSplitLutBytes];
-  prefill_sparse_body<TR, TT, KS, D, true>(values, masks, X, Y, rows, cols, tokens, xs, lut);
+  const TileCoord tc = tile_of(int(blockIdx.x), (rows + T::kRows - 1) / T::kRows, (tokens + T::kTokens - 1) / T::kTokens);
+  prefill_sparse_body<TR, TT, KS, D, true, false>(values, masks, X, Y, rows, cols, tokens, xs, lut, tc, 0, cols,
+                                                  ColSplit{});
+}
+
+// Column-split sparse products (2:4 when !SPLIT, 4:8 and 8:16 when SPLIT): workgroup b takes
+// split b % splits of tile b / splits (row tile fastest), columns [split, split + 1) *
+// blocks * kColBlock of the row.
+template <int TR, int TT, int KS, int D, bool SPLIT>
+__global__ __launch_bounds__(kThreads) void prefill_colsplit_kernel(const uint16_t* __restrict__ values,
+                                                                    const uint32_t* __restrict__ masks,
+                                                                    const uint16_t* __restrict__ X,
+                                                                    uint16_t* __restrict__ Y, int rows, int cols,
+                                                                    int tokens, int splits, int blocks,
+                                                                    float4* __restrict__ part,
+                                                                    unsigned* __restrict__ cnt) {
+  using T = Tile<TR, TT, KS>;
+  __shared__ __attribute__((aligned(16))) char xs[2][T::kXBytes];
+  __shared__ __attribute__((aligned(16))) char lut[SPLIT ? kSplitLutBytes : 16];
+  __shared__ unsigned flag;
+  const int b = int(blockIdx.x);
+  const int tile = b / splits, split = b - tile * splits;
+  const int nrx = (rows + T::kRows - 1) / T::kRows;
+  const TileCoord tc{tile % nrx, tile / nrx};
+  const int c_beg = split * blocks * kColBlock;
+  const int c_end = min(cols, c_beg + blocks * kColBlock);
+  prefill_sparse_body<TR, TT, KS, D, SPLIT, true>(values, masks, X, Y, rows, cols, tokens, xs, SPLIT ? lut : nullptr,
+                                                  tc, c_beg, c_end, ColSplit{part, cnt, splits, tile, split, &flag});
 }
 
 // Dense product: W [rows][cols] fp16.

@@ -115,24 +115,6 @@ __host__ __device__ constexpr uint32_t lead_bytes() {
                              : 0u;
 }
 
-// Partial tiles of column splits cross workgroups on different XCDs, whose L2 caches are
-// not coherent with each other: buffer accesses with the SC1 cache-policy bit are (the form
-// the compiler gives device-scope atomic loads and stores), so no fence has to write back or
-// invalidate a whole L2.
-constexpr int kCoherentAux = 16;   // SC1
-
-__device__ __forceinline__ void coherent_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v) {
-  typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
-  const u4_t u = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
-  __builtin_amdgcn_raw_buffer_store_b128(u, r, off, 0, kCoherentAux);
-}
-
-__device__ __forceinline__ float4 coherent_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
-  const u4_t u = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherentAux);
-  return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
-}
-
 // The workgroup's view of the launch: its rows, the wave's place in them, and the buffer
 // resources of its slices of the packed matrix and of X. With `splits` > 1 the columns of
 // each group of row tiles are split over that many consecutive workgroups (split = which).

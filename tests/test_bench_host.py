@@ -120,8 +120,8 @@ def test_best_dense_is_the_faster_of_ours_and_the_vendor_blas():
 
 def test_batch_workspace_arguments_and_kernel_names():
     """--batch B > 1 runs nm_spmm_ws: a layer with a workspace passes its pointer and size and
-    is named after the column-split kernel; one without passes NULL and is named as nm_spmm's
-    routing names it; batch one passes nothing."""
+    is named as nm_spmm_ws's routing names it; one without passes NULL and is named as
+    nm_spmm's routing names it; batch one passes nothing."""
     import bench
 
     class FakeWs:
@@ -136,12 +136,16 @@ def test_batch_workspace_arguments_and_kernel_names():
         def spmm_variant(R, C, B, N, M):
             return f"routed<{R},{C},{B},{N},{M}>"
 
+        @staticmethod
+        def spmm_ws_variant(R, C, B, N, M):
+            return f"ws<{R},{C},{B},{N},{M}>"
+
     L2 = dict(R=1024, C=8192, N=2, M=4, ws=FakeWs())
     L8 = dict(R=1024, C=4096, N=8, M=16, ws=FakeWs())
     Ln = dict(R=4096, C=4096, N=2, M=4, ws=None)
     assert bench.ws_args(L2, 1) == ()
     assert bench.ws_args(L2, 8) == (0x1000, 263168)
     assert bench.ws_args(Ln, 8) == (None, 0)
-    assert bench.batch_kernel_name(FakeNm, L2, 8) == "skinny_colsplit_kernel<false>"
-    assert bench.batch_kernel_name(FakeNm, L8, 12) == "skinny_colsplit_kernel<true>"
+    assert bench.batch_kernel_name(FakeNm, L2, 8) == "ws<1024,8192,8,2,4>"
+    assert bench.batch_kernel_name(FakeNm, L8, 12) == "ws<1024,4096,12,8,16>"
     assert bench.batch_kernel_name(FakeNm, Ln, 8) == "routed<4096,4096,8,2,4>"

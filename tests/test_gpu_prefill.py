@@ -249,3 +249,97 @@ def test_prefill_split_full_size_down_proj(N, M):
     W = synth.weight(R, C, synth.weight_seed(6, 3, (N, M)))
     X = synth.activations(T, C, synth.x_seed(6, 0, (N, M)))
     check_split(W, X, N, M, "down", sample_rows(R, k=24, rpb=128))
+
+
+# Column splits (nm_spmm_ws with a workspace of nm_spmm_workspace_bytes, batches of more than
+# 16 vectors whose prefill grid leaves CUs idle): ragged rows (64-row tiles; rows % 8 != 0 on
+# the direct stores), ragged tokens (32- and 64-token tiles), columns ending inside a
+# 512-column block and a last split of one 32-column step (1056 columns over 2 splits),
+# 2, 4, 7 (uneven: 28 blocks of 4) and 8 splits, one and two workgroups per CU
+COLSPLIT = [(1000, 4064, 17), (130, 1056, 100), (1024, 4096, 32), (2048, 8192, 48), (4096, 4096, 64),
+            (4096, 14336, 40), (1024, 8192, 256), (14336, 4096, 20), (4100, 1024, 150)]
+COLSPLIT_NAMES = {f"prefill_colsplit_kernel<1, {tt}, 64, 2, {sp}>" for tt in (2, 4) for sp in ("false", "true")}
+
+
+def _counter_bytes():
+    cus = torch.cuda.get_device_properties(device()).multi_processor_count
+    return -(-(4 * cus) // 256) * 256
+
+
+@pytest.mark.parametrize("N,M", [(2, 4), (4, 8), (8, 16)])
+def test_colsplit_small_and_ragged(N, M):
+    names = set()
+    for i, (R, C, T) in enumerate(COLSPLIT):
+        name = nm.spmm_ws_variant(R, C, T, N, M)
+        names.add(name)
+        need = nm.spmm_workspace_bytes(R, C, T, N, M)
+        say(f"colsplit {N}:{M} {R}x{C} tokens={T} {name} workspace={need}")
+        assert name.startswith("prefill_colsplit_kernel"), (R, C, T, name)
+        W = synth.weight(R, C, seed=4100 + 10 * i + N)
+        X = synth.activations(T, C, seed=4150 + i)
+        values, masks = nm.nm_pack(up_f16(W), N, M)
+        ws = nm.spmm_workspace(R, C, T, N, M)
+        assert ws.numel() == need
+        Y = down_f16(nm.nm_spmm_ws(values, masks, up_f16(X), N, M, ws))
+        assert int(ws[:_counter_bytes()].count_nonzero()) == 0   # every launch leaves them zero
+        idx = np.arange(R) if R * T <= 300 * 300 else sample_rows(R, k=24, rpb=64)
+        rv, rm = oracle.pack_ref(W[idx], N, M)
+        rep = oracle.y_tolerance_report(Y[:, idx], oracle.spmm_ref(rv, rm, X, C, N, M))
+        assert rep["ok"], ((R, C, T), N, M, rep)
+    want = {n for n in COLSPLIT_NAMES if n.endswith("false>" if N == 2 else "true>")}
+    assert names == want, names
+
+
+def test_colsplit_one_hot_deterministic_and_shared_workspace():
+    """One-hot tokens give the pruned matrix's columns bit-exactly (one nonzero product per
+    output, the other splits add zeros); repeated calls give the same bits; one workspace
+    sized for the largest shape serves a sequence of shapes and patterns, each bit-identical
+    to its own fresh workspace's result."""
+    R, C = 1000, 4096
+    W = synth.weight(R, C, seed=4200)
+    rv, rm = oracle.pack_ref(W, 2, 4)
+    D = oracle.unpack_ref(rv, rm, C, 2, 4)
+    X = np.eye(C, dtype=np.float16)[:40]
+    v, m = up_f16(rv), up_u32(rm)
+    assert nm.spmm_ws_variant(R, C, 40, 2, 4).startswith("prefill_colsplit_kernel")
+    ws = nm.spmm_workspace(R, C, 40, 2, 4)
+    Y = down_bits16(nm.nm_spmm_ws(v, m, up_f16(X), 2, 4, ws))
+    want = D.T[:40].copy()
+    want[want == 0x8000] = 0
+    assert np.array_equal(Y, want)
+    Xr = up_f16(synth.activations(40, C, seed=4201))
+    Y0 = down_bits16(nm.nm_spmm_ws(v, m, Xr, 2, 4, ws))
+    for _ in range(5):
+        assert np.array_equal(down_bits16(nm.nm_spmm_ws(v, m, Xr, 2, 4, ws)), Y0)
+    cases = [((2, 4), 1024, 4096, 32), ((8, 16), 4096, 14336, 40), ((2, 4), 130, 1056, 100), ((4, 8), 2048, 8192, 17),
+             ((2, 4), 1024, 8192, 16)]
+    big = torch.zeros(max(nm.spmm_workspace_bytes(R, C, T, N, M) for (N, M), R, C, T in cases), dtype=torch.uint8,
+                      device=device())
+    for k, ((N, M), R, C, T) in enumerate(cases):
+        Wk = synth.weight(R, C, 4210 + k)
+        vk, mk = nm.nm_pack(up_f16(Wk), N, M)
+        Xk = up_f16(synth.activations(T, C, 4220 + k))
+        got = down_bits16(nm.nm_spmm_ws(vk, mk, Xk, N, M, big))
+        assert np.array_equal(got, down_bits16(nm.nm_spmm_ws(vk, mk, Xk, N, M, nm.spmm_workspace(R, C, T, N, M)))), k
+
+
+def test_colsplit_small_workspace_takes_nm_spmm_route():
+    """A workspace smaller than the column split needs (or none) runs nm_spmm's route, bit for
+    bit: the prefill kernel at 64 vectors, skinny launches at 32 on a small layer."""
+    for R, C, T in ((4096, 14336, 64), (1024, 4096, 32)):
+        W = synth.weight(R, C, 4300 + T)
+        v, m = nm.nm_pack(up_f16(W), 2, 4)
+        X = up_f16(synth.activations(T, C, 4301 + T))
+        need = nm.spmm_workspace_bytes(R, C, T, 2, 4)
+        assert need > 0
+        small = torch.zeros(need - 16, dtype=torch.uint8, device=device())
+        want = down_bits16(nm.nm_spmm(v, m, X, 2, 4))
+        assert np.array_equal(down_bits16(nm.nm_spmm_ws(v, m, X, 2, 4, None)), want)
+        got = down_bits16(nm.nm_spmm_ws(v, m, X, 2, 4, small))
+        if nm.spmm_variant(R, C, T, 2, 4).startswith("prefill"):
+            assert np.array_equal(got, want)
+        else:   # skinny launches may split their columns with the smaller workspace
+            rv, rm = oracle.pack_ref(W[:64], 2, 4)
+            rep = oracle.y_tolerance_report(down_f16(nm.nm_spmm_ws(v, m, X, 2, 4, small))[:, :64],
+                                            oracle.spmm_ref(rv, rm, down_f16(X), C, 2, 4))
+            assert rep["ok"], rep

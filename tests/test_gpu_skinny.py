@@ -183,12 +183,13 @@ def test_skinny_malformed_masks_stay_in_bounds(N, M):
 # workgroups per tile where that pays (rows of >= 64 lines of 128 columns; >= 40 lines from 8
 # vectors; the split patterns from 9 vectors), each on a range of whole lines, the last to
 # arrive summing the partial tiles. Ragged rows; a ragged last split (8224 columns = 64.25
-# lines over 8 splits, 2080 = 16.25 over 4); several X phases inside one split (16 vectors x
-# 14336 columns); two launches on one workspace, both split (31 vectors), or the second on
-# the small-batch kernel (17 and 20 vectors: the last 1 or 4).
-SPLIT_CASES = [((2, 4), 1024, 8192, 8), ((2, 4), 512, 8192, 5), ((2, 4), 1000, 8192, 17), ((2, 4), 300, 8224, 6),
+# lines over 8 splits); several X phases inside one split (16 vectors x 14336 columns).
+# (Batches of more than 16 vectors with a workspace of nm_spmm_workspace_bytes take the
+# column-split prefill kernel; their skinny launches are covered below with a workspace sized
+# for 16 vectors.)
+SPLIT_CASES = [((2, 4), 1024, 8192, 8), ((2, 4), 512, 8192, 5), ((2, 4), 300, 8224, 6),
                ((2, 4), 2048, 14336, 16), ((4, 8), 1024, 4096, 9), ((8, 16), 1030, 8192, 16),
-               ((8, 16), 512, 8192, 12), ((4, 8), 777, 2080, 31), ((2, 4), 256, 5120, 31), ((2, 4), 1024, 5120, 20)]
+               ((8, 16), 512, 8192, 12)]
 
 
 def _counter_bytes():
@@ -217,6 +218,24 @@ def test_skinny_column_split(pat, R, C, T):
     assert int(ws[:_counter_bytes()].count_nonzero()) == 0
 
 
+# two skinny launches on one workspace, both split (31 vectors), or the second on the
+# small-batch kernel (17 and 20 vectors: the last 1 or 4), with a workspace sized for 16
+# vectors (enough for every skinny launch of the shape, too small for the column-split
+# prefill kernel); a ragged last split (2080 columns = 16.25 lines over 4)
+MULTI_CASES = [((2, 4), 1000, 8192, 17), ((4, 8), 777, 2080, 31), ((2, 4), 256, 5120, 31), ((2, 4), 1024, 5120, 20)]
+
+
+@pytest.mark.parametrize("pat,R,C,T", MULTI_CASES)
+def test_skinny_column_split_several_launches(pat, R, C, T):
+    N, M = pat
+    ws = nm.spmm_workspace(R, C, 16, N, M)
+    assert ws is not None and ws.numel() < nm.spmm_workspace_bytes(R, C, T, N, M), (R, C, T)
+    say(f"skinny split launches {N}:{M} {R}x{C} vectors={T} workspace={ws.numel()}")
+    check(R, C, T, 3450 + R % 97 + C % 89 + T + N, N, M,
+          fn=lambda v, m, x, n, mm: nm.nm_spmm_ws(v, m, x, n, mm, ws))
+    assert int(ws[:_counter_bytes()].count_nonzero()) == 0
+
+
 def test_skinny_column_split_small_workspace_runs_unsplit():
     """A workspace smaller than nm_spmm_workspace_bytes (or none) runs nm_spmm's kernels:
     bit-identical to nm_spmm; shapes without a split need no workspace."""
@@ -231,12 +250,14 @@ def test_skinny_column_split_small_workspace_runs_unsplit():
     assert np.array_equal(down_bits16(nm.nm_spmm_ws(v, m, X, N, M, small)), want)
     assert np.array_equal(down_bits16(nm.nm_spmm_ws(v, m, X, N, M, None)), want)
     assert int(small.count_nonzero()) == 0
-    # no split: 16:32 (expanded fragments), fewer than 5 vectors, layers that fill the GPU,
-    # the prefill sizes, and where the hand-off costs more than it saves (2:4 rows of 32 lines)
+    # no split: 16:32 (expanded fragments; at any batch), fewer than 5 vectors, layers that
+    # fill the GPU, prompts whose prefill grid fills it, and where the hand-off costs more
+    # than it saves (2:4 rows of 32 lines)
     assert nm.spmm_workspace_bytes(4096, 4096, 16, 16, 32) == 0
+    assert nm.spmm_workspace_bytes(4096, 4096, 64, 16, 32) == 0
     assert nm.spmm_workspace_bytes(1024, 8192, 4, 2, 4) == 0
     assert nm.spmm_workspace_bytes(4096, 8192, 8, 2, 4) == 0
-    assert nm.spmm_workspace_bytes(1024, 8192, 64, 2, 4) == 0
+    assert nm.spmm_workspace_bytes(4096, 4096, 2048, 2, 4) == 0
     assert nm.spmm_workspace_bytes(1024, 4096, 16, 2, 4) == 0
     assert nm.spmm_workspace_bytes(2048, 4096, 16, 4, 8) == 0
     assert nm.spmm_workspace_bytes(1024, 5120, 5, 2, 4) == 0
@@ -265,17 +286,16 @@ def test_skinny_column_split_shared_workspace():
         assert np.array_equal(got, want), ((N, M), R, C, T)
 
 
-# boundaries of the column split: 128 tiles (half the CUs of a 256-CU part: 2 splits) against
-# 129 (none); batch 5 (first skinny size), 31 and 48 (two and three split launches on a
-# 1024-row layer) and 49 (prefill route, no workspace); a workspace of exactly
-# nm_spmm_workspace_bytes
-@pytest.mark.parametrize("R,C,T,N,M", [(2048, 8192, 5, 2, 4), (2064, 8192, 8, 2, 4), (2048, 8192, 31, 8, 16),
-                                       (1024, 8192, 48, 2, 4), (1024, 8192, 49, 2, 4), (1040, 14336, 16, 2, 4)])
+# boundaries of the skinny column split: 128 tiles (half the CUs of a 256-CU part: 2 splits)
+# against 129 (none); batch 5 (first skinny size) and 16 (one full launch); a workspace of
+# exactly nm_spmm_workspace_bytes
+@pytest.mark.parametrize("R,C,T,N,M", [(2048, 8192, 5, 2, 4), (2064, 8192, 8, 2, 4), (2048, 8192, 16, 8, 16),
+                                       (1040, 14336, 16, 2, 4)])
 def test_skinny_column_split_boundaries(R, C, T, N, M):
     need = nm.spmm_workspace_bytes(R, C, T, N, M)
     cus = torch.cuda.get_device_properties(device()).multi_processor_count
     tiles = -(-R // 16)
-    if T > 48 or 2 * tiles > cus:
+    if 2 * tiles > cus:
         assert need == 0, (R, C, T, need)
     else:
         assert need > 0, (R, C, T)

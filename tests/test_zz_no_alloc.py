@@ -39,7 +39,8 @@ def _oracle_ok(W, X, Y, N, M):
 PAIRS = [
     (((2, 4), 2048, 14336, 16), ((2, 4), 1024, 8192, 8)),     # 2 splits x 128 tiles, then 4 x 64
     (((8, 16), 1024, 4096, 12), ((4, 8), 512, 4096, 9)),      # the split patterns: 4 x 64, then 8 x 32
-    (((2, 4), 1000, 8192, 17), ((2, 4), 300, 8224, 6)),       # two launches, ragged rows; a ragged last split
+    (((2, 4), 1000, 8192, 17), ((2, 4), 300, 8224, 6)),       # column-split prefill kernel; skinny, ragged
+    (((4, 8), 4096, 14336, 40), ((2, 4), 1024, 4096, 20)),    # column-split prefill: 7 x 64 tiles, then 8 x 16
 ]
 
 
@@ -66,7 +67,7 @@ def test_noalloc_repeated_calls_are_identical():
 
 
 @pytest.mark.parametrize("pat,R,C,T", [((2, 4), 4096, 4096, 8), ((16, 32), 4096, 4096, 12), ((2, 4), 1024, 4096, 4),
-                                       ((8, 16), 1024, 4096, 64), ((2, 4), 2048, 2048, 1)])
+                                       ((8, 16), 4096, 4096, 1024), ((2, 4), 2048, 2048, 1)])
 def test_noalloc_unsplit_routes_match_nm_spmm(pat, R, C, T):
     """Shapes that take no column split (large layers, 16:32, fewer than 5 vectors, prefill
     sizes, one vector) run nm_spmm's kernels: bit-identical Y."""
