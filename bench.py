@@ -904,8 +904,10 @@ def decode_roofline(nm, items, ms_token, N, M):
 def prefill_main(args, torch, nm, synth, dev):
     """Prefill: the Llama-3.1-8B projection shapes (q, kv, gate_up, down) as 2:4 packed
     weights (or the first of --patterns: 4:8 or 8:16, as two 2:4 operands) times a prompt of
-    --prompt tokens (X [tokens][cols], seeded N(0,1)), on the sparse matrix cores
-    (nm_spmm_prefill); a step is one pass over the four products. Also
+    --prompt tokens (X [tokens][cols], seeded N(0,1)), on the sparse matrix cores (nm_spmm_ws
+    with a workspace per layer: the prefill kernel, whose output tiles' columns are split
+    over several workgroups where the prompt is too short for the tiles to fill the GPU); a
+    step is one pass over the four products. Also
     timed: the dense matrix-core product over the same dense weights (nm_gemm_dense_prefill)
     and, as context only, torch.mm (the vendor BLAS) on the same shapes.
 
@@ -924,7 +926,6 @@ def prefill_main(args, torch, nm, synth, dev):
             print(f"prefill: pattern {pat} has no matrix-core product (2:4, 4:8, 8:16)", file=sys.stderr)
             sys.exit(2)
     N, M = pat
-    split = pat != (2, 4)
     t_gen = time.time()
     items = []
     for li, (name, R, C) in enumerate(shapes):
@@ -934,21 +935,22 @@ def prefill_main(args, torch, nm, synth, dev):
         Xd = torch.from_numpy(X).to(dev)
         values, masks = nm.nm_pack(Wd, N, M)
         items.append(dict(name=name, R=R, C=C, W=Wd, Wt=Wd.t().contiguous(), X=Xd, X_host=X, values=values,
-                          masks=masks, Y=torch.empty((T, R), dtype=torch.float16, device=dev),
+                          masks=masks, ws=nm.spmm_workspace(R, C, T, N, M, device=dev),
+                          Y=torch.empty((T, R), dtype=torch.float16, device=dev),
                           Yd=torch.empty((T, R), dtype=torch.float16, device=dev),
                           W_cpu=W, flops_useful=R * C * T, flops_dense=2 * R * C * T))
         del W
     torch.cuda.synchronize()
     log(f"prefill: generated and packed {len(items)} layers x {T} tokens in {time.time() - t_gen:.1f}s")
     sp_a = [(q["values"].data_ptr(), q["masks"].data_ptr(), q["X"].data_ptr(), q["Y"].data_ptr(), q["R"], q["C"],
-             T, N, M) for q in items]
+             T, N, M) + ((None, 0) if q["ws"] is None else (q["ws"].data_ptr(), q["ws"].numel())) for q in items]
     dn_a = [(q["W"].data_ptr(), q["X"].data_ptr(), q["Yd"].data_ptr(), q["R"], q["C"], T) for q in items]
 
     def sp_step(s_):
         for a in sp_a:
-            st = lib.nm_spmm_prefill(*a, s_)
+            st = lib.nm_spmm_ws(*a, s_)
             if st:
-                raise RuntimeError(f"nm_spmm_prefill: {nm.status_string(st)}")
+                raise RuntimeError(f"nm_spmm_ws: {nm.status_string(st)}")
 
     def dn_step(s_):
         for a in dn_a:
@@ -992,7 +994,7 @@ def prefill_main(args, torch, nm, synth, dev):
     # per layer: each product alone, 20 launches in a graph, median of 3 replays
     per_layer = []
     for i, q in enumerate(items):
-        us_s = graph_ms(lambda s_, a=sp_a[i]: lib.nm_spmm_prefill(*a, s_), 20, 3) * 1e3
+        us_s = graph_ms(lambda s_, a=sp_a[i]: lib.nm_spmm_ws(*a, s_), 20, 3) * 1e3
         us_d = graph_ms(lambda s_, a=dn_a[i]: lib.nm_gemm_dense_prefill(*a, s_), 20, 3) * 1e3
         Wt, Xd = q["Wt"], q["X"]
         try:   # context only: the vendor BLAS on the same dense product
@@ -1001,8 +1003,9 @@ def prefill_main(args, torch, nm, synth, dev):
             log(f"torch.mm timing unavailable: {e}")
             us_t = float("nan")
         per_layer.append({"layer": q["name"], "shape": f"{q['R']}x{q['C']}", "tokens": T,
-                          "kernel": nm.prefill_variant(q["R"], q["C"], T, True, split=split),
+                          "kernel": nm.spmm_ws_variant(q["R"], q["C"], T, N, M),
                           "us": round(us_s, 2), "useful_TFLOPs": round(q["flops_useful"] / us_s / 1e6, 1),
+                          "alg_GBs": round(alg_bytes_sparse(q["R"], q["C"], N, M, T) / us_s / 1e3, 1),
                           "dense_equiv_TFLOPs": round(q["flops_dense"] / us_s / 1e6, 1),
                           "dense_kernel": nm.prefill_variant(q["R"], q["C"], T, False),
                           "dense_us": round(us_d, 2), "dense_TFLOPs": round(q["flops_dense"] / us_d / 1e6, 1),
