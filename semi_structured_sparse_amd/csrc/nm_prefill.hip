@@ -13,17 +13,12 @@ namespace {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Tile shapes (TR x TT output tiles of 16 x 16 per wave, KS columns per step, loads D steps
-// ahead), from sweeps on MI355X over 4096..14336 rows and columns at 2048 tokens. Large
-// tiles: the sparse product 256 rows x 128 tokens per workgroup (each X fragment serves 4
-// row tiles), the dense one 128 x 256 (each weight fragment serves 16 token tiles); each was
-// the fastest for its kernel. The sparse product takes 256 x 256 when that grid still has
-// a workgroup per CU (14336 x 4096 x 2048: 247 against 294 us; with fewer workgroups it
-// loses: 4096 x 4096 x 2048: 102 against 71 us). The small tile (64 x 64) serves problems
-// whose large-tile grid would leave CUs idle.
-using SparseHuge = Tile<4, 16, 64>;   // 256 rows x 256 tokens: when even this grid fills the CUs
-using SparseLarge = Tile<4, 8, 64>;
+// ahead). Dense: 128 rows x 256 tokens per workgroup (each weight fragment serves 16 token
+// tiles) where the grid has a workgroup per CU, else 64 x 64. Sparse: the tile with the least
+// modelled time (sparse_tile), from 64 x 64 up to 256 x 256.
 using DenseLarge = Tile<2, 16, 64>;
 using Small = Tile<1, 4, 64>;
+using SparseLarge = Tile<4, 8, 64>;
 constexpr int kDepth = 2;
 
 template <typename T>
@@ -35,6 +30,55 @@ template <typename T>
 bool use_large(int64_t rows, int64_t tokens, const DeviceInfo& dev) {
   const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
   return workgroups<T>(rows, tokens) >= cus;
+}
+
+// Sparse tile choice. A workgroup's time is its 64-column steps times the time of a step,
+// which grows with the workgroups n = ceil(grid / CUs) that share a CU: t1 + (n - 1) * tn
+// (us; where fewer of them fit a CU at once the later ones wait, so tn >= t1 there). Fitted
+// per tile to sweeps on MI355X (256 .. 4096 tokens, 1024 .. 14336 rows and columns; the model
+// is within about 15% of every measured time and picks the fastest tile or one within 7% of
+// it): 14336 x 4096 x 512, 2:4, 58.6 us on 256 x 128 against 119.2 on 64 x 64; 4096 x 14336 x
+// 1024, 125.6 on 128 x 128 against 219.7; 4:8 at 4096 x 4096 x 2048, 96.3 on 128 x 256
+// against 116.4 on 256 x 128. The split patterns' steps cost more (two instructions and the
+// table lookups per fragment), so their wide token tiles pay off sooner.
+struct TileCost {
+  int tr, tt;
+  double t1, tn;
+};
+constexpr TileCost kDirectTiles[] = {{1, 4, 0.266, 0.210}, {2, 4, 0.378, 0.328}, {2, 8, 0.537, 0.475},
+                                     {4, 8, 0.717, 0.825}, {4, 16, 1.27, 1.38}};
+constexpr TileCost kSplitTiles[] = {{1, 4, 0.45, 0.273},  {2, 4, 0.68, 0.443}, {2, 8, 0.91, 0.693},
+                                    {4, 8, 1.57, 1.57},   {2, 16, 1.40, 1.42}, {4, 16, 2.28, 2.37}};
+
+TileCost sparse_tile(int64_t rows, int64_t tokens, bool split, const DeviceInfo& dev) {
+  const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
+  const TileCost* c = split ? kSplitTiles : kDirectTiles;
+  const int n = split ? int(sizeof(kSplitTiles) / sizeof(TileCost)) : int(sizeof(kDirectTiles) / sizeof(TileCost));
+  TileCost best = c[0];
+  double best_t = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t grid = ceil_div(rows, 64 * c[i].tr) * ceil_div(tokens, 16 * c[i].tt);
+    const double t = c[i].t1 + double(ceil_div(grid, cus) - 1) * c[i].tn;
+    if (i == 0 || t < best_t) {
+      best = c[i];
+      best_t = t;
+    }
+  }
+  return best;
+}
+
+template <int TR, int TT>
+const void* sparse_kernel(bool split) {
+  return split ? reinterpret_cast<const void*>(&prefill_split_kernel<TR, TT, 64, kDepth>)
+               : reinterpret_cast<const void*>(&prefill_spmm_kernel<TR, TT, 64, kDepth>);
+}
+
+const void* sparse_kernel_of(const TileCost& t, bool split) {
+  if (t.tr == 1) return sparse_kernel<1, 4>(split);
+  if (t.tr == 2) return t.tt == 4 ? sparse_kernel<2, 4>(split)
+                        : t.tt == 8 ? sparse_kernel<2, 8>(split)
+                                    : reinterpret_cast<const void*>(&prefill_split_kernel<2, 16, 64, kDepth>);
+  return t.tt == 8 ? sparse_kernel<4, 8>(split) : sparse_kernel<4, 16>(split);
 }
 
 }  // namespace
@@ -113,17 +157,9 @@ hipError_t launch_prefill_spmm(const uint16_t* values, const uint32_t* masks, co
                   dim3(unsigned(p.tiles * p.splits)), dim3(kThreads), cargs, 0, stream, dev);
   }
   void* args[] = {&values, &masks, &X, &Y, &r, &c, &t};
-  if (use_large<SparseHuge>(rows, tokens, dev))
-    return launch(split ? reinterpret_cast<const void*>(&prefill_split_kernel<4, 16, 64, kDepth>)
-                        : reinterpret_cast<const void*>(&prefill_spmm_kernel<4, 16, 64, kDepth>),
-                  dim3(unsigned(workgroups<SparseHuge>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
-  if (use_large<SparseLarge>(rows, tokens, dev))
-    return launch(split ? reinterpret_cast<const void*>(&prefill_split_kernel<4, 8, 64, kDepth>)
-                        : reinterpret_cast<const void*>(&prefill_spmm_kernel<4, 8, 64, kDepth>),
-                  dim3(unsigned(workgroups<SparseLarge>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
-  return launch(split ? reinterpret_cast<const void*>(&prefill_split_kernel<1, 4, 64, kDepth>)
-                      : reinterpret_cast<const void*>(&prefill_spmm_kernel<1, 4, 64, kDepth>),
-                dim3(unsigned(workgroups<Small>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
+  const TileCost tc = sparse_tile(rows, tokens, split, dev);
+  const int64_t grid = ceil_div(rows, 64 * tc.tr) * ceil_div(tokens, 16 * tc.tt);
+  return launch(sparse_kernel_of(tc, split), dim3(unsigned(grid)), dim3(kThreads), args, 0, stream, dev);
 }
 
 hipError_t launch_prefill_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y, int64_t rows, int64_t cols,
@@ -147,14 +183,22 @@ const char* prefill_colsplit_variant(int64_t rows, int64_t cols, int64_t tokens,
 }
 
 const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev, bool split) {
-  if (sparse && split)
-    return use_large<SparseHuge>(rows, tokens, dev)    ? "prefill_split_kernel<4, 16, 64, 2>"
-           : use_large<SparseLarge>(rows, tokens, dev) ? "prefill_split_kernel<4, 8, 64, 2>"
-                                                       : "prefill_split_kernel<1, 4, 64, 2>";
-  if (sparse)
-    return use_large<SparseHuge>(rows, tokens, dev)    ? "prefill_spmm_kernel<4, 16, 64, 2>"
-           : use_large<SparseLarge>(rows, tokens, dev) ? "prefill_spmm_kernel<4, 8, 64, 2>"
-                                                       : "prefill_spmm_kernel<1, 4, 64, 2>";
+  if (sparse) {
+    static const char* const kNames[2][5][3] = {
+        {{"prefill_spmm_kernel<1, 4, 64, 2>", "", ""},
+         {"prefill_spmm_kernel<2, 4, 64, 2>", "prefill_spmm_kernel<2, 8, 64, 2>", ""},
+         {"", "", ""},
+         {"prefill_spmm_kernel<4, 8, 64, 2>", "prefill_spmm_kernel<4, 16, 64, 2>", ""},
+         {"", "", ""}},
+        {{"prefill_split_kernel<1, 4, 64, 2>", "", ""},
+         {"prefill_split_kernel<2, 4, 64, 2>", "prefill_split_kernel<2, 8, 64, 2>", "prefill_split_kernel<2, 16, 64, 2>"},
+         {"", "", ""},
+         {"prefill_split_kernel<4, 8, 64, 2>", "prefill_split_kernel<4, 16, 64, 2>", ""},
+         {"", "", ""}}};
+    const TileCost t = sparse_tile(rows, tokens, split, dev);
+    const int col = t.tr == 1 ? 0 : t.tr == 2 ? (t.tt == 4 ? 0 : t.tt == 8 ? 1 : 2) : (t.tt == 8 ? 0 : 1);
+    return kNames[split ? 1 : 0][t.tr - 1][col];
+  }
   return use_large<DenseLarge>(rows, tokens, dev) ? "prefill_gemm_kernel<2, 16, 64, 2>"
                                                   : "prefill_gemm_kernel<1, 4, 64, 2>";
 }
