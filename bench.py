@@ -338,6 +338,23 @@ def per_layer_times(torch, nm, layers, dense, B, pool_bytes, launches, ceiling=N
         per_d[(D["R"], D["C"])] = graph_us_per_launch(
             torch, lambda c, sp, A=argsets: dn_call(*A[c % len(A)], sp), launches)
         del pool
+    # batches: the vendor BLAS on the same dense product too (torch.mm on a transposed copy of
+    # W, rotated the same way), so that each layer's speedup can be quoted against the faster
+    # dense product
+    per_t = {}
+    if B > 1:
+        for D in dense.values():
+            Xb = D["x"].view(B, D["C"])
+            pool = rotation([D["W"][0].t().contiguous()], D["bytes"])
+            try:
+                for P in pool:   # eager first calls: the BLAS sets itself up outside the capture
+                    torch.mm(Xb, P[0])
+                torch.cuda.synchronize()
+                per_t[(D["R"], D["C"])] = graph_us_per_launch(
+                    torch, lambda c, sp, P=pool, Xb=Xb: torch.mm(Xb, P[c % len(P)][0]), launches)
+            except Exception as e:  # pragma: no cover
+                log(f"torch.mm timing unavailable: {e}")
+            del pool
     torch.cuda.synchronize()
     rows = []
     for L, us in zip(layers, per_s):
@@ -354,6 +371,10 @@ def per_layer_times(torch, nm, layers, dense, B, pool_bytes, launches, ceiling=N
             rec["workgroup"] = f"{ls['rows_per_workgroup']} rows, {ls['row_groups']}x{ls['waves_per_row_group']} waves"
         rec.update({"us": round(us, 2), "GBps": round(gbps, 1), "pct_peak": round(gbps / HBM_PEAK_GBPS, 4),
                     "dense_us": round(dus, 2), "speedup": round(dus / us, 3)})
+        tus = per_t.get((L["R"], L["C"]))
+        if tus is not None:
+            rec.update({"torch_mm_us": round(tus, 2), "best_dense_us": round(best_dense_us(dus, tus), 2),
+                        "speedup_vs_best_dense": round(best_dense_us(dus, tus) / us, 3)})
         if ceiling is not None:
             att, shape = ceiling.attainable_us(L["bytes"])
             rec["attainable_us"] = round(att, 2)
@@ -621,6 +642,9 @@ def main():
                   "rotation, in a graph, median of 5 replays; attainable_us: the fastest shape of the "
                   "read probe reading the layer's bytes in one launch, timed the same way",
         "per_layer": per_layer + more,
+        "speedup_vs_best_dense_per_layer_sum": (
+            round(sum(r["best_dense_us"] for r in per_layer) / sum(r["us"] for r in per_layer), 3)
+            if per_layer and all("best_dense_us" in r for r in per_layer) else None),
         "pattern_spread": pattern_spread(per_layer),
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -147,11 +147,13 @@ int nm_gemv_dense(const uint16_t* W, const uint16_t* x, uint16_t* y,
  *     smaller ones from 9 or 12 vectors): nm_spmm_skinny, 16 vectors per launch, each
  *     launch routed by the same rule at its own count (17..20 vectors: the last 1..4 on
  *     the small-batch kernel).
- *   - 16:32 from 5 vectors (any batch: it has no prefill kernel), per launch of up to 16
- *     vectors: nm_spmm_skinny's expansion kernel for a launch of at least 14 vectors on
- *     layers of at least 2048 rows (4096 if wider than 4096 columns), or of at least 12 on
- *     layers of at least 4096 rows and at most 4096 columns; the small-batch kernel for the
- *     other launches (e.g. 24 vectors: one launch of 16 expanded, 8 on the small-batch one).
+ *   - 16:32 from 64 vectors: nm_spmm_prefill (fragments expanded for the dense matrix
+ *     instruction), with its limits.
+ *   - 16:32 from 5 to 63 vectors, per launch of up to 16 vectors: nm_spmm_skinny's
+ *     expansion kernel for a launch of at least 14 vectors on layers of at least 2048 rows
+ *     (4096 if wider than 4096 columns), or of at least 12 on layers of at least 4096 rows
+ *     and at most 4096 columns; the small-batch kernel for the other launches (e.g. 24
+ *     vectors: one launch of 16 expanded, 8 on the small-batch one).
  *   - otherwise the small-batch kernel (vector units; x staged in LDS in column phases
  *     when it does not fit at once, so any width is accepted), on consecutive groups of
  *     8 rows of X (one launch per group). batch == 1 gives the same result as nm_spmv
@@ -168,7 +170,7 @@ int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, ui
  *   - skinny launches (50% patterns at 5..16 vectors per launch, nm_spmm's route) on layers
  *     too short to fill the GPU (e.g. 1024 rows): the columns of each 16-row tile go to 2, 4
  *     or 8 workgroups;
- *   - 2:4, 4:8 and 8:16 batches of more than 16 vectors whose output tiles of 64 rows x 32
+ *   - batches of more than 16 vectors (any 50% pattern) whose output tiles of 64 rows x 32
  *     (up to 32 vectors) or 64 vectors are too few to fill the GPU (mid-size batches: e.g.
  *     up to 256 tokens on 4096 x 4096): instead of nm_spmm's route, one launch of the
  *     prefill kernel with each tile's columns split over 2 .. 8 workgroups, whole blocks of
@@ -232,10 +234,13 @@ int nm_gemm_dense(const uint16_t* W, const uint16_t* X, uint16_t* Y,
  * sparse matrix hardware speeds inference up, and the bitmask format): for tokens >= 1
  * rows of X,
  *   Y[t][r] = fp16( sum_c W'[r][c] * X[t][c] ),  X fp16 [tokens][cols], Y fp16 [tokens][rows],
- * with the (values, masks) of nm_pack for (N, M) = (2, 4), (4, 8) or (8, 16) (others are
- * NM_ERR_PATTERN). 2:4 runs on the 2:4 sparse instruction directly; 4:8 and 8:16, which
- * keep 8 values in every 16 columns, as two 2:4 operands per 4-column group (its first two
- * kept values, and the rest), so at twice the instruction count. fp16 products, fp32 sums
+ * with the (values, masks) of nm_pack for a 50% pattern, (N, M) = (2, 4), (4, 8), (8, 16) or
+ * (16, 32) (others are NM_ERR_PATTERN). 2:4 runs on the 2:4 sparse instruction directly; 4:8
+ * and 8:16, which keep 8 values in every 16 columns, as two 2:4 operands per 4-column group
+ * (its first two kept values, and the rest), so at twice the instruction count; 16:32, whose
+ * 16 kept values may sit anywhere in a word's 32 columns, on the dense instruction with each
+ * lane's 8 columns expanded from its mask byte ([KERNEL]: the bitmask gives every kept
+ * value's column). fp16 products, fp32 sums
  * in the matrix instruction's order (fixed, so bit-identical run to run), one RNE
  * rounding. Limits: cols <= 2^21, tokens <= 2^24 (NM_ERR_SHAPE beyond). Masks must be as
  * nm_pack writes them; a malformed mask gives an unspecified Y but never an out-of-bounds
@@ -260,7 +265,8 @@ const char* nm_spmm_variant(int64_t rows, int64_t cols, int64_t batch, int N, in
 const char* nm_spmm_ws_variant(int64_t rows, int64_t cols, int64_t batch, int N, int M);
 
 /* Introspection: the name of the kernel configuration nm_spmm_prefill (sparse == 1: 2:4;
- * sparse == 2: 4:8 or 8:16) or nm_gemm_dense_prefill (sparse == 0) launches for this shape
+ * sparse == 2: 4:8 or 8:16; sparse == 3: 16:32) or nm_gemm_dense_prefill (sparse == 0)
+ * launches for this shape
  * on the current device, as it appears in profiler traces (for example
  * "prefill_spmm_kernel<4, 8, 64, 2>"); "" if the arguments are invalid. Static string,
  * never NULL. */

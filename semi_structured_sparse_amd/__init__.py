@@ -315,10 +315,12 @@ def spmm_ws_variant(rows: int, cols: int, batch: int, N: int, M: int) -> str:
     return lib().nm_spmm_ws_variant(rows, cols, batch, N, M).decode()
 
 
-def prefill_variant(rows: int, cols: int, tokens: int, sparse: bool, split: bool = False) -> str:
-    """Kernel configuration nm_spmm_prefill (sparse; split: for 4:8 / 8:16) or
-    nm_gemm_dense_prefill launches."""
-    return lib().nm_prefill_variant(rows, cols, tokens, (2 if split else 1) if sparse else 0).decode()
+def prefill_variant(rows: int, cols: int, tokens: int, sparse: bool, split: bool = False,
+                    expand: bool = False) -> str:
+    """Kernel configuration nm_spmm_prefill (sparse; split: for 4:8 / 8:16; expand: for
+    16:32) or nm_gemm_dense_prefill launches."""
+    code = (3 if expand else 2 if split else 1) if sparse else 0
+    return lib().nm_prefill_variant(rows, cols, tokens, code).decode()
 
 
 def _batch_args(values, masks, X, N, M, out):
@@ -415,8 +417,8 @@ def nm_spmm_skinny(values, masks, X, N: int, M: int, out=None):
 
 
 def nm_spmm_prefill(values, masks, X, N: int = 2, M: int = 4, out=None):
-    """Prefill product Y = X W'^T of a 2:4, 4:8 or 8:16 packed matrix on the sparse matrix
-    cores: X fp16 [tokens, cols] -> Y fp16 [tokens, rows]."""
+    """Prefill product Y = X W'^T of a 50% packed matrix (2:4, 4:8, 8:16 or 16:32) on the
+    matrix cores: X fp16 [tokens, cols] -> Y fp16 [tokens, rows]."""
     torch = _torch()
     rows, cols, tokens, out = _batch_args(values, masks, X, N, M, out)
     with torch.cuda.device(X.device):

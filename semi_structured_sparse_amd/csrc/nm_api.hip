@@ -87,8 +87,10 @@ hipError_t launch(const void* kernel, dim3 grid, dim3 block, void** args, size_t
 // 26.3; 4096 x 14336 44.6 / 65.0 / 84.8 against 82; 8192 x 8192 40.4 / 59.7 against 51;
 // 14336 x 4096 32.7 against 27.9 already at 32. So: up to 48 vectors on layers of at most
 // 4096 rows, up to 32 on layers of at most 8192, where the skinny kernels take the layer.
+int64_t prefill_min_batch(int N) { return N == 16 ? kExpandPrefillMinBatch : kMatrixCoreMinBatch; }
+
 bool prefill_route(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev) {
-  if (batch < kMatrixCoreMinBatch || !prefill_pattern(N, M)) return false;
+  if (!prefill_pattern(N, M) || batch < prefill_min_batch(N)) return false;
   const bool short_batch = (batch <= kSkinnyBeforePrefillMaxBatch && rows <= kSkinnyBeforePrefillMaxRows) ||
                            (batch <= kMatrixCoreMinBatch && rows <= 2 * kSkinnyBeforePrefillMaxRows);
   return !(short_batch && use_skinny(rows, cols, kSkinnyBatch, N, M, dev));
@@ -112,7 +114,7 @@ int spmm_check(const uint16_t* values, const uint32_t* masks, const uint16_t* X,
   if (!aligned(values, 16) || !aligned(masks, 4) || !aligned(X, 16) || !aligned(Y, 2)) return NM_ERR_ALIGN;
   // beyond 2^21 columns no skinny launch fits, so such batches go to the prefill kernels,
   // whose limit this is
-  if (batch >= kMatrixCoreMinBatch && prefill_pattern(N, M) && cols > kPrefillMaxCols) return NM_ERR_SHAPE;
+  if (prefill_pattern(N, M) && batch >= prefill_min_batch(N) && cols > kPrefillMaxCols) return NM_ERR_SHAPE;
   return NM_OK;
 }
 
@@ -387,7 +389,7 @@ const char* nm_spmm_variant(int64_t rows, int64_t cols, int64_t batch, int N, in
   if (nm::current_device_info(&dev) != hipSuccess) return "";
   if (batch == 1 && cols <= nm::max_cols_for(dev)) return nm::spmv_variant(rows, cols, N, M, dev);
   if (nm::prefill_route(rows, cols, batch, N, M, dev))
-    return nm::prefill_fits(rows, cols, batch) ? nm::prefill_variant(rows, batch, true, dev, N != 2) : "";
+    return nm::prefill_fits(rows, cols, batch) ? nm::prefill_variant(rows, batch, true, dev, N) : "";
   if (N == 16 && batch >= nm::kSkinnyMinBatch &&
       nm::skinny_expand_chunk(rows, cols, batch < nm::kSkinnyBatch ? batch : nm::kSkinnyBatch, dev))
     return nm::skinny_variant(N);
@@ -401,7 +403,7 @@ const char* nm_spmm_ws_variant(int64_t rows, int64_t cols, int64_t batch, int N,
   if (*v == '\0') return v;
   nm::DeviceInfo dev;
   if (nm::current_device_info(&dev) != hipSuccess) return "";
-  if (nm::colsplit_route(rows, cols, batch, N, M, dev)) return nm::prefill_colsplit_variant(rows, cols, batch, dev, N != 2);
+  if (nm::colsplit_route(rows, cols, batch, N, M, dev)) return nm::prefill_colsplit_variant(rows, cols, batch, dev, N);
   const int nb = int(batch < nm::kSkinnyBatch ? batch : nm::kSkinnyBatch);
   if (N != 16 && std::strcmp(v, nm::skinny_variant(N)) == 0 && nm::skinny_workspace_bytes(rows, cols, nb, N, dev) > 0)
     return N == 2 ? "skinny_colsplit_kernel<false>" : "skinny_colsplit_kernel<true>";
@@ -412,7 +414,7 @@ const char* nm_prefill_variant(int64_t rows, int64_t cols, int64_t tokens, int s
   if (!nm::valid_shape(rows, cols) || tokens < 1 || !nm::prefill_fits(rows, cols, tokens)) return "";
   nm::DeviceInfo dev;
   if (nm::current_device_info(&dev) != hipSuccess) return "";
-  return nm::prefill_variant(rows, tokens, sparse != 0, dev, sparse == 2);
+  return nm::prefill_variant(rows, tokens, sparse != 0, dev, sparse == 3 ? 16 : sparse == 2 ? 4 : 2);
 }
 
 const char* nm_spmv_variant(int64_t rows, int64_t cols, int N, int M) {

@@ -81,12 +81,13 @@ WorkgroupShape dense_shape(int64_t rows, int64_t cols, const DeviceInfo& dev);
 int64_t max_cols_for(const DeviceInfo& dev);
 
 // Prefill-sized products on the matrix cores: X [tokens][cols], Y [tokens][rows]. The
-// sparse one takes 2:4 packed weights only. Limits: cols <= kPrefillMaxCols (byte offsets
+// sparse one takes the 50% patterns: 2:4 on the sparse instruction, 4:8 and 8:16 as two 2:4
+// operands, 16:32 expanded to dense fragments. Limits: cols <= kPrefillMaxCols (byte offsets
 // inside a workgroup's slices are 32-bit), tokens <= kPrefillMaxTokens.
 constexpr int64_t kPrefillMaxCols = int64_t(1) << 21;
 constexpr int64_t kPrefillMaxTokens = int64_t(1) << 24;
 bool prefill_fits(int64_t rows, int64_t cols, int64_t tokens);
-// 50% patterns with a matrix-core product: 2:4, and 4:8 / 8:16 as two 2:4 operands.
+// 50% patterns with a matrix-core prefill product: all four.
 bool prefill_pattern(int n, int m);
 // With a workspace of at least prefill_workspace_bytes (0: the shape takes no column split)
 // a grid too small for the CUs (mid-size batches) splits each output tile's columns over
@@ -143,6 +144,10 @@ constexpr int64_t kSkinnyExpandFullChunk = 14;     // vectors of a nearly full 1
 // Batches of 32 .. kSkinnyBeforePrefillMaxBatch vectors stay on skinny launches on layers of
 // at most kSkinnyBeforePrefillMaxRows rows (32 vectors up to twice that), see prefill_route.
 constexpr int64_t kSkinnyBeforePrefillMaxBatch = 48;
+// 16:32 takes the prefill kernels (expanded fragments) from this batch on: below it, its
+// 16-vector launches are as fast (4096 x 4096 at 32 vectors: 28.8 us against about 51 for one
+// launch of 64 x 64 tiles walking every column; at 64 vectors 55.7 against 51).
+constexpr int64_t kExpandPrefillMinBatch = 64;
 constexpr int64_t kSkinnyBeforePrefillMaxRows = 4096;
 constexpr int64_t kSkinnyExpandFullMinRows = 2048;
 bool use_skinny(int64_t rows, int64_t cols, int64_t batch, int n, int m, const DeviceInfo& dev);
@@ -164,14 +169,17 @@ size_t spmm_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, int N, in
 
 // Whether nm_spmm runs a batch on the prefill kernels (else on skinny or small-batch launches).
 bool prefill_route(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev);
+// The smallest batch nm_spmm runs on the prefill kernels for pattern N (32; 16:32: 64).
+int64_t prefill_min_batch(int N);
 // Whether nm_spmm_ws, given a workspace of prefill_workspace_bytes, runs a batch on the
 // column-split prefill kernel: 2:4, 4:8 and 8:16 batches of more than kSkinnyBatch vectors
 // whose small-tile grid leaves CUs idle.
 bool colsplit_route(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev);
 
 // Name of the kernel configuration the prefill launchers pick (static string).
-const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev, bool split = false);
+// (sparse: n = the pattern's N, 2, 4, 8 or 16)
+const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev, int n = 2);
 // The column-split kernel launch_prefill_spmm runs with a workspace ("" if none).
-const char* prefill_colsplit_variant(int64_t rows, int64_t cols, int64_t tokens, const DeviceInfo& dev, bool split);
+const char* prefill_colsplit_variant(int64_t rows, int64_t cols, int64_t tokens, const DeviceInfo& dev, int n);
 
 }  // namespace nm

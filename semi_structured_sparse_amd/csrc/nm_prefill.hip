@@ -49,11 +49,21 @@ constexpr TileCost kDirectTiles[] = {{1, 4, 0.266, 0.210}, {2, 4, 0.378, 0.328},
                                      {4, 8, 0.717, 0.825}, {4, 16, 1.27, 1.38}};
 constexpr TileCost kSplitTiles[] = {{1, 4, 0.45, 0.273},  {2, 4, 0.68, 0.443}, {2, 8, 0.91, 0.693},
                                     {4, 8, 1.57, 1.57},   {2, 16, 1.40, 1.42}, {4, 16, 2.28, 2.37}};
+// 16:32's steps expand each word's fragments through LDS first (about twice the split
+// patterns' step time). It has no 256-row tiles: 256 x 128 (2.62 us a step) lost to
+// 128 x 256 at every measured size, and 256 x 256 would spill its expansion registers.
+constexpr TileCost kExpandTiles[] = {{1, 4, 0.80, 0.51}, {2, 4, 1.28, 0.93}, {2, 8, 1.46, 1.09},
+                                     {2, 16, 1.85, 1.83}};
 
-TileCost sparse_tile(int64_t rows, int64_t tokens, bool split, const DeviceInfo& dev) {
+// the kernel family of a 50% pattern: 2:4 direct, 4:8 / 8:16 split, 16:32 expanded
+int pf_mode(int n) { return n == 2 ? kPfDirect : n == 16 ? kPfExpand : kPfSplit; }
+
+TileCost sparse_tile(int64_t rows, int64_t tokens, int mode, const DeviceInfo& dev) {
   const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
-  const TileCost* c = split ? kSplitTiles : kDirectTiles;
-  const int n = split ? int(sizeof(kSplitTiles) / sizeof(TileCost)) : int(sizeof(kDirectTiles) / sizeof(TileCost));
+  const TileCost* c = mode == kPfDirect ? kDirectTiles : mode == kPfSplit ? kSplitTiles : kExpandTiles;
+  const int n = mode == kPfDirect ? int(sizeof(kDirectTiles) / sizeof(TileCost))
+              : mode == kPfSplit  ? int(sizeof(kSplitTiles) / sizeof(TileCost))
+                                  : int(sizeof(kExpandTiles) / sizeof(TileCost));
   TileCost best = c[0];
   double best_t = 0;
   for (int i = 0; i < n; ++i) {
@@ -68,17 +78,26 @@ TileCost sparse_tile(int64_t rows, int64_t tokens, bool split, const DeviceInfo&
 }
 
 template <int TR, int TT>
-const void* sparse_kernel(bool split) {
-  return split ? reinterpret_cast<const void*>(&prefill_split_kernel<TR, TT, 64, kDepth>)
-               : reinterpret_cast<const void*>(&prefill_spmm_kernel<TR, TT, 64, kDepth>);
+const void* sparse_kernel(int mode) {
+  return mode == kPfDirect  ? reinterpret_cast<const void*>(&prefill_spmm_kernel<TR, TT, 64, kDepth>)
+         : mode == kPfSplit ? reinterpret_cast<const void*>(&prefill_split_kernel<TR, TT, 64, kDepth>)
+                            : reinterpret_cast<const void*>(&prefill_expand_kernel<TR, TT, 64, kDepth>);
 }
 
-const void* sparse_kernel_of(const TileCost& t, bool split) {
-  if (t.tr == 1) return sparse_kernel<1, 4>(split);
-  if (t.tr == 2) return t.tt == 4 ? sparse_kernel<2, 4>(split)
-                        : t.tt == 8 ? sparse_kernel<2, 8>(split)
-                                    : reinterpret_cast<const void*>(&prefill_split_kernel<2, 16, 64, kDepth>);
-  return t.tt == 8 ? sparse_kernel<4, 8>(split) : sparse_kernel<4, 16>(split);
+// The kernel of a tile in the mode's table (2:4 has no 128 x 256 tile, 16:32 no 256-row one).
+const void* sparse_kernel_of(const TileCost& t, int mode) {
+  if (t.tr == 1) return sparse_kernel<1, 4>(mode);
+  if (t.tr == 2) {
+    if (t.tt == 4) return sparse_kernel<2, 4>(mode);
+    if (t.tt == 8) return sparse_kernel<2, 8>(mode);
+    return mode == kPfSplit ? reinterpret_cast<const void*>(&prefill_split_kernel<2, 16, 64, kDepth>)
+                            : reinterpret_cast<const void*>(&prefill_expand_kernel<2, 16, 64, kDepth>);
+  }
+  if (t.tt == 8)
+    return mode == kPfSplit ? reinterpret_cast<const void*>(&prefill_split_kernel<4, 8, 64, kDepth>)
+                            : reinterpret_cast<const void*>(&prefill_spmm_kernel<4, 8, 64, kDepth>);
+  return mode == kPfSplit ? reinterpret_cast<const void*>(&prefill_split_kernel<4, 16, 64, kDepth>)
+                          : reinterpret_cast<const void*>(&prefill_spmm_kernel<4, 16, 64, kDepth>);
 }
 
 }  // namespace
@@ -88,7 +107,7 @@ bool prefill_fits(int64_t rows, int64_t cols, int64_t tokens) {
   return cols <= kPrefillMaxCols && tokens <= kPrefillMaxTokens && workgroups<Small>(rows, tokens) <= INT32_MAX;
 }
 
-bool prefill_pattern(int n, int m) { return 2 * n == m && (n == 2 || n == 4 || n == 8); }
+bool prefill_pattern(int n, int m) { return 2 * n == m && (n == 2 || n == 4 || n == 8 || n == 16); }
 
 namespace {
 
@@ -127,10 +146,15 @@ size_t colsplit_bytes(const ColPlan& p, const DeviceInfo& dev) {
   return counter_bytes(dev) + size_t(p.tiles) * size_t(p.splits) * size_t(kThreads) * size_t(p.tt) * 16u;
 }
 
-template <bool SPLIT>
-const void* colsplit_kernel(int tt) {
-  return tt == 2 ? reinterpret_cast<const void*>(&prefill_colsplit_kernel<1, 2, 64, kDepth, SPLIT>)
-                 : reinterpret_cast<const void*>(&prefill_colsplit_kernel<1, 4, 64, kDepth, SPLIT>);
+const void* colsplit_kernel(int tt, int mode) {
+  if (mode == kPfExpand)
+    return tt == 2 ? reinterpret_cast<const void*>(&prefill_colsplit_expand_kernel<1, 2, 64, kDepth>)
+                   : reinterpret_cast<const void*>(&prefill_colsplit_expand_kernel<1, 4, 64, kDepth>);
+  if (mode == kPfSplit)
+    return tt == 2 ? reinterpret_cast<const void*>(&prefill_colsplit_kernel<1, 2, 64, kDepth, true>)
+                   : reinterpret_cast<const void*>(&prefill_colsplit_kernel<1, 4, 64, kDepth, true>);
+  return tt == 2 ? reinterpret_cast<const void*>(&prefill_colsplit_kernel<1, 2, 64, kDepth, false>)
+                 : reinterpret_cast<const void*>(&prefill_colsplit_kernel<1, 4, 64, kDepth, false>);
 }
 
 }  // namespace
@@ -145,7 +169,7 @@ hipError_t launch_prefill_spmm(const uint16_t* values, const uint32_t* masks, co
                                const DeviceInfo& dev, void* workspace, size_t workspace_bytes) {
   if (!prefill_fits(rows, cols, tokens) || !prefill_pattern(n, m)) return hipErrorInvalidValue;
   int r = int(rows), c = int(cols), t = int(tokens);
-  const bool split = n != 2;
+  const int mode = pf_mode(n);
   const ColPlan p = colsplit_plan(rows, cols, tokens, dev);
   const size_t need = colsplit_bytes(p, dev);
   if (need > 0 && workspace != nullptr && workspace_bytes >= need) {
@@ -153,13 +177,13 @@ hipError_t launch_prefill_spmm(const uint16_t* values, const uint32_t* masks, co
     unsigned* cnt = static_cast<unsigned*>(workspace);
     float4* part = reinterpret_cast<float4*>(static_cast<char*>(workspace) + counter_bytes(dev));
     void* cargs[] = {&values, &masks, &X, &Y, &r, &c, &t, &sp, &bl, &part, &cnt};
-    return launch(split ? colsplit_kernel<true>(p.tt) : colsplit_kernel<false>(p.tt),
-                  dim3(unsigned(p.tiles * p.splits)), dim3(kThreads), cargs, 0, stream, dev);
+    return launch(colsplit_kernel(p.tt, mode), dim3(unsigned(p.tiles * p.splits)), dim3(kThreads), cargs, 0, stream,
+                  dev);
   }
   void* args[] = {&values, &masks, &X, &Y, &r, &c, &t};
-  const TileCost tc = sparse_tile(rows, tokens, split, dev);
+  const TileCost tc = sparse_tile(rows, tokens, mode, dev);
   const int64_t grid = ceil_div(rows, 64 * tc.tr) * ceil_div(tokens, 16 * tc.tt);
-  return launch(sparse_kernel_of(tc, split), dim3(unsigned(grid)), dim3(kThreads), args, 0, stream, dev);
+  return launch(sparse_kernel_of(tc, mode), dim3(unsigned(grid)), dim3(kThreads), args, 0, stream, dev);
 }
 
 hipError_t launch_prefill_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y, int64_t rows, int64_t cols,
@@ -174,17 +198,20 @@ hipError_t launch_prefill_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y
                 dim3(unsigned(workgroups<Small>(rows, tokens))), dim3(kThreads), args, 0, stream, dev);
 }
 
-const char* prefill_colsplit_variant(int64_t rows, int64_t cols, int64_t tokens, const DeviceInfo& dev, bool split) {
+const char* prefill_colsplit_variant(int64_t rows, int64_t cols, int64_t tokens, const DeviceInfo& dev, int n) {
   const ColPlan p = colsplit_plan(rows, cols, tokens, dev);
   if (p.splits == 1) return "";
-  if (split)
+  const int mode = pf_mode(n);
+  if (mode == kPfExpand)
+    return p.tt == 2 ? "prefill_colsplit_expand_kernel<1, 2, 64, 2>" : "prefill_colsplit_expand_kernel<1, 4, 64, 2>";
+  if (mode == kPfSplit)
     return p.tt == 2 ? "prefill_colsplit_kernel<1, 2, 64, 2, true>" : "prefill_colsplit_kernel<1, 4, 64, 2, true>";
   return p.tt == 2 ? "prefill_colsplit_kernel<1, 2, 64, 2, false>" : "prefill_colsplit_kernel<1, 4, 64, 2, false>";
 }
 
-const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev, bool split) {
+const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev, int n) {
   if (sparse) {
-    static const char* const kNames[2][5][3] = {
+    static const char* const kNames[3][5][3] = {
         {{"prefill_spmm_kernel<1, 4, 64, 2>", "", ""},
          {"prefill_spmm_kernel<2, 4, 64, 2>", "prefill_spmm_kernel<2, 8, 64, 2>", ""},
          {"", "", ""},
@@ -194,10 +221,17 @@ const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const Dev
          {"prefill_split_kernel<2, 4, 64, 2>", "prefill_split_kernel<2, 8, 64, 2>", "prefill_split_kernel<2, 16, 64, 2>"},
          {"", "", ""},
          {"prefill_split_kernel<4, 8, 64, 2>", "prefill_split_kernel<4, 16, 64, 2>", ""},
+         {"", "", ""}},
+        {{"prefill_expand_kernel<1, 4, 64, 2>", "", ""},
+         {"prefill_expand_kernel<2, 4, 64, 2>", "prefill_expand_kernel<2, 8, 64, 2>",
+          "prefill_expand_kernel<2, 16, 64, 2>"},
+         {"", "", ""},
+         {"prefill_expand_kernel<4, 8, 64, 2>", "prefill_expand_kernel<4, 16, 64, 2>", ""},
          {"", "", ""}}};
-    const TileCost t = sparse_tile(rows, tokens, split, dev);
+    const int mode = pf_mode(n);
+    const TileCost t = sparse_tile(rows, tokens, mode, dev);
     const int col = t.tr == 1 ? 0 : t.tr == 2 ? (t.tt == 4 ? 0 : t.tt == 8 ? 1 : 2) : (t.tt == 8 ? 0 : 1);
-    return kNames[split ? 1 : 0][t.tr - 1][col];
+    return kNames[mode][t.tr - 1][col];
   }
   return use_large<DenseLarge>(rows, tokens, dev) ? "prefill_gemm_kernel<2, 16, 64, 2>"
                                                   : "prefill_gemm_kernel<1, 4, 64, 2>";

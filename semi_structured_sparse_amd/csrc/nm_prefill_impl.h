@@ -187,6 +187,52 @@ __host__ __device__ constexpr SplitTable make_split_table() {
 
 __device__ const SplitTable kSplitTable = make_split_table();
 
+// ---- 16:32 on the dense matrix instruction (expanded fragments) ----
+// A 16:32 word keeps 16 values anywhere in its 32 columns, so no fixed share of them lands in
+// a lane's columns and no 2:4 split fits. The dense 16 x 16 x 32 instruction takes the word
+// as it is: lane (row, q) supplies the 8 dense halves of columns 8q .. 8q+7, i.e. mask byte q.
+// Its kept values are the word's packed values pc .. pc+c-1 (pc the bit count of the word
+// below byte q, c the byte's): the lane reads the 8 halves from pc on into 4 dwords w0..w3,
+// and a table indexed by the mask byte gives, per output dword (columns 2d, 2d+1), two
+// v_perm_b32 byte selectors, one over w0:w1 and one over w2:w3, whose results are ORed:
+// the value of rank r = (bits of the byte below column j) for a set bit j, a zero byte pair
+// for a clear one. Selector byte 0x0C gives a zero byte.
+constexpr int kExpandEntries = 256;
+constexpr uint32_t kExpandBytes = kExpandEntries * 32;
+
+// selector bytes placing half `rank` of the 8-half window (-1: zero) in one output half,
+// for the perm over w0:w1 when !high (halves 0..3), over w2:w3 when high (halves 4..7)
+__host__ __device__ constexpr uint32_t expand_half_sel(int rank, bool high) {
+  if (rank < 0 || (rank >= 4) != high) return 0x0C0Cu;
+  const uint32_t b = 2u * uint32_t(rank & 3);
+  return b | (b + 1u) << 8;
+}
+
+struct ExpandTable {
+  uint4 sel[2 * kExpandEntries];   // entry b: sel[2b] = (lo0, hi0, lo1, hi1), sel[2b+1] = (lo2, hi2, lo3, hi3)
+};
+static_assert(sizeof(ExpandTable) == kExpandBytes, "expand table layout");
+
+__host__ __device__ constexpr ExpandTable make_expand_table() {
+  ExpandTable t{};
+  for (int b = 0; b < kExpandEntries; ++b) {
+    uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int rank = 0;
+    int r[8] = {-1, -1, -1, -1, -1, -1, -1, -1};
+    for (int j = 0; j < 8; ++j)
+      if ((b >> j) & 1) r[j] = rank++;
+    for (int d = 0; d < 4; ++d) {
+      v[2 * d] = expand_half_sel(r[2 * d], false) | expand_half_sel(r[2 * d + 1], false) << 16;
+      v[2 * d + 1] = expand_half_sel(r[2 * d], true) | expand_half_sel(r[2 * d + 1], true) << 16;
+    }
+    t.sel[2 * b] = uint4{v[0], v[1], v[2], v[3]};
+    t.sel[2 * b + 1] = uint4{v[4], v[5], v[6], v[7]};
+  }
+  return t;
+}
+
+__device__ const ExpandTable kExpandTable = make_expand_table();
+
 // Buffer loads: a resource spans one workgroup's slice of an operand and the hardware
 // returns zero for offsets at or past its end, so lanes with nothing to load (tokens or
 // rows past the end, columns past the row) take kOutOfRange instead of a branch.
@@ -565,18 +611,27 @@ __device__ __forceinline__ bool split_handoff(f4_t (&acc)[TR][TT], const ColSpli
   return true;
 }
 
-// The sparse products: values [rows][cols / 2] fp16, masks [rows][cols / 32]; 2:4 directly
-// (SPLIT false), 4:8 and 8:16 split into two 2:4 operands (SPLIT true, lut = the split
-// tables in LDS).
+// How the sparse body turns a lane's packed values and mask bits into matrix operands:
+// 2:4 directly on the sparse instruction; 4:8 and 8:16 split into two 2:4 operands (the
+// split tables); 16:32 expanded to dense fragments for the dense instruction (the expansion
+// table), one per 32-column word.
+constexpr int kPfDirect = 0, kPfSplit = 1, kPfExpand = 2;
+// EXPAND: LDS bytes of one wave's value area per row tile: the step's values of its 16 rows
+// (64 bytes each) and room for a window read past the last row's second word
+constexpr uint32_t kPfAreaBytes = 16 * 64 + 64;
+
+// The sparse products: values [rows][cols / 2] fp16, masks [rows][cols / 32]; MODE as above
+// (lut: the pattern's table in LDS; area: EXPAND's per-wave value areas, TR per wave).
 // COLS: one of a tile's column splits (columns c_beg .. c_end - 1; the hand-off to the
 // tile's last workgroup in split_handoff), else the whole row (c_beg = 0, c_end = cols).
-template <int TR, int TT, int KS, int D, bool SPLIT, bool COLS>
+template <int TR, int TT, int KS, int D, int MODE, bool COLS>
 __device__ __forceinline__ void prefill_sparse_body(const uint16_t* __restrict__ values,
                                                     const uint32_t* __restrict__ masks,
                                                     const uint16_t* __restrict__ X, uint16_t* __restrict__ Y,
                                                     int rows, int cols, int tokens,
-                                                    char (*xs)[Tile<TR, TT, KS>::kXBytes], char* lut,
+                                                    char (*xs)[Tile<TR, TT, KS>::kXBytes], char* lut, char* area,
                                                     TileCoord tc, int c_beg, int c_end, const ColSplit& cs) {
+  constexpr bool SPLIT = MODE == kPfSplit, EXPAND = MODE == kPfExpand;
   using T = Tile<TR, TT, KS>;
   constexpr int SUB = T::kSub;
   const int tid = threadIdx.x;
@@ -586,18 +641,19 @@ __device__ __forceinline__ void prefill_sparse_body(const uint16_t* __restrict__
   const int t0 = tc.ty * T::kTokens;
   const int words = cols >> 5;
 
-  // SPLIT: this thread's 16-byte chunks of the split tables, loaded before anything else
-  // and written to LDS with the first X chunks (the wait for those covers them)
-  constexpr int kLutChunks = int(kSplitLutBytes / 16);
-  constexpr int kLutPer = SPLIT ? (kLutChunks + kThreads - 1) / kThreads : 1;
+  // SPLIT, EXPAND: this thread's 16-byte chunks of the pattern's table, loaded before
+  // anything else and written to LDS with the first X chunks (the wait for those covers them)
+  constexpr int kLutChunks = int((EXPAND ? kExpandBytes : kSplitLutBytes) / 16);
+  constexpr int kLutPer = SPLIT || EXPAND ? (kLutChunks + kThreads - 1) / kThreads : 1;
   uint4 lreg[kLutPer];
-  if constexpr (SPLIT) {
-    const uint4* tab = reinterpret_cast<const uint4*>(&kSplitTable);
+  if constexpr (SPLIT || EXPAND) {
+    const uint4* tab = EXPAND ? reinterpret_cast<const uint4*>(&kExpandTable)
+                              : reinterpret_cast<const uint4*>(&kSplitTable);
 #pragma unroll
     for (int j = 0; j < kLutPer; ++j) lreg[j] = tab[min(tid + kThreads * j, kLutChunks - 1)];
   }
   auto stage = [&] {
-    if constexpr (SPLIT) {
+    if constexpr (SPLIT || EXPAND) {
 #pragma unroll
       for (int j = 0; j < kLutPer; ++j)
         if (tid + kThreads * j < kLutChunks) reinterpret_cast<uint4*>(lut)[tid + kThreads * j] = lreg[j];
@@ -656,9 +712,10 @@ __device__ __forceinline__ void prefill_sparse_body(const uint16_t* __restrict__
     if constexpr (P == 0) {   // 2:4: the position codes of the block's words, once per block
 #pragma unroll
       for (int a = 0; a < TR; ++a)
-        mcur[a] = SPLIT ? mnext[a]
-                        : make_uint4(pair_codes32(mnext[a].x), pair_codes32(mnext[a].y), pair_codes32(mnext[a].z),
-                                     pair_codes32(mnext[a].w));
+        mcur[a] = SPLIT || EXPAND
+                      ? mnext[a]
+                      : make_uint4(pair_codes32(mnext[a].x), pair_codes32(mnext[a].y), pair_codes32(mnext[a].z),
+                                   pair_codes32(mnext[a].w));
     }
     if constexpr (P == kMaskSteps - D) load_masks(s0 / kMaskSteps + 1);
   };
@@ -667,7 +724,72 @@ __device__ __forceinline__ void prefill_sparse_body(const uint16_t* __restrict__
   zero(acc);
   // X fragment of token 16 b + li: column chunks q and 4 + q of the step
   const uint32_t b_lo = x_offset<T::kRowBytes>(li, q), b_hi = x_offset<T::kRowBytes>(li, 4 + q);
-  auto compute = [&](const AF& f, const char* buf, auto pc) {
+  // EXPAND: this wave's value areas (row tile a at a * kPfAreaBytes)
+  char* const warea = EXPAND ? area + uint32_t(wave) * TR * kPfAreaBytes : nullptr;
+  auto compute_expand = [&](const AF& f, const char* buf, auto pc) {
+    constexpr int J = decltype(pc)::value;
+    const int src = 4 * (li + 16 * (J >> 1));
+    // the step's values of the wave's rows to its areas (row li at 64 li: word 0's 16 values,
+    // then word 1's; lane q's 16 bytes at 16 q), visible to the wave's other lanes before
+    // they read them back
+#pragma unroll
+    for (int a = 0; a < TR; ++a) *reinterpret_cast<uint4*>(warea + a * kPfAreaBytes + 64 * li + 16 * q) = f.v[a][0];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // lane (q, li): the dense halves of columns 8q .. 8q+7 of each word of row li: the 8
+    // halves from its mask byte's first kept value on, placed by the expansion table
+    uint4 dense[TR][2];
+#pragma unroll
+    for (int a = 0; a < TR; ++a) {
+      const uint32_t w0 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int((J & 1) ? mcur[a].z : mcur[a].x)));
+      const uint32_t w1 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int((J & 1) ? mcur[a].w : mcur[a].y)));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t wi = i ? w1 : w0;
+        const uint32_t byte = __builtin_amdgcn_ubfe(wi, 8u * uint32_t(q), 8);
+        // first kept value of the byte among the word's 16 (clamped: any mask keeps the
+        // window inside the areas)
+        const uint32_t first = min(uint32_t(__builtin_popcount(wi & ((1u << (8 * q)) - 1u))), 16u);
+        const uint32_t off = uint32_t(a) * kPfAreaBytes + 64u * uint32_t(li) + 32u * uint32_t(i) + 2u * first;
+        const uint32_t* wd = reinterpret_cast<const uint32_t*>(warea + (off & ~3u));
+        const uint32_t sh = (off & 2u) * 8u;   // 16 when the window starts mid-dword
+        const uint32_t r0 = wd[0], r1 = wd[1], r2 = wd[2], r3 = wd[3], r4 = wd[4];
+        const uint32_t v0 = __builtin_amdgcn_alignbit(r1, r0, sh), v1 = __builtin_amdgcn_alignbit(r2, r1, sh);
+        const uint32_t v2 = __builtin_amdgcn_alignbit(r3, r2, sh), v3 = __builtin_amdgcn_alignbit(r4, r3, sh);
+        const uint4 s0 = *reinterpret_cast<const uint4*>(lut + 32u * byte);
+        const uint4 s1 = *reinterpret_cast<const uint4*>(lut + 32u * byte + 16u);
+        auto pick = [&](uint32_t lo_sel, uint32_t hi_sel) {
+          return __builtin_amdgcn_perm(v1, v0, lo_sel) | __builtin_amdgcn_perm(v3, v2, hi_sel);
+        };
+        dense[a][i] = make_uint4(pick(s0.x, s0.y), pick(s0.z, s0.w), pick(s1.x, s1.y), pick(s1.z, s1.w));
+      }
+    }
+    // every lane has read the areas before the next step writes them
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // X fragments (chunks q and 4 + q: the columns of word 0, word 1), one token tile ahead
+    uint4 lo[2], hi[2];
+    lo[0] = lds_read16(buf, b_lo);
+    hi[0] = lds_read16(buf, b_hi);
+#pragma unroll
+    for (int b = 0; b < TT; ++b) {
+      if (b + 1 < TT) {
+        const char* tb = buf + (b + 1) * 16 * T::kRowBytes;
+        lo[(b + 1) & 1] = lds_read16(tb, b_lo);
+        hi[(b + 1) & 1] = lds_read16(tb, b_hi);
+      }
+#pragma unroll
+      for (int a = 0; a < TR; ++a) {
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, dense[a][0]),
+                                                           __builtin_bit_cast(h8_t, lo[b & 1]), acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, dense[a][1]),
+                                                           __builtin_bit_cast(h8_t, hi[b & 1]), acc[a][b], 0, 0, 0);
+      }
+    }
+  };
+  auto compute_sparse = [&](const AF& f, const char* buf, auto pc) {
     constexpr int J = decltype(pc)::value;           // step within the mask block
     const int src = 4 * (li + 16 * (J >> 1));        // byte address of lane li + 16 (J / 2)
     h8_t av[TR], bv[SPLIT ? TR : 1];
@@ -722,6 +844,12 @@ __device__ __forceinline__ void prefill_sparse_body(const uint16_t* __restrict__
       }
     }
   };
+  auto compute = [&](const AF& f, const char* buf, auto pc) {
+    if constexpr (EXPAND)
+      compute_expand(f, buf, pc);
+    else
+      compute_sparse(f, buf, pc);
+  };
   sparse_main_loop<TR, TT, KS, D, kMaskSteps, AF>(xst, xs, cols, c_beg, c_end, load_a, hook, compute, stage);
   if constexpr (COLS) {
     if (!split_handoff<TR, TT>(acc, cs)) return;
@@ -744,8 +872,8 @@ __global__ __launch_bounds__(kThreads) void prefill_spmm_kernel(const uint16_t* 
   using T = Tile<TR, TT, KS>;
   __shared__ __attribute__((aligned(16))) char xs[2][T::kXBytes];
   const TileCoord tc = tile_of(int(blockIdx.x), (rows + T::kRows - 1) / T::kRows, (tokens + T::kTokens - 1) / T::kTokens);
-  prefill_sparse_body<TR, TT, KS, D, false, false>(values, masks, X, Y, rows, cols, tokens, xs, nullptr, tc, 0, cols,
-                                                   ColSplit{});
+  prefill_sparse_body<TR, TT, KS, D, kPfDirect, false>(values, masks, X, Y, rows, cols, tokens, xs, nullptr, nullptr,
+                                                       tc, 0, cols, ColSplit{});
 }
 
 // 4:8 and 8:16 sparse product (split operands).
@@ -759,8 +887,24 @@ __global__ __launch_bounds__(kThreads) void prefill_split_kernel(const uint16_t*
   __shared__ __attribute__((aligned(16))) char xs[2][T::kXBytes];
   __shared__ __attribute__((aligned(16))) char lut[kSplitLutBytes];
   const TileCoord tc = tile_of(int(blockIdx.x), (rows + T::kRows - 1) / T::kRows, (tokens + T::kTokens - 1) / T::kTokens);
-  prefill_sparse_body<TR, TT, KS, D, true, false>(values, masks, X, Y, rows, cols, tokens, xs, lut, tc, 0, cols,
-                                                  ColSplit{});
+  prefill_sparse_body<TR, TT, KS, D, kPfSplit, false>(values, masks, X, Y, rows, cols, tokens, xs, lut, nullptr, tc, 0,
+                                                      cols, ColSplit{});
+}
+
+// 16:32 sparse product (fragments expanded for the dense instruction).
+template <int TR, int TT, int KS, int D>
+__global__ __launch_bounds__(kThreads) void prefill_expand_kernel(const uint16_t* __restrict__ values,
+                                                                  const uint32_t* __restrict__ masks,
+                                                                  const uint16_t* __restrict__ X,
+                                                                  uint16_t* __restrict__ Y, int rows, int cols,
+                                                                  int tokens) {
+  using T = Tile<TR, TT, KS>;
+  __shared__ __attribute__((aligned(16))) char xs[2][T::kXBytes];
+  __shared__ __attribute__((aligned(16))) char lut[kExpandBytes];
+  __shared__ __attribute__((aligned(16))) char area[kWaves * TR * kPfAreaBytes];
+  const TileCoord tc = tile_of(int(blockIdx.x), (rows + T::kRows - 1) / T::kRows, (tokens + T::kTokens - 1) / T::kTokens);
+  prefill_sparse_body<TR, TT, KS, D, kPfExpand, false>(values, masks, X, Y, rows, cols, tokens, xs, lut, area, tc, 0,
+                                                       cols, ColSplit{});
 }
 
 // Column-split sparse products (2:4 when !SPLIT, 4:8 and 8:16 when SPLIT): workgroup b takes
@@ -784,8 +928,33 @@ __global__ __launch_bounds__(kThreads) void prefill_colsplit_kernel(const uint16
   const TileCoord tc{tile % nrx, tile / nrx};
   const int c_beg = split * blocks * kColBlock;
   const int c_end = min(cols, c_beg + blocks * kColBlock);
-  prefill_sparse_body<TR, TT, KS, D, SPLIT, true>(values, masks, X, Y, rows, cols, tokens, xs, SPLIT ? lut : nullptr,
-                                                  tc, c_beg, c_end, ColSplit{part, cnt, splits, tile, split, &flag});
+  prefill_sparse_body<TR, TT, KS, D, SPLIT ? kPfSplit : kPfDirect, true>(
+      values, masks, X, Y, rows, cols, tokens, xs, SPLIT ? lut : nullptr, nullptr, tc, c_beg, c_end,
+      ColSplit{part, cnt, splits, tile, split, &flag});
+}
+
+// The column-split 16:32 product (expanded fragments), laid out as prefill_colsplit_kernel.
+template <int TR, int TT, int KS, int D>
+__global__ __launch_bounds__(kThreads) void prefill_colsplit_expand_kernel(const uint16_t* __restrict__ values,
+                                                                           const uint32_t* __restrict__ masks,
+                                                                           const uint16_t* __restrict__ X,
+                                                                           uint16_t* __restrict__ Y, int rows,
+                                                                           int cols, int tokens, int splits,
+                                                                           int blocks, float4* __restrict__ part,
+                                                                           unsigned* __restrict__ cnt) {
+  using T = Tile<TR, TT, KS>;
+  __shared__ __attribute__((aligned(16))) char xs[2][T::kXBytes];
+  __shared__ __attribute__((aligned(16))) char lut[kExpandBytes];
+  __shared__ __attribute__((aligned(16))) char area[kWaves * TR * kPfAreaBytes];
+  __shared__ unsigned flag;
+  const int b = int(blockIdx.x);
+  const int tile = b / splits, split = b - tile * splits;
+  const int nrx = (rows + T::kRows - 1) / T::kRows;
+  const TileCoord tc{tile % nrx, tile / nrx};
+  const int c_beg = split * blocks * kColBlock;
+  const int c_end = min(cols, c_beg + blocks * kColBlock);
+  prefill_sparse_body<TR, TT, KS, D, kPfExpand, true>(values, masks, X, Y, rows, cols, tokens, xs, lut, area, tc,
+                                                      c_beg, c_end, ColSplit{part, cnt, splits, tile, split, &flag});
 }
 
 // Dense product: W [rows][cols] fp16.

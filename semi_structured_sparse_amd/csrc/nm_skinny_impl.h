@@ -37,52 +37,6 @@ namespace skinny_detail {
 
 using namespace prefill_detail;
 
-// ---- 16:32 on the dense matrix instruction (expanded fragments) ----
-// A 16:32 word keeps 16 values anywhere in its 32 columns, so no fixed share of them lands in
-// a lane's columns and no 2:4 split fits. The dense 16 x 16 x 32 instruction takes the word
-// as it is: lane (row, q) supplies the 8 dense halves of columns 8q .. 8q+7, i.e. mask byte q.
-// Its kept values are the word's packed values pc .. pc+c-1 (pc the bit count of the word
-// below byte q, c the byte's): the lane reads the 8 halves from pc on into 4 dwords w0..w3,
-// and a table indexed by the mask byte gives, per output dword (columns 2d, 2d+1), two
-// v_perm_b32 byte selectors, one over w0:w1 and one over w2:w3, whose results are ORed:
-// the value of rank r = (bits of the byte below column j) for a set bit j, a zero byte pair
-// for a clear one. Selector byte 0x0C gives a zero byte.
-constexpr int kExpandEntries = 256;
-constexpr uint32_t kExpandBytes = kExpandEntries * 32;
-
-// selector bytes placing half `rank` of the 8-half window (-1: zero) in one output half,
-// for the perm over w0:w1 when !high (halves 0..3), over w2:w3 when high (halves 4..7)
-__host__ __device__ constexpr uint32_t expand_half_sel(int rank, bool high) {
-  if (rank < 0 || (rank >= 4) != high) return 0x0C0Cu;
-  const uint32_t b = 2u * uint32_t(rank & 3);
-  return b | (b + 1u) << 8;
-}
-
-struct ExpandTable {
-  uint4 sel[2 * kExpandEntries];   // entry b: sel[2b] = (lo0, hi0, lo1, hi1), sel[2b+1] = (lo2, hi2, lo3, hi3)
-};
-static_assert(sizeof(ExpandTable) == kExpandBytes, "expand table layout");
-
-__host__ __device__ constexpr ExpandTable make_expand_table() {
-  ExpandTable t{};
-  for (int b = 0; b < kExpandEntries; ++b) {
-    uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int rank = 0;
-    int r[8] = {-1, -1, -1, -1, -1, -1, -1, -1};
-    for (int j = 0; j < 8; ++j)
-      if ((b >> j) & 1) r[j] = rank++;
-    for (int d = 0; d < 4; ++d) {
-      v[2 * d] = expand_half_sel(r[2 * d], false) | expand_half_sel(r[2 * d + 1], false) << 16;
-      v[2 * d + 1] = expand_half_sel(r[2 * d], true) | expand_half_sel(r[2 * d + 1], true) << 16;
-    }
-    t.sel[2 * b] = uint4{v[0], v[1], v[2], v[3]};
-    t.sel[2 * b + 1] = uint4{v[4], v[5], v[6], v[7]};
-  }
-  return t;
-}
-
-__device__ const ExpandTable kExpandTable = make_expand_table();
-
 constexpr int kMaxWaves = 16;
 constexpr int kMaxTokens = 16;
 constexpr int kThreadsFixed = 64 * kMaxWaves;           // every launch uses 16 waves

@@ -282,12 +282,14 @@ def test_spmm_workspace_bytes_invalid_arguments():
     (dict(Y=None), nm.NM_ERR_NULL),
     (dict(tokens=0), nm.NM_ERR_SHAPE), (dict(tokens=(1 << 24) + 1), nm.NM_ERR_SHAPE), (dict(rows=0), nm.NM_ERR_SHAPE),
     (dict(cols=80), nm.NM_ERR_SHAPE), (dict(cols=(1 << 21) + 32), nm.NM_ERR_SHAPE),
-    (dict(N=16, M=32), nm.NM_ERR_PATTERN), (dict(N=1, M=4), nm.NM_ERR_PATTERN), (dict(N=3, M=4), nm.NM_ERR_PATTERN),
+    (dict(N=1, M=4), nm.NM_ERR_PATTERN), (dict(N=3, M=4), nm.NM_ERR_PATTERN), (dict(N=8, M=32), nm.NM_ERR_PATTERN),
     (dict(N=2, M=8), nm.NM_ERR_PATTERN),
     (dict(values=A16 + 8), nm.NM_ERR_ALIGN), (dict(masks=A16 + 2), nm.NM_ERR_ALIGN),
     (dict(X=A16 + 4), nm.NM_ERR_ALIGN), (dict(Y=A16 + 1), nm.NM_ERR_ALIGN),
-    # 4:8 and 8:16 pass the pattern check (the split operands) and reach the alignment check
+    # 4:8, 8:16 (the split operands) and 16:32 (expanded fragments) pass the pattern check and
+    # reach the alignment check
     (dict(N=4, M=8, values=A16 + 8), nm.NM_ERR_ALIGN), (dict(N=8, M=16, X=A16 + 4), nm.NM_ERR_ALIGN),
+    (dict(N=16, M=32, masks=A16 + 2), nm.NM_ERR_ALIGN),
 ])
 def test_spmm_prefill_validation(kw, want):
     a = dict(values=A16, masks=A16, X=A16, Y=A16, rows=64, cols=128, tokens=300, N=2, M=4)

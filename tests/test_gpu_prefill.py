@@ -157,8 +157,8 @@ def test_prefill_argument_errors():
     v = torch.zeros((4, 64), dtype=torch.float16, device=device())
     m = torch.zeros((4, 4), dtype=torch.int32, device=device())
     X = torch.zeros((3, 128), dtype=torch.float16, device=device())
-    with pytest.raises(nm.NMArgumentError) as e:
-        nm.nm_spmm_prefill(v, m, X, 16, 32)
+    with pytest.raises(nm.NMArgumentError) as e:   # a 25% pattern: no matrix-core product
+        nm.nm_spmm_prefill(torch.zeros((4, 32), dtype=torch.float16, device=device()), m, X, 1, 4)
     assert e.value.status == nm.NM_ERR_PATTERN
     with pytest.raises(ValueError):
         nm.nm_spmm_prefill(v, m, torch.zeros((3, 96), dtype=torch.float16, device=device()))
@@ -265,7 +265,9 @@ def test_prefill_split_full_size_down_proj(N, M):
 # 2, 4, 7 (uneven: 28 blocks of 4) and 8 splits, one and two workgroups per CU
 COLSPLIT = [(1000, 4064, 17), (130, 1056, 100), (1024, 4096, 32), (2048, 8192, 48), (4096, 4096, 64),
             (4096, 14336, 40), (1024, 8192, 256), (14336, 4096, 20), (4100, 1024, 150)]
-COLSPLIT_NAMES = {f"prefill_colsplit_kernel<1, {tt}, 64, 2, {sp}>" for tt in (2, 4) for sp in ("false", "true")}
+COLSPLIT_NAMES = {(N, M): {f"prefill_colsplit_kernel<1, {tt}, 64, 2, {'false' if N == 2 else 'true'}>" for tt in (2, 4)}
+                  for N, M in ((2, 4), (4, 8), (8, 16))}
+COLSPLIT_NAMES[(16, 32)] = {f"prefill_colsplit_expand_kernel<1, {tt}, 64, 2>" for tt in (2, 4)}
 
 
 def _counter_bytes():
@@ -273,7 +275,7 @@ def _counter_bytes():
     return -(-(4 * cus) // 256) * 256
 
 
-@pytest.mark.parametrize("N,M", [(2, 4), (4, 8), (8, 16)])
+@pytest.mark.parametrize("N,M", [(2, 4), (4, 8), (8, 16), (16, 32)])
 def test_colsplit_small_and_ragged(N, M):
     names = set()
     for i, (R, C, T) in enumerate(COLSPLIT):
@@ -281,7 +283,7 @@ def test_colsplit_small_and_ragged(N, M):
         names.add(name)
         need = nm.spmm_workspace_bytes(R, C, T, N, M)
         say(f"colsplit {N}:{M} {R}x{C} tokens={T} {name} workspace={need}")
-        assert name.startswith("prefill_colsplit_kernel"), (R, C, T, name)
+        assert name in COLSPLIT_NAMES[(N, M)], (R, C, T, name)
         W = synth.weight(R, C, seed=4100 + 10 * i + N)
         X = synth.activations(T, C, seed=4150 + i)
         values, masks = nm.nm_pack(up_f16(W), N, M)
@@ -293,8 +295,7 @@ def test_colsplit_small_and_ragged(N, M):
         rv, rm = oracle.pack_ref(W[idx], N, M)
         rep = oracle.y_tolerance_report(Y[:, idx], oracle.spmm_ref(rv, rm, X, C, N, M))
         assert rep["ok"], ((R, C, T), N, M, rep)
-    want = {n for n in COLSPLIT_NAMES if n.endswith("false>" if N == 2 else "true>")}
-    assert names == want, names
+    assert names == COLSPLIT_NAMES[(N, M)], names
 
 
 def test_colsplit_one_hot_deterministic_and_shared_workspace():
@@ -350,3 +351,52 @@ def test_colsplit_small_workspace_takes_nm_spmm_route():
             rep = oracle.y_tolerance_report(down_f16(nm.nm_spmm_ws(v, m, X, 2, 4, small))[:, :64],
                                             oracle.spmm_ref(rv, rm, down_f16(X), C, 2, 4))
             assert rep["ok"], rep
+
+
+# 16:32 (fragments expanded for the dense instruction): ragged rows and tokens, a 32-column
+# tail step, a last block of mask steps cut short, every tile configuration it picks (64 x 64,
+# 128 x 64, 128 x 128, 128 x 256)
+EXPAND_SMALL = [(17, 64, 5), (33, 128, 17), (65, 4096, 64), (300, 1056, 255), (8256, 160, 65), (16448, 1056, 65),
+                (2600, 2208, 3000)]
+EXPAND_NAMES = {"prefill_expand_kernel<1, 4, 64, 2>", "prefill_expand_kernel<2, 4, 64, 2>",
+                "prefill_expand_kernel<2, 8, 64, 2>", "prefill_expand_kernel<2, 16, 64, 2>"}
+
+
+def test_prefill_expand_small_and_ragged():
+    names = set()
+    for i, (R, C, T) in enumerate(EXPAND_SMALL):
+        names.add(nm.prefill_variant(R, C, T, True, expand=True))
+        say(f"prefill 16:32 {R}x{C} tokens={T} {nm.prefill_variant(R, C, T, True, expand=True)}")
+        W = synth.weight(R, C, seed=2900 + i)
+        X = synth.activations(T, C, seed=2950 + i)
+        check_split(W, X, 16, 32, (R, C, T), None if R * T <= 300 * 300 else sample_rows(R, rpb=128))
+    if torch.cuda.get_device_properties(device()).multi_processor_count == 256:   # shapes chosen for 256 CUs
+        assert names == EXPAND_NAMES, names
+
+
+def test_prefill_expand_one_hot_routing_and_malformed_masks():
+    """One-hot tokens give the pruned matrix's columns bit-exactly; nm_spmm from 64 vectors
+    runs the same kernel (same bits) and below keeps its 16-vector launches; the result is
+    deterministic; masks that are not 16:32 stay in bounds."""
+    R, C = 200, 256
+    W = synth.weight(R, C, seed=2990)
+    rv, rm = oracle.pack_ref(W, 16, 32)
+    D = oracle.unpack_ref(rv, rm, C, 16, 32)
+    X = np.eye(C, dtype=np.float16)
+    v, m = up_f16(rv), up_u32(rm)
+    Y = down_bits16(nm.nm_spmm_prefill(v, m, up_f16(X), 16, 32))
+    want = D.T.copy()
+    want[want == 0x8000] = 0
+    assert np.array_equal(Y, want)
+    Xr = up_f16(synth.activations(70, C, seed=2991))
+    assert nm.spmm_variant(R, C, 70, 16, 32).startswith("prefill_expand_kernel")
+    assert not nm.spmm_variant(R, C, 63, 16, 32).startswith("prefill")
+    Y0 = down_bits16(nm.nm_spmm_prefill(v, m, Xr, 16, 32))
+    assert np.array_equal(down_bits16(nm.nm_spmm(v, m, Xr, 16, 32)), Y0)
+    for _ in range(5):
+        assert np.array_equal(down_bits16(nm.nm_spmm_prefill(v, m, Xr, 16, 32)), Y0)
+    for word in (0, 1, 0xFFFFFFFF, 0x12345678):
+        mm = torch.full((R, C // 32), np.uint32(word).view(np.int32).item(), dtype=torch.int32, device=device())
+        Yb = nm.nm_spmm_prefill(v, mm, Xr, 16, 32)
+        torch.cuda.synchronize()
+        assert Yb.shape == (70, R)

@@ -138,8 +138,12 @@ def test_skinny_routing():
     assert nm.spmm_variant(14336, 4096, 32, 2, 4).startswith("prefill_spmm_kernel")
     assert nm.spmm_variant(4096, 4096, 64, 4, 8).startswith("prefill_split_kernel")
     assert nm.spmm_variant(200, 1024, 40, 2, 4).startswith("prefill_spmm_kernel")   # no skinny below 256 rows
-    assert nm.spmm_variant(4096, 4096, 2048, 8, 16) == "prefill_split_kernel<4, 8, 64, 2>"
+    if torch.cuda.get_device_properties(device()).multi_processor_count == 256:   # the tile model's pick
+        assert nm.spmm_variant(4096, 4096, 2048, 8, 16) == "prefill_split_kernel<2, 16, 64, 2>"
+    # 16:32: 16-vector launches up to 63 vectors, the expansion prefill kernels from 64
     assert nm.spmm_variant(4096, 4096, 40, 16, 32) == SKINNY[16]
+    assert nm.spmm_variant(4096, 4096, 63, 16, 32) == SKINNY[16]
+    assert nm.spmm_variant(4096, 4096, 64, 16, 32).startswith("prefill_expand_kernel")
     assert nm.spmm_variant(4096, 4096, 64, 2, 4).startswith("prefill_spmm_kernel")
     assert nm.spmm_variant(4096, 4096, 1, 2, 4).startswith("spmv_kernel")
 
@@ -250,11 +254,10 @@ def test_skinny_column_split_small_workspace_runs_unsplit():
     assert np.array_equal(down_bits16(nm.nm_spmm_ws(v, m, X, N, M, small)), want)
     assert np.array_equal(down_bits16(nm.nm_spmm_ws(v, m, X, N, M, None)), want)
     assert int(small.count_nonzero()) == 0
-    # no split: 16:32 (expanded fragments; at any batch), fewer than 5 vectors, layers that
-    # fill the GPU, prompts whose prefill grid fills it, and where the hand-off costs more
-    # than it saves (2:4 rows of 32 lines)
+    # no split: 16:32 up to 16 vectors (expanded fragments), fewer than 5 vectors, layers
+    # that fill the GPU, prompts whose prefill grid fills it, and where the hand-off costs
+    # more than it saves (2:4 rows of 32 lines)
     assert nm.spmm_workspace_bytes(4096, 4096, 16, 16, 32) == 0
-    assert nm.spmm_workspace_bytes(4096, 4096, 64, 16, 32) == 0
     assert nm.spmm_workspace_bytes(1024, 8192, 4, 2, 4) == 0
     assert nm.spmm_workspace_bytes(4096, 8192, 8, 2, 4) == 0
     assert nm.spmm_workspace_bytes(4096, 4096, 2048, 2, 4) == 0
