@@ -174,7 +174,8 @@ int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, ui
  *     (up to 32 vectors) or 64 vectors are too few to fill the GPU (mid-size batches: e.g.
  *     up to 256 tokens on 4096 x 4096): instead of nm_spmm's route, one launch of the
  *     prefill kernel with each tile's columns split over 2 .. 8 workgroups, whole blocks of
- *     512 columns each ([NEWS-NEW]: batched tokens run matrix-matrix products).
+ *     512 columns each ([NEWS-NEW]: batched tokens run matrix-matrix products); the same
+ *     for 16:32 batches of 12 .. 16 vectors on layers of at most 2048 rows.
  * In both the last-arriving workgroup of a tile sums the fp32 partial tiles in split order
  * (fixed, so bit-identical run to run, but not bit-identical to nm_spmm's order: the same
  * tolerance against the exact product). workspace: device memory, 16-byte aligned, owned by

@@ -102,7 +102,9 @@ bool prefill_route(int64_t rows, int64_t cols, int64_t batch, int N, int M, cons
 // against 97.2 and 106; 14336 x 4096 at 64 26.8 against 27.9. At 16 vectors and below one
 // skinny launch is as fast or faster (4096 x 4096 2:4: 9.2 against 11.9).
 bool colsplit_route(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev) {
-  return batch > kSkinnyBatch && prefill_pattern(N, M) && prefill_workspace_bytes(rows, cols, batch, dev) > 0;
+  const bool size = batch > kSkinnyBatch || (N == 16 && batch >= kExpandColSplitMinBatch &&
+                                             rows <= kExpandColSplitMaxRows);
+  return size && prefill_pattern(N, M) && prefill_workspace_bytes(rows, cols, batch, dev) > 0;
 }
 
 // nm_spmm's argument checks, before any HIP call.

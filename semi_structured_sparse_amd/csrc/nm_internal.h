@@ -148,6 +148,12 @@ constexpr int64_t kSkinnyBeforePrefillMaxBatch = 48;
 // 16-vector launches are as fast (4096 x 4096 at 32 vectors: 28.8 us against about 51 for one
 // launch of 64 x 64 tiles walking every column; at 64 vectors 55.7 against 51).
 constexpr int64_t kExpandPrefillMinBatch = 64;
+// With a workspace, 16:32 batches of kExpandColSplitMinBatch..kSkinnyBatch vectors on layers
+// of at most kExpandColSplitMaxRows rows take the column-split expansion kernel instead of
+// the small-batch or 16-vector expansion launch (1024 x 4096 at 16 vectors: 11.2 against
+// 15.2 us; 2048 x 4096: 11.7 against 14.7; 4096 x 4096: 16.4 against 15.7, so not there).
+constexpr int64_t kExpandColSplitMinBatch = 12;
+constexpr int64_t kExpandColSplitMaxRows = 2048;
 constexpr int64_t kSkinnyBeforePrefillMaxRows = 4096;
 constexpr int64_t kSkinnyExpandFullMinRows = 2048;
 bool use_skinny(int64_t rows, int64_t cols, int64_t batch, int n, int m, const DeviceInfo& dev);
@@ -172,8 +178,8 @@ bool prefill_route(int64_t rows, int64_t cols, int64_t batch, int N, int M, cons
 // The smallest batch nm_spmm runs on the prefill kernels for pattern N (32; 16:32: 64).
 int64_t prefill_min_batch(int N);
 // Whether nm_spmm_ws, given a workspace of prefill_workspace_bytes, runs a batch on the
-// column-split prefill kernel: 2:4, 4:8 and 8:16 batches of more than kSkinnyBatch vectors
-// whose small-tile grid leaves CUs idle.
+// column-split prefill kernel: 50% batches of more than kSkinnyBatch vectors whose
+// small-tile grid leaves CUs idle, and the 16:32 batches above on small layers.
 bool colsplit_route(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev);
 
 // Name of the kernel configuration the prefill launchers pick (static string).

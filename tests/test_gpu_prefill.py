@@ -400,3 +400,24 @@ def test_prefill_expand_one_hot_routing_and_malformed_masks():
         Yb = nm.nm_spmm_prefill(v, mm, Xr, 16, 32)
         torch.cuda.synchronize()
         assert Yb.shape == (70, R)
+
+
+@pytest.mark.parametrize("R,C,T", [(1000, 4064, 12), (2048, 4096, 16), (300, 1056, 13)])
+def test_colsplit_expand_small_batches(R, C, T):
+    """16:32 at 12..16 vectors on layers of at most 2048 rows takes the column-split
+    expansion kernel with a workspace (Y within tolerance of the oracle on every row); on
+    larger layers, or with fewer vectors, nm_spmm's route."""
+    name = nm.spmm_ws_variant(R, C, T, 16, 32)
+    say(f"colsplit 16:32 small batch {R}x{C} vectors={T} {name}")
+    assert name in COLSPLIT_NAMES[(16, 32)], name
+    W = synth.weight(R, C, seed=4400 + T)
+    X = synth.activations(T, C, seed=4401 + T)
+    v, m = nm.nm_pack(up_f16(W), 16, 32)
+    ws = nm.spmm_workspace(R, C, T, 16, 32)
+    Y = down_f16(nm.nm_spmm_ws(v, m, up_f16(X), 16, 32, ws))
+    assert int(ws[:_counter_bytes()].count_nonzero()) == 0
+    rv, rm = oracle.pack_ref(W, 16, 32)
+    rep = oracle.y_tolerance_report(Y, oracle.spmm_ref(rv, rm, X, C, 16, 32))
+    assert rep["ok"], rep
+    assert nm.spmm_ws_variant(4096, 4096, 16, 16, 32) == nm.spmm_variant(4096, 4096, 16, 16, 32)
+    assert nm.spmm_ws_variant(R, C, 11, 16, 32) == nm.spmm_variant(R, C, 11, 16, 32)
