@@ -92,9 +92,10 @@ int nm_pack(const uint16_t* W, uint16_t* values, uint32_t* masks,
  * [rows][cols] fp16 that (values, masks) describe: the kept values at their columns (the
  * value of set bit j of word w is the one after the set bits below j), +0 elsewhere.
  * Bit-exact and deterministic. A mask word with the wrong number of set bits gives an
- * unspecified W' but no access outside the inputs. For products that have no sparse path
- * (for example a prefill-sized batch of a 4:8 ... 16:32 matrix), decoding once and using
- * nm_gemm_dense_prefill is the fast route. values, W 16-byte aligned; masks 4-byte. */
+ * unspecified W' but no access outside the inputs. For prompt-sized products of 4:8, 8:16
+ * and 16:32, whose sparse prefill kernels are slower than the dense one (they keep half the
+ * bytes, not half the instructions), decoding once and using nm_gemm_dense_prefill is the
+ * fastest route where a dense copy fits. values, W 16-byte aligned; masks 4-byte. */
 int nm_unpack(const uint16_t* values, const uint32_t* masks, uint16_t* W,
               int64_t rows, int64_t cols, int N, int M, void* stream);
 

@@ -144,9 +144,9 @@ int spmm_dispatch(const uint16_t* values, const uint32_t* masks, const uint16_t*
   }
   if (M != 2 * N && cols > max_cols_for(dev)) return NM_ERR_TOO_WIDE;  // 25%: single-vector kernel only
   if (N == 16 && M == 32 && batch >= kSkinnyMinBatch) {
-    // 16:32 from 5 vectors, any batch (it has no prefill kernel): each launch of up to 16
-    // vectors on the expansion kernel where that measured faster, else on the small-batch
-    // kernel 8 vectors at a time
+    // 16:32 from 5 vectors up to the prefill route's batch: each launch of up to 16 vectors
+    // on the expansion kernel where that measured faster, else on the small-batch kernel 8
+    // vectors at a time
     for (int64_t b0 = 0; b0 < batch; b0 += kSkinnyBatch) {
       const int64_t nb = batch - b0 < kSkinnyBatch ? batch - b0 : kSkinnyBatch;
       if (skinny_expand_chunk(rows, cols, nb, dev)) {
