@@ -605,6 +605,13 @@ def main():
         torch.cuda.empty_cache()
         decode = decode_sweep(args, torch, nm, synth, dev, args.tokens, max(1, min(args.warmup, 5)),
                               with_cpu=not args.no_cpu_baseline)
+        torch.cuda.empty_cache()
+        # the batch products and the prefill product, summarised (their own workloads give
+        # the full lines: --batch B, --workload prefill)
+        batches = [batch_summary(args, torch, nm, synth, dev, b) for b in EXTRA_BATCHES]
+        torch.cuda.empty_cache()
+        prefill = prefill_summary(prefill_run(args, torch, nm, synth, dev, EXTRA_PROMPT, (2, 4), 5, 2,
+                                              None if args.no_cpu_baseline else EXTRA_PREFILL_CPU_FRAC))
 
     out = {
         "metric": METRIC,
@@ -651,7 +658,70 @@ def main():
     }
     if decode is not None:
         out["decode"] = decode
+        out["batch_products"] = batches
+        out["prefill"] = prefill
     sys.exit(emit(out))
+
+
+EXTRA_BATCHES = (8, 24)        # batch products summarised in the default line
+EXTRA_PROMPT = 2048            # prompt of the prefill summary
+EXTRA_PREFILL_CPU_FRAC = 1 / 64  # rows of each prefill layer the oracle checks (all tokens)
+
+
+def batch_summary(args, torch, nm, synth, dev, B):
+    """The Llama-3.1-8B projections (4 shapes x 4 patterns) at B activation vectors through
+    nm_spmm_ws (a workspace per layer), each layer alone as in --batch B: time per layer for
+    the sparse product, our dense batch product and torch.mm, the step's effective GB/s (the
+    sum of the layers' bytes over the sum of their times), and the oracle's Y against the
+    GPU's on each layer's first rows (all B vectors)."""
+    import oracle
+    wl = synth.WORKLOADS[2]
+    pats = [tuple(p) for p in wl["patterns"]]
+    t0 = time.time()
+    layers, dense = make_layers(torch, nm, synth, dev, 2, list(enumerate(wl["layers"])), pats, B, 1 / 64)
+    for L in layers:
+        L["ws"] = nm.spmm_workspace(L["R"], L["C"], B, L["N"], L["M"], device=dev)
+    pool_bytes = args.pool_gib * (1 << 30)
+    launches = max(40, max(pool_copies(L["bytes"], pool_bytes) for L in layers),
+                   max(pool_copies(D["bytes"], pool_bytes) for D in dense.values()))
+    per_layer, per_s = per_layer_times(torch, nm, layers, dense, B, pool_bytes, launches)
+    worst, rel = 0.0, 0.0
+    for L in layers:
+        rv, rm = oracle.pack_ref(L["W_cpu"], L["N"], L["M"])
+        ref = oracle.spmm_ref(rv, rm, L["x_host"], L["C"], L["N"], L["M"])
+        rep = oracle.y_tolerance_report(L["y"][:, :ref.shape[-1]].cpu().numpy(), ref)
+        worst, rel = max(worst, rep["max_err_over_bound"]), max(rel, rep["rel_l2"])
+    us = sum(per_s)
+    nbytes = sum(L["bytes"] for L in layers)
+    best = [r.get("best_dense_us", r["dense_us"]) for r in per_layer]
+    log(f"batch {B}: {nbytes / (us * 1e-6) / 1e9:.0f} GB/s, {sum(r['dense_us'] for r in per_layer) / us:.3f}x "
+        f"over the dense kernel, {sum(best) / us:.3f}x over the faster dense ({time.time() - t0:.1f}s)")
+    out = {"batch": B, "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "us_per_step": round(us, 2),
+           "speedup_vs_dense": round(sum(r["dense_us"] for r in per_layer) / us, 3),
+           "speedup_vs_best_dense": round(sum(best) / us, 3),
+           "slowest_layer_vs_best_dense": min(r.get("speedup_vs_best_dense", r["speedup"]) for r in per_layer),
+           "per_layer": [{k: r[k] for k in ("shape", "pattern", "kernel", "us", "dense_us", "torch_mm_us",
+                                            "speedup_vs_best_dense") if k in r} for r in per_layer],
+           "timing": "each layer alone as in --batch B (sum of the layers' times, no step graph)",
+           "parity_vs_gpu": {"rows": "first 1/64 of each layer's rows, all vectors", "max_err_over_bound": worst,
+                             "rel_l2": rel, "ok": worst <= 1.0 and rel <= 1e-3}}
+    del layers, dense
+    return out
+
+
+def prefill_summary(full):
+    """The fields of a prefill line (prefill_run) that the default line carries."""
+    keep = ("value", "unit", "ms_per_step", "speedup_vs_dense", "speedup_vs_best_dense_per_layer_sum",
+            "dense_equiv_TFLOPs")
+    out = {k: full[k] for k in keep}
+    out["config"] = full["config"]["workload"]
+    out["roofline"] = {k: full["roofline"][k] for k in ("kernel", "achieved", "peak", "frac", "traffic")}
+    out["per_layer"] = [{k: r[k] for k in ("layer", "kernel", "us", "useful_TFLOPs", "dense_us", "torch_mm_us",
+                                           "speedup_vs_best_dense")} for r in full["per_layer"]]
+    if full.get("cpu_baseline"):
+        out["parity_vs_gpu"] = dict(full["cpu_baseline"]["parity_vs_gpu"],
+                                    rows=full["cpu_baseline"]["sample"])
+    return out
 
 
 def decode_sweep(args, torch, nm, synth, dev, K, Wm, with_cpu=True):
@@ -926,8 +996,20 @@ def decode_roofline(nm, items, ms_token, N, M):
 
 
 def prefill_main(args, torch, nm, synth, dev):
-    """Prefill: the Llama-3.1-8B projection shapes (q, kv, gate_up, down) as 2:4 packed
-    weights (or the first of --patterns: 4:8 or 8:16, as two 2:4 operands) times a prompt of
+    """The prefill workload (prefill_run) at --prompt tokens, 2:4 or the first of --patterns."""
+    pat = (2, 4)
+    if args.patterns:   # one of the patterns with a matrix-core product
+        pat = tuple(int(v) for v in args.patterns.split(",")[0].split(":"))
+        if pat not in ((2, 4), (4, 8), (8, 16), (16, 32)):
+            print(f"prefill: pattern {pat} has no matrix-core product (2:4, 4:8, 8:16, 16:32)", file=sys.stderr)
+            sys.exit(2)
+    return emit(prefill_run(args, torch, nm, synth, dev, args.prompt, pat, args.steps, args.warmup,
+                            None if args.no_cpu_baseline else args.cpu_rows_frac))
+
+
+def prefill_run(args, torch, nm, synth, dev, T, pat, K, Wm, cpu_frac):
+    """Prefill: the Llama-3.1-8B projection shapes (q, kv, gate_up, down) as packed weights of
+    pattern `pat` (4:8 and 8:16 as two 2:4 operands, 16:32 expanded) times a prompt of
     --prompt tokens (X [tokens][cols], seeded N(0,1)), on the sparse matrix cores (nm_spmm_ws
     with a workspace per layer: the prefill kernel, whose output tiles' columns are split
     over several workgroups where the prompt is too short for the tiles to fill the GPU); a
@@ -940,15 +1022,8 @@ def prefill_main(args, torch, nm, synth, dev):
     instruction's doubled rate is not counted as peak)."""
     import numpy as np
     lib = nm.lib()
-    T = args.prompt
     cfg = 6
     shapes = synth.LLAMA31_8B
-    pat = (2, 4)
-    if args.patterns:   # one of the patterns with a matrix-core product
-        pat = tuple(int(v) for v in args.patterns.split(",")[0].split(":"))
-        if pat not in ((2, 4), (4, 8), (8, 16)):
-            print(f"prefill: pattern {pat} has no matrix-core product (2:4, 4:8, 8:16)", file=sys.stderr)
-            sys.exit(2)
     N, M = pat
     t_gen = time.time()
     items = []
@@ -1012,7 +1087,6 @@ def prefill_main(args, torch, nm, synth, dev):
     torch.cuda.synchronize()
     del cal
 
-    K, Wm = args.steps, args.warmup
     ms_sp = graph_ms(sp_step, K, Wm)
     ms_dn = graph_ms(dn_step, K, Wm)
     # per layer: each product alone, 20 launches in a graph, median of 3 replays
@@ -1061,8 +1135,8 @@ def prefill_main(args, torch, nm, synth, dev):
                 "avg_launch_us": round(kern_us[dom] / kern_n[dom], 3),
                 "flops_counted": "useful: 2 x rows x cols/2 x tokens (kept weights)"}
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = prefill_cpu_baseline(items, T, args.cpu_rows_frac, N, M)
+    if cpu_frac is not None:
+        cpu = prefill_cpu_baseline(items, T, cpu_frac, N, M)
     out = {
         "metric": f"{N}:{M} prefill SpMM useful TFLOP/s on the sparse matrix cores + speedup vs dense matrix-core GEMM",
         "value": round(value, 1),
@@ -1093,7 +1167,7 @@ def prefill_main(args, torch, nm, synth, dev):
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
-    return emit(out)
+    return out
 
 
 def best_dense_us(ours_us, torch_mm_us):

@@ -149,3 +149,28 @@ def test_batch_workspace_arguments_and_kernel_names():
     assert bench.batch_kernel_name(FakeNm, L2, 8) == "ws<1024,8192,8,2,4>"
     assert bench.batch_kernel_name(FakeNm, L8, 12) == "ws<1024,4096,12,8,16>"
     assert bench.batch_kernel_name(FakeNm, Ln, 8) == "routed<4096,4096,8,2,4>"
+
+
+def test_prefill_summary_and_parity_gate():
+    """The default line's prefill object keeps the prefill line's headline fields, roofline
+    and per-layer figures; a failed parity record inside it (or inside a batch summary)
+    fails the whole line."""
+    import bench
+    full = {"value": 600.0, "unit": "TFLOP/s", "ms_per_step": 0.47, "speedup_vs_dense": 1.5,
+            "speedup_vs_best_dense_per_layer_sum": 1.2, "dense_equiv_TFLOPs": 1200.0,
+            "config": {"workload": "w", "tokens": 2048},
+            "roofline": {"kernel": "k", "achieved": 700.0, "peak": 2500.0, "frac": 0.28, "traffic": None,
+                         "bound": "mfma"},
+            "per_layer": [{"layer": "q", "kernel": "k", "us": 50.0, "useful_TFLOPs": 600.0, "dense_us": 70.0,
+                           "torch_mm_us": 80.0, "speedup_vs_best_dense": 1.4, "extra": 1}],
+            "cpu_baseline": {"sample": "s", "parity_vs_gpu": {"max_err_over_bound": 0.05, "rel_l2": 2e-4,
+                                                              "ok": True}}}
+    out = bench.prefill_summary(full)
+    assert out["value"] == 600.0 and out["roofline"]["frac"] == 0.28 and out["config"] == "w"
+    assert out["per_layer"] == [{"layer": "q", "kernel": "k", "us": 50.0, "useful_TFLOPs": 600.0, "dense_us": 70.0,
+                                 "torch_mm_us": 80.0, "speedup_vs_best_dense": 1.4}]
+    assert out["parity_vs_gpu"]["ok"] is True and out["parity_vs_gpu"]["rows"] == "s"
+    line = {"value": 1.0, "prefill": out, "batch_products": [{"batch": 8, "parity_vs_gpu": {"ok": True}}]}
+    assert bench.parity_failures(line) == []
+    line["batch_products"][0]["parity_vs_gpu"]["ok"] = False
+    assert bench.parity_failures(line) == ["batch_products[0].parity_vs_gpu"]
