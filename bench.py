@@ -1138,7 +1138,9 @@ def prefill_run(args, torch, nm, synth, dev, T, pat, K, Wm, cpu_frac):
     if cpu_frac is not None:
         cpu = prefill_cpu_baseline(items, T, cpu_frac, N, M)
     out = {
-        "metric": f"{N}:{M} prefill SpMM useful TFLOP/s on the sparse matrix cores + speedup vs dense matrix-core GEMM",
+        "metric": f"{N}:{M} prefill SpMM useful TFLOP/s on the "
+                  f"{'dense matrix cores (expanded fragments)' if N == 16 else 'sparse matrix cores'} "
+                  f"+ speedup vs dense matrix-core GEMM",
         "value": round(value, 1),
         "unit": "TFLOP/s",
         "n_gpus": 1,
