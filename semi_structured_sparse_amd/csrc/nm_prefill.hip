@@ -39,21 +39,24 @@ bool use_large(int64_t rows, int64_t tokens, const DeviceInfo& dev) {
 // is within about 15% of every measured time and picks the fastest tile or one within 7% of
 // it): 14336 x 4096 x 512, 2:4, 58.6 us on 256 x 128 against 119.2 on 64 x 64; 4096 x 14336 x
 // 1024, 125.6 on 128 x 128 against 219.7; 4:8 at 4096 x 4096 x 2048, 96.3 on 128 x 256
-// against 116.4 on 256 x 128. The split patterns' steps cost more (two instructions and the
-// table lookups per fragment), so their wide token tiles pay off sooner.
+// against 116.4 on 256 x 128; 64 x 128 tiles (three or more workgroups per CU) at 512 tokens:
+// 4:8 at 4096 x 14336, 136 against 156 us on 128 x 64; 16:32 at 4096 x 4096, 64 against 83
+// on 64 x 64. The split patterns' steps cost more (two instructions and the table lookups per
+// fragment), so their wide token tiles pay off sooner.
 struct TileCost {
   int tr, tt;
   double t1, tn;
 };
-constexpr TileCost kDirectTiles[] = {{1, 4, 0.266, 0.210}, {2, 4, 0.378, 0.328}, {2, 8, 0.537, 0.475},
-                                     {4, 8, 0.717, 0.825}, {4, 16, 1.27, 1.38}};
-constexpr TileCost kSplitTiles[] = {{1, 4, 0.45, 0.273},  {2, 4, 0.68, 0.443}, {2, 8, 0.91, 0.693},
-                                    {4, 8, 1.57, 1.57},   {2, 16, 1.40, 1.42}, {4, 16, 2.28, 2.37}};
+constexpr TileCost kDirectTiles[] = {{1, 4, 0.266, 0.210}, {1, 8, 0.428, 0.310}, {2, 4, 0.378, 0.328},
+                                     {2, 8, 0.537, 0.475}, {4, 8, 0.717, 0.825}, {4, 16, 1.27, 1.38}};
+constexpr TileCost kSplitTiles[] = {{1, 4, 0.45, 0.273}, {1, 8, 0.625, 0.435}, {2, 4, 0.68, 0.443},
+                                    {2, 8, 0.91, 0.693}, {4, 8, 1.57, 1.57},   {2, 16, 1.40, 1.42},
+                                    {4, 16, 2.28, 2.37}};
 // 16:32's steps expand each word's fragments through LDS first (about twice the split
 // patterns' step time). It has no 256-row tiles: 256 x 128 (2.62 us a step) lost to
 // 128 x 256 at every measured size, and 256 x 256 would spill its expansion registers.
-constexpr TileCost kExpandTiles[] = {{1, 4, 0.80, 0.51}, {2, 4, 1.28, 0.93}, {2, 8, 1.46, 1.09},
-                                     {2, 16, 1.85, 1.83}};
+constexpr TileCost kExpandTiles[] = {{1, 4, 0.80, 0.51},  {1, 8, 0.963, 0.627}, {1, 16, 1.37, 0.944},
+                                     {2, 4, 1.28, 0.93},  {2, 8, 1.46, 1.09},   {2, 16, 1.85, 1.83}};
 
 // the kernel family of a 50% pattern: 2:4 direct, 4:8 / 8:16 split, 16:32 expanded
 int pf_mode(int n) { return n == 2 ? kPfDirect : n == 16 ? kPfExpand : kPfSplit; }
@@ -84,9 +87,14 @@ const void* sparse_kernel(int mode) {
                             : reinterpret_cast<const void*>(&prefill_expand_kernel<TR, TT, 64, kDepth>);
 }
 
-// The kernel of a tile in the mode's table (2:4 has no 128 x 256 tile, 16:32 no 256-row one).
+// The kernel of a tile in the mode's table (64 x 256 for 16:32 only; 128 x 256 not for 2:4;
+// 256-row tiles not for 16:32).
 const void* sparse_kernel_of(const TileCost& t, int mode) {
-  if (t.tr == 1) return sparse_kernel<1, 4>(mode);
+  if (t.tr == 1) {
+    if (t.tt == 4) return sparse_kernel<1, 4>(mode);
+    if (t.tt == 8) return sparse_kernel<1, 8>(mode);
+    return reinterpret_cast<const void*>(&prefill_expand_kernel<1, 16, 64, kDepth>);   // 16:32 only
+  }
   if (t.tr == 2) {
     if (t.tt == 4) return sparse_kernel<2, 4>(mode);
     if (t.tt == 8) return sparse_kernel<2, 8>(mode);
@@ -212,17 +220,18 @@ const char* prefill_colsplit_variant(int64_t rows, int64_t cols, int64_t tokens,
 const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const DeviceInfo& dev, int n) {
   if (sparse) {
     static const char* const kNames[3][5][3] = {
-        {{"prefill_spmm_kernel<1, 4, 64, 2>", "", ""},
+        {{"prefill_spmm_kernel<1, 4, 64, 2>", "prefill_spmm_kernel<1, 8, 64, 2>", ""},
          {"prefill_spmm_kernel<2, 4, 64, 2>", "prefill_spmm_kernel<2, 8, 64, 2>", ""},
          {"", "", ""},
          {"prefill_spmm_kernel<4, 8, 64, 2>", "prefill_spmm_kernel<4, 16, 64, 2>", ""},
          {"", "", ""}},
-        {{"prefill_split_kernel<1, 4, 64, 2>", "", ""},
+        {{"prefill_split_kernel<1, 4, 64, 2>", "prefill_split_kernel<1, 8, 64, 2>", ""},
          {"prefill_split_kernel<2, 4, 64, 2>", "prefill_split_kernel<2, 8, 64, 2>", "prefill_split_kernel<2, 16, 64, 2>"},
          {"", "", ""},
          {"prefill_split_kernel<4, 8, 64, 2>", "prefill_split_kernel<4, 16, 64, 2>", ""},
          {"", "", ""}},
-        {{"prefill_expand_kernel<1, 4, 64, 2>", "", ""},
+        {{"prefill_expand_kernel<1, 4, 64, 2>", "prefill_expand_kernel<1, 8, 64, 2>",
+          "prefill_expand_kernel<1, 16, 64, 2>"},
          {"prefill_expand_kernel<2, 4, 64, 2>", "prefill_expand_kernel<2, 8, 64, 2>",
           "prefill_expand_kernel<2, 16, 64, 2>"},
          {"", "", ""},
@@ -230,7 +239,8 @@ const char* prefill_variant(int64_t rows, int64_t tokens, bool sparse, const Dev
          {"", "", ""}}};
     const int mode = pf_mode(n);
     const TileCost t = sparse_tile(rows, tokens, mode, dev);
-    const int col = t.tr == 1 ? 0 : t.tr == 2 ? (t.tt == 4 ? 0 : t.tt == 8 ? 1 : 2) : (t.tt == 8 ? 0 : 1);
+    const int col = t.tr == 4 ? (t.tt == 8 ? 0 : 1) : t.tr == 1 ? (t.tt == 4 ? 0 : t.tt == 8 ? 1 : 2)
+                                                  : (t.tt == 4 ? 0 : t.tt == 8 ? 1 : 2);
     return kNames[mode][t.tr - 1][col];
   }
   return use_large<DenseLarge>(rows, tokens, dev) ? "prefill_gemm_kernel<2, 16, 64, 2>"

@@ -20,11 +20,12 @@ pytestmark = pytest.mark.gpu
 # (rows, cols, tokens): ragged rows (tiles of 16, 64, 128 and 256 rows), ragged tokens
 # (tiles of 16, 64, 128 and 256), a 32-column tail step, one step, many steps, a last block
 # of mask steps cut short; every tile configuration the sparse kernel picks (64 x 64,
-# 128 x 64, 128 x 128, 256 x 128, 256 x 256: the larger ones where their grid still fills
-# the CUs) and both of the dense kernel's
+# 64 x 128, 128 x 64, 128 x 128, 256 x 128, 256 x 256: the larger ones where their grid
+# still fills the CUs) and both of the dense kernel's
 SMALL = [(1, 32, 1), (17, 64, 5), (16, 96, 16), (33, 128, 17), (64, 4064, 63), (65, 4096, 64),
          (127, 544, 65), (300, 1056, 255), (129, 2080, 257), (1000, 4064, 700), (4100, 1024, 2050),
-         (4096, 160, 2048), (2600, 2208, 3000), (16400, 160, 1100), (16448, 160, 16), (16448, 1056, 80)]
+         (4096, 160, 2048), (2600, 2208, 3000), (16400, 160, 1100), (16448, 160, 16), (16448, 1056, 80),
+         (5440, 1056, 336)]
 
 
 def check_prefill(W, X, tag, rows_idx=None, dense=True):
@@ -64,7 +65,8 @@ def test_prefill_both_tile_configurations_are_exercised():
     if torch.cuda.get_device_properties(device()).multi_processor_count != 256:
         pytest.skip("the shapes are chosen for a 256-CU part")
     names = {nm.prefill_variant(R, C, T, s) for R, C, T in SMALL for s in (True, False)}
-    assert names == {"prefill_spmm_kernel<1, 4, 64, 2>", "prefill_spmm_kernel<2, 4, 64, 2>",
+    assert names == {"prefill_spmm_kernel<1, 4, 64, 2>", "prefill_spmm_kernel<1, 8, 64, 2>",
+                     "prefill_spmm_kernel<2, 4, 64, 2>",
                      "prefill_spmm_kernel<2, 8, 64, 2>", "prefill_spmm_kernel<4, 8, 64, 2>",
                      "prefill_spmm_kernel<4, 16, 64, 2>",
                      "prefill_gemm_kernel<1, 4, 64, 2>", "prefill_gemm_kernel<2, 16, 64, 2>"}, names
@@ -180,11 +182,12 @@ def test_prefill_full_size_llama8b(name, R, C):
 
 
 # 4:8 and 8:16 (split into two 2:4 operands): ragged rows and tokens, a 32-column tail step,
-# every tile configuration the split kernel picks (64 x 64, 128 x 64, 128 x 128, 128 x 256,
-# 256 x 128, 256 x 256)
+# every tile configuration the split kernel picks (64 x 64, 64 x 128, 128 x 64, 128 x 128,
+# 128 x 256, 256 x 128, 256 x 256)
 SPLIT_SMALL = [(17, 64, 5), (33, 128, 17), (65, 4096, 64), (300, 1056, 255), (129, 2080, 257), (4100, 1024, 2050),
-               (16400, 160, 1100), (2600, 2208, 3000), (16448, 1056, 16), (19648, 160, 272)]
-SPLIT_NAMES = {"prefill_split_kernel<1, 4, 64, 2>", "prefill_split_kernel<2, 4, 64, 2>",
+               (16400, 160, 1100), (2600, 2208, 3000), (16448, 1056, 16), (19648, 160, 272), (8256, 1056, 65)]
+SPLIT_NAMES = {"prefill_split_kernel<1, 4, 64, 2>", "prefill_split_kernel<1, 8, 64, 2>",
+               "prefill_split_kernel<2, 4, 64, 2>",
                "prefill_split_kernel<2, 8, 64, 2>", "prefill_split_kernel<2, 16, 64, 2>",
                "prefill_split_kernel<4, 8, 64, 2>", "prefill_split_kernel<4, 16, 64, 2>"}
 
@@ -355,10 +358,11 @@ def test_colsplit_small_workspace_takes_nm_spmm_route():
 
 # 16:32 (fragments expanded for the dense instruction): ragged rows and tokens, a 32-column
 # tail step, a last block of mask steps cut short, every tile configuration it picks (64 x 64,
-# 128 x 64, 128 x 128, 128 x 256)
+# 64 x 128, 64 x 256, 128 x 64, 128 x 128, 128 x 256)
 EXPAND_SMALL = [(17, 64, 5), (33, 128, 17), (65, 4096, 64), (300, 1056, 255), (8256, 160, 65), (16448, 1056, 65),
-                (2600, 2208, 3000)]
-EXPAND_NAMES = {"prefill_expand_kernel<1, 4, 64, 2>", "prefill_expand_kernel<2, 4, 64, 2>",
+                (2600, 2208, 3000), (10944, 160, 144), (16448, 160, 16)]
+EXPAND_NAMES = {"prefill_expand_kernel<1, 4, 64, 2>", "prefill_expand_kernel<1, 8, 64, 2>",
+                "prefill_expand_kernel<1, 16, 64, 2>", "prefill_expand_kernel<2, 4, 64, 2>",
                 "prefill_expand_kernel<2, 8, 64, 2>", "prefill_expand_kernel<2, 16, 64, 2>"}
 
 
