@@ -176,14 +176,20 @@ int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, ui
  *     up to 256 tokens on 4096 x 4096): instead of nm_spmm's route, one launch of the
  *     prefill kernel with each tile's columns split over 2 .. 8 workgroups, whole blocks of
  *     512 columns each ([NEWS-NEW]: batched tokens run matrix-matrix products); the same
- *     for 16:32 batches of 12 .. 16 vectors on layers of at most 2048 rows.
+ *     for 16:32 batches of 12 .. 16 vectors on layers of at most 2048 rows;
+ *   - prompts of more than 128 tokens (2:4, 4:8, 8:16) where a model of the kernels' step
+ *     times puts it well ahead: tiles of 128 x 128 or 256 x 128 (2:4 only) with their
+ *     columns split over 2 .. 8 workgroups, at most one workgroup per CU (e.g. 4096 x 14336
+ *     at 256 .. 1024 tokens).
  * In both the last-arriving workgroup of a tile sums the fp32 partial tiles in split order
  * (fixed, so bit-identical run to run, but not bit-identical to nm_spmm's order: the same
  * tolerance against the exact product). workspace: device memory, 16-byte aligned, owned by
  * the caller; its first 4 * CU-count bytes, rounded up to 256 (1 KiB on MI355X), are
  * counters that must be zero before the first call on it (e.g. one hipMemset when
  * allocated); every call leaves them zero again, so one workspace serves any sequence of
- * shapes on the device. NULL or a smaller workspace runs nm_spmm's kernels (no error). Calls
+ * shapes on the device. NULL or a smaller workspace runs nm_spmm's kernels (no error; a
+ * prompt whose taller split does not fit takes the 64-row split where that applies and
+ * fits). Calls
  * that use one workspace must be ordered (one stream): overlapping calls on it race. Other
  * arguments and errors as nm_spmm; a misaligned workspace is NM_ERR_ALIGN. */
 int nm_spmm_ws(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
@@ -194,7 +200,8 @@ int nm_spmm_ws(const uint16_t* values, const uint32_t* masks, const uint16_t* X,
  * the shape takes no split (or the arguments are invalid, or no device): the counters, then
  * the partial tiles, 1 KiB per 16-row tile and split on the skinny kernels (at most 257 KiB
  * on MI355X), 8 or 16 KiB per 64-row tile and split on the prefill kernel (the grid within
- * two workgroups per CU: at most 8 MiB + 1 KiB on MI355X). */
+ * two workgroups per CU: at most 8 MiB + 1 KiB on MI355X), 64 or 128 KiB per 128- or 256-row
+ * tile and split on the taller splits (one workgroup per CU: at most 32 MiB + 1 KiB). */
 size_t nm_spmm_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, int N, int M);
 
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight
@@ -203,12 +210,12 @@ size_t nm_spmm_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, int N,
  * call on that GPU until the process ends. The same arguments, routing, Y and errors as
  * nm_spmm_ws with a workspace of that size; a shape whose split needs more
  * (nm_spmm_workspace_bytes > NM_NOALLOC_SCRATCH_BYTES; none on MI355X, whose largest is
- * 8 MiB + 1 KiB) is NM_ERR_SCRATCH before any launch. Calls no hipMalloc/hipFree. The first call
+ * 32 MiB + 1 KiB) is NM_ERR_SCRATCH before any launch. Calls no hipMalloc/hipFree. The first call
  * on a GPU looks the array up (hipGetSymbolAddress) and queues a fill kernel that clears it
  * on `stream`, ahead of its own kernels; the kernels leave the counters at zero after every
  * call. All calls on one GPU share the array: calls that overlap on one GPU (other streams,
  * other threads, without ordering between them) race and give unspecified Y. */
-#define NM_NOALLOC_SCRATCH_BYTES (8u * 1024u * 1024u + 4096u)
+#define NM_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u + 4096u)
 int nm_spmm_noalloc(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
                     int64_t rows, int64_t cols, int64_t batch, int N, int M, void* stream);
 

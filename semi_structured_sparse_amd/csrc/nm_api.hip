@@ -104,7 +104,7 @@ bool prefill_route(int64_t rows, int64_t cols, int64_t batch, int N, int M, cons
 bool colsplit_route(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev) {
   const bool size = batch > kSkinnyBatch || (N == 16 && batch >= kExpandColSplitMinBatch &&
                                              rows <= kExpandColSplitMaxRows);
-  return size && prefill_pattern(N, M) && prefill_workspace_bytes(rows, cols, batch, dev) > 0;
+  return size && prefill_pattern(N, M) && prefill_workspace_bytes(rows, cols, batch, N, dev) > 0;
 }
 
 // nm_spmm's argument checks, before any HIP call.
@@ -130,7 +130,7 @@ int spmm_dispatch(const uint16_t* values, const uint32_t* masks, const uint16_t*
   hipError_t e = current_device_info(&dev);
   if (e != hipSuccess) return hip_fail(e);
   if (workspace != nullptr && colsplit_route(rows, cols, batch, N, M, dev) &&
-      workspace_bytes >= prefill_workspace_bytes(rows, cols, batch, dev)) {
+      workspace_bytes >= prefill_workspace_bytes(rows, cols, batch, N, dev)) {
     // column-split prefill product (launch_prefill_spmm takes the split with this workspace)
     e = launch_prefill_spmm(values, masks, X, Y, rows, cols, batch, N, M, static_cast<hipStream_t>(stream), dev,
                             workspace, workspace_bytes);
@@ -198,7 +198,7 @@ int spmm_dispatch(const uint16_t* values, const uint32_t* masks, const uint16_t*
 // Workspace bytes spmm_dispatch can use for the product (0 when it would not use one).
 size_t spmm_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev) {
   if (!valid_shape(rows, cols) || !valid_pattern(N, M) || batch < 1 || batch > kPrefillMaxTokens) return 0;
-  if (colsplit_route(rows, cols, batch, N, M, dev)) return prefill_workspace_bytes(rows, cols, batch, dev);
+  if (colsplit_route(rows, cols, batch, N, M, dev)) return prefill_workspace_bytes(rows, cols, batch, N, dev);
   if (prefill_route(rows, cols, batch, N, M, dev)) return 0;
   if (!use_skinny(rows, cols, batch < kSkinnyBatch ? batch : kSkinnyBatch, N, M, dev)) return 0;
   return skinny_workspace_bytes(rows, cols, int(batch < kSkinnyBatch ? batch : kSkinnyBatch), N, dev);

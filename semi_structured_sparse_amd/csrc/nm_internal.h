@@ -90,11 +90,13 @@ bool prefill_fits(int64_t rows, int64_t cols, int64_t tokens);
 // 50% patterns with a matrix-core prefill product: all four.
 bool prefill_pattern(int n, int m);
 // With a workspace of at least prefill_workspace_bytes (0: the shape takes no column split)
-// a grid too small for the CUs (mid-size batches) splits each output tile's columns over
-// several workgroups; without one (or a smaller one) it runs unsplit. The counters must be
-// zero before the launch, which leaves them zero (the same counter region as the skinny
-// kernels' column splits, so one workspace serves both in stream order).
-size_t prefill_workspace_bytes(int64_t rows, int64_t cols, int64_t tokens, const DeviceInfo& dev);
+// a grid too small for the CUs (mid-size batches), or a prompt of more than 128 tokens whose
+// columns are better split over taller tiles, splits each output tile's columns over several
+// workgroups; without one (or a smaller one) it runs the 64-row split if that fits, else
+// unsplit. The counters must be zero before the launch, which leaves them zero (the same
+// counter region as the skinny kernels' column splits, so one workspace serves both in
+// stream order). n: the pattern's N (the split kernels and their costs depend on it).
+size_t prefill_workspace_bytes(int64_t rows, int64_t cols, int64_t tokens, int n, const DeviceInfo& dev);
 hipError_t launch_prefill_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, uint16_t* Y,
                                int64_t rows, int64_t cols, int64_t tokens, int n, int m, hipStream_t stream,
                                const DeviceInfo& dev, void* workspace = nullptr, size_t workspace_bytes = 0);
@@ -179,7 +181,8 @@ bool prefill_route(int64_t rows, int64_t cols, int64_t batch, int N, int M, cons
 int64_t prefill_min_batch(int N);
 // Whether nm_spmm_ws, given a workspace of prefill_workspace_bytes, runs a batch on the
 // column-split prefill kernel: 50% batches of more than kSkinnyBatch vectors whose
-// small-tile grid leaves CUs idle, and the 16:32 batches above on small layers.
+// small-tile grid leaves CUs idle or that split better over taller tiles, and the 16:32
+// batches above on small layers.
 bool colsplit_route(int64_t rows, int64_t cols, int64_t batch, int N, int M, const DeviceInfo& dev);
 
 // Name of the kernel configuration the prefill launchers pick (static string).

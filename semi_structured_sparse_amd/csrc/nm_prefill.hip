@@ -154,6 +154,106 @@ size_t colsplit_bytes(const ColPlan& p, const DeviceInfo& dev) {
   return counter_bytes(dev) + size_t(p.tiles) * size_t(p.splits) * size_t(kThreads) * size_t(p.tt) * 16u;
 }
 
+// Taller column splits for prompts of more than 128 tokens. There the 64-row tiles fill the
+// CUs, but each walks every column (or half of them) with little reuse of its operands, while
+// 128 x 128 and 256 x 128 tiles do more products per step but leave CUs idle unsplit. Their
+// columns go to S = 2, 4 or 8 workgroups with at most one workgroup per CU (tiles * S <= CUs).
+// Estimated time of a column split, fitted to sweeps on MI355X (256 .. 1024 tokens, 1024 ..
+// 14336 rows and columns, 2:4 and 4:8, each split and tile; within about 15% on the large
+// layers): kSplitFixedUs + kSplitRoundUs per further round of partial loads in the hand-off
+// + kSplitStepScale * (the tile's modelled step time) per 64-column step of a split. The same
+// form estimates what runs otherwise (the 64-row split, else the unsplit tile, one round), and
+// a taller split is taken below kTallMargin of that (the margin leaves out the shapes where
+// the split measured no faster, e.g. 4096 x 4096 at 768 and 1024 tokens). Measured (µs, the
+// split against what ran before, weights read from memory / resident in the last-level
+// cache): 2:4 4096 x 14336 x 512 80 / 71 against 121 / 95 (256 x 128, 4 splits), x 256 51 / 48
+// against 65 / 54 (128 x 128, 4 splits); 8192 x 28672 x 256 145 / 132 against 243 / 234;
+// 5120 x 25600 x 256 114 / 94 against 210 / 164; 4096 x 4096 x 384 29 / 27 against 36 / 30;
+// 4:8 4096 x 14336 x 384 114 / 107 against 135 / 131.
+constexpr int64_t kTallMinTokens = 128;
+constexpr double kSplitFixedUs = 7.6;
+constexpr double kSplitRoundUs = 3.0;
+constexpr double kSplitStepScale = 1.17;
+constexpr double kTallMargin = 0.78;
+constexpr int kStepsPerBlock = kColBlock / 64;
+
+struct TallPlan {
+  int tr = 0, tt = 0, splits = 1, blocks = 0;
+  int64_t tiles = 0;   // 0: no taller split
+};
+
+const TileCost* mode_tile(int mode, int tr, int tt) {
+  const TileCost* c = mode == kPfDirect ? kDirectTiles : mode == kPfSplit ? kSplitTiles : kExpandTiles;
+  const int n = mode == kPfDirect ? int(sizeof(kDirectTiles) / sizeof(TileCost))
+              : mode == kPfSplit  ? int(sizeof(kSplitTiles) / sizeof(TileCost))
+                                  : int(sizeof(kExpandTiles) / sizeof(TileCost));
+  for (int i = 0; i < n; ++i)
+    if (c[i].tr == tr && c[i].tt == tt) return &c[i];
+  return nullptr;
+}
+
+// steps: 64-column steps of one workgroup; n: workgroups per CU; rounds: hand-off rounds
+double split_estimate_us(int64_t steps, const TileCost& c, int64_t n, int rounds) {
+  return kSplitFixedUs + kSplitRoundUs * double(rounds - 1) + kSplitStepScale * double(steps) * (c.t1 + double(n - 1) * c.tn);
+}
+
+int handoff_rounds(int tr, int tt, int splits) {
+  const int r = handoff_slots(tr * tt);
+  return (splits + r - 1) / r;
+}
+
+TallPlan tall_plan(int64_t rows, int64_t cols, int64_t tokens, int mode, const DeviceInfo& dev) {
+  TallPlan best;
+  if (mode == kPfExpand || tokens <= kTallMinTokens) return best;
+  const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
+  const int64_t nblk = ceil_div(cols, kColBlock);
+  double current;
+  const ColPlan p = colsplit_plan(rows, cols, tokens, dev);
+  const TileCost* small = mode_tile(mode, 1, p.tt);
+  if (p.splits > 1 && small != nullptr) {
+    current = split_estimate_us(int64_t(p.blocks) * kStepsPerBlock, *small, ceil_div(p.tiles * p.splits, cus),
+                                handoff_rounds(1, p.tt, p.splits));
+  } else {
+    const TileCost u = sparse_tile(rows, tokens, mode, dev);
+    const int64_t grid = ceil_div(rows, 64 * u.tr) * ceil_div(tokens, 16 * u.tt);
+    current = split_estimate_us(ceil_div(cols, 64), u, ceil_div(grid, cus), 1);
+  }
+  double best_t = kTallMargin * current;
+  static const int kTall[2][2] = {{2, 8}, {4, 8}};
+  for (const auto& tl : kTall) {
+    const int tr = tl[0], tt = tl[1];
+    if (mode == kPfSplit && tr == 4) continue;   // the split operands' 256-row tiles are not built split
+    const TileCost* c = mode_tile(mode, tr, tt);
+    if (c == nullptr) continue;
+    const int64_t tiles = ceil_div(rows, 64 * tr) * ceil_div(tokens, 16 * tt);
+    for (int s = 2; s <= kMaxColSplits && s <= nblk && tiles * s <= cus; s *= 2) {
+      const int blocks = int(ceil_div(nblk, s));
+      const int splits = int(ceil_div(nblk, blocks));
+      const double t = split_estimate_us(int64_t(blocks) * kStepsPerBlock, *c, 1, handoff_rounds(tr, tt, splits));
+      if (t < best_t) {
+        best_t = t;
+        best.tr = tr;
+        best.tt = tt;
+        best.splits = splits;
+        best.blocks = blocks;
+        best.tiles = tiles;
+      }
+    }
+  }
+  return best;
+}
+
+size_t tall_bytes(const TallPlan& t, const DeviceInfo& dev) {
+  if (t.tiles == 0) return 0;
+  return counter_bytes(dev) + size_t(t.tiles) * size_t(t.splits) * size_t(kThreads) * size_t(t.tr) * size_t(t.tt) * 16u;
+}
+
+const void* tall_kernel(const TallPlan& t, int mode) {
+  if (mode == kPfSplit) return reinterpret_cast<const void*>(&prefill_colsplit_kernel<2, 8, 64, kDepth, true>);
+  return t.tr == 2 ? reinterpret_cast<const void*>(&prefill_colsplit_kernel<2, 8, 64, kDepth, false>)
+                   : reinterpret_cast<const void*>(&prefill_colsplit_kernel<4, 8, 64, kDepth, false>);
+}
+
 const void* colsplit_kernel(int tt, int mode) {
   if (mode == kPfExpand)
     return tt == 2 ? reinterpret_cast<const void*>(&prefill_colsplit_expand_kernel<1, 2, 64, kDepth>)
@@ -167,8 +267,10 @@ const void* colsplit_kernel(int tt, int mode) {
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int64_t rows, int64_t cols, int64_t tokens, const DeviceInfo& dev) {
+size_t prefill_workspace_bytes(int64_t rows, int64_t cols, int64_t tokens, int n, const DeviceInfo& dev) {
   if (!prefill_fits(rows, cols, tokens)) return 0;
+  const TallPlan t = tall_plan(rows, cols, tokens, pf_mode(n), dev);
+  if (t.tiles > 0) return tall_bytes(t, dev);
   return colsplit_bytes(colsplit_plan(rows, cols, tokens, dev), dev);
 }
 
@@ -178,6 +280,17 @@ hipError_t launch_prefill_spmm(const uint16_t* values, const uint32_t* masks, co
   if (!prefill_fits(rows, cols, tokens) || !prefill_pattern(n, m)) return hipErrorInvalidValue;
   int r = int(rows), c = int(cols), t = int(tokens);
   const int mode = pf_mode(n);
+  if (workspace != nullptr) {
+    const TallPlan tp = tall_plan(rows, cols, tokens, mode, dev);
+    if (tp.tiles > 0 && workspace_bytes >= tall_bytes(tp, dev)) {
+      int sp = tp.splits, bl = tp.blocks;
+      unsigned* cnt = static_cast<unsigned*>(workspace);
+      float4* part = reinterpret_cast<float4*>(static_cast<char*>(workspace) + counter_bytes(dev));
+      void* cargs[] = {&values, &masks, &X, &Y, &r, &c, &t, &sp, &bl, &part, &cnt};
+      return launch(tall_kernel(tp, mode), dim3(unsigned(tp.tiles * tp.splits)), dim3(kThreads), cargs, 0, stream,
+                    dev);
+    }
+  }
   const ColPlan p = colsplit_plan(rows, cols, tokens, dev);
   const size_t need = colsplit_bytes(p, dev);
   if (need > 0 && workspace != nullptr && workspace_bytes >= need) {
@@ -207,9 +320,14 @@ hipError_t launch_prefill_gemm(const uint16_t* W, const uint16_t* X, uint16_t* Y
 }
 
 const char* prefill_colsplit_variant(int64_t rows, int64_t cols, int64_t tokens, const DeviceInfo& dev, int n) {
+  const int mode = pf_mode(n);
+  const TallPlan t = tall_plan(rows, cols, tokens, mode, dev);
+  if (t.tiles > 0) {
+    if (mode == kPfSplit) return "prefill_colsplit_kernel<2, 8, 64, 2, true>";
+    return t.tr == 2 ? "prefill_colsplit_kernel<2, 8, 64, 2, false>" : "prefill_colsplit_kernel<4, 8, 64, 2, false>";
+  }
   const ColPlan p = colsplit_plan(rows, cols, tokens, dev);
   if (p.splits == 1) return "";
-  const int mode = pf_mode(n);
   if (mode == kPfExpand)
     return p.tt == 2 ? "prefill_colsplit_expand_kernel<1, 2, 64, 2>" : "prefill_colsplit_expand_kernel<1, 4, 64, 2>";
   if (mode == kPfSplit)

@@ -556,6 +556,13 @@ __device__ __forceinline__ void sparse_main_loop(const XStager<TR, TT, KS>& xst,
 constexpr int kColBlock = 512;
 constexpr int kMaxColSplits = 8;
 
+// Partial tiles the last workgroup of a tile loads at once in the hand-off (split_handoff): 32
+// float4 per lane in flight, so all 8 of a 64 x 64 tile at once and one at a time for
+// 256 x 128 (tiles = 16 x 16 output tiles per wave, TR * TT).
+constexpr int handoff_slots(int tiles) {
+  return tiles >= 32 ? 1 : (32 / tiles < kMaxColSplits ? 32 / tiles : kMaxColSplits);
+}
+
 struct ColSplit {
   float4* part;
   unsigned* cnt;
@@ -582,30 +589,33 @@ __device__ __forceinline__ bool split_handoff(f4_t (&acc)[TR][TT], const ColSpli
   if (tid == 0) *cs.flag = atomicAdd(cs.cnt + cs.tile, 1u);
   __syncthreads();
   if (*cs.flag != unsigned(cs.splits - 1)) return false;
-  // the tile's last workgroup: every split's partial is complete. All kMaxColSplits loads
-  // are issued at once (one memory round trip), then summed in split order; those past the
+  // the tile's last workgroup: every split's partial is complete. The partials are loaded R
+  // splits at a time (one memory round trip per R) and summed in split order; slots past the
   // last split are outside the resource and read zero, and adding zero after the last split
   // leaves the sum as it is.
-  float4 v[kMaxColSplits][TR][TT];
-#pragma unroll
-  for (int k = 0; k < kMaxColSplits; ++k)
-#pragma unroll
-    for (int a = 0; a < TR; ++a)
-#pragma unroll
-      for (int b = 0; b < TT; ++b)
-        v[k][a][b] = coherent_load16(pr, uint32_t((k * TR * TT + a * TT + b) * kThreads + tid) * 16u);
+  constexpr int R = handoff_slots(TR * TT);
   zero(acc);
+  for (int k0 = 0; k0 < cs.splits; k0 += R) {
+    float4 v[R][TR][TT];
 #pragma unroll
-  for (int k = 0; k < kMaxColSplits; ++k) {
+    for (int k = 0; k < R; ++k)
 #pragma unroll
-    for (int a = 0; a < TR; ++a)
+      for (int a = 0; a < TR; ++a)
 #pragma unroll
-      for (int b = 0; b < TT; ++b) {
-        acc[a][b][0] += v[k][a][b].x;
-        acc[a][b][1] += v[k][a][b].y;
-        acc[a][b][2] += v[k][a][b].z;
-        acc[a][b][3] += v[k][a][b].w;
-      }
+        for (int b = 0; b < TT; ++b)
+          v[k][a][b] = coherent_load16(pr, uint32_t(((k0 + k) * TR * TT + a * TT + b) * kThreads + tid) * 16u);
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+#pragma unroll
+      for (int a = 0; a < TR; ++a)
+#pragma unroll
+        for (int b = 0; b < TT; ++b) {
+          acc[a][b][0] += v[k][a][b].x;
+          acc[a][b][1] += v[k][a][b].y;
+          acc[a][b][2] += v[k][a][b].z;
+          acc[a][b][3] += v[k][a][b].w;
+        }
+    }
   }
   if (tid == 0) atomicExch(cs.cnt + cs.tile, 0u);
   return true;

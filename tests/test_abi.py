@@ -262,10 +262,10 @@ def test_noalloc_scratch_is_static_and_bounded():
     for alloc in ("hipMalloc", "hipFree", "hipMemset", "hipExtMalloc", "hipHostMalloc", "malloc(", "new "):
         assert alloc not in code, alloc
     hdr = open(os.path.join(ROOT, "include", "nm_sparse.h")).read()
-    # 8 MiB of partial tiles (the largest split on a 256-CU part: 512 workgroups x 16 KiB)
-    # and room for the counters
+    # 32 MiB of partial tiles (the largest split on a 256-CU part: 256 workgroups x 128 KiB
+    # of a 256 x 128 tile) and room for the counters
     m = re.search(r"#define NM_NOALLOC_SCRATCH_BYTES \((\d+)u \* (\d+)u \* (\d+)u \+ (\d+)u\)", hdr)
-    assert m and int(m.group(1)) * int(m.group(2)) * int(m.group(3)) + int(m.group(4)) == 8 * 1024 * 1024 + 4096
+    assert m and int(m.group(1)) * int(m.group(2)) * int(m.group(3)) + int(m.group(4)) == 32 * 1024 * 1024 + 4096
 
 
 def test_spmm_workspace_bytes_invalid_arguments():

@@ -129,7 +129,8 @@ def test_prefill_graph_replays():
 # column splits (nm_spmm_ws, and nm_spmm_noalloc on the library's static scratch): the
 # counters are reset by the kernels themselves, so replays find them at zero
 SPLIT_GRAPH_CASES = [(2, 4, 1024, 8192, 8), (4, 8, 1024, 4096, 12), (2, 4, 1000, 8192, 17), (8, 16, 4096, 4096, 64),
-                     (2, 4, 1024, 4096, 256), (16, 32, 1024, 4096, 16), (16, 32, 4096, 14336, 40)]
+                     (2, 4, 1024, 4096, 256), (16, 32, 1024, 4096, 16), (16, 32, 4096, 14336, 40),
+                     (2, 4, 4000, 14304, 300), (8, 16, 2050, 10240, 260)]
 
 
 @pytest.mark.parametrize("N,M,R,C,B", SPLIT_GRAPH_CASES)

@@ -425,3 +425,59 @@ def test_colsplit_expand_small_batches(R, C, T):
     assert rep["ok"], rep
     assert nm.spmm_ws_variant(4096, 4096, 16, 16, 32) == nm.spmm_variant(4096, 4096, 16, 16, 32)
     assert nm.spmm_ws_variant(R, C, 11, 16, 32) == nm.spmm_variant(R, C, 11, 16, 32)
+
+
+# Prompts of more than 128 tokens whose columns split better over taller tiles (nm_spmm_ws):
+# 256 x 128 (2:4) and 128 x 128 tiles, 2 and 4 splits, ragged rows (tiles of 128 and 256
+# rows), ragged tokens (128-token tiles), columns ending inside a 512-column block, an uneven
+# last split (28 blocks over 4), one and several hand-off rounds of partial loads
+TALL = {(2, 4): [(4000, 14304, 300, "<4, 8, 64, 2, false>"), (2050, 10240, 260, "<2, 8, 64, 2, false>"),
+                 (1900, 8160, 1000, "<4, 8, 64, 2, false>"), (8100, 8160, 290, "<4, 8, 64, 2, false>")],
+        (4, 8): [(4000, 14304, 300, "<2, 8, 64, 2, true>"), (1900, 8160, 1000, "<2, 8, 64, 2, true>")],
+        (8, 16): [(2050, 10240, 260, "<2, 8, 64, 2, true>"), (3000, 6144, 600, "<2, 8, 64, 2, true>")]}
+
+
+@pytest.mark.parametrize("N,M", [(2, 4), (4, 8), (8, 16)])
+def test_tall_colsplit_ragged(N, M):
+    """The taller column splits: Y within the oracle's tolerance on sampled rows (every token),
+    the counters left at zero, the same bits on a second call; a workspace one block too small
+    for them runs the route that ran before (within tolerance of the same rows)."""
+    for i, (R, C, T, tmpl) in enumerate(TALL[(N, M)]):
+        name = nm.spmm_ws_variant(R, C, T, N, M)
+        need = nm.spmm_workspace_bytes(R, C, T, N, M)
+        say(f"tall colsplit {N}:{M} {R}x{C} tokens={T} {name} workspace={need}")
+        assert name == "prefill_colsplit_kernel" + tmpl, (R, C, T, name)
+        W = synth.weight(R, C, seed=4500 + 10 * i + N)
+        X = synth.activations(T, C, seed=4550 + i)
+        values, masks = nm.nm_pack(up_f16(W), N, M)
+        Xd = up_f16(X)
+        ws = nm.spmm_workspace(R, C, T, N, M)
+        Yb = down_bits16(nm.nm_spmm_ws(values, masks, Xd, N, M, ws))
+        assert int(ws[:_counter_bytes()].count_nonzero()) == 0
+        assert np.array_equal(down_bits16(nm.nm_spmm_ws(values, masks, Xd, N, M, ws)), Yb)
+        idx = sample_rows(R, k=24, rpb=128)
+        rv, rm = oracle.pack_ref(W[idx], N, M)
+        ref = oracle.spmm_ref(rv, rm, X, C, N, M)
+        rep = oracle.y_tolerance_report(Yb.view(np.float16)[:, idx], ref)
+        assert rep["ok"], ((R, C, T), N, M, rep)
+        small = torch.zeros(need - 256, dtype=torch.uint8, device=device())
+        rep = oracle.y_tolerance_report(down_f16(nm.nm_spmm_ws(values, masks, Xd, N, M, small))[:, idx], ref)
+        assert rep["ok"], ((R, C, T), N, M, "smaller workspace", rep)
+
+
+@pytest.mark.parametrize("N,M,R,C,T", [(2, 4, 4000, 14304, 300), (4, 8, 1900, 8160, 1000)])
+def test_tall_colsplit_one_hot_columns_are_exact(N, M, R, C, T):
+    """Token t one-hot at column (37 t) mod C, so the nonzero products fall in every split:
+    each output is one kept weight (the other splits add zeros), bit-exact."""
+    W = synth.weight(R, C, seed=4600 + N)
+    rv, rm = oracle.pack_ref(W, N, M)
+    D = oracle.unpack_ref(rv, rm, C, N, M)
+    cols = (37 * np.arange(T)) % C
+    X = np.zeros((T, C), dtype=np.float16)
+    X[np.arange(T), cols] = 1.0
+    assert nm.spmm_ws_variant(R, C, T, N, M).startswith("prefill_colsplit_kernel<" + ("4" if N == 2 else "2") + ", 8")
+    ws = nm.spmm_workspace(R, C, T, N, M)
+    Y = down_bits16(nm.nm_spmm_ws(up_f16(rv), up_u32(rm), up_f16(X), N, M, ws))
+    want = D[:, cols].T.copy()
+    want[want == 0x8000] = 0
+    assert np.array_equal(Y, want)

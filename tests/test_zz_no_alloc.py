@@ -41,6 +41,7 @@ PAIRS = [
     (((8, 16), 1024, 4096, 12), ((4, 8), 512, 4096, 9)),      # the split patterns: 4 x 64, then 8 x 32
     (((2, 4), 1000, 8192, 17), ((2, 4), 300, 8224, 6)),       # column-split prefill kernel; skinny, ragged
     (((4, 8), 4096, 14336, 40), ((2, 4), 1024, 4096, 20)),    # column-split prefill: 7 x 64 tiles, then 8 x 16
+    (((2, 4), 4000, 14304, 300), ((8, 16), 2050, 10240, 260)),  # taller splits: 4 x 48 tiles of 256 x 128, then 4 x 51 of 128 x 128
 ]
 
 
