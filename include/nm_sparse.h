@@ -177,7 +177,7 @@ int nm_spmm(const uint16_t* values, const uint32_t* masks, const uint16_t* X, ui
  *     prefill kernel with each tile's columns split over 2 .. 8 workgroups, whole blocks of
  *     512 columns each ([NEWS-NEW]: batched tokens run matrix-matrix products); the same
  *     for 16:32 batches of 12 .. 16 vectors on layers of at most 2048 rows;
- *   - prompts of more than 128 tokens (2:4, 4:8, 8:16) where a model of the kernels' step
+ *   - prompts of more than 128 tokens (any 50% pattern) where a model of the kernels' step
  *     times puts it well ahead: tiles of 128 x 128 or 256 x 128 (2:4 only) with their
  *     columns split over 2 .. 8 workgroups, at most one workgroup per CU (e.g. 4096 x 14336
  *     at 256 .. 1024 tokens).

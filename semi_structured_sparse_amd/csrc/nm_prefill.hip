@@ -169,7 +169,8 @@ size_t colsplit_bytes(const ColPlan& p, const DeviceInfo& dev) {
 // cache): 2:4 4096 x 14336 x 512 80 / 71 against 121 / 95 (256 x 128, 4 splits), x 256 51 / 48
 // against 65 / 54 (128 x 128, 4 splits); 8192 x 28672 x 256 145 / 132 against 243 / 234;
 // 5120 x 25600 x 256 114 / 94 against 210 / 164; 4096 x 4096 x 384 29 / 27 against 36 / 30;
-// 4:8 4096 x 14336 x 384 114 / 107 against 135 / 131.
+// 4:8 4096 x 14336 x 384 114 / 107 against 135 / 131; 16:32 (128 x 128 only) 4096 x 14336 x 256
+// 96 / 94 against 134 / 135, 8192 x 28672 x 256 329 / 320 against 404 / 404.
 constexpr int64_t kTallMinTokens = 128;
 constexpr double kSplitFixedUs = 7.6;
 constexpr double kSplitRoundUs = 3.0;
@@ -204,7 +205,7 @@ int handoff_rounds(int tr, int tt, int splits) {
 
 TallPlan tall_plan(int64_t rows, int64_t cols, int64_t tokens, int mode, const DeviceInfo& dev) {
   TallPlan best;
-  if (mode == kPfExpand || tokens <= kTallMinTokens) return best;
+  if (tokens <= kTallMinTokens) return best;
   const int64_t cus = dev.cu_count > 0 ? dev.cu_count : 256;
   const int64_t nblk = ceil_div(cols, kColBlock);
   double current;
@@ -222,7 +223,7 @@ TallPlan tall_plan(int64_t rows, int64_t cols, int64_t tokens, int mode, const D
   static const int kTall[2][2] = {{2, 8}, {4, 8}};
   for (const auto& tl : kTall) {
     const int tr = tl[0], tt = tl[1];
-    if (mode == kPfSplit && tr == 4) continue;   // the split operands' 256-row tiles are not built split
+    if (mode != kPfDirect && tr == 4) continue;   // 256-row tiles: 2:4 only
     const TileCost* c = mode_tile(mode, tr, tt);
     if (c == nullptr) continue;
     const int64_t tiles = ceil_div(rows, 64 * tr) * ceil_div(tokens, 16 * tt);
@@ -249,6 +250,7 @@ size_t tall_bytes(const TallPlan& t, const DeviceInfo& dev) {
 }
 
 const void* tall_kernel(const TallPlan& t, int mode) {
+  if (mode == kPfExpand) return reinterpret_cast<const void*>(&prefill_colsplit_expand_kernel<2, 8, 64, kDepth>);
   if (mode == kPfSplit) return reinterpret_cast<const void*>(&prefill_colsplit_kernel<2, 8, 64, kDepth, true>);
   return t.tr == 2 ? reinterpret_cast<const void*>(&prefill_colsplit_kernel<2, 8, 64, kDepth, false>)
                    : reinterpret_cast<const void*>(&prefill_colsplit_kernel<4, 8, 64, kDepth, false>);
@@ -323,6 +325,7 @@ const char* prefill_colsplit_variant(int64_t rows, int64_t cols, int64_t tokens,
   const int mode = pf_mode(n);
   const TallPlan t = tall_plan(rows, cols, tokens, mode, dev);
   if (t.tiles > 0) {
+    if (mode == kPfExpand) return "prefill_colsplit_expand_kernel<2, 8, 64, 2>";
     if (mode == kPfSplit) return "prefill_colsplit_kernel<2, 8, 64, 2, true>";
     return t.tr == 2 ? "prefill_colsplit_kernel<2, 8, 64, 2, false>" : "prefill_colsplit_kernel<4, 8, 64, 2, false>";
   }

@@ -428,16 +428,20 @@ def test_colsplit_expand_small_batches(R, C, T):
 
 
 # Prompts of more than 128 tokens whose columns split better over taller tiles (nm_spmm_ws):
-# 256 x 128 (2:4) and 128 x 128 tiles, 2 and 4 splits, ragged rows (tiles of 128 and 256
+# 256 x 128 (2:4) and 128 x 128 tiles, 2, 4 and 8 splits, ragged rows (tiles of 128 and 256
 # rows), ragged tokens (128-token tiles), columns ending inside a 512-column block, an uneven
 # last split (28 blocks over 4), one and several hand-off rounds of partial loads
-TALL = {(2, 4): [(4000, 14304, 300, "<4, 8, 64, 2, false>"), (2050, 10240, 260, "<2, 8, 64, 2, false>"),
-                 (1900, 8160, 1000, "<4, 8, 64, 2, false>"), (8100, 8160, 290, "<4, 8, 64, 2, false>")],
-        (4, 8): [(4000, 14304, 300, "<2, 8, 64, 2, true>"), (1900, 8160, 1000, "<2, 8, 64, 2, true>")],
-        (8, 16): [(2050, 10240, 260, "<2, 8, 64, 2, true>"), (3000, 6144, 600, "<2, 8, 64, 2, true>")]}
+_CS = "prefill_colsplit_kernel"
+TALL = {(2, 4): [(4000, 14304, 300, _CS + "<4, 8, 64, 2, false>"), (2050, 10240, 260, _CS + "<2, 8, 64, 2, false>"),
+                 (1900, 8160, 1000, _CS + "<4, 8, 64, 2, false>"), (8100, 8160, 290, _CS + "<4, 8, 64, 2, false>")],
+        (4, 8): [(4000, 14304, 300, _CS + "<2, 8, 64, 2, true>"), (1900, 8160, 1000, _CS + "<2, 8, 64, 2, true>")],
+        (8, 16): [(2050, 10240, 260, _CS + "<2, 8, 64, 2, true>"), (3000, 6144, 600, _CS + "<2, 8, 64, 2, true>")],
+        (16, 32): [(4000, 14304, 300, "prefill_colsplit_expand_kernel<2, 8, 64, 2>"),
+                   (2050, 10240, 300, "prefill_colsplit_expand_kernel<2, 8, 64, 2>"),
+                   (1900, 8160, 150, "prefill_colsplit_expand_kernel<2, 8, 64, 2>")]}
 
 
-@pytest.mark.parametrize("N,M", [(2, 4), (4, 8), (8, 16)])
+@pytest.mark.parametrize("N,M", [(2, 4), (4, 8), (8, 16), (16, 32)])
 def test_tall_colsplit_ragged(N, M):
     """The taller column splits: Y within the oracle's tolerance on sampled rows (every token),
     the counters left at zero, the same bits on a second call; a workspace one block too small
@@ -446,7 +450,7 @@ def test_tall_colsplit_ragged(N, M):
         name = nm.spmm_ws_variant(R, C, T, N, M)
         need = nm.spmm_workspace_bytes(R, C, T, N, M)
         say(f"tall colsplit {N}:{M} {R}x{C} tokens={T} {name} workspace={need}")
-        assert name == "prefill_colsplit_kernel" + tmpl, (R, C, T, name)
+        assert name == tmpl, (R, C, T, name)
         W = synth.weight(R, C, seed=4500 + 10 * i + N)
         X = synth.activations(T, C, seed=4550 + i)
         values, masks = nm.nm_pack(up_f16(W), N, M)
