@@ -160,9 +160,10 @@ size_t colsplit_bytes(const ColPlan& p, const DeviceInfo& dev) {
 // columns go to S = 2, 4 or 8 workgroups with at most one workgroup per CU (tiles * S <= CUs).
 // Estimated time of a column split, fitted to sweeps on MI355X (256 .. 1024 tokens, 1024 ..
 // 14336 rows and columns, 2:4 and 4:8, each split and tile; within about 15% on the large
-// layers): kSplitFixedUs + kSplitRoundUs per further round of partial loads in the hand-off
-// + kSplitStepScale * (the tile's modelled step time) per 64-column step of a split. The same
-// form estimates what runs otherwise (the 64-row split, else the unsplit tile, one round), and
+// layers): kSplitFixedUs + kSplitRoundUs per further unit of partial loads in the hand-off
+// (handoff_units) + kSplitStepScale * (the tile's modelled step time) per 64-column step of a
+// split. The same form estimates what runs otherwise (the 64-row split, else the unsplit tile,
+// one unit), and
 // a taller split is taken below kTallMargin of that (the margin leaves out the shapes where
 // the split measured no faster, e.g. 4096 x 4096 at 768 and 1024 tokens). Measured (µs, the
 // split against what ran before, weights read from memory / resident in the last-level
@@ -193,15 +194,14 @@ const TileCost* mode_tile(int mode, int tr, int tt) {
   return nullptr;
 }
 
-// steps: 64-column steps of one workgroup; n: workgroups per CU; rounds: hand-off rounds
-double split_estimate_us(int64_t steps, const TileCost& c, int64_t n, int rounds) {
-  return kSplitFixedUs + kSplitRoundUs * double(rounds - 1) + kSplitStepScale * double(steps) * (c.t1 + double(n - 1) * c.tn);
+// steps: 64-column steps of one workgroup; n: workgroups per CU; units: hand-off load units
+double split_estimate_us(int64_t steps, const TileCost& c, int64_t n, int units) {
+  return kSplitFixedUs + kSplitRoundUs * double(units - 1) + kSplitStepScale * double(steps) * (c.t1 + double(n - 1) * c.tn);
 }
 
-int handoff_rounds(int tr, int tt, int splits) {
-  const int r = handoff_slots(tr * tt);
-  return (splits + r - 1) / r;
-}
+// The partials the last workgroup of a tile loads in the hand-off, in units of 32 float4 per
+// lane (a 64 x 64 tile's 8 splits make one unit, a 256 x 128 tile's S splits make S).
+int handoff_units(int tr, int tt, int splits) { return (splits * tr * tt + 31) / 32; }
 
 TallPlan tall_plan(int64_t rows, int64_t cols, int64_t tokens, int mode, const DeviceInfo& dev) {
   TallPlan best;
@@ -213,7 +213,7 @@ TallPlan tall_plan(int64_t rows, int64_t cols, int64_t tokens, int mode, const D
   const TileCost* small = mode_tile(mode, 1, p.tt);
   if (p.splits > 1 && small != nullptr) {
     current = split_estimate_us(int64_t(p.blocks) * kStepsPerBlock, *small, ceil_div(p.tiles * p.splits, cus),
-                                handoff_rounds(1, p.tt, p.splits));
+                                handoff_units(1, p.tt, p.splits));
   } else {
     const TileCost u = sparse_tile(rows, tokens, mode, dev);
     const int64_t grid = ceil_div(rows, 64 * u.tr) * ceil_div(tokens, 16 * u.tt);
@@ -230,7 +230,7 @@ TallPlan tall_plan(int64_t rows, int64_t cols, int64_t tokens, int mode, const D
     for (int s = 2; s <= kMaxColSplits && s <= nblk && tiles * s <= cus; s *= 2) {
       const int blocks = int(ceil_div(nblk, s));
       const int splits = int(ceil_div(nblk, blocks));
-      const double t = split_estimate_us(int64_t(blocks) * kStepsPerBlock, *c, 1, handoff_rounds(tr, tt, splits));
+      const double t = split_estimate_us(int64_t(blocks) * kStepsPerBlock, *c, 1, handoff_units(tr, tt, splits));
       if (t < best_t) {
         best_t = t;
         best.tr = tr;
