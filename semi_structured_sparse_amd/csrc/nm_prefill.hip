@@ -163,9 +163,10 @@ size_t colsplit_bytes(const ColPlan& p, const DeviceInfo& dev) {
 // layers): kSplitFixedUs + kSplitRoundUs per further unit of partial loads in the hand-off
 // (handoff_units) + kSplitStepScale * (the tile's modelled step time) per 64-column step of a
 // split. The same form estimates what runs otherwise (the 64-row split, else the unsplit tile,
-// one unit), and
-// a taller split is taken below kTallMargin of that (the margin leaves out the shapes where
-// the split measured no faster, e.g. 4096 x 4096 at 768 and 1024 tokens). Measured (µs, the
+// one unit), and a taller split is taken below kTallMargin of that (the margin leaves out the
+// shapes where the split measured no faster, e.g. 4096 x 4096 at 768 and 1024 tokens). The
+// hand-off's cost follows the partial bytes the last workgroup loads (kSplitRoundUs per unit of
+// 32 float4 per lane), not its round trips. Measured (µs, the
 // split against what ran before, weights read from memory / resident in the last-level
 // cache): 2:4 4096 x 14336 x 512 80 / 71 against 121 / 95 (256 x 128, 4 splits), x 256 51 / 48
 // against 65 / 54 (128 x 128, 4 splits); 8192 x 28672 x 256 145 / 132 against 243 / 234;
