@@ -606,12 +606,15 @@ def main():
         decode = decode_sweep(args, torch, nm, synth, dev, args.tokens, max(1, min(args.warmup, 5)),
                               with_cpu=not args.no_cpu_baseline)
         torch.cuda.empty_cache()
-        # the batch products and the prefill product, summarised (their own workloads give
-        # the full lines: --batch B, --workload prefill)
+        # the batch products and the prefill product (2048 and 512 tokens), summarised (their
+        # own workloads give the full lines: --batch B, --workload prefill --prompt T)
         batches = [batch_summary(args, torch, nm, synth, dev, b) for b in EXTRA_BATCHES]
         torch.cuda.empty_cache()
         prefill = prefill_summary(prefill_run(args, torch, nm, synth, dev, EXTRA_PROMPT, (2, 4), 5, 2,
                                               None if args.no_cpu_baseline else EXTRA_PREFILL_CPU_FRAC))
+        torch.cuda.empty_cache()
+        prefill_mid = prefill_summary(prefill_run(args, torch, nm, synth, dev, EXTRA_MID_PROMPT, (2, 4), 10, 3,
+                                                  None if args.no_cpu_baseline else EXTRA_PREFILL_CPU_FRAC))
 
     out = {
         "metric": METRIC,
@@ -660,11 +663,13 @@ def main():
         out["decode"] = decode
         out["batch_products"] = batches
         out["prefill"] = prefill
+        out["prefill_mid"] = prefill_mid
     sys.exit(emit(out))
 
 
 EXTRA_BATCHES = (8, 24)        # batch products summarised in the default line
 EXTRA_PROMPT = 2048            # prompt of the prefill summary
+EXTRA_MID_PROMPT = 512         # prompt of the mid-size prefill summary (column splits of taller tiles)
 EXTRA_PREFILL_CPU_FRAC = 1 / 64  # rows of each prefill layer the oracle checks (all tokens)
 
 
